@@ -1,0 +1,107 @@
+"""Planted mistakes in the oracle are caught by its pins (CPU only).
+
+Each case rewrites one line of an oracle module's source text (a dropped
+term, a wrong sign, a wrong index, a transposed operand), loads the mutant
+next to the real module, and checks that an independent pin rejects it.
+Nothing here touches the GPU.
+"""
+import inspect
+import math
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.decode as dec
+import oracle.jacobi as jac
+import oracle.factorize as rs
+from oracle.brute import decode_brute
+
+
+def _mutant(module, old, new):
+    src = inspect.getsource(module)
+    assert src.count(old) >= 1, old
+    m = types.ModuleType(module.__name__ + "_mutant")
+    m.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new, 1), module.__name__ + "_mutant", "exec"), m.__dict__)
+    return m
+
+
+def _brute_pin_ok(decode_fn):
+    g = np.random.default_rng(7)
+    N, r, r_lo, k, Hkv, Hq, d, T = 7, 4, 2, 3, 2, 4, 3, 2
+    W = Hkv * d
+    Uk, Bk, Uv, Bv = (g.standard_normal(s) for s in [(N, r), (r, W), (N, r), (r, W)])
+    Kt, Vt = g.standard_normal((T, W)), g.standard_normal((T, W))
+    q = g.standard_normal(Hq * d)
+    try:
+        res = decode_fn(Uk, Bk, Uv, Bv, q, Hkv, d, r_lo, k, 0.7, Kt, Vt)
+    except Exception:
+        return False
+    out, tops = decode_brute(Uk.tolist(), Bk.tolist(), Uv.tolist(), Bv.tolist(), q.tolist(),
+                             Hkv, d, r_lo, k, 0.7, Kt.tolist(), Vt.tolist())
+    ok = (np.max(np.abs(res["out"] - np.array(out))) <= 1e-12
+          and [list(t) for t in res["top"]] == tops)
+    # a case made of ties: duplicated key rows cut through by the top-k boundary
+    Uk2 = Uk.copy()
+    Uk2[[2, 4, 6]] = Uk2[0]
+    q2 = np.zeros_like(q)                   # every score ties: top-k = lowest indices
+    res2 = decode_fn(Uk2, Bk, Uv, Bv, q2, Hkv, d, r, 2, 0.7, Kt, Vt)
+    out2, tops2 = decode_brute(Uk2.tolist(), Bk.tolist(), Uv.tolist(), Bv.tolist(), q2.tolist(),
+                               Hkv, d, r, 2, 0.7, Kt.tolist(), Vt.tolist())
+    return bool(ok and np.max(np.abs(res2["out"] - np.array(out2))) <= 1e-12
+                and [list(t) for t in res2["top"]] == tops2)
+
+
+def test_real_decode_passes_brute_pin():
+    assert _brute_pin_ok(dec.decode_ref)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("g = h // G", "g = h % n_kv_heads"),                              # wrong KV head
+    ("order = np.lexsort((n, -s_lo))", "order = np.lexsort((n, s_lo))"),  # smallest instead of largest
+    ("order = np.lexsort((n, -s_lo))", "order = np.lexsort((-n, -s_lo))"),  # ties to higher index
+    ("o = o + p[N:] @ text_v[:, cols]", "o = o"),                    # text values dropped
+    ("V_sel[top] = V_full[top]", "pass"),                             # V never upgraded
+    ("s[top] = scale * (K_full[top] @ qh)", "s[top] = K_full[top] @ qh"),  # scale dropped
+    ("K_lo = U_k[:, :r_lo] @ B_k[:r_lo, cols]", "K_lo = U_k[:, :r_lo] @ B_k[:r_lo, cols] * 1.0001"),
+])
+def test_decode_mutants_are_caught(old, new):
+    m = _mutant(dec, old, new)
+    assert not _brute_pin_ok(m.decode_ref)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("new_i = c * xi - s * xj", "new_i = c * xi + s * xj"),
+    ("zeta = (beta - alpha) / (2.0 * gamma)", "zeta = (alpha - beta) / (2.0 * gamma)"),
+    ("V[:, i] = c * vi - s * vj", "V[:, i] = c * vi + s * vj"),
+])
+def test_jacobi_mutants_are_caught(old, new):
+    m = _mutant(jac, old, new)
+    A = np.random.default_rng(3).standard_normal((12, 9))
+    try:
+        U, s, V = m.jacobi_svd(A, max_sweeps=30)
+    except RuntimeError:
+        return       # failing to converge is also a rejection
+    ok = (np.allclose(s, np.linalg.svd(A, compute_uv=False), rtol=1e-12)
+          and np.linalg.norm(A - (U * s) @ V.T) <= 1e-12 * np.linalg.norm(A))
+    assert not ok
+
+
+@pytest.mark.parametrize("old,new", [
+    ("U = (Q @ Uc[:, :r]) * s[None, :r]", "U = Q @ Uc[:, :r]"),     # singular values dropped
+    ("Qt = orth_mgs2(A.T @ Q)", "Qt = orth_mgs2(A @ Q[:A.shape[1]])"),  # wrong operand
+    ("C = Q.T @ A", "C = Q.T @ A[::-1]"),                              # rows scrambled
+])
+def test_rsvd_mutants_are_caught(old, new):
+    m = _mutant(rs, old, new)
+    g = np.random.default_rng(4)
+    N, W, k = 30, 20, 4
+    A = g.standard_normal((N, k)) @ g.standard_normal((k, W))
+    try:
+        U, B, _ = m.rsvd(A, 4, g.standard_normal((W, 8)))
+        ok = np.linalg.norm(A - U @ B) <= 1e-11 * np.linalg.norm(A)
+    except (ValueError, RuntimeError, np.linalg.LinAlgError):
+        ok = False
+    assert not ok

@@ -1,0 +1,319 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test names the pin it implements:
+  P1  Jacobi SVD against numpy.linalg.svd, orthogonality, reconstruction
+  P2  Eckart–Young: truncation error = sqrt(sum of trailing sigma^2)
+  P3  exact recovery of a rank-k matrix (Jacobi, and rsvd with ell >= k)
+  P4  rsvd error >= optimum, and within 1% of it on the workloads' spectra
+  P5  full rank: decode == dense softmax attention (torch SDPA, float64)
+  P6  no-selection identities (r_lo = r, k = N, k = 0) against SDPA
+  P7  brute force in pure-Python loops on tiny inputs
+  P8  the latent (factor-space) formulation the GPU uses == explicit decode
+  P9  token permutation equivariance; GQA == MHA with duplicated KV heads
+  P10 edge values: N = 1, q = 0 (uniform weights, lowest-index ties)
+  P11 storage accounting against the numbers printed on the pages
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.brute import decode_brute
+from oracle.decode import decode_ref, select_top
+from oracle.jacobi import jacobi_svd
+from oracle.factorize import orth_mgs2, rsvd, round_to_storage
+from oracle import accounting
+from rank_compressed_kv_ap_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, K, V, n_kv_heads, d, scale):
+    """Dense attention of one query vector by torch's SDPA (float64, CPU)."""
+    Hq = q.shape[0] // d
+    G = Hq // n_kv_heads
+    out = np.zeros(Hq * d)
+    for h in range(Hq):
+        g = h // G
+        qt = torch.tensor(q[h * d:(h + 1) * d]).view(1, 1, 1, d)
+        kt = torch.tensor(np.ascontiguousarray(K[:, g * d:(g + 1) * d])).view(1, 1, -1, d)
+        vt = torch.tensor(np.ascontiguousarray(V[:, g * d:(g + 1) * d])).view(1, 1, -1, d)
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+        out[h * d:(h + 1) * d] = o.view(-1).numpy()
+    return out
+
+
+# ------------------------------------------------------------------ P1 / P2 / P3
+@pytest.mark.parametrize("shape", [(40, 30), (30, 40), (64, 64), (7, 1), (1, 5)])
+def test_p1_jacobi_matches_library_svd(shape):
+    A = _rand(1, *shape)
+    U, s, V = jacobi_svd(A)
+    s_np = np.linalg.svd(A, compute_uv=False)
+    assert np.allclose(s, s_np, rtol=1e-12, atol=1e-12 * s_np[0])
+    p = min(shape)
+    assert np.allclose(U.T @ U, np.eye(p), atol=1e-12)
+    assert np.allclose(V.T @ V, np.eye(p), atol=1e-12)
+    assert np.linalg.norm(A - (U * s) @ V.T) <= 1e-12 * np.linalg.norm(A)
+    assert np.all(np.diff(s) <= 0)
+
+
+def test_p1_jacobi_rank_deficient():
+    A = _rand(2, 30, 5) @ _rand(3, 5, 20)     # rank 5
+    U, s, V = jacobi_svd(A)
+    s_np = np.linalg.svd(A, compute_uv=False)
+    assert np.allclose(s[:5], s_np[:5], rtol=1e-12)
+    assert np.all(s[5:] <= 1e-12 * s[0])
+    assert np.linalg.norm(A - (U * s) @ V.T) <= 1e-12 * np.linalg.norm(A)
+
+
+@pytest.mark.parametrize("r", [1, 4, 16, 31])
+def test_p2_eckart_young(r):
+    A = (_rand(4, 48, 32) * (np.arange(1, 33) ** -1.0)) @ _rand(5, 32, 32)
+    U, s, V = jacobi_svd(A)
+    Ar = (U[:, :r] * s[:r]) @ V[:, :r].T
+    err = np.linalg.norm(A - Ar)
+    s_lib = np.linalg.svd(A, compute_uv=False)
+    closed = math.sqrt(float(np.sum(s_lib[r:] ** 2)))
+    assert abs(err - closed) <= 1e-11 * max(closed, 1e-300) + 1e-12 * np.linalg.norm(A)
+
+
+@pytest.mark.parametrize("k,r", [(3, 3), (3, 8), (10, 12)])
+def test_p3_rank_k_recovery(k, r):
+    N, W = 64, 48
+    A = _rand(6, N, k) @ _rand(7, k, W)
+    U, s, V = jacobi_svd(A)
+    assert np.linalg.norm(A - (U[:, :r] * s[:r]) @ V[:, :r].T) <= 1e-12 * np.linalg.norm(A)
+    ell = r + 4
+    Ur, Br, _ = rsvd(A, r, _rand(8, W, ell), power_iters=2)
+    assert np.linalg.norm(A - Ur @ Br) <= 1e-11 * np.linalg.norm(A)
+    # B has orthonormal rows on the captured range
+    assert np.allclose((Br @ Br.T)[:k, :k], np.eye(k), atol=1e-12)
+
+
+def test_orth_mgs2_is_orthonormal_and_spans():
+    Y = _rand(9, 50, 12)
+    Q = orth_mgs2(Y)
+    assert np.allclose(Q.T @ Q, np.eye(12), atol=1e-13)
+    # Y lies in range(Q)
+    assert np.linalg.norm(Y - Q @ (Q.T @ Y)) <= 1e-12 * np.linalg.norm(Y)
+    # rank-deficient input: vanishing columns become exact zeros
+    Yd = np.concatenate([Y[:, :3], Y[:, :3] @ _rand(10, 3, 2)], axis=1)
+    Qd = orth_mgs2(Yd)
+    assert np.allclose(Qd[:, 3:], 0.0)
+    assert np.allclose(Qd[:, :3].T @ Qd[:, :3], np.eye(3), atol=1e-13)
+
+
+# ------------------------------------------------------------------ P4
+@pytest.mark.parametrize("cfg,shrink", [(1, 1), (2, 8), (3, 8)])
+def test_p4_rsvd_near_optimal(cfg, shrink):
+    w = wl.WORKLOADS[cfg]
+    N = w.n_tokens // shrink
+    W = w.width // shrink
+    w = w.replace(n_tokens=N, n_kv_heads=max(1, w.n_kv_heads // shrink),
+                  inner_dim=min(N, W), grid=None)
+    W = w.width
+    A = wl.gen_kv(w, 0, 0).astype(np.float64)
+    s_all = np.linalg.svd(A, compute_uv=False)
+    e_opt = math.sqrt(float(np.sum(s_all[w.rank:] ** 2))) / np.linalg.norm(A)
+    U, B, _ = rsvd(A, w.rank, wl.gen_omega(w, 0, 0).astype(np.float64), w.power_iters)
+    e = oracle.recon_error(A, U, B)
+    assert e >= e_opt * (1 - 1e-12)
+    assert e <= 1.01 * e_opt
+
+
+# ------------------------------------------------------------------ P5 / P6
+def _exact_factors(A):
+    U, s, V = jacobi_svd(A)
+    return U * s, V.T
+
+
+@pytest.mark.parametrize("k", [0, 3, 10])
+def test_p5_full_rank_is_dense_attention(k):
+    N, Hkv, Hq, d = 10, 2, 4, 8
+    W = Hkv * d
+    K, V = _rand(11, N, W), _rand(12, N, W)
+    Uk, Bk = _exact_factors(K)
+    Uv, Bv = _exact_factors(V)
+    r = Uk.shape[1]           # = N = rank(K)
+    q = _rand(13, Hq * d)
+    scale = 1 / math.sqrt(d)
+    res = decode_ref(Uk, Bk, Uv, Bv, q, Hkv, d, r, k, scale)
+    ref = _sdpa(q, K, V, Hkv, d, scale)
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-10
+
+
+def test_p5_full_rank_with_text_is_dense_attention():
+    N, T, Hkv, Hq, d = 9, 4, 2, 2, 8
+    W = Hkv * d
+    K, V = _rand(14, N, W), _rand(15, N, W)
+    Kt, Vt = _rand(16, T, W), _rand(17, T, W)
+    Uk, Bk = _exact_factors(K)
+    Uv, Bv = _exact_factors(V)
+    q = _rand(18, Hq * d)
+    res = decode_ref(Uk, Bk, Uv, Bv, q, Hkv, d, N, 4, 0.3, Kt, Vt)
+    ref = _sdpa(q, np.vstack([K, Kt]), np.vstack([V, Vt]), Hkv, d, 0.3)
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-10
+
+
+def test_p6_no_selection_identities():
+    N, r, Hkv, Hq, d = 20, 6, 2, 4, 8
+    W = Hkv * d
+    Uk, Bk = _rand(20, N, r), _rand(21, r, W)
+    Uv, Bv = _rand(22, N, r), _rand(23, r, W)
+    q = _rand(24, Hq * d)
+    sc = 0.25
+    full = _sdpa(q, Uk @ Bk, Uv @ Bv, Hkv, d, sc)
+    for r_lo, k in [(r, 0), (r, 7), (2, N)]:
+        res = decode_ref(Uk, Bk, Uv, Bv, q, Hkv, d, r_lo, k, sc)
+        assert np.max(np.abs(res["out"] - full)) <= 1e-12
+    lo = _sdpa(q, Uk[:, :2] @ Bk[:2], Uv[:, :2] @ Bv[:2], Hkv, d, sc)
+    res = decode_ref(Uk, Bk, Uv, Bv, q, Hkv, d, 2, 0, sc)
+    assert np.max(np.abs(res["out"] - lo)) <= 1e-12
+
+
+# ------------------------------------------------------------------ P7
+@pytest.mark.parametrize("seed,N,r,r_lo,k,Hkv,Hq,d,T", [
+    (30, 7, 4, 2, 3, 2, 4, 3, 2),
+    (31, 8, 3, 1, 2, 1, 2, 4, 0),
+    (32, 5, 5, 5, 5, 1, 1, 2, 1),
+    (33, 6, 4, 1, 0, 2, 2, 2, 3),
+])
+def test_p7_brute_force(seed, N, r, r_lo, k, Hkv, Hq, d, T):
+    g = np.random.default_rng(seed)
+    W = Hkv * d
+    Uk, Bk, Uv, Bv = (g.standard_normal(s) for s in [(N, r), (r, W), (N, r), (r, W)])
+    Kt, Vt = g.standard_normal((T, W)), g.standard_normal((T, W))
+    q = g.standard_normal(Hq * d)
+    res = decode_ref(Uk, Bk, Uv, Bv, q, Hkv, d, r_lo, k, 0.7,
+                     Kt if T else None, Vt if T else None)
+    out, tops = decode_brute(Uk.tolist(), Bk.tolist(), Uv.tolist(), Bv.tolist(), q.tolist(),
+                             Hkv, d, r_lo, k, 0.7, Kt.tolist(), Vt.tolist())
+    assert np.max(np.abs(res["out"] - np.array(out))) <= 1e-12
+    assert [list(t) for t in res["top"]] == tops
+
+
+# ------------------------------------------------------------------ P8
+def _latent_decode(Uk, Bk, Uv, Bv, q, Hkv, d, r_lo, k, scale):
+    """Factor-space formulation: scores from U (B q), values accumulated on U_v rows."""
+    N, r = Uk.shape
+    Hq = q.shape[0] // d
+    G = Hq // Hkv
+    out = np.zeros(Hq * d)
+    for h in range(Hq):
+        g = h // G
+        cols = slice(g * d, (g + 1) * d)
+        qt = Bk[:, cols] @ q[h * d:(h + 1) * d]          # latent query, r
+        s_lo = scale * (Uk[:, :r_lo] @ qt[:r_lo])
+        sel = np.zeros(N, bool)
+        sel[select_top(s_lo, k)] = True
+        s = s_lo + sel * scale * (Uk[:, r_lo:] @ qt[r_lo:])
+        p = np.exp(s - s.max()); p /= p.sum()
+        z = np.zeros(r)
+        z[:r_lo] = p @ Uv[:, :r_lo]
+        z[r_lo:] = (p * sel) @ Uv[:, r_lo:]
+        out[h * d:(h + 1) * d] = z @ Bv[:, cols]
+    return out
+
+
+def test_p8_latent_formulation_matches_explicit():
+    w = wl.TINY
+    inp = wl.gen_decode_inputs(w, 0)
+    args = [inp[k].astype(np.float64) for k in ("U_k", "B_k", "U_v", "B_v", "q")]
+    res = decode_ref(*args, w.n_kv_heads, w.head_dim, w.r_lo, w.top_k, w.scale)
+    lat = _latent_decode(*args, w.n_kv_heads, w.head_dim, w.r_lo, w.top_k, w.scale)
+    assert np.max(np.abs(res["out"] - lat)) <= 1e-12 * max(1.0, np.max(np.abs(lat)))
+
+
+# ------------------------------------------------------------------ P9
+def test_p9_permutation_equivariance():
+    N, r, Hkv, Hq, d = 40, 8, 2, 4, 8
+    g = np.random.default_rng(40)
+    Uk, Bk, Uv, Bv = (g.standard_normal(s) for s in [(N, r), (r, Hkv * d), (N, r), (r, Hkv * d)])
+    q = g.standard_normal(Hq * d)
+    perm = g.permutation(N)
+    a = decode_ref(Uk, Bk, Uv, Bv, q, Hkv, d, 2, 10, 0.3)
+    b = decode_ref(Uk[perm], Bk, Uv[perm], Bv, q, Hkv, d, 2, 10, 0.3)
+    assert np.max(np.abs(a["out"] - b["out"])) <= 1e-12
+    for h in range(Hq):
+        assert sorted(perm[b["top"][h]].tolist()) == a["top"][h].tolist()
+
+
+def test_p9_gqa_equals_mha_with_duplicated_kv_heads():
+    N, r, Hkv, Hq, d = 24, 6, 2, 8, 4
+    G = Hq // Hkv
+    g = np.random.default_rng(41)
+    Uk, Bk, Uv, Bv = (g.standard_normal(s) for s in [(N, r), (r, Hkv * d), (N, r), (r, Hkv * d)])
+    Kt, Vt = g.standard_normal((3, Hkv * d)), g.standard_normal((3, Hkv * d))
+    q = g.standard_normal(Hq * d)
+    dup = np.concatenate([np.arange(h // G * d, (h // G + 1) * d) for h in range(Hq)])
+    a = decode_ref(Uk, Bk, Uv, Bv, q, Hkv, d, 2, 6, 0.5, Kt, Vt)
+    b = decode_ref(Uk, Bk[:, dup], Uv, Bv[:, dup], q, Hq, d, 2, 6, 0.5, Kt[:, dup], Vt[:, dup])
+    assert np.max(np.abs(a["out"] - b["out"])) <= 1e-14
+    assert np.array_equal(a["top"], b["top"])
+
+
+# ------------------------------------------------------------------ P10
+def test_p10_single_token():
+    g = np.random.default_rng(50)
+    Uk, Bk, Uv, Bv = (g.standard_normal(s) for s in [(1, 4), (4, 6), (1, 4), (4, 6)])
+    q = g.standard_normal(6)
+    for k, rr in [(1, 4), (0, 2)]:
+        res = decode_ref(Uk, Bk, Uv, Bv, q, 1, 6, 2, k, 1.0)
+        assert np.allclose(res["out"], Uv[0, :rr] @ Bv[:rr], rtol=0, atol=1e-14)
+
+
+def test_p10_zero_query_uniform_and_lowest_index_ties():
+    g = np.random.default_rng(51)
+    N, r, d = 12, 4, 3
+    Uk, Bk, Uv, Bv = (g.standard_normal(s) for s in [(N, r), (r, d), (N, r), (r, d)])
+    res = decode_ref(Uk, Bk, Uv, Bv, np.zeros(d), 1, d, 1, 5, 1.0)
+    assert res["top"][0].tolist() == [0, 1, 2, 3, 4]
+    Vsel = Uv[:, :1] @ Bv[:1]
+    Vsel[:5] = Uv[:5] @ Bv
+    assert np.allclose(res["out"], Vsel.mean(axis=0), atol=1e-14)
+
+
+def test_select_top_ties_and_bounds():
+    s = np.array([1.0, 3.0, 3.0, 2.0, 3.0, -1.0])
+    assert select_top(s, 2).tolist() == [1, 2]
+    assert select_top(s, 4).tolist() == [1, 2, 3, 4]
+    assert select_top(s, 0).tolist() == []
+    assert select_top(s, 6).tolist() == [0, 1, 2, 3, 4, 5]
+
+
+# ------------------------------------------------------------------ P11
+def test_p11_storage_accounting_matches_pages():
+    gold = json.load(open(os.path.join(GOLDEN, "pages_numbers.json")))
+    m = gold["assumed_model"]
+    per_token = 2 * m["layers"] * m["hidden"] * m["bytes_per_value"]    # K and V, all layers
+    full = gold["llava15_7b_cache_mb_full"]["value"] * 1e6
+    n_vis = m["visual_tokens_per_image"]
+    n_text = full / per_token - n_vis                    # text tokens implied by 328 MB
+    R = gold["best_rank"]["value"]
+    comp = (2 * m["layers"] * accounting.factored_bytes(n_vis, R, m["hidden"], m["bytes_per_value"])
+            + n_text * per_token)
+    assert abs(comp / 1e6 - gold["llava15_7b_cache_mb_compressed"]["value"]) <= 0.01 * 64.5
+    one = accounting.dense_bytes(n_vis, m["hidden"], 2) / accounting.factored_bytes(n_vis, R, m["hidden"], 2)
+    assert 7.5 <= one <= gold["max_reduction_factor"]["value"]
+    frac = accounting.decompression_flop_fraction(gold["fraction_full_rank"]["value"], R // 4, R)
+    assert abs(frac - 0.4375) < 1e-15       # 56.25% cut, not the printed 67.5% (unpinned)
+
+
+def test_round_to_storage_bf16_known_values():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -7, -3.14159265, 1e-40])
+    y = round_to_storage(x, "bf16")
+    # ties to even: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> 1
+    assert y[0] == 1.0 and y[1] == 1.0 and y[2] == 1.0 + 2 ** -6 and y[3] == 1.0 + 2 ** -7
+    assert y[4] == -3.140625
+    # agrees with torch's bfloat16 conversion (a library routine)
+    t = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(y, t)
+    assert np.array_equal(wl.round_bf16(x).astype(np.float64), t)
