@@ -1,0 +1,178 @@
+/*
+ * ap.h — C ABI of the compressed-KV decode-attention library (libap.so, gfx950).
+ *
+ * The method is AttentionPack as summarised on the gist.science pages (es, fr, de)
+ * for "Attention-aware Inference Optimizations for Large Vision-Language Models with
+ * Memory-efficient Decoding"; sections are cited as [fr §2.A] etc.
+ *
+ * Conventions for every entry point:
+ *   - Plain C types only.  Device buffers are passed as device pointers, the HIP
+ *     stream as `void*` (a hipStream_t; NULL = the null stream).
+ *   - Every call validates all of its arguments before it enqueues anything.  On a
+ *     validation error nothing is enqueued, nothing is allocated and output
+ *     handles are set to NULL.  ap_last_error() gives a message for the failure.
+ *   - Work is enqueued asynchronously on `stream`; a kernel fault surfaces at the
+ *     caller's next synchronisation, as with any stream API.  Inputs must stay
+ *     valid, and outputs untouched, until the stream has passed the call.
+ *   - A cache handle is used by one stream at a time; calls on one handle from
+ *     several streams at once race.  Different handles are independent.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef RANK_COMPRESSED_KV_AP_H
+#define RANK_COMPRESSED_KV_AP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AP_OK = 0,
+  AP_ERR_NULL_ARG = 1,       /* a required pointer was NULL                          */
+  AP_ERR_BAD_SHAPE = 2,      /* sizes out of range or inconsistent                   */
+  AP_ERR_BAD_DTYPE = 3,      /* storage dtype not one of ap_dtype                    */
+  AP_ERR_UNSUPPORTED = 4,    /* valid by the method, outside what this build handles */
+  AP_ERR_OUT_OF_MEMORY = 5,  /* a device allocation failed                           */
+  AP_ERR_HIP = 6             /* a HIP runtime call failed                            */
+} ap_status;
+
+typedef enum { AP_F32 = 0, AP_BF16 = 1 } ap_dtype;
+
+/* Shape of one attention layer's visual cache and how it is factored.
+ *
+ * [fr §2.A "Approche", de §2.A "Optimierung"]: the keys of all KV heads are
+ * concatenated along the hidden axis, so one sequence's visual keys form one
+ * N x W matrix, W = n_kv_heads * head_dim, columns head-major (head g owns
+ * columns g*d .. g*d+d-1).  The same holds for the values.
+ * [fr §2.A "Mécanisme"/"Gain"]: each matrix is stored as a compressed matrix
+ * U (N x rank) and a decompression matrix B (rank x W).
+ */
+typedef struct {
+  int32_t batch;        /* B >= 0 sequences (0: an empty cache, every call is a no-op)  */
+  int32_t n_tokens;     /* N, 1 <= N <= 32768 visual tokens per sequence                */
+  int32_t n_kv_heads;   /* Hkv >= 1                                                      */
+  int32_t n_q_heads;    /* Hq, a multiple of Hkv, Hq <= 64 (decode workspace is sized here) */
+  int32_t head_dim;     /* d, 1 <= d <= 256                                              */
+  int32_t rank;         /* r, 1 <= r <= min(128, N, W)                                   */
+  int32_t oversample;   /* p >= 0; the range finder keeps ell = min(r + p, N, W) columns */
+  int32_t power_iters;  /* q, 0 <= q <= 8 power iterations                               */
+  int32_t storage;      /* ap_dtype of K, V in and of U, B stored                        */
+  int32_t reserved;     /* must be 0                                                     */
+  uint64_t seed;        /* seed of the device-generated test matrix (omega == NULL)      */
+  const float* omega;   /* optional device [B][2][W][ell] float32 test matrices
+                           (index 0: for K, 1: for V), row-major, caller-owned and read
+                           during ap_compress only; NULL: drawn on the device from seed. */
+} ap_compress_params;
+
+/* Opaque handle: the factored cache of a batch plus its decode workspace.  All of
+ * its device memory is owned by the library and released by ap_free. */
+typedef struct ap_cache ap_cache;
+
+/* Factor each sequence's heads-merged visual K and V to rank r.
+ *
+ * Defines: [fr §2.A], [es §2.A], [de §2.A] — K ~= K* D_k and V ~= V* D_v by a
+ * singular value decomposition of the heads-merged matrix, K and V separately, no
+ * token removed.  This library computes it by randomized subspace iteration (Halko,
+ * Martinsson & Tropp 2011): ell = min(r+p, N, W) probe columns, q power iterations,
+ * then a one-sided Jacobi SVD of the ell x ell core; U = Q V_r diag(sigma_r) carries
+ * the singular values, B has orthonormal rows, components in decreasing order.
+ *
+ * k, v:   device [B][N][W] row-major in p->storage dtype, caller-owned, read on
+ *         `stream` during the call.  k == v == NULL allocates the cache without
+ *         computing factors (load them with ap_cache_set_factors).  Exactly one of
+ *         them NULL is AP_ERR_NULL_ARG.
+ * p:      host struct, read during the call only.
+ * out:    receives the new handle (NULL on any error).  The call allocates device
+ *         memory synchronously, then enqueues the factorisation on `stream`.
+ * Errors: AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_BAD_DTYPE, AP_ERR_UNSUPPORTED,
+ *         AP_ERR_OUT_OF_MEMORY, AP_ERR_HIP.
+ */
+ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p,
+                      void* stream, ap_cache** out);
+
+/* Load factors into a cache: U_k, U_v device [B][N][r], B_k, B_v device [B][r][W],
+ * row-major, in the cache's storage dtype, caller-owned, read on `stream`.  The
+ * layout is the plain one of [fr §2.A "Mécanisme"] (K ~= U_k B_k); the cache keeps
+ * its own tiled copy.  Errors: AP_ERR_NULL_ARG, AP_ERR_HIP. */
+ap_status ap_cache_set_factors(ap_cache* c, const void* U_k, const void* B_k,
+                               const void* U_v, const void* B_v, void* stream);
+
+/* Copy the factors out in the same plain layout as ap_cache_set_factors (any of the
+ * four pointers may be NULL to skip it).  sigma_k / sigma_v variants: see below. */
+ap_status ap_cache_get_factors(const ap_cache* c, void* U_k, void* B_k, void* U_v,
+                               void* B_v, void* stream);
+
+/* Copy the r leading singular values found by ap_compress for each sequence,
+ * device [B][r] float32 each (NULL to skip).  Zeros if the factors were loaded. */
+ap_status ap_cache_get_sigma(const ap_cache* c, float* sigma_k, float* sigma_v, void* stream);
+
+/* Shape of a cache and the device bytes it holds (factors + decode workspace). */
+ap_status ap_cache_info(const ap_cache* c, ap_compress_params* p_out, size_t* factor_bytes,
+                        size_t* device_bytes);
+
+/* Per-step decode parameters.
+ * [fr §2.B "Stratégie"]: the most important tokens are decompressed at the full rank
+ * R_kv, the others at a reduced rank (R_kv/4 is the page's example).  [es §4 "Análisis
+ * de Sensibilidad"]: 25% of the tokens at full rank.  Importance here is the
+ * current-step low-rank logit of each token for each query head (see ap_decode_attn). */
+typedef struct {
+  int32_t r_lo;          /* reduced rank, 1 <= r_lo <= r                                  */
+  int32_t top_k;         /* tokens at full rank per (sequence, query head), 0 <= k <= N   */
+  float scale;           /* softmax scale, finite and > 0 (usually 1/sqrt(d))              */
+  int32_t n_text;        /* T >= 0 dense text tokens joining the softmax                  */
+  const void* text_k;    /* device [B][T][W] storage dtype, NULL iff T == 0               */
+  const void* text_v;    /* device [B][T][W] storage dtype, NULL iff T == 0               */
+  int32_t* sel_out;      /* optional device [B][Hq][top_k] int32: the selected token ids,
+                            ascending per (sequence, head); NULL to skip                  */
+  int32_t splits;        /* 0: library's choice; else the number of N-splits per sequence
+                            (clamped to the workspace sized at ap_compress)                */
+} ap_decode_params;
+
+/* One decode step of attention over the compressed cache, for every sequence.
+ *
+ * Defines: [es §2.B], [fr §2.B], [de §2.B] — per token and step, important tokens are
+ * decompressed at full rank and the rest at reduced rank; attention follows.  For
+ * sequence b and query head h (KV head g = h / (Hq/Hkv)), with q~ = B_k[:, g-th
+ * head's columns] q_h:
+ *   s_lo[n] = scale * U_k[n, :r_lo] . q~[:r_lo]                     (all n)
+ *   Top_h   = the top_k tokens of largest s_lo (ties: lower index)
+ *   s[n]    = s_lo[n] + [n in Top_h] * scale * U_k[n, r_lo:] . q~[r_lo:]
+ *   p       = softmax over the N visual scores and the T text scores
+ *             scale * K_text[t, g-th head's columns] . q_h
+ *   out_h   = (sum_n p[n] U_v[n, :r(n)]) B_v[:r(n), g-th head's columns]
+ *             + sum_t p[t] V_text[t, g-th head's columns],   r(n) = r if n in Top_h else r_lo
+ * which equals explicit decompression K^[n] = U_k[n, :r(n)] B_k[:r(n)] followed by
+ * dense attention, without forming K^ or V^.
+ *
+ * q:    device [B][Hq*d] float32, caller-owned.
+ * out:  device [B][Hq*d] float32, caller-owned, fully overwritten.
+ * The call allocates nothing; it enqueues three kernels on `stream`.
+ * Errors: AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_UNSUPPORTED (r_lo or r not
+ * supported by the tiling), AP_ERR_HIP.
+ */
+ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decode_params* p,
+                         void* stream);
+
+/* Release a cache (NULL is a no-op).  Waits for the last stream used with the cache,
+ * then frees all of its device memory. */
+void ap_free(ap_cache* c);
+
+/* Kernel timing for measurement.  While enabled, ap_decode_attn records HIP events
+ * around each of its kernels on the caller's stream (at most max_calls calls are
+ * recorded; later calls are not timed).  ap_timing_read waits for the recorded events,
+ * writes the summed milliseconds per kernel (index: 0 select, 1 attention, 2 combine)
+ * and the number of timed calls, and starts a new recording.  max_calls == 0 disables. */
+enum { AP_KERNEL_SELECT = 0, AP_KERNEL_ATTN = 1, AP_KERNEL_COMBINE = 2, AP_N_KERNELS = 3 };
+ap_status ap_timing_enable(ap_cache* c, int32_t max_calls);
+ap_status ap_timing_read(ap_cache* c, float* ms_per_kernel /* [AP_N_KERNELS] */, int32_t* calls);
+
+/* Text for a status code, and the detail of the calling thread's last failure. */
+const char* ap_status_string(ap_status s);
+const char* ap_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RANK_COMPRESSED_KV_AP_H */

@@ -1,0 +1,216 @@
+"""Python binding of libap.so: argument marshalling only.
+
+Every call passes torch device tensors' data pointers and the current HIP
+stream straight to the C ABI declared in include/ap.h; all arithmetic runs in
+the library's kernels.  Importing this module fails loudly if the library has
+not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libap.so")
+
+AP_OK, AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_BAD_DTYPE, AP_ERR_UNSUPPORTED, \
+    AP_ERR_OUT_OF_MEMORY, AP_ERR_HIP = range(7)
+AP_F32, AP_BF16 = 0, 1
+KERNEL_NAMES = ("select", "attn", "combine")
+
+EXPORTED = (
+    "ap_compress", "ap_cache_set_factors", "ap_cache_get_factors", "ap_cache_get_sigma",
+    "ap_cache_info", "ap_decode_attn", "ap_free", "ap_timing_enable", "ap_timing_read",
+    "ap_status_string", "ap_last_error",
+)
+
+
+class CompressParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_tokens", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("rank", ctypes.c_int32),
+        ("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32), ("storage", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64), ("omega", ctypes.c_void_p),
+    ]
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("r_lo", ctypes.c_int32), ("top_k", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("n_text", ctypes.c_int32), ("text_k", ctypes.c_void_p), ("text_v", ctypes.c_void_p),
+        ("sel_out", ctypes.c_void_p), ("splits", ctypes.c_int32),
+    ]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m rank_compressed_kv_ap_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.ap_compress.argtypes = [vp, vp, ctypes.POINTER(CompressParams), vp, ctypes.POINTER(vp)]
+    lib.ap_cache_set_factors.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.ap_cache_get_factors.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.ap_cache_get_sigma.argtypes = [vp, vp, vp, vp]
+    lib.ap_cache_info.argtypes = [vp, ctypes.POINTER(CompressParams), ctypes.POINTER(ctypes.c_size_t),
+                                  ctypes.POINTER(ctypes.c_size_t)]
+    lib.ap_decode_attn.argtypes = [vp, vp, vp, ctypes.POINTER(DecodeParams), vp]
+    lib.ap_free.argtypes = [vp]
+    lib.ap_free.restype = None
+    lib.ap_timing_enable.argtypes = [vp, i32]
+    lib.ap_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.ap_status_string.argtypes = [i32]
+    lib.ap_status_string.restype = ctypes.c_char_p
+    lib.ap_last_error.argtypes = []
+    lib.ap_last_error.restype = ctypes.c_char_p
+    for name in ("ap_compress", "ap_cache_set_factors", "ap_cache_get_factors", "ap_cache_get_sigma",
+                 "ap_cache_info", "ap_decode_attn", "ap_timing_enable", "ap_timing_read"):
+        getattr(lib, name).restype = i32
+    return lib
+
+
+lib = load_library()
+
+
+class APError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.ap_status_string(status).decode()
+        detail = lib.ap_last_error().decode()
+        super().__init__(f"{where}: {msg} ({detail})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != AP_OK:
+        raise APError(status, where)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def storage_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return AP_F32
+    if dtype == torch.bfloat16:
+        return AP_BF16
+    raise ValueError(f"unsupported storage dtype {dtype}")
+
+
+def torch_dtype(storage: int) -> torch.dtype:
+    return torch.bfloat16 if storage == AP_BF16 else torch.float32
+
+
+class Cache:
+    """A factored visual cache (owned by the library) for a batch of sequences."""
+
+    def __init__(self, handle: int, params: CompressParams):
+        self._h = ctypes.c_void_p(handle)
+        self.params = params
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if not self._h:
+            raise RuntimeError("cache already freed")
+        return self._h
+
+    @property
+    def batch(self): return self.params.batch
+    @property
+    def n_tokens(self): return self.params.n_tokens
+    @property
+    def rank(self): return self.params.rank
+    @property
+    def width(self): return self.params.n_kv_heads * self.params.head_dim
+    @property
+    def dtype(self): return torch_dtype(self.params.storage)
+
+    def set_factors(self, U_k, B_k, U_v, B_v) -> None:
+        _check(lib.ap_cache_set_factors(self.handle, _ptr(U_k), _ptr(B_k), _ptr(U_v), _ptr(B_v),
+                                        _stream()), "ap_cache_set_factors")
+
+    def get_factors(self):
+        p = self.params
+        dev = torch.device("cuda")
+        U_k = torch.empty(p.batch, p.n_tokens, p.rank, dtype=self.dtype, device=dev)
+        U_v = torch.empty_like(U_k)
+        B_k = torch.empty(p.batch, p.rank, self.width, dtype=self.dtype, device=dev)
+        B_v = torch.empty_like(B_k)
+        _check(lib.ap_cache_get_factors(self.handle, _ptr(U_k), _ptr(B_k), _ptr(U_v), _ptr(B_v),
+                                        _stream()), "ap_cache_get_factors")
+        return U_k, B_k, U_v, B_v
+
+    def get_sigma(self):
+        p = self.params
+        sk = torch.empty(p.batch, p.rank, dtype=torch.float32, device="cuda")
+        sv = torch.empty_like(sk)
+        _check(lib.ap_cache_get_sigma(self.handle, _ptr(sk), _ptr(sv), _stream()), "ap_cache_get_sigma")
+        return sk, sv
+
+    def info(self):
+        p = CompressParams()
+        fb, db = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(lib.ap_cache_info(self.handle, ctypes.byref(p), ctypes.byref(fb), ctypes.byref(db)),
+               "ap_cache_info")
+        return p, fb.value, db.value
+
+    def timing_enable(self, max_calls: int) -> None:
+        _check(lib.ap_timing_enable(self.handle, max_calls), "ap_timing_enable")
+
+    def timing_read(self):
+        ms = (ctypes.c_float * 3)()
+        calls = ctypes.c_int32()
+        _check(lib.ap_timing_read(self.handle, ms, ctypes.byref(calls)), "ap_timing_read")
+        return dict(zip(KERNEL_NAMES, list(ms))), calls.value
+
+    def free(self) -> None:
+        if self._h:
+            lib.ap_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def compress(k: Optional[torch.Tensor], v: Optional[torch.Tensor], *, batch: int, n_tokens: int,
+             n_kv_heads: int, n_q_heads: int, head_dim: int, rank: int, storage: torch.dtype,
+             oversample: int = 16, power_iters: int = 2, seed: int = 0,
+             omega: Optional[torch.Tensor] = None) -> Cache:
+    """ap_compress: factor k, v [B, N, W] (or allocate only when both are None)."""
+    p = CompressParams(batch, n_tokens, n_kv_heads, n_q_heads, head_dim, rank, oversample,
+                       power_iters, storage_code(storage), 0, seed, _ptr(omega))
+    out = ctypes.c_void_p()
+    _check(lib.ap_compress(_ptr(k), _ptr(v), ctypes.byref(p), _stream(), ctypes.byref(out)),
+           "ap_compress")
+    p.omega = None
+    return Cache(out.value, p)
+
+
+def decode(cache: Cache, q: torch.Tensor, *, r_lo: int, top_k: int, scale: float,
+           text_k: Optional[torch.Tensor] = None, text_v: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, sel_out: Optional[torch.Tensor] = None,
+           splits: int = 0) -> torch.Tensor:
+    """ap_decode_attn: q [B, Hq*d] float32 -> out [B, Hq*d] float32."""
+    if out is None:
+        out = torch.empty_like(q)
+    n_text = 0 if text_k is None else text_k.shape[1]
+    p = DecodeParams(r_lo, top_k, scale, n_text, _ptr(text_k) if n_text else None,
+                     _ptr(text_v) if n_text else None, _ptr(sel_out), splits)
+    _check(lib.ap_decode_attn(cache.handle, _ptr(q), _ptr(out), ctypes.byref(p), _stream()),
+           "ap_decode_attn")
+    return out

@@ -1,0 +1,85 @@
+// Host-side internals shared by the API implementation and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/ap.h"
+
+namespace ap {
+
+constexpr int kBlockTokHost = 32;                  // tokens per tiled block
+constexpr float kLog2eHost = 1.4426950408889634f;  // scores are kept in log2 units
+
+// Derived sizes of one cache.
+struct Dims {
+  int B, N, Hkv, Hq, d, W, r, ell, p, q;
+  int storage;          // ap_dtype
+  int esize;            // bytes per stored element
+  int NP;               // panels of 16 columns: r_pad = 16 * NP
+  int r_pad;
+  int N_pad;            // tokens rounded up to a 32-token block
+  int nblk;             // N_pad / 32
+  int HT;               // query-head tiles of 16: Hq_pad = 16 * HT
+  int Hq_pad;
+  int G;                // Hq / Hkv
+  int S_cap;            // most N-splits the decode workspace holds
+};
+
+struct TimingState {
+  int max_calls = 0;
+  int calls = 0;
+  std::vector<hipEvent_t> ev;  // [max_calls][AP_N_KERNELS][2]
+};
+
+}  // namespace ap
+
+struct ap_cache {
+  ap::Dims dm;
+  ap_compress_params params;
+  // factors
+  void* Uk = nullptr;   // tiled K-layout  [B][NP][nblk][512]
+  void* Uv = nullptr;   // tiled V-layout  [B][NP][nblk][512]
+  void* Bk = nullptr;   // [B][r_pad][W] row-major (rows r..r_pad-1 zero)
+  void* Bv = nullptr;
+  float* sigma_k = nullptr;  // [B][r]
+  float* sigma_v = nullptr;
+  // decode workspace
+  float* qt = nullptr;        // [B][Hq_pad][r_pad] latent queries
+  uint32_t* mask = nullptr;   // [B][nblk][Hq_pad] selection bits per 32-token block
+  float* part_z = nullptr;    // [B][S_cap][Hq_pad][r_pad]
+  float* part_ml = nullptr;   // [B][S_cap][Hq_pad][2]  (running max in log2 units, sum)
+  size_t factor_bytes = 0;
+  size_t device_bytes = 0;
+  hipStream_t last_stream = nullptr;
+  ap::TimingState timing;
+};
+
+namespace ap {
+
+void set_error(const std::string& msg);
+
+// ---- launchers (decode_kernels.hip)
+hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
+                         int32_t* sel_out, hipStream_t st);
+hipError_t launch_attn(const ap_cache* c, int r_lo, float scale_log2e, int S, int CB,
+                       hipStream_t st);
+hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float scale_log2e,
+                          int S, int T, const void* text_k, const void* text_v, hipStream_t st);
+int select_heads_per_group(const Dims& dm);
+size_t select_lds_bytes(const Dims& dm, int Hg);
+
+// ---- launchers (pack_kernels.hip)
+hipError_t launch_pack_u(const ap_cache* c, const void* src, void* dst, bool v_layout,
+                         hipStream_t st);
+hipError_t launch_unpack_u(const ap_cache* c, const void* src, void* dst, bool v_layout,
+                           hipStream_t st);
+
+// ---- launchers (compress_kernels.hip)
+hipError_t run_compress(ap_cache* c, const void* k, const void* v, hipStream_t st);
+
+}  // namespace ap

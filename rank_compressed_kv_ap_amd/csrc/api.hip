@@ -1,0 +1,337 @@
+// C ABI of the compressed-KV decode-attention library: argument validation,
+// ownership of device memory, and the stream-ordered launch sequence.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "ap_internal.h"
+
+namespace ap {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+static ap_status fail(ap_status s, const std::string& msg) {
+  set_error(msg);
+  return s;
+}
+
+static ap_status hip_fail(hipError_t e, const char* what) {
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return AP_ERR_HIP;
+}
+
+static int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+static ap_status validate_shape(const ap_compress_params* p) {
+  if (p->storage != AP_F32 && p->storage != AP_BF16) return fail(AP_ERR_BAD_DTYPE, "storage must be AP_F32 or AP_BF16");
+  if (p->reserved != 0) return fail(AP_ERR_BAD_SHAPE, "reserved must be 0");
+  if (p->batch < 0) return fail(AP_ERR_BAD_SHAPE, "batch < 0");
+  if (p->n_tokens < 1) return fail(AP_ERR_BAD_SHAPE, "n_tokens < 1");
+  if (p->n_kv_heads < 1 || p->n_q_heads < 1) return fail(AP_ERR_BAD_SHAPE, "head counts must be >= 1");
+  if (p->n_q_heads % p->n_kv_heads != 0) return fail(AP_ERR_BAD_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (p->head_dim < 1) return fail(AP_ERR_BAD_SHAPE, "head_dim < 1");
+  const long long W = (long long)p->n_kv_heads * p->head_dim;
+  if (p->rank < 1 || p->rank > p->n_tokens || p->rank > W) return fail(AP_ERR_BAD_SHAPE, "need 1 <= rank <= min(n_tokens, n_kv_heads*head_dim)");
+  if (p->oversample < 0) return fail(AP_ERR_BAD_SHAPE, "oversample < 0");
+  if (p->power_iters < 0) return fail(AP_ERR_BAD_SHAPE, "power_iters < 0");
+  // limits of this build's tiling
+  if (p->n_tokens > 32768) return fail(AP_ERR_UNSUPPORTED, "n_tokens > 32768");
+  if (p->head_dim > 256) return fail(AP_ERR_UNSUPPORTED, "head_dim > 256");
+  if (p->n_q_heads > 64) return fail(AP_ERR_UNSUPPORTED, "n_q_heads > 64");
+  if (p->rank > 128) return fail(AP_ERR_UNSUPPORTED, "rank > 128");
+  if (p->power_iters > 8) return fail(AP_ERR_UNSUPPORTED, "power_iters > 8");
+  if (W > (1 << 20)) return fail(AP_ERR_UNSUPPORTED, "n_kv_heads*head_dim > 2^20");
+  const int NP = ceil_div(p->rank, 16);
+  const int hq_pad = p->n_q_heads <= 16 ? 16 : (p->n_q_heads <= 32 ? 32 : 64);
+  if (NP * (hq_pad / 16) > 16) return fail(AP_ERR_UNSUPPORTED, "rank x query heads too large for one tile set (need ceil(r/16)*ceil(Hq/16) <= 16)");
+  return AP_OK;
+}
+
+static Dims make_dims(const ap_compress_params* p) {
+  Dims d{};
+  d.B = p->batch;
+  d.N = p->n_tokens;
+  d.Hkv = p->n_kv_heads;
+  d.Hq = p->n_q_heads;
+  d.d = p->head_dim;
+  d.W = d.Hkv * d.d;
+  d.r = p->rank;
+  d.p = p->oversample;
+  d.q = p->power_iters;
+  d.ell = std::min(std::min(d.r + d.p, d.N), d.W);
+  d.storage = p->storage;
+  d.esize = p->storage == AP_BF16 ? 2 : 4;
+  d.NP = ceil_div(d.r, 16);
+  d.r_pad = 16 * d.NP;
+  d.N_pad = ceil_div(d.N, kBlockTokHost) * kBlockTokHost;
+  d.nblk = d.N_pad / kBlockTokHost;
+  d.Hq_pad = d.Hq <= 16 ? 16 : (d.Hq <= 32 ? 32 : 64);
+  d.HT = d.Hq_pad / 16;
+  d.G = d.Hq / d.Hkv;
+  const int want = d.B > 0 ? ceil_div(4096, d.B) : 1;
+  d.S_cap = std::min(d.nblk, std::max(16, want));
+  return d;
+}
+
+static void free_all(ap_cache* c) {
+  void* ptrs[] = {c->Uk, c->Uv, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->qt, c->mask, c->part_z, c->part_ml};
+  for (void* q : ptrs)
+    if (q) (void)hipFree(q);
+  for (hipEvent_t e : c->timing.ev) (void)hipEventDestroy(e);
+  c->timing.ev.clear();
+}
+
+static ap_status alloc_cache(ap_cache* c) {
+  const Dims& dm = c->dm;
+  struct Req { void** ptr; size_t bytes; };
+  const size_t uel = (size_t)dm.B * dm.NP * dm.nblk * 512;
+  Req reqs[] = {
+      {&c->Uk, uel * dm.esize},
+      {&c->Uv, uel * dm.esize},
+      {&c->Bk, (size_t)dm.B * dm.r_pad * dm.W * dm.esize},
+      {&c->Bv, (size_t)dm.B * dm.r_pad * dm.W * dm.esize},
+      {reinterpret_cast<void**>(&c->sigma_k), (size_t)dm.B * dm.r * 4},
+      {reinterpret_cast<void**>(&c->sigma_v), (size_t)dm.B * dm.r * 4},
+      {reinterpret_cast<void**>(&c->qt), (size_t)dm.B * dm.Hq_pad * dm.r_pad * 4},
+      {reinterpret_cast<void**>(&c->mask), (size_t)dm.B * dm.nblk * dm.Hq_pad * 4},
+      {reinterpret_cast<void**>(&c->part_z), (size_t)dm.B * dm.S_cap * dm.Hq_pad * dm.r_pad * 4},
+      {reinterpret_cast<void**>(&c->part_ml), (size_t)dm.B * dm.S_cap * dm.Hq_pad * 2 * 4},
+  };
+  size_t total = 0;
+  for (const Req& r : reqs) {
+    if (r.bytes == 0) continue;
+    hipError_t e = hipMalloc(r.ptr, r.bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      free_all(c);
+      return fail(AP_ERR_OUT_OF_MEMORY, std::string("hipMalloc failed: ") + hipGetErrorString(e));
+    }
+    total += r.bytes;
+  }
+  c->factor_bytes = 2 * uel * dm.esize + 2 * (size_t)dm.B * dm.r_pad * dm.W * dm.esize;
+  c->device_bytes = total;
+  // padded rows of B and the singular values start at zero
+  hipError_t e = hipSuccess;
+  if (dm.B > 0) {
+    e = hipMemset(c->Bk, 0, (size_t)dm.B * dm.r_pad * dm.W * dm.esize);
+    if (e == hipSuccess) e = hipMemset(c->Bv, 0, (size_t)dm.B * dm.r_pad * dm.W * dm.esize);
+    if (e == hipSuccess) e = hipMemset(c->sigma_k, 0, (size_t)dm.B * dm.r * 4);
+    if (e == hipSuccess) e = hipMemset(c->sigma_v, 0, (size_t)dm.B * dm.r * 4);
+  }
+  if (e != hipSuccess) {
+    free_all(c);
+    return hip_fail(e, "hipMemset");
+  }
+  return AP_OK;
+}
+
+}  // namespace ap
+
+using namespace ap;
+
+extern "C" {
+
+const char* ap_status_string(ap_status s) {
+  switch (s) {
+    case AP_OK: return "ok";
+    case AP_ERR_NULL_ARG: return "null argument";
+    case AP_ERR_BAD_SHAPE: return "bad shape";
+    case AP_ERR_BAD_DTYPE: return "bad dtype";
+    case AP_ERR_UNSUPPORTED: return "unsupported";
+    case AP_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case AP_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ap_last_error(void) { return g_last_error.c_str(); }
+
+ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p, void* stream,
+                      ap_cache** out) {
+  if (out) *out = nullptr;
+  if (!p || !out) return fail(AP_ERR_NULL_ARG, "params and out must not be NULL");
+  if ((k == nullptr) != (v == nullptr)) return fail(AP_ERR_NULL_ARG, "k and v must both be set or both be NULL");
+  ap_status s = validate_shape(p);
+  if (s != AP_OK) return s;
+  ap_cache* c = new (std::nothrow) ap_cache();
+  if (!c) return fail(AP_ERR_OUT_OF_MEMORY, "host allocation failed");
+  c->params = *p;
+  c->params.omega = nullptr;
+  c->dm = make_dims(p);
+  s = alloc_cache(c);
+  if (s != AP_OK) {
+    delete c;
+    return s;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  c->last_stream = st;
+  if (k != nullptr && c->dm.B > 0) {
+    c->params.omega = p->omega;
+    hipError_t e = run_compress(c, k, v, st);
+    c->params.omega = nullptr;
+    if (e != hipSuccess) {
+      std::string detail = g_last_error;
+      free_all(c);
+      delete c;
+      if (e == hipErrorOutOfMemory) return fail(AP_ERR_OUT_OF_MEMORY, "compress workspace: " + detail);
+      if (e == hipErrorNotSupported) return fail(AP_ERR_UNSUPPORTED, detail);
+      return hip_fail(e, "compress");
+    }
+  }
+  *out = c;
+  return AP_OK;
+}
+
+ap_status ap_cache_set_factors(ap_cache* c, const void* U_k, const void* B_k, const void* U_v,
+                               const void* B_v, void* stream) {
+  if (!c || !U_k || !B_k || !U_v || !B_v) return fail(AP_ERR_NULL_ARG, "cache and all factor pointers must be set");
+  const Dims& dm = c->dm;
+  if (dm.B == 0) return AP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  c->last_stream = st;
+  hipError_t e = launch_pack_u(c, U_k, c->Uk, false, st);
+  if (e == hipSuccess) e = launch_pack_u(c, U_v, c->Uv, true, st);
+  const size_t row = (size_t)dm.r * dm.W * dm.esize;
+  const size_t dpitch = (size_t)dm.r_pad * dm.W * dm.esize;
+  if (e == hipSuccess) e = hipMemcpy2DAsync(c->Bk, dpitch, B_k, row, row, dm.B, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess) e = hipMemcpy2DAsync(c->Bv, dpitch, B_v, row, row, dm.B, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "set_factors");
+  return AP_OK;
+}
+
+ap_status ap_cache_get_factors(const ap_cache* c, void* U_k, void* B_k, void* U_v, void* B_v, void* stream) {
+  if (!c) return fail(AP_ERR_NULL_ARG, "cache is NULL");
+  const Dims& dm = c->dm;
+  if (dm.B == 0) return AP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (U_k) e = launch_unpack_u(c, c->Uk, U_k, false, st);
+  if (e == hipSuccess && U_v) e = launch_unpack_u(c, c->Uv, U_v, true, st);
+  const size_t row = (size_t)dm.r * dm.W * dm.esize;
+  const size_t spitch = (size_t)dm.r_pad * dm.W * dm.esize;
+  if (e == hipSuccess && B_k) e = hipMemcpy2DAsync(B_k, row, c->Bk, spitch, row, dm.B, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && B_v) e = hipMemcpy2DAsync(B_v, row, c->Bv, spitch, row, dm.B, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "get_factors");
+  return AP_OK;
+}
+
+ap_status ap_cache_get_sigma(const ap_cache* c, float* sigma_k, float* sigma_v, void* stream) {
+  if (!c) return fail(AP_ERR_NULL_ARG, "cache is NULL");
+  const Dims& dm = c->dm;
+  if (dm.B == 0) return AP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t bytes = (size_t)dm.B * dm.r * 4;
+  hipError_t e = hipSuccess;
+  if (sigma_k) e = hipMemcpyAsync(sigma_k, c->sigma_k, bytes, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && sigma_v) e = hipMemcpyAsync(sigma_v, c->sigma_v, bytes, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "get_sigma");
+  return AP_OK;
+}
+
+ap_status ap_cache_info(const ap_cache* c, ap_compress_params* p_out, size_t* factor_bytes, size_t* device_bytes) {
+  if (!c) return fail(AP_ERR_NULL_ARG, "cache is NULL");
+  if (p_out) *p_out = c->params;
+  if (factor_bytes) *factor_bytes = c->factor_bytes;
+  if (device_bytes) *device_bytes = c->device_bytes;
+  return AP_OK;
+}
+
+ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decode_params* p, void* stream) {
+  if (!c || !p) return fail(AP_ERR_NULL_ARG, "cache and params must not be NULL");
+  const Dims& dm = c->dm;
+  if (p->r_lo < 1 || p->r_lo > dm.r) return fail(AP_ERR_BAD_SHAPE, "need 1 <= r_lo <= rank");
+  if (p->top_k < 0 || p->top_k > dm.N) return fail(AP_ERR_BAD_SHAPE, "need 0 <= top_k <= n_tokens");
+  if (!(std::isfinite(p->scale) && p->scale > 0.f)) return fail(AP_ERR_BAD_SHAPE, "scale must be finite and > 0");
+  if (p->n_text < 0) return fail(AP_ERR_BAD_SHAPE, "n_text < 0");
+  if (p->splits < 0) return fail(AP_ERR_BAD_SHAPE, "splits < 0");
+  if (dm.B == 0) return AP_OK;
+  if (!q || !out) return fail(AP_ERR_NULL_ARG, "q and out must not be NULL");
+  if (p->n_text > 0 && (!p->text_k || !p->text_v)) return fail(AP_ERR_NULL_ARG, "text_k/text_v must be set when n_text > 0");
+  if (p->n_text > (1 << 20)) return fail(AP_ERR_UNSUPPORTED, "n_text > 2^20");
+
+  // N-splits of the flash-decode kernel: about two workgroups per CU, >= 8 token blocks each
+  int S = p->splits;
+  if (S == 0) {
+    S = ceil_div(512, dm.B);
+    S = std::min(S, std::max(1, dm.nblk / 8));
+  }
+  S = std::max(1, std::min(S, dm.S_cap));
+  const int CB = ceil_div(dm.nblk, S);
+  S = ceil_div(dm.nblk, CB);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  c->last_stream = st;
+  const float sl2 = p->scale * kLog2eHost;
+  TimingState& tm = c->timing;
+  const bool timed = tm.max_calls > 0 && tm.calls < tm.max_calls;
+  auto mark = [&](int kernel, int edge) -> hipError_t {
+    if (!timed) return hipSuccess;
+    return hipEventRecord(tm.ev[((size_t)tm.calls * AP_N_KERNELS + kernel) * 2 + edge], st);
+  };
+  hipError_t e = mark(AP_KERNEL_SELECT, 0);
+  if (e == hipSuccess) e = launch_select(c, q, p->r_lo, p->top_k, p->sel_out, st);
+  if (e == hipSuccess) e = mark(AP_KERNEL_SELECT, 1);
+  if (e == hipSuccess) e = mark(AP_KERNEL_ATTN, 0);
+  if (e == hipSuccess) e = launch_attn(c, p->r_lo, sl2, S, CB, st);
+  if (e == hipSuccess) e = mark(AP_KERNEL_ATTN, 1);
+  if (e == hipSuccess) e = mark(AP_KERNEL_COMBINE, 0);
+  if (e == hipSuccess) e = launch_combine(c, q, out, sl2, S, p->n_text, p->text_k, p->text_v, st);
+  if (e == hipSuccess) e = mark(AP_KERNEL_COMBINE, 1);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (timed) tm.calls++;
+  return AP_OK;
+}
+
+void ap_free(ap_cache* c) {
+  if (!c) return;
+  (void)hipStreamSynchronize(c->last_stream);
+  free_all(c);
+  delete c;
+}
+
+ap_status ap_timing_enable(ap_cache* c, int32_t max_calls) {
+  if (!c) return fail(AP_ERR_NULL_ARG, "cache is NULL");
+  if (max_calls < 0) return fail(AP_ERR_BAD_SHAPE, "max_calls < 0");
+  TimingState& tm = c->timing;
+  for (hipEvent_t e : tm.ev) (void)hipEventDestroy(e);
+  tm.ev.clear();
+  tm.calls = 0;
+  tm.max_calls = 0;
+  const size_t n = (size_t)max_calls * AP_N_KERNELS * 2;
+  tm.ev.resize(n, nullptr);
+  for (size_t i = 0; i < n; ++i) {
+    hipError_t e = hipEventCreate(&tm.ev[i]);
+    if (e != hipSuccess) {
+      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(tm.ev[j]);
+      tm.ev.clear();
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  tm.max_calls = max_calls;
+  return AP_OK;
+}
+
+ap_status ap_timing_read(ap_cache* c, float* ms_per_kernel, int32_t* calls) {
+  if (!c || !ms_per_kernel) return fail(AP_ERR_NULL_ARG, "cache and ms_per_kernel must not be NULL");
+  TimingState& tm = c->timing;
+  for (int k = 0; k < AP_N_KERNELS; ++k) ms_per_kernel[k] = 0.f;
+  for (int i = 0; i < tm.calls; ++i)
+    for (int k = 0; k < AP_N_KERNELS; ++k) {
+      hipEvent_t a = tm.ev[((size_t)i * AP_N_KERNELS + k) * 2];
+      hipEvent_t b = tm.ev[((size_t)i * AP_N_KERNELS + k) * 2 + 1];
+      hipError_t e = hipEventSynchronize(b);
+      float ms = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+      if (e != hipSuccess) return hip_fail(e, "timing read");
+      ms_per_kernel[k] += ms;
+    }
+  if (calls) *calls = tm.calls;
+  tm.calls = 0;
+  return AP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, MFMA tiles,
+// wavefront reductions and the tiled layout of the compressed factors.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ap {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // raw bfloat16 payload
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // running-max start: finite so exp2 never sees inf - inf
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// float -> bfloat16, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <class T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t x) { return bf16_to_f32(x); }
+
+template <class T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+// Order-preserving map of a float score to an unsigned key (larger score -> larger key).
+// -0 is folded onto +0 so that equal scores give equal keys.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- MFMA tiles
+// 16x16 output tile D[i][j]: lane l holds D[4*(l/16) + t][l%16], t = 0..3.
+// bf16 16x16x16: lane l supplies A[l%16][4*(l/16) + e] and B[4*(l/16) + e][l%16], e = 0..3.
+__device__ __forceinline__ v4f mfma_bf16(v4s a, v4s b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// fp32 16x16x4: lane l supplies A[l%16][l/16] and B[l/16][l%16].
+__device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+// ---------------------------------------------------------------- factor tiling
+// A factor U (N x r) is stored per sequence as panels of 16 columns and blocks of
+// 32 tokens.  Block (panel p, token block t) holds 512 elements laid out
+// [lane 0..63][half 0..1][e 0..3]; lane l loads its 8 elements with one vector load.
+//   K-layout (score operand A, rows = tokens):
+//     token = 32t + 16*half + l%16,        column = 16p + 4*(l/16) + e
+//   V-layout (value operand A^T, rows = columns of U):
+//     token = 32t + 16*half + 4*(l/16) + e, column = 16p + l%16
+// Sequence b, panel p, block t starts at element ((b*NP + p)*nblk + t)*512.
+constexpr int kBlockTok = 32;
+constexpr int kBlockElems = 512;
+
+__host__ __device__ __forceinline__ size_t tile_base(int b, int p, int t, int NP, int nblk) {
+  return ((static_cast<size_t>(b) * NP + p) * nblk + t) * kBlockElems;
+}
+
+// Element index inside a block of (lane, half, e).
+__host__ __device__ __forceinline__ int tile_elem(int lane, int half, int e) {
+  return (lane * 2 + half) * 4 + e;
+}
+
+}  // namespace ap

@@ -1,0 +1,77 @@
+"""The C-ABI library loads, exports every symbol include/ap.h declares, and
+rejects invalid arguments before it touches the device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_symbols():
+    src = open(os.path.join(ROOT, "include", "ap.h")).read()
+    return sorted(set(re.findall(r"\b(ap_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    from rank_compressed_kv_ap_amd import binding
+    syms = _header_symbols()
+    assert "ap_compress" in syms and "ap_decode_attn" in syms and "ap_free" in syms
+    missing = [s for s in syms if not hasattr(binding.lib, s)]
+    assert not missing, missing
+    assert set(syms) == set(binding.EXPORTED)
+
+
+def test_struct_layouts_match_header():
+    from rank_compressed_kv_ap_amd import binding
+    assert ctypes.sizeof(binding.CompressParams) == 56
+    assert binding.CompressParams.seed.offset == 40 and binding.CompressParams.omega.offset == 48
+    assert ctypes.sizeof(binding.DecodeParams) == 48
+    assert binding.DecodeParams.text_k.offset == 16 and binding.DecodeParams.splits.offset == 40
+
+
+def _compress_status(**kw):
+    from rank_compressed_kv_ap_amd import binding as b
+    base = dict(batch=2, n_tokens=64, n_kv_heads=2, n_q_heads=4, head_dim=32, rank=16,
+                oversample=16, power_iters=2, storage=b.AP_BF16, reserved=0, seed=0, omega=None)
+    base.update(kw)
+    p = b.CompressParams(**base)
+    out = ctypes.c_void_p(1)
+    st = b.lib.ap_compress(None, None, ctypes.byref(p), None, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(storage=7), 3),
+    (dict(reserved=1), 2),
+    (dict(batch=-1), 2),
+    (dict(n_tokens=0), 2),
+    (dict(n_q_heads=3), 2),
+    (dict(rank=0), 2),
+    (dict(rank=65), 2),
+    (dict(head_dim=0), 2),
+    (dict(n_tokens=40000, rank=16), 4),
+    (dict(rank=144, n_tokens=256, head_dim=128), 4),
+    (dict(n_q_heads=128, n_kv_heads=2), 4),
+    (dict(power_iters=-1), 2),
+])
+def test_compress_validation_errors(kw, status):
+    st, out = _compress_status(**kw)
+    assert st == status
+    assert out is None
+
+
+def test_null_arguments():
+    from rank_compressed_kv_ap_amd import binding as b
+    out = ctypes.c_void_p(1)
+    assert b.lib.ap_compress(None, None, None, None, ctypes.byref(out)) == b.AP_ERR_NULL_ARG
+    p = b.CompressParams(2, 64, 2, 4, 32, 16, 16, 2, b.AP_BF16, 0, 0, None)
+    assert b.lib.ap_compress(ctypes.c_void_p(16), None, ctypes.byref(p), None,
+                             ctypes.byref(out)) == b.AP_ERR_NULL_ARG
+    assert out.value is None
+    dp = b.DecodeParams(4, 8, 0.1, 0, None, None, None, 0)
+    assert b.lib.ap_decode_attn(None, None, None, ctypes.byref(dp), None) == b.AP_ERR_NULL_ARG
+    b.lib.ap_free(None)
+    assert b.lib.ap_status_string(b.AP_ERR_UNSUPPORTED) == b"unsupported"
+    assert b"n_kv_heads" in b.lib.ap_last_error() or b.lib.ap_last_error() != b""

@@ -1,0 +1,127 @@
+"""GPU parity of ap_decode_attn against the CPU oracle (needs an MI355X).
+
+Inputs: seeded factored caches from rank_compressed_kv_ap_amd.workloads, the
+same storage-exact values on both sides.  Bar: top-k id sets equal except for
+tokens whose low-rank score is within 1e-3 (relative) of the cutoff; outputs
+within max-abs 2e-2 (bf16 storage) or 1e-4 (fp32 storage).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import check_against_oracle, make_inputs, run_decode, upload_decode
+from rank_compressed_kv_ap_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+# Small shapes that still span several tiles, with ragged token / rank / head tails.
+SMALL = {
+    "tiny_cfg": wl.TINY,
+    "bf16_ragged": wl.LLAVA.replace(cfg_id=101, batch=3, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                                    n_tokens=100, n_text=5, rank=24, r_lo=8, top_k=25, grid=None,
+                                    inner_dim=100),
+    "f32_gqa_straddle": wl.GQA.replace(cfg_id=102, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=32,
+                                       n_tokens=70, rank=40, r_lo=20, top_k=17, storage="f32",
+                                       inner_dim=64),
+    "bf16_48_heads": wl.LLAVA.replace(cfg_id=103, batch=2, n_q_heads=48, n_kv_heads=16, head_dim=16,
+                                      n_tokens=64, n_text=3, rank=32, r_lo=16, top_k=16, grid=None,
+                                      inner_dim=64),
+    "bf16_rank128": wl.VIDEO.replace(cfg_id=104, batch=2, n_tokens=300, top_k=75, frames=None,
+                                     inner_dim=300),
+    "bf16_straddle_text": wl.LLAVA.replace(cfg_id=105, batch=2, n_q_heads=8, n_kv_heads=8,
+                                           head_dim=64, n_tokens=200, n_text=70, rank=48, r_lo=20,
+                                           top_k=50, grid=None, inner_dim=200),
+    "f32_text_long": wl.TINY.replace(cfg_id=106, batch=2, n_text=300, n_tokens=90, top_k=22),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_parity_small(gpu_lib, name):
+    w = SMALL[name]
+    seqs = make_inputs(w)
+    out, sel = run_decode(w, seqs, gpu_lib)
+    err, flips = check_against_oracle(w, seqs, out, sel)
+    print(f"{name}: max abs err {err:.3e}, band flips {flips}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+def test_decode_split_count_does_not_change_result(gpu_lib, splits):
+    w = SMALL["bf16_straddle_text"]
+    seqs = make_inputs(w)
+    out, sel = run_decode(w, seqs, gpu_lib, splits=splits)
+    check_against_oracle(w, seqs, out, sel)
+
+
+@pytest.mark.parametrize("top_k,r_lo", [(0, 8), (100, 8), (25, 24), (1, 1)])
+def test_decode_edge_selection(gpu_lib, top_k, r_lo):
+    w = SMALL["bf16_ragged"].replace(top_k=top_k, r_lo=r_lo)
+    seqs = make_inputs(w)
+    out, sel = run_decode(w, seqs, gpu_lib)
+    check_against_oracle(w, seqs, out, sel)
+    if top_k == w.n_tokens:
+        assert np.array_equal(sel[0, 0], np.arange(w.n_tokens))
+
+
+def test_decode_single_token(gpu_lib):
+    for k in (0, 1):
+        w = wl.TINY.replace(cfg_id=110, batch=2, n_tokens=1, rank=1, r_lo=1, top_k=k, inner_dim=1)
+        seqs = make_inputs(w)
+        out, sel = run_decode(w, seqs, gpu_lib)
+        check_against_oracle(w, seqs, out, sel)
+
+
+def test_decode_zero_query_ties_take_lowest_ids(gpu_lib):
+    w = SMALL["bf16_ragged"]
+    seqs = make_inputs(w)
+    for s in seqs:
+        s["q"] = np.zeros_like(s["q"])
+    out, sel = run_decode(w, seqs, gpu_lib)
+    check_against_oracle(w, seqs, out, sel)
+    for b in range(w.batch):
+        for h in range(w.n_q_heads):
+            assert sel[b, h].tolist() == list(range(w.top_k))
+
+
+def test_decode_is_deterministic(gpu_lib):
+    w = SMALL["bf16_rank128"]
+    seqs = make_inputs(w)
+    cache, q, tk, tv = upload_decode(w, seqs, gpu_lib)
+    outs = [gpu_lib.decode(cache, q, r_lo=w.r_lo, top_k=w.top_k, scale=w.scale).cpu() for _ in range(3)]
+    cache.free()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("cfg,n_distinct", [(2, 3), (3, 2), (4, 2), (5, 2)])
+def test_decode_parity_full_configs(gpu_lib, cfg, n_distinct):
+    """Full batch at the workload's real shape; distinct sequences are checked against
+    the oracle and every replica must equal its original bit for bit."""
+    w = wl.WORKLOADS[cfg]
+    seqs = make_inputs(w, n_distinct)
+    out, sel = run_decode(w, seqs, gpu_lib)
+    err, flips = check_against_oracle(w, seqs, out, sel)
+    for b in range(len(seqs), w.batch):
+        o = b % len(seqs)
+        assert np.array_equal(out[b], out[o]) and np.array_equal(sel[b], sel[o]), f"replica {b}"
+    print(f"cfg {cfg}: max abs err {err:.3e}, band flips {flips}")
+
+
+def test_empty_batch_is_a_noop(gpu_lib):
+    c = gpu_lib.compress(None, None, batch=0, n_tokens=8, n_kv_heads=1, n_q_heads=1, head_dim=16,
+                         rank=4, storage=torch.bfloat16)
+    q = torch.zeros(0, 16, device="cuda")
+    gpu_lib.decode(c, q, r_lo=2, top_k=2, scale=0.25)
+    c.free()
+
+
+def test_factor_roundtrip(gpu_lib):
+    w = SMALL["bf16_ragged"]
+    seqs = make_inputs(w)
+    cache, q, tk, tv = upload_decode(w, seqs, gpu_lib)
+    U_k, B_k, U_v, B_v = cache.get_factors()
+    for b in range(w.batch):
+        s = seqs[b % len(seqs)]
+        assert np.array_equal(U_k[b].float().cpu().numpy(), s["U_k"])
+        assert np.array_equal(U_v[b].float().cpu().numpy(), s["U_v"])
+        assert np.array_equal(B_k[b].float().cpu().numpy(), s["B_k"])
+        assert np.array_equal(B_v[b].float().cpu().numpy(), s["B_v"])
+    cache.free()
