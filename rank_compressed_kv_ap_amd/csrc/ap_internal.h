@@ -48,6 +48,7 @@ struct ap_cache {
   void* Bv = nullptr;
   float* sigma_k = nullptr;  // [B][r]
   float* sigma_v = nullptr;
+  float* rn = nullptr;        // [B][NP] max_n |U_k[n, :16(p+1)]|, bounds the low-rank scores
   // decode workspace
   float* qt = nullptr;        // [B][Hq_pad][r_pad] latent queries
   uint32_t* mask = nullptr;   // [B][nblk][Hq_pad] selection bits per 32-token block
@@ -63,15 +64,18 @@ namespace ap {
 
 void set_error(const std::string& msg);
 
-// ---- launchers (decode_kernels.hip)
+// ---- launchers (decode_kernels.hip, select_kernel.hip)
 hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
                          int32_t* sel_out, hipStream_t st);
 hipError_t launch_attn(const ap_cache* c, int r_lo, float scale_log2e, int S, int CB,
                        hipStream_t st);
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float scale_log2e,
                           int S, int T, const void* text_k, const void* text_v, hipStream_t st);
+
+// ---- launchers (select_kernel.hip)
 int select_heads_per_group(const Dims& dm);
 size_t select_lds_bytes(const Dims& dm, int Hg);
+hipError_t launch_rownorm(const ap_cache* c, hipStream_t st);
 
 // ---- launchers (pack_kernels.hip)
 hipError_t launch_pack_u(const ap_cache* c, const void* src, void* dst, bool v_layout,

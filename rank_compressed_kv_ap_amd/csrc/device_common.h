@@ -57,6 +57,24 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, kWave));
 }
 
+// DPP lane moves inside a row of 16 lanes (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Sum over aligned groups of n lanes (n = 1, 2, 4, 8, 16, 32 or 64); every lane of a
+// group gets the group's sum.  Within a 16-lane row: quad swaps, then half-row and
+// row mirrors (sums are order-free, so mirrors serve as well as xor swaps).
+__device__ __forceinline__ float group_sum(float v, int n) {
+  if (n >= 2) v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  if (n >= 4) v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  if (n >= 8) v += dpp_f32<0x141>(v);   // row_half_mirror
+  if (n >= 16) v += dpp_f32<0x140>(v);  // row_mirror
+  if (n >= 32) v += __shfl_xor(v, 16, kWave);
+  if (n >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
 // ---------------------------------------------------------------- factor tiling
 // A factor U (N x r) is stored per sequence as panels of 16 columns and blocks of
 // 32 tokens.  Block (panel p, token block t) holds 512 elements laid out

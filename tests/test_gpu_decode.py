@@ -70,8 +70,11 @@ def test_decode_single_token(gpu_lib):
         check_against_oracle(w, seqs, out, sel)
 
 
-def test_decode_zero_query_ties_take_lowest_ids(gpu_lib):
-    w = SMALL["bf16_ragged"]
+@pytest.mark.parametrize("name", ["bf16_ragged", "bf16_rank128", "f32_text_long"])
+def test_decode_zero_query_ties_take_lowest_ids(gpu_lib, name):
+    # every score ties: N <= 256 exercises exact ranking inside the boundary bin,
+    # N = 300 the radix fallback
+    w = SMALL[name]
     seqs = make_inputs(w)
     for s in seqs:
         s["q"] = np.zeros_like(s["q"])
@@ -80,6 +83,37 @@ def test_decode_zero_query_ties_take_lowest_ids(gpu_lib):
     for b in range(w.batch):
         for h in range(w.n_q_heads):
             assert sel[b, h].tolist() == list(range(w.top_k))
+
+
+@pytest.mark.parametrize("scale_row", [1e3, 1e6])
+def test_decode_outlier_token(gpu_lib, scale_row):
+    # one huge key row makes the score bound loose, so many tokens share a bin
+    w = SMALL["bf16_rank128"]
+    seqs = make_inputs(w)
+    for s in seqs:
+        s["U_k"][7] = wl.round_bf16(s["U_k"][7] * scale_row)
+    out, sel = run_decode(w, seqs, gpu_lib)
+    check_against_oracle(w, seqs, out, sel)
+
+
+def test_decode_duplicated_tokens_tie_to_lower_ids(gpu_lib):
+    # 40 identical key rows around the cutoff: the tied group is cut by index
+    w = SMALL["bf16_straddle_text"]
+    seqs = make_inputs(w)
+    for s in seqs:
+        s["U_k"][60:100] = s["U_k"][60]
+    out, sel = run_decode(w, seqs, gpu_lib)
+    check_against_oracle(w, seqs, out, sel)
+    from gpu_helpers import oracle_decode
+    for b, s in enumerate(seqs):
+        ref = oracle_decode(w, s)
+        for h in range(w.n_q_heads):
+            got = set(sel[b, h].tolist())
+            tied = set(range(60, 100))
+            # inside the tied group the chosen ids are the lowest ones
+            chosen = sorted(got & tied)
+            if chosen and len(chosen) < len(tied):
+                assert chosen == list(range(60, 60 + len(chosen))), (b, h, chosen[:5])
 
 
 def test_decode_is_deterministic(gpu_lib):
