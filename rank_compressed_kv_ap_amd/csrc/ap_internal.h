@@ -42,8 +42,8 @@ struct ap_cache {
   ap::Dims dm;
   ap_compress_params params;
   // factors
-  void* Uk = nullptr;   // tiled K-layout  [B][NP][nblk][512]
-  void* Uv = nullptr;   // tiled V-layout  [B][NP][nblk][512]
+  void* Uk = nullptr;   // [B][nblk][2][NP][512]: K-layout panels then V-layout panels
+  void* Uv = nullptr;   // = Uk + NP*512 elements (same allocation)
   void* Bk = nullptr;   // [B][r_pad][W] row-major (rows r..r_pad-1 zero)
   void* Bv = nullptr;
   float* sigma_k = nullptr;  // [B][r]

@@ -78,7 +78,7 @@ static Dims make_dims(const ap_compress_params* p) {
 }
 
 static void free_all(ap_cache* c) {
-  void* ptrs[] = {c->Uk, c->Uv, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->rn, c->qt, c->mask, c->part_z, c->part_ml};
+  void* ptrs[] = {c->Uk, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->rn, c->qt, c->mask, c->part_z, c->part_ml};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   for (hipEvent_t e : c->timing.ev) (void)hipEventDestroy(e);
@@ -90,8 +90,7 @@ static ap_status alloc_cache(ap_cache* c) {
   struct Req { void** ptr; size_t bytes; };
   const size_t uel = (size_t)dm.B * dm.NP * dm.nblk * 512;
   Req reqs[] = {
-      {&c->Uk, uel * dm.esize},
-      {&c->Uv, uel * dm.esize},
+      {&c->Uk, 2 * uel * dm.esize},
       {&c->Bk, (size_t)dm.B * dm.r_pad * dm.W * dm.esize},
       {&c->Bv, (size_t)dm.B * dm.r_pad * dm.W * dm.esize},
       {reinterpret_cast<void**>(&c->sigma_k), (size_t)dm.B * dm.r * 4},
@@ -113,6 +112,7 @@ static ap_status alloc_cache(ap_cache* c) {
     }
     total += r.bytes;
   }
+  c->Uv = c->Uk ? static_cast<char*>(c->Uk) + (size_t)dm.NP * 512 * dm.esize : nullptr;
   c->factor_bytes = 2 * uel * dm.esize + 2 * (size_t)dm.B * dm.r_pad * dm.W * dm.esize;
   c->device_bytes = total;
   // padded rows of B and the singular values start at zero

@@ -79,12 +79,12 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        const bool live = 16 * ht + l16 < Hq;
-        const float v[4] = {live ? qraw[p][ht].x : 0.f, live ? qraw[p][ht].y : 0.f,
-                            live ? qraw[p][ht].z : 0.f, live ? qraw[p][ht].w : 0.f};
+        // the softmax scale (in log2 units) is folded into the latent query
+        const float f = 16 * ht + l16 < Hq ? sl2 : 0.f;
+        const float v[4] = {qraw[p][ht].x * f, qraw[p][ht].y * f, qraw[p][ht].z * f, qraw[p][ht].w * f};
         if constexpr (BF) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) qop[p][ht][e] = static_cast<short>(f32_to_bf16(v[e]));
+          const uint2 w = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          qop[p][ht] = __builtin_bit_cast(v4s, w);
         } else {
           qop[p][ht].set(v);
         }
@@ -110,80 +110,173 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
     uint32_t nmw[HT];
     const bool more = blk + 4 < blk1;
     if (more) attn_load<T, NP, HT>(Uk, Uv, mask, b, blk + 4, nblk, Hq, lane, nk, nv, nmw);
+    const bool tail = (blk + 1) * kBlockTok > N;
 
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+    if constexpr (BF) {
+      // bf16: one 32-token step per head tile.  Scores per 16-token half, one column
+      // max for the block, and the value product of both halves in one 16x16x32 MFMA
+      // (k-slot 8*(l/16) + 4*half + e <-> token 16*half + 4*(l/16) + e, which is how
+      // the V-layout tile and the score tiles already place their elements).
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        v4f slo = v4f{0, 0, 0, 0}, shi = v4f{0, 0, 0, 0};
+        v4f slo[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}}, shi[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}};
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          if constexpr (BF) {
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
             const v4s a = uk[p].half(hf);
             if (16 * p + 16 <= r_lo) {
-              slo = mfma_bf16(a, qop[p][ht], slo);
+              slo[hf] = mfma_bf16(a, qop[p][ht], slo[hf]);
             } else if (16 * p >= r_lo) {
-              shi = mfma_bf16(a, qop[p][ht], shi);
+              shi[hf] = mfma_bf16(a, qop[p][ht], shi[hf]);
             } else {
               v4s ql = qop[p][ht], qh = qop[p][ht];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 if (16 * p + 4 * lg + e < r_lo) qh[e] = 0; else ql[e] = 0;
               }
-              slo = mfma_bf16(a, ql, slo);
-              shi = mfma_bf16(a, qh, shi);
-            }
-          } else {
-            if (16 * p + 16 <= r_lo) {
-              slo = score_mma(uk[p], hf, qop[p][ht], slo);
-            } else if (16 * p >= r_lo) {
-              shi = score_mma(uk[p], hf, qop[p][ht], shi);
-            } else {
-              const int cl = 16 * p + 4 * lg;
-              slo = score_mma(uk[p], hf, qop[p][ht].masked(cl, r_lo, true), slo);
-              shi = score_mma(uk[p], hf, qop[p][ht].masked(cl, r_lo, false), shi);
+              slo[hf] = mfma_bf16(a, ql, slo[hf]);
+              shi[hf] = mfma_bf16(a, qh, shi[hf]);
             }
           }
-        }
-        float sc[4];
-        float bm = -INFINITY;
+        uint32_t bit[8];
+        float sc[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int pos = 16 * hf + 4 * lg + t;
-          const bool bit = (mw[ht] >> pos) & 1u;
-          const float v = (slo[t] + (bit ? shi[t] : 0.f)) * sl2;
-          sc[t] = (blk * kBlockTok + pos < N) ? v : -INFINITY;
-          bm = fmaxf(bm, sc[t]);
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint32_t wb = mw[ht] >> (16 * hf + 4 * lg);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            bit[4 * hf + t] = __builtin_amdgcn_ubfe(wb, t, 1);
+            sc[4 * hf + t] = bit[4 * hf + t] ? slo[hf][t] + shi[hf][t] : slo[hf][t];
+          }
         }
-        bm = wave_max_xor(bm, 16);
-        bm = wave_max_xor(bm, 32);
+        if (tail) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (blk * kBlockTok + 16 * (j >> 2) + 4 * lg + (j & 3) >= N) sc[j] = -INFINITY;
+        }
+        float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        bm = column_max4(bm);
         const float mn = fmaxf(m[ht], bm);
-        const float alpha = exp2f(m[ht] - mn);
-        m[ht] = mn;
-        lsum[ht] *= alpha;
+        if (__ballot(mn > m[ht])) {   // rescale only when some running max grew
+          const float alpha = exp2f(m[ht] - mn);
+          lsum[ht] *= alpha;
 #pragma unroll
-        for (int p = 0; p < NP; ++p) Z[p][ht] *= alpha;
-        float pv[4], phv[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float e = exp2f(sc[t] - mn);
-          lsum[ht] += e;
-          pv[t] = e;
-          phv[t] = ((mw[ht] >> (16 * hf + 4 * lg + t)) & 1u) ? e : 0.f;
+          for (int p = 0; p < NP; ++p) Z[p][ht] *= alpha;
+          m[ht] = mn;
         }
-        POp<T> pa, ph;
-        pa.set(pv);
-        ph.set(phv);
+        float pv[8];
+        uint32_t pa[4], ph[4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = exp2f(sc[j] - mn);
+          lsum[ht] += pv[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pa[j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+          ph[j] = pack_bf16x2(bit[2 * j] ? pv[2 * j] : 0.f, bit[2 * j + 1] ? pv[2 * j + 1] : 0.f);
+        }
+        const v8bf pa8 = __builtin_bit_cast(v8bf, make_uint4(pa[0], pa[1], pa[2], pa[3]));
+        const v8bf ph8 = __builtin_bit_cast(v8bf, make_uint4(ph[0], ph[1], ph[2], ph[3]));
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
+          const v8bf a8 = __builtin_bit_cast(v8bf, uv[p].raw);
           if (16 * p + 16 <= r_lo) {
-            Z[p][ht] = value_mma(uv[p], hf, true, pa, Z[p][ht]);
+            Z[p][ht] = mfma_bf16_k32(a8, pa8, Z[p][ht]);
           } else if (16 * p >= r_lo) {
-            Z[p][ht] = value_mma(uv[p], hf, true, ph, Z[p][ht]);
+            Z[p][ht] = mfma_bf16_k32(a8, ph8, Z[p][ht]);
           } else {
             const bool lo_row = 16 * p + l16 < r_lo;  // this lane's A row is latent column 16p+l16
-            Z[p][ht] = value_mma(uv[p], hf, lo_row, pa, Z[p][ht]);
-            Z[p][ht] = value_mma(uv[p], hf, !lo_row, ph, Z[p][ht]);
+            const v8bf zero8 = __builtin_bit_cast(v8bf, make_uint4(0u, 0u, 0u, 0u));
+            Z[p][ht] = mfma_bf16_k32(lo_row ? a8 : zero8, pa8, Z[p][ht]);
+            Z[p][ht] = mfma_bf16_k32(lo_row ? zero8 : a8, ph8, Z[p][ht]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+  #pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          v4f slo = v4f{0, 0, 0, 0}, shi = v4f{0, 0, 0, 0};
+  #pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            if constexpr (BF) {
+              const v4s a = uk[p].half(hf);
+              if (16 * p + 16 <= r_lo) {
+                slo = mfma_bf16(a, qop[p][ht], slo);
+              } else if (16 * p >= r_lo) {
+                shi = mfma_bf16(a, qop[p][ht], shi);
+              } else {
+                v4s ql = qop[p][ht], qh = qop[p][ht];
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  if (16 * p + 4 * lg + e < r_lo) qh[e] = 0; else ql[e] = 0;
+                }
+                slo = mfma_bf16(a, ql, slo);
+                shi = mfma_bf16(a, qh, shi);
+              }
+            } else {
+              if (16 * p + 16 <= r_lo) {
+                slo = score_mma(uk[p], hf, qop[p][ht], slo);
+              } else if (16 * p >= r_lo) {
+                shi = score_mma(uk[p], hf, qop[p][ht], shi);
+              } else {
+                const int cl = 16 * p + 4 * lg;
+                slo = score_mma(uk[p], hf, qop[p][ht].masked(cl, r_lo, true), slo);
+                shi = score_mma(uk[p], hf, qop[p][ht].masked(cl, r_lo, false), shi);
+              }
+            }
+          }
+          // selection bits of this lane's 4 tokens, scores already scaled (log2 units)
+          const uint32_t wb = mw[ht] >> (16 * hf + 4 * lg);
+          uint32_t bit[4];
+          float sc[4];
+  #pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            bit[t] = __builtin_amdgcn_ubfe(wb, t, 1);
+            sc[t] = bit[t] ? slo[t] + shi[t] : slo[t];
+          }
+          if (tail) {
+  #pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (blk * kBlockTok + 16 * hf + 4 * lg + t >= N) sc[t] = -INFINITY;
+          }
+          float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+          bm = wave_max_xor(bm, 16);
+          bm = wave_max_xor(bm, 32);
+          const float mn = fmaxf(m[ht], bm);
+          if (__ballot(mn > m[ht])) {   // rescale only when some running max grew
+            const float alpha = exp2f(m[ht] - mn);
+            lsum[ht] *= alpha;
+  #pragma unroll
+            for (int p = 0; p < NP; ++p) Z[p][ht] *= alpha;
+            m[ht] = mn;
+          }
+          float pv[4], phv[4];
+  #pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float e = exp2f(sc[t] - mn);
+            lsum[ht] += e;
+            pv[t] = e;
+            phv[t] = bit[t] ? e : 0.f;
+          }
+          POp<T> pa, ph;
+          pa.set(pv);
+          ph.set(phv);
+  #pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            if (16 * p + 16 <= r_lo) {
+              Z[p][ht] = value_mma(uv[p], hf, true, pa, Z[p][ht]);
+            } else if (16 * p >= r_lo) {
+              Z[p][ht] = value_mma(uv[p], hf, true, ph, Z[p][ht]);
+            } else {
+              const bool lo_row = 16 * p + l16 < r_lo;  // this lane's A row is latent column 16p+l16
+              Z[p][ht] = value_mma(uv[p], hf, lo_row, pa, Z[p][ht]);
+              Z[p][ht] = value_mma(uv[p], hf, !lo_row, ph, Z[p][ht]);
+            }
           }
         }
       }

@@ -18,12 +18,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
-// float -> bfloat16, round to nearest, ties to even (NaN kept quiet).
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// float -> bfloat16, round to nearest, ties to even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+// Two floats -> two bfloat16 packed in one dword (lo = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const v2f x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
 }
 
 template <class T> __device__ __forceinline__ float to_f32(T x);
@@ -47,6 +52,13 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 __device__ __forceinline__ v4f mfma_bf16(v4s a, v4s b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+// bf16 16x16x32 (gfx950): lane l supplies 8 k-values of row/column l%16 for its lane
+// group l/16; A and B use the same k-slot assignment, so any token order works as long
+// as the two operands agree.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v4f mfma_bf16_k32(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 // fp32 16x16x4: lane l supplies A[l%16][l/16] and B[l/16][l%16].
 __device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -55,6 +67,15 @@ __device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+// Maximum over the four lanes l%16 + 16k (the same column of a 16x16 tile), with the
+// gfx950 lane swaps: permlane16 pairs rows 0/1 and 2/3, permlane32 pairs the two halves.
+__device__ __forceinline__ float column_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
 // DPP lane moves inside a row of 16 lanes (no LDS traffic).
@@ -83,12 +104,16 @@ __device__ __forceinline__ float group_sum(float v, int n) {
 //     token = 32t + 16*half + l%16,        column = 16p + 4*(l/16) + e
 //   V-layout (value operand A^T, rows = columns of U):
 //     token = 32t + 16*half + 4*(l/16) + e, column = 16p + l%16
-// Sequence b, panel p, block t starts at element ((b*NP + p)*nblk + t)*512.
+// U_k and U_v share one buffer, block-major: for sequence b and token block t the NP
+// K panels are followed by the NP V panels, so the 2*NP KB one 32-token step of the
+// flash-decode kernel reads are contiguous.  With U_v = U_k + NP*512 elements,
+// panel p of block t of sequence b starts at element ((b*nblk + t)*2*NP + p)*512 of
+// either base.
 constexpr int kBlockTok = 32;
 constexpr int kBlockElems = 512;
 
 __host__ __device__ __forceinline__ size_t tile_base(int b, int p, int t, int NP, int nblk) {
-  return ((static_cast<size_t>(b) * NP + p) * nblk + t) * kBlockElems;
+  return (((size_t)b * nblk + t) * 2 * NP + p) * kBlockElems;
 }
 
 // Element index inside a block of (lane, half, e).

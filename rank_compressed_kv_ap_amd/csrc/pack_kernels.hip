@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_pack_u(const T* __restrict__ src, T* __
     tile_coord<VL>(t, p, within, token, col);
     T v = T(0);
     if (token < N && col < r) v = src[((size_t)b * N + token) * r + col];
-    dst[idx] = v;
+    dst[tile_base(b, p, t, NP, nblk) + within] = v;
   }
 }
 

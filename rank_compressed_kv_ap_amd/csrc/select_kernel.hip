@@ -67,9 +67,10 @@ __host__ __device__ inline SelLayout sel_layout(int Hg, int N_pad, int nblk, int
   return L;
 }
 
-__device__ __forceinline__ uint32_t score_bin(float s, float M, float mul) {
-  float x = (s + M) * mul;
-  x = fminf(fmaxf(x, 0.f), 65535.f);  // NaN -> 0
+// Monotone map of a score to a 16-bit bin: floor((s + M) * mul) clamped to [0, 65535],
+// computed as one fused multiply-add (Mmul = M * mul) and a median-of-three clamp.
+__device__ __forceinline__ uint32_t score_bin(float s, float Mmul, float mul) {
+  const float x = __builtin_amdgcn_fmed3f(fmaf(s, mul, Mmul), 0.f, 65535.f);
   return static_cast<uint32_t>(x);
 }
 
@@ -248,15 +249,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
       for (int i = 0; i < r_lo; ++i) n2 = fmaf(qs[tid * r_pad + i], qs[tid * r_pad + i], n2);
       const float M = sqrtf(n2) * rn[(size_t)b * NP + nplo - 1] * 1.0001f + 1e-30f;
       const float mul = (M < 3.0e38f && M > 1e-30f) ? 32767.0f / M : 0.f;
-      mm[2 * tid] = M;
+      mm[2 * tid] = M * mul;
       mm[2 * tid + 1] = mul;
     }
     __syncthreads();
-    const float Mh = l16 < nh ? mm[2 * l16] : 0.f, mulh = l16 < nh ? mm[2 * l16 + 1] : 0.f;
+    const float Mmulh = l16 < nh ? mm[2 * l16] : 0.f, mulh = l16 < nh ? mm[2 * l16 + 1] : 0.f;
     auto put = [&](int blk, int t, float sv) {
       const int n = blk * kBlockTok + 16 * (t >> 2) + 4 * lg + (t & 3);
       if (n < N) {
-        const uint32_t bn = score_bin(sv, Mh, mulh);
+        const uint32_t bn = score_bin(sv, Mmulh, mulh);
         bins[(size_t)l16 * N_pad + n] = static_cast<uint16_t>(bn);
         atomicAdd(&hist[l16 * 256 + (bn >> 8)], 1u);
       }

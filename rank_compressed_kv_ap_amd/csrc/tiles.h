@@ -86,7 +86,8 @@ template <class T> struct POp;
 template <> struct POp<bf16_t> {
   v4s v;
   __device__ __forceinline__ void set(const float p[4]) {
-    for (int t = 0; t < 4; ++t) v[t] = static_cast<short>(f32_to_bf16(p[t]));
+    const uint2 w = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    v = __builtin_bit_cast(v4s, w);
   }
 };
 template <> struct POp<float> {
