@@ -60,7 +60,10 @@ typedef struct {
   int32_t power_iters;  /* q, 0 <= q <= 8 power iterations                               */
   int32_t storage;      /* ap_dtype of K, V in and of U, B stored                        */
   int32_t reserved;     /* must be 0                                                     */
-  uint64_t seed;        /* seed of the device-generated test matrix (omega == NULL)      */
+  uint64_t seed;        /* omega == NULL: the test matrix of matrix m (2b: K, 2b+1: V) has
+                           entry (w, j) = -1 if bit i%32 of word (i/32)%4 of
+                           Philox4x32-10(counter (i/128, m, 0, 0), key (seed lo, seed hi))
+                           is set, else +1, with i = j*W + w (random signs)               */
   const float* omega;   /* optional device [B][2][W][ell] float32 test matrices
                            (index 0: for K, 1: for V), row-major, caller-owned and read
                            during ap_compress only; NULL: drawn on the device from seed. */
@@ -85,7 +88,12 @@ typedef struct ap_cache ap_cache;
  *         them NULL is AP_ERR_NULL_ARG.
  * p:      host struct, read during the call only.
  * out:    receives the new handle (NULL on any error).  The call allocates device
- *         memory synchronously, then enqueues the factorisation on `stream`.
+ *         memory synchronously (the cache, plus a workspace of about
+ *         2B * ell * (3 max(N, W) + N + W) * 4 bytes held until the enqueued work is
+ *         done), then enqueues the factorisation on `stream`.
+ * Limit:  when factoring (k, v set) ell = min(r + p, N, W) must be <= 128: the core
+ *         SVD and the orthonormalisation of each matrix live in one workgroup's LDS.
+ *         Larger ell is AP_ERR_UNSUPPORTED before anything is allocated.
  * Errors: AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_BAD_DTYPE, AP_ERR_UNSUPPORTED,
  *         AP_ERR_OUT_OF_MEMORY, AP_ERR_HIP.
  */

@@ -1,5 +1,6 @@
 // C ABI of the compressed-KV decode-attention library: argument validation,
 // ownership of device memory, and the stream-ordered launch sequence.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -158,6 +159,11 @@ ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p,
   if ((k == nullptr) != (v == nullptr)) return fail(AP_ERR_NULL_ARG, "k and v must both be set or both be NULL");
   ap_status s = validate_shape(p);
   if (s != AP_OK) return s;
+  if (k != nullptr) {
+    const int W = p->n_kv_heads * p->head_dim;
+    const int ell = std::min(std::min(p->rank + p->oversample, p->n_tokens), W);
+    if (ell > 128) return fail(AP_ERR_UNSUPPORTED, "min(rank + oversample, n_tokens, width) must be <= 128");
+  }
   ap_cache* c = new (std::nothrow) ap_cache();
   if (!c) return fail(AP_ERR_OUT_OF_MEMORY, "host allocation failed");
   c->params = *p;
@@ -171,6 +177,7 @@ ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p,
   hipStream_t st = static_cast<hipStream_t>(stream);
   c->last_stream = st;
   if (k != nullptr && c->dm.B > 0) {
+    set_error("");
     c->params.omega = p->omega;
     hipError_t e = run_compress(c, k, v, st);
     c->params.omega = nullptr;
@@ -180,7 +187,8 @@ ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p,
       delete c;
       if (e == hipErrorOutOfMemory) return fail(AP_ERR_OUT_OF_MEMORY, "compress workspace: " + detail);
       if (e == hipErrorNotSupported) return fail(AP_ERR_UNSUPPORTED, detail);
-      return hip_fail(e, "compress");
+      return fail(AP_ERR_HIP, std::string("compress: ") + hipGetErrorString(e) +
+                                  (detail.empty() ? std::string() : " (" + detail + ")"));
     }
   }
   *out = c;

@@ -1,13 +1,797 @@
-// Randomized factorisation of the heads-merged K and V (placeholder until the
-// device compressor lands: loading factors through ap_cache_set_factors works).
+// Randomized low-rank factorisation of the heads-merged K and V caches (gfx950).
+//
+// [fr §2.A "Approche"/"Mécanisme"], [es §2.A], [de §2.A "Technik"]: per sequence the
+// keys of all heads form one N x W matrix A (heads concatenated along the hidden
+// axis), compressed by a singular value decomposition into U (N x r) and B (r x W);
+// K and V separately.  The SVD is reached by randomized subspace iteration (Halko,
+// Martinsson & Tropp 2011) with ell = min(r + p, N, W) probe columns and q power
+// iterations:
+//   Y = A Omega; Q = orth(Y); q times { Q~ = orth(A^T Q); Q = orth(A Q~) }
+//   C^T = A^T Q = Qc R;  R^T = P Sigma S^T (one-sided Jacobi)
+//   U = Q P[:, :r] Sigma_r,   B = (Qc S[:, :r])^T
+// All 2B matrices of a batch are processed together, launch by launch.
+//
+// Kernels:
+//   k_gemm_n / k_gemm_t   Y = A X, Y = A^T X (X given transposed, k contiguous); bf16 MFMA
+//                         16x16x32 with A tiles staged in LDS (transposed for A^T); fp32 out
+//   k_gramchol            Gram Y^T Y (fp32 MFMA), shifted Cholesky, inverse of R
+//   k_apply               Q = Y R^-1 in place (fp32 MFMA), plus Q^T in storage precision
+//   k_jacobi              one-sided Jacobi SVD of R^T in LDS, components sorted by sigma
+//   k_assemble_u / _b     factors in the decode layouts
+//   k_omega_*             the test matrix: copied from the caller, or random signs from
+//                         Philox4x32-10 (Salmon et al., SC'11) keyed by the seed
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
 #include "ap_internal.h"
+#include "device_common.h"
 
 namespace ap {
 
+constexpr int kGemmThreads = 256;
+constexpr int kMaxEll = 128;          // largest ell the LDS-resident Cholesky/Jacobi handle
+
+// ---------------------------------------------------------------- workspace
+struct CompressWs {
+  int nmat, M, ellp;                  // matrices, max(N, W), ell padded to 16
+  void* omT = nullptr;                // [nmat][ellp][W]   storage dtype
+  float* Y = nullptr;                 // [nmat][M][ellp]   products, then orthonormal bases
+  void* XT = nullptr;                 // [nmat][ellp][M]   basis transposed, storage dtype
+  void* XTlo = nullptr;               // [nmat][ellp][M]   its rounding remainder (bf16 only)
+  float* Qn = nullptr;                // [nmat][N][ellp]   final range basis of A
+  float* Qc = nullptr;                // [nmat][W][ellp]   basis of C^T
+  float* Rinv = nullptr;              // [nmat][ellp][ellp]
+  float* Racc = nullptr;              // [nmat][ellp][ellp] R of the last orthonormalisation
+  float* PS = nullptr;                // [nmat][ellp][ellp] P Sigma (columns sorted)
+  float* Sv = nullptr;                // [nmat][ellp][ellp] S (columns sorted)
+  float* sig = nullptr;               // [nmat][ellp]
+};
+
+// ================================================================ test matrix
+// Philox4x32-10 (Salmon, Moraes, Dror & Shaw, SC'11): counter-based, 10 rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint2 k) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = M0 * c.x, hi0 = __umulhi(M0, c.x);
+    const uint32_t lo1 = M1 * c.z, hi1 = __umulhi(M1, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k.x, lo1, hi0 ^ c.w ^ k.y, lo0);
+    k.x += W0;
+    k.y += W1;
+  }
+  return c;
+}
+
+// Omega^T[mat][j][w]: element (w, j) of the W x ell random-sign test matrix of
+// matrix mat (sub-Gaussian test matrices: Halko, Martinsson & Tropp 2011, §4.6).
+// Linear index i = j*W + w; one Philox call with counter (i/128, mat, 0, 0) and key
+// (seed lo, seed hi) yields 128 bits for elements 128*(i/128) ..; bit i%32 of word
+// (i/32)%4 set means -1.  One thread per 128-element block.
+template <class T>
+__global__ __launch_bounds__(256) void k_omega_philox(T* __restrict__ omT, int nmat, int W, int ell,
+                                                      int ellp, uint64_t seed) {
+  const size_t per = (size_t)ell * W;
+  const size_t blocks = (per + 127) / 128;
+  const uint2 key = make_uint2(static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < blocks * nmat;
+       g += (size_t)gridDim.x * blockDim.x) {
+    const int mat = static_cast<int>(g / blocks);
+    const size_t blk = g % blocks;
+    const uint4 x = philox4x32_10(make_uint4(static_cast<uint32_t>(blk), static_cast<uint32_t>(mat), 0u, 0u), key);
+    const uint32_t words[4] = {x.x, x.y, x.z, x.w};
+    const size_t i0 = 128 * blk;
+    const int cnt = static_cast<int>(per - i0 < 128 ? per - i0 : 128);
+    int j = static_cast<int>(i0 / W), w = static_cast<int>(i0 % W);
+    for (int t = 0; t < cnt; ++t) {
+      const bool neg = (words[t >> 5] >> (t & 31)) & 1u;
+      omT[((size_t)mat * ellp + j) * W + w] = from_f32<T>(neg ? -1.f : 1.f);
+      if (++w == W) { w = 0; ++j; }
+    }
+  }
+}
+
+// Caller's Omega [B][2][W][ell] float32 -> Omega^T[mat][j][w] in storage precision.
+template <class T>
+__global__ __launch_bounds__(256) void k_omega_copy(const float* __restrict__ om, T* __restrict__ omT,
+                                                    int nmat, int W, int ell, int ellp) {
+  const size_t total = (size_t)nmat * ell * W;
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (size_t)gridDim.x * blockDim.x) {
+    const int mat = static_cast<int>(g / ((size_t)ell * W));
+    const size_t rem = g % ((size_t)ell * W);
+    const int j = static_cast<int>(rem / W), w = static_cast<int>(rem % W);
+    omT[((size_t)mat * ellp + j) * W + w] = from_f32<T>(om[((size_t)mat * W + w) * ell + j]);
+  }
+}
+
+// ================================================================ tall-skinny GEMMs
+// Output Y[mat][m][j] (fp32, row stride ellp) for m in a 128-row tile:
+//   TRANS = false: Y = A X,   A [M][K] rows m, X^T [ellp][K]        (M = N, K = W)
+//   TRANS = true : Y = A^T X, A [K][M] columns m, X^T [ellp][K]     (M = W, K = N)
+// A 32-wide k slice of A is staged in LDS as [128 m][32 k] (transposed on the way in
+// for TRANS), so both MFMA operands read 8 consecutive k values per lane.
+constexpr int kGemmBM = 128, kGemmBK = 32, kGemmLdsStride = kGemmBK + 8;  // padded bf16 row
+
+template <class T, bool TRANS, int NT, bool SPLIT>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kmat,
+                                                        const T* __restrict__ Vmat,
+                                                        const T* __restrict__ XT,
+                                                        const T* __restrict__ XTlo, float* __restrict__ Y,
+                                                        int N, int W, int ellp, size_t x_mat_stride,
+                                                        int tiles_m) {
+  static_assert(std::is_same<T, bf16_t>::value, "MFMA GEMM path is bf16");
+  __shared__ __align__(16) bf16_t As[kGemmBM * kGemmLdsStride];
+  const int mat = blockIdx.x / tiles_m;
+  const int m0 = (blockIdx.x % tiles_m) * kGemmBM;
+  const int b = mat >> 1;
+  const T* A = ((mat & 1) ? Vmat : Kmat) + (size_t)b * N * W;
+  const int M = TRANS ? W : N;
+  const int K = TRANS ? N : W;
+  const T* X = XT + (size_t)mat * x_mat_stride;
+  const T* Xl = SPLIT ? XTlo + (size_t)mat * x_mat_stride : nullptr;
+  const bool avec = (W & 7) == 0;   // 16-byte loads of A rows stay aligned
+  const bool xvec = (K & 7) == 0;   // 16-byte loads of X^T rows stay aligned
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  // wave owns rows m0 + 32*wave .. +31 (two 16-row tiles) x NT column tiles
+  v4f acc[2][NT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[i][c] = v4f{0, 0, 0, 0};
+
+  for (int k0 = 0; k0 < K; k0 += kGemmBK) {
+    // stage A tile: 128 x 32 bf16 = 8 KB = 256 threads x 2 x 16 B
+    if (!TRANS) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = (tid >> 2) + 64 * h, kk = (tid & 3) * 8;
+        const int gm = min(m0 + row, M - 1), gk = k0 + kk;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (avec && gk + 8 <= K) {
+          v = *reinterpret_cast<const uint4*>(A + (size_t)gm * W + gk);
+        } else {
+          uint16_t t[8];
+          for (int e = 0; e < 8; ++e) t[e] = gk + e < K ? A[(size_t)gm * W + gk + e] : bf16_t(0);
+          v = make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16),
+                         t[4] | (uint32_t(t[5]) << 16), t[6] | (uint32_t(t[7]) << 16));
+        }
+        *reinterpret_cast<uint4*>(&As[row * kGemmLdsStride + kk]) = v;
+      }
+    } else {
+      // A rows are k (tokens), columns are m: read 32 rows x 128 columns coalesced,
+      // write transposed so that As[m][k] holds k contiguous.
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = (tid >> 4) + 16 * h, mm = (tid & 15) * 8;
+        const int gk = k0 + kk, gm = m0 + mm;
+        uint16_t t[8];
+        if (avec && gk < K && gm + 8 <= M) {
+          const uint4 v = *reinterpret_cast<const uint4*>(A + (size_t)gk * W + gm);
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+          for (int e = 0; e < 4; ++e) {
+            t[2 * e] = static_cast<uint16_t>(w4[e] & 0xffffu);
+            t[2 * e + 1] = static_cast<uint16_t>(w4[e] >> 16);
+          }
+        } else {
+          for (int e = 0; e < 8; ++e) t[e] = (gk < K && gm + e < M) ? A[(size_t)gk * W + gm + e] : bf16_t(0);
+        }
+        for (int e = 0; e < 8; ++e) As[(mm + e) * kGemmLdsStride + kk] = t[e];
+      }
+    }
+    __syncthreads();
+    // X operand: columns 16c + l16, k = k0 + 8*lg .. +7 (zero past K); with SPLIT the
+    // operand is hi + lo, two bf16 halves of an fp32 basis (about 16 significant bits)
+    auto load_x = [&](const T* base, int c) {
+      const int gk = k0 + 8 * lg;
+      const T* xr = base + (size_t)(16 * c + l16) * K + gk;
+      uint4 v;
+      if (xvec && gk + 8 <= K) {
+        v = *reinterpret_cast<const uint4*>(xr);
+      } else {
+        uint16_t t[8];
+        for (int e = 0; e < 8; ++e) t[e] = gk + e < K ? xr[e] : bf16_t(0);
+        v = make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16),
+                       t[4] | (uint32_t(t[5]) << 16), t[6] | (uint32_t(t[7]) << 16));
+      }
+      return __builtin_bit_cast(v8bf, v);
+    };
+    v8bf xb[NT], xl[SPLIT ? NT : 1];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      xb[c] = load_x(X, c);
+      if constexpr (SPLIT) xl[c] = load_x(Xl, c);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 32 * wave + 16 * i + l16;
+      const v8bf ab = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&As[row * kGemmLdsStride + 8 * lg]));
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        acc[i][c] = mfma_bf16_k32(ab, xb[c], acc[i][c]);
+        if constexpr (SPLIT) acc[i][c] = mfma_bf16_k32(ab, xl[c], acc[i][c]);
+      }
+    }
+    __syncthreads();
+  }
+  // D tile: lane holds rows 4*lg + t, column l16
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int m = m0 + 32 * wave + 16 * i + 4 * lg + t;
+        if (m < M) Y[((size_t)mat * (TRANS ? W : N) + m) * ellp + 16 * c + l16] = acc[i][c][t];
+      }
+}
+
+// fp32 storage: plain VALU products (small shapes only).
+template <bool TRANS>
+__global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ Kmat,
+                                                  const float* __restrict__ Vmat,
+                                                  const float* __restrict__ XT, float* __restrict__ Y,
+                                                  int N, int W, int ellp, size_t x_mat_stride, int nmat) {
+  const int M = TRANS ? W : N, K = TRANS ? N : W;
+  const size_t total = (size_t)nmat * M * ellp;
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (size_t)gridDim.x * blockDim.x) {
+    const int j = static_cast<int>(g % ellp);
+    const int m = static_cast<int>((g / ellp) % M);
+    const int mat = static_cast<int>(g / ((size_t)ellp * M));
+    const float* A = ((mat & 1) ? Vmat : Kmat) + (size_t)(mat >> 1) * N * W;
+    const float* x = XT + (size_t)mat * x_mat_stride + (size_t)j * K;
+    float acc = 0.f;
+    if (!TRANS) {
+      for (int k = 0; k < K; ++k) acc = fmaf(A[(size_t)m * W + k], x[k], acc);
+    } else {
+      for (int k = 0; k < K; ++k) acc = fmaf(A[(size_t)k * W + m], x[k], acc);
+    }
+    Y[((size_t)mat * M + m) * ellp + j] = acc;
+  }
+}
+
+// ================================================================ orthonormalisation
+// One workgroup per matrix: G = Y^T Y (fp32 MFMA 16x16x4 over the M rows), a shifted
+// Cholesky G + eps I = L L^T in LDS, and Rinv = L^-T (so that Y Rinv is orthonormal).
+// When Rprev is given the product R = L^T Rprev is written as well (two-pass QR).
+constexpr int kCholThreads = 256;
+
+__global__ __launch_bounds__(kCholThreads) void k_gramchol(const float* __restrict__ Y, int M,
+                                                           int ell, int ellp, float* __restrict__ Rinv,
+                                                           const float* __restrict__ Rprev,
+                                                           float* __restrict__ Rout) {
+  extern __shared__ __align__(16) float sh[];
+  const int S = ellp + 1;
+  float* G = sh;                 // [ellp][S] Gram, then L (lower)
+  float* Li = G + ellp * S;      // [ellp][S] L^-1
+  const int mat = blockIdx.x;
+  const float* Ym = Y + (size_t)mat * M * ellp;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int T = ellp / 16;
+  // Each wavefront accumulates every upper tile (ti <= tj) over its share of the rows:
+  // one 4-row slice of Y per MFMA k-step, all column tiles of it held in registers.
+  constexpr int kMaxT = kMaxEll / 16;
+  v4f acc[kMaxT * (kMaxT + 1) / 2];
+#pragma unroll
+  for (int t = 0; t < kMaxT * (kMaxT + 1) / 2; ++t) acc[t] = v4f{0, 0, 0, 0};
+  constexpr int UR = 4;   // k-steps whose loads are in flight together
+  for (int n0 = 4 * UR * wave; n0 < M; n0 += 4 * UR * 4) {
+    float y[UR][kMaxT];
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int n = min(n0 + 4 * u + lg, M - 1);
+      const bool live = n0 + 4 * u + lg < M;
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t) {
+        const float v = t < T ? Ym[(size_t)n * ellp + 16 * t + l16] : 0.f;
+        y[u][t] = live ? v : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      int idx = 0;
+#pragma unroll
+      for (int ti = 0; ti < kMaxT; ++ti)
+#pragma unroll
+        for (int tj = ti; tj < kMaxT; ++tj, ++idx)
+          if (tj < T) acc[idx] = mfma_f32(y[u][ti], y[u][tj], acc[idx]);
+    }
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+      int idx = 0;
+#pragma unroll
+      for (int ti = 0; ti < kMaxT; ++ti)
+#pragma unroll
+        for (int tj = ti; tj < kMaxT; ++tj, ++idx) {
+          if (tj >= T) continue;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int i = 16 * ti + 4 * lg + t, j = 16 * tj + l16;
+            const float v = acc[idx][t] + (w == 0 ? 0.f : G[i * S + j]);
+            G[i * S + j] = v;
+            if (ti != tj) G[j * S + i] = v;
+          }
+        }
+    }
+    __syncthreads();
+  }
+  // diagonal tiles hold both triangles already; mirror their lower half for symmetry
+  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
+    const int i = idx / ellp, j = idx % ellp;
+    if ((i >> 4) == (j >> 4) && j < i) G[i * S + j] = G[j * S + i];
+  }
+  __syncthreads();
+  // shift: relative to the mean diagonal; padded columns get a unit diagonal
+  __shared__ float trace_sh;
+  if (tid == 0) {
+    float tr = 0.f;
+    for (int i = 0; i < ell; ++i) tr += G[i * S + i];
+    trace_sh = tr;
+  }
+  __syncthreads();
+  const float eps = 1e-6f * (trace_sh / static_cast<float>(ell > 0 ? ell : 1)) + 1e-30f;
+  for (int i = tid; i < ellp; i += kCholThreads) {
+    if (i < ell) {
+      G[i * S + i] += eps;
+    } else {
+      for (int j = 0; j < ellp; ++j) { G[i * S + j] = 0.f; G[j * S + i] = 0.f; }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < ellp; i += kCholThreads)
+    if (i >= ell) G[i * S + i] = 1.f;
+  __syncthreads();
+  // right-looking Cholesky, lower triangle
+  for (int j = 0; j < ellp; ++j) {
+    if (tid == 0) G[j * S + j] = sqrtf(fmaxf(G[j * S + j], 1e-30f));
+    __syncthreads();
+    const float inv = 1.f / G[j * S + j];
+    for (int i = j + 1 + tid; i < ellp; i += kCholThreads) G[i * S + j] *= inv;
+    __syncthreads();
+    const int nt = ellp - j - 1;
+    for (int idx = tid; idx < nt * nt; idx += kCholThreads) {
+      const int i = j + 1 + idx / nt, k = j + 1 + idx % nt;
+      if (k <= i) G[i * S + k] -= G[i * S + j] * G[k * S + j];
+    }
+    __syncthreads();
+  }
+  // L^-1 by forward substitution, one column per thread
+  for (int c = tid; c < ellp; c += kCholThreads) {
+    for (int i = 0; i < ellp; ++i) {
+      float v = (i == c) ? 1.f : 0.f;
+      for (int k = c; k < i; ++k) v -= G[i * S + k] * Li[k * S + c];
+      Li[i * S + c] = i >= c ? v / G[i * S + i] : 0.f;
+    }
+  }
+  __syncthreads();
+  // Rinv = L^-T ; R = L^T (times Rprev).  Rprev is copied into LDS (over L^-1, after
+  // Rinv is written) before R is overwritten, since both may be the same buffer.
+  float* Ri = Rinv + (size_t)mat * ellp * ellp;
+  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
+    const int i = idx / ellp, j = idx % ellp;
+    Ri[idx] = Li[j * S + i];
+  }
+  if (Rout != nullptr) {
+    __syncthreads();
+    const float* Rp = Rprev ? Rprev + (size_t)mat * ellp * ellp : nullptr;
+    for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
+      const int i = idx / ellp, j = idx % ellp;
+      Li[i * S + j] = Rp ? Rp[idx] : (i == j ? 1.f : 0.f);
+    }
+    __syncthreads();
+    float* Ro = Rout + (size_t)mat * ellp * ellp;
+    for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
+      const int i = idx / ellp, j = idx % ellp;
+      float v = 0.f;
+      for (int k = i; k < ellp; ++k) v = fmaf(G[k * S + i], Li[k * S + j], v);
+      Ro[idx] = v;
+    }
+  }
+}
+
+// Q = Y Rinv for 64 rows per workgroup (fp32 MFMA), written in place; optionally
+// Q^T in storage precision for the next product (XT[mat][j][m]), and the rounding
+// remainder Q^T - XT in XTlo for a two-term product.
+template <class T>
+__global__ __launch_bounds__(256) void k_apply(float* __restrict__ Y, int M, int ellp,
+                                               const float* __restrict__ Rinv, T* __restrict__ XT,
+                                               T* __restrict__ XTlo, size_t xt_mat_stride, int tiles_m) {
+  extern __shared__ __align__(16) float sh[];
+  const int S = ellp + 1;
+  float* Ys = sh;                  // [64][S]
+  float* Rs = Ys + 64 * S;         // [ellp][ellp]
+  const int mat = blockIdx.x / tiles_m;
+  const int m0 = (blockIdx.x % tiles_m) * 64;
+  float* Ym = Y + (size_t)mat * M * ellp;
+  const float* Rm = Rinv + (size_t)mat * ellp * ellp;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  for (int idx = tid; idx < 64 * ellp; idx += 256) {
+    const int r = idx / ellp, j = idx % ellp;
+    Ys[r * S + j] = m0 + r < M ? Ym[(size_t)(m0 + r) * ellp + j] : 0.f;
+  }
+  for (int idx = tid; idx < ellp * ellp; idx += 256) Rs[idx] = Rm[idx];
+  __syncthreads();
+  const int T16 = ellp / 16;
+  // wave owns rows 16*wave .. +15, all column tiles
+  for (int c = 0; c < T16; ++c) {
+    v4f acc = v4f{0, 0, 0, 0};
+    for (int k0 = 0; k0 < ellp; k0 += 4) {
+      const float a = Ys[(16 * wave + l16) * S + k0 + lg];
+      const float bb = Rs[(k0 + lg) * ellp + 16 * c + l16];
+      acc = mfma_f32(a, bb, acc);
+    }
+    for (int t = 0; t < 4; ++t) {
+      const int m = m0 + 16 * wave + 4 * lg + t, j = 16 * c + l16;
+      if (m < M) {
+        Ym[(size_t)m * ellp + j] = acc[t];
+        if (XT != nullptr) {
+          const size_t o = (size_t)mat * xt_mat_stride + (size_t)j * M + m;
+          const T hi = from_f32<T>(acc[t]);
+          XT[o] = hi;
+          if (XTlo != nullptr) XTlo[o] = from_f32<T>(acc[t] - to_f32<T>(hi));
+        }
+      }
+    }
+  }
+}
+
+// ================================================================ core SVD
+// One-sided Jacobi on the columns of Mj = R^T (ell x ell, LDS): rotations make the
+// columns mutually orthogonal, Mj J = P Sigma, J = S.  Round-robin pair order, one
+// wavefront per pair; stops when every pair is orthogonal to 3e-6 relative (fp32).
+constexpr int kJacThreads = 512;
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum(v, 16);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kJacThreads) void k_jacobi(const float* __restrict__ Rm, int ell, int ellp,
+                                                        float* __restrict__ PS, float* __restrict__ Sv,
+                                                        float* __restrict__ sig) {
+  extern __shared__ __align__(16) float sh[];
+  const int S = ellp + 1;
+  const int E = (ell + 1) & ~1;            // even number of columns for the tournament
+  float* Mj = sh;                          // [ellp][S]  (row i, column j)
+  float* J = Mj + ellp * S;                // [ellp][S]
+  float* nrm = J + ellp * S;               // [ellp]
+  int* perm = reinterpret_cast<int*>(nrm + ellp);  // [ellp]
+  __shared__ unsigned int rotated;
+  const int mat = blockIdx.x;
+  const float* R = Rm + (size_t)mat * ellp * ellp;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int nwave = kJacThreads / 64;
+  for (int idx = tid; idx < ellp * ellp; idx += kJacThreads) {
+    const int i = idx / ellp, j = idx % ellp;
+    Mj[i * S + j] = (i < ell && j < ell) ? R[j * ellp + i] : 0.f;   // transpose
+    J[i * S + j] = i == j ? 1.f : 0.f;
+  }
+  __syncthreads();
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    if (tid == 0) rotated = 0u;
+    __syncthreads();
+    for (int step = 0; step < E - 1; ++step) {
+      // tournament: position 0 fixed, the others rotate
+      for (int pr = wave; pr < E / 2; pr += nwave) {
+        auto pos = [&](int x) { return x == 0 ? 0 : 1 + (x - 1 + step) % (E - 1); };
+        int p = pos(pr), qq = pos(E - 1 - pr);
+        if (p > qq) { const int t = p; p = qq; qq = t; }
+        if (qq >= ell) continue;
+        float a = 0.f, bsum = 0.f, g = 0.f;
+        for (int i = lane; i < ell; i += 64) {
+          const float x = Mj[i * S + p], y = Mj[i * S + qq];
+          a = fmaf(x, x, a);
+          bsum = fmaf(y, y, bsum);
+          g = fmaf(x, y, g);
+        }
+        a = wave_sum(a);
+        bsum = wave_sum(bsum);
+        g = wave_sum(g);
+        if (g == 0.f || fabsf(g) <= 3e-6f * sqrtf(a * bsum)) continue;
+        if (lane == 0) rotated = 1u;
+        const float zeta = (bsum - a) / (2.f * g);
+        const float t = copysignf(1.f, zeta) / (fabsf(zeta) + sqrtf(1.f + zeta * zeta));
+        const float c = 1.f / sqrtf(1.f + t * t), s = c * t;
+        for (int i = lane; i < ellp; i += 64) {
+          const float x = Mj[i * S + p], y = Mj[i * S + qq];
+          Mj[i * S + p] = c * x - s * y;
+          Mj[i * S + qq] = s * x + c * y;
+          const float u = J[i * S + p], v = J[i * S + qq];
+          J[i * S + p] = c * u - s * v;
+          J[i * S + qq] = s * u + c * v;
+        }
+      }
+      __syncthreads();
+    }
+    if (rotated == 0u) break;
+    __syncthreads();
+  }
+  // singular values and their descending order (ties: lower column first)
+  for (int j = tid; j < ellp; j += kJacThreads) {
+    float s2 = 0.f;
+    for (int i = 0; i < ellp; ++i) s2 = fmaf(Mj[i * S + j], Mj[i * S + j], s2);
+    nrm[j] = j < ell ? sqrtf(s2) : -1.f;
+  }
+  __syncthreads();
+  for (int j = tid; j < ellp; j += kJacThreads) {
+    int rank = 0;
+    for (int o = 0; o < ellp; ++o) rank += (nrm[o] > nrm[j] || (nrm[o] == nrm[j] && o < j)) ? 1 : 0;
+    perm[rank] = j;
+  }
+  __syncthreads();
+  float* PSm = PS + (size_t)mat * ellp * ellp;
+  float* Sm = Sv + (size_t)mat * ellp * ellp;
+  for (int idx = tid; idx < ellp * ellp; idx += kJacThreads) {
+    const int i = idx / ellp, c = idx % ellp;
+    const int j = perm[c];
+    PSm[idx] = Mj[i * S + j];
+    Sm[idx] = J[i * S + j];
+  }
+  for (int c = tid; c < ellp; c += kJacThreads) sig[(size_t)mat * ellp + c] = fmaxf(nrm[perm[c]], 0.f);
+}
+
+// ================================================================ assembly
+// U[n][i] = sum_j Qn[n][j] PS[j][i] (i < r) into the decode tiles of one 32-token block;
+// the block's 32 rows of Qn and the r_pad used columns of PS are staged in LDS.
+template <class T>
+__global__ __launch_bounds__(256) void k_assemble_u(const float* __restrict__ Qn, const float* __restrict__ PS,
+                                                    T* __restrict__ Ukv, int N, int ellp, int r, int NP,
+                                                    int nblk) {
+  extern __shared__ __align__(16) float sh[];
+  const int rp = 16 * NP;
+  float* Qs = sh;                      // [32][ellp + 1]
+  float* Ps = Qs + 32 * (ellp + 1);    // [ellp][rp]
+  const int mat = blockIdx.x / nblk, t = blockIdx.x % nblk;
+  const int b = mat >> 1;
+  const bool vl = mat & 1;
+  const float* Q = Qn + (size_t)mat * N * ellp;
+  const float* P = PS + (size_t)mat * ellp * ellp;
+  for (int idx = threadIdx.x; idx < 32 * ellp; idx += blockDim.x) {
+    const int rr = idx / ellp, j = idx % ellp;
+    const int token = kBlockTok * t + rr;
+    Qs[rr * (ellp + 1) + j] = token < N ? Q[(size_t)token * ellp + j] : 0.f;
+  }
+  for (int idx = threadIdx.x; idx < ellp * rp; idx += blockDim.x) {
+    const int j = idx / rp, col = idx % rp;
+    Ps[idx] = col < r ? P[j * ellp + col] : 0.f;
+  }
+  __syncthreads();
+  T* base = Ukv + (vl ? (size_t)NP * kBlockElems : 0);
+  for (int idx = threadIdx.x; idx < NP * kBlockElems; idx += blockDim.x) {
+    const int p = idx / kBlockElems, within = idx % kBlockElems;
+    const int e = within & 3, half = (within >> 2) & 1, lane = within >> 3;
+    int rr, col;
+    if (!vl) {
+      rr = 16 * half + (lane & 15);
+      col = 16 * p + 4 * (lane >> 4) + e;
+    } else {
+      rr = 16 * half + 4 * (lane >> 4) + e;
+      col = 16 * p + (lane & 15);
+    }
+    float v = 0.f;
+    for (int j = 0; j < ellp; ++j) v = fmaf(Qs[rr * (ellp + 1) + j], Ps[j * rp + col], v);
+    base[tile_base(b, p, t, NP, nblk) + within] = from_f32<T>(v);
+  }
+}
+
+// B[i][w] = sum_j Qc[w][j] S[j][i] for i < r (rows r..r_pad-1 stay zero).
+template <class T>
+__global__ __launch_bounds__(256) void k_assemble_b(const float* __restrict__ Qc, const float* __restrict__ Sv,
+                                                    T* __restrict__ Bk, T* __restrict__ Bv, int W, int ellp,
+                                                    int r, int r_pad, int tiles_w) {
+  const int mat = blockIdx.x / tiles_w;
+  const int w = (blockIdx.x % tiles_w) * 256 + threadIdx.x;
+  if (w >= W) return;
+  const float* Q = Qc + ((size_t)mat * W + w) * ellp;
+  const float* Sm = Sv + (size_t)mat * ellp * ellp;
+  T* B = ((mat & 1) ? Bv : Bk) + (size_t)(mat >> 1) * r_pad * W;
+  for (int i = 0; i < r; ++i) {
+    float v = 0.f;
+    for (int j = 0; j < ellp; ++j) v = fmaf(Q[j], Sm[j * ellp + i], v);
+    B[(size_t)i * W + w] = from_f32<T>(v);
+  }
+}
+
+__global__ void k_copy_sigma(const float* __restrict__ sig, float* __restrict__ sk, float* __restrict__ sv,
+                             int nmat, int ellp, int r) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= nmat * r) return;
+  const int mat = g / r, i = g % r;
+  ((mat & 1) ? sv : sk)[(size_t)(mat >> 1) * r + i] = sig[(size_t)mat * ellp + i];
+}
+
+// ================================================================ driver
+static dim3 grid_1d(size_t total, int threads = 256) {
+  size_t g = (total + threads - 1) / threads;
+  g = g < 1 ? 1 : (g > 65536 ? 65536 : g);
+  return dim3(static_cast<unsigned>(g));
+}
+
+template <class T>
+static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const void* XT, const void* XTlo,
+                       float* Y, bool trans, size_t x_stride, hipStream_t st) {
+  const Dims& dm = c->dm;
+  const int nmat = 2 * dm.B;
+  const int ellp = (dm.ell + 15) / 16 * 16;
+  const int M = trans ? dm.W : dm.N;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    const int tiles_m = (M + kGemmBM - 1) / kGemmBM;
+    const dim3 grid(nmat * tiles_m);
+#define AP_GEMM_LAUNCH(TR, NTV, SP)                                                                     \
+  hipLaunchKernelGGL((k_gemm<bf16_t, TR, NTV, SP>), grid, dim3(kGemmThreads), 0, st,                   \
+                     static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),                     \
+                     static_cast<const bf16_t*>(XT), static_cast<const bf16_t*>(XTlo), Y, dm.N, dm.W, \
+                     ellp, x_stride, tiles_m)
+#define AP_GEMM_CASE(NTV)                                                                              \
+  case NTV:                                                                                            \
+    if (trans && XTlo != nullptr) AP_GEMM_LAUNCH(true, NTV, true);                                     \
+    else if (trans) AP_GEMM_LAUNCH(true, NTV, false);                                                  \
+    else AP_GEMM_LAUNCH(false, NTV, false);                                                            \
+    break;
+    switch (ellp / 16) {
+      AP_GEMM_CASE(1) AP_GEMM_CASE(2) AP_GEMM_CASE(3) AP_GEMM_CASE(4)
+      AP_GEMM_CASE(5) AP_GEMM_CASE(6) AP_GEMM_CASE(7) AP_GEMM_CASE(8)
+      default: return hipErrorInvalidValue;
+    }
+#undef AP_GEMM_CASE
+#undef AP_GEMM_LAUNCH
+  } else {
+    if (trans)
+      hipLaunchKernelGGL((k_gemm_f32<true>), grid_1d((size_t)nmat * M * ellp), dim3(256), 0, st,
+                         static_cast<const float*>(k), static_cast<const float*>(v),
+                         static_cast<const float*>(XT), Y, dm.N, dm.W, ellp, x_stride, nmat);
+    else
+      hipLaunchKernelGGL((k_gemm_f32<false>), grid_1d((size_t)nmat * M * ellp), dim3(256), 0, st,
+                         static_cast<const float*>(k), static_cast<const float*>(v),
+                         static_cast<const float*>(XT), Y, dm.N, dm.W, ellp, x_stride, nmat);
+  }
+  return hipGetLastError();
+}
+
+// Two-pass Cholesky QR of Y [nmat][M][ellp] in place; Q^T to XT (if given); R to Racc (if given).
+template <class T>
+static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void* XTlo, float* Racc,
+                       hipStream_t st) {
+  const Dims& dm = c->dm;
+  const int nmat = 2 * dm.B, ellp = ws.ellp;
+  const size_t lds_chol = (size_t)2 * ellp * (ellp + 1) * sizeof(float);
+  const size_t lds_apply = (size_t)(64 * (ellp + 1) + ellp * ellp) * sizeof(float);
+  const int tiles_m = (M + 63) / 64;
+  hipLaunchKernelGGL(k_gramchol, dim3(nmat), dim3(kCholThreads), lds_chol, st, ws.Y, M, dm.ell, ellp,
+                     ws.Rinv, nullptr, Racc);
+  hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
+                     static_cast<T*>(nullptr), static_cast<T*>(nullptr), (size_t)0, tiles_m);
+  hipLaunchKernelGGL(k_gramchol, dim3(nmat), dim3(kCholThreads), lds_chol, st, ws.Y, M, dm.ell, ellp,
+                     ws.Rinv, Racc, Racc);
+  hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
+                     static_cast<T*>(XT), static_cast<T*>(XTlo), (size_t)ellp * ws.M, tiles_m);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStream_t st) {
+  const Dims& dm = c->dm;
+  CompressWs ws;
+  ws.nmat = 2 * dm.B;
+  ws.M = std::max(dm.N, dm.W);
+  ws.ellp = (dm.ell + 15) / 16 * 16;
+  if (ws.ellp > kMaxEll) {
+    set_error("ap_compress: ell = min(rank + oversample, n_tokens, width) must be <= 128");
+    return hipErrorNotSupported;
+  }
+  const int nmat = ws.nmat, ellp = ws.ellp;
+  const size_t es = sizeof(T);
+  struct Buf { void** p; size_t bytes; };
+  Buf bufs[] = {
+      {&ws.omT, (size_t)nmat * ellp * dm.W * es},
+      {reinterpret_cast<void**>(&ws.Y), (size_t)nmat * ws.M * ellp * 4},
+      {&ws.XT, (size_t)nmat * ellp * ws.M * es},
+      {&ws.XTlo, std::is_same<T, bf16_t>::value ? (size_t)nmat * ellp * ws.M * es : 0},
+      {reinterpret_cast<void**>(&ws.Qn), (size_t)nmat * dm.N * ellp * 4},
+      {reinterpret_cast<void**>(&ws.Qc), (size_t)nmat * dm.W * ellp * 4},
+      {reinterpret_cast<void**>(&ws.Rinv), (size_t)nmat * ellp * ellp * 4},
+      {reinterpret_cast<void**>(&ws.Racc), (size_t)nmat * ellp * ellp * 4},
+      {reinterpret_cast<void**>(&ws.PS), (size_t)nmat * ellp * ellp * 4},
+      {reinterpret_cast<void**>(&ws.Sv), (size_t)nmat * ellp * ellp * 4},
+      {reinterpret_cast<void**>(&ws.sig), (size_t)nmat * ellp * 4},
+  };
+  hipError_t e = hipSuccess;
+  for (Buf& bf : bufs) {
+    if (bf.bytes == 0) continue;
+    e = hipMallocAsync(bf.p, bf.bytes, st);
+    if (e != hipSuccess) break;
+  }
+  auto release = [&]() {
+    for (Buf& bf : bufs)
+      if (*bf.p) (void)hipFreeAsync(*bf.p, st);
+  };
+  if (e != hipSuccess) {
+    set_error("compress workspace allocation failed");
+    release();
+    return hipErrorOutOfMemory;
+  }
+  auto fail_stage = [&](hipError_t err, const char* stage) {
+    set_error(std::string("ap_compress, ") + stage + ": " + hipGetErrorString(err));
+    release();
+    return err;
+  };
+  // padded rows of Omega^T and X^T must read as zero
+  e = hipMemsetAsync(ws.omT, 0, (size_t)nmat * ellp * dm.W * es, st);
+  if (e == hipSuccess) e = hipMemsetAsync(ws.XT, 0, (size_t)nmat * ellp * ws.M * es, st);
+  if (e == hipSuccess && ws.XTlo) e = hipMemsetAsync(ws.XTlo, 0, (size_t)nmat * ellp * ws.M * es, st);
+  if (e != hipSuccess) return fail_stage(e, "workspace clear");
+  if (c->params.omega != nullptr)
+    hipLaunchKernelGGL(k_omega_copy<T>, grid_1d((size_t)nmat * dm.ell * dm.W), dim3(256), 0, st,
+                       c->params.omega, static_cast<T*>(ws.omT), nmat, dm.W, dm.ell, ellp);
+  else
+    hipLaunchKernelGGL(k_omega_philox<T>, grid_1d((size_t)nmat * ((dm.ell * (size_t)dm.W + 127) / 128)),
+                       dim3(256), 0, st, static_cast<T*>(ws.omT), nmat, dm.W, dm.ell, ellp, c->params.seed);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail_stage(e, "test matrix");
+
+  // dynamic LDS above the 64 KB default: request exactly what each launch uses
+  const size_t lds_chol = (size_t)2 * ellp * (ellp + 1) * sizeof(float);
+  const size_t lds_jac = (size_t)(2 * ellp * (ellp + 1) + 2 * ellp) * sizeof(float);
+  const size_t lds_apply = (size_t)(64 * (ellp + 1) + ellp * ellp) * sizeof(float);
+  const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP) * sizeof(float);
+  const struct { const void* fn; size_t bytes; const char* name; } lds_req[] = {
+      {reinterpret_cast<const void*>(&k_gramchol), lds_chol, "LDS size of k_gramchol"},
+      {reinterpret_cast<const void*>(&k_jacobi), lds_jac, "LDS size of k_jacobi"},
+      {reinterpret_cast<const void*>(&k_apply<T>), lds_apply, "LDS size of k_apply"},
+      {reinterpret_cast<const void*>(&k_assemble_u<T>), lds_u, "LDS size of k_assemble_u"},
+  };
+  for (const auto& rq : lds_req) {
+    e = hipFuncSetAttribute(rq.fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rq.bytes));
+    if (e != hipSuccess) return fail_stage(e, rq.name);
+  }
+  // Y = A Omega ; Q = orth(Y)
+  // The last basis of range(A) also keeps its bf16 rounding remainder, so that the
+  // projection C^T = A^T Q is taken with Q to about 16 bits (U is built from the
+  // fp32 Q; with Q rounded to 8 bits here the two would disagree at 2^-9).
+  e = gemm<T>(c, k, v, ws.omT, nullptr, ws.Y, false, (size_t)ellp * dm.W, st);
+  if (e != hipSuccess) return fail_stage(e, "A Omega");
+  e = orth<T>(c, ws, dm.N, ws.XT, dm.q == 0 ? ws.XTlo : nullptr, nullptr, st);
+  if (e != hipSuccess) return fail_stage(e, "orthonormalisation of A Omega");
+  for (int it = 0; it < dm.q; ++it) {
+    e = gemm<T>(c, k, v, ws.XT, nullptr, ws.Y, true, (size_t)ellp * ws.M, st);     // A^T Q
+    if (e == hipSuccess) e = orth<T>(c, ws, dm.W, ws.XT, nullptr, nullptr, st);
+    if (e == hipSuccess) e = gemm<T>(c, k, v, ws.XT, nullptr, ws.Y, false, (size_t)ellp * ws.M, st);  // A Q~
+    if (e == hipSuccess) e = orth<T>(c, ws, dm.N, ws.XT, it == dm.q - 1 ? ws.XTlo : nullptr, nullptr, st);
+    if (e != hipSuccess) return fail_stage(e, "power iteration");
+  }
+  // keep Q (fp32) for U, then C^T = A^T Q and its QR
+  e = hipMemcpyAsync(ws.Qn, ws.Y, (size_t)nmat * dm.N * ellp * 4, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess) e = gemm<T>(c, k, v, ws.XT, ws.XTlo, ws.Y, true, (size_t)ellp * ws.M, st);
+  if (e == hipSuccess) e = orth<T>(c, ws, dm.W, nullptr, nullptr, ws.Racc, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(ws.Qc, ws.Y, (size_t)nmat * dm.W * ellp * 4, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return fail_stage(e, "projection C^T = A^T Q");
+  hipLaunchKernelGGL(k_jacobi, dim3(nmat), dim3(kJacThreads), lds_jac, st, ws.Racc, dm.ell, ellp, ws.PS,
+                     ws.Sv, ws.sig);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail_stage(e, "core SVD");
+  hipLaunchKernelGGL(k_assemble_u<T>, dim3(nmat * dm.nblk), dim3(256), lds_u, st, ws.Qn, ws.PS,
+                     static_cast<T*>(c->Uk), dm.N, ellp, dm.r, dm.NP, dm.nblk);
+  const int tiles_w = (dm.W + 255) / 256;
+  hipLaunchKernelGGL(k_assemble_b<T>, dim3(nmat * tiles_w), dim3(256), 0, st, ws.Qc, ws.Sv,
+                     static_cast<T*>(c->Bk), static_cast<T*>(c->Bv), dm.W, ellp, dm.r, dm.r_pad, tiles_w);
+  hipLaunchKernelGGL(k_copy_sigma, grid_1d((size_t)nmat * dm.r), dim3(256), 0, st, ws.sig, c->sigma_k,
+                     c->sigma_v, nmat, ellp, dm.r);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = launch_rownorm(c, st);
+  if (e != hipSuccess) return fail_stage(e, "factor assembly");
+  release();
+  return e;
+}
+
 hipError_t run_compress(ap_cache* c, const void* k, const void* v, hipStream_t st) {
-  (void)c; (void)k; (void)v; (void)st;
-  set_error("the device compressor is not built yet; load factors with ap_cache_set_factors");
-  return hipErrorNotSupported;
+  if (c->dm.storage == AP_BF16) return compress_t<bf16_t>(c, k, v, st);
+  return compress_t<float>(c, k, v, st);
 }
 
 }  // namespace ap

@@ -75,3 +75,15 @@ def test_null_arguments():
     b.lib.ap_free(None)
     assert b.lib.ap_status_string(b.AP_ERR_UNSUPPORTED) == b"unsupported"
     assert b"n_kv_heads" in b.lib.ap_last_error() or b.lib.ap_last_error() != b""
+
+
+def test_compress_rejects_large_probe_count_before_touching_memory():
+    # ell = min(r + p, N, W) = 144 > 128: refused during validation, so the (never
+    # dereferenced) fake device pointers are safe on a machine without a GPU
+    from rank_compressed_kv_ap_amd import binding as b
+    p = b.CompressParams(1, 512, 4, 4, 64, 128, 16, 2, b.AP_BF16, 0, 0, None)
+    out = ctypes.c_void_p(1)
+    st = b.lib.ap_compress(ctypes.c_void_p(256), ctypes.c_void_p(512), ctypes.byref(p), None,
+                           ctypes.byref(out))
+    assert st == b.AP_ERR_UNSUPPORTED and out.value is None
+    assert b"128" in b.lib.ap_last_error()

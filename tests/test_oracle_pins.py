@@ -317,3 +317,34 @@ def test_round_to_storage_bf16_known_values():
     t = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(y, t)
     assert np.array_equal(wl.round_bf16(x).astype(np.float64), t)
+
+
+def _kat():
+    import json
+    path = os.path.join(os.path.dirname(__file__), "golden", "philox_kat.json")
+    return json.load(open(path))["vectors"]
+
+
+def test_p12_philox_known_answers():
+    """Philox4x32-10 reproduces the generator's published known-answer vectors."""
+    from oracle.philox import philox4x32_10
+    for v in _kat():
+        got = philox4x32_10([int(x, 16) for x in v["counter"]], [int(x, 16) for x in v["key"]])
+        assert ["%08x" % g for g in got] == v["out"]
+
+
+def test_p12_sign_matrix_layout_from_known_answer():
+    """With seed 0 and matrix 0 the first 128 entries (column 0 of a W = 128 matrix)
+    are the bits of the all-zero known answer: bit t of word t//32 set -> -1."""
+    from oracle.philox import sign_omega
+    words = [int(x, 16) for x in _kat()[0]["out"]]
+    om = sign_omega(0, 0, 128, 2)
+    for t in range(128):
+        want = -1.0 if (words[t // 32] >> (t % 32)) & 1 else 1.0
+        assert om[t, 0] == want
+    # different matrices and seeds give different, balanced signs
+    a, b = sign_omega(5, 0, 64, 40), sign_omega(5, 1, 64, 40)
+    c = sign_omega(6, 0, 64, 40)
+    assert set(np.unique(a)) == {-1.0, 1.0}
+    assert not np.array_equal(a, b) and not np.array_equal(a, c)
+    assert abs(a.mean()) < 0.1 and abs(np.mean(a * b)) < 0.1
