@@ -5,13 +5,21 @@
 Workload: the LLaVA-7B-like layer (batch 32, 32 heads of 128, 2880 visual tokens
 factored at rank 64 with 64 dense text tokens, r_lo = 16, 25% of tokens at full
 rank, bf16 factors).  One step = one ap_decode_attn call over the batch (latent
-query, low-rank scores, per-head top-k, mixed-rank flash-decode, combine).  The
-factored caches are built on the device before timing; R copies are rotated so
-the 256 MB MALL cannot hold the working set.
+query, low-rank scores, per-head top-k, mixed-rank flash-decode, dense text,
+combine).  The factored caches are built on the device before timing; R copies
+are rotated so that the 256 MB MALL cannot hold the working set.
 
-Prints one JSON line: tokens attended/s for the whole GPU, the per-kernel HIP-event
-breakdown, the dominant kernel's roofline, and the CPU oracle timed on a bounded
-sample on this host.
+Timed regions, in order:
+  1. the headline: K steps with nothing else on the stream (wall clock around
+     synchronisations, and HIP events on the launch stream as a cross-check);
+  2. K more steps with the library's per-kernel HIP events (ap_timing_*) for the
+     kernel breakdown and the dominant kernel's roofline;
+  3. the compressor: ap_recompress of the same batch's K and V (randomized
+     subspace iteration), which runs once per cache, not per step;
+  4. the CPU oracle's decode step on a bounded sample of the same sequences.
+
+Prints one JSON line.  `--calib-copy` instead runs only a plain device copy of a
+known size (the calibration run for the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -28,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
+METRIC = "compressed-KV decode attention: tokens attended/s + HBM GB/s (% of peak), batch 32"
 
 
 def parse():
@@ -37,13 +46,20 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cfg", type=int, default=2, help="workload id (2 = the batch-32 LLaVA layer)")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-compress", action="store_true")
+    ap.add_argument("--compress-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 10 times (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
+                    help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this "
+                         "bench and of --calib-copy into profiles/traffic_<workload>.json")
     return ap.parse_args()
 
 
 def kernel_bytes(w):
-    """Algorithmic bytes per sequence read/written by each kernel of one step."""
+    """Algorithmic bytes per sequence read/written by each decode kernel."""
     s = 2 if w.storage == "bf16" else 4
     W, r, N, T = w.width, w.rank, w.n_tokens, w.n_text
     qb = 4 * w.n_q_heads * w.head_dim
@@ -54,6 +70,68 @@ def kernel_bytes(w):
     }
 
 
+def compress_bytes(w):
+    """Algorithmic bytes of one ap_compress/ap_recompress over the batch: 2q + 2
+    passes over every K and V matrix (A Omega, q times A^T Q and A Q~, A^T Q)."""
+    s = 2 if w.storage == "bf16" else 4
+    return (2 * w.power_iters + 2) * 2 * w.batch * w.n_tokens * w.width * s
+
+
+# Sources whose change invalidates measured decode traffic.
+DECODE_SOURCES = ["rank_compressed_kv_ap_amd/csrc/select_kernel.hip",
+                  "rank_compressed_kv_ap_amd/csrc/decode_kernels.hip",
+                  "rank_compressed_kv_ap_amd/csrc/device_common.h",
+                  "rank_compressed_kv_ap_amd/csrc/tiles.h",
+                  "rank_compressed_kv_ap_amd/csrc/ap_internal.h",
+                  "rank_compressed_kv_ap_amd/csrc/api.hip"]
+KERNEL_SYMBOL = {"select": "k_select", "attn": "k_attn", "combine": "k_combine"}
+
+
+def write_traffic(cfg, fetch_csv, write_csv, cfetch_csv, cwrite_csv):
+    """HBM bytes per launch of each decode kernel from two counter runs (FETCH_SIZE,
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
+    plain device copy of 1 GiB (the copy reads and writes exactly 2^30 bytes)."""
+    import csv
+
+    from rank_compressed_kv_ap_amd import workloads as wl
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+
+    def copy_kib(path, counter):
+        vals = [v for name, vs in per_kernel(path, counter).items() if "copyBuffer" in name for v in vs]
+        return sum(vals) / len(vals)
+
+    f_scale = (1 << 30) / 1024 / copy_kib(cfetch_csv, "FETCH_SIZE")
+    w_scale = (1 << 30) / 1024 / copy_kib(cwrite_csv, "WRITE_SIZE")
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    w = wl.WORKLOADS[cfg]
+    kb = kernel_bytes(w)
+    kernels = {}
+    for k, sym in KERNEL_SYMBOL.items():
+        fv = [v for name, vs in fetch.items() if f"ap::{sym}<" in name for v in vs]
+        wv = [v for name, vs in write.items() if f"ap::{sym}<" in name for v in vs]
+        if not fv or not wv:
+            continue
+        fb = 1024 * f_scale * sum(fv) / len(fv)
+        wb = 1024 * w_scale * sum(wv) / len(wv)
+        kernels[k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                      "algorithmic_bytes_per_launch": w.batch * kb[k], "dispatches": len(fv)}
+    out = {"workload": w.name, "kernels": kernels,
+           "calibration": {"fetch_scale": f_scale, "write_scale": w_scale,
+                           "copy_bytes": 1 << 30},
+           "sources": DECODE_SOURCES, "source_digest": source_digest(DECODE_SOURCES)}
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def source_digest(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -61,11 +139,29 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
+def calib_copy():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 10}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+    if args.write_traffic:
+        write_traffic(args.cfg, *args.write_traffic)
+        return
 
     import numpy as np
     import torch
@@ -110,15 +206,24 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, HIP events around every kernel on the launch stream
-    for c in caches:
-        c.timing_enable(math.ceil(args.steps / R) + 1)
+    # ---- 1. headline: K steps, nothing else on the stream
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    event_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- 2. per-kernel breakdown: K steps with HIP events around every kernel
+    for c in caches:
+        c.timing_enable(math.ceil(args.steps / R) + 1)
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     kms = {k: 0.0 for k in binding.KERNEL_NAMES}
     ncalls = 0
     for c in caches:
@@ -126,6 +231,7 @@ def main():
         ncalls += n
         for k in kms:
             kms[k] += ms[k]
+        c.timing_enable(0)
     kernel_avg_ms = {k: v / max(ncalls, 1) for k, v in kms.items()}
 
     ms_per_step = 1e3 * elapsed / args.steps
@@ -139,11 +245,12 @@ def main():
     tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     if os.path.exists(tfile):
         t = json.load(open(tfile))
-        if t.get("kernel") == dom and t.get("source_digest") == source_digest(t.get("sources", [])):
-            traffic = t.get("bytes_per_launch")
+        k = t.get("kernels", {}).get(dom)
+        if k is not None and t.get("source_digest") == source_digest(t.get("sources", [])):
+            traffic = k.get("bytes_per_launch")
 
     result = {
-        "metric": "compressed-KV decode attention: tokens attended/s + HBM GB/s (% of peak), batch 32",
+        "metric": METRIC,
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -159,6 +266,7 @@ def main():
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "rank": w.rank, "r_lo": w.r_lo, "top_k": w.top_k, "storage": w.storage,
                    "cache_copies_rotated": R, "distinct_sequences": S},
+        "ms_per_step_hip_events": event_ms,
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "GB/s": step_bytes / (elapsed / args.steps) / 1e9,
                 "frac_of_peak": step_bytes / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBPS},
@@ -170,16 +278,45 @@ def main():
 
     for c in caches:
         c.free()
+    del caches, qs, texts
+
+    if not args.no_compress:
+        result["compress"] = compress_leg(w, args.compress_reps, binding, wl, np, torch)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, seqs, args.cpu_seconds)
     print(json.dumps(result))
 
 
+def compress_leg(w, reps, binding, wl, np, torch):
+    """ap_recompress of the whole batch (2 distinct sequences tiled), HIP events on
+    the launch stream; the first call (workspace pool warm-up) is not timed."""
+    dt = torch.bfloat16 if w.storage == "bf16" else torch.float32
+    S = min(w.batch, 2)
+    idx = torch.tensor([b % S for b in range(w.batch)], device="cuda")
+    k = torch.from_numpy(np.stack([wl.gen_kv(w, b, 0) for b in range(S)])).to(dt).cuda()[idx].contiguous()
+    v = torch.from_numpy(np.stack([wl.gen_kv(w, b, 1) for b in range(S)])).to(dt).cuda()[idx].contiguous()
+    c = binding.compress(k, v, batch=w.batch, n_tokens=w.n_tokens, n_kv_heads=w.n_kv_heads,
+                         n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=w.rank, storage=dt,
+                         oversample=w.oversample, power_iters=w.power_iters, seed=1)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(reps):
+        c.recompress(k, v, seed=2 + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    c.free()
+    nbytes = compress_bytes(w)
+    return {"ms": ms, "reps": reps, "matrices": 2 * w.batch, "ell": w.ell,
+            "power_iters": w.power_iters, "algorithmic_bytes": nbytes,
+            "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
 def cpu_baseline(w, seqs, budget_s):
     """The oracle's decode step (explicit decompression + dense softmax, float64) on
     this host, on as many of the distinct sequences as fit the time budget."""
-    import os as _os
     from threadpoolctl import threadpool_info
 
     from oracle.decode import decode_ref
@@ -195,7 +332,7 @@ def cpu_baseline(w, seqs, budget_s):
     return {"value": done * (w.n_tokens + w.n_text) / el, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{done} sequences of the {w.name} workload (one decode step each), "
-                      f"{el:.1f} s on {_os.cpu_count()} visible host CPUs"}
+                      f"{el:.1f} s on {os.cpu_count()} visible host CPUs"}
 
 
 if __name__ == "__main__":

@@ -100,6 +100,19 @@ typedef struct ap_cache ap_cache;
 ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p,
                       void* stream, ap_cache** out);
 
+/* Factor new K and V of the cache's own shape into an existing cache, replacing its
+ * factors and singular values (a serving slot reused for another batch).  Same
+ * method, layout and limits as ap_compress ([fr §2.A], [es §2.A], [de §2.A]); the
+ * cache's decode workspace is kept, only the factorisation workspace is taken
+ * (stream-ordered) and released on `stream`.
+ * k, v:   device [B][N][W] in the cache's storage dtype, caller-owned, read on `stream`.
+ * omega:  optional device [B][2][W][ell] float32 test matrices (as in
+ *         ap_compress_params); NULL: random signs from `seed`, as ap_compress draws them.
+ * Errors: AP_ERR_NULL_ARG, AP_ERR_UNSUPPORTED (ell > 128), AP_ERR_OUT_OF_MEMORY,
+ *         AP_ERR_HIP.  On an error the factors are unspecified. */
+ap_status ap_recompress(ap_cache* c, const void* k, const void* v, const float* omega, uint64_t seed,
+                        void* stream);
+
 /* Load factors into a cache: U_k, U_v device [B][N][r], B_k, B_v device [B][r][W],
  * row-major, in the cache's storage dtype, caller-owned, read on `stream`.  The
  * layout is the plain one of [fr §2.A "Mécanisme"] (K ~= U_k B_k); the cache keeps

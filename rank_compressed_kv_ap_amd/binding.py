@@ -22,9 +22,9 @@ AP_F32, AP_BF16 = 0, 1
 KERNEL_NAMES = ("select", "attn", "combine")
 
 EXPORTED = (
-    "ap_compress", "ap_cache_set_factors", "ap_cache_get_factors", "ap_cache_get_sigma",
-    "ap_cache_info", "ap_decode_attn", "ap_free", "ap_timing_enable", "ap_timing_read",
-    "ap_status_string", "ap_last_error",
+    "ap_compress", "ap_recompress", "ap_cache_set_factors", "ap_cache_get_factors",
+    "ap_cache_get_sigma", "ap_cache_info", "ap_decode_attn", "ap_free", "ap_timing_enable",
+    "ap_timing_read", "ap_status_string", "ap_last_error",
 )
 
 
@@ -51,6 +51,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.ap_compress.argtypes = [vp, vp, ctypes.POINTER(CompressParams), vp, ctypes.POINTER(vp)]
+    lib.ap_recompress.argtypes = [vp, vp, vp, vp, ctypes.c_uint64, vp]
     lib.ap_cache_set_factors.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.ap_cache_get_factors.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.ap_cache_get_sigma.argtypes = [vp, vp, vp, vp]
@@ -65,7 +66,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ap_status_string.restype = ctypes.c_char_p
     lib.ap_last_error.argtypes = []
     lib.ap_last_error.restype = ctypes.c_char_p
-    for name in ("ap_compress", "ap_cache_set_factors", "ap_cache_get_factors", "ap_cache_get_sigma",
+    for name in ("ap_compress", "ap_recompress", "ap_cache_set_factors", "ap_cache_get_factors", "ap_cache_get_sigma",
                  "ap_cache_info", "ap_decode_attn", "ap_timing_enable", "ap_timing_read"):
         getattr(lib, name).restype = i32
     return lib
@@ -136,6 +137,12 @@ class Cache:
     def width(self): return self.params.n_kv_heads * self.params.head_dim
     @property
     def dtype(self): return torch_dtype(self.params.storage)
+
+    def recompress(self, k: torch.Tensor, v: torch.Tensor, *, seed: int = 0,
+                   omega: Optional[torch.Tensor] = None) -> None:
+        """ap_recompress: factor new k, v [B, N, W] into this cache."""
+        _check(lib.ap_recompress(self.handle, _ptr(k), _ptr(v), _ptr(omega), seed, _stream()),
+               "ap_recompress")
 
     def set_factors(self, U_k, B_k, U_v, B_v) -> None:
         _check(lib.ap_cache_set_factors(self.handle, _ptr(U_k), _ptr(B_k), _ptr(U_v), _ptr(B_v),

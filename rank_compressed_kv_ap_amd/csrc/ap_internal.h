@@ -64,13 +64,20 @@ namespace ap {
 
 void set_error(const std::string& msg);
 
+// Events that a launch's own dispatch timestamps at the kernel's start and end
+// (hipExtLaunchKernelGGL), or null for an untimed launch.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // ---- launchers (decode_kernels.hip, select_kernel.hip)
 hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
-                         int32_t* sel_out, hipStream_t st);
+                         int32_t* sel_out, hipStream_t st, const KernelEvents& ev);
 hipError_t launch_attn(const ap_cache* c, int r_lo, float scale_log2e, int S, int CB,
-                       hipStream_t st);
+                       hipStream_t st, const KernelEvents& ev);
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float scale_log2e,
-                          int S, int T, const void* text_k, const void* text_v, hipStream_t st);
+                          int S, int T, const void* text_k, const void* text_v, hipStream_t st,
+                          const KernelEvents& ev);
 
 // ---- launchers (select_kernel.hip)
 int select_heads_per_group(const Dims& dm);

@@ -195,6 +195,32 @@ ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p,
   return AP_OK;
 }
 
+ap_status ap_recompress(ap_cache* c, const void* k, const void* v, const float* omega, uint64_t seed,
+                        void* stream) {
+  if (!c || !k || !v) return fail(AP_ERR_NULL_ARG, "cache, k and v must not be NULL");
+  const Dims& dm = c->dm;
+  const int ell = std::min(std::min(dm.r + dm.p, dm.N), dm.W);
+  if (ell > 128) return fail(AP_ERR_UNSUPPORTED, "min(rank + oversample, n_tokens, width) must be <= 128");
+  if (dm.B == 0) return AP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  c->last_stream = st;
+  set_error("");
+  c->params.omega = omega;
+  const uint64_t seed0 = c->params.seed;
+  c->params.seed = seed;
+  hipError_t e = run_compress(c, k, v, st);
+  c->params.omega = nullptr;
+  if (e != hipSuccess) {
+    c->params.seed = seed0;
+    std::string detail = g_last_error;
+    if (e == hipErrorOutOfMemory) return fail(AP_ERR_OUT_OF_MEMORY, "compress workspace: " + detail);
+    if (e == hipErrorNotSupported) return fail(AP_ERR_UNSUPPORTED, detail);
+    return fail(AP_ERR_HIP, std::string("compress: ") + hipGetErrorString(e) +
+                                (detail.empty() ? std::string() : " (" + detail + ")"));
+  }
+  return AP_OK;
+}
+
 ap_status ap_cache_set_factors(ap_cache* c, const void* U_k, const void* B_k, const void* U_v,
                                const void* B_v, void* stream) {
   if (!c || !U_k || !B_k || !U_v || !B_v) return fail(AP_ERR_NULL_ARG, "cache and all factor pointers must be set");
@@ -278,19 +304,19 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
   const float sl2 = p->scale * kLog2eHost;
   TimingState& tm = c->timing;
   const bool timed = tm.max_calls > 0 && tm.calls < tm.max_calls;
-  auto mark = [&](int kernel, int edge) -> hipError_t {
-    if (!timed) return hipSuccess;
-    return hipEventRecord(tm.ev[((size_t)tm.calls * AP_N_KERNELS + kernel) * 2 + edge], st);
+  // timed calls: each kernel's own dispatch stamps its start and end events
+  auto events = [&](int kernel) {
+    KernelEvents ev;
+    if (timed) {
+      ev.start = tm.ev[((size_t)tm.calls * AP_N_KERNELS + kernel) * 2];
+      ev.stop = tm.ev[((size_t)tm.calls * AP_N_KERNELS + kernel) * 2 + 1];
+    }
+    return ev;
   };
-  hipError_t e = mark(AP_KERNEL_SELECT, 0);
-  if (e == hipSuccess) e = launch_select(c, q, p->r_lo, p->top_k, p->sel_out, st);
-  if (e == hipSuccess) e = mark(AP_KERNEL_SELECT, 1);
-  if (e == hipSuccess) e = mark(AP_KERNEL_ATTN, 0);
-  if (e == hipSuccess) e = launch_attn(c, p->r_lo, sl2, S, CB, st);
-  if (e == hipSuccess) e = mark(AP_KERNEL_ATTN, 1);
-  if (e == hipSuccess) e = mark(AP_KERNEL_COMBINE, 0);
-  if (e == hipSuccess) e = launch_combine(c, q, out, sl2, S, p->n_text, p->text_k, p->text_v, st);
-  if (e == hipSuccess) e = mark(AP_KERNEL_COMBINE, 1);
+  hipError_t e = launch_select(c, q, p->r_lo, p->top_k, p->sel_out, st, events(AP_KERNEL_SELECT));
+  if (e == hipSuccess) e = launch_attn(c, p->r_lo, sl2, S, CB, st, events(AP_KERNEL_ATTN));
+  if (e == hipSuccess)
+    e = launch_combine(c, q, out, sl2, S, p->n_text, p->text_k, p->text_v, st, events(AP_KERNEL_COMBINE));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (timed) tm.calls++;
   return AP_OK;

@@ -14,7 +14,8 @@
 // Kernels:
 //   k_gemm_n / k_gemm_t   Y = A X, Y = A^T X (X given transposed, k contiguous); bf16 MFMA
 //                         16x16x32 with A tiles staged in LDS (transposed for A^T); fp32 out
-//   k_gramchol            Gram Y^T Y (fp32 MFMA), shifted Cholesky, inverse of R
+//   k_gram / k_chol       Gram Y^T Y (fp32 MFMA, split over rows), shifted Cholesky,
+//                         inverse of the triangular factor
 //   k_apply               Q = Y R^-1 in place (fp32 MFMA), plus Q^T in storage precision
 //   k_jacobi              one-sided Jacobi SVD of R^T in LDS, components sorted by sigma
 //   k_assemble_u / _b     factors in the decode layouts
@@ -41,6 +42,7 @@ struct CompressWs {
   void* XTlo = nullptr;               // [nmat][ellp][M]   its rounding remainder (bf16 only)
   float* Qn = nullptr;                // [nmat][N][ellp]   final range basis of A
   float* Qc = nullptr;                // [nmat][W][ellp]   basis of C^T
+  float* Gpart = nullptr;             // [nmat][nsplit][ellp][ellp] partial Grams
   float* Rinv = nullptr;              // [nmat][ellp][ellp]
   float* Racc = nullptr;              // [nmat][ellp][ellp] R of the last orthonormalisation
   float* PS = nullptr;                // [nmat][ellp][ellp] P Sigma (columns sorted)
@@ -66,25 +68,27 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint2 k) {
 // matrix mat (sub-Gaussian test matrices: Halko, Martinsson & Tropp 2011, §4.6).
 // Linear index i = j*W + w; one Philox call with counter (i/128, mat, 0, 0) and key
 // (seed lo, seed hi) yields 128 bits for elements 128*(i/128) ..; bit i%32 of word
-// (i/32)%4 set means -1.  One thread per 128-element block.
+// (i/32)%4 set means -1.  One thread per 8 consecutive elements (the 16 threads of
+// a 128-element block each evaluate its Philox call).
 template <class T>
 __global__ __launch_bounds__(256) void k_omega_philox(T* __restrict__ omT, int nmat, int W, int ell,
                                                       int ellp, uint64_t seed) {
   const size_t per = (size_t)ell * W;
-  const size_t blocks = (per + 127) / 128;
+  const size_t groups = (per + 7) / 8;
   const uint2 key = make_uint2(static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
-  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < blocks * nmat;
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups * nmat;
        g += (size_t)gridDim.x * blockDim.x) {
-    const int mat = static_cast<int>(g / blocks);
-    const size_t blk = g % blocks;
+    const int mat = static_cast<int>(g / groups);
+    const size_t i0 = 8 * (g % groups);
+    const size_t blk = i0 / 128;
     const uint4 x = philox4x32_10(make_uint4(static_cast<uint32_t>(blk), static_cast<uint32_t>(mat), 0u, 0u), key);
-    const uint32_t words[4] = {x.x, x.y, x.z, x.w};
-    const size_t i0 = 128 * blk;
-    const int cnt = static_cast<int>(per - i0 < 128 ? per - i0 : 128);
+    const int t0 = static_cast<int>(i0 % 128);
+    const uint32_t word = (t0 >> 5) == 0 ? x.x : ((t0 >> 5) == 1 ? x.y : ((t0 >> 5) == 2 ? x.z : x.w));
+    const uint32_t bits = (word >> (t0 & 31)) & 0xffu;
     int j = static_cast<int>(i0 / W), w = static_cast<int>(i0 % W);
+    const int cnt = static_cast<int>(per - i0 < 8 ? per - i0 : 8);
     for (int t = 0; t < cnt; ++t) {
-      const bool neg = (words[t >> 5] >> (t & 31)) & 1u;
-      omT[((size_t)mat * ellp + j) * W + w] = from_f32<T>(neg ? -1.f : 1.f);
+      omT[((size_t)mat * ellp + j) * W + w] = from_f32<T>(((bits >> t) & 1u) ? -1.f : 1.f);
       if (++w == W) { w = 0; ++j; }
     }
   }
@@ -252,40 +256,41 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ Kmat
 }
 
 // ================================================================ orthonormalisation
-// One workgroup per matrix: G = Y^T Y (fp32 MFMA 16x16x4 over the M rows), a shifted
-// Cholesky G + eps I = L L^T in LDS, and Rinv = L^-T (so that Y Rinv is orthonormal).
-// When Rprev is given the product R = L^T Rprev is written as well (two-pass QR).
-constexpr int kCholThreads = 256;
+// Shifted Cholesky QR, two passes (CholeskyQR2 with a shift on the first Gram, in the
+// spirit of Fukaya et al. 2020): G = Y^T Y, G + eps I = L L^T, Q = Y L^-T.
+//
+// k_gram: partial Grams.  Workgroup (mat, split) takes rows [split*rows, +rows) of
+// Y [M][ellp]; each wavefront accumulates every upper 16x16 tile (fp32 MFMA 16x16x4,
+// one 4-row slice per k-step) over its quarter of them, the four are summed in LDS
+// and the workgroup writes Gpart[mat][split] (full, symmetric).  Deterministic:
+// the partials are summed in a fixed order by k_chol.
+constexpr int kGramThreads = 256;
 
-__global__ __launch_bounds__(kCholThreads) void k_gramchol(const float* __restrict__ Y, int M,
-                                                           int ell, int ellp, float* __restrict__ Rinv,
-                                                           const float* __restrict__ Rprev,
-                                                           float* __restrict__ Rout) {
+template <int T>   // ellp / 16
+__global__ __launch_bounds__(kGramThreads) void k_gram(const float* __restrict__ Y, int M, int ellp,
+                                                       int rows, int nsplit, float* __restrict__ Gpart) {
   extern __shared__ __align__(16) float sh[];
   const int S = ellp + 1;
-  float* G = sh;                 // [ellp][S] Gram, then L (lower)
-  float* Li = G + ellp * S;      // [ellp][S] L^-1
-  const int mat = blockIdx.x;
+  float* G = sh;   // [ellp][S]
+  const int mat = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
   const float* Ym = Y + (size_t)mat * M * ellp;
+  const int r0 = split * rows, r1 = min(M, r0 + rows);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int T = ellp / 16;
-  // Each wavefront accumulates every upper tile (ti <= tj) over its share of the rows:
-  // one 4-row slice of Y per MFMA k-step, all column tiles of it held in registers.
-  constexpr int kMaxT = kMaxEll / 16;
-  v4f acc[kMaxT * (kMaxT + 1) / 2];
+  v4f acc[T * (T + 1) / 2];
 #pragma unroll
-  for (int t = 0; t < kMaxT * (kMaxT + 1) / 2; ++t) acc[t] = v4f{0, 0, 0, 0};
-  constexpr int UR = 4;   // k-steps whose loads are in flight together
-  for (int n0 = 4 * UR * wave; n0 < M; n0 += 4 * UR * 4) {
-    float y[UR][kMaxT];
+  for (int t = 0; t < T * (T + 1) / 2; ++t) acc[t] = v4f{0, 0, 0, 0};
+  constexpr int UR = 4;   // 4-row k-steps whose loads are in flight together
+  for (int n0 = r0 + 4 * UR * wave; n0 < r1; n0 += 4 * UR * 4) {
+    float y[UR][T];
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
-      const int n = min(n0 + 4 * u + lg, M - 1);
-      const bool live = n0 + 4 * u + lg < M;
+      const int n = n0 + 4 * u + lg;
+      const bool live = n < r1;
+      const float* row = Ym + (size_t)(live ? n : r0) * ellp + l16;
 #pragma unroll
-      for (int t = 0; t < kMaxT; ++t) {
-        const float v = t < T ? Ym[(size_t)n * ellp + 16 * t + l16] : 0.f;
+      for (int t = 0; t < T; ++t) {
+        const float v = row[16 * t];
         y[u][t] = live ? v : 0.f;
       }
     }
@@ -293,20 +298,18 @@ __global__ __launch_bounds__(kCholThreads) void k_gramchol(const float* __restri
     for (int u = 0; u < UR; ++u) {
       int idx = 0;
 #pragma unroll
-      for (int ti = 0; ti < kMaxT; ++ti)
+      for (int ti = 0; ti < T; ++ti)
 #pragma unroll
-        for (int tj = ti; tj < kMaxT; ++tj, ++idx)
-          if (tj < T) acc[idx] = mfma_f32(y[u][ti], y[u][tj], acc[idx]);
+        for (int tj = ti; tj < T; ++tj, ++idx) acc[idx] = mfma_f32(y[u][ti], y[u][tj], acc[idx]);
     }
   }
   for (int w = 0; w < 4; ++w) {
     if (wave == w) {
       int idx = 0;
 #pragma unroll
-      for (int ti = 0; ti < kMaxT; ++ti)
+      for (int ti = 0; ti < T; ++ti)
 #pragma unroll
-        for (int tj = ti; tj < kMaxT; ++tj, ++idx) {
-          if (tj >= T) continue;
+        for (int tj = ti; tj < T; ++tj, ++idx) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int i = 16 * ti + 4 * lg + t, j = 16 * tj + l16;
@@ -318,81 +321,190 @@ __global__ __launch_bounds__(kCholThreads) void k_gramchol(const float* __restri
     }
     __syncthreads();
   }
-  // diagonal tiles hold both triangles already; mirror their lower half for symmetry
-  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
+  float* out = Gpart + ((size_t)mat * nsplit + split) * ellp * ellp;
+  for (int idx = tid; idx < ellp * ellp; idx += kGramThreads) {
     const int i = idx / ellp, j = idx % ellp;
-    if ((i >> 4) == (j >> 4) && j < i) G[i * S + j] = G[j * S + i];
-  }
-  __syncthreads();
-  // shift: relative to the mean diagonal; padded columns get a unit diagonal
-  __shared__ float trace_sh;
-  if (tid == 0) {
-    float tr = 0.f;
-    for (int i = 0; i < ell; ++i) tr += G[i * S + i];
-    trace_sh = tr;
-  }
-  __syncthreads();
-  const float eps = 1e-6f * (trace_sh / static_cast<float>(ell > 0 ? ell : 1)) + 1e-30f;
-  for (int i = tid; i < ellp; i += kCholThreads) {
-    if (i < ell) {
-      G[i * S + i] += eps;
-    } else {
-      for (int j = 0; j < ellp; ++j) { G[i * S + j] = 0.f; G[j * S + i] = 0.f; }
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < ellp; i += kCholThreads)
-    if (i >= ell) G[i * S + i] = 1.f;
-  __syncthreads();
-  // right-looking Cholesky, lower triangle
-  for (int j = 0; j < ellp; ++j) {
-    if (tid == 0) G[j * S + j] = sqrtf(fmaxf(G[j * S + j], 1e-30f));
-    __syncthreads();
-    const float inv = 1.f / G[j * S + j];
-    for (int i = j + 1 + tid; i < ellp; i += kCholThreads) G[i * S + j] *= inv;
-    __syncthreads();
-    const int nt = ellp - j - 1;
-    for (int idx = tid; idx < nt * nt; idx += kCholThreads) {
-      const int i = j + 1 + idx / nt, k = j + 1 + idx % nt;
-      if (k <= i) G[i * S + k] -= G[i * S + j] * G[k * S + j];
-    }
-    __syncthreads();
-  }
-  // L^-1 by forward substitution, one column per thread
-  for (int c = tid; c < ellp; c += kCholThreads) {
-    for (int i = 0; i < ellp; ++i) {
-      float v = (i == c) ? 1.f : 0.f;
-      for (int k = c; k < i; ++k) v -= G[i * S + k] * Li[k * S + c];
-      Li[i * S + c] = i >= c ? v / G[i * S + i] : 0.f;
-    }
-  }
-  __syncthreads();
-  // Rinv = L^-T ; R = L^T (times Rprev).  Rprev is copied into LDS (over L^-1, after
-  // Rinv is written) before R is overwritten, since both may be the same buffer.
-  float* Ri = Rinv + (size_t)mat * ellp * ellp;
-  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
-    const int i = idx / ellp, j = idx % ellp;
-    Ri[idx] = Li[j * S + i];
-  }
-  if (Rout != nullptr) {
-    __syncthreads();
-    const float* Rp = Rprev ? Rprev + (size_t)mat * ellp * ellp : nullptr;
-    for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
-      const int i = idx / ellp, j = idx % ellp;
-      Li[i * S + j] = Rp ? Rp[idx] : (i == j ? 1.f : 0.f);
-    }
-    __syncthreads();
-    float* Ro = Rout + (size_t)mat * ellp * ellp;
-    for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
-      const int i = idx / ellp, j = idx % ellp;
-      float v = 0.f;
-      for (int k = i; k < ellp; ++k) v = fmaf(G[k * S + i], Li[k * S + j], v);
-      Ro[idx] = v;
-    }
+    out[idx] = G[i * S + j];
   }
 }
 
-// Q = Y Rinv for 64 rows per workgroup (fp32 MFMA), written in place; optionally
+// k_chol: one workgroup (4 wavefronts) per matrix, blocked over 16 x 16 tiles.
+// Sums the partial Grams, adds the shift eps = 1e-6 * trace / ell (padded columns
+// get a unit diagonal) and factors G + eps I = L L^T right-looking by block
+// columns: the diagonal block is factored and inverted in registers by wavefront 0
+// (lane i holds row i; values broadcast with readlane), the panel below it is
+// L_IJ = A_IJ L_JJ^-T and the trailing update A_IK -= L_IJ L_KJ^T, both on fp32
+// MFMA.  L^-1 follows by block forward substitution (X_IJ = -X_II sum_K L_IK X_KJ),
+// Rinv = L^-T is written, and when Rout is given R = L^T Rprev (Rprev NULL:
+// identity; Rprev may equal Rout: it is staged in LDS before R is written).
+constexpr int kCholThreads = 256;
+
+__device__ __forceinline__ float lane_bcast(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// acc += op(A) op(B) for 16 x 16 tiles of LDS matrices with row strides SA, SB.
+template <bool TA, bool TB, bool NEG>
+__device__ __forceinline__ v4f tile_mma(const float* MA, int ar, int ac, int SA, const float* MB, int br,
+                                        int bc, int SB, v4f acc, int l16, int lg) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    float a = TA ? MA[(ar + 4 * ks + lg) * SA + ac + l16] : MA[(ar + l16) * SA + ac + 4 * ks + lg];
+    const float b = TB ? MB[(br + l16) * SB + bc + 4 * ks + lg] : MB[(br + 4 * ks + lg) * SB + bc + l16];
+    if (NEG) a = -a;
+    acc = mfma_f32(a, b, acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ v4f tile_load(const float* M, int r0, int c0, int S, int l16, int lg) {
+  v4f d;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) d[t] = M[(r0 + 4 * lg + t) * S + c0 + l16];
+  return d;
+}
+__device__ __forceinline__ void tile_store(float* M, int r0, int c0, int S, int l16, int lg, v4f d) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) M[(r0 + 4 * lg + t) * S + c0 + l16] = d[t];
+}
+
+__global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__ Gpart, int nsplit, int ell,
+                                                       int ellp, float* __restrict__ Rinv,
+                                                       const float* __restrict__ Rprev,
+                                                       float* __restrict__ Rout) {
+  extern __shared__ __align__(16) float sh[];
+  const int S = ellp + 1;
+  float* G = sh;                 // [ellp][S] Gram, then L (lower; diagonal blocks exact)
+  float* X = G + ellp * S;       // [ellp][S] L^-1, later Rprev
+  float* Wk = X + ellp * S;      // [4][16][17] per-wavefront scratch tile
+  const int mat = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int T = ellp / 16;
+  const size_t e2 = (size_t)ellp * ellp;
+  // ---- sum of the partial Grams (fixed order), X = 0
+  const float* gp = Gpart + (size_t)mat * nsplit * e2;
+  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
+    float v = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) v += gp[sp * e2 + idx];
+    G[(idx / ellp) * S + idx % ellp] = v;
+    X[(idx / ellp) * S + idx % ellp] = 0.f;
+  }
+  __syncthreads();
+  // ---- shift; padded rows and columns become the identity
+  __shared__ float trace_sh;
+  if (wave == 0) {
+    float tr = 0.f;
+    for (int i = lane; i < ell; i += 64) tr += G[i * S + i];
+    tr = group_sum(tr, 64);
+    if (lane == 0) trace_sh = tr;
+  }
+  __syncthreads();
+  const float eps = 1e-6f * (trace_sh / static_cast<float>(ell > 0 ? ell : 1)) + 1e-30f;
+  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
+    const int i = idx / ellp, j = idx % ellp;
+    if (i >= ell || j >= ell) G[i * S + j] = i == j ? 1.f : 0.f;
+    else if (i == j) G[i * S + j] += eps;
+  }
+  __syncthreads();
+  // ---- blocked Cholesky
+  for (int J = 0; J < T; ++J) {
+    const int c0 = 16 * J;
+    if (wave == 0) {
+      const int li = lane < 16 ? lane : 15;
+      float row[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) row[c] = G[(c0 + li) * S + c0 + c];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float d = sqrtf(fmaxf(lane_bcast(row[j], j), 1e-30f));
+        const float inv = 1.f / d;
+        row[j] = lane == j ? d : (lane > j ? row[j] * inv : 0.f);
+#pragma unroll
+        for (int k = j + 1; k < 16; ++k) row[k] = fmaf(-row[j], lane_bcast(row[j], k), row[k]);
+      }
+      // inverse of the 16 x 16 block: lane c computes column c of X_JJ
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = lane == i ? 1.f : 0.f;
+#pragma unroll
+        for (int k = 0; k < i; ++k) v = fmaf(-lane_bcast(row[k], i), x[k], v);
+        x[i] = v / lane_bcast(row[i], i);
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) G[(c0 + lane) * S + c0 + c] = row[c];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) X[(c0 + i) * S + c0 + lane] = x[i];
+      }
+    }
+    __syncthreads();
+    // panel: L_IJ = A_IJ X_JJ^T
+    for (int I = J + 1 + wave; I < T; I += 4) {
+      const v4f p = tile_mma<false, true, false>(G, 16 * I, c0, S, X, c0, c0, S, v4f{0, 0, 0, 0}, l16, lg);
+      tile_store(G, 16 * I, c0, S, l16, lg, p);
+    }
+    __syncthreads();
+    // trailing update of the lower block triangle: A_IK -= L_IJ L_KJ^T, J < K <= I
+    const int m = T - J - 1;
+    for (int t = wave; t < m * (m + 1) / 2; t += 4) {
+      int I = 0, rem = t;
+      while (rem > I) { rem -= I + 1; ++I; }   // t -> (I, K) with K <= I
+      const int Ib = J + 1 + I, Kb = J + 1 + rem;
+      v4f acc = tile_load(G, 16 * Ib, 16 * Kb, S, l16, lg);
+      acc = tile_mma<false, true, true>(G, 16 * Ib, c0, S, G, 16 * Kb, c0, S, acc, l16, lg);
+      tile_store(G, 16 * Ib, 16 * Kb, S, l16, lg, acc);
+    }
+    __syncthreads();
+  }
+  // ---- L^-1 below the diagonal blocks, block row by block row
+  float* wk = Wk + wave * 16 * 17;
+  for (int I = 1; I < T; ++I) {
+    for (int Jb = wave; Jb < I; Jb += 4) {
+      v4f acc = v4f{0, 0, 0, 0};
+      for (int K = Jb; K < I; ++K)
+        acc = tile_mma<false, false, false>(G, 16 * I, 16 * K, S, X, 16 * K, 16 * Jb, S, acc, l16, lg);
+      tile_store(wk, 0, 0, 17, l16, lg, acc);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const v4f xr = tile_mma<false, false, true>(X, 16 * I, 16 * I, S, wk, 0, 0, 17, v4f{0, 0, 0, 0}, l16, lg);
+      tile_store(X, 16 * I, 16 * Jb, S, l16, lg, xr);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __syncthreads();
+  }
+  // ---- Rinv = X^T
+  float* Ri = Rinv + (size_t)mat * e2;
+  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
+    const int i = idx / ellp, j = idx % ellp;
+    Ri[idx] = X[j * S + i];
+  }
+  if (Rout == nullptr) return;
+  __syncthreads();
+  // ---- R = L^T Rprev
+  const float* Rp = Rprev ? Rprev + (size_t)mat * e2 : nullptr;
+  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
+    const int i = idx / ellp, j = idx % ellp;
+    X[i * S + j] = Rp ? Rp[idx] : (i == j ? 1.f : 0.f);
+  }
+  __syncthreads();
+  float* Ro = Rout + (size_t)mat * e2;
+  for (int t = wave; t < T * T; t += 4) {
+    const int I = t / T, Jb = t % T;
+    v4f acc = v4f{0, 0, 0, 0};
+    for (int K = I; K < T; ++K)
+      acc = tile_mma<true, false, false>(G, 16 * K, 16 * I, S, X, 16 * K, 16 * Jb, S, acc, l16, lg);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Ro[(size_t)(16 * I + 4 * lg + u) * ellp + 16 * Jb + l16] = acc[u];
+  }
+}
+
+constexpr int kApplyRows = 128;
+
+// Q = Y Rinv for 128 rows per workgroup (fp32 MFMA), written in place; optionally
 // Q^T in storage precision for the next product (XT[mat][j][m]), and the rounding
 // remainder Q^T - XT in XTlo for a two-term product.
 template <class T>
@@ -401,31 +513,32 @@ __global__ __launch_bounds__(256) void k_apply(float* __restrict__ Y, int M, int
                                                T* __restrict__ XTlo, size_t xt_mat_stride, int tiles_m) {
   extern __shared__ __align__(16) float sh[];
   const int S = ellp + 1;
-  float* Ys = sh;                  // [64][S]
-  float* Rs = Ys + 64 * S;         // [ellp][ellp]
+  float* Ys = sh;                  // [kApplyRows][S]
+  float* Rs = Ys + kApplyRows * S; // [ellp][ellp]
   const int mat = blockIdx.x / tiles_m;
-  const int m0 = (blockIdx.x % tiles_m) * 64;
+  const int m0 = (blockIdx.x % tiles_m) * kApplyRows;
   float* Ym = Y + (size_t)mat * M * ellp;
   const float* Rm = Rinv + (size_t)mat * ellp * ellp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  for (int idx = tid; idx < 64 * ellp; idx += 256) {
+  for (int idx = tid; idx < kApplyRows * ellp; idx += 256) {
     const int r = idx / ellp, j = idx % ellp;
     Ys[r * S + j] = m0 + r < M ? Ym[(size_t)(m0 + r) * ellp + j] : 0.f;
   }
   for (int idx = tid; idx < ellp * ellp; idx += 256) Rs[idx] = Rm[idx];
   __syncthreads();
   const int T16 = ellp / 16;
-  // wave owns rows 16*wave .. +15, all column tiles
+  // wave owns row tiles wave, wave + 4, ... (16 rows each), all column tiles
+  for (int rt = wave; rt < kApplyRows / 16; rt += 4)
   for (int c = 0; c < T16; ++c) {
     v4f acc = v4f{0, 0, 0, 0};
     for (int k0 = 0; k0 < ellp; k0 += 4) {
-      const float a = Ys[(16 * wave + l16) * S + k0 + lg];
+      const float a = Ys[(16 * rt + l16) * S + k0 + lg];
       const float bb = Rs[(k0 + lg) * ellp + 16 * c + l16];
       acc = mfma_f32(a, bb, acc);
     }
     for (int t = 0; t < 4; ++t) {
-      const int m = m0 + 16 * wave + 4 * lg + t, j = 16 * c + l16;
+      const int m = m0 + 16 * rt + 4 * lg + t, j = 16 * c + l16;
       if (m < M) {
         Ym[(size_t)m * ellp + j] = acc[t];
         if (XT != nullptr) {
@@ -441,20 +554,14 @@ __global__ __launch_bounds__(256) void k_apply(float* __restrict__ Y, int M, int
 
 // ================================================================ core SVD
 // One-sided Jacobi on the columns of Mj = R^T (ell x ell, LDS): rotations make the
-// columns mutually orthogonal, Mj J = P Sigma, J = S.  Round-robin pair order, one
-// wavefront per pair; stops when every pair is orthogonal to 3e-6 relative (fp32).
-constexpr int kJacThreads = 512;
-
-__device__ __forceinline__ float wave_sum(float v) {
-  v = group_sum(v, 16);
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
-}
-
-__global__ __launch_bounds__(kJacThreads) void k_jacobi(const float* __restrict__ Rm, int ell, int ellp,
-                                                        float* __restrict__ PS, float* __restrict__ Sv,
-                                                        float* __restrict__ sig) {
+// columns mutually orthogonal, Mj J = P Sigma, J = S.  Round-robin (tournament) pair
+// order; one 16-lane group per pair, each lane holding every 16th row, reductions
+// by DPP inside the group; a step's E/2 disjoint pairs run at once, one barrier per
+// step.  Stops when every pair is orthogonal to 3e-6 relative (fp32), or after 40
+// sweeps.
+__global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, int ell, int ellp,
+                                                 float* __restrict__ PS, float* __restrict__ Sv,
+                                                 float* __restrict__ sig) {
   extern __shared__ __align__(16) float sh[];
   const int S = ellp + 1;
   const int E = (ell + 1) & ~1;            // even number of columns for the tournament
@@ -465,9 +572,9 @@ __global__ __launch_bounds__(kJacThreads) void k_jacobi(const float* __restrict_
   __shared__ unsigned int rotated;
   const int mat = blockIdx.x;
   const float* R = Rm + (size_t)mat * ellp * ellp;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int nwave = kJacThreads / 64;
-  for (int idx = tid; idx < ellp * ellp; idx += kJacThreads) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int l16 = tid & 15, slot = tid >> 4, nslot = nthr >> 4;
+  for (int idx = tid; idx < ellp * ellp; idx += nthr) {
     const int i = idx / ellp, j = idx % ellp;
     Mj[i * S + j] = (i < ell && j < ell) ? R[j * ellp + i] : 0.f;   // transpose
     J[i * S + j] = i == j ? 1.f : 0.f;
@@ -477,28 +584,28 @@ __global__ __launch_bounds__(kJacThreads) void k_jacobi(const float* __restrict_
     if (tid == 0) rotated = 0u;
     __syncthreads();
     for (int step = 0; step < E - 1; ++step) {
-      // tournament: position 0 fixed, the others rotate
-      for (int pr = wave; pr < E / 2; pr += nwave) {
-        auto pos = [&](int x) { return x == 0 ? 0 : 1 + (x - 1 + step) % (E - 1); };
-        int p = pos(pr), qq = pos(E - 1 - pr);
+      for (int pr = slot; pr < E / 2; pr += nslot) {
+        const int x0 = pr, x1 = E - 1 - pr;
+        int p = x0 == 0 ? 0 : 1 + (x0 - 1 + step) % (E - 1);
+        int qq = 1 + (x1 - 1 + step) % (E - 1);
         if (p > qq) { const int t = p; p = qq; qq = t; }
-        if (qq >= ell) continue;
+        if (qq >= ell) continue;           // uniform over the 16-lane group
         float a = 0.f, bsum = 0.f, g = 0.f;
-        for (int i = lane; i < ell; i += 64) {
+        for (int i = l16; i < ell; i += 16) {
           const float x = Mj[i * S + p], y = Mj[i * S + qq];
           a = fmaf(x, x, a);
           bsum = fmaf(y, y, bsum);
           g = fmaf(x, y, g);
         }
-        a = wave_sum(a);
-        bsum = wave_sum(bsum);
-        g = wave_sum(g);
+        a = group_sum(a, 16);
+        bsum = group_sum(bsum, 16);
+        g = group_sum(g, 16);
         if (g == 0.f || fabsf(g) <= 3e-6f * sqrtf(a * bsum)) continue;
-        if (lane == 0) rotated = 1u;
+        if (l16 == 0) rotated = 1u;
         const float zeta = (bsum - a) / (2.f * g);
         const float t = copysignf(1.f, zeta) / (fabsf(zeta) + sqrtf(1.f + zeta * zeta));
         const float c = 1.f / sqrtf(1.f + t * t), s = c * t;
-        for (int i = lane; i < ellp; i += 64) {
+        for (int i = l16; i < ellp; i += 16) {
           const float x = Mj[i * S + p], y = Mj[i * S + qq];
           Mj[i * S + p] = c * x - s * y;
           Mj[i * S + qq] = s * x + c * y;
@@ -513,13 +620,13 @@ __global__ __launch_bounds__(kJacThreads) void k_jacobi(const float* __restrict_
     __syncthreads();
   }
   // singular values and their descending order (ties: lower column first)
-  for (int j = tid; j < ellp; j += kJacThreads) {
+  for (int j = tid; j < ellp; j += nthr) {
     float s2 = 0.f;
     for (int i = 0; i < ellp; ++i) s2 = fmaf(Mj[i * S + j], Mj[i * S + j], s2);
     nrm[j] = j < ell ? sqrtf(s2) : -1.f;
   }
   __syncthreads();
-  for (int j = tid; j < ellp; j += kJacThreads) {
+  for (int j = tid; j < ellp; j += nthr) {
     int rank = 0;
     for (int o = 0; o < ellp; ++o) rank += (nrm[o] > nrm[j] || (nrm[o] == nrm[j] && o < j)) ? 1 : 0;
     perm[rank] = j;
@@ -527,13 +634,13 @@ __global__ __launch_bounds__(kJacThreads) void k_jacobi(const float* __restrict_
   __syncthreads();
   float* PSm = PS + (size_t)mat * ellp * ellp;
   float* Sm = Sv + (size_t)mat * ellp * ellp;
-  for (int idx = tid; idx < ellp * ellp; idx += kJacThreads) {
+  for (int idx = tid; idx < ellp * ellp; idx += nthr) {
     const int i = idx / ellp, c = idx % ellp;
     const int j = perm[c];
     PSm[idx] = Mj[i * S + j];
     Sm[idx] = J[i * S + j];
   }
-  for (int c = tid; c < ellp; c += kJacThreads) sig[(size_t)mat * ellp + c] = fmaxf(nrm[perm[c]], 0.f);
+  for (int c = tid; c < ellp; c += nthr) sig[(size_t)mat * ellp + c] = fmaxf(nrm[perm[c]], 0.f);
 }
 
 // ================================================================ assembly
@@ -580,21 +687,52 @@ __global__ __launch_bounds__(256) void k_assemble_u(const float* __restrict__ Qn
   }
 }
 
-// B[i][w] = sum_j Qc[w][j] S[j][i] for i < r (rows r..r_pad-1 stay zero).
+// B[i][w] = sum_j Qc[w][j] S[j][i] for i < r (rows r..r_pad-1 stay zero).  One
+// workgroup per (matrix, 64 columns w): the 64 rows of Qc and S[:, :r_pad] are staged
+// in LDS; each thread accumulates a 4 (i) x 4 (w) block and stores 4 consecutive w.
 template <class T>
 __global__ __launch_bounds__(256) void k_assemble_b(const float* __restrict__ Qc, const float* __restrict__ Sv,
                                                     T* __restrict__ Bk, T* __restrict__ Bv, int W, int ellp,
                                                     int r, int r_pad, int tiles_w) {
+  extern __shared__ __align__(16) float sh[];
+  const int QS = ellp + 1;
+  float* Qs = sh;                 // [64][QS]
+  float* Ss = Qs + 64 * QS;       // [ellp][r_pad]
   const int mat = blockIdx.x / tiles_w;
-  const int w = (blockIdx.x % tiles_w) * 256 + threadIdx.x;
-  if (w >= W) return;
-  const float* Q = Qc + ((size_t)mat * W + w) * ellp;
+  const int w0 = (blockIdx.x % tiles_w) * 64;
+  const float* Q = Qc + (size_t)mat * W * ellp;
   const float* Sm = Sv + (size_t)mat * ellp * ellp;
+  for (int idx = threadIdx.x; idx < 64 * ellp; idx += blockDim.x) {
+    const int ww = idx / ellp, j = idx % ellp;
+    Qs[ww * QS + j] = w0 + ww < W ? Q[(size_t)(w0 + ww) * ellp + j] : 0.f;
+  }
+  for (int idx = threadIdx.x; idx < ellp * r_pad; idx += blockDim.x) {
+    const int j = idx / r_pad, i = idx % r_pad;
+    Ss[idx] = i < r ? Sm[j * ellp + i] : 0.f;
+  }
+  __syncthreads();
   T* B = ((mat & 1) ? Bv : Bk) + (size_t)(mat >> 1) * r_pad * W;
-  for (int i = 0; i < r; ++i) {
-    float v = 0.f;
-    for (int j = 0; j < ellp; ++j) v = fmaf(Q[j], Sm[j * ellp + i], v);
-    B[(size_t)i * W + w] = from_f32<T>(v);
+  const int wb = (threadIdx.x & 15) * 4;          // 4 consecutive columns
+  for (int ib = (threadIdx.x >> 4) * 4; ib < r; ib += 64) {
+    float acc[4][4] = {};
+    for (int j = 0; j < ellp; ++j) {
+      const float4 sv = *reinterpret_cast<const float4*>(&Ss[j * r_pad + ib]);
+      const float sj[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float q = Qs[(wb + c) * QS + j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u][c] = fmaf(q, sj[u], acc[u][c]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = ib + u;
+      if (i >= r) break;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (w0 + wb + c < W) B[(size_t)i * W + w0 + wb + c] = from_f32<T>(acc[u][c]);
+    }
   }
 }
 
@@ -654,23 +792,48 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
   return hipGetLastError();
 }
 
+// Row split of the Gram of an M-row basis: about 1024 workgroups over all matrices,
+// at least 64 rows each.
+static void gram_split(int M, int nmat, int& rows, int& nsplit) {
+  int want = (1024 + nmat - 1) / std::max(nmat, 1);
+  want = std::max(1, std::min(want, (M + 63) / 64));
+  rows = ((M + want - 1) / want + 63) / 64 * 64;
+  nsplit = (M + rows - 1) / rows;
+}
+
 // Two-pass Cholesky QR of Y [nmat][M][ellp] in place; Q^T to XT (if given); R to Racc (if given).
 template <class T>
 static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void* XTlo, float* Racc,
                        hipStream_t st) {
   const Dims& dm = c->dm;
   const int nmat = 2 * dm.B, ellp = ws.ellp;
-  const size_t lds_chol = (size_t)2 * ellp * (ellp + 1) * sizeof(float);
-  const size_t lds_apply = (size_t)(64 * (ellp + 1) + ellp * ellp) * sizeof(float);
-  const int tiles_m = (M + 63) / 64;
-  hipLaunchKernelGGL(k_gramchol, dim3(nmat), dim3(kCholThreads), lds_chol, st, ws.Y, M, dm.ell, ellp,
-                     ws.Rinv, nullptr, Racc);
-  hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
-                     static_cast<T*>(nullptr), static_cast<T*>(nullptr), (size_t)0, tiles_m);
-  hipLaunchKernelGGL(k_gramchol, dim3(nmat), dim3(kCholThreads), lds_chol, st, ws.Y, M, dm.ell, ellp,
-                     ws.Rinv, Racc, Racc);
-  hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
-                     static_cast<T*>(XT), static_cast<T*>(XTlo), (size_t)ellp * ws.M, tiles_m);
+  const size_t lds_gram = (size_t)ellp * (ellp + 1) * sizeof(float);
+  const size_t lds_chol = (size_t)(2 * ellp * (ellp + 1) + 4 * 16 * 17) * sizeof(float);
+  const size_t lds_apply = (size_t)(kApplyRows * (ellp + 1) + ellp * ellp) * sizeof(float);
+  const int tiles_m = (M + kApplyRows - 1) / kApplyRows;
+  int rows, nsplit;
+  gram_split(M, nmat, rows, nsplit);
+  for (int pass = 0; pass < 2; ++pass) {
+    switch (ellp / 16) {
+#define AP_GRAM_CASE(TV)                                                                              \
+  case TV:                                                                                            \
+    hipLaunchKernelGGL(k_gram<TV>, dim3(nmat * nsplit), dim3(kGramThreads), lds_gram, st, ws.Y, M, ellp, \
+                       rows, nsplit, ws.Gpart);                                                       \
+    break;
+      AP_GRAM_CASE(1) AP_GRAM_CASE(2) AP_GRAM_CASE(3) AP_GRAM_CASE(4)
+      AP_GRAM_CASE(5) AP_GRAM_CASE(6) AP_GRAM_CASE(7) AP_GRAM_CASE(8)
+#undef AP_GRAM_CASE
+      default: return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(k_chol, dim3(nmat), dim3(kCholThreads), lds_chol, st, ws.Gpart, nsplit, dm.ell, ellp,
+                       ws.Rinv, pass == 0 ? nullptr : Racc, Racc);
+    if (pass == 0)
+      hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
+                         static_cast<T*>(nullptr), static_cast<T*>(nullptr), (size_t)0, tiles_m);
+    else
+      hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
+                         static_cast<T*>(XT), static_cast<T*>(XTlo), (size_t)ellp * ws.M, tiles_m);
+  }
   return hipGetLastError();
 }
 
@@ -687,6 +850,10 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   }
   const int nmat = ws.nmat, ellp = ws.ellp;
   const size_t es = sizeof(T);
+  int rows_n, split_n, rows_w, split_w;
+  gram_split(dm.N, nmat, rows_n, split_n);
+  gram_split(dm.W, nmat, rows_w, split_w);
+  const size_t max_split = (size_t)std::max(split_n, split_w);
   struct Buf { void** p; size_t bytes; };
   Buf bufs[] = {
       {&ws.omT, (size_t)nmat * ellp * dm.W * es},
@@ -695,6 +862,7 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
       {&ws.XTlo, std::is_same<T, bf16_t>::value ? (size_t)nmat * ellp * ws.M * es : 0},
       {reinterpret_cast<void**>(&ws.Qn), (size_t)nmat * dm.N * ellp * 4},
       {reinterpret_cast<void**>(&ws.Qc), (size_t)nmat * dm.W * ellp * 4},
+      {reinterpret_cast<void**>(&ws.Gpart), (size_t)nmat * max_split * ellp * ellp * 4},
       {reinterpret_cast<void**>(&ws.Rinv), (size_t)nmat * ellp * ellp * 4},
       {reinterpret_cast<void**>(&ws.Racc), (size_t)nmat * ellp * ellp * 4},
       {reinterpret_cast<void**>(&ws.PS), (size_t)nmat * ellp * ellp * 4},
@@ -730,18 +898,21 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
     hipLaunchKernelGGL(k_omega_copy<T>, grid_1d((size_t)nmat * dm.ell * dm.W), dim3(256), 0, st,
                        c->params.omega, static_cast<T*>(ws.omT), nmat, dm.W, dm.ell, ellp);
   else
-    hipLaunchKernelGGL(k_omega_philox<T>, grid_1d((size_t)nmat * ((dm.ell * (size_t)dm.W + 127) / 128)),
+    hipLaunchKernelGGL(k_omega_philox<T>, grid_1d((size_t)nmat * ((dm.ell * (size_t)dm.W + 7) / 8)),
                        dim3(256), 0, st, static_cast<T*>(ws.omT), nmat, dm.W, dm.ell, ellp, c->params.seed);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_stage(e, "test matrix");
 
   // dynamic LDS above the 64 KB default: request exactly what each launch uses
-  const size_t lds_chol = (size_t)2 * ellp * (ellp + 1) * sizeof(float);
+  const size_t lds_chol = (size_t)(2 * ellp * (ellp + 1) + 4 * 16 * 17) * sizeof(float);
   const size_t lds_jac = (size_t)(2 * ellp * (ellp + 1) + 2 * ellp) * sizeof(float);
-  const size_t lds_apply = (size_t)(64 * (ellp + 1) + ellp * ellp) * sizeof(float);
+  const size_t lds_apply = (size_t)(kApplyRows * (ellp + 1) + ellp * ellp) * sizeof(float);
   const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP) * sizeof(float);
+  const size_t lds_b = (size_t)(64 * (ellp + 1) + ellp * dm.r_pad) * sizeof(float);
   const struct { const void* fn; size_t bytes; const char* name; } lds_req[] = {
-      {reinterpret_cast<const void*>(&k_gramchol), lds_chol, "LDS size of k_gramchol"},
+      {reinterpret_cast<const void*>(&k_gram<8>), (size_t)ellp * (ellp + 1) * sizeof(float), "LDS size of k_gram"},
+      {reinterpret_cast<const void*>(&k_chol), lds_chol, "LDS size of k_chol"},
+      {reinterpret_cast<const void*>(&k_assemble_b<T>), lds_b, "LDS size of k_assemble_b"},
       {reinterpret_cast<const void*>(&k_jacobi), lds_jac, "LDS size of k_jacobi"},
       {reinterpret_cast<const void*>(&k_apply<T>), lds_apply, "LDS size of k_apply"},
       {reinterpret_cast<const void*>(&k_assemble_u<T>), lds_u, "LDS size of k_assemble_u"},
@@ -771,14 +942,15 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   if (e == hipSuccess) e = orth<T>(c, ws, dm.W, nullptr, nullptr, ws.Racc, st);
   if (e == hipSuccess) e = hipMemcpyAsync(ws.Qc, ws.Y, (size_t)nmat * dm.W * ellp * 4, hipMemcpyDeviceToDevice, st);
   if (e != hipSuccess) return fail_stage(e, "projection C^T = A^T Q");
-  hipLaunchKernelGGL(k_jacobi, dim3(nmat), dim3(kJacThreads), lds_jac, st, ws.Racc, dm.ell, ellp, ws.PS,
+  const int jac_threads = std::min(1024, std::max(64, (16 * ((dm.ell + 1) / 2) + 63) / 64 * 64));
+  hipLaunchKernelGGL(k_jacobi, dim3(nmat), dim3(jac_threads), lds_jac, st, ws.Racc, dm.ell, ellp, ws.PS,
                      ws.Sv, ws.sig);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_stage(e, "core SVD");
   hipLaunchKernelGGL(k_assemble_u<T>, dim3(nmat * dm.nblk), dim3(256), lds_u, st, ws.Qn, ws.PS,
                      static_cast<T*>(c->Uk), dm.N, ellp, dm.r, dm.NP, dm.nblk);
-  const int tiles_w = (dm.W + 255) / 256;
-  hipLaunchKernelGGL(k_assemble_b<T>, dim3(nmat * tiles_w), dim3(256), 0, st, ws.Qc, ws.Sv,
+  const int tiles_w = (dm.W + 63) / 64;
+  hipLaunchKernelGGL(k_assemble_b<T>, dim3(nmat * tiles_w), dim3(256), lds_b, st, ws.Qc, ws.Sv,
                      static_cast<T*>(c->Bk), static_cast<T*>(c->Bv), dm.W, ellp, dm.r, dm.r_pad, tiles_w);
   hipLaunchKernelGGL(k_copy_sigma, grid_1d((size_t)nmat * dm.r), dim3(256), 0, st, ws.sig, c->sigma_k,
                      c->sigma_v, nmat, ellp, dm.r);

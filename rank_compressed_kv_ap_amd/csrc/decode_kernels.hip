@@ -20,6 +20,8 @@
 //             splits, projection of z through B_v, output.
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "ap_internal.h"
 #include "device_common.h"
 #include "tiles.h"
@@ -580,7 +582,8 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
 
 // ================================================================ launchers
 template <class T, int NP, int HT>
-static hipError_t launch_attn_t(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st) {
+static hipError_t launch_attn_t(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st,
+                                const KernelEvents& ev) {
   const Dims& dm = c->dm;
   constexpr int RP = NP * 16, HP = HT * 16;
   const size_t lds = (size_t)(4 * HP * (RP + 1) + 8 * HP) * sizeof(float);
@@ -591,27 +594,28 @@ static hipError_t launch_attn_t(const ap_cache* c, int r_lo, float sl2, int S, i
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_attn<T, NP, HT>), dim3(dm.B * S), dim3(256), lds, st,
+  hipExtLaunchKernelGGL((k_attn<T, NP, HT>), dim3(dm.B * S), dim3(256), lds, st, ev.start, ev.stop, 0,
                      static_cast<const T*>(c->Uk), static_cast<const T*>(c->Uv), c->qt, c->mask,
                      c->part_z, c->part_ml, dm.N, dm.nblk, CB, S, dm.Hq, r_lo, sl2);
   return hipGetLastError();
 }
 
 template <class T, int HT>
-static hipError_t dispatch_np(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st) {
+static hipError_t dispatch_np(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st,
+                              const KernelEvents& ev) {
   switch (c->dm.NP) {
-    case 1: return launch_attn_t<T, 1, HT>(c, r_lo, sl2, S, CB, st);
-    case 2: return launch_attn_t<T, 2, HT>(c, r_lo, sl2, S, CB, st);
-    case 3: return launch_attn_t<T, 3, HT>(c, r_lo, sl2, S, CB, st);
-    case 4: return launch_attn_t<T, 4, HT>(c, r_lo, sl2, S, CB, st);
+    case 1: return launch_attn_t<T, 1, HT>(c, r_lo, sl2, S, CB, st, ev);
+    case 2: return launch_attn_t<T, 2, HT>(c, r_lo, sl2, S, CB, st, ev);
+    case 3: return launch_attn_t<T, 3, HT>(c, r_lo, sl2, S, CB, st, ev);
+    case 4: return launch_attn_t<T, 4, HT>(c, r_lo, sl2, S, CB, st, ev);
     default: break;
   }
   if constexpr (HT <= 2) {
     switch (c->dm.NP) {
-      case 5: return launch_attn_t<T, 5, HT>(c, r_lo, sl2, S, CB, st);
-      case 6: return launch_attn_t<T, 6, HT>(c, r_lo, sl2, S, CB, st);
-      case 7: return launch_attn_t<T, 7, HT>(c, r_lo, sl2, S, CB, st);
-      case 8: return launch_attn_t<T, 8, HT>(c, r_lo, sl2, S, CB, st);
+      case 5: return launch_attn_t<T, 5, HT>(c, r_lo, sl2, S, CB, st, ev);
+      case 6: return launch_attn_t<T, 6, HT>(c, r_lo, sl2, S, CB, st, ev);
+      case 7: return launch_attn_t<T, 7, HT>(c, r_lo, sl2, S, CB, st, ev);
+      case 8: return launch_attn_t<T, 8, HT>(c, r_lo, sl2, S, CB, st, ev);
       default: break;
     }
   }
@@ -619,23 +623,26 @@ static hipError_t dispatch_np(const ap_cache* c, int r_lo, float sl2, int S, int
 }
 
 template <class T>
-static hipError_t dispatch_ht(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st) {
+static hipError_t dispatch_ht(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st,
+                              const KernelEvents& ev) {
   switch (c->dm.HT) {
-    case 1: return dispatch_np<T, 1>(c, r_lo, sl2, S, CB, st);
-    case 2: return dispatch_np<T, 2>(c, r_lo, sl2, S, CB, st);
-    case 4: return dispatch_np<T, 4>(c, r_lo, sl2, S, CB, st);
+    case 1: return dispatch_np<T, 1>(c, r_lo, sl2, S, CB, st, ev);
+    case 2: return dispatch_np<T, 2>(c, r_lo, sl2, S, CB, st, ev);
+    case 4: return dispatch_np<T, 4>(c, r_lo, sl2, S, CB, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_attn(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st) {
-  if (c->dm.storage == AP_BF16) return dispatch_ht<bf16_t>(c, r_lo, sl2, S, CB, st);
-  return dispatch_ht<float>(c, r_lo, sl2, S, CB, st);
+hipError_t launch_attn(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st,
+                       const KernelEvents& ev) {
+  if (c->dm.storage == AP_BF16) return dispatch_ht<bf16_t>(c, r_lo, sl2, S, CB, st, ev);
+  return dispatch_ht<float>(c, r_lo, sl2, S, CB, st, ev);
 }
 
 template <class T>
 static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out, float sl2, int S,
-                                   int Tn, const void* tk, const void* tv, hipStream_t st) {
+                                   int Tn, const void* tk, const void* tv, hipStream_t st,
+                                   const KernelEvents& ev) {
   const Dims& dm = c->dm;
   constexpr int V = 16 / sizeof(T);
   const int lpr = dm.d / V;
@@ -645,13 +652,15 @@ static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out
   if (vec) {
     const int rpp = kCombThreads / lpr;
     const size_t lds = (size_t)(dm.d + dm.r_pad + kTextChunk + 4 + rpp * dm.d + 2 * S) * sizeof(float);
-    hipLaunchKernelGGL(k_combine<T>, dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st, c->part_z,
+    hipExtLaunchKernelGGL(k_combine<T>, dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st, ev.start,
+                          ev.stop, 0, c->part_z,
                        c->part_ml, static_cast<const T*>(c->Bv), q, out, static_cast<const T*>(tk),
                        static_cast<const T*>(tv), S, dm.Hq, dm.Hq_pad, dm.r_pad, dm.W, dm.d, dm.G, Tn,
                        sl2);
   } else {
     const size_t lds = (size_t)(dm.d + dm.r_pad + kCombThreads + 4) * sizeof(float);
-    hipLaunchKernelGGL(k_combine_scalar<T>, dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st,
+    hipExtLaunchKernelGGL(k_combine_scalar<T>, dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st,
+                          ev.start, ev.stop, 0,
                        c->part_z, c->part_ml, static_cast<const T*>(c->Bv), q, out,
                        static_cast<const T*>(tk), static_cast<const T*>(tv), S, dm.Hq, dm.Hq_pad,
                        dm.r_pad, dm.W, dm.d, dm.G, Tn, sl2);
@@ -660,9 +669,9 @@ static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out
 }
 
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float sl2, int S, int Tn,
-                          const void* tk, const void* tv, hipStream_t st) {
-  if (c->dm.storage == AP_BF16) return launch_combine_t<bf16_t>(c, q, out, sl2, S, Tn, tk, tv, st);
-  return launch_combine_t<float>(c, q, out, sl2, S, Tn, tk, tv, st);
+                          const void* tk, const void* tv, hipStream_t st, const KernelEvents& ev) {
+  if (c->dm.storage == AP_BF16) return launch_combine_t<bf16_t>(c, q, out, sl2, S, Tn, tk, tv, st, ev);
+  return launch_combine_t<float>(c, q, out, sl2, S, Tn, tk, tv, st, ev);
 }
 
 }  // namespace ap

@@ -19,6 +19,8 @@
 //     keys decides instead;
 //  4. one wavefront per head writes the selection bitmask per 32-token block (and, on
 //     request, the ascending selected ids).
+#include <hip/hip_ext.h>
+
 #include "ap_internal.h"
 #include "device_common.h"
 #include "tiles.h"
@@ -609,7 +611,7 @@ size_t select_lds_bytes(const Dims& dm, int Hg) {
 
 template <class T>
 static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, int top_k,
-                                  int32_t* sel_out, hipStream_t st) {
+                                  int32_t* sel_out, hipStream_t st, const KernelEvents& ev) {
   const Dims& dm = c->dm;
   const int Hg = select_heads_per_group(dm);
   const int HG = (dm.Hq + Hg - 1) / Hg;
@@ -631,19 +633,19 @@ static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, i
       c->mask, sel_out, dm.B, dm.N, dm.N_pad, dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d, dm.G, dm.Hq,  \
       dm.Hq_pad, Hg, HG, r_lo, top_k
   if (nplo == 1)
-    hipLaunchKernelGGL((k_select<T, 16>), dim3(grid), dim3(kSelThreads), lds, st, AP_SELECT_ARGS);
+    hipExtLaunchKernelGGL((k_select<T, 16>), dim3(grid), dim3(kSelThreads), lds, st, ev.start, ev.stop, 0, AP_SELECT_ARGS);
   else if (nplo == 2)
-    hipLaunchKernelGGL((k_select<T, 8>), dim3(grid), dim3(kSelThreads), lds, st, AP_SELECT_ARGS);
+    hipExtLaunchKernelGGL((k_select<T, 8>), dim3(grid), dim3(kSelThreads), lds, st, ev.start, ev.stop, 0, AP_SELECT_ARGS);
   else
-    hipLaunchKernelGGL((k_select<T, 0>), dim3(grid), dim3(kSelThreads), lds, st, AP_SELECT_ARGS);
+    hipExtLaunchKernelGGL((k_select<T, 0>), dim3(grid), dim3(kSelThreads), lds, st, ev.start, ev.stop, 0, AP_SELECT_ARGS);
 #undef AP_SELECT_ARGS
   return hipGetLastError();
 }
 
 hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k, int32_t* sel_out,
-                         hipStream_t st) {
-  if (c->dm.storage == AP_BF16) return launch_select_t<bf16_t>(c, q, r_lo, top_k, sel_out, st);
-  return launch_select_t<float>(c, q, r_lo, top_k, sel_out, st);
+                         hipStream_t st, const KernelEvents& ev) {
+  if (c->dm.storage == AP_BF16) return launch_select_t<bf16_t>(c, q, r_lo, top_k, sel_out, st, ev);
+  return launch_select_t<float>(c, q, r_lo, top_k, sel_out, st, ev);
 }
 
 hipError_t launch_rownorm(const ap_cache* c, hipStream_t st) {

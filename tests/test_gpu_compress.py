@@ -199,3 +199,27 @@ def test_compress_full_configs_then_decode(gpu_lib, cfg):
     torch.cuda.synchronize()
     c.free()
     check_against_oracle(w, seqs, out.cpu().numpy(), sel.cpu().numpy())
+
+
+def test_recompress_equals_fresh_compress(gpu_lib):
+    """ap_recompress into a cache built from other inputs gives the factors a fresh
+    ap_compress of the new inputs gives, bit for bit."""
+    w = SMALL["bf16_ragged"][0]
+    K1, V1, _ = host_inputs(w, w.batch)
+    w2 = w.replace(cfg_id=208)
+    K2, V2, om2 = host_inputs(w2, w2.batch)
+    c_ref, ref = gpu_compress(w, K2, V2, gpu_lib, om=om2)
+    c_ref.free()
+    c, _ = gpu_compress(w, K1, V1, gpu_lib, seed=9)
+    dt = torch_storage(w)
+    k = torch.from_numpy(np.stack(K2)).to(dt).cuda()
+    v = torch.from_numpy(np.stack(V2)).to(dt).cuda()
+    om = torch.from_numpy(np.stack([np.stack(o) for o in om2]).astype(np.float32)).cuda()
+    c.recompress(k, v, omega=om)
+    U_k, B_k, U_v, B_v = c.get_factors()
+    sk, sv = c.get_sigma()
+    torch.cuda.synchronize()
+    got = [x.float().cpu().numpy().astype(np.float64) for x in (U_k, B_k, U_v, B_v, sk, sv)]
+    c.free()
+    for x, y in zip(got, ref):
+        assert np.array_equal(x, y)
