@@ -289,11 +289,12 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
   if (p->n_text > 0 && (!p->text_k || !p->text_v)) return fail(AP_ERR_NULL_ARG, "text_k/text_v must be set when n_text > 0");
   if (p->n_text > (1 << 20)) return fail(AP_ERR_UNSUPPORTED, "n_text > 2^20");
 
-  // N-splits of the flash-decode kernel: about two workgroups per CU, >= 8 token blocks each
+  // N-splits of the flash-decode kernel: about two workgroups per CU, >= 5 token blocks
+  // each (measured best on the batch-32 LLaVA layer: 16 splits of 5-6 blocks)
   int S = p->splits;
   if (S == 0) {
     S = ceil_div(512, dm.B);
-    S = std::min(S, std::max(1, dm.nblk / 8));
+    S = std::min(S, std::max(1, dm.nblk / 5));
   }
   S = std::max(1, std::min(S, dm.S_cap));
   const int CB = ceil_div(dm.nblk, S);

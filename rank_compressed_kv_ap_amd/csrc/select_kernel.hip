@@ -173,16 +173,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
   const bool select = !none && !all;
   const int nplo = (r_lo + 15) >> 4;
 
-  // ---- A. loads in flight together: U_k low panels (first batch), B_k rows, q
+  // ---- A. loads in flight together: B_k rows first (the latent queries wait only for
+  // them), then q, then the first batch of U_k low panels
   LaneTile<T> a[UBA][NPL];
-  if (UB > 0 && select) {
-#pragma unroll
-    for (int u = 0; u < UBA; ++u) {
-      const int blk = min(wave + u * kSelWaves, nblk - 1);   // clamped: loads stay unconditional
-      a[u][0].load(Uk + tile_base(b, 0, blk, NP, nblk), lane);
-      if (NPL > 1) a[u][NPL - 1].load(Uk + tile_base(b, NPL - 1, blk, NP, nblk), lane);
-    }
-  }
   constexpr int V = Vec16<T>::n;
   constexpr int XB = 16;   // B_k row slices per lane in flight
   const int ginv_num = (65536 + G - 1) / G;   // (h * ginv_num) >> 16 == h / G for h, G <= 64
@@ -206,7 +199,22 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     }
   };
   if (vec) load_rows(wave * RPW + rw);
-  for (int i = tid; i < nh * d; i += kSelThreads) qh[i] = q[((size_t)b * Hq + h0) * d + i];
+  constexpr int QPT = (kMaxHg * 256 + kSelThreads - 1) / kSelThreads;   // q values per thread
+  float qv[QPT];
+  const int nq = nh * d;
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) qv[u] = q[((size_t)b * Hq + h0) * d + min(tid + u * kSelThreads, nq - 1)];
+  if (UB > 0 && select) {
+#pragma unroll
+    for (int u = 0; u < UBA; ++u) {
+      const int blk = min(wave + u * kSelWaves, nblk - 1);   // clamped: loads stay unconditional
+      a[u][0].load(Uk + tile_base(b, 0, blk, NP, nblk), lane);
+      if (NPL > 1) a[u][NPL - 1].load(Uk + tile_base(b, NPL - 1, blk, NP, nblk), lane);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < QPT; ++u)
+    if (tid + u * kSelThreads < nq) qh[tid + u * kSelThreads] = qv[u];
   for (int i = tid; i < nh * 256; i += kSelThreads) hist[i] = 0;
   for (int i = tid; i < nblk; i += kSelThreads) bflag[i] = 0;
   if (tid < nh) {
