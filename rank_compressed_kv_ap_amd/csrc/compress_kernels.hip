@@ -43,6 +43,7 @@ struct CompressWs {
   float* Qn = nullptr;                // [nmat][N][ellp]   final range basis of A
   float* Qc = nullptr;                // [nmat][W][ellp]   basis of C^T
   float* Gpart = nullptr;             // [nmat][nsplit][ellp][ellp] partial Grams
+  float* Gsum = nullptr;              // [nmat][ellp][ellp] their sum
   float* Rinv = nullptr;              // [nmat][ellp][ellp]
   float* Racc = nullptr;              // [nmat][ellp][ellp] R of the last orthonormalisation
   float* PS = nullptr;                // [nmat][ellp][ellp] P Sigma (columns sorted)
@@ -112,9 +113,11 @@ __global__ __launch_bounds__(256) void k_omega_copy(const float* __restrict__ om
 // Output Y[mat][m][j] (fp32, row stride ellp) for m in a 128-row tile:
 //   TRANS = false: Y = A X,   A [M][K] rows m, X^T [ellp][K]        (M = N, K = W)
 //   TRANS = true : Y = A^T X, A [K][M] columns m, X^T [ellp][K]     (M = W, K = N)
-// A 32-wide k slice of A is staged in LDS as [128 m][32 k] (transposed on the way in
-// for TRANS), so both MFMA operands read 8 consecutive k values per lane.
-constexpr int kGemmBM = 128, kGemmBK = 32, kGemmLdsStride = kGemmBK + 8;  // padded bf16 row
+// A 64-wide k slice of A is staged in LDS as [128 m][64 k] (transposed on the way in
+// for TRANS), so both MFMA operands read 8 consecutive k values per lane.  The next
+// slice of A and of X is loaded into registers while the current one is multiplied
+// (software pipelining: the loads of slice s+1 are in flight during the MFMAs of s).
+constexpr int kGemmBM = 128, kGemmBK = 64, kGemmLdsStride = kGemmBK + 8;  // padded bf16 row
 
 template <class T, bool TRANS, int NT, bool SPLIT>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kmat,
@@ -124,7 +127,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
                                                         int N, int W, int ellp, size_t x_mat_stride,
                                                         int tiles_m) {
   static_assert(std::is_same<T, bf16_t>::value, "MFMA GEMM path is bf16");
+  constexpr int XR = NT * 16;                        // rows of X^T (= ellp)
+  constexpr int XU = (XR * 8 + kGemmThreads - 1) / kGemmThreads;   // 16-byte X loads per thread
   __shared__ __align__(16) bf16_t As[kGemmBM * kGemmLdsStride];
+  __shared__ __align__(16) bf16_t Xs[(SPLIT ? 2 : 1) * XR * kGemmLdsStride];
   const int mat = blockIdx.x / tiles_m;
   const int m0 = (blockIdx.x % tiles_m) * kGemmBM;
   const int b = mat >> 1;
@@ -144,79 +150,125 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
 #pragma unroll
     for (int c = 0; c < NT; ++c) acc[i][c] = v4f{0, 0, 0, 0};
 
-  for (int k0 = 0; k0 < K; k0 += kGemmBK) {
-    // stage A tile: 128 x 32 bf16 = 8 KB = 256 threads x 2 x 16 B
+  auto pack8 = [](const uint16_t* t) {
+    return make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16),
+                      t[4] | (uint32_t(t[5]) << 16), t[6] | (uint32_t(t[7]) << 16));
+  };
+  // ---- one 64-wide k slice in registers: A (4 x 8 elements per thread) and X^T
+  // (XU x 8 elements per thread), both staged in LDS before the MFMAs
+  struct Slice {
+    uint4 a[4];
+    uint4 x[XU];
+    uint4 xl[SPLIT ? XU : 1];
+  };
+  auto load_slice = [&](int k0, Slice& sl) {
     if (!TRANS) {
+      // rows (tid >> 3) + 32 h, k = k0 + 8 (tid & 7) .. +7
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = (tid >> 2) + 64 * h, kk = (tid & 3) * 8;
+      for (int h = 0; h < 4; ++h) {
+        const int row = (tid >> 3) + 32 * h, kk = (tid & 7) * 8;
         const int gm = min(m0 + row, M - 1), gk = k0 + kk;
-        uint4 v = make_uint4(0, 0, 0, 0);
         if (avec && gk + 8 <= K) {
-          v = *reinterpret_cast<const uint4*>(A + (size_t)gm * W + gk);
+          sl.a[h] = *reinterpret_cast<const uint4*>(A + (size_t)gm * W + gk);
         } else {
           uint16_t t[8];
           for (int e = 0; e < 8; ++e) t[e] = gk + e < K ? A[(size_t)gm * W + gk + e] : bf16_t(0);
-          v = make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16),
-                         t[4] | (uint32_t(t[5]) << 16), t[6] | (uint32_t(t[7]) << 16));
+          sl.a[h] = pack8(t);
         }
-        *reinterpret_cast<uint4*>(&As[row * kGemmLdsStride + kk]) = v;
       }
     } else {
-      // A rows are k (tokens), columns are m: read 32 rows x 128 columns coalesced,
-      // write transposed so that As[m][k] holds k contiguous.
+      // k rows 4 (tid >> 4) + h, m = m0 + 8 (tid & 15) .. +7 (transposed into LDS later)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kk = (tid >> 4) + 16 * h, mm = (tid & 15) * 8;
+      for (int h = 0; h < 4; ++h) {
+        const int kk = 4 * (tid >> 4) + h, mm = (tid & 15) * 8;
         const int gk = k0 + kk, gm = m0 + mm;
-        uint16_t t[8];
         if (avec && gk < K && gm + 8 <= M) {
-          const uint4 v = *reinterpret_cast<const uint4*>(A + (size_t)gk * W + gm);
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-          for (int e = 0; e < 4; ++e) {
-            t[2 * e] = static_cast<uint16_t>(w4[e] & 0xffffu);
-            t[2 * e + 1] = static_cast<uint16_t>(w4[e] >> 16);
-          }
+          sl.a[h] = *reinterpret_cast<const uint4*>(A + (size_t)gk * W + gm);
         } else {
+          uint16_t t[8];
           for (int e = 0; e < 8; ++e) t[e] = (gk < K && gm + e < M) ? A[(size_t)gk * W + gm + e] : bf16_t(0);
+          sl.a[h] = pack8(t);
         }
-        for (int e = 0; e < 8; ++e) As[(mm + e) * kGemmLdsStride + kk] = t[e];
       }
     }
-    __syncthreads();
-    // X operand: columns 16c + l16, k = k0 + 8*lg .. +7 (zero past K); with SPLIT the
-    // operand is hi + lo, two bf16 halves of an fp32 basis (about 16 significant bits)
-    auto load_x = [&](const T* base, int c) {
-      const int gk = k0 + 8 * lg;
-      const T* xr = base + (size_t)(16 * c + l16) * K + gk;
-      uint4 v;
+    // X^T rows j = idx / 8, k = k0 + 8 (idx % 8) .. +7 (zero past K)
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int idx = min(tid + u * kGemmThreads, XR * 8 - 1);
+      const int j = idx >> 3, gk = k0 + 8 * (idx & 7);
+      const size_t off = (size_t)j * K + gk;
       if (xvec && gk + 8 <= K) {
-        v = *reinterpret_cast<const uint4*>(xr);
+        sl.x[u] = *reinterpret_cast<const uint4*>(X + off);
+        if constexpr (SPLIT) sl.xl[u] = *reinterpret_cast<const uint4*>(Xl + off);
       } else {
-        uint16_t t[8];
-        for (int e = 0; e < 8; ++e) t[e] = gk + e < K ? xr[e] : bf16_t(0);
-        v = make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16),
-                       t[4] | (uint32_t(t[5]) << 16), t[6] | (uint32_t(t[7]) << 16));
+        uint16_t t[8], tl[8];
+        for (int e = 0; e < 8; ++e) {
+          t[e] = gk + e < K ? X[off + e] : bf16_t(0);
+          if constexpr (SPLIT) tl[e] = gk + e < K ? Xl[off + e] : bf16_t(0);
+        }
+        sl.x[u] = pack8(t);
+        if constexpr (SPLIT) sl.xl[u] = pack8(tl);
       }
-      return __builtin_bit_cast(v8bf, v);
-    };
-    v8bf xb[NT], xl[SPLIT ? NT : 1];
+    }
+  };
+  auto stage = [&](const Slice& sl) {
+    if (!TRANS) {
 #pragma unroll
-    for (int c = 0; c < NT; ++c) {
-      xb[c] = load_x(X, c);
-      if constexpr (SPLIT) xl[c] = load_x(Xl, c);
+      for (int h = 0; h < 4; ++h)
+        *reinterpret_cast<uint4*>(&As[((tid >> 3) + 32 * h) * kGemmLdsStride + (tid & 7) * 8]) = sl.a[h];
+    } else {
+      // 4 k rows x 8 m columns in registers -> 8 columns of 4 consecutive k (8 bytes)
+      const int kk = 4 * (tid >> 4), mm = (tid & 15) * 8;
+      const uint32_t r0[4] = {sl.a[0].x, sl.a[0].y, sl.a[0].z, sl.a[0].w};
+      const uint32_t r1[4] = {sl.a[1].x, sl.a[1].y, sl.a[1].z, sl.a[1].w};
+      const uint32_t r2[4] = {sl.a[2].x, sl.a[2].y, sl.a[2].z, sl.a[2].w};
+      const uint32_t r3[4] = {sl.a[3].x, sl.a[3].y, sl.a[3].z, sl.a[3].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint2 ev = make_uint2((r0[c] & 0xffffu) | (r1[c] << 16), (r2[c] & 0xffffu) | (r3[c] << 16));
+        const uint2 od = make_uint2((r0[c] >> 16) | (r1[c] & 0xffff0000u), (r2[c] >> 16) | (r3[c] & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&As[(mm + 2 * c) * kGemmLdsStride + kk]) = ev;
+        *reinterpret_cast<uint2*>(&As[(mm + 2 * c + 1) * kGemmLdsStride + kk]) = od;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = 32 * wave + 16 * i + l16;
-      const v8bf ab = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&As[row * kGemmLdsStride + 8 * lg]));
+    for (int u = 0; u < XU; ++u) {
+      const int idx = min(tid + u * kGemmThreads, XR * 8 - 1);
+      const int o = (idx >> 3) * kGemmLdsStride + 8 * (idx & 7);
+      *reinterpret_cast<uint4*>(&Xs[o]) = sl.x[u];
+      if constexpr (SPLIT) *reinterpret_cast<uint4*>(&Xs[XR * kGemmLdsStride + o]) = sl.xl[u];
+    }
+  };
+
+  Slice cur, nxt;
+  load_slice(0, cur);
+  for (int k0 = 0; k0 < K; k0 += kGemmBK) {
+    const bool more = k0 + kGemmBK < K;
+    if (more) load_slice(k0 + kGemmBK, nxt);   // in flight during this slice's MFMAs
+    stage(cur);
+    __syncthreads();
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      v8bf ab[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        ab[i] = __builtin_bit_cast(
+            v8bf, *reinterpret_cast<const uint4*>(&As[(32 * wave + 16 * i + l16) * kGemmLdsStride + 32 * s2 + 8 * lg]));
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
-        acc[i][c] = mfma_bf16_k32(ab, xb[c], acc[i][c]);
-        if constexpr (SPLIT) acc[i][c] = mfma_bf16_k32(ab, xl[c], acc[i][c]);
+        const int xo = (16 * c + l16) * kGemmLdsStride + 32 * s2 + 8 * lg;
+        const v8bf xb = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&Xs[xo]));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][c] = mfma_bf16_k32(ab[i], xb, acc[i][c]);
+        if constexpr (SPLIT) {
+          const v8bf xlb = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&Xs[XR * kGemmLdsStride + xo]));
+#pragma unroll
+          for (int i = 0; i < 2; ++i) acc[i][c] = mfma_bf16_k32(ab[i], xlb, acc[i][c]);
+        }
       }
     }
     __syncthreads();
+    if (more) cur = nxt;
   }
   // D tile: lane holds rows 4*lg + t, column l16
 #pragma unroll
@@ -325,6 +377,23 @@ __global__ __launch_bounds__(kGramThreads) void k_gram(const float* __restrict__
   for (int idx = tid; idx < ellp * ellp; idx += kGramThreads) {
     const int i = idx / ellp, j = idx % ellp;
     out[idx] = G[i * S + j];
+  }
+}
+
+// Sum of the partial Grams in a fixed order (deterministic), four floats per thread.
+__global__ __launch_bounds__(256) void k_gram_reduce(const float* __restrict__ Gpart, int nsplit, int nmat,
+                                                     int e2, float* __restrict__ G) {
+  const int e4 = e2 >> 2;   // e2 = ellp^2 is a multiple of 256
+  const size_t total = (size_t)nmat * e4;
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += (size_t)gridDim.x * blockDim.x) {
+    const size_t mat = g / e4, i = g % e4;
+    const float4* src = reinterpret_cast<const float4*>(Gpart + mat * nsplit * (size_t)e2) + i;
+    float4 acc = src[0];
+    for (int sp = 1; sp < nsplit; ++sp) {
+      const float4 v = src[(size_t)sp * e4];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    reinterpret_cast<float4*>(G + mat * (size_t)e2)[i] = acc;
   }
 }
 
@@ -502,51 +571,97 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
   }
 }
 
-constexpr int kApplyRows = 128;
+// Row tile of k_apply.
+static int apply_rows(int) { return 128; }
 
-// Q = Y Rinv for 128 rows per workgroup (fp32 MFMA), written in place; optionally
+// Q = Y Rinv for a tile of rows per workgroup (fp32 MFMA), written in place; optionally
 // Q^T in storage precision for the next product (XT[mat][j][m]), and the rounding
-// remainder Q^T - XT in XTlo for a two-term product.
+// remainder Q^T - XT in XTlo for a two-term product.  The Q tile is kept in LDS so
+// that Q^T leaves in 16-byte runs along m.
 template <class T>
 __global__ __launch_bounds__(256) void k_apply(float* __restrict__ Y, int M, int ellp,
                                                const float* __restrict__ Rinv, T* __restrict__ XT,
-                                               T* __restrict__ XTlo, size_t xt_mat_stride, int tiles_m) {
+                                               T* __restrict__ XTlo, size_t xt_mat_stride, int tiles_m,
+                                               int rows) {
   extern __shared__ __align__(16) float sh[];
+  constexpr int kMaxRT = 2, kMaxCT = kMaxEll / 16;   // row tiles per wavefront (rows = 128)
   const int S = ellp + 1;
-  float* Ys = sh;                  // [kApplyRows][S]
-  float* Rs = Ys + kApplyRows * S; // [ellp][ellp]
+  float* Ys = sh;                  // [rows][S]
+  float* Rs = Ys + rows * S;       // [ellp][ellp]
   const int mat = blockIdx.x / tiles_m;
-  const int m0 = (blockIdx.x % tiles_m) * kApplyRows;
+  const int m0 = (blockIdx.x % tiles_m) * rows;
   float* Ym = Y + (size_t)mat * M * ellp;
   const float* Rm = Rinv + (size_t)mat * ellp * ellp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  for (int idx = tid; idx < kApplyRows * ellp; idx += 256) {
+  for (int idx = tid; idx < rows * ellp; idx += 256) {
     const int r = idx / ellp, j = idx % ellp;
     Ys[r * S + j] = m0 + r < M ? Ym[(size_t)(m0 + r) * ellp + j] : 0.f;
   }
   for (int idx = tid; idx < ellp * ellp; idx += 256) Rs[idx] = Rm[idx];
   __syncthreads();
   const int T16 = ellp / 16;
-  // wave owns row tiles wave, wave + 4, ... (16 rows each), all column tiles
-  for (int rt = wave; rt < kApplyRows / 16; rt += 4)
-  for (int c = 0; c < T16; ++c) {
-    v4f acc = v4f{0, 0, 0, 0};
+  // wave owns row tiles wave and wave + 4 (16 rows each), all column tiles
+  v4f acc[kMaxRT][kMaxCT];
+#pragma unroll
+  for (int i = 0; i < kMaxRT; ++i)
+#pragma unroll
+    for (int c = 0; c < kMaxCT; ++c) acc[i][c] = v4f{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < kMaxRT; ++i) {
+    const int rt = wave + 4 * i;
     for (int k0 = 0; k0 < ellp; k0 += 4) {
       const float a = Ys[(16 * rt + l16) * S + k0 + lg];
-      const float bb = Rs[(k0 + lg) * ellp + 16 * c + l16];
-      acc = mfma_f32(a, bb, acc);
+#pragma unroll
+      for (int c = 0; c < kMaxCT; ++c)
+        if (c < T16) acc[i][c] = mfma_f32(a, Rs[(k0 + lg) * ellp + 16 * c + l16], acc[i][c]);
     }
-    for (int t = 0; t < 4; ++t) {
-      const int m = m0 + 16 * rt + 4 * lg + t, j = 16 * c + l16;
-      if (m < M) {
-        Ym[(size_t)m * ellp + j] = acc[t];
-        if (XT != nullptr) {
-          const size_t o = (size_t)mat * xt_mat_stride + (size_t)j * M + m;
-          const T hi = from_f32<T>(acc[t]);
-          XT[o] = hi;
-          if (XTlo != nullptr) XTlo[o] = from_f32<T>(acc[t] - to_f32<T>(hi));
-        }
+  }
+  __syncthreads();   // every read of the Y tile is done: it now takes Q
+#pragma unroll
+  for (int i = 0; i < kMaxRT; ++i) {
+    const int rt = wave + 4 * i;
+#pragma unroll
+    for (int c = 0; c < kMaxCT; ++c) {
+      if (c >= T16) continue;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 16 * rt + 4 * lg + t, j = 16 * c + l16;
+        Ys[r * S + j] = acc[i][c][t];
+        if (m0 + r < M) Ym[(size_t)(m0 + r) * ellp + j] = acc[i][c][t];
+      }
+    }
+  }
+  if (XT == nullptr) return;
+  __syncthreads();
+  // Q^T[j][m0 .. m0 + rows): 8 consecutive m per thread
+  const int R8 = rows / 8;
+  T* xt = XT + (size_t)mat * xt_mat_stride;
+  T* xl = XTlo != nullptr ? XTlo + (size_t)mat * xt_mat_stride : nullptr;
+  const bool vec = std::is_same<T, bf16_t>::value && (M & 7) == 0;
+  for (int idx = tid; idx < ellp * R8; idx += 256) {
+    const int j = idx / R8, m8 = idx - (idx / R8) * R8;
+    const int mb = m0 + 8 * m8;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = Ys[(8 * m8 + e) * S + j];
+    if (vec && mb + 8 <= M) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hw[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+        const float r0 = v[2 * e] - __uint_as_float(hw[e] << 16);
+        const float r1 = v[2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u);
+        lw[e] = pack_bf16x2(r0, r1);
+      }
+      *reinterpret_cast<uint4*>(xt + (size_t)j * M + mb) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      if (xl != nullptr) *reinterpret_cast<uint4*>(xl + (size_t)j * M + mb) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    } else {
+      for (int e = 0; e < 8; ++e) {
+        if (mb + e >= M) break;
+        const T hi = from_f32<T>(v[e]);
+        xt[(size_t)j * M + mb + e] = hi;
+        if (xl != nullptr) xl[(size_t)j * M + mb + e] = from_f32<T>(v[e] - to_f32<T>(hi));
       }
     }
   }
@@ -801,19 +916,23 @@ static void gram_split(int M, int nmat, int& rows, int& nsplit) {
   nsplit = (M + rows - 1) / rows;
 }
 
-// Two-pass Cholesky QR of Y [nmat][M][ellp] in place; Q^T to XT (if given); R to Racc (if given).
+// Shifted Cholesky QR of Y [nmat][M][ellp] in place, `passes` times (1 for bases that
+// only feed the next power-iteration product, 2 where U or B are built from the
+// basis); Q^T to XT after the last pass (if given); R to Racc (if given).
 template <class T>
 static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void* XTlo, float* Racc,
-                       hipStream_t st) {
+                       int passes, hipStream_t st) {
   const Dims& dm = c->dm;
   const int nmat = 2 * dm.B, ellp = ws.ellp;
   const size_t lds_gram = (size_t)ellp * (ellp + 1) * sizeof(float);
   const size_t lds_chol = (size_t)(2 * ellp * (ellp + 1) + 4 * 16 * 17) * sizeof(float);
-  const size_t lds_apply = (size_t)(kApplyRows * (ellp + 1) + ellp * ellp) * sizeof(float);
-  const int tiles_m = (M + kApplyRows - 1) / kApplyRows;
+  const int arows = apply_rows(ellp);
+  const size_t lds_apply = (size_t)(arows * (ellp + 1) + ellp * ellp) * sizeof(float);
+  const int tiles_m = (M + arows - 1) / arows;
   int rows, nsplit;
   gram_split(M, nmat, rows, nsplit);
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < passes; ++pass) {
+    const bool last = pass == passes - 1;
     switch (ellp / 16) {
 #define AP_GRAM_CASE(TV)                                                                              \
   case TV:                                                                                            \
@@ -825,14 +944,17 @@ static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void*
 #undef AP_GRAM_CASE
       default: return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(k_chol, dim3(nmat), dim3(kCholThreads), lds_chol, st, ws.Gpart, nsplit, dm.ell, ellp,
+    const float* Gsum = ws.Gpart;
+    if (nsplit > 1) {
+      hipLaunchKernelGGL(k_gram_reduce, grid_1d((size_t)nmat * ellp * ellp / 4), dim3(256), 0, st, ws.Gpart,
+                         nsplit, nmat, ellp * ellp, ws.Gsum);
+      Gsum = ws.Gsum;
+    }
+    hipLaunchKernelGGL(k_chol, dim3(nmat), dim3(kCholThreads), lds_chol, st, Gsum, 1, dm.ell, ellp,
                        ws.Rinv, pass == 0 ? nullptr : Racc, Racc);
-    if (pass == 0)
-      hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
-                         static_cast<T*>(nullptr), static_cast<T*>(nullptr), (size_t)0, tiles_m);
-    else
-      hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
-                         static_cast<T*>(XT), static_cast<T*>(XTlo), (size_t)ellp * ws.M, tiles_m);
+    hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
+                       static_cast<T*>(last ? XT : nullptr), static_cast<T*>(last ? XTlo : nullptr),
+                       (size_t)ellp * ws.M, tiles_m, arows);
   }
   return hipGetLastError();
 }
@@ -863,6 +985,7 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
       {reinterpret_cast<void**>(&ws.Qn), (size_t)nmat * dm.N * ellp * 4},
       {reinterpret_cast<void**>(&ws.Qc), (size_t)nmat * dm.W * ellp * 4},
       {reinterpret_cast<void**>(&ws.Gpart), (size_t)nmat * max_split * ellp * ellp * 4},
+      {reinterpret_cast<void**>(&ws.Gsum), (size_t)nmat * ellp * ellp * 4},
       {reinterpret_cast<void**>(&ws.Rinv), (size_t)nmat * ellp * ellp * 4},
       {reinterpret_cast<void**>(&ws.Racc), (size_t)nmat * ellp * ellp * 4},
       {reinterpret_cast<void**>(&ws.PS), (size_t)nmat * ellp * ellp * 4},
@@ -906,7 +1029,7 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   // dynamic LDS above the 64 KB default: request exactly what each launch uses
   const size_t lds_chol = (size_t)(2 * ellp * (ellp + 1) + 4 * 16 * 17) * sizeof(float);
   const size_t lds_jac = (size_t)(2 * ellp * (ellp + 1) + 2 * ellp) * sizeof(float);
-  const size_t lds_apply = (size_t)(kApplyRows * (ellp + 1) + ellp * ellp) * sizeof(float);
+  const size_t lds_apply = (size_t)(apply_rows(ellp) * (ellp + 1) + ellp * ellp) * sizeof(float);
   const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP) * sizeof(float);
   const size_t lds_b = (size_t)(64 * (ellp + 1) + ellp * dm.r_pad) * sizeof(float);
   const struct { const void* fn; size_t bytes; const char* name; } lds_req[] = {
@@ -927,19 +1050,21 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   // fp32 Q; with Q rounded to 8 bits here the two would disagree at 2^-9).
   e = gemm<T>(c, k, v, ws.omT, nullptr, ws.Y, false, (size_t)ellp * dm.W, st);
   if (e != hipSuccess) return fail_stage(e, "A Omega");
-  e = orth<T>(c, ws, dm.N, ws.XT, dm.q == 0 ? ws.XTlo : nullptr, nullptr, st);
+  e = orth<T>(c, ws, dm.N, ws.XT, dm.q == 0 ? ws.XTlo : nullptr, nullptr, dm.q == 0 ? 2 : 1, st);
   if (e != hipSuccess) return fail_stage(e, "orthonormalisation of A Omega");
   for (int it = 0; it < dm.q; ++it) {
+    const bool final_basis = it == dm.q - 1;
     e = gemm<T>(c, k, v, ws.XT, nullptr, ws.Y, true, (size_t)ellp * ws.M, st);     // A^T Q
-    if (e == hipSuccess) e = orth<T>(c, ws, dm.W, ws.XT, nullptr, nullptr, st);
+    if (e == hipSuccess) e = orth<T>(c, ws, dm.W, ws.XT, nullptr, nullptr, 1, st);
     if (e == hipSuccess) e = gemm<T>(c, k, v, ws.XT, nullptr, ws.Y, false, (size_t)ellp * ws.M, st);  // A Q~
-    if (e == hipSuccess) e = orth<T>(c, ws, dm.N, ws.XT, it == dm.q - 1 ? ws.XTlo : nullptr, nullptr, st);
+    if (e == hipSuccess)
+      e = orth<T>(c, ws, dm.N, ws.XT, final_basis ? ws.XTlo : nullptr, nullptr, final_basis ? 2 : 1, st);
     if (e != hipSuccess) return fail_stage(e, "power iteration");
   }
   // keep Q (fp32) for U, then C^T = A^T Q and its QR
   e = hipMemcpyAsync(ws.Qn, ws.Y, (size_t)nmat * dm.N * ellp * 4, hipMemcpyDeviceToDevice, st);
   if (e == hipSuccess) e = gemm<T>(c, k, v, ws.XT, ws.XTlo, ws.Y, true, (size_t)ellp * ws.M, st);
-  if (e == hipSuccess) e = orth<T>(c, ws, dm.W, nullptr, nullptr, ws.Racc, st);
+  if (e == hipSuccess) e = orth<T>(c, ws, dm.W, nullptr, nullptr, ws.Racc, 2, st);
   if (e == hipSuccess) e = hipMemcpyAsync(ws.Qc, ws.Y, (size_t)nmat * dm.W * ellp * 4, hipMemcpyDeviceToDevice, st);
   if (e != hipSuccess) return fail_stage(e, "projection C^T = A^T Q");
   const int jac_threads = std::min(1024, std::max(64, (16 * ((dm.ell + 1) / 2) + 63) / 64 * 64));
