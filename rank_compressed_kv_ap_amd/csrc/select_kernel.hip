@@ -133,15 +133,15 @@ __device__ __forceinline__ bool digit_search(const uint32_t* hist, uint32_t need
   return true;
 }
 
-// UB: blocks per wavefront whose U_k loads are in flight at once (16 with one low panel,
-// 8 with two); UB == 0 walks blocks one at a time (more than two low panels).
+// UB: blocks per wavefront whose U_k loads are in flight at once (12 or 16 with one low
+// panel, 8 with two); UB == 0 walks blocks one at a time (more than two low panels).
 template <class T, int UB>
 __global__ __launch_bounds__(kSelThreads) void k_select(
     const T* __restrict__ Uk, const T* __restrict__ Bk, const float* __restrict__ rn,
     const float* __restrict__ q, float* __restrict__ qt, uint32_t* __restrict__ mask,
     int32_t* __restrict__ sel_out, int B, int N, int N_pad, int nblk, int NP, int r_pad, int W,
     int d, int G, int Hq, int Hq_pad, int Hg, int HG, int r_lo, int top_k) {
-  constexpr int NPL = UB == 16 ? 1 : 2;   // low panels held per block
+  constexpr int NPL = UB >= 12 ? 1 : 2;   // low panels held per block
   constexpr int UBA = UB > 0 ? UB : 1;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   // All head groups of one sequence share blockIdx % 8 (one XCD), so its L2 serves
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
   // them), then q, then the first batch of U_k low panels
   LaneTile<T> a[UBA][NPL];
   constexpr int V = Vec16<T>::n;
-  constexpr int XB = 16;   // B_k row slices per lane in flight
+  constexpr int XB = 8;    // B_k row slices per lane in flight (256 rows of 16 lanes per pass)
   const int ginv_num = (65536 + G - 1) / G;   // (h * ginv_num) >> 16 == h / G for h, G <= 64
   const int LPR = d / V;
   const bool vec = d % V == 0 && LPR > 0 && LPR <= 64 && (LPR & (LPR - 1)) == 0 &&
@@ -626,13 +626,15 @@ static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, i
   const size_t lds = select_lds_bytes(dm, Hg);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const int nplo = (r_lo + 15) / 16;
-  const void* fn = nplo == 1 ? reinterpret_cast<const void*>(&k_select<T, 16>)
-                 : (nplo == 2 ? reinterpret_cast<const void*>(&k_select<T, 8>)
-                              : reinterpret_cast<const void*>(&k_select<T, 0>));
-  static bool attr_set[3] = {false, false, false};
-  const int which = nplo == 1 ? 0 : (nplo == 2 ? 1 : 2);
+  // one low panel: 12 blocks per wavefront in flight when that covers the sequence
+  const int which = nplo == 1 ? (dm.nblk <= 12 * kSelWaves ? 0 : 1) : (nplo == 2 ? 2 : 3);
+  const void* fns[4] = {reinterpret_cast<const void*>(&k_select<T, 12>),
+                        reinterpret_cast<const void*>(&k_select<T, 16>),
+                        reinterpret_cast<const void*>(&k_select<T, 8>),
+                        reinterpret_cast<const void*>(&k_select<T, 0>)};
+  static bool attr_set[4] = {false, false, false, false};
   if (!attr_set[which]) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e = hipFuncSetAttribute(fns[which], hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set[which] = true;
   }
@@ -640,12 +642,15 @@ static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, i
 #define AP_SELECT_ARGS static_cast<const T*>(c->Uk), static_cast<const T*>(c->Bk), c->rn, q, c->qt, \
       c->mask, sel_out, dm.B, dm.N, dm.N_pad, dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d, dm.G, dm.Hq,  \
       dm.Hq_pad, Hg, HG, r_lo, top_k
-  if (nplo == 1)
-    hipExtLaunchKernelGGL((k_select<T, 16>), dim3(grid), dim3(kSelThreads), lds, st, ev.start, ev.stop, 0, AP_SELECT_ARGS);
-  else if (nplo == 2)
-    hipExtLaunchKernelGGL((k_select<T, 8>), dim3(grid), dim3(kSelThreads), lds, st, ev.start, ev.stop, 0, AP_SELECT_ARGS);
-  else
-    hipExtLaunchKernelGGL((k_select<T, 0>), dim3(grid), dim3(kSelThreads), lds, st, ev.start, ev.stop, 0, AP_SELECT_ARGS);
+#define AP_SELECT_LAUNCH(UBV) \
+  hipExtLaunchKernelGGL((k_select<T, UBV>), dim3(grid), dim3(kSelThreads), lds, st, ev.start, ev.stop, 0, AP_SELECT_ARGS)
+  switch (which) {
+    case 0: AP_SELECT_LAUNCH(12); break;
+    case 1: AP_SELECT_LAUNCH(16); break;
+    case 2: AP_SELECT_LAUNCH(8); break;
+    default: AP_SELECT_LAUNCH(0); break;
+  }
+#undef AP_SELECT_LAUNCH
 #undef AP_SELECT_ARGS
   return hipGetLastError();
 }
