@@ -48,7 +48,6 @@ struct ap_cache {
   void* Bv = nullptr;
   float* sigma_k = nullptr;  // [B][r]
   float* sigma_v = nullptr;
-  float* rn = nullptr;        // [B][NP] max_n |U_k[n, :16(p+1)]|, bounds the low-rank scores
   // decode workspace
   float* qt = nullptr;        // [B][Hq_pad][r_pad] latent queries
   uint32_t* mask = nullptr;   // [B][nblk][Hq_pad] selection bits per 32-token block
@@ -78,11 +77,6 @@ hipError_t launch_attn(const ap_cache* c, int r_lo, float scale_log2e, int S, in
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float scale_log2e,
                           int S, int T, const void* text_k, const void* text_v, hipStream_t st,
                           const KernelEvents& ev);
-
-// ---- launchers (select_kernel.hip)
-int select_heads_per_group(const Dims& dm);
-size_t select_lds_bytes(const Dims& dm, int Hg);
-hipError_t launch_rownorm(const ap_cache* c, hipStream_t st);
 
 // ---- launchers (pack_kernels.hip)
 hipError_t launch_pack_u(const ap_cache* c, const void* src, void* dst, bool v_layout,

@@ -79,7 +79,7 @@ static Dims make_dims(const ap_compress_params* p) {
 }
 
 static void free_all(ap_cache* c) {
-  void* ptrs[] = {c->Uk, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->rn, c->qt, c->mask, c->part_z, c->part_ml};
+  void* ptrs[] = {c->Uk, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->qt, c->mask, c->part_z, c->part_ml};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   for (hipEvent_t e : c->timing.ev) (void)hipEventDestroy(e);
@@ -96,7 +96,6 @@ static ap_status alloc_cache(ap_cache* c) {
       {&c->Bv, (size_t)dm.B * dm.r_pad * dm.W * dm.esize},
       {reinterpret_cast<void**>(&c->sigma_k), (size_t)dm.B * dm.r * 4},
       {reinterpret_cast<void**>(&c->sigma_v), (size_t)dm.B * dm.r * 4},
-      {reinterpret_cast<void**>(&c->rn), (size_t)dm.B * dm.NP * 4},
       {reinterpret_cast<void**>(&c->qt), (size_t)dm.B * dm.Hq_pad * dm.r_pad * 4},
       {reinterpret_cast<void**>(&c->mask), (size_t)dm.B * dm.nblk * dm.Hq_pad * 4},
       {reinterpret_cast<void**>(&c->part_z), (size_t)dm.B * dm.S_cap * dm.Hq_pad * dm.r_pad * 4},
@@ -234,7 +233,6 @@ ap_status ap_cache_set_factors(ap_cache* c, const void* U_k, const void* B_k, co
   const size_t dpitch = (size_t)dm.r_pad * dm.W * dm.esize;
   if (e == hipSuccess) e = hipMemcpy2DAsync(c->Bk, dpitch, B_k, row, row, dm.B, hipMemcpyDeviceToDevice, st);
   if (e == hipSuccess) e = hipMemcpy2DAsync(c->Bv, dpitch, B_v, row, row, dm.B, hipMemcpyDeviceToDevice, st);
-  if (e == hipSuccess) e = launch_rownorm(c, st);
   if (e != hipSuccess) return hip_fail(e, "set_factors");
   return AP_OK;
 }

@@ -1080,7 +1080,6 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   hipLaunchKernelGGL(k_copy_sigma, grid_1d((size_t)nmat * dm.r), dim3(256), 0, st, ws.sig, c->sigma_k,
                      c->sigma_v, nmat, ellp, dm.r);
   e = hipGetLastError();
-  if (e == hipSuccess) e = launch_rownorm(c, st);
   if (e != hipSuccess) return fail_stage(e, "factor assembly");
   release();
   return e;

@@ -11,8 +11,9 @@
 //
 // Three kernels per call:
 //   k_select  (sequence, head group): latent queries q~ = B_k,g q_h, low-rank scores
-//             for every token by MFMA, exact top-k by MSB-first radix select over
-//             order-preserving keys held in LDS, selection bitmask per 32-token block.
+//             for every token by MFMA (kept in registers), exact top-k through a
+//             linear-bin histogram and an exact resolution of the boundary bin,
+//             selection bitmask per 32-token block.
 //   k_attn    (sequence, N-split): mixed-rank rescoring, online softmax and latent V
 //             accumulation on MFMA tiles, cross-wavefront merge in LDS, one partial
 //             (m, l, z[Hq][r]) per split.

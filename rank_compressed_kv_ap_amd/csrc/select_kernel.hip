@@ -5,20 +5,23 @@
 // token n for query head h is its low-rank logit s_lo = U_k[n, :r_lo] . q~_h[:r_lo];
 // the k largest are chosen, ties to the lower token index.
 //
-// One workgroup per (sequence, group of query heads):
-//  0. latent queries q~_h = B_k[:, head g's columns] q_h (written for the flash-decode
-//     kernel as well);
-//  1. low-rank scores of every token by MFMA; each score is mapped to a 16-bit bin by a
-//     monotone linear map over [-M_h, M_h], where M_h = |q~_h[:r_lo]| * max_n |U_k[n,:r_lo]|
-//     bounds |s_lo| (Cauchy-Schwarz).  Bins (2 bytes per token) stay in LDS;
-//  2. two 8-bit histogram passes over the bins locate the bin b* holding the k-th
-//     largest score and how many of its tokens are still needed;
-//  3. if only part of b* is taken, its tokens' exact scores are recomputed (same MFMA
-//     sequence, so bit-identical) and ranked exactly by (score desc, index asc); if b*
-//     is very large (ties, a zero query) an exact radix select over recomputed 32-bit
-//     keys decides instead;
-//  4. one wavefront per head writes the selection bitmask per 32-token block (and, on
-//     request, the ascending selected ids).
+// One workgroup per (sequence, group of HG query heads), 16 wavefronts:
+//  A. latent queries q~_h = B_k[:, head g's columns] q_h (also written out for the
+//     flash-decode kernel), with the first U_k low-panel tiles already in flight;
+//  B. low-rank scores of every token on MFMA.  The 16 output columns of a 16x16x32 tile
+//     are (token block, tile half, head) triples: the latent-query operand of a column
+//     is non-zero only in the k-slots of its own half and only for its own block, so
+//     one accumulation yields the scores of 8/HG blocks x 32 tokens x HG heads and
+//     every lane holds four scores of one head.  Scores stay in registers;
+//  C. each head's scores are mapped by a monotone linear map over [min, max] onto
+//     2048 bins; one LDS histogram locates the bin b* holding the k-th largest score;
+//  D. tokens above b* are taken; inside b*, either all of it is taken, or its few
+//     tokens are ranked exactly by (score desc, index asc), or - when b* is crowded
+//     (ties, a zero query, an outlier stretching the range) - an MSB-first radix
+//     select over the exact 32-bit keys finds the cutoff key and ties at it are
+//     taken in index order;
+//  E. the selection bits per (head, 32-token block) are written (and, on request, the
+//     ascending selected ids).
 #include <hip/hip_ext.h>
 
 #include "ap_internal.h"
@@ -27,83 +30,84 @@
 
 namespace ap {
 
-constexpr int kSelThreads = 512;     // 8 wavefronts
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kMaxHg = 8;             // heads per workgroup (one wavefront per head in per-head steps)
-constexpr int kSelCap = 128;          // boundary-bin tokens resolved by exact ranking
-constexpr int kSelList = 512;         // tokens of the coarse boundary digit remembered per head
+constexpr int kSelMaxWaves = 16;
+constexpr int kSelBins = 2048;   // linear bins of the histogram pass
+constexpr int kSelCap = 128;     // boundary-bin tokens ranked exactly by comparison
 
 enum SelMode : int { kNone = 0, kAll = 1, kWholeBin = 2, kRank = 3, kRadix = 4 };
 
 struct SelState {
-  int nlist;      // tokens of the coarse boundary digit (list holds the first kSelList)
-  int bstar;      // boundary bin (coarse digit after the first pass)
-  int need;       // tokens still to take inside the boundary bin
-  int cnt;        // tokens in the boundary bin
+  float lo, mul;   // bin(s) = min(kSelBins - 1, (s - lo) * mul)
+  int bstar;       // boundary bin
+  int need;        // tokens still to take inside the boundary bin (radix: ties at tau)
+  int cnt;         // tokens in the boundary bin
   int mode;
-  int ncand;      // candidates gathered (kRank)
-  uint32_t tau;   // kRadix: key of the k-th token
-  unsigned long long thr;  // kRank: composite (key << 32 | ~index) of the k-th token
+  int ncand;       // kRank: candidates gathered
+  uint32_t tau;    // kRadix: key of the last token taken
 };
 
 struct SelLayout {
-  size_t bins, hc, selb, qs, mm, st, bflag, list, total;
+  size_t qh, qs, st, rng, hist, selw, cand, total;
+  int hs;          // words per head in hist
 };
 
-// hc holds the 256-bin histogram of each head, later its candidates (kSelCap x 8 bytes);
-// selb holds the q vectors while the latent queries are formed, later the selected-token
-// bits of the boundary bin.
-__host__ __device__ inline SelLayout sel_layout(int Hg, int N_pad, int nblk, int r_pad, int d) {
+// hist holds each head's bin counts; in the radix fallback it is reused as
+// [256 digit counts][nblk tie bits][nblk tie prefix] per head.
+__host__ __device__ inline SelLayout sel_layout(int HG, int nblk, int r_pad, int d) {
   auto up = [](size_t x) { return (x + 15) & ~(size_t)15; };
   SelLayout L;
+  L.hs = kSelBins > 256 + 2 * nblk ? kSelBins : 256 + 2 * nblk;
   size_t o = 0;
-  L.bins = o;  o = up(o + (size_t)Hg * N_pad * 2);
-  L.hc = o;    o = up(o + (size_t)Hg * 256 * 4);
-  L.selb = o;  o = up(o + (size_t)Hg * (nblk > d ? nblk : d) * 4);
-  L.qs = o;    o = up(o + (size_t)Hg * r_pad * 4);
-  L.mm = o;    o = up(o + (size_t)Hg * 2 * 4);
-  L.st = o;    o = up(o + (size_t)Hg * sizeof(SelState));
-  L.bflag = o; o = up(o + (size_t)nblk * 4);
-  L.list = o;  o = up(o + (size_t)Hg * kSelList * 2);
+  L.qh = o;   o = up(o + (size_t)(HG * d > 1024 ? HG * d : 1024) * 4);   // >= one float per thread
+  L.qs = o;   o = up(o + (size_t)HG * r_pad * 4);
+  L.st = o;   o = up(o + (size_t)HG * sizeof(SelState));
+  L.rng = o;  o = up(o + (size_t)HG * 2 * 4);
+  L.hist = o; o = up(o + (size_t)HG * L.hs * 4);
+  L.selw = o; o = up(o + (size_t)HG * nblk * 4);
+  L.cand = o; o = up(o + (size_t)HG * kSelCap * 8);
   L.total = o;
   return L;
 }
 
-// Monotone map of a score to a 16-bit bin: floor((s + M) * mul) clamped to [0, 65535],
-// computed as one fused multiply-add (Mmul = M * mul) and a median-of-three clamp.
-__device__ __forceinline__ uint32_t score_bin(float s, float Mmul, float mul) {
-  const float x = __builtin_amdgcn_fmed3f(fmaf(s, mul, Mmul), 0.f, 65535.f);
-  return static_cast<uint32_t>(x);
+// Inverse of score_key.
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Low-rank score operand of panel p for this lane (head l%16, columns 16p+4(l/16)+e < r_lo).
-template <class T>
-__device__ __forceinline__ QOp<T> low_qop(const float* qs, int r_pad, int nh, int r_lo, int p, int lane) {
-  const int l16 = lane & 15, c0 = 16 * p + 4 * (lane >> 4);
-  float v[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = (l16 < nh && c0 + e < r_lo) ? qs[l16 * r_pad + c0 + e] : 0.f;
-  QOp<T> qo;
-  qo.set(v);
-  return qo;
+template <int N>
+__device__ __forceinline__ uint32_t dpp_ror(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x120 + N, 0xF, 0xF, true));
 }
 
-// Scores of the 32 tokens of block blk (lane head = l%16); the MFMA sequence is the same
-// one every pass uses, so a recomputed score is bit-identical to the first.
-template <class T>
-__device__ __forceinline__ void score_block(const T* __restrict__ Uk, int b, int blk, int NP,
-                                            int nblk, int r_lo, const float* qs, int r_pad,
-                                            int nh, int lane, v4f& a0, v4f& a1) {
-  const int nplo = (r_lo + 15) >> 4;
-  a0 = v4f{0, 0, 0, 0};
-  a1 = v4f{0, 0, 0, 0};
-  for (int p = 0; p < nplo; ++p) {
-    LaneTile<T> a;
-    a.load(Uk + tile_base(b, p, blk, NP, nblk), lane);
-    const QOp<T> qo = low_qop<T>(qs, r_pad, nh, r_lo, p, lane);
-    a0 = score_mma(a, 0, qo, a0);
-    a1 = score_mma(a, 1, qo, a1);
-  }
+// Maximum over the lanes of a wavefront that hold the same head (lane%16 congruent
+// mod HG): rotations by HG, 2HG, .. inside each 16-lane row, then across the 4 rows.
+template <int HG>
+__device__ __forceinline__ uint32_t head_max(uint32_t v) {
+  if constexpr (HG <= 1) v = max(v, dpp_ror<1>(v));
+  if constexpr (HG <= 2) v = max(v, dpp_ror<2>(v));
+  if constexpr (HG <= 4) v = max(v, dpp_ror<4>(v));
+  if constexpr (HG <= 8) v = max(v, dpp_ror<8>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(c[0], c[1]);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP only: shifts by 1, 2, 4, 8 inside
+// each 16-lane row (lanes shifted in from outside the row read 0), then lane 15 of each
+// row added to the next row and lane 31 to the upper half.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, true));
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int) {
+  v += dpp_u32<0x111, 0xF>(v);   // row_shr:1
+  v += dpp_u32<0x112, 0xF>(v);   // row_shr:2
+  v += dpp_u32<0x114, 0xF>(v);   // row_shr:4
+  v += dpp_u32<0x118, 0xF>(v);   // row_shr:8
+  v += dpp_u32<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_u32<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
 // Wavefront search over a 256-bin histogram (descending digit order): the digit D whose
@@ -113,12 +117,7 @@ __device__ __forceinline__ bool digit_search(const uint32_t* hist, uint32_t need
   const uint4 c4 = *reinterpret_cast<const uint4*>(hist + 252 - 4 * lane);  // bins 252-4l..255-4l
   const uint32_t c0 = c4.w, c1 = c4.z, c2 = c4.y, c3 = c4.x;               // descending digits
   const uint32_t tot = c0 + c1 + c2 + c3;
-  uint32_t incl = tot;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(tot, lane);
   const uint32_t excl = incl - tot;
   if (!(excl < need && incl >= need)) return false;
   uint32_t run = excl;
@@ -133,58 +132,156 @@ __device__ __forceinline__ bool digit_search(const uint32_t* hist, uint32_t need
   return true;
 }
 
-// UB: blocks per wavefront whose U_k loads are in flight at once (12 or 16 with one low
-// panel, 8 with two); UB == 0 walks blocks one at a time (more than two low panels).
-template <class T, int UB>
-__global__ __launch_bounds__(kSelThreads) void k_select(
-    const T* __restrict__ Uk, const T* __restrict__ Bk, const float* __restrict__ rn,
-    const float* __restrict__ q, float* __restrict__ qt, uint32_t* __restrict__ mask,
-    int32_t* __restrict__ sel_out, int B, int N, int N_pad, int nblk, int NP, int r_pad, int W,
-    int d, int G, int Hq, int Hq_pad, int Hg, int HG, int r_lo, int top_k) {
-  constexpr int NPL = UB >= 12 ? 1 : 2;   // low panels held per block
-  constexpr int UBA = UB > 0 ? UB : 1;
+// The same search over kSelBins bins, by a whole wavefront: lane l first sums bins
+// [kSelBins-32(l+1), kSelBins-32l); then the 32 bins of the slice holding the need-th
+// element are scanned one per lane.  Every lane returns the result.
+__device__ __forceinline__ void bin_search(const uint32_t* hist, uint32_t need, int lane,
+                                           int* bin, uint32_t* above, uint32_t* in_bin) {
+  static_assert(kSelBins == 64 * 32, "one 32-bin slice per lane");
+  const uint4* sl = reinterpret_cast<const uint4*>(hist + kSelBins - 32 * (lane + 1));
+  uint32_t tot = 0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const uint4 x = sl[v];
+    tot += x.x + x.y + x.z + x.w;
+  }
+  const uint32_t incl = wave_incl_scan(tot, lane);
+  const uint32_t excl = incl - tot;
+  const uint64_t hit = __ballot(excl < need && incl >= need);
+  const int L = hit ? static_cast<int>(__ffsll(static_cast<unsigned long long>(hit))) - 1 : 63;
+  const uint32_t base = __shfl(excl, L, 64);
+  // bins of slice L in descending order, lanes 0..31
+  const int bn = kSelBins - 32 * L - 1 - (lane & 31);
+  const uint32_t c = lane < 32 ? hist[bn] : 0u;
+  const uint32_t ci = base + wave_incl_scan(c, lane);
+  const uint64_t hit2 = __ballot(lane < 32 && ci >= need);
+  const int e = hit2 ? static_cast<int>(__ffsll(static_cast<unsigned long long>(hit2))) - 1 : 31;
+  *bin = kSelBins - 32 * L - 1 - e;
+  *in_bin = __shfl(c, e, 64);
+  *above = __shfl(ci, e, 64) - *in_bin;
+}
+
+// Scores of one accumulation step (one panel): NSL tiles of 32 tokens.  Column
+// c = l%16 of the tile is (block slot c / 2HG, half (c / HG) % 2, head c % HG); its
+// latent-query operand is this lane's 4 values placed in the k-slots of its half,
+// and zero for every other slot.
+template <int NSL>
+__device__ __forceinline__ v4f score_step(const LaneTile<bf16_t> (&t)[NSL], uint4 bh, uint4 bl,
+                                          int my_slot, int my_j, v4f acc) {
+  (void)my_j;
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
+    const bool on = sl == my_slot;
+    const uint4 h = on ? bh : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 l = on ? bl : make_uint4(0u, 0u, 0u, 0u);
+    const v8bf a = __builtin_bit_cast(v8bf, t[sl].raw);
+    acc = mfma_bf16_k32(a, __builtin_bit_cast(v8bf, h), acc);
+    acc = mfma_bf16_k32(a, __builtin_bit_cast(v8bf, l), acc);
+  }
+  return acc;
+}
+template <int NSL>
+__device__ __forceinline__ v4f score_step(const LaneTile<float> (&t)[NSL], const float (&qv)[4],
+                                          int my_slot, int my_j, v4f acc) {
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const bool on = sl == my_slot && hf == my_j;
+      const float4 x = t[sl].half(hf);
+      acc = mfma_f32(x.x, on ? qv[0] : 0.f, acc);
+      acc = mfma_f32(x.y, on ? qv[1] : 0.f, acc);
+      acc = mfma_f32(x.z, on ? qv[2] : 0.f, acc);
+      acc = mfma_f32(x.w, on ? qv[3] : 0.f, acc);
+    }
+  }
+  return acc;
+}
+
+// Latent-query operand of one panel for this lane (head my_h, columns 16p+4lg+e < r_lo).
+template <class T> struct SelQ;
+template <> struct SelQ<bf16_t> {
+  uint4 h, l;
+  __device__ __forceinline__ void set(const float v[4], int my_j) {
+    QOp<bf16_t> qo;
+    qo.set(v);
+    const uint2 hh = __builtin_bit_cast(uint2, qo.hi), ll = __builtin_bit_cast(uint2, qo.lo);
+    h = my_j == 0 ? make_uint4(hh.x, hh.y, 0u, 0u) : make_uint4(0u, 0u, hh.x, hh.y);
+    l = my_j == 0 ? make_uint4(ll.x, ll.y, 0u, 0u) : make_uint4(0u, 0u, ll.x, ll.y);
+  }
+  template <int NSL>
+  __device__ __forceinline__ v4f step(const LaneTile<bf16_t> (&t)[NSL], int my_slot, int my_j, v4f acc) const {
+    return score_step<NSL>(t, h, l, my_slot, my_j, acc);
+  }
+};
+template <> struct SelQ<float> {
+  float v[4];
+  __device__ __forceinline__ void set(const float x[4], int) {
+    for (int e = 0; e < 4; ++e) v[e] = x[e];
+  }
+  template <int NSL>
+  __device__ __forceinline__ v4f step(const LaneTile<float> (&t)[NSL], int my_slot, int my_j, v4f acc) const {
+    return score_step<NSL>(t, v, my_slot, my_j, acc);
+  }
+};
+
+// HG: query heads per workgroup (4 or 1); NPL: low panels (1 or 2 with the tiles of
+// several steps in flight; 8 = any count up to 8, one panel's tiles at a time); NACC:
+// accumulation steps per wavefront (2, 3, 4 or 8).
+template <class T, int HG, int NPL, int NACC>
+__global__ __launch_bounds__(1024) void k_select(
+    const T* __restrict__ Uk, const T* __restrict__ Bk, const float* __restrict__ q,
+    float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
+    int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
+    int r_lo, int top_k) {
+  constexpr int NSL = 8 / HG;                                   // token blocks per step
+  constexpr int KPL = 4 * NACC;                                 // scores per lane
+  constexpr int NSTEP = NACC * NPL;
+  constexpr int TREG = static_cast<int>(sizeof(LaneTile<T>) / 4);
+  constexpr int PBUD = (NACC <= 4 ? 64 : 32) / TREG / NSL;      // steps in flight (register budget)
+  constexpr int PREF = PBUD < 1 ? 1 : (PBUD > NSTEP ? NSTEP : PBUD);
   extern __shared__ __align__(16) unsigned char smem_raw[];
   // All head groups of one sequence share blockIdx % 8 (one XCD), so its L2 serves
   // the repeated reads of U_k's low panels.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, slot = bid >> 3;
-  const int b = (slot / HG) * 8 + xcd;
-  const int hg = slot % HG;
+  const int b = (slot / HGN) * 8 + xcd;
+  const int hg = slot % HGN;
   if (b >= B) return;
-  const int h0 = hg * Hg;
-  const int nh = min(Hg, Hq - h0);
+  const int h0 = hg * HG;
+  const int nh = min(HG, Hq - h0);
   if (nh <= 0) return;
+  const int nthr = blockDim.x, nwv = nthr >> 6;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;
+  const int c16 = lane & 15, lg = lane >> 4;
+  const int my_slot = c16 / (2 * HG), my_j = (c16 / HG) & 1, my_h = c16 % HG;
+  const bool my_on = my_h < nh;
 
-  const SelLayout Ly = sel_layout(Hg, N_pad, nblk, r_pad, d);
-  uint16_t* bins = reinterpret_cast<uint16_t*>(smem_raw + Ly.bins);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem_raw + Ly.hc);
-  unsigned long long* cand = reinterpret_cast<unsigned long long*>(smem_raw + Ly.hc);
-  uint32_t* selb = reinterpret_cast<uint32_t*>(smem_raw + Ly.selb);
-  float* qh = reinterpret_cast<float*>(smem_raw + Ly.selb);
+  const SelLayout Ly = sel_layout(HG, nblk, r_pad, d);
+  float* qh = reinterpret_cast<float*>(smem_raw + Ly.qh);
   float* qs = reinterpret_cast<float*>(smem_raw + Ly.qs);
-  float* mm = reinterpret_cast<float*>(smem_raw + Ly.mm);
   SelState* st = reinterpret_cast<SelState*>(smem_raw + Ly.st);
-  uint32_t* bflag = reinterpret_cast<uint32_t*>(smem_raw + Ly.bflag);
-  uint16_t* list = reinterpret_cast<uint16_t*>(smem_raw + Ly.list);
+  uint32_t* rng = reinterpret_cast<uint32_t*>(smem_raw + Ly.rng);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem_raw + Ly.hist);
+  uint32_t* selw = reinterpret_cast<uint32_t*>(smem_raw + Ly.selw);
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(smem_raw + Ly.cand);
+  const int HS = Ly.hs;
 
   const bool none = top_k <= 0, all = top_k >= N;
   const bool select = !none && !all;
   const int nplo = (r_lo + 15) >> 4;
 
   // ---- A. loads in flight together: B_k rows first (the latent queries wait only for
-  // them), then q, then the first batch of U_k low panels
-  LaneTile<T> a[UBA][NPL];
+  // them), then q, then the first U_k low-panel tiles
   constexpr int V = Vec16<T>::n;
-  constexpr int XB = 8;    // B_k row slices per lane in flight (256 rows of 16 lanes per pass)
+  constexpr int XB = 4;    // B_k row slices per lane in flight
   const int ginv_num = (65536 + G - 1) / G;   // (h * ginv_num) >> 16 == h / G for h, G <= 64
   const int LPR = d / V;
   const bool vec = d % V == 0 && LPR > 0 && LPR <= 64 && (LPR & (LPR - 1)) == 0 &&
                    ((size_t)W * sizeof(T)) % 16 == 0;
   const int nrows = nh * r_pad;
   const int RPW = vec ? 64 / LPR : 1, seg = vec ? lane % LPR : 0, rw = vec ? lane / LPR : 0;
-  const int rstep = kSelWaves * RPW;
+  const int rstep = nwv * RPW;
   const float inv_rpad = 1.0f / static_cast<float>(r_pad);
   // head of a flattened (head, latent row) index without an integer division:
   // (row + 0.5) / r_pad is never within float rounding of an integer here
@@ -199,28 +296,33 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     }
   };
   if (vec) load_rows(wave * RPW + rw);
-  constexpr int QPT = (kMaxHg * 256 + kSelThreads - 1) / kSelThreads;   // q values per thread
-  float qv[QPT];
+  // one q value per thread (HG * d <= 1024 threads); stored unconditionally below so the
+  // load is never sunk behind the tile loads
   const int nq = nh * d;
+  const float qv = q[((size_t)b * Hq + h0) * d + min(tid, nq - 1)];
+
+  LaneTile<T> tb[PREF][NSL];
+  auto load_step = [&](int s) {   // s is a compile-time constant after unrolling
+    const int a = s / NPL, p = s % NPL;
+    const int grp = wave + nwv * a;
 #pragma unroll
-  for (int u = 0; u < QPT; ++u) qv[u] = q[((size_t)b * Hq + h0) * d + min(tid + u * kSelThreads, nq - 1)];
-  if (UB > 0 && select) {
-#pragma unroll
-    for (int u = 0; u < UBA; ++u) {
-      const int blk = min(wave + u * kSelWaves, nblk - 1);   // clamped: loads stay unconditional
-      a[u][0].load(Uk + tile_base(b, 0, blk, NP, nblk), lane);
-      if (NPL > 1) a[u][NPL - 1].load(Uk + tile_base(b, NPL - 1, blk, NP, nblk), lane);
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int blk = min(grp * NSL + sl, nblk - 1);   // clamped: loads stay unconditional
+      tb[s % PREF][sl].load(Uk + tile_base(b, min(p, nplo - 1), blk, NP, nblk), lane);
     }
-  }
+  };
+  if constexpr (NPL <= 2) {
 #pragma unroll
-  for (int u = 0; u < QPT; ++u)
-    if (tid + u * kSelThreads < nq) qh[tid + u * kSelThreads] = qv[u];
-  for (int i = tid; i < nh * 256; i += kSelThreads) hist[i] = 0;
-  for (int i = tid; i < nblk; i += kSelThreads) bflag[i] = 0;
+    for (int s = 0; s < PREF; ++s) load_step(s);
+  }
+  qh[tid] = qv;
+  for (int i = tid; i < nh * HS; i += nthr) hist[i] = 0;
+  for (int i = tid; i < nh * nblk; i += nthr) selw[i] = 0;
   if (tid < nh) {
     st[tid].mode = none ? kNone : (all ? kAll : kWholeBin);
     st[tid].ncand = 0;
-    st[tid].nlist = 0;
+    rng[2 * tid] = 0u;
+    rng[2 * tid + 1] = 0u;
   }
   __syncthreads();
   // latent queries q~[h][i] = B_k[i, g*d : g*d+d] . q_h
@@ -232,124 +334,137 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         const int row = r0 + u * rstep;
         float part = 0.f;
         if (row < nrows) {
-          const float* qv = qh + head_of(row) * d + seg * V;
+          const float* qp = qh + head_of(row) * d + seg * V;
 #pragma unroll
-          for (int e = 0; e < V; ++e) part = fmaf(x[u].get(e), qv[e], part);
+          for (int e = 0; e < V; ++e) part = fmaf(x[u].get(e), qp[e], part);
         }
         part = group_sum(part, LPR);
         if (seg == 0 && row < nrows) qs[row] = part;   // row = hl * r_pad + i
       }
     }
   } else {
-    for (int idx = tid; idx < nrows; idx += kSelThreads) {
+    for (int idx = tid; idx < nrows; idx += nthr) {
       const int hl = idx / r_pad, i = idx - hl * r_pad;
       const T* brow = Bk + ((size_t)b * r_pad + i) * W + (size_t)((h0 + hl) / G) * d;
-      const float* qv = qh + hl * d;
+      const float* qp = qh + hl * d;
       float acc = 0.f;
-      for (int j = 0; j < d; ++j) acc = fmaf(to_f32(brow[j]), qv[j], acc);
+      for (int j = 0; j < d; ++j) acc = fmaf(to_f32(brow[j]), qp[j], acc);
       qs[hl * r_pad + i] = acc;
     }
   }
   __syncthreads();
 
   if (select) {
-    // ---- B. score bounds; scores -> 16-bit bins; coarse histogram
-    if (tid < nh) {
-      float n2 = 0.f;
-      for (int i = 0; i < r_lo; ++i) n2 = fmaf(qs[tid * r_pad + i], qs[tid * r_pad + i], n2);
-      const float M = sqrtf(n2) * rn[(size_t)b * NP + nplo - 1] * 1.0001f + 1e-30f;
-      const float mul = (M < 3.0e38f && M > 1e-30f) ? 32767.0f / M : 0.f;
-      mm[2 * tid] = M * mul;
-      mm[2 * tid + 1] = mul;
-    }
-    __syncthreads();
-    const float Mmulh = l16 < nh ? mm[2 * l16] : 0.f, mulh = l16 < nh ? mm[2 * l16 + 1] : 0.f;
-    auto put = [&](int blk, int t, float sv) {
-      const int n = blk * kBlockTok + 16 * (t >> 2) + 4 * lg + (t & 3);
-      if (n < N) {
-        const uint32_t bn = score_bin(sv, Mmulh, mulh);
-        bins[(size_t)l16 * N_pad + n] = static_cast<uint16_t>(bn);
-        atomicAdd(&hist[l16 * 256 + (bn >> 8)], 1u);
+    // ---- B. scores of this lane's tokens (head my_h), kept in registers
+    constexpr int NQ = NPL <= 2 ? NPL : 1;
+    SelQ<T> qop[NQ];
+#pragma unroll
+    for (int p = 0; p < NQ; ++p) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = 16 * p + 4 * lg + e;
+        v[e] = (my_on && col < r_lo) ? qs[my_h * r_pad + col] : 0.f;
       }
-    };
-    if constexpr (UB > 0) {
-      const QOp<T> q0 = low_qop<T>(qs, r_pad, nh, r_lo, 0, lane);
-      const QOp<T> q1 = low_qop<T>(qs, r_pad, nh, r_lo, NPL - 1, lane);
-      for (int base = wave; base < nblk; base += kSelWaves * UB) {
-        if (base != wave) {
+      qop[p].set(v, my_j);
+    }
+    float sc[KPL];
+    if constexpr (NPL <= 2) {
 #pragma unroll
-          for (int u = 0; u < UB; ++u) {
-            const int blk = min(base + u * kSelWaves, nblk - 1);
-            a[u][0].load(Uk + tile_base(b, 0, blk, NP, nblk), lane);
-            if (NPL > 1) a[u][NPL - 1].load(Uk + tile_base(b, NPL - 1, blk, NP, nblk), lane);
-          }
+      for (int a = 0; a < NACC; ++a) {
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NPL; ++p) {
+          const int s = a * NPL + p;
+          acc = qop[p].template step<NSL>(tb[s % PREF], my_slot, my_j, acc);
+          if (s + PREF < NSTEP) load_step(s + PREF);
         }
 #pragma unroll
-        for (int u = 0; u < UB; ++u) {
-          const int blk = base + u * kSelWaves;
-          if (blk < nblk) {
-            v4f s0 = v4f{0, 0, 0, 0}, s1 = v4f{0, 0, 0, 0};
-            s0 = score_mma(a[u][0], 0, q0, s0);
-            s1 = score_mma(a[u][0], 1, q0, s1);
-            if (NPL > 1 && nplo > 1) {
-              s0 = score_mma(a[u][NPL - 1], 0, q1, s0);
-              s1 = score_mma(a[u][NPL - 1], 1, q1, s1);
-            }
-            if (l16 < nh) {
-#pragma unroll
-              for (int t = 0; t < 8; ++t) put(blk, t, t < 4 ? s0[t & 3] : s1[t & 3]);
-            }
-          }
-        }
+        for (int t = 0; t < 4; ++t) sc[4 * a + t] = acc[t];
       }
     } else {
-      for (int blk = wave; blk < nblk; blk += kSelWaves) {
-        v4f s0, s1;
-        score_block(Uk, b, blk, NP, nblk, r_lo, qs, r_pad, nh, lane, s0, s1);
-        if (l16 < nh) {
+      // many low panels: one panel's tiles at a time, the latent-query operand rebuilt
+      // from LDS per panel
 #pragma unroll
-          for (int t = 0; t < 8; ++t) put(blk, t, t < 4 ? s0[t & 3] : s1[t & 3]);
+      for (int a = 0; a < NACC; ++a) {
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+        const int grp = wave + nwv * a;
+        for (int p = 0; p < nplo; ++p) {
+          LaneTile<T> t1[NSL];
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl)
+            t1[sl].load(Uk + tile_base(b, p, min(grp * NSL + sl, nblk - 1), NP, nblk), lane);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int col = 16 * p + 4 * lg + e;
+            v[e] = (my_on && col < r_lo) ? qs[my_h * r_pad + col] : 0.f;
+          }
+          SelQ<T> q1;
+          q1.set(v, my_j);
+          acc = q1.template step<NSL>(t1, my_slot, my_j, acc);
         }
-      }
-    }
-    __syncthreads();
-
-    // ---- C. coarse boundary digit, fine histogram inside it, fine boundary bin
-    if (wave < nh) {
-      int dg; uint32_t above, inb;
-      if (digit_search(hist + wave * 256, static_cast<uint32_t>(top_k), lane, &dg, &above, &inb)) {
-        st[wave].bstar = dg;
-        st[wave].need = top_k - static_cast<int>(above);
-      }
-    }
-    __syncthreads();
-    for (int i = tid; i < nh * 256; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    {
-      const int n8 = N_pad / 8;   // 8 bins per 16-byte read
-      for (int idx = tid; idx < nh * n8; idx += kSelThreads) {
-        const int hl = idx / n8, j = idx - hl * n8;
-        const uint32_t c = static_cast<uint32_t>(st[hl].bstar);
-        const uint4 x8 = *reinterpret_cast<const uint4*>(bins + (size_t)hl * N_pad + 8 * j);
-        const uint32_t w8[4] = {x8.x, x8.y, x8.z, x8.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int n = 8 * j + e;
-          const uint32_t bn = (e & 1) ? (w8[e >> 1] >> 16) : (w8[e >> 1] & 0xffffu);
-          if (n < N && (bn >> 8) == c) {
-            atomicAdd(&hist[hl * 256 + (bn & 255u)], 1u);
-            const int pos = atomicAdd(&st[hl].nlist, 1);
-            if (pos < kSelList) list[hl * kSelList + pos] = static_cast<uint16_t>(n);
+        for (int t = 0; t < 4; ++t) sc[4 * a + t] = acc[t];
+      }
+    }
+    // token of score 4a+t: 32 * (block of step a) + 16 * my_j + 4 * lg + t
+    auto tok = [&](int a) { return 32 * ((wave + nwv * a) * NSL + my_slot) + 16 * my_j + 4 * lg; };
+
+    // ---- C. per-head range, linear bins, histogram, boundary bin
+    {
+      uint32_t kmax = 0u, kmin = 0u;   // kmin holds ~key
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) {
+        const int n0 = tok(a);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (n0 + t < N) {
+            const uint32_t k = score_key(sc[4 * a + t]);
+            kmax = max(kmax, k);
+            kmin = max(kmin, ~k);
           }
         }
       }
+      kmax = head_max<HG>(kmax);
+      kmin = head_max<HG>(kmin);
+      if (lg == 0 && c16 < HG && my_on) {
+        atomicMax(&rng[2 * my_h], kmax);
+        atomicMax(&rng[2 * my_h + 1], kmin);
+      }
+    }
+    __syncthreads();
+    if (tid < nh) {
+      const float hi = key_score(rng[2 * tid]), lo = key_score(~rng[2 * tid + 1]);
+      const float range = hi - lo;
+      st[tid].lo = lo;
+      st[tid].mul = (range > 1e-30f && range < 3.0e38f) ? static_cast<float>(kSelBins - 1) / range : 0.f;
+    }
+    __syncthreads();
+    const float lo_h = my_on ? st[my_h].lo : 0.f, mul_h = my_on ? st[my_h].mul : 0.f;
+    // clamped in float first: any input (NaN included) gives a bin in [0, kSelBins)
+    auto bin_of = [&](float s) {
+      return static_cast<uint32_t>(fminf(fmaxf((s - lo_h) * mul_h, 0.f), static_cast<float>(kSelBins - 1)));
+    };
+    {
+      // branch-free: tokens past N (and absent heads) add 0, so the LDS atomics issue
+      // back to back; any float maps to a bin inside the head's range
+      uint32_t* hh = hist + my_h * HS;
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) {
+        const int n0 = tok(a);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          atomicAdd(&hh[bin_of(sc[4 * a + t])], (my_on && n0 + t < N) ? 1u : 0u);
+      }
     }
     __syncthreads();
     if (wave < nh) {
-      int dg; uint32_t above, inb;
-      if (digit_search(hist + wave * 256, static_cast<uint32_t>(st[wave].need), lane, &dg, &above, &inb)) {
-        const int need = st[wave].need - static_cast<int>(above);
-        st[wave].bstar = (st[wave].bstar << 8) | dg;
+      int bn; uint32_t above, inb;
+      bin_search(hist + wave * HS, static_cast<uint32_t>(top_k), lane, &bn, &above, &inb);
+      if (lane == 0) {
+        const int need = top_k - static_cast<int>(above);
+        st[wave].bstar = bn;
         st[wave].need = need;
         st[wave].cnt = static_cast<int>(inb);
         st[wave].mode = need == static_cast<int>(inb) ? kWholeBin
@@ -358,318 +473,271 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     }
     __syncthreads();
 
-    // ---- D. exact resolution inside a boundary bin that is only partly taken
+    // ---- D. tokens above the boundary bin (and all of it when it is taken whole);
+    // candidates of a partly taken bin
     bool any_rank = false, any_radix = false;
     for (int hl = 0; hl < nh; ++hl) {
       any_rank |= st[hl].mode == kRank;
       any_radix |= st[hl].mode == kRadix;
     }
-    if (any_rank || any_radix) {
-      for (int i = tid; i < nh * nblk; i += kSelThreads) selb[i] = 0;
-      for (int hl = 0; hl < nh; ++hl) {
-        if (st[hl].mode < kRank) continue;
-        const uint16_t bs = static_cast<uint16_t>(st[hl].bstar);
-        const uint16_t* bh = bins + (size_t)hl * N_pad;
-        if (st[hl].nlist <= kSelList) {
-          for (int i = tid; i < st[hl].nlist; i += kSelThreads) {
-            const int n = list[hl * kSelList + i];
-            if (bh[n] == bs) bflag[n / kBlockTok] = 1u;
-          }
-        } else {
-          for (int n = tid; n < N; n += kSelThreads)
-            if (bh[n] == bs) bflag[n / kBlockTok] = 1u;
-        }
-      }
-      __syncthreads();
-    }
-    if (any_rank) {
-      for (int blk = wave; blk < nblk; blk += kSelWaves) {
-        if (!bflag[blk]) continue;
-        v4f s0, s1;
-        score_block(Uk, b, blk, NP, nblk, r_lo, qs, r_pad, nh, lane, s0, s1);
-        if (l16 < nh && st[l16].mode == kRank) {
-          const uint16_t bs = static_cast<uint16_t>(st[l16].bstar);
+    const int bstar_h = my_on ? st[my_h].bstar : 0;
+    const int mode_h = my_on ? st[my_h].mode : kNone;
+    {
+      const int bwhole = mode_h == kWholeBin ? bstar_h : bstar_h + 1;   // lowest bin taken whole
+      uint32_t cbits = 0;   // scores in a partly taken boundary bin (bit 4a+t)
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int n = blk * kBlockTok + 16 * (t >> 2) + 4 * lg + (t & 3);
-            if (n < N && bins[(size_t)l16 * N_pad + n] == bs) {
+      for (int a = 0; a < NACC; ++a) {
+        const int n0 = tok(a);
+        uint32_t nib = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int bn = static_cast<int>(bin_of(sc[4 * a + t]));
+          const bool ok = my_on && n0 + t < N;
+          nib |= (ok && bn >= bwhole) ? (1u << t) : 0u;
+          cbits |= (ok && mode_h == kRank && bn == bstar_h) ? (1u << (4 * a + t)) : 0u;
+        }
+        // n0 < 32 * nblk always (blocks past the end hold no set bits but stay in range)
+        atomicOr(&selw[my_h * nblk + min(n0 >> 5, nblk - 1)], nib << (n0 & 31));
+      }
+      if (cbits) {
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if ((cbits >> (4 * a + t)) & 1u) {
+              const int n = tok(a) + t;
               const unsigned long long comp =
-                  (static_cast<unsigned long long>(score_key(t < 4 ? s0[t & 3] : s1[t & 3])) << 32) |
+                  (static_cast<unsigned long long>(score_key(sc[4 * a + t])) << 32) |
                   static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(n));
-              const int pos = atomicAdd(&st[l16].ncand, 1);
-              if (pos < kSelCap) cand[l16 * kSelCap + pos] = comp;
+              const int pos = atomicAdd(&st[my_h].ncand, 1);
+              if (pos < kSelCap) cand[my_h * kSelCap + pos] = comp;
             }
           }
         }
       }
+    }
+    if (any_rank) {
       __syncthreads();
-      for (int hl = 0; hl < nh; ++hl) {
-        if (st[hl].mode != kRank) continue;
-        const int C = min(st[hl].ncand, kSelCap);
-        const unsigned long long* ch = cand + hl * kSelCap;
-        for (int c = tid; c < C; c += kSelThreads) {
+      if (wave < nh && st[wave].mode == kRank) {
+        const int C = min(st[wave].ncand, kSelCap);
+        const unsigned long long* ch = cand + wave * kSelCap;
+        for (int c = lane; c < C; c += 64) {
           const unsigned long long me = ch[c];
           int rank = 0;
           for (int o = 0; o < C; ++o) rank += ch[o] > me ? 1 : 0;
-          if (rank < st[hl].need) {
+          if (rank < st[wave].need) {
             const uint32_t n = 0xFFFFFFFFu - static_cast<uint32_t>(me & 0xFFFFFFFFull);
-            atomicOr(&selb[hl * nblk + n / kBlockTok], 1u << (n % kBlockTok));
+            atomicOr(&selw[wave * nblk + (n >> 5)], 1u << (n & 31));
+          }
+        }
+      }
+    }
+    if (any_radix) {
+      // Exact MSB-first radix select over the 32-bit keys of the boundary-bin tokens of
+      // every head in this mode, then ties at the cutoff key taken in index order.
+      uint32_t* rh = hist + my_h * HS;                 // this lane's head: digit counts
+      const bool in_radix = mode_h == kRadix;
+      __syncthreads();
+      for (int i = tid; i < nh * HS; i += nthr) hist[i] = 0;
+      if (tid < nh) st[tid].tau = 0u;
+      for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        const uint32_t pmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+        __syncthreads();
+        if (pass > 0)
+          for (int i = tid; i < nh * 256; i += nthr) hist[(i >> 8) * HS + (i & 255)] = 0;
+        __syncthreads();
+        if (in_radix) {
+          const uint32_t prefix = st[my_h].tau;
+#pragma unroll
+          for (int a = 0; a < NACC; ++a) {
+            const int n0 = tok(a);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              if (n0 + t < N && static_cast<int>(bin_of(sc[4 * a + t])) == bstar_h) {
+                const uint32_t key = score_key(sc[4 * a + t]);
+                if ((key & pmask) == prefix) atomicAdd(&rh[(key >> shift) & 255u], 1u);
+              }
+            }
+          }
+        }
+        __syncthreads();
+        if (wave < nh && st[wave].mode == kRadix) {
+          int dg; uint32_t above, inb;
+          if (digit_search(hist + wave * HS, static_cast<uint32_t>(st[wave].need), lane, &dg, &above, &inb)) {
+            st[wave].tau |= static_cast<uint32_t>(dg) << shift;
+            st[wave].need -= static_cast<int>(above);
           }
         }
       }
       __syncthreads();
-    }
-    if (any_radix) {
-      // Exact radix select over the 32-bit keys of the boundary-bin tokens, keys recomputed
-      // per pass; then the boundary tokens are taken in index order (ties to lower index).
-      for (int hl = 0; hl < nh; ++hl) {
-        if (st[hl].mode != kRadix) continue;
-        const uint16_t bs = static_cast<uint16_t>(st[hl].bstar);
-        uint32_t prefix = 0;
-        uint32_t need = static_cast<uint32_t>(st[hl].need);
-        for (int pass = 0; pass < 4; ++pass) {
-          const int shift = 24 - 8 * pass;
-          const uint32_t pmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-          for (int i = tid; i < 256; i += kSelThreads) hist[hl * 256 + i] = 0;
-          __syncthreads();
-          for (int blk = wave; blk < nblk; blk += kSelWaves) {
-            if (!bflag[blk]) continue;
-            v4f s0, s1;
-            score_block(Uk, b, blk, NP, nblk, r_lo, qs, r_pad, nh, lane, s0, s1);
-            if (l16 == hl) {
+      // tie bits per block, then their exclusive prefix counts in index order
+      uint32_t* tie = hist + my_h * HS + 256;
+      const uint32_t tau_h = in_radix ? st[my_h].tau : 0u;
+      if (in_radix) {
 #pragma unroll
-              for (int t = 0; t < 8; ++t) {
-                const int n = blk * kBlockTok + 16 * (t >> 2) + 4 * lg + (t & 3);
-                if (n < N && bins[(size_t)hl * N_pad + n] == bs) {
-                  const uint32_t key = score_key(t < 4 ? s0[t & 3] : s1[t & 3]);
-                  if ((key & pmask) == prefix) atomicAdd(&hist[hl * 256 + ((key >> shift) & 255u)], 1u);
-                }
-              }
-            }
-          }
-          __syncthreads();
-          if (wave == 0) {
-            int dg; uint32_t above, inb;
-            if (digit_search(hist + hl * 256, need, lane, &dg, &above, &inb)) {
-              st[hl].tau = prefix | (static_cast<uint32_t>(dg) << shift);
-              st[hl].need = static_cast<int>(need - above);
-            }
-          }
-          __syncthreads();
-          prefix = st[hl].tau;
-          need = static_cast<uint32_t>(st[hl].need);
+        for (int a = 0; a < NACC; ++a) {
+          const int n0 = tok(a);
+          uint32_t nib = 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (n0 + t < N && static_cast<int>(bin_of(sc[4 * a + t])) == bstar_h &&
+                score_key(sc[4 * a + t]) == tau_h)
+              nib |= 1u << t;
+          if (nib) atomicOr(&tie[n0 >> 5], nib << (n0 & 31));
         }
-        if (wave == 0) {
-          const uint32_t tau = prefix;
-          uint32_t left = need;
-          for (int blk = 0; blk < nblk; ++blk) {
-            if (!bflag[blk]) continue;
-            v4f s0, s1;
-            score_block(Uk, b, blk, NP, nblk, r_lo, qs, r_pad, nh, lane, s0, s1);
-            uint32_t gtm = 0, eqm = 0;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              const int hf = t >> 2, tt = t & 3;
-              const int n = blk * kBlockTok + 16 * hf + 4 * lg + tt;
-              bool gt = false, eq = false;
-              if (l16 == hl && n < N && bins[(size_t)hl * N_pad + n] == bs) {
-                const uint32_t key = score_key(t < 4 ? s0[tt] : s1[tt]);
-                gt = key > tau;
-                eq = key == tau;
-              }
-              const uint64_t bg = __ballot(gt), be = __ballot(eq);
-#pragma unroll
-              for (int g4 = 0; g4 < 4; ++g4) {
-                const int bit = 16 * hf + 4 * g4 + tt;
-                if ((bg >> (g4 * 16 + hl)) & 1ull) gtm |= 1u << bit;
-                if ((be >> (g4 * 16 + hl)) & 1ull) eqm |= 1u << bit;
-              }
-            }
-            uint32_t take = gtm;
-            while (eqm && left) {
-              const uint32_t low = eqm & (~eqm + 1u);
-              take |= low;
-              eqm ^= low;
-              --left;
-            }
-            if (lane == 0) selb[hl * nblk + blk] |= take;
-          }
+      }
+      __syncthreads();
+      if (wave < nh && st[wave].mode == kRadix) {
+        const uint32_t* tw = hist + wave * HS + 256;
+        uint32_t* tp = hist + wave * HS + 256 + nblk;
+        uint32_t carry = 0;
+        for (int c0 = 0; c0 < nblk; c0 += 64) {
+          const int blk = c0 + lane;
+          const uint32_t cnt = blk < nblk ? static_cast<uint32_t>(__popc(tw[blk])) : 0u;
+          const uint32_t incl = wave_incl_scan(cnt, lane);
+          if (blk < nblk) tp[blk] = carry + incl - cnt;
+          carry += __shfl(incl, 63, 64);
         }
-        __syncthreads();
+      }
+      __syncthreads();
+      if (in_radix) {
+        const uint32_t* tp = hist + my_h * HS + 256 + nblk;
+        const uint32_t need_t = static_cast<uint32_t>(st[my_h].need);
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) {
+          const int n0 = tok(a);
+          uint32_t nib = 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int n = n0 + t;
+            if (n < N && static_cast<int>(bin_of(sc[4 * a + t])) == bstar_h) {
+              const uint32_t key = score_key(sc[4 * a + t]);
+              bool take = key > tau_h;
+              if (key == tau_h) {
+                const uint32_t w = tie[n >> 5];
+                const uint32_t pos = tp[n >> 5] + static_cast<uint32_t>(__popc(w & ((1u << (n & 31)) - 1u)));
+                take = pos < need_t;
+              }
+              if (take) nib |= 1u << t;
+            }
+          }
+          if (nib) atomicOr(&selw[my_h * nblk + (n0 >> 5)], nib << (n0 & 31));
+        }
       }
     }
   }
+  __syncthreads();
 
   // ---- E. selection bits per (head, 32-token block)
-  if (sel_out == nullptr) {
-    for (int idx = tid; idx < nh * nblk; idx += kSelThreads) {
-      const int hl = idx / nblk, blk = idx - hl * nblk;
-      const int mode = st[hl].mode;
-      uint32_t word = 0;
+  auto word_of = [&](int hl, int blk) -> uint32_t {
+    const int mode = st[hl].mode;
+    if (mode == kNone) return 0u;
+    if (mode == kAll) {
       const int nvalid = min(kBlockTok, N - blk * kBlockTok);
-      const uint32_t valid = nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
-      if (mode == kAll) {
-        word = valid;
-      } else if (mode != kNone) {
-        const uint32_t bs = static_cast<uint32_t>(st[hl].bstar);
-        const uint4* bp = reinterpret_cast<const uint4*>(bins + (size_t)hl * N_pad + blk * kBlockTok);
-        uint32_t gt = 0, eq = 0;
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const uint4 x = bp[v4];
-          const uint32_t w8[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = w8[e] & 0xffffu, hi = w8[e] >> 16;
-            const int bit = 8 * v4 + 2 * e;
-            gt |= (lo > bs ? 1u : 0u) << bit;
-            gt |= (hi > bs ? 1u : 0u) << (bit + 1);
-            eq |= (lo == bs ? 1u : 0u) << bit;
-            eq |= (hi == bs ? 1u : 0u) << (bit + 1);
-          }
-        }
-        word = (mode == kWholeBin) ? (gt | eq) : (gt | (eq & selb[hl * nblk + blk]));
-        word &= valid;
-      }
-      mask[((size_t)b * nblk + blk) * Hq_pad + h0 + hl] = word;
+      return nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
     }
-  } else {
-    // ascending ids as well: one wavefront per head walks its tokens in order
-    for (int hl = wave; hl < nh; hl += kSelWaves) {
-      const int h = h0 + hl;
-      const int mode = st[hl].mode;
-      const uint32_t bs = mode >= kWholeBin ? static_cast<uint32_t>(st[hl].bstar) : 0u;
-      uint32_t run_sel = 0;
-      const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      for (int c0 = 0; c0 < N_pad; c0 += 64) {
-        const int n = c0 + lane;
-        const bool valid = n < N;
-        bool sel;
-        if (mode == kNone) {
-          sel = false;
-        } else if (mode == kAll) {
-          sel = valid;
-        } else {
-          const uint32_t bn = valid ? bins[(size_t)hl * N_pad + n] : 0u;
-          if (mode == kWholeBin)
-            sel = valid && bn >= bs;
-          else
-            sel = valid && (bn > bs || (bn == bs && ((selb[hl * nblk + n / kBlockTok] >> (n % kBlockTok)) & 1u)));
+    return selw[hl * nblk + blk];
+  };
+  for (int idx = tid; idx < nh * nblk; idx += nthr) {
+    const int blk = idx / nh, hl = idx - blk * nh;
+    mask[((size_t)b * nblk + blk) * Hq_pad + h0 + hl] = word_of(hl, blk);
+  }
+  if (sel_out != nullptr) {
+    // ascending ids: one wavefront per head, block counts prefix-summed in order
+    for (int hl = wave; hl < nh; hl += nwv) {
+      int32_t* out = sel_out + ((size_t)b * Hq + h0 + hl) * top_k;
+      uint32_t carry = 0;
+      for (int c0 = 0; c0 < nblk; c0 += 64) {
+        const int blk = c0 + lane;
+        uint32_t w = blk < nblk ? word_of(hl, blk) : 0u;
+        const uint32_t cnt = static_cast<uint32_t>(__popc(w));
+        const uint32_t incl = wave_incl_scan(cnt, lane);
+        uint32_t pos = carry + incl - cnt;
+        while (w) {
+          const int bit = __ffs(w) - 1;
+          w &= w - 1u;
+          if (pos < static_cast<uint32_t>(top_k)) out[pos] = blk * kBlockTok + bit;
+          ++pos;
         }
-        const uint64_t sb = __ballot(sel);
-        const int t0 = c0 / kBlockTok;
-        if (lane == 0) {
-          mask[((size_t)b * nblk + t0) * Hq_pad + h] = static_cast<uint32_t>(sb);
-          if (t0 + 1 < nblk) mask[((size_t)b * nblk + t0 + 1) * Hq_pad + h] = static_cast<uint32_t>(sb >> 32);
-        }
-        const uint32_t pos = run_sel + static_cast<uint32_t>(__popcll(sb & lt_mask));
-        if (sel) sel_out[((size_t)b * Hq + h) * top_k + pos] = n;
-        run_sel += static_cast<uint32_t>(__popcll(sb));
+        carry += __shfl(incl, 63, 64);
       }
     }
   }
   // latent queries for the flash-decode kernel (stored last: stores share the load counter)
-  for (int i = tid; i < nh * r_pad; i += kSelThreads)
+  for (int i = tid; i < nh * r_pad; i += nthr)
     qt[((size_t)b * Hq_pad + h0) * r_pad + i] = qs[i];
 }
 
-// ---------------------------------------------------------------- row-norm bound
-// rn[b][p] = max_n |U_k[n, :16(p+1)]|_2 (slightly rounded up): bounds the low-rank score.
-template <class T>
-__global__ __launch_bounds__(256) void k_rownorm(const T* __restrict__ Uk, float* __restrict__ rn,
-                                                 int N, int NP, int nblk) {
-  __shared__ uint32_t mx[16];
-  const int b = blockIdx.x;
-  if (threadIdx.x < 16) mx[threadIdx.x] = 0u;
-  __syncthreads();
-  float best[16];
-  for (int p = 0; p < NP; ++p) best[p] = 0.f;
-  for (int n = threadIdx.x; n < N; n += blockDim.x) {
-    const int t = n / kBlockTok, nn = n % kBlockTok, half = nn >> 4;
-    float cum = 0.f;
-    for (int p = 0; p < NP; ++p) {
-      const T* base = Uk + tile_base(b, p, t, NP, nblk);
-      for (int cc = 0; cc < 16; ++cc) {
-        const int lane = (cc >> 2) * 16 + (nn & 15);
-        const float v = to_f32(base[tile_elem(lane, half, cc & 3)]);
-        cum = fmaf(v, v, cum);
-      }
-      best[p] = fmaxf(best[p], cum);
-    }
-  }
-  for (int p = 0; p < NP; ++p) atomicMax(&mx[p], __float_as_uint(best[p]));
-  __syncthreads();
-  if (threadIdx.x < NP) rn[(size_t)b * NP + threadIdx.x] = sqrtf(__uint_as_float(mx[threadIdx.x])) * 1.0001f;
-}
-
 // ---------------------------------------------------------------- launchers
-int select_heads_per_group(const Dims& dm) {
-  // LDS budget ~150 KB, and enough workgroups to cover the GPU's 256 CUs
-  int hg_lds = kMaxHg;
-  while (hg_lds > 1 && sel_layout(hg_lds, dm.N_pad, dm.nblk, dm.r_pad, dm.d).total > 150 * 1024) --hg_lds;
-  int groups = (dm.Hq + hg_lds - 1) / hg_lds;
-  const int want = dm.B > 0 ? (256 + dm.B - 1) / dm.B : 1;
-  groups = std::max(groups, std::min(dm.Hq, want));
-  return (dm.Hq + groups - 1) / groups;
+struct SelPlan {
+  int HG, NPL, NACC, waves;
+};
+
+static SelPlan select_plan(const Dims& dm, int r_lo) {
+  const int nplo = (r_lo + 15) / 16;
+  SelPlan pl;
+  // 16 wavefronts; four heads per workgroup while 8 steps per wavefront cover the
+  // tokens and the low rank fits two panels, else one head with the panels streamed one
+  // at a time.  Steps per wavefront: the fewest of 2, 3, 4, 8 that cover the tokens.
+  const int g4 = (dm.nblk + 1) / 2;
+  pl.HG = (nplo <= 2 && g4 <= kSelMaxWaves * 8) ? 4 : 1;
+  pl.NPL = pl.HG == 1 ? 8 : (nplo <= 1 ? 1 : 2);
+  const int ngrp = (dm.nblk + 8 / pl.HG - 1) / (8 / pl.HG);
+  const int per = (ngrp + kSelMaxWaves - 1) / kSelMaxWaves;
+  pl.NACC = pl.HG == 1 ? 8 : (per <= 2 ? 2 : (per <= 3 ? 3 : (per <= 4 ? 4 : 8)));
+  pl.waves = kSelMaxWaves;
+  return pl;
 }
 
-size_t select_lds_bytes(const Dims& dm, int Hg) {
-  return sel_layout(Hg, dm.N_pad, dm.nblk, dm.r_pad, dm.d).total;
+template <class T, int HG, int NPL, int NACC>
+static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, int top_k,
+                                  int32_t* sel_out, int waves, hipStream_t st, const KernelEvents& ev) {
+  const Dims& dm = c->dm;
+  const int HGN = (dm.Hq + HG - 1) / HG;
+  const size_t lds = sel_layout(HG, dm.nblk, dm.r_pad, dm.d).total;
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  if ((dm.nblk + 8 / HG - 1) / (8 / HG) > waves * NACC) return hipErrorInvalidValue;
+  const void* fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC>);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int grid = ((dm.B + 7) / 8) * 8 * HGN;
+  hipExtLaunchKernelGGL((k_select<T, HG, NPL, NACC>), dim3(grid), dim3(64 * waves), lds, st,
+                        ev.start, ev.stop, 0, static_cast<const T*>(c->Uk),
+                        static_cast<const T*>(c->Bk), q, c->qt, c->mask, sel_out, dm.B, dm.N,
+                        dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d, dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo,
+                        top_k);
+  return hipGetLastError();
 }
 
 template <class T>
 static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, int top_k,
                                   int32_t* sel_out, hipStream_t st, const KernelEvents& ev) {
-  const Dims& dm = c->dm;
-  const int Hg = select_heads_per_group(dm);
-  const int HG = (dm.Hq + Hg - 1) / Hg;
-  const size_t lds = select_lds_bytes(dm, Hg);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  const int nplo = (r_lo + 15) / 16;
-  // one low panel: 12 blocks per wavefront in flight when that covers the sequence
-  const int which = nplo == 1 ? (dm.nblk <= 12 * kSelWaves ? 0 : 1) : (nplo == 2 ? 2 : 3);
-  const void* fns[4] = {reinterpret_cast<const void*>(&k_select<T, 12>),
-                        reinterpret_cast<const void*>(&k_select<T, 16>),
-                        reinterpret_cast<const void*>(&k_select<T, 8>),
-                        reinterpret_cast<const void*>(&k_select<T, 0>)};
-  static bool attr_set[4] = {false, false, false, false};
-  if (!attr_set[which]) {
-    hipError_t e = hipFuncSetAttribute(fns[which], hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set[which] = true;
-  }
-  const int grid = ((dm.B + 7) / 8) * 8 * HG;
-#define AP_SELECT_ARGS static_cast<const T*>(c->Uk), static_cast<const T*>(c->Bk), c->rn, q, c->qt, \
-      c->mask, sel_out, dm.B, dm.N, dm.N_pad, dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d, dm.G, dm.Hq,  \
-      dm.Hq_pad, Hg, HG, r_lo, top_k
-#define AP_SELECT_LAUNCH(UBV) \
-  hipExtLaunchKernelGGL((k_select<T, UBV>), dim3(grid), dim3(kSelThreads), lds, st, ev.start, ev.stop, 0, AP_SELECT_ARGS)
-  switch (which) {
-    case 0: AP_SELECT_LAUNCH(12); break;
-    case 1: AP_SELECT_LAUNCH(16); break;
-    case 2: AP_SELECT_LAUNCH(8); break;
-    default: AP_SELECT_LAUNCH(0); break;
-  }
-#undef AP_SELECT_LAUNCH
-#undef AP_SELECT_ARGS
-  return hipGetLastError();
+  const SelPlan pl = select_plan(c->dm, r_lo);
+#define AP_SEL(HGV, NPLV, NACCV)                                                        \
+  if (pl.HG == HGV && pl.NPL == NPLV && pl.NACC == NACCV)                               \
+    return launch_select_v<T, HGV, NPLV, NACCV>(c, q, r_lo, top_k, sel_out, pl.waves, st, ev);
+  AP_SEL(4, 1, 2)
+  AP_SEL(4, 1, 3)
+  AP_SEL(4, 1, 4)
+  AP_SEL(4, 1, 8)
+  AP_SEL(4, 2, 2)
+  AP_SEL(4, 2, 3)
+  AP_SEL(4, 2, 4)
+  AP_SEL(4, 2, 8)
+  AP_SEL(1, 8, 8)
+#undef AP_SEL
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k, int32_t* sel_out,
                          hipStream_t st, const KernelEvents& ev) {
   if (c->dm.storage == AP_BF16) return launch_select_t<bf16_t>(c, q, r_lo, top_k, sel_out, st, ev);
   return launch_select_t<float>(c, q, r_lo, top_k, sel_out, st, ev);
-}
-
-hipError_t launch_rownorm(const ap_cache* c, hipStream_t st) {
-  const Dims& dm = c->dm;
-  if (dm.storage == AP_BF16)
-    hipLaunchKernelGGL(k_rownorm<bf16_t>, dim3(dm.B), dim3(256), 0, st,
-                       static_cast<const bf16_t*>(c->Uk), c->rn, dm.N, dm.NP, dm.nblk);
-  else
-    hipLaunchKernelGGL(k_rownorm<float>, dim3(dm.B), dim3(256), 0, st,
-                       static_cast<const float*>(c->Uk), c->rn, dm.N, dm.NP, dm.nblk);
-  return hipGetLastError();
 }
 
 }  // namespace ap

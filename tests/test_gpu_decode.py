@@ -72,8 +72,8 @@ def test_decode_single_token(gpu_lib):
 
 @pytest.mark.parametrize("name", ["bf16_ragged", "bf16_rank128", "f32_text_long"])
 def test_decode_zero_query_ties_take_lowest_ids(gpu_lib, name):
-    # every score ties: N <= 256 exercises exact ranking inside the boundary bin,
-    # N = 300 the radix fallback
+    # every score ties: N <= 128 exercises exact ranking inside the boundary bin,
+    # N = 300 the radix fallback over exact keys
     w = SMALL[name]
     seqs = make_inputs(w)
     for s in seqs:
