@@ -147,8 +147,10 @@ typedef struct {
   const void* text_v;    /* device [B][T][W] storage dtype, NULL iff T == 0               */
   int32_t* sel_out;      /* optional device [B][Hq][top_k] int32: the selected token ids,
                             ascending per (sequence, head); NULL to skip                  */
-  int32_t splits;        /* 0: library's choice; else the number of N-splits per sequence
-                            (clamped to the workspace sized at ap_compress)                */
+  int32_t splits;        /* 0: library's choice (one kernel per step for the shapes it
+                            covers, else split-N); >= 1: the split-N path with that many
+                            N-splits per sequence (clamped to the workspace sized at
+                            ap_compress)                                                 */
 } ap_decode_params;
 
 /* One decode step of attention over the compressed cache, for every sequence.
@@ -169,7 +171,11 @@ typedef struct {
  *
  * q:    device [B][Hq*d] float32, caller-owned.
  * out:  device [B][Hq*d] float32, caller-owned, fully overwritten.
- * The call allocates nothing; it enqueues three kernels on `stream`.
+ * The call allocates nothing.  It enqueues one kernel on `stream` when splits == 0 and
+ * the shape allows (bf16 factors, r <= 64, r_lo <= 32, N <= 8192, head_dim a power of
+ * two multiple of 8, T <= 1024, B * ceil(Hq/4) <= 256): one workgroup per (sequence,
+ * 4 query heads) then selects, attends over all tokens and projects.  Otherwise three
+ * kernels: selection, split-N flash-decode, combine.
  * Errors: AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_UNSUPPORTED (r_lo or r not
  * supported by the tiling), AP_ERR_HIP.
  */
@@ -183,9 +189,11 @@ void ap_free(ap_cache* c);
 /* Kernel timing for measurement.  While enabled, ap_decode_attn records HIP events
  * around each of its kernels on the caller's stream (at most max_calls calls are
  * recorded; later calls are not timed).  ap_timing_read waits for the recorded events,
- * writes the summed milliseconds per kernel (index: 0 select, 1 attention, 2 combine)
- * and the number of timed calls, and starts a new recording.  max_calls == 0 disables. */
-enum { AP_KERNEL_SELECT = 0, AP_KERNEL_ATTN = 1, AP_KERNEL_COMBINE = 2, AP_N_KERNELS = 3 };
+ * writes the summed milliseconds per kernel (index: 0 select, 1 attention, 2 combine,
+ * 3 the single-kernel decode) and the number of timed calls, and starts a new recording.
+ * max_calls == 0 disables. */
+enum { AP_KERNEL_SELECT = 0, AP_KERNEL_ATTN = 1, AP_KERNEL_COMBINE = 2, AP_KERNEL_DECODE = 3,
+       AP_N_KERNELS = 4 };
 ap_status ap_timing_enable(ap_cache* c, int32_t max_calls);
 ap_status ap_timing_read(ap_cache* c, float* ms_per_kernel /* [AP_N_KERNELS] */, int32_t* calls);
 

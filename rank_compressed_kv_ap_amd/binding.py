@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libap.so")
 AP_OK, AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_BAD_DTYPE, AP_ERR_UNSUPPORTED, \
     AP_ERR_OUT_OF_MEMORY, AP_ERR_HIP = range(7)
 AP_F32, AP_BF16 = 0, 1
-KERNEL_NAMES = ("select", "attn", "combine")
+KERNEL_NAMES = ("select", "attn", "combine", "decode")
 
 EXPORTED = (
     "ap_compress", "ap_recompress", "ap_cache_set_factors", "ap_cache_get_factors",
@@ -177,7 +177,7 @@ class Cache:
         _check(lib.ap_timing_enable(self.handle, max_calls), "ap_timing_enable")
 
     def timing_read(self):
-        ms = (ctypes.c_float * 3)()
+        ms = (ctypes.c_float * len(KERNEL_NAMES))()
         calls = ctypes.c_int32()
         _check(lib.ap_timing_read(self.handle, ms, ctypes.byref(calls)), "ap_timing_read")
         return dict(zip(KERNEL_NAMES, list(ms))), calls.value

@@ -34,6 +34,7 @@ struct TimingState {
   int max_calls = 0;
   int calls = 0;
   std::vector<hipEvent_t> ev;  // [max_calls][AP_N_KERNELS][2]
+  std::vector<uint8_t> used;   // [max_calls][AP_N_KERNELS]: the kernel ran in that call
 };
 
 }  // namespace ap
@@ -74,6 +75,11 @@ hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
                          int32_t* sel_out, hipStream_t st, const KernelEvents& ev);
 hipError_t launch_attn(const ap_cache* c, int r_lo, float scale_log2e, int S, int CB,
                        hipStream_t st, const KernelEvents& ev);
+// Single-kernel decode (select_kernel.hip): shapes it takes, and its launch.
+bool decode_fused_supported(const Dims& dm, int r_lo, int n_text);
+hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, int r_lo, int top_k,
+                               int32_t* sel_out, int n_text, const void* text_k, const void* text_v,
+                               float sl2, hipStream_t st, const KernelEvents& ev);
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float scale_log2e,
                           int S, int T, const void* text_k, const void* text_v, hipStream_t st,
                           const KernelEvents& ev);

@@ -309,13 +309,23 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
     if (timed) {
       ev.start = tm.ev[((size_t)tm.calls * AP_N_KERNELS + kernel) * 2];
       ev.stop = tm.ev[((size_t)tm.calls * AP_N_KERNELS + kernel) * 2 + 1];
+      tm.used[(size_t)tm.calls * AP_N_KERNELS + kernel] = 1;
     }
     return ev;
   };
-  hipError_t e = launch_select(c, q, p->r_lo, p->top_k, p->sel_out, st, events(AP_KERNEL_SELECT));
-  if (e == hipSuccess) e = launch_attn(c, p->r_lo, sl2, S, CB, st, events(AP_KERNEL_ATTN));
-  if (e == hipSuccess)
-    e = launch_combine(c, q, out, sl2, S, p->n_text, p->text_k, p->text_v, st, events(AP_KERNEL_COMBINE));
+  if (timed)
+    for (int k = 0; k < AP_N_KERNELS; ++k) tm.used[(size_t)tm.calls * AP_N_KERNELS + k] = 0;
+  hipError_t e = hipSuccess;
+  if (p->splits == 0 && decode_fused_supported(dm, p->r_lo, p->n_text)) {
+    // one kernel per step: each (sequence, 4 heads) workgroup selects, attends and projects
+    e = launch_decode_fused(c, q, out, p->r_lo, p->top_k, p->sel_out, p->n_text, p->text_k,
+                            p->text_v, sl2, st, events(AP_KERNEL_DECODE));
+  } else {
+    e = launch_select(c, q, p->r_lo, p->top_k, p->sel_out, st, events(AP_KERNEL_SELECT));
+    if (e == hipSuccess) e = launch_attn(c, p->r_lo, sl2, S, CB, st, events(AP_KERNEL_ATTN));
+    if (e == hipSuccess)
+      e = launch_combine(c, q, out, sl2, S, p->n_text, p->text_k, p->text_v, st, events(AP_KERNEL_COMBINE));
+  }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (timed) tm.calls++;
   return AP_OK;
@@ -338,6 +348,7 @@ ap_status ap_timing_enable(ap_cache* c, int32_t max_calls) {
   tm.max_calls = 0;
   const size_t n = (size_t)max_calls * AP_N_KERNELS * 2;
   tm.ev.resize(n, nullptr);
+  tm.used.assign((size_t)max_calls * AP_N_KERNELS, 0);
   for (size_t i = 0; i < n; ++i) {
     hipError_t e = hipEventCreate(&tm.ev[i]);
     if (e != hipSuccess) {
@@ -356,6 +367,7 @@ ap_status ap_timing_read(ap_cache* c, float* ms_per_kernel, int32_t* calls) {
   for (int k = 0; k < AP_N_KERNELS; ++k) ms_per_kernel[k] = 0.f;
   for (int i = 0; i < tm.calls; ++i)
     for (int k = 0; k < AP_N_KERNELS; ++k) {
+      if (!tm.used[(size_t)i * AP_N_KERNELS + k]) continue;   // not launched in that call
       hipEvent_t a = tm.ev[((size_t)i * AP_N_KERNELS + k) * 2];
       hipEvent_t b = tm.ev[((size_t)i * AP_N_KERNELS + k) * 2 + 1];
       hipError_t e = hipEventSynchronize(b);

@@ -22,6 +22,8 @@
 //     taken in index order;
 //  E. the selection bits per (head, 32-token block) are written (and, on request, the
 //     ascending selected ids).
+#include <type_traits>
+
 #include <hip/hip_ext.h>
 
 #include "ap_internal.h"
@@ -47,13 +49,18 @@ struct SelState {
 };
 
 struct SelLayout {
-  size_t qh, qs, st, rng, hist, selw, cand, total;
+  size_t qh, qs, st, rng, hist, selw, cand;
+  size_t sts, zs, hmx, lpart, ltx, lfin;   // single-kernel decode only
+  size_t total;
   int hs;          // words per head in hist
 };
 
 // hist holds each head's bin counts; in the radix fallback it is reused as
-// [256 digit counts][nblk tie bits][nblk tie prefix] per head.
-__host__ __device__ inline SelLayout sel_layout(int HG, int nblk, int r_pad, int d) {
+// [256 digit counts][nblk tie bits][nblk tie prefix] per head, and in the single-kernel
+// decode as the per-wavefront latent sums and then the output partial sums.
+// Tn > 0 (text tokens) or fused adds the single-kernel decode regions.
+__host__ __device__ inline SelLayout sel_layout(int HG, int nblk, int r_pad, int d, bool fused = false,
+                                                int Tn = 0) {
   auto up = [](size_t x) { return (x + 15) & ~(size_t)15; };
   SelLayout L;
   L.hs = kSelBins > 256 + 2 * nblk ? kSelBins : 256 + 2 * nblk;
@@ -65,6 +72,15 @@ __host__ __device__ inline SelLayout sel_layout(int HG, int nblk, int r_pad, int
   L.hist = o; o = up(o + (size_t)HG * L.hs * 4);
   L.selw = o; o = up(o + (size_t)HG * nblk * 4);
   L.cand = o; o = up(o + (size_t)HG * kSelCap * 8);
+  L.sts = L.zs = L.hmx = L.lpart = L.ltx = L.lfin = o;
+  if (fused) {
+    L.sts = o;   o = up(o + (size_t)HG * Tn * 4);
+    L.zs = o;    o = up(o + (size_t)HG * r_pad * 4);
+    L.hmx = o;   o = up(o + (size_t)HG * 4);
+    L.lpart = o; o = up(o + (size_t)kSelMaxWaves * HG * 4);
+    L.ltx = o;   o = up(o + (size_t)HG * 4);
+    L.lfin = o;  o = up(o + (size_t)HG * 4);
+  }
   L.total = o;
   return L;
 }
@@ -100,6 +116,30 @@ template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, true));
 }
+// Sum over the lanes of one 16-lane row that hold the same head (lane%16 congruent mod
+// HG), by rotations; every such lane gets the sum.
+template <int N>
+__device__ __forceinline__ float dpp_ror_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, true));
+}
+template <int HG>
+__device__ __forceinline__ float head_sum_row(float v) {
+  if constexpr (HG <= 1) v += dpp_ror_f<1>(v);
+  if constexpr (HG <= 2) v += dpp_ror_f<2>(v);
+  if constexpr (HG <= 4) v += dpp_ror_f<4>(v);
+  if constexpr (HG <= 8) v += dpp_ror_f<8>(v);
+  return v;
+}
+// The same over the whole wavefront (then across the 4 rows).
+template <int HG>
+__device__ __forceinline__ float head_sum(float v) {
+  v = head_sum_row<HG>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int) {
   v += dpp_u32<0x111, 0xF>(v);   // row_shr:1
   v += dpp_u32<0x112, 0xF>(v);   // row_shr:2
@@ -225,15 +265,30 @@ template <> struct SelQ<float> {
   }
 };
 
+// Operands of the single-kernel decode (unused by the selection-only kernel).
+struct FusedArgs {
+  const void* Uv;       // V-layout panels
+  const void* Bv;       // [B][r_pad][W]
+  const void* text_k;   // [B][Tn][W] or null
+  const void* text_v;
+  float* out;           // [B][Hq][d]
+  int Tn;
+  float sl2;            // softmax scale in log2 units
+};
+
 // HG: query heads per workgroup (4 or 1); NPL: low panels (1 or 2 with the tiles of
 // several steps in flight; 8 = any count up to 8, one panel's tiles at a time); NACC:
-// accumulation steps per wavefront (2, 3, 4 or 8).
-template <class T, int HG, int NPL, int NACC>
-__global__ __launch_bounds__(1024) void k_select(
+// accumulation steps per wavefront (2, 3, 4 or 8).  FUSED: the same workgroup goes on
+// to the attention of its heads over all tokens, the text tokens and the output
+// projection (bf16 factors, HG = 4, r <= 64), so one kernel makes the whole step.
+template <class T, int HG, int NPL, int NACC, bool FUSED>
+__device__ __forceinline__ void select_body(
     const T* __restrict__ Uk, const T* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
     int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
-    int r_lo, int top_k) {
+    int r_lo, int top_k, const FusedArgs& fa) {
+  static_assert(!FUSED || (HG == 4 && NPL <= 2 && std::is_same<T, bf16_t>::value),
+                "single-kernel decode: bf16, four heads per workgroup");
   constexpr int NSL = 8 / HG;                                   // token blocks per step
   constexpr int KPL = 4 * NACC;                                 // scores per lane
   constexpr int NSTEP = NACC * NPL;
@@ -252,12 +307,13 @@ __global__ __launch_bounds__(1024) void k_select(
   const int nh = min(HG, Hq - h0);
   if (nh <= 0) return;
   const int nthr = blockDim.x, nwv = nthr >> 6;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile offsets in SGPRs
   const int c16 = lane & 15, lg = lane >> 4;
   const int my_slot = c16 / (2 * HG), my_j = (c16 / HG) & 1, my_h = c16 % HG;
   const bool my_on = my_h < nh;
 
-  const SelLayout Ly = sel_layout(HG, nblk, r_pad, d);
+  const SelLayout Ly = sel_layout(HG, nblk, r_pad, d, FUSED, FUSED ? fa.Tn : 0);
   float* qh = reinterpret_cast<float*>(smem_raw + Ly.qh);
   float* qs = reinterpret_cast<float*>(smem_raw + Ly.qs);
   SelState* st = reinterpret_cast<SelState*>(smem_raw + Ly.st);
@@ -323,6 +379,10 @@ __global__ __launch_bounds__(1024) void k_select(
     st[tid].ncand = 0;
     rng[2 * tid] = 0u;
     rng[2 * tid + 1] = 0u;
+    if constexpr (FUSED) {
+      reinterpret_cast<uint32_t*>(smem_raw + Ly.hmx)[tid] = 0u;
+      reinterpret_cast<float*>(smem_raw + Ly.ltx)[tid] = 0.f;
+    }
   }
   __syncthreads();
   // latent queries q~[h][i] = B_k[i, g*d : g*d+d] . q_h
@@ -354,8 +414,33 @@ __global__ __launch_bounds__(1024) void k_select(
   }
   __syncthreads();
 
-  if (select) {
-    // ---- B. scores of this lane's tokens (head my_h), kept in registers
+  // single-kernel decode: tiles of the full-rank score pass (U_k panels holding columns
+  // >= r_lo) and then of the value pass (all U_v panels), 2 tiles per step, PD steps in
+  // flight; the first ones are issued right after the low-rank scores
+  constexpr int NPM = 4;                        // panels (r <= 64)
+  constexpr int NSK = NACC * NPM;               // steps of each pass
+  constexpr int PD = NACC <= 3 ? 6 : (NACC <= 4 ? 4 : 2);
+  const int p0 = r_lo >> 4;                     // first panel with a column >= r_lo
+  LaneTile<T> rb[FUSED ? PD : 1][NSL];
+  auto ld = [&](int s) {   // s is a compile-time constant after unrolling
+    const bool isv = s >= NSK;
+    const int ss = isv ? s - NSK : s;
+    const int a = ss / NPM, j = ss % NPM;
+    const int grp = wave + nwv * a;
+    const int pan = isv ? min(j, NP - 1) : min(p0 + j, NP - 1);
+    const T* base = isv ? static_cast<const T*>(fa.Uv) : Uk;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int blk = min(grp * NSL + sl, nblk - 1);   // clamped: loads stay unconditional
+      rb[s % PD][sl].load(base + tile_base(b, pan, blk, NP, nblk), lane);
+    }
+  };
+
+  // ---- B. scores of this lane's tokens (head my_h), kept in registers
+  float sc[KPL];
+  // token of score 4a+t: 32 * (block of step a) + 16 * my_j + 4 * lg + t
+  auto tok = [&](int a) { return 32 * ((wave + nwv * a) * NSL + my_slot) + 16 * my_j + 4 * lg; };
+  if (select || FUSED) {
     constexpr int NQ = NPL <= 2 ? NPL : 1;
     SelQ<T> qop[NQ];
 #pragma unroll
@@ -368,7 +453,6 @@ __global__ __launch_bounds__(1024) void k_select(
       }
       qop[p].set(v, my_j);
     }
-    float sc[KPL];
     if constexpr (NPL <= 2) {
 #pragma unroll
       for (int a = 0; a < NACC; ++a) {
@@ -408,9 +492,12 @@ __global__ __launch_bounds__(1024) void k_select(
         for (int t = 0; t < 4; ++t) sc[4 * a + t] = acc[t];
       }
     }
-    // token of score 4a+t: 32 * (block of step a) + 16 * my_j + 4 * lg + t
-    auto tok = [&](int a) { return 32 * ((wave + nwv * a) * NSL + my_slot) + 16 * my_j + 4 * lg; };
-
+  }
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) ld(s);
+  }
+  if (select) {
     // ---- C. per-head range, linear bins, histogram, boundary bin
     {
       uint32_t kmax = 0u, kmin = 0u;   // kmin holds ~key
@@ -639,9 +726,11 @@ __global__ __launch_bounds__(1024) void k_select(
     }
     return selw[hl * nblk + blk];
   };
-  for (int idx = tid; idx < nh * nblk; idx += nthr) {
-    const int blk = idx / nh, hl = idx - blk * nh;
-    mask[((size_t)b * nblk + blk) * Hq_pad + h0 + hl] = word_of(hl, blk);
+  if constexpr (!FUSED) {
+    for (int idx = tid; idx < nh * nblk; idx += nthr) {
+      const int blk = idx / nh, hl = idx - blk * nh;
+      mask[((size_t)b * nblk + blk) * Hq_pad + h0 + hl] = word_of(hl, blk);
+    }
   }
   if (sel_out != nullptr) {
     // ascending ids: one wavefront per head, block counts prefix-summed in order
@@ -664,9 +753,267 @@ __global__ __launch_bounds__(1024) void k_select(
       }
     }
   }
-  // latent queries for the flash-decode kernel (stored last: stores share the load counter)
-  for (int i = tid; i < nh * r_pad; i += nthr)
-    qt[((size_t)b * Hq_pad + h0) * r_pad + i] = qs[i];
+  if constexpr (!FUSED) {
+    // latent queries for the flash-decode kernel (stored last: stores share the load counter)
+    for (int i = tid; i < nh * r_pad; i += nthr)
+      qt[((size_t)b * Hq_pad + h0) * r_pad + i] = qs[i];
+  } else {
+    // ================= single-kernel decode of heads h0..h0+nh-1 over every token
+    const T* __restrict__ Uv = static_cast<const T*>(fa.Uv);
+    const T* __restrict__ Bv = static_cast<const T*>(fa.Bv);
+    const T* __restrict__ tk = static_cast<const T*>(fa.text_k);
+    const T* __restrict__ tv = static_cast<const T*>(fa.text_v);
+    const int Tn = fa.Tn;
+    const float sl2 = fa.sl2;
+    (void)Uv;
+    float* sts = reinterpret_cast<float*>(smem_raw + Ly.sts);      // [HG][Tn] text scores, then p
+    float* zs = reinterpret_cast<float*>(smem_raw + Ly.zs);        // [HG][r_pad] latent sums
+    uint32_t* hmx = reinterpret_cast<uint32_t*>(smem_raw + Ly.hmx);  // [HG] max score key
+    float* lpart = reinterpret_cast<float*>(smem_raw + Ly.lpart);  // [waves][HG]
+    float* ltx = reinterpret_cast<float*>(smem_raw + Ly.ltx);      // [HG] text sums
+    float* lfin = reinterpret_cast<float*>(smem_raw + Ly.lfin);    // [HG] softmax denominators
+    float* zpart = reinterpret_cast<float*>(hist);                 // [waves][HG][r_pad]
+    float* red = reinterpret_cast<float*>(hist);                   // [row groups][HG * d]
+
+    // ---- F1. text scores in log2 units (LPR lanes per text row); running max per head
+    if (Tn > 0) {
+      const int nrt = nh * Tn;
+      for (int r0 = wave * RPW + rw; r0 - rw < nrt; r0 += XB * rstep) {
+        Vec16<T> xt[XB];
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
+          const int row = min(r0 + u * rstep, nrt - 1);
+          const int hl = row / Tn, t = row - hl * Tn;
+          xt[u].load(tk + ((size_t)b * Tn + t) * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + seg * V);
+        }
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
+          const int row = r0 + u * rstep;
+          const int hl = min(row, nrt - 1) / Tn;
+          const float* qp = qh + hl * d + seg * V;
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < V; ++e) part = fmaf(xt[u].get(e), qp[e], part);
+          part = group_sum(part, LPR);
+          if (seg == 0 && row < nrt) {
+            const float sv = part * sl2;
+            sts[row] = sv;
+            atomicMax(&hmx[hl], score_key(sv));
+          }
+        }
+      }
+    }
+
+    // ---- F2. full-rank part of the selected tokens' scores (columns >= r_lo), on the
+    // same block-diagonal tiles as the low-rank scores; final scores in log2 units
+    const int nph = NP - p0;
+    uint2 qhi[NPM];
+#pragma unroll
+    for (int j = 0; j < NPM; ++j) {
+      const int p = p0 + j;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = 16 * p + 4 * lg + e;
+        v[e] = (my_on && p < NP && col >= r_lo) ? qs[my_h * r_pad + col] : 0.f;
+      }
+      qhi[j] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+    uint32_t selb = 0;   // bit 4a+t: token at full rank
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) {
+      const int n0 = tok(a);
+      const uint32_t w = word_of(my_h, min(n0 >> 5, nblk - 1)) >> (n0 & 31);
+      v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NPM; ++j) {
+        const int s = a * NPM + j;
+        if (j < nph) {
+          const uint4 bo = my_j == 0 ? make_uint4(qhi[j].x, qhi[j].y, 0u, 0u)
+                                     : make_uint4(0u, 0u, qhi[j].x, qhi[j].y);
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) {
+            const uint4 bb = sl == my_slot ? bo : make_uint4(0u, 0u, 0u, 0u);
+            acc = mfma_bf16_k32(__builtin_bit_cast(v8bf, rb[s % PD][sl].raw),
+                                __builtin_bit_cast(v8bf, bb), acc);
+          }
+        }
+        if (s + PD < 2 * NSK) ld(s + PD);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool ok = my_on && tok(a) + t < N;
+        const bool full = ok && ((w >> t) & 1u);
+        selb |= full ? (1u << (4 * a + t)) : 0u;
+        sc[4 * a + t] = ok ? sl2 * (sc[4 * a + t] + (full ? acc[t] : 0.f)) : -INFINITY;
+      }
+    }
+    // ---- F3. softmax over text and visual tokens: per-head maximum, probabilities, sums
+    {
+      uint32_t km = 0u;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) km = max(km, score_key(sc[i]));
+      km = head_max<HG>(km);
+      if (lg == 0 && c16 < HG && my_on) atomicMax(&hmx[my_h], km);
+    }
+    __syncthreads();
+    {
+      const float Mh = my_on ? key_score(hmx[my_h]) : 0.f;
+      float lp = 0.f;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const float pv = exp2f(sc[i] - Mh);   // -inf -> 0
+        sc[i] = pv;
+        lp += pv;
+      }
+      lp = head_sum<HG>(lp);
+      if (lg == 0 && c16 < HG) lpart[wave * HG + c16] = lp;
+      if (wave < nh && Tn > 0) {
+        const float M = key_score(hmx[wave]);
+        float lt = 0.f;
+        for (int t = lane; t < Tn; t += 64) {
+          const float pv = exp2f(sts[wave * Tn + t] - M);
+          sts[wave * Tn + t] = pv;
+          lt += pv;
+        }
+        lt = group_sum(lt, 64);
+        if (lane == 0) ltx[wave] = lt;
+      }
+    }
+    // ---- F4. latent values z_h = sum_n p[n] U_v[n, :r(n)]: U_v tiles as the A operand
+    // (rows = latent columns), probabilities as the block-diagonal B operand
+    v4f Z[NPM];
+#pragma unroll
+    for (int p = 0; p < NPM; ++p) Z[p] = v4f{0.f, 0.f, 0.f, 0.f};
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) {
+      const uint32_t sb = selb >> (4 * a);
+      const float* pv = sc + 4 * a;
+      const uint32_t pa0 = pack_bf16x2(pv[0], pv[1]), pa1 = pack_bf16x2(pv[2], pv[3]);
+      const uint32_t ps0 = pack_bf16x2((sb & 1u) ? pv[0] : 0.f, (sb & 2u) ? pv[1] : 0.f);
+      const uint32_t ps1 = pack_bf16x2((sb & 4u) ? pv[2] : 0.f, (sb & 8u) ? pv[3] : 0.f);
+      const uint4 BA = my_j == 0 ? make_uint4(pa0, pa1, 0u, 0u) : make_uint4(0u, 0u, pa0, pa1);
+      const uint4 BS = my_j == 0 ? make_uint4(ps0, ps1, 0u, 0u) : make_uint4(0u, 0u, ps0, ps1);
+#pragma unroll
+      for (int p = 0; p < NPM; ++p) {
+        const int s = NSK + a * NPM + p;
+        if (p < NP) {
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) {
+            const bool on = sl == my_slot;
+            const v8bf ba = __builtin_bit_cast(v8bf, on ? BA : z4);
+            const v8bf bs = __builtin_bit_cast(v8bf, on ? BS : z4);
+            const v8bf av = __builtin_bit_cast(v8bf, rb[s % PD][sl].raw);
+            if (16 * p + 16 <= r_lo) {
+              Z[p] = mfma_bf16_k32(av, ba, Z[p]);
+            } else if (16 * p >= r_lo) {
+              Z[p] = mfma_bf16_k32(av, bs, Z[p]);
+            } else {   // panel straddling r_lo: this lane's A row is latent column 16p + c16
+              const bool lo_row = 16 * p + c16 < r_lo;
+              const v8bf zz = __builtin_bit_cast(v8bf, z4);
+              Z[p] = mfma_bf16_k32(lo_row ? av : zz, ba, Z[p]);
+              Z[p] = mfma_bf16_k32(lo_row ? zz : av, bs, Z[p]);
+            }
+          }
+        }
+        if (s + PD < 2 * NSK) ld(s + PD);
+      }
+    }
+    // lane l holds Z for latent columns 16p + 4lg + t and tile column c16: sum the
+    // columns of one head inside the row, one partial per wavefront (fixed-order sums)
+#pragma unroll
+    for (int p = 0; p < NPM; ++p)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Z[p][t] = head_sum_row<HG>(Z[p][t]);
+    if (c16 < HG) {
+#pragma unroll
+      for (int p = 0; p < NPM; ++p)
+        if (p < NP) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) zpart[(wave * HG + c16) * r_pad + 16 * p + 4 * lg + t] = Z[p][t];
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nh * r_pad; idx += nthr) {
+      const int hl = idx / r_pad, i = idx - hl * r_pad;
+      float z = 0.f;
+      for (int w2 = 0; w2 < nwv; ++w2) z += zpart[(w2 * HG + hl) * r_pad + i];
+      zs[idx] = z;
+    }
+    if (tid < nh) {
+      float l = ltx[tid];
+      for (int w2 = 0; w2 < nwv; ++w2) l += lpart[w2 * HG + tid];
+      lfin[tid] = l;
+    }
+    __syncthreads();
+
+    // ---- F5. out_h = (z_h B_v[:, g's columns] + sum_t p_t V_text[t, g's columns]) / l_h:
+    // weighted sums of r_pad + Tn rows; thread = (head, 16-byte column chunk, row group)
+    {
+      const int units = nh * LPR;
+      const int RS = nthr / units;
+      const int unit = tid % units, rsub = tid / units;
+      const int hl = unit / LPR, cc = unit - hl * LPR;
+      const int g = ((h0 + hl) * ginv_num) >> 16;
+      const int rows = r_pad + Tn;
+      float acc[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = 0.f;
+      if (rsub < RS) {
+        constexpr int UO = 4;   // rows in flight per thread
+        for (int r0 = rsub; r0 < rows; r0 += UO * RS) {
+          Vec16<T> xo[UO];
+#pragma unroll
+          for (int u = 0; u < UO; ++u) {
+            const int row = min(r0 + u * RS, rows - 1);
+            const T* src = row < r_pad ? Bv + ((size_t)b * r_pad + row) * W
+                                       : tv + ((size_t)b * Tn + (row - r_pad)) * W;
+            xo[u].load(src + (size_t)g * d + cc * V);
+          }
+#pragma unroll
+          for (int u = 0; u < UO; ++u) {
+            const int row = r0 + u * RS;
+            const float wgt = row < rows ? (row < r_pad ? zs[hl * r_pad + row] : sts[hl * Tn + row - r_pad]) : 0.f;
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[e] = fmaf(wgt, xo[u].get(e), acc[e]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) red[(rsub * units + unit) * V + e] = acc[e];
+      }
+      __syncthreads();
+      for (int idx = tid; idx < units * V; idx += nthr) {
+        float o = 0.f;
+        for (int r = 0; r < RS; ++r) o += red[(size_t)r * units * V + idx];
+        const int h2 = idx / d, j = idx - h2 * d;
+        fa.out[((size_t)b * Hq + h0 + h2) * d + j] = o / lfin[h2];
+      }
+    }
+  }
+}
+
+// Selection only: writes the selection words and the latent queries for the split-N
+// flash-decode kernel.
+template <class T, int HG, int NPL, int NACC>
+__global__ __launch_bounds__(1024) void k_select(
+    const T* __restrict__ Uk, const T* __restrict__ Bk, const float* __restrict__ q,
+    float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
+    int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
+    int r_lo, int top_k, FusedArgs fa) {
+  select_body<T, HG, NPL, NACC, false>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad, W, d,
+                                       G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
+}
+
+// The whole decode step of four query heads of one sequence (bf16 factors).
+template <int NPL, int NACC>
+__global__ __launch_bounds__(1024) void k_decode(
+    const bf16_t* __restrict__ Uk, const bf16_t* __restrict__ Bk, const float* __restrict__ q,
+    float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
+    int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
+    int r_lo, int top_k, FusedArgs fa) {
+  select_body<bf16_t, 4, NPL, NACC, true>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad, W,
+                                          d, G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -690,15 +1037,18 @@ static SelPlan select_plan(const Dims& dm, int r_lo) {
   return pl;
 }
 
-template <class T, int HG, int NPL, int NACC>
+template <class T, int HG, int NPL, int NACC, bool FUSED>
 static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, int top_k,
-                                  int32_t* sel_out, int waves, hipStream_t st, const KernelEvents& ev) {
+                                  int32_t* sel_out, int waves, const FusedArgs& fa, hipStream_t st,
+                                  const KernelEvents& ev) {
   const Dims& dm = c->dm;
   const int HGN = (dm.Hq + HG - 1) / HG;
-  const size_t lds = sel_layout(HG, dm.nblk, dm.r_pad, dm.d).total;
+  const size_t lds = sel_layout(HG, dm.nblk, dm.r_pad, dm.d, FUSED, FUSED ? fa.Tn : 0).total;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   if ((dm.nblk + 8 / HG - 1) / (8 / HG) > waves * NACC) return hipErrorInvalidValue;
-  const void* fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC>);
+  const void* fn;
+  if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<NPL, NACC>);
+  else fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC>);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -706,11 +1056,17 @@ static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, i
     attr_set = true;
   }
   const int grid = ((dm.B + 7) / 8) * 8 * HGN;
-  hipExtLaunchKernelGGL((k_select<T, HG, NPL, NACC>), dim3(grid), dim3(64 * waves), lds, st,
-                        ev.start, ev.stop, 0, static_cast<const T*>(c->Uk),
-                        static_cast<const T*>(c->Bk), q, c->qt, c->mask, sel_out, dm.B, dm.N,
-                        dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d, dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo,
-                        top_k);
+  if constexpr (FUSED)
+    hipExtLaunchKernelGGL((k_decode<NPL, NACC>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
+                          ev.stop, 0, static_cast<const T*>(c->Uk), static_cast<const T*>(c->Bk), q,
+                          c->qt, c->mask, sel_out, dm.B, dm.N, dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d,
+                          dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo, top_k, fa);
+  else
+    hipExtLaunchKernelGGL((k_select<T, HG, NPL, NACC>), dim3(grid), dim3(64 * waves), lds, st,
+                          ev.start, ev.stop, 0, static_cast<const T*>(c->Uk),
+                          static_cast<const T*>(c->Bk), q, c->qt, c->mask, sel_out, dm.B, dm.N,
+                          dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d, dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo,
+                          top_k, fa);
   return hipGetLastError();
 }
 
@@ -718,9 +1074,10 @@ template <class T>
 static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, int top_k,
                                   int32_t* sel_out, hipStream_t st, const KernelEvents& ev) {
   const SelPlan pl = select_plan(c->dm, r_lo);
+  const FusedArgs fa{};
 #define AP_SEL(HGV, NPLV, NACCV)                                                        \
   if (pl.HG == HGV && pl.NPL == NPLV && pl.NACC == NACCV)                               \
-    return launch_select_v<T, HGV, NPLV, NACCV>(c, q, r_lo, top_k, sel_out, pl.waves, st, ev);
+    return launch_select_v<T, HGV, NPLV, NACCV, false>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
   AP_SEL(4, 1, 2)
   AP_SEL(4, 1, 3)
   AP_SEL(4, 1, 4)
@@ -738,6 +1095,47 @@ hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
                          hipStream_t st, const KernelEvents& ev) {
   if (c->dm.storage == AP_BF16) return launch_select_t<bf16_t>(c, q, r_lo, top_k, sel_out, st, ev);
   return launch_select_t<float>(c, q, r_lo, top_k, sel_out, st, ev);
+}
+
+bool decode_fused_supported(const Dims& dm, int r_lo, int n_text) {
+  if (dm.storage != AP_BF16 || dm.NP > 4 || n_text > 1024) return false;
+  const SelPlan pl = select_plan(dm, r_lo);
+  if (pl.HG != 4) return false;
+  // each workgroup re-reads its sequence's U_k / U_v from L2 and runs one long chain:
+  // worth it while the workgroups fit the GPU at one per CU (256 CUs); with more, the
+  // split-N path spreads the same bytes better (measured on the batch-64 GQA and the
+  // batch-256 layers)
+  if ((size_t)dm.B * ((dm.Hq + 3) / 4) > 256) return false;
+  const int LPR = dm.d / 8;
+  if (dm.d % 8 != 0 || LPR > 64 || (LPR & (LPR - 1)) != 0 || dm.W % 8 != 0) return false;
+  return sel_layout(4, dm.nblk, dm.r_pad, dm.d, true, n_text).total <= 160 * 1024;
+}
+
+hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, int r_lo, int top_k,
+                               int32_t* sel_out, int n_text, const void* text_k, const void* text_v,
+                               float sl2, hipStream_t st, const KernelEvents& ev) {
+  const SelPlan pl = select_plan(c->dm, r_lo);
+  FusedArgs fa;
+  fa.Uv = c->Uv;
+  fa.Bv = c->Bv;
+  fa.text_k = n_text > 0 ? text_k : nullptr;
+  fa.text_v = n_text > 0 ? text_v : nullptr;
+  fa.out = out;
+  fa.Tn = n_text;
+  fa.sl2 = sl2;
+#define AP_FUS(NPLV, NACCV)                                                             \
+  if (pl.NPL == NPLV && pl.NACC == NACCV)                                               \
+    return launch_select_v<bf16_t, 4, NPLV, NACCV, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
+  AP_FUS(1, 2)
+  AP_FUS(1, 3)
+  AP_FUS(1, 4)
+  AP_FUS(1, 8)
+  AP_FUS(2, 2)
+  AP_FUS(2, 3)
+  AP_FUS(2, 4)
+  AP_FUS(2, 8)
+#undef AP_FUS
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ap

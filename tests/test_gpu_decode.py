@@ -116,27 +116,54 @@ def test_decode_duplicated_tokens_tie_to_lower_ids(gpu_lib):
                 assert chosen == list(range(60, 60 + len(chosen))), (b, h, chosen[:5])
 
 
-def test_decode_is_deterministic(gpu_lib):
-    w = SMALL["bf16_rank128"]
+@pytest.mark.parametrize("name,splits", [("bf16_rank128", 0), ("bf16_straddle_text", 0),
+                                         ("bf16_straddle_text", 3)])
+def test_decode_is_deterministic(gpu_lib, name, splits):
+    w = SMALL[name]
     seqs = make_inputs(w)
     cache, q, tk, tv = upload_decode(w, seqs, gpu_lib)
-    outs = [gpu_lib.decode(cache, q, r_lo=w.r_lo, top_k=w.top_k, scale=w.scale).cpu() for _ in range(3)]
+    outs = [gpu_lib.decode(cache, q, r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, text_k=tk,
+                           text_v=tv, splits=splits).cpu() for _ in range(3)]
     cache.free()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
-@pytest.mark.parametrize("cfg,n_distinct", [(2, 3), (3, 2), (4, 2), (5, 2)])
-def test_decode_parity_full_configs(gpu_lib, cfg, n_distinct):
-    """Full batch at the workload's real shape; distinct sequences are checked against
+@pytest.mark.parametrize("name,splits,path", [("bf16_straddle_text", 0, "decode"),
+                                              ("bf16_straddle_text", 2, "split"),
+                                              ("bf16_rank128", 0, "split"),
+                                              ("f32_text_long", 0, "split")])
+def test_decode_path_taken(gpu_lib, name, splits, path):
+    """splits == 0 on a covered shape runs the single-kernel decode; an explicit split
+    count, rank 128 or fp32 factors run selection + split-N flash-decode + combine."""
+    w = SMALL[name]
+    seqs = make_inputs(w)
+    cache, q, tk, tv = upload_decode(w, seqs, gpu_lib)
+    cache.timing_enable(1)
+    gpu_lib.decode(cache, q, r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, text_k=tk, text_v=tv,
+                   splits=splits)
+    ms, n = cache.timing_read()
+    cache.free()
+    assert n == 1
+    if path == "decode":
+        assert ms["decode"] > 0 and ms["select"] == ms["attn"] == ms["combine"] == 0
+    else:
+        assert ms["decode"] == 0 and min(ms["select"], ms["attn"], ms["combine"]) > 0
+
+
+@pytest.mark.parametrize("cfg,n_distinct,splits", [(2, 3, 0), (2, 3, 16), (3, 2, 0), (4, 2, 0),
+                                                   (5, 2, 0)])
+def test_decode_parity_full_configs(gpu_lib, cfg, n_distinct, splits):
+    """Full batch at the workload's real shape (splits 0: the single-kernel decode where
+    the shape allows; 16: the split-N path); distinct sequences are checked against
     the oracle and every replica must equal its original bit for bit."""
     w = wl.WORKLOADS[cfg]
     seqs = make_inputs(w, n_distinct)
-    out, sel = run_decode(w, seqs, gpu_lib)
+    out, sel = run_decode(w, seqs, gpu_lib, splits=splits)
     err, flips = check_against_oracle(w, seqs, out, sel)
     for b in range(len(seqs), w.batch):
         o = b % len(seqs)
         assert np.array_equal(out[b], out[o]) and np.array_equal(sel[b], sel[o]), f"replica {b}"
-    print(f"cfg {cfg}: max abs err {err:.3e}, band flips {flips}")
+    print(f"cfg {cfg} splits {splits}: max abs err {err:.3e}, band flips {flips}")
 
 
 def test_empty_batch_is_a_noop(gpu_lib):
