@@ -33,7 +33,7 @@
 namespace ap {
 
 constexpr int kSelMaxWaves = 16;
-constexpr int kSelBins = 2048;   // linear bins of the histogram pass
+constexpr int kSelBins = 1024;   // linear bins of the histogram pass
 constexpr int kSelCap = 128;     // boundary-bin tokens ranked exactly by comparison
 
 enum SelMode : int { kNone = 0, kAll = 1, kWholeBin = 2, kRank = 3, kRadix = 4 };
@@ -50,7 +50,7 @@ struct SelState {
 
 struct SelLayout {
   size_t qh, qs, st, rng, hist, selw, cand;
-  size_t sts, zs, hmx, lpart, ltx, lfin;   // single-kernel decode only
+  size_t sts, zs, hmx, lpart, ltx, lfin, red;   // single-kernel decode only
   size_t total;
   int hs;          // words per head in hist
 };
@@ -72,7 +72,7 @@ __host__ __device__ inline SelLayout sel_layout(int HG, int nblk, int r_pad, int
   L.hist = o; o = up(o + (size_t)HG * L.hs * 4);
   L.selw = o; o = up(o + (size_t)HG * nblk * 4);
   L.cand = o; o = up(o + (size_t)HG * kSelCap * 8);
-  L.sts = L.zs = L.hmx = L.lpart = L.ltx = L.lfin = o;
+  L.sts = L.zs = L.hmx = L.lpart = L.ltx = L.lfin = L.red = o;
   if (fused) {
     L.sts = o;   o = up(o + (size_t)HG * Tn * 4);
     L.zs = o;    o = up(o + (size_t)HG * r_pad * 4);
@@ -80,9 +80,20 @@ __host__ __device__ inline SelLayout sel_layout(int HG, int nblk, int r_pad, int
     L.lpart = o; o = up(o + (size_t)kSelMaxWaves * HG * 4);
     L.ltx = o;   o = up(o + (size_t)HG * 4);
     L.lfin = o;  o = up(o + (size_t)HG * 4);
+    // the output partial sums [1024 threads][8 floats]
+    L.red = o;   o = up(o + (size_t)1024 * 8 * 4);
   }
   L.total = o;
   return L;
+}
+
+// Workgroup barrier that orders LDS only: the workgroup's waves exchange data through
+// LDS alone, so global loads still in flight (prefetched tiles and rows) are not
+// waited for here, as a full __syncthreads() would.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Inverse of score_key.
@@ -172,16 +183,17 @@ __device__ __forceinline__ bool digit_search(const uint32_t* hist, uint32_t need
   return true;
 }
 
-// The same search over kSelBins bins, by a whole wavefront: lane l first sums bins
-// [kSelBins-32(l+1), kSelBins-32l); then the 32 bins of the slice holding the need-th
-// element are scanned one per lane.  Every lane returns the result.
+// The same search over kSelBins bins, by a whole wavefront: lane l first sums the SPL
+// bins [kSelBins-SPL(l+1), kSelBins-SPL*l); then the SPL bins of the slice holding the
+// need-th element are scanned one per lane.  Every lane returns the result.
 __device__ __forceinline__ void bin_search(const uint32_t* hist, uint32_t need, int lane,
                                            int* bin, uint32_t* above, uint32_t* in_bin) {
-  static_assert(kSelBins == 64 * 32, "one 32-bin slice per lane");
-  const uint4* sl = reinterpret_cast<const uint4*>(hist + kSelBins - 32 * (lane + 1));
+  constexpr int SPL = kSelBins / 64;
+  static_assert(SPL % 4 == 0 && SPL <= 64, "whole 16-byte reads, one scan");
+  const uint4* sl = reinterpret_cast<const uint4*>(hist + kSelBins - SPL * (lane + 1));
   uint32_t tot = 0;
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
+  for (int v = 0; v < SPL / 4; ++v) {
     const uint4 x = sl[v];
     tot += x.x + x.y + x.z + x.w;
   }
@@ -190,13 +202,12 @@ __device__ __forceinline__ void bin_search(const uint32_t* hist, uint32_t need, 
   const uint64_t hit = __ballot(excl < need && incl >= need);
   const int L = hit ? static_cast<int>(__ffsll(static_cast<unsigned long long>(hit))) - 1 : 63;
   const uint32_t base = __shfl(excl, L, 64);
-  // bins of slice L in descending order, lanes 0..31
-  const int bn = kSelBins - 32 * L - 1 - (lane & 31);
-  const uint32_t c = lane < 32 ? hist[bn] : 0u;
+  // bins of slice L in descending order, one per lane 0..SPL-1
+  const uint32_t c = lane < SPL ? hist[kSelBins - SPL * L - 1 - lane] : 0u;
   const uint32_t ci = base + wave_incl_scan(c, lane);
-  const uint64_t hit2 = __ballot(lane < 32 && ci >= need);
-  const int e = hit2 ? static_cast<int>(__ffsll(static_cast<unsigned long long>(hit2))) - 1 : 31;
-  *bin = kSelBins - 32 * L - 1 - e;
+  const uint64_t hit2 = __ballot(lane < SPL && ci >= need);
+  const int e = hit2 ? static_cast<int>(__ffsll(static_cast<unsigned long long>(hit2))) - 1 : SPL - 1;
+  *bin = kSelBins - SPL * L - 1 - e;
   *in_bin = __shfl(c, e, 64);
   *above = __shfl(ci, e, 64) - *in_bin;
 }
@@ -356,6 +367,20 @@ __device__ __forceinline__ void select_body(
   // load is never sunk behind the tile loads
   const int nq = nh * d;
   const float qv = q[((size_t)b * Hq + h0) * d + min(tid, nq - 1)];
+  // single-kernel decode: the first text K rows ride along (text scores need only q)
+  const int Tn = FUSED ? fa.Tn : 0;
+  const int nrt = nh * Tn;                   // text rows (head, token)
+  // with no text the loads read B_k instead (always valid), so they stay unconditional
+  const T* __restrict__ tk = Tn > 0 ? static_cast<const T*>(fa.text_k) : Bk;
+  Vec16<T> xt[FUSED ? XB : 1];
+  auto load_text = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < XB; ++u) {
+      const int row = max(min(r0 + u * rstep, nrt - 1), 0);
+      const int hl = row / max(Tn, 1), t = row - hl * Tn;
+      xt[u].load(tk + ((size_t)b * Tn + t) * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + seg * V);
+    }
+  };
 
   LaneTile<T> tb[PREF][NSL];
   auto load_step = [&](int s) {   // s is a compile-time constant after unrolling
@@ -384,7 +409,7 @@ __device__ __forceinline__ void select_body(
       reinterpret_cast<float*>(smem_raw + Ly.ltx)[tid] = 0.f;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // latent queries q~[h][i] = B_k[i, g*d : g*d+d] . q_h
   if (vec) {
     for (int r0 = wave * RPW + rw; r0 - rw < nrows; r0 += XB * rstep) {
@@ -412,14 +437,17 @@ __device__ __forceinline__ void select_body(
       qs[hl * r_pad + i] = acc;
     }
   }
-  __syncthreads();
+  lds_barrier();
+  // single-kernel decode: the text K rows are requested now, behind B_k, and scored
+  // after the selection
+  if constexpr (FUSED) load_text(wave * RPW + rw);
 
   // single-kernel decode: tiles of the full-rank score pass (U_k panels holding columns
   // >= r_lo) and then of the value pass (all U_v panels), 2 tiles per step, PD steps in
   // flight; the first ones are issued right after the low-rank scores
   constexpr int NPM = 4;                        // panels (r <= 64)
   constexpr int NSK = NACC * NPM;               // steps of each pass
-  constexpr int PD = NACC <= 3 ? 6 : (NACC <= 4 ? 4 : 2);
+  constexpr int PD = NACC <= 4 ? 4 : 2;
   const int p0 = r_lo >> 4;                     // first panel with a column >= r_lo
   LaneTile<T> rb[FUSED ? PD : 1][NSL];
   auto ld = [&](int s) {   // s is a compile-time constant after unrolling
@@ -493,10 +521,7 @@ __device__ __forceinline__ void select_body(
       }
     }
   }
-  if constexpr (FUSED) {
-#pragma unroll
-    for (int s = 0; s < PD; ++s) ld(s);
-  }
+
   if (select) {
     // ---- C. per-head range, linear bins, histogram, boundary bin
     {
@@ -520,14 +545,14 @@ __device__ __forceinline__ void select_body(
         atomicMax(&rng[2 * my_h + 1], kmin);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < nh) {
       const float hi = key_score(rng[2 * tid]), lo = key_score(~rng[2 * tid + 1]);
       const float range = hi - lo;
       st[tid].lo = lo;
       st[tid].mul = (range > 1e-30f && range < 3.0e38f) ? static_cast<float>(kSelBins - 1) / range : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     const float lo_h = my_on ? st[my_h].lo : 0.f, mul_h = my_on ? st[my_h].mul : 0.f;
     // clamped in float first: any input (NaN included) gives a bin in [0, kSelBins)
     auto bin_of = [&](float s) {
@@ -545,7 +570,7 @@ __device__ __forceinline__ void select_body(
           atomicAdd(&hh[bin_of(sc[4 * a + t])], (my_on && n0 + t < N) ? 1u : 0u);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave < nh) {
       int bn; uint32_t above, inb;
       bin_search(hist + wave * HS, static_cast<uint32_t>(top_k), lane, &bn, &above, &inb);
@@ -558,7 +583,7 @@ __device__ __forceinline__ void select_body(
                         : (inb <= static_cast<uint32_t>(kSelCap) ? kRank : kRadix);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- D. tokens above the boundary bin (and all of it when it is taken whole);
     // candidates of a partly taken bin
@@ -604,7 +629,7 @@ __device__ __forceinline__ void select_body(
       }
     }
     if (any_rank) {
-      __syncthreads();
+      lds_barrier();
       if (wave < nh && st[wave].mode == kRank) {
         const int C = min(st[wave].ncand, kSelCap);
         const unsigned long long* ch = cand + wave * kSelCap;
@@ -624,16 +649,16 @@ __device__ __forceinline__ void select_body(
       // every head in this mode, then ties at the cutoff key taken in index order.
       uint32_t* rh = hist + my_h * HS;                 // this lane's head: digit counts
       const bool in_radix = mode_h == kRadix;
-      __syncthreads();
+      lds_barrier();
       for (int i = tid; i < nh * HS; i += nthr) hist[i] = 0;
       if (tid < nh) st[tid].tau = 0u;
       for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         const uint32_t pmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-        __syncthreads();
+        lds_barrier();
         if (pass > 0)
           for (int i = tid; i < nh * 256; i += nthr) hist[(i >> 8) * HS + (i & 255)] = 0;
-        __syncthreads();
+        lds_barrier();
         if (in_radix) {
           const uint32_t prefix = st[my_h].tau;
 #pragma unroll
@@ -648,7 +673,7 @@ __device__ __forceinline__ void select_body(
             }
           }
         }
-        __syncthreads();
+        lds_barrier();
         if (wave < nh && st[wave].mode == kRadix) {
           int dg; uint32_t above, inb;
           if (digit_search(hist + wave * HS, static_cast<uint32_t>(st[wave].need), lane, &dg, &above, &inb)) {
@@ -657,7 +682,7 @@ __device__ __forceinline__ void select_body(
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       // tie bits per block, then their exclusive prefix counts in index order
       uint32_t* tie = hist + my_h * HS + 256;
       const uint32_t tau_h = in_radix ? st[my_h].tau : 0u;
@@ -674,7 +699,7 @@ __device__ __forceinline__ void select_body(
           if (nib) atomicOr(&tie[n0 >> 5], nib << (n0 & 31));
         }
       }
-      __syncthreads();
+      lds_barrier();
       if (wave < nh && st[wave].mode == kRadix) {
         const uint32_t* tw = hist + wave * HS + 256;
         uint32_t* tp = hist + wave * HS + 256 + nblk;
@@ -687,7 +712,7 @@ __device__ __forceinline__ void select_body(
           carry += __shfl(incl, 63, 64);
         }
       }
-      __syncthreads();
+      lds_barrier();
       if (in_radix) {
         const uint32_t* tp = hist + my_h * HS + 256 + nblk;
         const uint32_t need_t = static_cast<uint32_t>(st[my_h].need);
@@ -714,7 +739,7 @@ __device__ __forceinline__ void select_body(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- E. selection bits per (head, 32-token block)
   auto word_of = [&](int hl, int blk) -> uint32_t {
@@ -761,9 +786,7 @@ __device__ __forceinline__ void select_body(
     // ================= single-kernel decode of heads h0..h0+nh-1 over every token
     const T* __restrict__ Uv = static_cast<const T*>(fa.Uv);
     const T* __restrict__ Bv = static_cast<const T*>(fa.Bv);
-    const T* __restrict__ tk = static_cast<const T*>(fa.text_k);
     const T* __restrict__ tv = static_cast<const T*>(fa.text_v);
-    const int Tn = fa.Tn;
     const float sl2 = fa.sl2;
     (void)Uv;
     float* sts = reinterpret_cast<float*>(smem_raw + Ly.sts);      // [HG][Tn] text scores, then p
@@ -773,34 +796,37 @@ __device__ __forceinline__ void select_body(
     float* ltx = reinterpret_cast<float*>(smem_raw + Ly.ltx);      // [HG] text sums
     float* lfin = reinterpret_cast<float*>(smem_raw + Ly.lfin);    // [HG] softmax denominators
     float* zpart = reinterpret_cast<float*>(hist);                 // [waves][HG][r_pad]
-    float* red = reinterpret_cast<float*>(hist);                   // [row groups][HG * d]
+    float* red = reinterpret_cast<float*>(smem_raw + Ly.red);      // [row groups][HG * d]
 
-    // ---- F1. text scores in log2 units (LPR lanes per text row); running max per head
+    // first tiles of the full-rank score pass (after the selection: requests in flight
+    // during its LDS-bound phases slow them more than they gain)
+#pragma unroll
+    for (int s = 0; s < PD; ++s) ld(s);
+    // ---- F1. text scores in log2 units (LPR lanes per text row), running max per head
+    // the first XB * rstep rows come from the loads issued after the latent queries;
+    // any further rows are loaded here
+    auto text_scores = [&](int r0) {
+#pragma unroll
+      for (int u = 0; u < XB; ++u) {
+        const int row = r0 + u * rstep;
+        const int hl = max(min(row, nrt - 1), 0) / max(Tn, 1);
+        const float* qp = qh + hl * d + seg * V;
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < V; ++e) part = fmaf(xt[u].get(e), qp[e], part);
+        part = group_sum(part, LPR);
+        if (seg == 0 && row < nrt) {
+          const float sv = part * fa.sl2;
+          sts[row] = sv;
+          atomicMax(&hmx[hl], score_key(sv));
+        }
+      }
+    };
     if (Tn > 0) {
-      const int nrt = nh * Tn;
-      for (int r0 = wave * RPW + rw; r0 - rw < nrt; r0 += XB * rstep) {
-        Vec16<T> xt[XB];
-#pragma unroll
-        for (int u = 0; u < XB; ++u) {
-          const int row = min(r0 + u * rstep, nrt - 1);
-          const int hl = row / Tn, t = row - hl * Tn;
-          xt[u].load(tk + ((size_t)b * Tn + t) * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + seg * V);
-        }
-#pragma unroll
-        for (int u = 0; u < XB; ++u) {
-          const int row = r0 + u * rstep;
-          const int hl = min(row, nrt - 1) / Tn;
-          const float* qp = qh + hl * d + seg * V;
-          float part = 0.f;
-#pragma unroll
-          for (int e = 0; e < V; ++e) part = fmaf(xt[u].get(e), qp[e], part);
-          part = group_sum(part, LPR);
-          if (seg == 0 && row < nrt) {
-            const float sv = part * sl2;
-            sts[row] = sv;
-            atomicMax(&hmx[hl], score_key(sv));
-          }
-        }
+      text_scores(wave * RPW + rw);
+      for (int r0 = wave * RPW + rw + XB * rstep; r0 - rw < nrt; r0 += XB * rstep) {
+        load_text(r0);
+        text_scores(r0);
       }
     }
 
@@ -856,7 +882,7 @@ __device__ __forceinline__ void select_body(
       km = head_max<HG>(km);
       if (lg == 0 && c16 < HG && my_on) atomicMax(&hmx[my_h], km);
     }
-    __syncthreads();
+    lds_barrier();
     {
       const float Mh = my_on ? key_score(hmx[my_h]) : 0.f;
       float lp = 0.f;
@@ -880,6 +906,27 @@ __device__ __forceinline__ void select_body(
         if (lane == 0) ltx[wave] = lt;
       }
     }
+    // output rows (F5): thread = (head, 16-byte column chunk, row group); rows 0..r_pad-1
+    // of a head are B_v rows, then its text V rows.  The first UP rows of each thread are
+    // requested as soon as the value pass has issued its last tile load
+    const int ounits = nh * LPR;
+    const int RS = nthr / ounits;
+    const int ounit = tid % ounits, rsub = tid / ounits;
+    const int ohl = ounit / LPR, occ = ounit - ohl * LPR;
+    const int og = ((h0 + ohl) * ginv_num) >> 16;
+    const int orows = r_pad + Tn;
+    constexpr int UP = 8;
+    Vec16<T> xo[UP];
+    auto load_out = [&](int r0) {
+#pragma unroll
+      for (int u = 0; u < UP; ++u) {
+        const int row = min(r0 + u * RS, orows - 1);   // clamped: loads stay unconditional
+        const T* src = row < r_pad ? Bv + ((size_t)b * r_pad + row) * W
+                                   : tv + ((size_t)b * Tn + (row - r_pad)) * W;
+        xo[u].load(src + (size_t)og * d + occ * V);
+      }
+    };
+
     // ---- F4. latent values z_h = sum_n p[n] U_v[n, :r(n)]: U_v tiles as the A operand
     // (rows = latent columns), probabilities as the block-diagonal B operand
     v4f Z[NPM];
@@ -918,6 +965,7 @@ __device__ __forceinline__ void select_body(
           }
         }
         if (s + PD < 2 * NSK) ld(s + PD);
+        if (s + PD == 2 * NSK - 1) load_out(min(rsub, RS - 1));   // right after the last tile load
       }
     }
     // lane l holds Z for latent columns 16p + 4lg + t and tile column c16: sum the
@@ -934,7 +982,7 @@ __device__ __forceinline__ void select_body(
           for (int t = 0; t < 4; ++t) zpart[(wave * HG + c16) * r_pad + 16 * p + 4 * lg + t] = Z[p][t];
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int idx = tid; idx < nh * r_pad; idx += nthr) {
       const int hl = idx / r_pad, i = idx - hl * r_pad;
       float z = 0.f;
@@ -946,43 +994,34 @@ __device__ __forceinline__ void select_body(
       for (int w2 = 0; w2 < nwv; ++w2) l += lpart[w2 * HG + tid];
       lfin[tid] = l;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- F5. out_h = (z_h B_v[:, g's columns] + sum_t p_t V_text[t, g's columns]) / l_h:
-    // weighted sums of r_pad + Tn rows; thread = (head, 16-byte column chunk, row group)
+    // weighted sums of the r_pad + Tn output rows, partial sums per row group
     {
-      const int units = nh * LPR;
-      const int RS = nthr / units;
-      const int unit = tid % units, rsub = tid / units;
-      const int hl = unit / LPR, cc = unit - hl * LPR;
-      const int g = ((h0 + hl) * ginv_num) >> 16;
-      const int rows = r_pad + Tn;
       float acc[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] = 0.f;
-      if (rsub < RS) {
-        constexpr int UO = 4;   // rows in flight per thread
-        for (int r0 = rsub; r0 < rows; r0 += UO * RS) {
-          Vec16<T> xo[UO];
+      auto accumulate = [&](int r0) {
 #pragma unroll
-          for (int u = 0; u < UO; ++u) {
-            const int row = min(r0 + u * RS, rows - 1);
-            const T* src = row < r_pad ? Bv + ((size_t)b * r_pad + row) * W
-                                       : tv + ((size_t)b * Tn + (row - r_pad)) * W;
-            xo[u].load(src + (size_t)g * d + cc * V);
-          }
+        for (int u = 0; u < UP; ++u) {
+          const int row = r0 + u * RS;
+          const float wgt = row < orows ? (row < r_pad ? zs[ohl * r_pad + row] : sts[ohl * Tn + row - r_pad]) : 0.f;
 #pragma unroll
-          for (int u = 0; u < UO; ++u) {
-            const int row = r0 + u * RS;
-            const float wgt = row < rows ? (row < r_pad ? zs[hl * r_pad + row] : sts[hl * Tn + row - r_pad]) : 0.f;
-#pragma unroll
-            for (int e = 0; e < V; ++e) acc[e] = fmaf(wgt, xo[u].get(e), acc[e]);
-          }
+          for (int e = 0; e < V; ++e) acc[e] = fmaf(wgt, xo[u].get(e), acc[e]);
         }
+      };
+      accumulate(rsub);
+      for (int r0 = rsub + UP * RS; r0 < orows; r0 += UP * RS) {
+        load_out(r0);
+        accumulate(r0);
+      }
+      const int units = ounits, unit = ounit;
+      if (rsub < RS) {
 #pragma unroll
         for (int e = 0; e < V; ++e) red[(rsub * units + unit) * V + e] = acc[e];
       }
-      __syncthreads();
+      lds_barrier();
       for (int idx = tid; idx < units * V; idx += nthr) {
         float o = 0.f;
         for (int r = 0; r < RS; ++r) o += red[(size_t)r * units * V + idx];
