@@ -12,7 +12,10 @@ import math
 
 
 def decode_brute(U_k, B_k, U_v, B_v, q, n_kv_heads, head_dim, r_lo, top_k, scale,
-                 text_k=(), text_v=()):
+                 text_k=(), text_v=(), keys=None, weights=None):
+    """keys: optional per-head importance lists to rank by instead of the low-rank
+    score; weights: if a list is given, each head's visual attention weights are
+    appended to it."""
     N = len(U_k)
     r = len(B_k)
     d = head_dim
@@ -37,7 +40,8 @@ def decode_brute(U_k, B_k, U_v, B_v, q, n_kv_heads, head_dim, r_lo, top_k, scale
             return sum(x * y for x, y in zip(a, b))
 
         s_lo = [scale * dot(khat(n, r_lo), qh) for n in range(N)]
-        ranked = sorted(range(N), key=lambda n: (-s_lo[n], n))
+        rank_by = s_lo if keys is None else [float(x) for x in keys[h]]
+        ranked = sorted(range(N), key=lambda n: (-rank_by[n], n))
         top = sorted(ranked[:top_k])
         chosen = set(top)
         scores = []
@@ -59,4 +63,42 @@ def decode_brute(U_k, B_k, U_v, B_v, q, n_kv_heads, head_dim, r_lo, top_k, scale
                 o[j] += w[N + t] / z * float(text_v[t][g * d + j])
         out[h * d:(h + 1) * d] = o
         tops.append(top)
+        if weights is not None:
+            weights.append([w[n] / z for n in range(N)])
     return out, tops
+
+
+def decode_ema_brute(U_k, B_k, U_v, B_v, qs, n_kv_heads, head_dim, r_lo, top_k, scale,
+                     alpha, per_head, text_k=(), text_v=()):
+    """Several steps of the moving-average selector with explicit loops: the first
+    step ranks by the low-rank score and sets the importance to its attention
+    weights; later steps rank by the importance, then blend in their own weights."""
+    d = head_dim
+    Hq = len(qs[0]) // d
+    N = len(U_k)
+    imp = None
+    outs, tops_all, states = [], [], []
+    for q in qs:
+        if imp is None:
+            keys = None
+        elif per_head:
+            keys = imp
+        else:
+            keys = [imp for _ in range(Hq)]
+        wts = []
+        out, tops = decode_brute(U_k, B_k, U_v, B_v, q, n_kv_heads, head_dim, r_lo, top_k,
+                                 scale, text_k, text_v, keys=keys, weights=wts)
+        if per_head:
+            new = wts
+        else:
+            new = [sum(wts[h][n] for h in range(Hq)) / Hq for n in range(N)]
+        if imp is None:
+            imp = new
+        elif per_head:
+            imp = [[alpha * imp[h][n] + (1.0 - alpha) * new[h][n] for n in range(N)] for h in range(Hq)]
+        else:
+            imp = [alpha * imp[n] + (1.0 - alpha) * new[n] for n in range(N)]
+        outs.append(out)
+        tops_all.append(tops)
+        states.append([list(row) for row in imp] if per_head else list(imp))
+    return outs, tops_all, states

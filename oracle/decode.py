@@ -43,11 +43,15 @@ def select_top(s_lo: np.ndarray, k: int) -> np.ndarray:
 
 
 def decode_ref(U_k, B_k, U_v, B_v, q, n_kv_heads: int, head_dim: int, r_lo: int,
-               top_k: int, scale: float, text_k=None, text_v=None):
+               top_k: int, scale: float, text_k=None, text_v=None, select_keys=None):
     """Decode one query vector q [Hq*d] for one sequence.
 
     U_k, U_v: N x r;  B_k, B_v: r x (Hkv*d);  text_k, text_v: T x (Hkv*d).
-    Returns dict(out [Hq*d], top [Hq][top_k] ascending ids, s_lo [Hq][N]).
+    select_keys: optional [Hq][N] importance to rank tokens by instead of s_lo
+    (the moving-average selector, see ``decode_ema_steps``).
+    Returns dict(out [Hq*d], top [Hq][top_k] ascending ids, s_lo [Hq][N],
+    p [Hq][N] the attention weight of each visual token, text included in the
+    normalisation).
     """
     U_k = np.asarray(U_k, np.float64); B_k = np.asarray(B_k, np.float64)
     U_v = np.asarray(U_v, np.float64); B_v = np.asarray(B_v, np.float64)
@@ -61,7 +65,7 @@ def decode_ref(U_k, B_k, U_v, B_v, q, n_kv_heads: int, head_dim: int, r_lo: int,
         text_k = np.asarray(text_k, np.float64)
         text_v = np.asarray(text_v, np.float64)
     out = np.zeros(Hq * d)
-    tops, s_los = [], []
+    tops, s_los, ps = [], [], []
     for h in range(Hq):
         g = h // G
         cols = slice(g * d, (g + 1) * d)
@@ -71,7 +75,7 @@ def decode_ref(U_k, B_k, U_v, B_v, q, n_kv_heads: int, head_dim: int, r_lo: int,
         V_lo = U_v[:, :r_lo] @ B_v[:r_lo, cols]
         V_full = U_v @ B_v[:, cols]
         s_lo = scale * (K_lo @ qh)
-        top = select_top(s_lo, top_k)
+        top = select_top(s_lo if select_keys is None else np.asarray(select_keys[h], np.float64), top_k)
         s = s_lo.copy()
         s[top] = scale * (K_full[top] @ qh)
         V_sel = V_lo.copy()
@@ -88,8 +92,43 @@ def decode_ref(U_k, B_k, U_v, B_v, q, n_kv_heads: int, head_dim: int, r_lo: int,
         out[h * d:(h + 1) * d] = o
         tops.append(top)
         s_los.append(s_lo)
+        ps.append(p[:N])
     return dict(out=out, top=np.array(tops, dtype=np.int64).reshape(Hq, top_k),
-                s_lo=np.array(s_los))
+                s_lo=np.array(s_los), p=np.array(ps))
+
+
+def decode_ema_steps(U_k, B_k, U_v, B_v, qs, n_kv_heads: int, head_dim: int, r_lo: int,
+                     top_k: int, scale: float, alpha: float, per_head: bool,
+                     text_k=None, text_v=None, state=None):
+    """Several decode steps with the moving-average importance selector.
+
+    [es §2.B], [fr §2.B "Score d'importance"], [de §2.B "Mechanismus"]: each token's
+    importance is a moving average, with parameter alpha, of the attention it has
+    received; the tokens of highest importance are decompressed at full rank.
+    Readings (listed in the design doc): the average is taken over the attention weights
+    p of each step, I <- alpha * I + (1 - alpha) * p; a step selects with the
+    importance left by the steps before it; the first step (state None) has no
+    history and selects by its own low-rank logit, and then I = p.  per_head: one
+    importance per (query head, token), else one per token, fed with the mean of
+    the query heads' weights and shared by all of them.
+
+    qs: [steps][Hq*d].  Returns (list of decode_ref results, state after each step:
+    [Hq][N] per head, [N] shared).
+    """
+    results, states = [], []
+    I = None if state is None else np.asarray(state, np.float64).copy()
+    Hq = np.asarray(qs[0]).shape[0] // head_dim
+    for q in qs:
+        keys = None
+        if I is not None:
+            keys = I if per_head else np.broadcast_to(I, (Hq, I.shape[-1]))
+        res = decode_ref(U_k, B_k, U_v, B_v, q, n_kv_heads, head_dim, r_lo, top_k, scale,
+                         text_k, text_v, select_keys=keys)
+        p = res["p"] if per_head else res["p"].mean(axis=0)
+        I = p.copy() if I is None else alpha * I + (1.0 - alpha) * p
+        results.append(res)
+        states.append(I.copy())
+    return results, states
 
 
 def band_mask(s_lo_h: np.ndarray, k: int, rel: float = 1e-3) -> np.ndarray:

@@ -105,3 +105,29 @@ def test_rsvd_mutants_are_caught(old, new):
     except (ValueError, RuntimeError, np.linalg.LinAlgError):
         ok = False
     assert not ok
+
+
+@pytest.mark.parametrize("old,new", [
+    ("I = p.copy() if I is None else alpha * I + (1.0 - alpha) * p",
+     "I = p.copy() if I is None else (1.0 - alpha) * I + alpha * p"),        # swapped weights
+    ("p = res[\"p\"] if per_head else res[\"p\"].mean(axis=0)",
+     "p = res[\"p\"] if per_head else res[\"p\"].sum(axis=0)"),              # sum, not mean
+    ("            keys = I if per_head else np.broadcast_to(I, (Hq, I.shape[-1]))",
+     "            keys = None"),                                               # history ignored
+])
+def test_mutated_ema_selector_is_caught(old, new):
+    from oracle.brute import decode_ema_brute
+    m = _mutant(dec, old, new)
+    g = np.random.default_rng(70)
+    N, r, Hkv, Hq, d, T = 9, 4, 2, 4, 3, 2
+    W = Hkv * d
+    Uk, Bk, Uv, Bv = (g.standard_normal(s) for s in [(N, r), (r, W), (N, r), (r, W)])
+    Kt, Vt = g.standard_normal((T, W)), g.standard_normal((T, W))
+    qs = [g.standard_normal(Hq * d) for _ in range(4)]
+    res, states = m.decode_ema_steps(Uk, Bk, Uv, Bv, qs, Hkv, d, 2, 3, 0.8, 0.7, False, Kt, Vt)
+    outs, tops, bstates = decode_ema_brute(Uk.tolist(), Bk.tolist(), Uv.tolist(), Bv.tolist(),
+                                           [q.tolist() for q in qs], Hkv, d, 2, 3, 0.8, 0.7,
+                                           False, Kt.tolist(), Vt.tolist())
+    agree = all(np.max(np.abs(states[t] - np.array(bstates[t]))) <= 1e-12 and
+                [list(x) for x in res[t]["top"]] == tops[t] for t in range(len(qs)))
+    assert not agree, "the planted mistake went unnoticed"

@@ -12,6 +12,9 @@ Each test names the pin it implements:
   P9  token permutation equivariance; GQA == MHA with duplicated KV heads
   P10 edge values: N = 1, q = 0 (uniform weights, lowest-index ties)
   P11 storage accounting against the numbers printed on the pages
+  P13 the moving-average importance selector over several steps: brute force,
+      alpha = 0 closed form, weights that stay a distribution, shared == per-head
+      for one head, first step == the low-rank-logit selector
 """
 import json
 import math
@@ -22,8 +25,8 @@ import pytest
 import torch
 
 import oracle
-from oracle.brute import decode_brute
-from oracle.decode import decode_ref, select_top
+from oracle.brute import decode_brute, decode_ema_brute
+from oracle.decode import decode_ema_steps, decode_ref, select_top
 from oracle.jacobi import jacobi_svd
 from oracle.factorize import orth_mgs2, rsvd, round_to_storage
 from oracle import accounting
@@ -348,3 +351,66 @@ def test_p12_sign_matrix_layout_from_known_answer():
     assert set(np.unique(a)) == {-1.0, 1.0}
     assert not np.array_equal(a, b) and not np.array_equal(a, c)
     assert abs(a.mean()) < 0.1 and abs(np.mean(a * b)) < 0.1
+
+
+# ------------------------------------------------------------------ P13
+def _ema_case(seed, N=9, r=4, Hkv=2, Hq=4, d=3, T=2, steps=4):
+    g = np.random.default_rng(seed)
+    W = Hkv * d
+    Uk, Bk, Uv, Bv = (g.standard_normal(s) for s in [(N, r), (r, W), (N, r), (r, W)])
+    Kt, Vt = g.standard_normal((T, W)), g.standard_normal((T, W))
+    qs = [g.standard_normal(Hq * d) for _ in range(steps)]
+    return Uk, Bk, Uv, Bv, Kt, Vt, qs
+
+
+@pytest.mark.parametrize("per_head", [True, False])
+@pytest.mark.parametrize("seed,alpha,T", [(60, 0.7, 2), (61, 0.0, 0), (62, 0.95, 3)])
+def test_p13_ema_brute_force(seed, alpha, T, per_head):
+    Uk, Bk, Uv, Bv, Kt, Vt, qs = _ema_case(seed, T=T)
+    res, states = decode_ema_steps(Uk, Bk, Uv, Bv, qs, 2, 3, 2, 3, 0.8, alpha, per_head,
+                                   Kt if T else None, Vt if T else None)
+    outs, tops, bstates = decode_ema_brute(Uk.tolist(), Bk.tolist(), Uv.tolist(), Bv.tolist(),
+                                           [q.tolist() for q in qs], 2, 3, 2, 3, 0.8, alpha,
+                                           per_head, Kt.tolist() if T else (), Vt.tolist() if T else ())
+    for t in range(len(qs)):
+        assert np.max(np.abs(res[t]["out"] - np.array(outs[t]))) <= 1e-12
+        assert [list(x) for x in res[t]["top"]] == tops[t]
+        assert np.max(np.abs(states[t] - np.array(bstates[t]))) <= 1e-12
+
+
+def test_p13_ema_alpha_zero_selects_by_last_weights():
+    # alpha = 0: the importance is exactly the last step's weights, so step t+1 picks
+    # the k tokens that step t attended to most
+    Uk, Bk, Uv, Bv, Kt, Vt, qs = _ema_case(63)
+    res, states = decode_ema_steps(Uk, Bk, Uv, Bv, qs, 2, 3, 2, 3, 0.8, 0.0, True, Kt, Vt)
+    for t in range(len(qs) - 1):
+        assert np.array_equal(states[t], res[t]["p"])
+        for h in range(4):
+            assert res[t + 1]["top"][h].tolist() == select_top(res[t]["p"][h], 3).tolist()
+
+
+@pytest.mark.parametrize("per_head", [True, False])
+def test_p13_ema_state_stays_a_distribution_without_text(per_head):
+    # with no text tokens each step's weights sum to 1 per head; a convex blend of
+    # distributions (and their mean over heads) is again one
+    Uk, Bk, Uv, Bv, Kt, Vt, qs = _ema_case(64, T=0, steps=5)
+    _, states = decode_ema_steps(Uk, Bk, Uv, Bv, qs, 2, 3, 2, 3, 0.8, 0.6, per_head)
+    for I in states:
+        assert np.allclose(np.asarray(I).sum(axis=-1), 1.0, atol=1e-13)
+        assert np.all(np.asarray(I) > 0)
+
+
+def test_p13_ema_shared_equals_per_head_for_one_head():
+    Uk, Bk, Uv, Bv, Kt, Vt, qs = _ema_case(65, Hkv=1, Hq=1)
+    a, sa = decode_ema_steps(Uk, Bk, Uv, Bv, qs, 1, 3, 2, 3, 0.8, 0.5, True, Kt, Vt)
+    b, sb = decode_ema_steps(Uk, Bk, Uv, Bv, qs, 1, 3, 2, 3, 0.8, 0.5, False, Kt, Vt)
+    for t in range(len(qs)):
+        assert np.array_equal(a[t]["out"], b[t]["out"])
+        assert np.array_equal(sa[t][0], sb[t])
+
+
+def test_p13_ema_first_step_is_the_logit_selector():
+    Uk, Bk, Uv, Bv, Kt, Vt, qs = _ema_case(66)
+    res, _ = decode_ema_steps(Uk, Bk, Uv, Bv, qs[:1], 2, 3, 2, 3, 0.8, 0.5, False, Kt, Vt)
+    ref = decode_ref(Uk, Bk, Uv, Bv, qs[0], 2, 3, 2, 3, 0.8, Kt, Vt)
+    assert np.array_equal(res[0]["out"], ref["out"]) and np.array_equal(res[0]["top"], ref["top"])
