@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cfg", type=int, default=2, help="workload id (2 = the batch-32 LLaVA layer)")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--select", default="logit", choices=["logit", "ema_token", "ema_head"],
+                    help="which tokens get full rank: the current low-rank logit (default), or "
+                         "the moving average of past attention per token or per (head, token)")
+    ap.add_argument("--ema-alpha", type=float, default=0.9)
     ap.add_argument("--no-compress", action="store_true")
     ap.add_argument("--compress-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -196,13 +200,23 @@ def main():
         qs.append(stack("q", torch.float32))
         texts.append((stack("text_k", dt), stack("text_v", dt)) if w.n_text else (None, None))
     out = torch.empty(B, w.n_q_heads * w.head_dim, dtype=torch.float32, device=dev)
+    ema = args.select != "logit"
+    # moving-average selector: one importance state per cache copy (the first call of
+    # each copy has no history), one shared logit workspace
+    imps = [torch.zeros((B, w.n_q_heads, w.n_tokens) if args.select == "ema_head" else (B, w.n_tokens),
+                        dtype=torch.float32, device=dev) for _ in range(R)] if ema else [None] * R
+    scratch = torch.empty(B, w.n_q_heads, w.n_tokens, dtype=torch.float32, device=dev) if ema else None
+    first = [True] * R
     torch.cuda.synchronize()
 
     def step(i):
         j = i % R
         tk, tv = texts[j]
         binding.decode(caches[j], qs[j], r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, text_k=tk,
-                       text_v=tv, out=out, splits=args.splits)
+                       text_v=tv, out=out, splits=args.splits, select=args.select,
+                       ema_alpha=args.ema_alpha, ema_first=first[j], importance=imps[j],
+                       ema_scratch=scratch)
+        first[j] = False
 
     for i in range(args.warmup):
         step(i)
@@ -267,7 +281,8 @@ def main():
         "config": {"workload": w.name, "batch": B, "n_tokens": w.n_tokens, "n_text": w.n_text,
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "rank": w.rank, "r_lo": w.r_lo, "top_k": w.top_k, "storage": w.storage,
-                   "cache_copies_rotated": R, "distinct_sequences": S},
+                   "cache_copies_rotated": R, "distinct_sequences": S, "select": args.select,
+                   **({"ema_alpha": args.ema_alpha} if ema else {})},
         "ms_per_step_hip_events": event_ms,
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "GB/s": step_bytes / (elapsed / args.steps) / 1e9,

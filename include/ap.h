@@ -151,7 +151,26 @@ typedef struct {
                             covers, else split-N); >= 1: the split-N path with that many
                             N-splits per sequence (clamped to the workspace sized at
                             ap_compress)                                                 */
+  /* Which tokens get full rank.  [es §2.B], [fr §2.B "Score d'importance"], [de §2.B
+   * "Mechanismus"]: a moving average (parameter alpha) of the attention each token has
+   * received.  AP_SELECT_LOGIT (0, the default when the struct is zeroed): the current
+   * step's low-rank logit, no state.  AP_SELECT_EMA_TOKEN: one importance per token,
+   * fed with the mean over query heads of the attention weights and shared by all
+   * heads.  AP_SELECT_EMA_HEAD: one importance per (query head, token).  The moving-
+   * average modes rank by the importance the earlier steps left (ema_first: no history
+   * yet, rank by the low-rank logit), then blend in this step's attention weights p
+   * (softmax over text and visual tokens): I <- alpha * I + (1 - alpha) * p, or I <- p
+   * on the first step.  They always run the split-N path.                              */
+  int32_t select_mode;
+  float ema_alpha;       /* 0 <= alpha < 1: weight of the history                          */
+  int32_t ema_first;     /* nonzero on the first step of a sequence's decode              */
+  float* importance;     /* device float32 state, caller-owned, read then updated in place:
+                            [B][N] (EMA_TOKEN) or [B][Hq][N] (EMA_HEAD)                    */
+  float* ema_scratch;    /* device float32 workspace [B][Hq][N], caller-owned: the step's
+                            logits; contents undefined between calls                      */
 } ap_decode_params;
+
+enum { AP_SELECT_LOGIT = 0, AP_SELECT_EMA_TOKEN = 1, AP_SELECT_EMA_HEAD = 2 };
 
 /* One decode step of attention over the compressed cache, for every sequence.
  *

@@ -42,7 +42,12 @@ class DecodeParams(ctypes.Structure):
         ("r_lo", ctypes.c_int32), ("top_k", ctypes.c_int32), ("scale", ctypes.c_float),
         ("n_text", ctypes.c_int32), ("text_k", ctypes.c_void_p), ("text_v", ctypes.c_void_p),
         ("sel_out", ctypes.c_void_p), ("splits", ctypes.c_int32),
+        ("select_mode", ctypes.c_int32), ("ema_alpha", ctypes.c_float), ("ema_first", ctypes.c_int32),
+        ("importance", ctypes.c_void_p), ("ema_scratch", ctypes.c_void_p),
     ]
+
+
+SELECT_MODES = {"logit": 0, "ema_token": 1, "ema_head": 2}
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -211,13 +216,21 @@ def compress(k: Optional[torch.Tensor], v: Optional[torch.Tensor], *, batch: int
 def decode(cache: Cache, q: torch.Tensor, *, r_lo: int, top_k: int, scale: float,
            text_k: Optional[torch.Tensor] = None, text_v: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, sel_out: Optional[torch.Tensor] = None,
-           splits: int = 0) -> torch.Tensor:
-    """ap_decode_attn: q [B, Hq*d] float32 -> out [B, Hq*d] float32."""
+           splits: int = 0, select: str = "logit", ema_alpha: float = 0.0,
+           ema_first: bool = False, importance: Optional[torch.Tensor] = None,
+           ema_scratch: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ap_decode_attn: q [B, Hq*d] float32 -> out [B, Hq*d] float32.
+
+    select: "logit" (current-step low-rank logit), "ema_token" or "ema_head" (moving
+    average of the attention weights; importance float32 [B, N] or [B, Hq, N] is read
+    and updated in place; ema_scratch float32 [B, Hq, N] is the step's workspace)."""
     if out is None:
         out = torch.empty_like(q)
     n_text = 0 if text_k is None else text_k.shape[1]
     p = DecodeParams(r_lo, top_k, scale, n_text, _ptr(text_k) if n_text else None,
-                     _ptr(text_v) if n_text else None, _ptr(sel_out), splits)
+                     _ptr(text_v) if n_text else None, _ptr(sel_out), splits,
+                     SELECT_MODES[select], ema_alpha, 1 if ema_first else 0, _ptr(importance),
+                     _ptr(ema_scratch))
     _check(lib.ap_decode_attn(cache.handle, _ptr(q), _ptr(out), ctypes.byref(p), _stream()),
            "ap_decode_attn")
     return out

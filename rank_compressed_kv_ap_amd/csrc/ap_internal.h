@@ -54,6 +54,7 @@ struct ap_cache {
   uint32_t* mask = nullptr;   // [B][nblk][Hq_pad] selection bits per 32-token block
   float* part_z = nullptr;    // [B][S_cap][Hq_pad][r_pad]
   float* part_ml = nullptr;   // [B][S_cap][Hq_pad][2]  (running max in log2 units, sum)
+  float* ml_final = nullptr;  // [B][Hq][2] softmax max (log2 units) and sum of the last step
   size_t factor_bytes = 0;
   size_t device_bytes = 0;
   hipStream_t last_stream = nullptr;
@@ -72,8 +73,9 @@ struct KernelEvents {
 
 // ---- launchers (decode_kernels.hip, select_kernel.hip)
 hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
-                         int32_t* sel_out, hipStream_t st, const KernelEvents& ev);
-hipError_t launch_attn(const ap_cache* c, int r_lo, float scale_log2e, int S, int CB,
+                         int32_t* sel_out, const float* keys, bool keys_per_head, hipStream_t st,
+                         const KernelEvents& ev);
+hipError_t launch_attn(const ap_cache* c, int r_lo, float scale_log2e, int S, int CB, float* ema_s,
                        hipStream_t st, const KernelEvents& ev);
 // Single-kernel decode (select_kernel.hip): shapes it takes, and its launch.
 bool decode_fused_supported(const Dims& dm, int r_lo, int n_text);
@@ -81,8 +83,10 @@ hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, in
                                int32_t* sel_out, int n_text, const void* text_k, const void* text_v,
                                float sl2, hipStream_t st, const KernelEvents& ev);
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float scale_log2e,
-                          int S, int T, const void* text_k, const void* text_v, hipStream_t st,
-                          const KernelEvents& ev);
+                          int S, int T, const void* text_k, const void* text_v, float* ml_out,
+                          hipStream_t st, const KernelEvents& ev);
+hipError_t launch_ema_update(const ap_cache* c, const float* s, const float* ml, float* imp,
+                             bool per_head, bool first, float alpha, hipStream_t st);
 
 // ---- launchers (pack_kernels.hip)
 hipError_t launch_pack_u(const ap_cache* c, const void* src, void* dst, bool v_layout,

@@ -79,7 +79,7 @@ static Dims make_dims(const ap_compress_params* p) {
 }
 
 static void free_all(ap_cache* c) {
-  void* ptrs[] = {c->Uk, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->qt, c->mask, c->part_z, c->part_ml};
+  void* ptrs[] = {c->Uk, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->qt, c->mask, c->part_z, c->part_ml, c->ml_final};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   for (hipEvent_t e : c->timing.ev) (void)hipEventDestroy(e);
@@ -100,6 +100,7 @@ static ap_status alloc_cache(ap_cache* c) {
       {reinterpret_cast<void**>(&c->mask), (size_t)dm.B * dm.nblk * dm.Hq_pad * 4},
       {reinterpret_cast<void**>(&c->part_z), (size_t)dm.B * dm.S_cap * dm.Hq_pad * dm.r_pad * 4},
       {reinterpret_cast<void**>(&c->part_ml), (size_t)dm.B * dm.S_cap * dm.Hq_pad * 2 * 4},
+      {reinterpret_cast<void**>(&c->ml_final), (size_t)dm.B * dm.Hq * 2 * 4},
   };
   size_t total = 0;
   for (const Req& r : reqs) {
@@ -282,10 +283,17 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
   if (!(std::isfinite(p->scale) && p->scale > 0.f)) return fail(AP_ERR_BAD_SHAPE, "scale must be finite and > 0");
   if (p->n_text < 0) return fail(AP_ERR_BAD_SHAPE, "n_text < 0");
   if (p->splits < 0) return fail(AP_ERR_BAD_SHAPE, "splits < 0");
+  if (p->select_mode < AP_SELECT_LOGIT || p->select_mode > AP_SELECT_EMA_HEAD)
+    return fail(AP_ERR_BAD_SHAPE, "select_mode must be AP_SELECT_LOGIT, AP_SELECT_EMA_TOKEN or AP_SELECT_EMA_HEAD");
+  const bool ema = p->select_mode != AP_SELECT_LOGIT;
+  if (ema && !(p->ema_alpha >= 0.f && p->ema_alpha < 1.f))
+    return fail(AP_ERR_BAD_SHAPE, "ema_alpha must satisfy 0 <= alpha < 1");
   if (dm.B == 0) return AP_OK;
   if (!q || !out) return fail(AP_ERR_NULL_ARG, "q and out must not be NULL");
   if (p->n_text > 0 && (!p->text_k || !p->text_v)) return fail(AP_ERR_NULL_ARG, "text_k/text_v must be set when n_text > 0");
   if (p->n_text > (1 << 20)) return fail(AP_ERR_UNSUPPORTED, "n_text > 2^20");
+  if (ema && (!p->importance || !p->ema_scratch))
+    return fail(AP_ERR_NULL_ARG, "importance and ema_scratch must be set for the moving-average selector");
 
   // N-splits of the flash-decode kernel: about two workgroups per CU, >= 5 token blocks
   // each (measured best on the batch-32 LLaVA layer: 16 splits of 5-6 blocks)
@@ -316,15 +324,24 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
   if (timed)
     for (int k = 0; k < AP_N_KERNELS; ++k) tm.used[(size_t)tm.calls * AP_N_KERNELS + k] = 0;
   hipError_t e = hipSuccess;
-  if (p->splits == 0 && decode_fused_supported(dm, p->r_lo, p->n_text)) {
+  const bool per_head = p->select_mode == AP_SELECT_EMA_HEAD;
+  if (!ema && p->splits == 0 && decode_fused_supported(dm, p->r_lo, p->n_text)) {
     // one kernel per step: each (sequence, 4 heads) workgroup selects, attends and projects
     e = launch_decode_fused(c, q, out, p->r_lo, p->top_k, p->sel_out, p->n_text, p->text_k,
                             p->text_v, sl2, st, events(AP_KERNEL_DECODE));
   } else {
-    e = launch_select(c, q, p->r_lo, p->top_k, p->sel_out, st, events(AP_KERNEL_SELECT));
-    if (e == hipSuccess) e = launch_attn(c, p->r_lo, sl2, S, CB, st, events(AP_KERNEL_ATTN));
+    // the moving-average selector ranks by the importance state, except on its first
+    // step (no history yet), which ranks by the low-rank logits like the default
+    const float* keys = (ema && !p->ema_first) ? p->importance : nullptr;
+    e = launch_select(c, q, p->r_lo, p->top_k, p->sel_out, keys, per_head, st, events(AP_KERNEL_SELECT));
     if (e == hipSuccess)
-      e = launch_combine(c, q, out, sl2, S, p->n_text, p->text_k, p->text_v, st, events(AP_KERNEL_COMBINE));
+      e = launch_attn(c, p->r_lo, sl2, S, CB, ema ? p->ema_scratch : nullptr, st, events(AP_KERNEL_ATTN));
+    if (e == hipSuccess)
+      e = launch_combine(c, q, out, sl2, S, p->n_text, p->text_k, p->text_v, ema ? c->ml_final : nullptr,
+                         st, events(AP_KERNEL_COMBINE));
+    if (e == hipSuccess && ema)
+      e = launch_ema_update(c, p->ema_scratch, c->ml_final, p->importance, per_head, p->ema_first != 0,
+                            p->ema_alpha, st);
   }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (timed) tm.calls++;

@@ -57,7 +57,7 @@ template <class T, int NP, int HT>
 __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_attn(
     const T* __restrict__ Uk, const T* __restrict__ Uv, const float* __restrict__ qt,
     const uint32_t* __restrict__ mask, float* __restrict__ part_z, float* __restrict__ part_ml,
-    int N, int nblk, int CB, int S, int Hq, int r_lo, float sl2) {
+    float* __restrict__ ema_s, int N, int nblk, int CB, int S, int Hq, int r_lo, float sl2) {
   constexpr int RP = NP * 16, HP = HT * 16, ZS = RP + 1;
   constexpr bool BF = std::is_same<T, bf16_t>::value;
   extern __shared__ __align__(16) float smem_f[];
@@ -158,6 +158,14 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
           for (int j = 0; j < 8; ++j)
             if (blk * kBlockTok + 16 * (j >> 2) + 4 * lg + (j & 3) >= N) sc[j] = -INFINITY;
         }
+        if (ema_s != nullptr) {   // moving-average selector: this step's logits (log2 units)
+          const int h = 16 * ht + l16;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int n = blk * kBlockTok + 16 * (j >> 2) + 4 * lg + (j & 3);
+            if (h < Hq && n < N) ema_s[((size_t)b * Hq + h) * N + n] = sc[j];
+          }
+        }
         float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                          fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
         bm = column_max4(bm);
@@ -246,6 +254,14 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
   #pragma unroll
             for (int t = 0; t < 4; ++t)
               if (blk * kBlockTok + 16 * hf + 4 * lg + t >= N) sc[t] = -INFINITY;
+          }
+          if (ema_s != nullptr) {   // moving-average selector: this step's logits (log2 units)
+            const int h = 16 * ht + l16;
+  #pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int n = blk * kBlockTok + 16 * hf + 4 * lg + t;
+              if (h < Hq && n < N) ema_s[((size_t)b * Hq + h) * N + n] = sc[t];
+            }
           }
           float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
           bm = wave_max_xor(bm, 16);
@@ -365,7 +381,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
     const float* __restrict__ part_z, const float* __restrict__ part_ml, const T* __restrict__ Bv,
     const float* __restrict__ q, float* __restrict__ out, const T* __restrict__ text_k,
     const T* __restrict__ text_v, int S, int Hq, int HP, int RP, int W, int d, int G, int Tn,
-    float sl2) {
+    float sl2, float* __restrict__ ml_out) {
   constexpr int V = Vec16<T>::n;
   constexpr int U = 8;                   // rows per thread with loads in flight
   extern __shared__ __align__(16) float smem_c[];
@@ -494,6 +510,10 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
   for (int e = 0; e < V; ++e) accb[rg * d + seg * V + e] = acc[e];
   __syncthreads();
   const float invL = 1.f / L;
+  if (ml_out != nullptr && tid == 0) {   // softmax max (log2 units) and sum, for the selector state
+    ml_out[((size_t)b * Hq + h) * 2] = M;
+    ml_out[((size_t)b * Hq + h) * 2 + 1] = L;
+  }
   for (int j = tid; j < d; j += kCombThreads) {
     float o = 0.f;
     for (int r = 0; r < RPP; ++r) o += accb[r * d + j];
@@ -507,7 +527,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
     const float* __restrict__ part_z, const float* __restrict__ part_ml, const T* __restrict__ Bv,
     const float* __restrict__ q, float* __restrict__ out, const T* __restrict__ text_k,
     const T* __restrict__ text_v, int S, int Hq, int HP, int RP, int W, int d, int G, int Tn,
-    float sl2) {
+    float sl2, float* __restrict__ ml_out) {
   extern __shared__ __align__(16) float smem_c[];
   float* qh = smem_c;
   float* zz = qh + d;
@@ -570,6 +590,10 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
   }
   __syncthreads();
   const float invL = 1.f / L;
+  if (ml_out != nullptr && tid == 0) {
+    ml_out[((size_t)b * Hq + h) * 2] = M;
+    ml_out[((size_t)b * Hq + h) * 2 + 1] = L;
+  }
   for (int jj = 0; jj < kMaxJ; ++jj) {
     const int j = tid + kCombThreads * jj;
     if (j < d) {
@@ -583,7 +607,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
 
 // ================================================================ launchers
 template <class T, int NP, int HT>
-static hipError_t launch_attn_t(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st,
+static hipError_t launch_attn_t(const ap_cache* c, int r_lo, float sl2, int S, int CB, float* ema_s, hipStream_t st,
                                 const KernelEvents& ev) {
   const Dims& dm = c->dm;
   constexpr int RP = NP * 16, HP = HT * 16;
@@ -597,26 +621,26 @@ static hipError_t launch_attn_t(const ap_cache* c, int r_lo, float sl2, int S, i
   }
   hipExtLaunchKernelGGL((k_attn<T, NP, HT>), dim3(dm.B * S), dim3(256), lds, st, ev.start, ev.stop, 0,
                      static_cast<const T*>(c->Uk), static_cast<const T*>(c->Uv), c->qt, c->mask,
-                     c->part_z, c->part_ml, dm.N, dm.nblk, CB, S, dm.Hq, r_lo, sl2);
+                     c->part_z, c->part_ml, ema_s, dm.N, dm.nblk, CB, S, dm.Hq, r_lo, sl2);
   return hipGetLastError();
 }
 
 template <class T, int HT>
-static hipError_t dispatch_np(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st,
+static hipError_t dispatch_np(const ap_cache* c, int r_lo, float sl2, int S, int CB, float* ema_s, hipStream_t st,
                               const KernelEvents& ev) {
   switch (c->dm.NP) {
-    case 1: return launch_attn_t<T, 1, HT>(c, r_lo, sl2, S, CB, st, ev);
-    case 2: return launch_attn_t<T, 2, HT>(c, r_lo, sl2, S, CB, st, ev);
-    case 3: return launch_attn_t<T, 3, HT>(c, r_lo, sl2, S, CB, st, ev);
-    case 4: return launch_attn_t<T, 4, HT>(c, r_lo, sl2, S, CB, st, ev);
+    case 1: return launch_attn_t<T, 1, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+    case 2: return launch_attn_t<T, 2, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+    case 3: return launch_attn_t<T, 3, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+    case 4: return launch_attn_t<T, 4, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
     default: break;
   }
   if constexpr (HT <= 2) {
     switch (c->dm.NP) {
-      case 5: return launch_attn_t<T, 5, HT>(c, r_lo, sl2, S, CB, st, ev);
-      case 6: return launch_attn_t<T, 6, HT>(c, r_lo, sl2, S, CB, st, ev);
-      case 7: return launch_attn_t<T, 7, HT>(c, r_lo, sl2, S, CB, st, ev);
-      case 8: return launch_attn_t<T, 8, HT>(c, r_lo, sl2, S, CB, st, ev);
+      case 5: return launch_attn_t<T, 5, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+      case 6: return launch_attn_t<T, 6, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+      case 7: return launch_attn_t<T, 7, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+      case 8: return launch_attn_t<T, 8, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
       default: break;
     }
   }
@@ -624,26 +648,26 @@ static hipError_t dispatch_np(const ap_cache* c, int r_lo, float sl2, int S, int
 }
 
 template <class T>
-static hipError_t dispatch_ht(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st,
+static hipError_t dispatch_ht(const ap_cache* c, int r_lo, float sl2, int S, int CB, float* ema_s, hipStream_t st,
                               const KernelEvents& ev) {
   switch (c->dm.HT) {
-    case 1: return dispatch_np<T, 1>(c, r_lo, sl2, S, CB, st, ev);
-    case 2: return dispatch_np<T, 2>(c, r_lo, sl2, S, CB, st, ev);
-    case 4: return dispatch_np<T, 4>(c, r_lo, sl2, S, CB, st, ev);
+    case 1: return dispatch_np<T, 1>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+    case 2: return dispatch_np<T, 2>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+    case 4: return dispatch_np<T, 4>(c, r_lo, sl2, S, CB, ema_s, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_attn(const ap_cache* c, int r_lo, float sl2, int S, int CB, hipStream_t st,
+hipError_t launch_attn(const ap_cache* c, int r_lo, float sl2, int S, int CB, float* ema_s, hipStream_t st,
                        const KernelEvents& ev) {
-  if (c->dm.storage == AP_BF16) return dispatch_ht<bf16_t>(c, r_lo, sl2, S, CB, st, ev);
-  return dispatch_ht<float>(c, r_lo, sl2, S, CB, st, ev);
+  if (c->dm.storage == AP_BF16) return dispatch_ht<bf16_t>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+  return dispatch_ht<float>(c, r_lo, sl2, S, CB, ema_s, st, ev);
 }
 
 template <class T>
 static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out, float sl2, int S,
-                                   int Tn, const void* tk, const void* tv, hipStream_t st,
-                                   const KernelEvents& ev) {
+                                   int Tn, const void* tk, const void* tv, float* ml_out,
+                                   hipStream_t st, const KernelEvents& ev) {
   const Dims& dm = c->dm;
   constexpr int V = 16 / sizeof(T);
   const int lpr = dm.d / V;
@@ -657,22 +681,62 @@ static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out
                           ev.stop, 0, c->part_z,
                        c->part_ml, static_cast<const T*>(c->Bv), q, out, static_cast<const T*>(tk),
                        static_cast<const T*>(tv), S, dm.Hq, dm.Hq_pad, dm.r_pad, dm.W, dm.d, dm.G, Tn,
-                       sl2);
+                       sl2, ml_out);
   } else {
     const size_t lds = (size_t)(dm.d + dm.r_pad + kCombThreads + 4) * sizeof(float);
     hipExtLaunchKernelGGL(k_combine_scalar<T>, dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st,
                           ev.start, ev.stop, 0,
                        c->part_z, c->part_ml, static_cast<const T*>(c->Bv), q, out,
                        static_cast<const T*>(tk), static_cast<const T*>(tv), S, dm.Hq, dm.Hq_pad,
-                       dm.r_pad, dm.W, dm.d, dm.G, Tn, sl2);
+                       dm.r_pad, dm.W, dm.d, dm.G, Tn, sl2, ml_out);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float sl2, int S, int Tn,
-                          const void* tk, const void* tv, hipStream_t st, const KernelEvents& ev) {
-  if (c->dm.storage == AP_BF16) return launch_combine_t<bf16_t>(c, q, out, sl2, S, Tn, tk, tv, st, ev);
-  return launch_combine_t<float>(c, q, out, sl2, S, Tn, tk, tv, st, ev);
+                          const void* tk, const void* tv, float* ml_out, hipStream_t st,
+                          const KernelEvents& ev) {
+  if (c->dm.storage == AP_BF16) return launch_combine_t<bf16_t>(c, q, out, sl2, S, Tn, tk, tv, ml_out, st, ev);
+  return launch_combine_t<float>(c, q, out, sl2, S, Tn, tk, tv, ml_out, st, ev);
+}
+
+// ================================================================ k_ema_update
+// Moving-average importance after a step ([fr §2.B "Score d'importance"]): the weight
+// of visual token n for head h is p = exp2(s - M_h) / L_h, with s the step's logit
+// (log2 units, written by k_attn) and (M_h, L_h) the softmax maximum and sum over
+// text and visual tokens (written by k_combine).  Per head: I[b][h][n] <- a I + (1-a) p;
+// per token: I[b][n] <- a I + (1-a) mean_h p (heads summed in a fixed order).  first:
+// no history yet, I <- p.
+__global__ __launch_bounds__(256) void k_ema_update(const float* __restrict__ s,
+                                                    const float* __restrict__ ml,
+                                                    float* __restrict__ imp, int B, int Hq, int N,
+                                                    int per_head, int first, float alpha) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (per_head) {
+    if (idx >= (size_t)B * Hq * N) return;
+    const size_t bh = idx / N;
+    const float p = exp2f(s[idx] - ml[bh * 2]) / ml[bh * 2 + 1];
+    imp[idx] = first ? p : fmaf(alpha, imp[idx], (1.f - alpha) * p);
+  } else {
+    if (idx >= (size_t)B * N) return;
+    const size_t b = idx / N, n = idx - b * N;
+    float acc = 0.f;
+    for (int h = 0; h < Hq; ++h) {
+      const size_t bh = b * Hq + h;
+      acc += exp2f(s[bh * N + n] - ml[bh * 2]) / ml[bh * 2 + 1];
+    }
+    const float p = acc / static_cast<float>(Hq);
+    imp[idx] = first ? p : fmaf(alpha, imp[idx], (1.f - alpha) * p);
+  }
+}
+
+hipError_t launch_ema_update(const ap_cache* c, const float* s, const float* ml, float* imp,
+                             bool per_head, bool first, float alpha, hipStream_t st) {
+  const Dims& dm = c->dm;
+  const size_t n = (size_t)dm.B * (per_head ? dm.Hq : 1) * dm.N;
+  hipLaunchKernelGGL(k_ema_update, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, ml, imp,
+                     dm.B, dm.Hq, dm.N, per_head ? 1 : 0, first ? 1 : 0, alpha);
+  return hipGetLastError();
 }
 
 }  // namespace ap

@@ -285,6 +285,10 @@ struct FusedArgs {
   float* out;           // [B][Hq][d]
   int Tn;
   float sl2;            // softmax scale in log2 units
+  // selection-only kernel: rank by these keys (the moving-average importance) instead
+  // of the low-rank logits; [B][Hq][N] when keys_per_head, else [B][N] shared by heads
+  const float* keys;
+  int keys_per_head;
 };
 
 // HG: query heads per workgroup (4 or 1); NPL: low panels (1 or 2 with the tiles of
@@ -468,7 +472,18 @@ __device__ __forceinline__ void select_body(
   float sc[KPL];
   // token of score 4a+t: 32 * (block of step a) + 16 * my_j + 4 * lg + t
   auto tok = [&](int a) { return 32 * ((wave + nwv * a) * NSL + my_slot) + 16 * my_j + 4 * lg; };
-  if (select || FUSED) {
+  if (!FUSED && fa.keys != nullptr) {
+    // moving-average selector: the keys are the importance state, read from memory
+    if (select) {
+      const size_t kb = fa.keys_per_head ? ((size_t)b * Hq + h0 + (my_on ? my_h : 0)) * N : (size_t)b * N;
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) {
+        const int n0 = tok(a);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sc[4 * a + t] = (my_on && n0 + t < N) ? fa.keys[kb + n0 + t] : 0.f;
+      }
+    }
+  } else if (select || FUSED) {
     constexpr int NQ = NPL <= 2 ? NPL : 1;
     SelQ<T> qop[NQ];
 #pragma unroll
@@ -1111,9 +1126,12 @@ static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, i
 
 template <class T>
 static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, int top_k,
-                                  int32_t* sel_out, hipStream_t st, const KernelEvents& ev) {
+                                  int32_t* sel_out, const float* keys, bool keys_per_head,
+                                  hipStream_t st, const KernelEvents& ev) {
   const SelPlan pl = select_plan(c->dm, r_lo);
-  const FusedArgs fa{};
+  FusedArgs fa{};
+  fa.keys = keys;
+  fa.keys_per_head = keys_per_head ? 1 : 0;
 #define AP_SEL(HGV, NPLV, NACCV)                                                        \
   if (pl.HG == HGV && pl.NPL == NPLV && pl.NACC == NACCV)                               \
     return launch_select_v<T, HGV, NPLV, NACCV, false>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
@@ -1131,9 +1149,10 @@ static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, i
 }
 
 hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k, int32_t* sel_out,
-                         hipStream_t st, const KernelEvents& ev) {
-  if (c->dm.storage == AP_BF16) return launch_select_t<bf16_t>(c, q, r_lo, top_k, sel_out, st, ev);
-  return launch_select_t<float>(c, q, r_lo, top_k, sel_out, st, ev);
+                         const float* keys, bool keys_per_head, hipStream_t st, const KernelEvents& ev) {
+  if (c->dm.storage == AP_BF16)
+    return launch_select_t<bf16_t>(c, q, r_lo, top_k, sel_out, keys, keys_per_head, st, ev);
+  return launch_select_t<float>(c, q, r_lo, top_k, sel_out, keys, keys_per_head, st, ev);
 }
 
 bool decode_fused_supported(const Dims& dm, int r_lo, int n_text) {
@@ -1162,6 +1181,8 @@ hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, in
   fa.out = out;
   fa.Tn = n_text;
   fa.sl2 = sl2;
+  fa.keys = nullptr;
+  fa.keys_per_head = 0;
 #define AP_FUS(NPLV, NACCV)                                                             \
   if (pl.NPL == NPLV && pl.NACC == NACCV)                                               \
     return launch_select_v<bf16_t, 4, NPLV, NACCV, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);

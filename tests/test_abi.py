@@ -23,12 +23,29 @@ def test_library_exports_every_declared_symbol():
     assert set(syms) == set(binding.EXPORTED)
 
 
-def test_struct_layouts_match_header():
+def test_struct_layouts_match_header(tmp_path):
+    """Every field offset and struct size of the binding's ctypes mirrors equals what a
+    C compiler computes from include/ap.h."""
+    import subprocess
     from rank_compressed_kv_ap_amd import binding
-    assert ctypes.sizeof(binding.CompressParams) == 56
-    assert binding.CompressParams.seed.offset == 40 and binding.CompressParams.omega.offset == 48
-    assert ctypes.sizeof(binding.DecodeParams) == 48
-    assert binding.DecodeParams.text_k.offset == 16 and binding.DecodeParams.splits.offset == 40
+    structs = {"ap_compress_params": binding.CompressParams, "ap_decode_params": binding.DecodeParams}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ap.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got[f"{cname} size"]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got[f"{cname} {f}"]) == getattr(py, f).offset, (cname, f)
 
 
 def _compress_status(**kw):
