@@ -62,8 +62,11 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_bytes(w):
-    """Algorithmic bytes per sequence read/written by each decode kernel."""
+def kernel_bytes(w, select="logit"):
+    """Algorithmic bytes per sequence read/written by each decode kernel.  With a
+    moving-average selector the importance state (fp32, per token or per (head, token))
+    is read by the selection and read + written by the update; the per-step logits the
+    update consumes are an intermediate and are not counted."""
     s = 2 if w.storage == "bf16" else 4
     W, r, N, T = w.width, w.rank, w.n_tokens, w.n_text
     qb = 4 * w.n_q_heads * w.head_dim
@@ -72,7 +75,11 @@ def kernel_bytes(w):
         "attn": s * 2 * N * r,                    # U_k, U_v
         "combine": s * r * W + s * 2 * T * W + qb,  # B_v, text K/V, out
     }
-    k["decode"] = k["select"] + k["attn"] + k["combine"]   # the single-kernel path reads all of it
+    if select != "logit":
+        state = 4 * N * (w.n_q_heads if select == "ema_head" else 1)
+        k["select"] += state
+        k["ema"] = 2 * state
+    k["decode"] = sum(k.values())   # every byte of the step, whichever path runs
     return k
 
 
@@ -188,7 +195,7 @@ def main():
     def stack(key, dtype):
         return torch.from_numpy(np.stack([seqs[b % S][key] for b in range(B)])).to(dtype).to(dev)
 
-    kb = kernel_bytes(w)
+    kb = kernel_bytes(w, args.select)
     step_bytes = B * kb["decode"]   # every byte of one step, whichever path runs
     R = max(1, math.ceil(2 * MALL_BYTES / step_bytes))
     caches, qs, texts = [], [], []

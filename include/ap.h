@@ -209,10 +209,10 @@ void ap_free(ap_cache* c);
  * around each of its kernels on the caller's stream (at most max_calls calls are
  * recorded; later calls are not timed).  ap_timing_read waits for the recorded events,
  * writes the summed milliseconds per kernel (index: 0 select, 1 attention, 2 combine,
- * 3 the single-kernel decode) and the number of timed calls, and starts a new recording.
- * max_calls == 0 disables. */
+ * 3 the single-kernel decode, 4 the importance-state update) and the number of timed
+ * calls, and starts a new recording.  max_calls == 0 disables. */
 enum { AP_KERNEL_SELECT = 0, AP_KERNEL_ATTN = 1, AP_KERNEL_COMBINE = 2, AP_KERNEL_DECODE = 3,
-       AP_N_KERNELS = 4 };
+       AP_KERNEL_EMA = 4, AP_N_KERNELS = 5 };
 ap_status ap_timing_enable(ap_cache* c, int32_t max_calls);
 ap_status ap_timing_read(ap_cache* c, float* ms_per_kernel /* [AP_N_KERNELS] */, int32_t* calls);
 

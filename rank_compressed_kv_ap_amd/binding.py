@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libap.so")
 AP_OK, AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_BAD_DTYPE, AP_ERR_UNSUPPORTED, \
     AP_ERR_OUT_OF_MEMORY, AP_ERR_HIP = range(7)
 AP_F32, AP_BF16 = 0, 1
-KERNEL_NAMES = ("select", "attn", "combine", "decode")
+KERNEL_NAMES = ("select", "attn", "combine", "decode", "ema")
 
 EXPORTED = (
     "ap_compress", "ap_recompress", "ap_cache_set_factors", "ap_cache_get_factors",

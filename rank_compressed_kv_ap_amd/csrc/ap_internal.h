@@ -86,7 +86,8 @@ hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float s
                           int S, int T, const void* text_k, const void* text_v, float* ml_out,
                           hipStream_t st, const KernelEvents& ev);
 hipError_t launch_ema_update(const ap_cache* c, const float* s, const float* ml, float* imp,
-                             bool per_head, bool first, float alpha, hipStream_t st);
+                             bool per_head, bool first, float alpha, hipStream_t st,
+                             const KernelEvents& ev);
 
 // ---- launchers (pack_kernels.hip)
 hipError_t launch_pack_u(const ap_cache* c, const void* src, void* dst, bool v_layout,

@@ -341,7 +341,7 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
                          st, events(AP_KERNEL_COMBINE));
     if (e == hipSuccess && ema)
       e = launch_ema_update(c, p->ema_scratch, c->ml_final, p->importance, per_head, p->ema_first != 0,
-                            p->ema_alpha, st);
+                            p->ema_alpha, st, events(AP_KERNEL_EMA));
   }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (timed) tm.calls++;

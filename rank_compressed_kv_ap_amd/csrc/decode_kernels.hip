@@ -707,35 +707,48 @@ hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float s
 // text and visual tokens (written by k_combine).  Per head: I[b][h][n] <- a I + (1-a) p;
 // per token: I[b][n] <- a I + (1-a) mean_h p (heads summed in a fixed order).  first:
 // no history yet, I <- p.
+// One thread per token; blockIdx.y is the state row (b * Hq + h per head, b per token), so
+// the softmax statistics are uniform per workgroup.  Per token, the heads' logits are
+// independent loads issued together, then summed in head order.
 __global__ __launch_bounds__(256) void k_ema_update(const float* __restrict__ s,
                                                     const float* __restrict__ ml,
-                                                    float* __restrict__ imp, int B, int Hq, int N,
-                                                    int per_head, int first, float alpha) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (per_head) {
-    if (idx >= (size_t)B * Hq * N) return;
-    const size_t bh = idx / N;
-    const float p = exp2f(s[idx] - ml[bh * 2]) / ml[bh * 2 + 1];
-    imp[idx] = first ? p : fmaf(alpha, imp[idx], (1.f - alpha) * p);
-  } else {
-    if (idx >= (size_t)B * N) return;
-    const size_t b = idx / N, n = idx - b * N;
-    float acc = 0.f;
-    for (int h = 0; h < Hq; ++h) {
-      const size_t bh = b * Hq + h;
-      acc += exp2f(s[bh * N + n] - ml[bh * 2]) / ml[bh * 2 + 1];
+                                                    float* __restrict__ imp, int Hq, int N,
+                                                    int rows, int per_head, int first,
+                                                    float alpha) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  for (size_t row = blockIdx.y; row < (size_t)rows; row += gridDim.y) {
+    float p;
+    if (per_head) {
+      p = exp2f(s[row * N + n] - ml[row * 2]) / ml[row * 2 + 1];
+    } else {
+      const float* sb = s + row * Hq * N + n;
+      const float* mb = ml + row * Hq * 2;
+      float acc = 0.f;
+      int h = 0;
+      for (; h + 8 <= Hq; h += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = sb[(size_t)(h + j) * N];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += exp2f(v[j] - mb[2 * (h + j)]) / mb[2 * (h + j) + 1];
+      }
+      for (; h < Hq; ++h) acc += exp2f(sb[(size_t)h * N] - mb[2 * h]) / mb[2 * h + 1];
+      p = acc / static_cast<float>(Hq);
     }
-    const float p = acc / static_cast<float>(Hq);
+    const size_t idx = row * N + n;
     imp[idx] = first ? p : fmaf(alpha, imp[idx], (1.f - alpha) * p);
   }
 }
 
 hipError_t launch_ema_update(const ap_cache* c, const float* s, const float* ml, float* imp,
-                             bool per_head, bool first, float alpha, hipStream_t st) {
+                             bool per_head, bool first, float alpha, hipStream_t st,
+                             const KernelEvents& ev) {
   const Dims& dm = c->dm;
-  const size_t n = (size_t)dm.B * (per_head ? dm.Hq : 1) * dm.N;
-  hipLaunchKernelGGL(k_ema_update, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, ml, imp,
-                     dm.B, dm.Hq, dm.N, per_head ? 1 : 0, first ? 1 : 0, alpha);
+  const int rows = dm.B * (per_head ? dm.Hq : 1);
+  hipExtLaunchKernelGGL(k_ema_update, dim3((unsigned)((dm.N + 255) / 256), (unsigned)std::min(rows, 65535)),
+                        dim3(256), 0, st, ev.start, ev.stop, 0, s, ml, imp, dm.Hq, dm.N, rows,
+                        per_head ? 1 : 0, first ? 1 : 0, alpha);
   return hipGetLastError();
 }
 
