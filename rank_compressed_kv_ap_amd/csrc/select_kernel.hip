@@ -367,7 +367,7 @@ __device__ __forceinline__ void select_body(
     }
   };
   if (vec) load_rows(wave * RPW + rw);
-  // one q value per thread (HG * d <= 1024 threads); stored unconditionally below so the
+  // one q value per thread (HG * d <= threads, checked at launch); stored unconditionally so the
   // load is never sunk behind the tile loads
   const int nq = nh * d;
   const float qv = q[((size_t)b * Hq + h0) * d + min(tid, nq - 1)];
@@ -1075,7 +1075,7 @@ struct SelPlan {
   int HG, NPL, NACC, waves;
 };
 
-static SelPlan select_plan(const Dims& dm, int r_lo) {
+static SelPlan select_plan(const Dims& dm, int r_lo, bool single_kernel) {
   const int nplo = (r_lo + 15) / 16;
   SelPlan pl;
   // 16 wavefronts; four heads per workgroup while 8 steps per wavefront cover the
@@ -1085,9 +1085,15 @@ static SelPlan select_plan(const Dims& dm, int r_lo) {
   pl.HG = (nplo <= 2 && g4 <= kSelMaxWaves * 8) ? 4 : 1;
   pl.NPL = pl.HG == 1 ? 8 : (nplo <= 1 ? 1 : 2);
   const int ngrp = (dm.nblk + 8 / pl.HG - 1) / (8 / pl.HG);
-  const int per = (ngrp + kSelMaxWaves - 1) / kSelMaxWaves;
-  pl.NACC = pl.HG == 1 ? 8 : (per <= 2 ? 2 : (per <= 3 ? 3 : (per <= 4 ? 4 : 8)));
   pl.waves = kSelMaxWaves;
+  // More workgroups than CUs (selection alone): 8 wavefronts, so two workgroups share a
+  // CU and one's loads overlap the other's selection (the batch-256 layer: 108 -> 77 us).
+  // Needs 8 steps per wavefront to cover the tokens and one q value per thread.
+  const size_t wgs = (size_t)dm.B * ((dm.Hq + pl.HG - 1) / pl.HG);
+  if (!single_kernel && pl.HG == 4 && wgs > 256 && ngrp <= 8 * 8 && 4 * dm.d <= 8 * 64)
+    pl.waves = 8;
+  const int per = (ngrp + pl.waves - 1) / pl.waves;
+  pl.NACC = pl.HG == 1 ? 8 : (per <= 2 ? 2 : (per <= 3 ? 3 : (per <= 4 ? 4 : 8)));
   return pl;
 }
 
@@ -1100,6 +1106,7 @@ static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, i
   const size_t lds = sel_layout(HG, dm.nblk, dm.r_pad, dm.d, FUSED, FUSED ? fa.Tn : 0).total;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   if ((dm.nblk + 8 / HG - 1) / (8 / HG) > waves * NACC) return hipErrorInvalidValue;
+  if (HG * dm.d > 64 * waves) return hipErrorInvalidValue;
   const void* fn;
   if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<NPL, NACC>);
   else fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC>);
@@ -1128,7 +1135,7 @@ template <class T>
 static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, int top_k,
                                   int32_t* sel_out, const float* keys, bool keys_per_head,
                                   hipStream_t st, const KernelEvents& ev) {
-  const SelPlan pl = select_plan(c->dm, r_lo);
+  const SelPlan pl = select_plan(c->dm, r_lo, false);
   FusedArgs fa{};
   fa.keys = keys;
   fa.keys_per_head = keys_per_head ? 1 : 0;
@@ -1157,7 +1164,7 @@ hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
 
 bool decode_fused_supported(const Dims& dm, int r_lo, int n_text) {
   if (dm.storage != AP_BF16 || dm.NP > 4 || n_text > 1024) return false;
-  const SelPlan pl = select_plan(dm, r_lo);
+  const SelPlan pl = select_plan(dm, r_lo, true);
   if (pl.HG != 4) return false;
   // each workgroup re-reads its sequence's U_k / U_v from L2 and runs one long chain:
   // worth it while the workgroups fit the GPU at one per CU (256 CUs); with more, the
@@ -1172,7 +1179,7 @@ bool decode_fused_supported(const Dims& dm, int r_lo, int n_text) {
 hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, int r_lo, int top_k,
                                int32_t* sel_out, int n_text, const void* text_k, const void* text_v,
                                float sl2, hipStream_t st, const KernelEvents& ev) {
-  const SelPlan pl = select_plan(c->dm, r_lo);
+  const SelPlan pl = select_plan(c->dm, r_lo, true);
   FusedArgs fa;
   fa.Uv = c->Uv;
   fa.Bv = c->Bv;

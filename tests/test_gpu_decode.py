@@ -150,6 +150,19 @@ def test_decode_path_taken(gpu_lib, name, splits, path):
         assert ms["decode"] == 0 and min(ms["select"], ms["attn"], ms["combine"]) > 0
 
 
+def test_decode_more_selection_workgroups_than_cus(gpu_lib):
+    """B * Hq / 4 > 256 workgroups: the selector runs 8 wavefronts per workgroup (two per
+    CU); ragged token tail, text, replicas bit-identical."""
+    w = wl.LLAVA.replace(cfg_id=107, batch=70, n_q_heads=16, n_kv_heads=16, head_dim=64,
+                         n_tokens=300, n_text=5, rank=32, r_lo=16, top_k=75, grid=None,
+                         inner_dim=300)
+    seqs = make_inputs(w, 2)
+    out, sel = run_decode(w, seqs, gpu_lib)
+    check_against_oracle(w, seqs, out, sel)
+    for b in range(2, w.batch):
+        assert np.array_equal(out[b], out[b % 2]) and np.array_equal(sel[b], sel[b % 2]), b
+
+
 @pytest.mark.parametrize("cfg,n_distinct,splits", [(2, 3, 0), (2, 3, 16), (3, 2, 0), (4, 2, 0),
                                                    (5, 2, 0)])
 def test_decode_parity_full_configs(gpu_lib, cfg, n_distinct, splits):

@@ -32,6 +32,10 @@ SHAPES = {
     "f32_gqa": wl.GQA.replace(cfg_id=122, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=32,
                               n_tokens=70, rank=40, r_lo=20, top_k=17, storage="f32", inner_dim=64),
     "llava7b_layer": wl.LLAVA,
+    # more selection workgroups than CUs: the 8-wavefront selector
+    "bf16_many_wgs": wl.LLAVA.replace(cfg_id=123, batch=70, n_q_heads=16, n_kv_heads=16,
+                                      head_dim=64, n_tokens=300, n_text=5, rank=32, r_lo=16,
+                                      top_k=75, grid=None, inner_dim=300),
 }
 def _weight_rtol(w, s, q):
     """Per-head relative error bound of the GPU's attention weights (see above)."""
@@ -122,6 +126,11 @@ def _run(gpu_lib, w, mode, alpha, steps, n_distinct=None, seed=5):
 @pytest.mark.parametrize("name,alpha", [("bf16_text", 0.8), ("f32_gqa", 0.5)])
 def test_ema_selector_steps(gpu_lib, name, mode, alpha):
     _run(gpu_lib, SHAPES[name], mode, alpha, steps=4)
+
+
+@pytest.mark.parametrize("mode", ["ema_token", "ema_head"])
+def test_ema_selector_many_workgroups(gpu_lib, mode):
+    _run(gpu_lib, SHAPES["bf16_many_wgs"], mode, 0.7, steps=3, n_distinct=2)
 
 
 def test_ema_alpha_zero_follows_last_weights(gpu_lib):
