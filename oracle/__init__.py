@@ -18,6 +18,7 @@ Modules
   decode      explicit mixed-rank decompression + softmax ([es §2.B] [fr §2.B] [de §2.B]),
               and the moving-average importance selector over several steps
   brute       the same decode in pure-Python loops        (tiny inputs only)
+  quant       4-bit token factors: codes and block scales  [es §3] [fr §4] [de §3] [de §4]
   accounting  storage / FLOP bookkeeping                  [fr §2.A] [es §4] [de §4]
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` to something
@@ -29,9 +30,10 @@ from .jacobi import jacobi_svd
 from .factorize import orth_mgs2, rsvd, round_to_storage
 from .decode import decode_ref, decode_ema_steps, select_top, band_mask, recon_error
 from .accounting import factored_bytes, dense_bytes, decompression_flop_fraction
+from .quant import quantize_u4, dequant_u4, quantize_dequant_u4
 
 __all__ = [
     "jacobi_svd", "orth_mgs2", "rsvd", "round_to_storage", "decode_ref", "decode_ema_steps",
     "select_top", "band_mask", "recon_error", "factored_bytes", "dense_bytes",
-    "decompression_flop_fraction",
+    "decompression_flop_fraction", "quantize_u4", "dequant_u4", "quantize_dequant_u4",
 ]

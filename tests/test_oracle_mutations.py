@@ -131,3 +131,41 @@ def test_mutated_ema_selector_is_caught(old, new):
     agree = all(np.max(np.abs(states[t] - np.array(bstates[t]))) <= 1e-12 and
                 [list(x) for x in res[t]["top"]] == tops[t] for t in range(len(qs)))
     assert not agree, "the planted mistake went unnoticed"
+
+
+# ---------------------------------------------------------------- 4-bit factors
+import oracle.quant as qnt
+
+
+def _quant_pins_ok(mod):
+    from test_oracle_pins import _quant_brute, _quant_case
+    try:
+        for seed in (70, 71):
+            U = _quant_case(seed)
+            codes, scales = mod.quantize_u4(U)
+            bc, bs = _quant_brute(U.astype(np.float64).tolist())
+            if codes.tolist() != bc or scales.astype(np.float64).tolist() != bs:
+                return False
+            dq = mod.dequant_u4(codes, scales)
+            s = np.repeat(np.asarray(bs), 32, axis=0)[:U.shape[0]]
+            if not np.all(np.abs(U.astype(np.float64) - dq) <= s / 2):
+                return False
+    except Exception:
+        return False
+    return True
+
+
+def test_real_quantizer_passes_pins():
+    assert _quant_pins_ok(qnt)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("np.rint(t)", "np.sign(t) * np.floor(np.abs(t) + 0.5)"),           # ties away from zero
+    ("m = np.max(np.abs(rows), axis=0)", "m = np.max(np.abs(U32), axis=0)"),  # one scale per column
+    ("inv7 = np.float32(1.0) / np.float32(QMAX)", "inv7 = np.float32(1.0) / np.float32(QMAX + 1)"),
+    ("s = _bf16_rne(m * inv7)", "s = m * inv7"),                         # scale not rounded to bf16
+    ("np.repeat(np.asarray(scales, np.float64), BLOCK, axis=0)[:N]",
+     "np.repeat(np.asarray(scales, np.float64), BLOCK, axis=0)[1:N + 1]"),  # dequant off by a token
+])
+def test_quantizer_mutants_are_caught(old, new):
+    assert not _quant_pins_ok(_mutant(qnt, old, new))

@@ -414,3 +414,106 @@ def test_p13_ema_first_step_is_the_logit_selector():
     res, _ = decode_ema_steps(Uk, Bk, Uv, Bv, qs[:1], 2, 3, 2, 3, 0.8, 0.5, False, Kt, Vt)
     ref = decode_ref(Uk, Bk, Uv, Bv, qs[0], 2, 3, 2, 3, 0.8, Kt, Vt)
     assert np.array_equal(res[0]["out"], ref["out"]) and np.array_equal(res[0]["top"], ref["top"])
+
+
+# ------------------------------------------------------------------ P14
+# 4-bit token factors (oracle.quant), against an exact-rational brute force written from
+# the definition: the float32 product rounded once (a product of two float32 values is
+# exact in a Python float), bf16 chosen as the nearer of the two neighbouring bf16 values
+# (ties to an even last bit), codes by Fraction rounding (ties to even).
+import struct
+from fractions import Fraction
+
+from oracle.quant import dequant_u4, quantize_u4
+
+
+def _f32(x: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def _bf16_nearest(x: float) -> float:
+    bits = struct.unpack("<I", struct.pack("<f", x))[0]
+    down = struct.unpack("<f", struct.pack("<I", bits & 0xFFFF0000))[0]
+    up = struct.unpack("<f", struct.pack("<I", (bits & 0xFFFF0000) + 0x10000))[0]
+    dd, du = abs(Fraction(x) - Fraction(down)), abs(Fraction(up) - Fraction(x))
+    if dd != du:
+        return down if dd < du else up
+    return down if ((bits >> 16) & 1) == 0 else up
+
+
+def _quant_brute(U):
+    N, r = len(U), len(U[0])
+    inv7 = _f32(1.0 / 7.0)
+    codes = [[0] * r for _ in range(N)]
+    scales = []
+    for j0 in range(0, N, 32):
+        row_s = []
+        for c in range(r):
+            m = max(abs(U[n][c]) for n in range(j0, min(N, j0 + 32)))
+            s = _bf16_nearest(_f32(m * inv7))
+            row_s.append(s)
+            for n in range(j0, min(N, j0 + 32)):
+                codes[n][c] = 0 if s == 0 else max(-7, min(7, round(Fraction(U[n][c]) / Fraction(s))))
+        scales.append(row_s)
+    return codes, scales
+
+
+def _quant_case(seed, N=70, r=5):
+    g = np.random.default_rng(seed)
+    U = (g.standard_normal((N, r)) * np.array([3.0, 1.0, 0.3, 0.05, 1e-3])[:r]).astype(np.float32)
+    # planted ties: block 1, column 1 has maximum 7 (scale exactly 1) and values on midpoints
+    U[32:37, 1] = [7.0, 0.5, 1.5, 2.5, -2.5]
+    U[37:64, 1] = np.clip(U[37:64, 1], -3.0, 3.0)
+    U[40, 1] = -3.5
+    if r > 4:
+        U[:, 4] = 0.0                       # an all-zero column
+    return U
+
+
+@pytest.mark.parametrize("seed", [70, 71])
+def test_p14_quant_matches_exact_brute_force(seed):
+    U = _quant_case(seed)
+    codes, scales = quantize_u4(U)
+    bc, bs = _quant_brute(U.astype(np.float64).tolist())
+    assert codes.tolist() == bc
+    assert scales.astype(np.float64).tolist() == bs
+    # the planted midpoints go to the even code
+    assert codes[33:37, 1].tolist() == [0, 2, 2, -2] and codes[40, 1] == -4 and scales[1, 1] == 1.0
+
+
+def test_p14_quant_error_bound_and_range():
+    U = _quant_case(72, N=200, r=5)
+    codes, scales = quantize_u4(U)
+    dq = dequant_u4(codes, scales)
+    s = np.repeat(scales.astype(np.float64), 32, axis=0)[:200]
+    assert np.all(np.abs(codes) <= 7)
+    assert np.all(np.abs(U.astype(np.float64) - dq) <= s / 2)
+    # the largest element of every non-zero (block, column) takes code +-7
+    for j in range(scales.shape[0]):
+        blk = np.abs(codes[32 * j:32 * j + 32]).max(axis=0)
+        assert np.all(blk[scales[j] > 0] == 7)
+    assert np.all(scales[:, 4] == 0) and np.all(codes[:, 4] == 0)
+
+
+def test_p14_quant_grid_values_are_fixed_points():
+    U = _quant_case(73, N=100, r=4)
+    codes, scales = quantize_u4(U)
+    c2, s2 = quantize_u4(dequant_u4(codes, scales).astype(np.float32))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+
+
+def test_p14_quant_scales_are_per_block_and_column():
+    U = _quant_case(74, N=96, r=4)
+    codes, scales = quantize_u4(U)
+    # a power of two on one column scales only that column's scales; codes unchanged
+    U2 = U.copy()
+    U2[:, 2] *= np.float32(8.0)
+    c2, s2 = quantize_u4(U2)
+    assert np.array_equal(c2, codes)
+    assert np.array_equal(s2[:, 2], scales[:, 2] * 8) and np.array_equal(np.delete(s2, 2, 1), np.delete(scales, 2, 1))
+    # an outlier in token 31 changes block 0 only
+    U3 = U.copy()
+    U3[31, 0] = 1e3
+    c3, s3 = quantize_u4(U3)
+    assert s3[0, 0] != scales[0, 0] and np.array_equal(s3[1:], scales[1:])
+    assert np.array_equal(c3[32:], codes[32:])
