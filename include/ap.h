@@ -38,7 +38,16 @@ typedef enum {
   AP_ERR_HIP = 6             /* a HIP runtime call failed                            */
 } ap_status;
 
-typedef enum { AP_F32 = 0, AP_BF16 = 1 } ap_dtype;
+/* Storage of a cache.  AP_F32, AP_BF16: K, V in and U, B stored in that type.
+ * AP_INT4: 4-bit token factors.  [es §3 "Integración Modular"], [fr §4 "Compatibilité"],
+ * [de §3 "Kombinierbarkeit"]: the method composes with 4-bit quantization of the cache;
+ * [fr §1 "Limites des solutions existantes"]: plain quantization struggles with
+ * outliers.  The pages fix no format; here K, V come in as bf16, B is stored bf16 and
+ * U as symmetric codes in [-7, 7] with one bf16 scale per (32-token block, column):
+ * scale = bf16_rne(fp32(max |x|) * fp32(1/7)) over the block's tokens of that column,
+ * code = x / scale rounded to nearest with ties to even (0 when the scale is 0), and
+ * the stored value is code * scale.  Decoding attends over exactly those values. */
+typedef enum { AP_F32 = 0, AP_BF16 = 1, AP_INT4 = 2 } ap_dtype;
 
 /* Shape of one attention layer's visual cache and how it is factored.
  *
@@ -58,7 +67,8 @@ typedef struct {
   int32_t rank;         /* r, 1 <= r <= min(128, N, W)                                   */
   int32_t oversample;   /* p >= 0; the range finder keeps ell = min(r + p, N, W) columns */
   int32_t power_iters;  /* q, 0 <= q <= 8 power iterations                               */
-  int32_t storage;      /* ap_dtype of K, V in and of U, B stored                        */
+  int32_t storage;      /* ap_dtype of K, V in and of U, B stored (AP_INT4: K, V and B
+                           bf16, U 4-bit)                                                */
   int32_t reserved;     /* must be 0                                                     */
   uint64_t seed;        /* omega == NULL: the test matrix of matrix m (2b: K, 2b+1: V) has
                            entry (w, j) = -1 if bit i%32 of word (i/32)%4 of
@@ -116,12 +126,15 @@ ap_status ap_recompress(ap_cache* c, const void* k, const void* v, const float* 
 /* Load factors into a cache: U_k, U_v device [B][N][r], B_k, B_v device [B][r][W],
  * row-major, in the cache's storage dtype, caller-owned, read on `stream`.  The
  * layout is the plain one of [fr §2.A "Mécanisme"] (K ~= U_k B_k); the cache keeps
- * its own tiled copy.  Errors: AP_ERR_NULL_ARG, AP_ERR_HIP. */
+ * its own tiled copy.  AP_INT4 caches take U as float32 and quantize it on the device
+ * (the codes and scales defined at ap_dtype), and B as bf16.
+ * Errors: AP_ERR_NULL_ARG, AP_ERR_HIP. */
 ap_status ap_cache_set_factors(ap_cache* c, const void* U_k, const void* B_k,
                                const void* U_v, const void* B_v, void* stream);
 
 /* Copy the factors out in the same plain layout as ap_cache_set_factors (any of the
- * four pointers may be NULL to skip it).  sigma_k / sigma_v variants: see below. */
+ * four pointers may be NULL to skip it).  AP_INT4 caches give U as float32, the stored
+ * values code * scale.  sigma_k / sigma_v variants: see below. */
 ap_status ap_cache_get_factors(const ap_cache* c, void* U_k, void* B_k, void* U_v,
                                void* B_v, void* stream);
 
@@ -143,8 +156,8 @@ typedef struct {
   int32_t top_k;         /* tokens at full rank per (sequence, query head), 0 <= k <= N   */
   float scale;           /* softmax scale, finite and > 0 (usually 1/sqrt(d))              */
   int32_t n_text;        /* T >= 0 dense text tokens joining the softmax                  */
-  const void* text_k;    /* device [B][T][W] storage dtype, NULL iff T == 0               */
-  const void* text_v;    /* device [B][T][W] storage dtype, NULL iff T == 0               */
+  const void* text_k;    /* device [B][T][W] storage dtype (bf16 for AP_INT4), NULL iff T == 0 */
+  const void* text_v;    /* device [B][T][W] storage dtype (bf16 for AP_INT4), NULL iff T == 0 */
   int32_t* sel_out;      /* optional device [B][Hq][top_k] int32: the selected token ids,
                             ascending per (sequence, head); NULL to skip                  */
   int32_t splits;        /* 0: library's choice (one kernel per step for the shapes it

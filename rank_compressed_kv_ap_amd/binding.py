@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libap.so")
 
 AP_OK, AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_BAD_DTYPE, AP_ERR_UNSUPPORTED, \
     AP_ERR_OUT_OF_MEMORY, AP_ERR_HIP = range(7)
-AP_F32, AP_BF16 = 0, 1
+AP_F32, AP_BF16, AP_INT4 = 0, 1, 2
 KERNEL_NAMES = ("select", "attn", "combine", "decode", "ema")
 
 EXPORTED = (
@@ -107,16 +107,20 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
-def storage_code(dtype: torch.dtype) -> int:
+def storage_code(dtype) -> int:
+    """torch.float32, torch.bfloat16, or "int4" (4-bit U, bf16 B)."""
+    if dtype == "int4":
+        return AP_INT4
     if dtype == torch.float32:
         return AP_F32
     if dtype == torch.bfloat16:
         return AP_BF16
-    raise ValueError(f"unsupported storage dtype {dtype}")
+    raise ValueError(f"unsupported storage {dtype}")
 
 
 def torch_dtype(storage: int) -> torch.dtype:
-    return torch.bfloat16 if storage == AP_BF16 else torch.float32
+    """dtype of K, V, text tokens and B for a storage code."""
+    return torch.float32 if storage == AP_F32 else torch.bfloat16
 
 
 class Cache:
@@ -142,6 +146,10 @@ class Cache:
     def width(self): return self.params.n_kv_heads * self.params.head_dim
     @property
     def dtype(self): return torch_dtype(self.params.storage)
+    @property
+    def u_dtype(self):
+        """dtype of U in set_factors / get_factors (float32 values for 4-bit caches)."""
+        return torch.float32 if self.params.storage == AP_INT4 else self.dtype
 
     def recompress(self, k: torch.Tensor, v: torch.Tensor, *, seed: int = 0,
                    omega: Optional[torch.Tensor] = None) -> None:
@@ -156,7 +164,7 @@ class Cache:
     def get_factors(self):
         p = self.params
         dev = torch.device("cuda")
-        U_k = torch.empty(p.batch, p.n_tokens, p.rank, dtype=self.dtype, device=dev)
+        U_k = torch.empty(p.batch, p.n_tokens, p.rank, dtype=self.u_dtype, device=dev)
         U_v = torch.empty_like(U_k)
         B_k = torch.empty(p.batch, p.rank, self.width, dtype=self.dtype, device=dev)
         B_v = torch.empty_like(B_k)

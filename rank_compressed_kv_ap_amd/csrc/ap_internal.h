@@ -19,7 +19,8 @@ constexpr float kLog2eHost = 1.4426950408889634f;  // scores are kept in log2 un
 struct Dims {
   int B, N, Hkv, Hq, d, W, r, ell, p, q;
   int storage;          // ap_dtype
-  int esize;            // bytes per stored element
+  int esize;            // bytes per stored element of B (and of K, V, text): 4 f32, 2 bf16 / int4
+  int ubytes;           // bytes per tiled U panel of 512 elements: 256 with 4-bit codes
   int NP;               // panels of 16 columns: r_pad = 16 * NP
   int r_pad;
   int N_pad;            // tokens rounded up to a 32-token block
@@ -45,6 +46,7 @@ struct ap_cache {
   // factors
   void* Uk = nullptr;   // [B][nblk][2][NP][512]: K-layout panels then V-layout panels
   void* Uv = nullptr;   // = Uk + NP*512 elements (same allocation)
+  uint16_t* Usc = nullptr;  // 4-bit codes only: bf16 block scales [B][nblk][2][r_pad]
   void* Bk = nullptr;   // [B][r_pad][W] row-major (rows r..r_pad-1 zero)
   void* Bv = nullptr;
   float* sigma_k = nullptr;  // [B][r]

@@ -28,7 +28,8 @@ static ap_status hip_fail(hipError_t e, const char* what) {
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 static ap_status validate_shape(const ap_compress_params* p) {
-  if (p->storage != AP_F32 && p->storage != AP_BF16) return fail(AP_ERR_BAD_DTYPE, "storage must be AP_F32 or AP_BF16");
+  if (p->storage != AP_F32 && p->storage != AP_BF16 && p->storage != AP_INT4)
+    return fail(AP_ERR_BAD_DTYPE, "storage must be AP_F32, AP_BF16 or AP_INT4");
   if (p->reserved != 0) return fail(AP_ERR_BAD_SHAPE, "reserved must be 0");
   if (p->batch < 0) return fail(AP_ERR_BAD_SHAPE, "batch < 0");
   if (p->n_tokens < 1) return fail(AP_ERR_BAD_SHAPE, "n_tokens < 1");
@@ -65,7 +66,8 @@ static Dims make_dims(const ap_compress_params* p) {
   d.q = p->power_iters;
   d.ell = std::min(std::min(d.r + d.p, d.N), d.W);
   d.storage = p->storage;
-  d.esize = p->storage == AP_BF16 ? 2 : 4;
+  d.esize = p->storage == AP_F32 ? 4 : 2;
+  d.ubytes = p->storage == AP_INT4 ? 256 : 512 * d.esize;
   d.NP = ceil_div(d.r, 16);
   d.r_pad = 16 * d.NP;
   d.N_pad = ceil_div(d.N, kBlockTokHost) * kBlockTokHost;
@@ -79,7 +81,7 @@ static Dims make_dims(const ap_compress_params* p) {
 }
 
 static void free_all(ap_cache* c) {
-  void* ptrs[] = {c->Uk, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->qt, c->mask, c->part_z, c->part_ml, c->ml_final};
+  void* ptrs[] = {c->Uk, c->Usc, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->qt, c->mask, c->part_z, c->part_ml, c->ml_final};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   for (hipEvent_t e : c->timing.ev) (void)hipEventDestroy(e);
@@ -89,9 +91,11 @@ static void free_all(ap_cache* c) {
 static ap_status alloc_cache(ap_cache* c) {
   const Dims& dm = c->dm;
   struct Req { void** ptr; size_t bytes; };
-  const size_t uel = (size_t)dm.B * dm.NP * dm.nblk * 512;
+  const size_t upan = (size_t)dm.B * dm.NP * dm.nblk;   // panels per factor
+  const size_t usc = dm.storage == AP_INT4 ? (size_t)dm.B * dm.nblk * 2 * dm.r_pad * 2 : 0;
   Req reqs[] = {
-      {&c->Uk, 2 * uel * dm.esize},
+      {&c->Uk, 2 * upan * dm.ubytes},
+      {reinterpret_cast<void**>(&c->Usc), usc},
       {&c->Bk, (size_t)dm.B * dm.r_pad * dm.W * dm.esize},
       {&c->Bv, (size_t)dm.B * dm.r_pad * dm.W * dm.esize},
       {reinterpret_cast<void**>(&c->sigma_k), (size_t)dm.B * dm.r * 4},
@@ -113,8 +117,8 @@ static ap_status alloc_cache(ap_cache* c) {
     }
     total += r.bytes;
   }
-  c->Uv = c->Uk ? static_cast<char*>(c->Uk) + (size_t)dm.NP * 512 * dm.esize : nullptr;
-  c->factor_bytes = 2 * uel * dm.esize + 2 * (size_t)dm.B * dm.r_pad * dm.W * dm.esize;
+  c->Uv = c->Uk ? static_cast<char*>(c->Uk) + (size_t)dm.NP * dm.ubytes : nullptr;
+  c->factor_bytes = 2 * upan * dm.ubytes + usc + 2 * (size_t)dm.B * dm.r_pad * dm.W * dm.esize;
   c->device_bytes = total;
   // padded rows of B and the singular values start at zero
   hipError_t e = hipSuccess;

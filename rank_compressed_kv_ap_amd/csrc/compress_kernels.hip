@@ -27,6 +27,7 @@
 
 #include "ap_internal.h"
 #include "device_common.h"
+#include "quant4.h"
 
 namespace ap {
 
@@ -802,6 +803,45 @@ __global__ __launch_bounds__(256) void k_assemble_u(const float* __restrict__ Qn
   }
 }
 
+// 4-bit factors: the same product for one block, kept in LDS in fp32, then quantized
+// with the block's per-column scales (quant4.h).
+__global__ __launch_bounds__(256) void k_assemble_u4(const float* __restrict__ Qn, const float* __restrict__ PS,
+                                                     i4_t* __restrict__ Ukv, bf16_t* __restrict__ scales,
+                                                     int N, int ellp, int r, int NP, int nblk) {
+  extern __shared__ __align__(16) float sh[];
+  const int rp = 16 * NP, ld = rp + 1;
+  float* Qs = sh;                      // [32][ellp + 1]
+  float* Ps = Qs + 32 * (ellp + 1);    // [ellp][rp]
+  float* Ub = Ps + ellp * rp;          // [32][ld]
+  float* scl = Ub + 32 * ld;           // [rp]
+  const int mat = blockIdx.x / nblk, t = blockIdx.x % nblk;
+  const int b = mat >> 1;
+  const bool vl = mat & 1;
+  const float* Q = Qn + (size_t)mat * N * ellp;
+  const float* P = PS + (size_t)mat * ellp * ellp;
+  for (int idx = threadIdx.x; idx < 32 * ellp; idx += blockDim.x) {
+    const int rr = idx / ellp, j = idx % ellp;
+    const int token = kBlockTok * t + rr;
+    Qs[rr * (ellp + 1) + j] = token < N ? Q[(size_t)token * ellp + j] : 0.f;
+  }
+  for (int idx = threadIdx.x; idx < ellp * rp; idx += blockDim.x) {
+    const int j = idx / rp, col = idx % rp;
+    Ps[idx] = col < r ? P[j * ellp + col] : 0.f;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 32 * rp; idx += blockDim.x) {
+    const int rr = idx / rp, col = idx % rp;
+    float v = 0.f;
+    for (int j = 0; j < ellp; ++j) v = fmaf(Qs[rr * (ellp + 1) + j], Ps[j * rp + col], v);
+    Ub[rr * ld + col] = v;
+  }
+  __syncthreads();
+  i4_t* tiles = tile_ptr(Ukv, tile_base(b, 0, t, NP, nblk) + (vl ? (size_t)NP * kBlockElems : 0));
+  bf16_t* srow = scales + (((size_t)b * nblk + t) * 2 + (vl ? 1 : 0)) * rp;
+  if (vl) q4_store_block<true>(Ub, ld, NP, tiles, srow, scl);
+  else q4_store_block<false>(Ub, ld, NP, tiles, srow, scl);
+}
+
 // B[i][w] = sum_j Qc[w][j] S[j][i] for i < r (rows r..r_pad-1 stay zero).  One
 // workgroup per (matrix, 64 columns w): the 64 rows of Qc and S[:, :r_pad] are staged
 // in LDS; each thread accumulates a 4 (i) x 4 (w) block and stores 4 consecutive w.
@@ -1030,7 +1070,9 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   const size_t lds_chol = (size_t)(2 * ellp * (ellp + 1) + 4 * 16 * 17) * sizeof(float);
   const size_t lds_jac = (size_t)(2 * ellp * (ellp + 1) + 2 * ellp) * sizeof(float);
   const size_t lds_apply = (size_t)(apply_rows(ellp) * (ellp + 1) + ellp * ellp) * sizeof(float);
-  const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP) * sizeof(float);
+  const bool u4 = dm.storage == AP_INT4;
+  const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP +
+                                (u4 ? 32 * (16 * dm.NP + 1) + 16 * dm.NP : 0)) * sizeof(float);
   const size_t lds_b = (size_t)(64 * (ellp + 1) + ellp * dm.r_pad) * sizeof(float);
   const struct { const void* fn; size_t bytes; const char* name; } lds_req[] = {
       {reinterpret_cast<const void*>(&k_gram<8>), (size_t)ellp * (ellp + 1) * sizeof(float), "LDS size of k_gram"},
@@ -1038,7 +1080,8 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
       {reinterpret_cast<const void*>(&k_assemble_b<T>), lds_b, "LDS size of k_assemble_b"},
       {reinterpret_cast<const void*>(&k_jacobi), lds_jac, "LDS size of k_jacobi"},
       {reinterpret_cast<const void*>(&k_apply<T>), lds_apply, "LDS size of k_apply"},
-      {reinterpret_cast<const void*>(&k_assemble_u<T>), lds_u, "LDS size of k_assemble_u"},
+      {u4 ? reinterpret_cast<const void*>(&k_assemble_u4) : reinterpret_cast<const void*>(&k_assemble_u<T>),
+       lds_u, "LDS size of k_assemble_u"},
   };
   for (const auto& rq : lds_req) {
     e = hipFuncSetAttribute(rq.fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rq.bytes));
@@ -1072,8 +1115,13 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
                      ws.Sv, ws.sig);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_stage(e, "core SVD");
-  hipLaunchKernelGGL(k_assemble_u<T>, dim3(nmat * dm.nblk), dim3(256), lds_u, st, ws.Qn, ws.PS,
-                     static_cast<T*>(c->Uk), dm.N, ellp, dm.r, dm.NP, dm.nblk);
+  if (u4)
+    hipLaunchKernelGGL(k_assemble_u4, dim3(nmat * dm.nblk), dim3(256), lds_u, st, ws.Qn, ws.PS,
+                       static_cast<i4_t*>(c->Uk), reinterpret_cast<bf16_t*>(c->Usc), dm.N, ellp, dm.r,
+                       dm.NP, dm.nblk);
+  else
+    hipLaunchKernelGGL(k_assemble_u<T>, dim3(nmat * dm.nblk), dim3(256), lds_u, st, ws.Qn, ws.PS,
+                       static_cast<T*>(c->Uk), dm.N, ellp, dm.r, dm.NP, dm.nblk);
   const int tiles_w = (dm.W + 63) / 64;
   hipLaunchKernelGGL(k_assemble_b<T>, dim3(nmat * tiles_w), dim3(256), lds_b, st, ws.Qc, ws.Sv,
                      static_cast<T*>(c->Bk), static_cast<T*>(c->Bv), dm.W, ellp, dm.r, dm.r_pad, tiles_w);
@@ -1086,7 +1134,8 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
 }
 
 hipError_t run_compress(ap_cache* c, const void* k, const void* v, hipStream_t st) {
-  if (c->dm.storage == AP_BF16) return compress_t<bf16_t>(c, k, v, st);
+  // 4-bit caches take bf16 K and V and keep B in bf16; only U's assembly differs
+  if (c->dm.storage != AP_F32) return compress_t<bf16_t>(c, k, v, st);
   return compress_t<float>(c, k, v, st);
 }
 

@@ -37,13 +37,24 @@ namespace ap {
 // rounding moves a score by about 2^-9 of its size, far inside the output tolerance.
 template <class T, int NP, int HT>
 __device__ __forceinline__ void attn_load(const T* __restrict__ Uk, const T* __restrict__ Uv,
+                                          const bf16_t* __restrict__ Usc,
                                           const uint32_t* __restrict__ mask, int b, int blk,
                                           int nblk, int Hq, int lane, LaneTile<T> (&uk)[NP],
-                                          LaneTile<T> (&uv)[NP], uint32_t (&mw)[HT]) {
+                                          LaneTile<T> (&uv)[NP], uint32_t (&mw)[HT],
+                                          uint2 (&scl)[2][NP]) {
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    uk[p].load(Uk + tile_base(b, p, blk, NP, nblk), lane);
-    uv[p].load(Uv + tile_base(b, p, blk, NP, nblk), lane);
+    uk[p].load(tile_ptr(Uk, tile_base(b, p, blk, NP, nblk)), lane);
+    uv[p].load(tile_ptr(Uv, tile_base(b, p, blk, NP, nblk)), lane);
+  }
+  if constexpr (std::is_same<T, i4_t>::value) {
+    // block scales of this lane's columns 16p + 4(l/16) + e, K row then V row
+    const bf16_t* row = Usc + ((size_t)b * nblk + blk) * 2 * (16 * NP) + (lane >> 4) * 4 * NP;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      scl[0][p] = *reinterpret_cast<const uint2*>(row + 4 * p);
+      scl[1][p] = *reinterpret_cast<const uint2*>(row + 16 * NP + 4 * p);
+    }
   }
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -53,13 +64,23 @@ __device__ __forceinline__ void attn_load(const T* __restrict__ Uk, const T* __r
   }
 }
 
+// two workgroups per CU while the tiles fit the registers (4-bit codes hold as many
+// expanded values as bf16)
+template <class T>
+constexpr int kAttnElemRegBytes = sizeof(T) == 1 ? 2 : static_cast<int>(sizeof(T));
 template <class T, int NP, int HT>
-__global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_attn(
-    const T* __restrict__ Uk, const T* __restrict__ Uv, const float* __restrict__ qt,
-    const uint32_t* __restrict__ mask, float* __restrict__ part_z, float* __restrict__ part_ml,
-    float* __restrict__ ema_s, int N, int nblk, int CB, int S, int Hq, int r_lo, float sl2) {
+__global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1) void k_attn(
+    const T* __restrict__ Uk, const T* __restrict__ Uv, const bf16_t* __restrict__ Usc,
+    const float* __restrict__ qt, const uint32_t* __restrict__ mask, float* __restrict__ part_z,
+    float* __restrict__ part_ml, float* __restrict__ ema_s, int N, int nblk, int CB, int S, int Hq,
+    int r_lo, float sl2) {
   constexpr int RP = NP * 16, HP = HT * 16, ZS = RP + 1;
-  constexpr bool BF = std::is_same<T, bf16_t>::value;
+  // 4-bit codes run the bf16 MFMA path on codes expanded to 136 + code; each product
+  // gets one more MFMA with -136 in every A element and the same other operand, which
+  // cancels the offset, and the block scales are folded into the latent query (scores)
+  // or applied to each block's product (values)
+  constexpr bool U4 = std::is_same<T, i4_t>::value;
+  constexpr bool BF = std::is_same<T, bf16_t>::value || U4;
   extern __shared__ __align__(16) float smem_f[];
   const int b = blockIdx.x / S, s = blockIdx.x - (blockIdx.x / S) * S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -69,7 +90,8 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
   // latent-query operands: panel p, head tile ht, this lane's 4 columns 16p+4lg+e.
   // Rows of padded heads are loaded too (the buffer holds them) and zeroed after, so
   // every load is unconditional and all of them are in flight together.
-  using QT = typename std::conditional<BF, v4s, QOp<float>>::type;
+  using QT = typename std::conditional<
+      U4, float4, typename std::conditional<BF, v4s, QOp<float>>::type>::type;
   QT qop[NP][HT];
   {
     float4 qraw[NP][HT];
@@ -85,7 +107,9 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
         // the softmax scale (in log2 units) is folded into the latent query
         const float f = 16 * ht + l16 < Hq ? sl2 : 0.f;
         const float v[4] = {qraw[p][ht].x * f, qraw[p][ht].y * f, qraw[p][ht].z * f, qraw[p][ht].w * f};
-        if constexpr (BF) {
+        if constexpr (U4) {
+          qop[p][ht] = make_float4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (BF) {
           const uint2 w = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
           qop[p][ht] = __builtin_bit_cast(v4s, w);
         } else {
@@ -106,13 +130,15 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
 
   LaneTile<T> uk[NP], uv[NP];
   uint32_t mw[HT];
+  uint2 ssc[2][NP];   // 4-bit codes: this block's K and V scales of the lane's columns
   int blk = blk0 + wave;
-  if (blk < blk1) attn_load<T, NP, HT>(Uk, Uv, mask, b, blk, nblk, Hq, lane, uk, uv, mw);
+  if (blk < blk1) attn_load<T, NP, HT>(Uk, Uv, Usc, mask, b, blk, nblk, Hq, lane, uk, uv, mw, ssc);
   for (; blk < blk1; blk += 4) {
     LaneTile<T> nk[NP], nv[NP];
     uint32_t nmw[HT];
+    uint2 nsc[2][NP];
     const bool more = blk + 4 < blk1;
-    if (more) attn_load<T, NP, HT>(Uk, Uv, mask, b, blk + 4, nblk, Hq, lane, nk, nv, nmw);
+    if (more) attn_load<T, NP, HT>(Uk, Uv, Usc, mask, b, blk + 4, nblk, Hq, lane, nk, nv, nmw, nsc);
     const bool tail = (blk + 1) * kBlockTok > N;
 
     if constexpr (BF) {
@@ -120,20 +146,43 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
       // max for the block, and the value product of both halves in one 16x16x32 MFMA
       // (k-slot 8*(l/16) + 4*half + e <-> token 16*half + 4*(l/16) + e, which is how
       // the V-layout tile and the score tiles already place their elements).
+      [[maybe_unused]] uint4 dk[NP];
+      if constexpr (U4) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) dk[p] = uk[p].deq();
+      }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         v4f slo[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}}, shi[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}};
+        v4s qb[NP];   // this block's latent-query operands
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          if constexpr (U4) {
+            float s[4];
+            q4_scales(ssc[0][p], s);
+            const float4 qv = qop[p][ht];
+            qb[p] = __builtin_bit_cast(v4s, make_uint2(pack_bf16x2(qv.x * s[0], qv.y * s[1]),
+                                                       pack_bf16x2(qv.z * s[2], qv.w * s[3])));
+          } else {
+            qb[p] = qop[p][ht];
+          }
+        }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
-            const v4s a = uk[p].half(hf);
-            if (16 * p + 16 <= r_lo) {
-              slo[hf] = mfma_bf16(a, qop[p][ht], slo[hf]);
-            } else if (16 * p >= r_lo) {
-              shi[hf] = mfma_bf16(a, qop[p][ht], shi[hf]);
+            v4s a;
+            if constexpr (U4) {
+              a = __builtin_bit_cast(v4s, hf == 0 ? make_uint2(dk[p].x, dk[p].y) : make_uint2(dk[p].z, dk[p].w));
             } else {
-              v4s ql = qop[p][ht], qh = qop[p][ht];
+              a = uk[p].half(hf);
+            }
+            if (16 * p + 16 <= r_lo) {
+              slo[hf] = mfma_bf16(a, qb[p], slo[hf]);
+            } else if (16 * p >= r_lo) {
+              shi[hf] = mfma_bf16(a, qb[p], shi[hf]);
+            } else {
+              v4s ql = qb[p], qh = qb[p];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 if (16 * p + 4 * lg + e < r_lo) qh[e] = 0; else ql[e] = 0;
@@ -142,6 +191,33 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
               shi[hf] = mfma_bf16(a, qh, shi[hf]);
             }
           }
+        if constexpr (U4) {
+          // the offset 136 of every expanded code: -136 * (sum of the query operand), the
+          // same for every token row, from the same bf16 operands
+          const v4s an = __builtin_bit_cast(v4s, make_uint2(kQ4NegOffset2, kQ4NegOffset2));
+          v4f clo = v4f{0, 0, 0, 0}, chi = v4f{0, 0, 0, 0};
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            if (16 * p + 16 <= r_lo) {
+              clo = mfma_bf16(an, qb[p], clo);
+            } else if (16 * p >= r_lo) {
+              chi = mfma_bf16(an, qb[p], chi);
+            } else {
+              v4s ql = qb[p], qh = qb[p];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (16 * p + 4 * lg + e < r_lo) qh[e] = 0; else ql[e] = 0;
+              }
+              clo = mfma_bf16(an, ql, clo);
+              chi = mfma_bf16(an, qh, chi);
+            }
+          }
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            slo[hf] += clo;
+            shi[hf] += chi;
+          }
+        }
         uint32_t bit[8];
         float sc[8];
 #pragma unroll
@@ -191,6 +267,31 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
         }
         const v8bf pa8 = __builtin_bit_cast(v8bf, make_uint4(pa[0], pa[1], pa[2], pa[3]));
         const v8bf ph8 = __builtin_bit_cast(v8bf, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+        if constexpr (U4) {
+          // per block: D = sum over its 32 tokens of code * p (offset cancelled), then
+          // Z += scale(column) * D; D row t of this lane is latent column 16p + 4(l/16) + t
+          const v8bf an8 = __builtin_bit_cast(v8bf, make_uint4(kQ4NegOffset2, kQ4NegOffset2, kQ4NegOffset2, kQ4NegOffset2));
+          const v4f z0 = v4f{0, 0, 0, 0};
+          const v4f cpa = mfma_bf16_k32(an8, pa8, z0), cph = mfma_bf16_k32(an8, ph8, z0);
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const v8bf a8 = __builtin_bit_cast(v8bf, uv[p].deq());
+            v4f D;
+            if (16 * p + 16 <= r_lo) {
+              D = mfma_bf16_k32(a8, pa8, cpa);
+            } else if (16 * p >= r_lo) {
+              D = mfma_bf16_k32(a8, ph8, cph);
+            } else {
+              const v4f D1 = mfma_bf16_k32(a8, pa8, cpa), D2 = mfma_bf16_k32(a8, ph8, cph);
+#pragma unroll
+              for (int t = 0; t < 4; ++t) D[t] = 16 * p + 4 * lg + t < r_lo ? D1[t] : D2[t];
+            }
+            float s[4];
+            q4_scales(ssc[1][p], s);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Z[p][ht][t] = fmaf(s[t], D[t], Z[p][ht][t]);
+          }
+        } else {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           const v8bf a8 = __builtin_bit_cast(v8bf, uv[p].raw);
@@ -204,6 +305,7 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
             Z[p][ht] = mfma_bf16_k32(lo_row ? a8 : zero8, pa8, Z[p][ht]);
             Z[p][ht] = mfma_bf16_k32(lo_row ? zero8 : a8, ph8, Z[p][ht]);
           }
+        }
         }
       }
     } else {
@@ -308,6 +410,13 @@ __global__ __launch_bounds__(256, (NP * HT * sizeof(T) <= 16) ? 2 : 1) void k_at
       }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) mw[ht] = nmw[ht];
+      if constexpr (U4) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          ssc[0][p] = nsc[0][p];
+          ssc[1][p] = nsc[1][p];
+        }
+      }
     }
   }
 
@@ -620,7 +729,8 @@ static hipError_t launch_attn_t(const ap_cache* c, int r_lo, float sl2, int S, i
     attr_set = true;
   }
   hipExtLaunchKernelGGL((k_attn<T, NP, HT>), dim3(dm.B * S), dim3(256), lds, st, ev.start, ev.stop, 0,
-                     static_cast<const T*>(c->Uk), static_cast<const T*>(c->Uv), c->qt, c->mask,
+                     static_cast<const T*>(c->Uk), static_cast<const T*>(c->Uv),
+                     reinterpret_cast<const bf16_t*>(c->Usc), c->qt, c->mask,
                      c->part_z, c->part_ml, ema_s, dm.N, dm.nblk, CB, S, dm.Hq, r_lo, sl2);
   return hipGetLastError();
 }
@@ -660,6 +770,7 @@ static hipError_t dispatch_ht(const ap_cache* c, int r_lo, float sl2, int S, int
 
 hipError_t launch_attn(const ap_cache* c, int r_lo, float sl2, int S, int CB, float* ema_s, hipStream_t st,
                        const KernelEvents& ev) {
+  if (c->dm.storage == AP_INT4) return dispatch_ht<i4_t>(c, r_lo, sl2, S, CB, ema_s, st, ev);
   if (c->dm.storage == AP_BF16) return dispatch_ht<bf16_t>(c, r_lo, sl2, S, CB, ema_s, st, ev);
   return dispatch_ht<float>(c, r_lo, sl2, S, CB, ema_s, st, ev);
 }
@@ -696,7 +807,8 @@ static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float sl2, int S, int Tn,
                           const void* tk, const void* tv, float* ml_out, hipStream_t st,
                           const KernelEvents& ev) {
-  if (c->dm.storage == AP_BF16) return launch_combine_t<bf16_t>(c, q, out, sl2, S, Tn, tk, tv, ml_out, st, ev);
+  // B and the text tokens are bf16 for 4-bit caches too
+  if (c->dm.storage != AP_F32) return launch_combine_t<bf16_t>(c, q, out, sl2, S, Tn, tk, tv, ml_out, st, ev);
   return launch_combine_t<float>(c, q, out, sl2, S, Tn, tk, tv, ml_out, st, ev);
 }
 

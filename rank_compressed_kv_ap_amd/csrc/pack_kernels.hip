@@ -1,8 +1,10 @@
 // Conversion between the plain factor layout U [B][N][r] (row-major, as in the
 // page's K ~= K* D_k, [fr §2.A "Mécanisme"]) and the tiled layouts the decode
-// kernels read with one vector load per lane (see device_common.h).
+// kernels read with one vector load per lane (see device_common.h), including the
+// 4-bit layout (quant4.h), whose codes are chosen here from fp32 rows.
 #include "ap_internal.h"
 #include "device_common.h"
+#include "quant4.h"
 
 namespace ap {
 
@@ -95,12 +97,93 @@ static hipError_t pack_t(const ap_cache* c, const void* src, void* dst, bool vl,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- 4-bit factors
+// One workgroup per (sequence, token block): the fp32 rows of U [B][N][r] are staged in
+// LDS, then quantized and stored in the tiled 4-bit layout with their block scales.
+template <bool VL>
+__global__ __launch_bounds__(256) void k_pack_u4(const float* __restrict__ src, i4_t* __restrict__ dst,
+                                                 bf16_t* __restrict__ scales, int N, int r, int NP,
+                                                 int nblk) {
+  extern __shared__ __align__(16) float sh[];
+  const int rp = 16 * NP, ld = rp + 1;
+  float* Ub = sh;               // [32][ld]
+  float* scl = Ub + 32 * ld;    // [rp]
+  const int b = blockIdx.x / nblk, t = blockIdx.x % nblk;
+  for (int idx = threadIdx.x; idx < 32 * rp; idx += blockDim.x) {
+    const int rr = idx / rp, col = idx % rp, token = kBlockTok * t + rr;
+    Ub[rr * ld + col] = (token < N && col < r) ? src[((size_t)b * N + token) * r + col] : 0.f;
+  }
+  __syncthreads();
+  q4_store_block<VL>(Ub, ld, NP, tile_ptr(dst, tile_base(b, 0, t, NP, nblk)),
+                     scales + (((size_t)b * nblk + t) * 2 + (VL ? 1 : 0)) * rp, scl);
+}
+
+// Dequantized values code * scale back to the plain fp32 layout.
+template <bool VL>
+__global__ __launch_bounds__(256) void k_unpack_u4(const i4_t* __restrict__ src,
+                                                   const bf16_t* __restrict__ scales,
+                                                   float* __restrict__ dst, int B, int N, int r,
+                                                   int NP, int nblk) {
+  const size_t total = (size_t)B * N * r;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int c = static_cast<int>(idx % r);
+    const size_t bn = idx / r;
+    const int n = static_cast<int>(bn % N);
+    const int b = static_cast<int>(bn / N);
+    const int t = n / kBlockTok, nn = n % kBlockTok, half = nn >> 4;
+    const int p = c >> 4, cc = c & 15;
+    int lane, e;
+    if (!VL) {
+      lane = (cc >> 2) * 16 + (nn & 15);
+      e = cc & 3;
+    } else {
+      const int rem = nn & 15;
+      lane = (rem >> 2) * 16 + cc;
+      e = rem & 3;
+    }
+    const uint32_t w = reinterpret_cast<const uint32_t*>(tile_ptr(src, tile_base(b, p, t, NP, nblk)))[lane];
+    const int code = static_cast<int>((w >> q4_shift(4 * half + e)) & 0xFu) - 8;
+    const float s = bf16_to_f32(scales[(((size_t)b * nblk + t) * 2 + (VL ? 1 : 0)) * 16 * NP + scale_slot(c, NP)]);
+    dst[idx] = static_cast<float>(code) * s;
+  }
+}
+
+static hipError_t pack_u4(const ap_cache* c, const void* src, void* dst, bool vl, bool unpack,
+                          hipStream_t st) {
+  const Dims& dm = c->dm;
+  if (!unpack) {
+    const size_t lds = (32 * (dm.r_pad + 1) + dm.r_pad) * sizeof(float);
+    if (vl)
+      hipLaunchKernelGGL(k_pack_u4<true>, dim3(dm.B * dm.nblk), dim3(256), lds, st,
+                         static_cast<const float*>(src), static_cast<i4_t*>(dst),
+                         reinterpret_cast<bf16_t*>(c->Usc), dm.N, dm.r, dm.NP, dm.nblk);
+    else
+      hipLaunchKernelGGL(k_pack_u4<false>, dim3(dm.B * dm.nblk), dim3(256), lds, st,
+                         static_cast<const float*>(src), static_cast<i4_t*>(dst),
+                         reinterpret_cast<bf16_t*>(c->Usc), dm.N, dm.r, dm.NP, dm.nblk);
+  } else {
+    const size_t total = (size_t)dm.B * dm.N * dm.r;
+    if (vl)
+      hipLaunchKernelGGL(k_unpack_u4<true>, grid_for(total), dim3(256), 0, st,
+                         static_cast<const i4_t*>(src), reinterpret_cast<const bf16_t*>(c->Usc), static_cast<float*>(dst), dm.B, dm.N,
+                         dm.r, dm.NP, dm.nblk);
+    else
+      hipLaunchKernelGGL(k_unpack_u4<false>, grid_for(total), dim3(256), 0, st,
+                         static_cast<const i4_t*>(src), reinterpret_cast<const bf16_t*>(c->Usc), static_cast<float*>(dst), dm.B, dm.N,
+                         dm.r, dm.NP, dm.nblk);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_u(const ap_cache* c, const void* src, void* dst, bool v_layout, hipStream_t st) {
+  if (c->dm.storage == AP_INT4) return pack_u4(c, src, dst, v_layout, false, st);
   if (c->dm.storage == AP_BF16) return pack_t<bf16_t>(c, src, dst, v_layout, false, st);
   return pack_t<float>(c, src, dst, v_layout, false, st);
 }
 
 hipError_t launch_unpack_u(const ap_cache* c, const void* src, void* dst, bool v_layout, hipStream_t st) {
+  if (c->dm.storage == AP_INT4) return pack_u4(c, src, dst, v_layout, true, st);
   if (c->dm.storage == AP_BF16) return pack_t<bf16_t>(c, src, dst, v_layout, true, st);
   return pack_t<float>(c, src, dst, v_layout, true, st);
 }

@@ -261,7 +261,7 @@ template <> struct SelQ<bf16_t> {
     l = my_j == 0 ? make_uint4(ll.x, ll.y, 0u, 0u) : make_uint4(0u, 0u, ll.x, ll.y);
   }
   template <int NSL>
-  __device__ __forceinline__ v4f step(const LaneTile<bf16_t> (&t)[NSL], int my_slot, int my_j, v4f acc) const {
+  __device__ __forceinline__ v4f step(const LaneTile<bf16_t> (&t)[NSL], uint2, int my_slot, int my_j, v4f acc) const {
     return score_step<NSL>(t, h, l, my_slot, my_j, acc);
   }
 };
@@ -271,10 +271,44 @@ template <> struct SelQ<float> {
     for (int e = 0; e < 4; ++e) v[e] = x[e];
   }
   template <int NSL>
-  __device__ __forceinline__ v4f step(const LaneTile<float> (&t)[NSL], int my_slot, int my_j, v4f acc) const {
+  __device__ __forceinline__ v4f step(const LaneTile<float> (&t)[NSL], uint2, int my_slot, int my_j, v4f acc) const {
     return score_step<NSL>(t, v, my_slot, my_j, acc);
   }
 };
+// 4-bit codes: the block scales of this lane's own slot (scw, its 4 columns) are folded
+// into the latent query before the hi/lo split; the codes enter as 136 + code and one
+// more pair of products with -136 in every A element removes the offset (the operands
+// of the other slots are zero in this lane, so one pair serves all slots).
+template <> struct SelQ<i4_t> {
+  float v[4];
+  __device__ __forceinline__ void set(const float x[4], int) {
+    for (int e = 0; e < 4; ++e) v[e] = x[e];
+  }
+  template <int NSL>
+  __device__ __forceinline__ v4f step(const LaneTile<i4_t> (&t)[NSL], uint2 scw, int my_slot, int my_j, v4f acc) const {
+    float s[4];
+    q4_scales(scw, s);
+    const float f[4] = {v[0] * s[0], v[1] * s[1], v[2] * s[2], v[3] * s[3]};
+    SelQ<bf16_t> qb;
+    qb.set(f, my_j);
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const bool on = sl == my_slot;
+      const uint4 h = on ? qb.h : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 l = on ? qb.l : make_uint4(0u, 0u, 0u, 0u);
+      const v8bf a = __builtin_bit_cast(v8bf, t[sl].deq());
+      acc = mfma_bf16_k32(a, __builtin_bit_cast(v8bf, h), acc);
+      acc = mfma_bf16_k32(a, __builtin_bit_cast(v8bf, l), acc);
+    }
+    const v8bf an = __builtin_bit_cast(v8bf, make_uint4(kQ4NegOffset2, kQ4NegOffset2, kQ4NegOffset2, kQ4NegOffset2));
+    acc = mfma_bf16_k32(an, __builtin_bit_cast(v8bf, qb.h), acc);
+    return mfma_bf16_k32(an, __builtin_bit_cast(v8bf, qb.l), acc);
+  }
+};
+
+// Element type of B: the storage type, bf16 for 4-bit token factors.
+template <class T>
+using StoreB = typename std::conditional<std::is_same<T, i4_t>::value, bf16_t, T>::type;
 
 // Operands of the single-kernel decode (unused by the selection-only kernel).
 struct FusedArgs {
@@ -289,6 +323,8 @@ struct FusedArgs {
   // of the low-rank logits; [B][Hq][N] when keys_per_head, else [B][N] shared by heads
   const float* keys;
   int keys_per_head;
+  // 4-bit codes: bf16 block scales [B][nblk][2][r_pad] (quant4.h)
+  const bf16_t* Usc;
 };
 
 // HG: query heads per workgroup (4 or 1); NPL: low panels (1 or 2 with the tiles of
@@ -298,12 +334,14 @@ struct FusedArgs {
 // projection (bf16 factors, HG = 4, r <= 64), so one kernel makes the whole step.
 template <class T, int HG, int NPL, int NACC, bool FUSED>
 __device__ __forceinline__ void select_body(
-    const T* __restrict__ Uk, const T* __restrict__ Bk, const float* __restrict__ q,
+    const T* __restrict__ Uk, const StoreB<T>* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
     int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
     int r_lo, int top_k, const FusedArgs& fa) {
   static_assert(!FUSED || (HG == 4 && NPL <= 2 && std::is_same<T, bf16_t>::value),
                 "single-kernel decode: bf16, four heads per workgroup");
+  constexpr bool U4 = std::is_same<T, i4_t>::value;
+  using TB = StoreB<T>;   // element type of B (and of the text tokens)
   constexpr int NSL = 8 / HG;                                   // token blocks per step
   constexpr int KPL = 4 * NACC;                                 // scores per lane
   constexpr int NSTEP = NACC * NPL;
@@ -344,12 +382,12 @@ __device__ __forceinline__ void select_body(
 
   // ---- A. loads in flight together: B_k rows first (the latent queries wait only for
   // them), then q, then the first U_k low-panel tiles
-  constexpr int V = Vec16<T>::n;
+  constexpr int V = Vec16<TB>::n;
   constexpr int XB = 4;    // B_k row slices per lane in flight
   const int ginv_num = (65536 + G - 1) / G;   // (h * ginv_num) >> 16 == h / G for h, G <= 64
   const int LPR = d / V;
   const bool vec = d % V == 0 && LPR > 0 && LPR <= 64 && (LPR & (LPR - 1)) == 0 &&
-                   ((size_t)W * sizeof(T)) % 16 == 0;
+                   ((size_t)W * sizeof(TB)) % 16 == 0;
   const int nrows = nh * r_pad;
   const int RPW = vec ? 64 / LPR : 1, seg = vec ? lane % LPR : 0, rw = vec ? lane / LPR : 0;
   const int rstep = nwv * RPW;
@@ -357,7 +395,7 @@ __device__ __forceinline__ void select_body(
   // head of a flattened (head, latent row) index without an integer division:
   // (row + 0.5) / r_pad is never within float rounding of an integer here
   auto head_of = [&](int row) { return static_cast<int>((static_cast<float>(row) + 0.5f) * inv_rpad); };
-  Vec16<T> x[XB];
+  Vec16<TB> x[XB];
   auto load_rows = [&](int r0) {
 #pragma unroll
     for (int u = 0; u < XB; ++u) {
@@ -375,8 +413,8 @@ __device__ __forceinline__ void select_body(
   const int Tn = FUSED ? fa.Tn : 0;
   const int nrt = nh * Tn;                   // text rows (head, token)
   // with no text the loads read B_k instead (always valid), so they stay unconditional
-  const T* __restrict__ tk = Tn > 0 ? static_cast<const T*>(fa.text_k) : Bk;
-  Vec16<T> xt[FUSED ? XB : 1];
+  const TB* __restrict__ tk = Tn > 0 ? static_cast<const TB*>(fa.text_k) : Bk;
+  Vec16<TB> xt[FUSED ? XB : 1];
   auto load_text = [&](int r0) {
 #pragma unroll
     for (int u = 0; u < XB; ++u) {
@@ -387,14 +425,21 @@ __device__ __forceinline__ void select_body(
   };
 
   LaneTile<T> tb[PREF][NSL];
+  [[maybe_unused]] uint2 tsc[PREF];   // 4-bit codes: K scales of this lane's slot and columns
+  // 4-bit codes: K scale word of block blk, panel p, for this lane's columns 16p + 4lg + e
+  auto scale_word = [&](int blk, int p) {
+    const bf16_t* row = fa.Usc + ((size_t)b * nblk + blk) * 2 * r_pad + lg * 4 * NP + 4 * p;
+    return *reinterpret_cast<const uint2*>(row);
+  };
   auto load_step = [&](int s) {   // s is a compile-time constant after unrolling
     const int a = s / NPL, p = s % NPL;
     const int grp = wave + nwv * a;
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
       const int blk = min(grp * NSL + sl, nblk - 1);   // clamped: loads stay unconditional
-      tb[s % PREF][sl].load(Uk + tile_base(b, min(p, nplo - 1), blk, NP, nblk), lane);
+      tb[s % PREF][sl].load(tile_ptr(Uk, tile_base(b, min(p, nplo - 1), blk, NP, nblk)), lane);
     }
+    if constexpr (U4) tsc[s % PREF] = scale_word(min(grp * NSL + my_slot, nblk - 1), min(p, nplo - 1));
   };
   if constexpr (NPL <= 2) {
 #pragma unroll
@@ -434,7 +479,7 @@ __device__ __forceinline__ void select_body(
   } else {
     for (int idx = tid; idx < nrows; idx += nthr) {
       const int hl = idx / r_pad, i = idx - hl * r_pad;
-      const T* brow = Bk + ((size_t)b * r_pad + i) * W + (size_t)((h0 + hl) / G) * d;
+      const TB* brow = Bk + ((size_t)b * r_pad + i) * W + (size_t)((h0 + hl) / G) * d;
       const float* qp = qh + hl * d;
       float acc = 0.f;
       for (int j = 0; j < d; ++j) acc = fmaf(to_f32(brow[j]), qp[j], acc);
@@ -464,7 +509,7 @@ __device__ __forceinline__ void select_body(
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
       const int blk = min(grp * NSL + sl, nblk - 1);   // clamped: loads stay unconditional
-      rb[s % PD][sl].load(base + tile_base(b, pan, blk, NP, nblk), lane);
+      rb[s % PD][sl].load(tile_ptr(base, tile_base(b, pan, blk, NP, nblk)), lane);
     }
   };
 
@@ -503,7 +548,7 @@ __device__ __forceinline__ void select_body(
 #pragma unroll
         for (int p = 0; p < NPL; ++p) {
           const int s = a * NPL + p;
-          acc = qop[p].template step<NSL>(tb[s % PREF], my_slot, my_j, acc);
+          acc = qop[p].template step<NSL>(tb[s % PREF], U4 ? tsc[s % PREF] : make_uint2(0u, 0u), my_slot, my_j, acc);
           if (s + PREF < NSTEP) load_step(s + PREF);
         }
 #pragma unroll
@@ -520,7 +565,8 @@ __device__ __forceinline__ void select_body(
           LaneTile<T> t1[NSL];
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl)
-            t1[sl].load(Uk + tile_base(b, p, min(grp * NSL + sl, nblk - 1), NP, nblk), lane);
+            t1[sl].load(tile_ptr(Uk, tile_base(b, p, min(grp * NSL + sl, nblk - 1), NP, nblk)), lane);
+          const uint2 scw = U4 ? scale_word(min(grp * NSL + my_slot, nblk - 1), p) : make_uint2(0u, 0u);
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -529,7 +575,7 @@ __device__ __forceinline__ void select_body(
           }
           SelQ<T> q1;
           q1.set(v, my_j);
-          acc = q1.template step<NSL>(t1, my_slot, my_j, acc);
+          acc = q1.template step<NSL>(t1, scw, my_slot, my_j, acc);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) sc[4 * a + t] = acc[t];
@@ -1051,7 +1097,7 @@ __device__ __forceinline__ void select_body(
 // flash-decode kernel.
 template <class T, int HG, int NPL, int NACC>
 __global__ __launch_bounds__(1024) void k_select(
-    const T* __restrict__ Uk, const T* __restrict__ Bk, const float* __restrict__ q,
+    const T* __restrict__ Uk, const StoreB<T>* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
     int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
     int r_lo, int top_k, FusedArgs fa) {
@@ -1125,7 +1171,7 @@ static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, i
   else
     hipExtLaunchKernelGGL((k_select<T, HG, NPL, NACC>), dim3(grid), dim3(64 * waves), lds, st,
                           ev.start, ev.stop, 0, static_cast<const T*>(c->Uk),
-                          static_cast<const T*>(c->Bk), q, c->qt, c->mask, sel_out, dm.B, dm.N,
+                          static_cast<const StoreB<T>*>(c->Bk), q, c->qt, c->mask, sel_out, dm.B, dm.N,
                           dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d, dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo,
                           top_k, fa);
   return hipGetLastError();
@@ -1139,6 +1185,7 @@ static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, i
   FusedArgs fa{};
   fa.keys = keys;
   fa.keys_per_head = keys_per_head ? 1 : 0;
+  fa.Usc = reinterpret_cast<const bf16_t*>(c->Usc);
 #define AP_SEL(HGV, NPLV, NACCV)                                                        \
   if (pl.HG == HGV && pl.NPL == NPLV && pl.NACC == NACCV)                               \
     return launch_select_v<T, HGV, NPLV, NACCV, false>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
@@ -1157,6 +1204,8 @@ static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, i
 
 hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k, int32_t* sel_out,
                          const float* keys, bool keys_per_head, hipStream_t st, const KernelEvents& ev) {
+  if (c->dm.storage == AP_INT4)
+    return launch_select_t<i4_t>(c, q, r_lo, top_k, sel_out, keys, keys_per_head, st, ev);
   if (c->dm.storage == AP_BF16)
     return launch_select_t<bf16_t>(c, q, r_lo, top_k, sel_out, keys, keys_per_head, st, ev);
   return launch_select_t<float>(c, q, r_lo, top_k, sel_out, keys, keys_per_head, st, ev);
@@ -1190,6 +1239,7 @@ hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, in
   fa.sl2 = sl2;
   fa.keys = nullptr;
   fa.keys_per_head = 0;
+  fa.Usc = nullptr;
 #define AP_FUS(NPLV, NACCV)                                                             \
   if (pl.NPL == NPLV && pl.NACC == NACCV)                                               \
     return launch_select_v<bf16_t, 4, NPLV, NACCV, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);

@@ -5,6 +5,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "quant4.h"
 
 namespace ap {
 
@@ -30,6 +31,23 @@ template <> struct LaneTile<float> {
   }
   __device__ __forceinline__ float4 half(int hf) const { return hf == 0 ? h0 : h1; }
 };
+
+// 4-bit codes: one 32-bit word per lane, expanded to bf16 (136 + code) for the MFMA.
+template <> struct LaneTile<i4_t> {
+  uint32_t w;
+  __device__ __forceinline__ void load(const i4_t* base, int lane) {
+    w = reinterpret_cast<const uint32_t*>(base)[lane];
+  }
+  __device__ __forceinline__ uint4 deq() const { return q4_expand(w); }
+};
+
+// Four bf16 block scales (one lane's columns of one panel) as floats.
+__device__ __forceinline__ void q4_scales(uint2 x, float (&s)[4]) {
+  s[0] = __uint_as_float(x.x << 16);
+  s[1] = __uint_as_float(x.x & 0xFFFF0000u);
+  s[2] = __uint_as_float(x.y << 16);
+  s[3] = __uint_as_float(x.y & 0xFFFF0000u);
+}
 
 // A latent-query operand: 4 values (one lane's k-slice) split for the dtype's MFMA.
 template <class T> struct QOp;

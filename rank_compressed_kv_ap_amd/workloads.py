@@ -45,7 +45,7 @@ class Workload:
     rank: int              # r
     r_lo: int              # low rank used for unselected tokens
     top_k: int             # tokens per (sequence, query head) at full rank
-    storage: str           # "f32" or "bf16"
+    storage: str           # "f32", "bf16" or "int4" (4-bit U; K, V, text, B in bf16)
     inner_dim: int         # m: number of spectral components drawn
     sigma_exp: float       # sigma_i = i ** -sigma_exp
     sigma_cut: int         # sigma_i = 0 for i > sigma_cut (0: no cut)
@@ -120,12 +120,19 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def to_storage(x: np.ndarray, storage: str) -> np.ndarray:
-    """Values exactly as a device buffer of the storage dtype holds them (float32)."""
+    """Values exactly as a device buffer of the storage dtype holds them (float32).
+    A 4-bit cache keeps its dense tensors (K, V, text, B) in bf16."""
     if storage == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
-    if storage == "bf16":
+    if storage in ("bf16", "int4"):
         return round_bf16(x)
     raise ValueError(storage)
+
+
+def u_storage(storage: str) -> str:
+    """Rounding of the token factor U handed to the library: a 4-bit cache takes U as
+    float32 values and chooses its codes itself."""
+    return "f32" if storage == "int4" else storage
 
 
 def bf16_bits(x32: np.ndarray) -> np.ndarray:
@@ -196,7 +203,8 @@ def gen_factors(w: Workload, b: int, which: int, step: int = 0):
     """A compressed cache drawn directly in factored form.
 
     U = G1[:, :r] diag(sigma_1..r) (same row structure as gen_kv) and
-    B = G2[:, :r]^T, each rounded to the storage dtype.  U @ B is the rank-r
+    B = G2[:, :r]^T, each rounded to the storage dtype (U to float32 for a 4-bit
+    cache, which quantizes it on loading).  U @ B is the rank-r
     part of the workload's K (which=0) or V (which=1) law; no factorisation
     is run to produce it.  Returns float32 arrays U [N, r], B [r, W].
     """
@@ -206,7 +214,7 @@ def gen_factors(w: Workload, b: int, which: int, step: int = 0):
     G2 = g.standard_normal((w.width, r))
     s = w.sigmas()[:r]
     U = G1 * s[None, :]
-    return to_storage(U, w.storage), to_storage(G2.T, w.storage)
+    return to_storage(U, u_storage(w.storage)), to_storage(G2.T, w.storage)
 
 
 def gen_text(w: Workload, b: int, which: int, rms: float, step: int = 0) -> np.ndarray:

@@ -6,13 +6,31 @@ import numpy as np
 import torch
 
 from oracle.decode import band_mask, decode_ref
+from oracle.quant import quantize_dequant_u4
 from rank_compressed_kv_ap_amd import workloads as wl
 
-TOL = {"bf16": 2e-2, "f32": 1e-4}
+# 4-bit caches attend over bf16-class operands (codes expanded to bf16, bf16 queries
+# and weights in the MFMAs): the bf16 bar
+TOL = {"bf16": 2e-2, "f32": 1e-4, "int4": 2e-2}
 
 
 def torch_storage(w):
-    return torch.bfloat16 if w.storage == "bf16" else torch.float32
+    """dtype of K, V, text and B on the device."""
+    return torch.float32 if w.storage == "f32" else torch.bfloat16
+
+
+def torch_u(w):
+    """dtype of U handed to set_factors (float32 values for a 4-bit cache)."""
+    return torch.float32 if w.storage in ("f32", "int4") else torch.bfloat16
+
+
+def binding_storage(w):
+    return "int4" if w.storage == "int4" else torch_storage(w)
+
+
+def stored_u(w, U):
+    """The U values the cache holds: the oracle's 4-bit round trip for a 4-bit cache."""
+    return quantize_dequant_u4(U) if w.storage == "int4" else U
 
 
 def make_inputs(w, n_distinct=None):
@@ -30,10 +48,12 @@ def upload_decode(w, seqs, binding):
     def stack(key, dtype):
         return torch.from_numpy(np.stack([seqs[i][key] for i in idx])).to(dtype).cuda().contiguous()
 
-    U_k, B_k, U_v, B_v = (stack(k, dt) for k in ("U_k", "B_k", "U_v", "B_v"))
+    U_k, U_v = (stack(k, torch_u(w)) for k in ("U_k", "U_v"))
+    B_k, B_v = (stack(k, dt) for k in ("B_k", "B_v"))
     q = stack("q", torch.float32)
     cache = binding.compress(None, None, batch=B, n_tokens=w.n_tokens, n_kv_heads=w.n_kv_heads,
-                             n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=w.rank, storage=dt)
+                             n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=w.rank,
+                             storage=binding_storage(w))
     cache.set_factors(U_k, B_k, U_v, B_v)
     text_k = text_v = None
     if w.n_text:
@@ -55,7 +75,8 @@ def run_decode(w, seqs, binding, splits=0, with_sel=True):
 
 
 def oracle_decode(w, s):
-    return decode_ref(s["U_k"], s["B_k"], s["U_v"], s["B_v"], s["q"], w.n_kv_heads, w.head_dim,
+    return decode_ref(stored_u(w, s["U_k"]), s["B_k"], stored_u(w, s["U_v"]), s["B_v"], s["q"],
+                      w.n_kv_heads, w.head_dim,
                       w.r_lo, w.top_k, w.scale,
                       s["text_k"] if w.n_text else None, s["text_v"] if w.n_text else None)
 

@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TOL, make_inputs, upload_decode
+from gpu_helpers import TOL, make_inputs, stored_u, upload_decode
 from oracle.decode import band_mask, decode_ref, select_top
 from rank_compressed_kv_ap_amd import workloads as wl
 
@@ -42,7 +42,7 @@ def _weight_rtol(w, s, q):
     if w.storage == "f32":
         return np.full(w.n_q_heads, 1e-4)
     d, G = w.head_dim, w.n_q_heads // w.n_kv_heads
-    Uk = np.asarray(s["U_k"], np.float64)
+    Uk = np.asarray(stored_u(w, s["U_k"]), np.float64)
     Bk = np.asarray(s["B_k"], np.float64)
     out = np.zeros(w.n_q_heads)
     for h in range(w.n_q_heads):
@@ -67,7 +67,8 @@ def _oracle_with_sets(w, s, q, sets):
     keys = np.zeros((w.n_q_heads, w.n_tokens))
     for h in range(w.n_q_heads):
         keys[h, sets[h]] = 1.0
-    return decode_ref(s["U_k"], s["B_k"], s["U_v"], s["B_v"], q, w.n_kv_heads, w.head_dim,
+    return decode_ref(stored_u(w, s["U_k"]), s["B_k"], stored_u(w, s["U_v"]), s["B_v"], q,
+                      w.n_kv_heads, w.head_dim,
                       w.r_lo, w.top_k, w.scale, s["text_k"] if w.n_text else None,
                       s["text_v"] if w.n_text else None, select_keys=keys)
 
@@ -93,7 +94,8 @@ def _run(gpu_lib, w, mode, alpha, steps, n_distinct=None, seed=5):
         for b in range(len(seqs)):
             s = seqs[b]
             if t == 0:
-                plain = decode_ref(s["U_k"], s["B_k"], s["U_v"], s["B_v"], qs[t][b], w.n_kv_heads,
+                plain = decode_ref(stored_u(w, s["U_k"]), s["B_k"], stored_u(w, s["U_v"]), s["B_v"],
+                                   qs[t][b], w.n_kv_heads,
                                    w.head_dim, w.r_lo, k, w.scale, s["text_k"] if w.n_text else None,
                                    s["text_v"] if w.n_text else None)
                 for h in range(Hq):
