@@ -50,6 +50,9 @@ def parse():
                     help="which tokens get full rank: the current low-rank logit (default), or "
                          "the moving average of past attention per token or per (head, token)")
     ap.add_argument("--ema-alpha", type=float, default=0.9)
+    ap.add_argument("--storage", default=None, choices=["int4"],
+                    help="int4: the workload with 4-bit token factors (U codes + block scales; B, "
+                         "K, V and text in bf16)")
     ap.add_argument("--no-compress", action="store_true")
     ap.add_argument("--compress-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -67,12 +70,14 @@ def kernel_bytes(w, select="logit"):
     moving-average selector the importance state (fp32, per token or per (head, token))
     is read by the selection and read + written by the update; the per-step logits the
     update consumes are an intermediate and are not counted."""
-    s = 2 if w.storage == "bf16" else 4
+    s = 4 if w.storage == "f32" else 2
     W, r, N, T = w.width, w.rank, w.n_tokens, w.n_text
     qb = 4 * w.n_q_heads * w.head_dim
+    # one token factor: 4-bit codes plus a bf16 scale per (32-token block, column)
+    u = N * r // 2 + (N + 31) // 32 * r * 2 if w.storage == "int4" else s * N * r
     k = {
         "select": s * r * W + qb,                 # B_k, q   (U_k's low panels are re-read, not counted)
-        "attn": s * 2 * N * r,                    # U_k, U_v
+        "attn": 2 * u,                            # U_k, U_v
         "combine": s * r * W + s * 2 * T * W + qb,  # B_v, text K/V, out
     }
     if select != "logit":
@@ -86,7 +91,7 @@ def kernel_bytes(w, select="logit"):
 def compress_bytes(w):
     """Algorithmic bytes of one ap_compress/ap_recompress over the batch: 2q + 2
     passes over every K and V matrix (A Omega, q times A^T Q and A Q~, A^T Q)."""
-    s = 2 if w.storage == "bf16" else 4
+    s = 4 if w.storage == "f32" else 2
     return (2 * w.power_iters + 2) * 2 * w.batch * w.n_tokens * w.width * s
 
 
@@ -183,9 +188,13 @@ def main():
     from rank_compressed_kv_ap_amd import workloads as wl
 
     w = wl.WORKLOADS[args.cfg]
+    if args.storage:
+        w = w.replace(storage=args.storage)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    dt = torch.bfloat16 if w.storage == "bf16" else torch.float32
+    dt = torch.float32 if w.storage == "f32" else torch.bfloat16      # B, text
+    du = torch.bfloat16 if w.storage == "bf16" else torch.float32     # U handed to set_factors
+    st_arg = "int4" if w.storage == "int4" else dt
     B = w.batch
 
     # ---- inputs: S distinct seeded sequences tiled over the batch
@@ -201,8 +210,8 @@ def main():
     caches, qs, texts = [], [], []
     for _ in range(R):
         c = binding.compress(None, None, batch=B, n_tokens=w.n_tokens, n_kv_heads=w.n_kv_heads,
-                             n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=w.rank, storage=dt)
-        c.set_factors(stack("U_k", dt), stack("B_k", dt), stack("U_v", dt), stack("B_v", dt))
+                             n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=w.rank, storage=st_arg)
+        c.set_factors(stack("U_k", du), stack("B_k", dt), stack("U_v", du), stack("B_v", dt))
         caches.append(c)
         qs.append(stack("q", torch.float32))
         texts.append((stack("text_k", dt), stack("text_v", dt)) if w.n_text else (None, None))
@@ -283,7 +292,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.storage == "bf16" else "f32",
+        "dtype": "f32" if w.storage == "f32" else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "n_tokens": w.n_tokens, "n_text": w.n_text,
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
@@ -315,13 +324,14 @@ def main():
 def compress_leg(w, reps, binding, wl, np, torch):
     """ap_recompress of the whole batch (2 distinct sequences tiled), HIP events on
     the launch stream; the first call (workspace pool warm-up) is not timed."""
-    dt = torch.bfloat16 if w.storage == "bf16" else torch.float32
+    dt = torch.float32 if w.storage == "f32" else torch.bfloat16
     S = min(w.batch, 2)
     idx = torch.tensor([b % S for b in range(w.batch)], device="cuda")
     k = torch.from_numpy(np.stack([wl.gen_kv(w, b, 0) for b in range(S)])).to(dt).cuda()[idx].contiguous()
     v = torch.from_numpy(np.stack([wl.gen_kv(w, b, 1) for b in range(S)])).to(dt).cuda()[idx].contiguous()
     c = binding.compress(k, v, batch=w.batch, n_tokens=w.n_tokens, n_kv_heads=w.n_kv_heads,
-                         n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=w.rank, storage=dt,
+                         n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=w.rank,
+                         storage="int4" if w.storage == "int4" else dt,
                          oversample=w.oversample, power_iters=w.power_iters, seed=1)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -344,6 +354,9 @@ def cpu_baseline(w, seqs, budget_s):
     from threadpoolctl import threadpool_info
 
     from oracle.decode import decode_ref
+    from oracle.quant import quantize_dequant_u4
+    if w.storage == "int4":   # the oracle attends over the values a 4-bit cache stores
+        seqs = [dict(s, U_k=quantize_dequant_u4(s["U_k"]), U_v=quantize_dequant_u4(s["U_v"])) for s in seqs]
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     done, t0 = 0, time.perf_counter()
     while done == 0 or (time.perf_counter() - t0 < budget_s and done < 4096):

@@ -306,6 +306,8 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
     S = ceil_div(512, dm.B);
     S = std::min(S, std::max(1, dm.nblk / 5));
   }
+  // 4-bit codes: a workgroup stages the block scales of its tokens in LDS (<= 64 blocks)
+  if (dm.storage == AP_INT4) S = std::max(S, ceil_div(dm.nblk, 64));
   S = std::max(1, std::min(S, dm.S_cap));
   const int CB = ceil_div(dm.nblk, S);
   S = ceil_div(dm.nblk, CB);

@@ -30,31 +30,20 @@
 namespace ap {
 
 // ================================================================ k_attn
-// Each wavefront walks its 32-token blocks with the next block's U_k / U_v tiles and
-// selection words already in flight (double buffering), and updates the online
-// softmax per 16-token half so few values stay live.  The latent query is rounded
+// Each wavefront walks its 32-token blocks with the next blocks' U_k / U_v tiles and
+// selection words already in flight (a ring of 2-4 stages, as deep as the registers
+// allow), and updates the online softmax per 16-token half so few values stay live.  The latent query is rounded
 // once to bf16 here (the selection kernel keeps it split for exact ranking); the
 // rounding moves a score by about 2^-9 of its size, far inside the output tolerance.
 template <class T, int NP, int HT>
 __device__ __forceinline__ void attn_load(const T* __restrict__ Uk, const T* __restrict__ Uv,
-                                          const bf16_t* __restrict__ Usc,
                                           const uint32_t* __restrict__ mask, int b, int blk,
                                           int nblk, int Hq, int lane, LaneTile<T> (&uk)[NP],
-                                          LaneTile<T> (&uv)[NP], uint32_t (&mw)[HT],
-                                          uint2 (&scl)[2][NP]) {
+                                          LaneTile<T> (&uv)[NP], uint32_t (&mw)[HT]) {
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     uk[p].load(tile_ptr(Uk, tile_base(b, p, blk, NP, nblk)), lane);
     uv[p].load(tile_ptr(Uv, tile_base(b, p, blk, NP, nblk)), lane);
-  }
-  if constexpr (std::is_same<T, i4_t>::value) {
-    // block scales of this lane's columns 16p + 4(l/16) + e, K row then V row
-    const bf16_t* row = Usc + ((size_t)b * nblk + blk) * 2 * (16 * NP) + (lane >> 4) * 4 * NP;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      scl[0][p] = *reinterpret_cast<const uint2*>(row + 4 * p);
-      scl[1][p] = *reinterpret_cast<const uint2*>(row + 16 * NP + 4 * p);
-    }
   }
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -68,7 +57,9 @@ __device__ __forceinline__ void attn_load(const T* __restrict__ Uk, const T* __r
 // expanded values as bf16)
 template <class T>
 constexpr int kAttnElemRegBytes = sizeof(T) == 1 ? 2 : static_cast<int>(sizeof(T));
-template <class T, int NP, int HT>
+// PLT > 0: r_lo = 16 * PLT, so which panels hold low-rank columns is known at compile
+// time and the per-panel MFMAs need no branches; PLT = 0: any r_lo, tested at run time.
+template <class T, int NP, int HT, int PLT>
 __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1) void k_attn(
     const T* __restrict__ Uk, const T* __restrict__ Uv, const bf16_t* __restrict__ Usc,
     const float* __restrict__ qt, const uint32_t* __restrict__ mask, float* __restrict__ part_z,
@@ -86,6 +77,9 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int blk0 = s * CB, blk1 = min(nblk, blk0 + CB);
+  // panels wholly below r_lo, and wholly at or above it (one panel may straddle)
+  auto lo_panel = [&](int p) { return PLT > 0 ? p < PLT : 16 * p + 16 <= r_lo; };
+  auto hi_panel = [&](int p) { return PLT > 0 ? p >= PLT : 16 * p >= r_lo; };
 
   // latent-query operands: panel p, head tile ht, this lane's 4 columns 16p+4lg+e.
   // Rows of padded heads are loaded too (the buffer holds them) and zeroed after, so
@@ -128,18 +122,41 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
     for (int p = 0; p < NP; ++p) Z[p][ht] = v4f{0, 0, 0, 0};
   }
 
-  LaneTile<T> uk[NP], uv[NP];
-  uint32_t mw[HT];
-  uint2 ssc[2][NP];   // 4-bit codes: this block's K and V scales of the lane's columns
-  int blk = blk0 + wave;
-  if (blk < blk1) attn_load<T, NP, HT>(Uk, Uv, Usc, mask, b, blk, nblk, Hq, lane, uk, uv, mw, ssc);
-  for (; blk < blk1; blk += 4) {
-    LaneTile<T> nk[NP], nv[NP];
-    uint32_t nmw[HT];
-    uint2 nsc[2][NP];
-    const bool more = blk + 4 < blk1;
-    if (more) attn_load<T, NP, HT>(Uk, Uv, Usc, mask, b, blk + 4, nblk, Hq, lane, nk, nv, nmw, nsc);
+  // Prefetch ring: each wavefront walks its blocks (blk0 + wave + 4i) with the next
+  // PD - 1 blocks' tiles and selection words in flight; loads past the wavefront's last
+  // block repeat that block (an L2 hit) so that every load is unconditional and the
+  // wait before each block counts exactly the PD - 1 younger stages.
+  constexpr int PD = U4 ? 4 : (BF && NP * HT <= 8 && NP <= 5 ? 3 : 2);
+  LaneTile<T> rk[PD][NP], rv[PD][NP];
+  uint32_t rm[PD][HT];
+  const int first = blk0 + wave;
+  const int nmine = first < blk1 ? (blk1 - first + 3) / 4 : 0;
+  auto bidx = [&](int i) { return min(first + 4 * i, blk1 - 1); };
+  if (nmine > 0) {
+#pragma unroll
+    for (int j = 0; j + 1 < PD; ++j)
+      attn_load<T, NP, HT>(Uk, Uv, mask, b, bidx(j), nblk, Hq, lane, rk[j], rv[j], rm[j]);
+  }
+  // 4-bit codes: this workgroup's block scales, [block][K row, V row] as bf16 pairs
+  [[maybe_unused]] uint32_t* ssl = reinterpret_cast<uint32_t*>(smem_f + 4 * HP * ZS + 8 * HP);
+  if constexpr (U4) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(Usc) + ((size_t)b * nblk + blk0) * RP;
+    for (int i = tid; i < (blk1 - blk0) * RP; i += 256) ssl[i] = src[i];
+    __syncthreads();
+  }
+
+  auto process = [&](const LaneTile<T> (&uk)[NP], const LaneTile<T> (&uv)[NP],
+                     const uint32_t (&mw)[HT], int blk) {
     const bool tail = (blk + 1) * kBlockTok > N;
+    [[maybe_unused]] uint2 ssc[2][NP];   // 4-bit codes: K and V scales of the lane's columns
+    if constexpr (U4) {
+      const uint32_t* row = ssl + (blk - blk0) * RP + lg * 2 * NP;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        ssc[0][p] = *reinterpret_cast<const uint2*>(row + 2 * p);
+        ssc[1][p] = *reinterpret_cast<const uint2*>(row + RP / 2 + 2 * p);
+      }
+    }
 
     if constexpr (BF) {
       // bf16: one 32-token step per head tile.  Scores per 16-token half, one column
@@ -177,9 +194,9 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
             } else {
               a = uk[p].half(hf);
             }
-            if (16 * p + 16 <= r_lo) {
+            if (lo_panel(p)) {
               slo[hf] = mfma_bf16(a, qb[p], slo[hf]);
-            } else if (16 * p >= r_lo) {
+            } else if (hi_panel(p)) {
               shi[hf] = mfma_bf16(a, qb[p], shi[hf]);
             } else {
               v4s ql = qb[p], qh = qb[p];
@@ -198,9 +215,9 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
           v4f clo = v4f{0, 0, 0, 0}, chi = v4f{0, 0, 0, 0};
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
-            if (16 * p + 16 <= r_lo) {
+            if (lo_panel(p)) {
               clo = mfma_bf16(an, qb[p], clo);
-            } else if (16 * p >= r_lo) {
+            } else if (hi_panel(p)) {
               chi = mfma_bf16(an, qb[p], chi);
             } else {
               v4s ql = qb[p], qh = qb[p];
@@ -247,7 +264,7 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
         bm = column_max4(bm);
         const float mn = fmaxf(m[ht], bm);
         if (__ballot(mn > m[ht])) {   // rescale only when some running max grew
-          const float alpha = exp2f(m[ht] - mn);
+          const float alpha = hw_exp2(m[ht] - mn);
           lsum[ht] *= alpha;
 #pragma unroll
           for (int p = 0; p < NP; ++p) Z[p][ht] *= alpha;
@@ -257,7 +274,7 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
         uint32_t pa[4], ph[4];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          pv[j] = exp2f(sc[j] - mn);
+          pv[j] = hw_exp2(sc[j] - mn);
           lsum[ht] += pv[j];
         }
 #pragma unroll
@@ -277,9 +294,9 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
           for (int p = 0; p < NP; ++p) {
             const v8bf a8 = __builtin_bit_cast(v8bf, uv[p].deq());
             v4f D;
-            if (16 * p + 16 <= r_lo) {
+            if (lo_panel(p)) {
               D = mfma_bf16_k32(a8, pa8, cpa);
-            } else if (16 * p >= r_lo) {
+            } else if (hi_panel(p)) {
               D = mfma_bf16_k32(a8, ph8, cph);
             } else {
               const v4f D1 = mfma_bf16_k32(a8, pa8, cpa), D2 = mfma_bf16_k32(a8, ph8, cph);
@@ -295,9 +312,9 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           const v8bf a8 = __builtin_bit_cast(v8bf, uv[p].raw);
-          if (16 * p + 16 <= r_lo) {
+          if (lo_panel(p)) {
             Z[p][ht] = mfma_bf16_k32(a8, pa8, Z[p][ht]);
-          } else if (16 * p >= r_lo) {
+          } else if (hi_panel(p)) {
             Z[p][ht] = mfma_bf16_k32(a8, ph8, Z[p][ht]);
           } else {
             const bool lo_row = 16 * p + l16 < r_lo;  // this lane's A row is latent column 16p+l16
@@ -318,9 +335,9 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
           for (int p = 0; p < NP; ++p) {
             if constexpr (BF) {
               const v4s a = uk[p].half(hf);
-              if (16 * p + 16 <= r_lo) {
+              if (lo_panel(p)) {
                 slo = mfma_bf16(a, qop[p][ht], slo);
-              } else if (16 * p >= r_lo) {
+              } else if (hi_panel(p)) {
                 shi = mfma_bf16(a, qop[p][ht], shi);
               } else {
                 v4s ql = qop[p][ht], qh = qop[p][ht];
@@ -332,9 +349,9 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
                 shi = mfma_bf16(a, qh, shi);
               }
             } else {
-              if (16 * p + 16 <= r_lo) {
+              if (lo_panel(p)) {
                 slo = score_mma(uk[p], hf, qop[p][ht], slo);
-              } else if (16 * p >= r_lo) {
+              } else if (hi_panel(p)) {
                 shi = score_mma(uk[p], hf, qop[p][ht], shi);
               } else {
                 const int cl = 16 * p + 4 * lg;
@@ -370,7 +387,7 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
           bm = wave_max_xor(bm, 32);
           const float mn = fmaxf(m[ht], bm);
           if (__ballot(mn > m[ht])) {   // rescale only when some running max grew
-            const float alpha = exp2f(m[ht] - mn);
+            const float alpha = hw_exp2(m[ht] - mn);
             lsum[ht] *= alpha;
   #pragma unroll
             for (int p = 0; p < NP; ++p) Z[p][ht] *= alpha;
@@ -379,7 +396,7 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
           float pv[4], phv[4];
   #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const float e = exp2f(sc[t] - mn);
+            const float e = hw_exp2(sc[t] - mn);
             lsum[ht] += e;
             pv[t] = e;
             phv[t] = bit[t] ? e : 0.f;
@@ -389,9 +406,9 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
           ph.set(phv);
   #pragma unroll
           for (int p = 0; p < NP; ++p) {
-            if (16 * p + 16 <= r_lo) {
+            if (lo_panel(p)) {
               Z[p][ht] = value_mma(uv[p], hf, true, pa, Z[p][ht]);
-            } else if (16 * p >= r_lo) {
+            } else if (hi_panel(p)) {
               Z[p][ht] = value_mma(uv[p], hf, true, ph, Z[p][ht]);
             } else {
               const bool lo_row = 16 * p + l16 < r_lo;  // this lane's A row is latent column 16p+l16
@@ -402,20 +419,16 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
         }
       }
     }
-    if (more) {
+  };
+
+  for (int i0 = 0; i0 < nmine; i0 += PD) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        uk[p] = nk[p];
-        uv[p] = nv[p];
-      }
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) mw[ht] = nmw[ht];
-      if constexpr (U4) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          ssc[0][p] = nsc[0][p];
-          ssc[1][p] = nsc[1][p];
-        }
+    for (int j = 0; j < PD; ++j) {
+      const int i = i0 + j;
+      if (i < nmine) {
+        const int ld = (j + PD - 1) % PD;
+        attn_load<T, NP, HT>(Uk, Uv, mask, b, bidx(i + PD - 1), nblk, Hq, lane, rk[ld], rv[ld], rm[ld]);
+        process(rk[j], rv[j], rm[j], first + 4 * i);
       }
     }
   }
@@ -715,42 +728,62 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
 }
 
 // ================================================================ launchers
-template <class T, int NP, int HT>
+template <class T, int NP, int HT, int PLT>
 static hipError_t launch_attn_t(const ap_cache* c, int r_lo, float sl2, int S, int CB, float* ema_s, hipStream_t st,
                                 const KernelEvents& ev) {
   const Dims& dm = c->dm;
   constexpr int RP = NP * 16, HP = HT * 16;
-  const size_t lds = (size_t)(4 * HP * (RP + 1) + 8 * HP) * sizeof(float);
+  // merge buffers, then (4-bit codes) the workgroup's block scales
+  const size_t lds = (size_t)(4 * HP * (RP + 1) + 8 * HP) * sizeof(float) +
+                     (std::is_same<T, i4_t>::value ? (size_t)CB * RP * 4 : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<T, NP, HT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<T, NP, HT, PLT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipExtLaunchKernelGGL((k_attn<T, NP, HT>), dim3(dm.B * S), dim3(256), lds, st, ev.start, ev.stop, 0,
+  hipExtLaunchKernelGGL((k_attn<T, NP, HT, PLT>), dim3(dm.B * S), dim3(256), lds, st, ev.start, ev.stop, 0,
                      static_cast<const T*>(c->Uk), static_cast<const T*>(c->Uv),
                      reinterpret_cast<const bf16_t*>(c->Usc), c->qt, c->mask,
                      c->part_z, c->part_ml, ema_s, dm.N, dm.nblk, CB, S, dm.Hq, r_lo, sl2);
   return hipGetLastError();
 }
 
+// bf16 / 4-bit factors with r <= 64 and r_lo a multiple of 16: the compile-time panel split
+template <class T, int NP, int HT>
+static hipError_t launch_attn_r(const ap_cache* c, int r_lo, float sl2, int S, int CB, float* ema_s,
+                                hipStream_t st, const KernelEvents& ev) {
+  if constexpr (!std::is_same<T, float>::value && NP <= 4) {
+    if (r_lo % 16 == 0) {
+      switch (r_lo / 16) {
+        case 1: return launch_attn_t<T, NP, HT, 1>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+        case 2: if constexpr (NP >= 2) return launch_attn_t<T, NP, HT, 2>(c, r_lo, sl2, S, CB, ema_s, st, ev); break;
+        case 3: if constexpr (NP >= 3) return launch_attn_t<T, NP, HT, 3>(c, r_lo, sl2, S, CB, ema_s, st, ev); break;
+        case 4: if constexpr (NP >= 4) return launch_attn_t<T, NP, HT, 4>(c, r_lo, sl2, S, CB, ema_s, st, ev); break;
+        default: break;
+      }
+    }
+  }
+  return launch_attn_t<T, NP, HT, 0>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+}
+
 template <class T, int HT>
 static hipError_t dispatch_np(const ap_cache* c, int r_lo, float sl2, int S, int CB, float* ema_s, hipStream_t st,
                               const KernelEvents& ev) {
   switch (c->dm.NP) {
-    case 1: return launch_attn_t<T, 1, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
-    case 2: return launch_attn_t<T, 2, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
-    case 3: return launch_attn_t<T, 3, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
-    case 4: return launch_attn_t<T, 4, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+    case 1: return launch_attn_r<T, 1, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+    case 2: return launch_attn_r<T, 2, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+    case 3: return launch_attn_r<T, 3, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+    case 4: return launch_attn_r<T, 4, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
     default: break;
   }
   if constexpr (HT <= 2) {
     switch (c->dm.NP) {
-      case 5: return launch_attn_t<T, 5, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
-      case 6: return launch_attn_t<T, 6, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
-      case 7: return launch_attn_t<T, 7, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
-      case 8: return launch_attn_t<T, 8, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+      case 5: return launch_attn_r<T, 5, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+      case 6: return launch_attn_r<T, 6, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+      case 7: return launch_attn_r<T, 7, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
+      case 8: return launch_attn_r<T, 8, HT>(c, r_lo, sl2, S, CB, ema_s, st, ev);
       default: break;
     }
   }

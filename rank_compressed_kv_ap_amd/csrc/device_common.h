@@ -46,6 +46,10 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// 2^x with the hardware v_exp_f32 alone (exp2f adds a range check and rescale for
+// results below 2^-126, which softmax weights can ignore): exp2(-inf) = 0.
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------- MFMA tiles
 // 16x16 output tile D[i][j]: lane l holds D[4*(l/16) + t][l%16], t = 0..3.
 // bf16 16x16x16: lane l supplies A[l%16][4*(l/16) + e] and B[4*(l/16) + e][l%16], e = 0..3.

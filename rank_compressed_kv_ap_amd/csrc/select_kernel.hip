@@ -949,7 +949,7 @@ __device__ __forceinline__ void select_body(
       float lp = 0.f;
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
-        const float pv = exp2f(sc[i] - Mh);   // -inf -> 0
+        const float pv = hw_exp2(sc[i] - Mh);   // -inf -> 0
         sc[i] = pv;
         lp += pv;
       }
@@ -959,7 +959,7 @@ __device__ __forceinline__ void select_body(
         const float M = key_score(hmx[wave]);
         float lt = 0.f;
         for (int t = lane; t < Tn; t += 64) {
-          const float pv = exp2f(sts[wave * Tn + t] - M);
+          const float pv = hw_exp2(sts[wave * Tn + t] - M);
           sts[wave * Tn + t] = pv;
           lt += pv;
         }
