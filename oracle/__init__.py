@@ -16,7 +16,8 @@ Modules
   jacobi      one-sided Jacobi SVD                        [es §2.A] [fr §2.A] [de §2.A]
   factorize   randomized range-finding + Jacobi core      (compression, [fr §2.A])
   decode      explicit mixed-rank decompression + softmax ([es §2.B] [fr §2.B] [de §2.B]),
-              and the moving-average importance selector over several steps
+              the moving-average importance selector over several steps, and
+              decode over several separately factored segments plus dense tokens
   brute       the same decode in pure-Python loops        (tiny inputs only)
   quant       4-bit token factors: codes and block scales  [es §3] [fr §4] [de §3] [de §4]
   accounting  storage / FLOP bookkeeping                  [fr §2.A] [es §4] [de §4]
@@ -28,12 +29,13 @@ listed as "parity unpinned" in the module that holds them.
 """
 from .jacobi import jacobi_svd
 from .factorize import orth_mgs2, rsvd, round_to_storage
-from .decode import decode_ref, decode_ema_steps, select_top, band_mask, recon_error
+from .decode import decode_ref, decode_ema_steps, decode_segments, select_top, band_mask, recon_error
 from .accounting import factored_bytes, dense_bytes, decompression_flop_fraction
 from .quant import quantize_u4, dequant_u4, quantize_dequant_u4
 
 __all__ = [
     "jacobi_svd", "orth_mgs2", "rsvd", "round_to_storage", "decode_ref", "decode_ema_steps",
+    "decode_segments",
     "select_top", "band_mask", "recon_error", "factored_bytes", "dense_bytes",
     "decompression_flop_fraction", "quantize_u4", "dequant_u4", "quantize_dequant_u4",
 ]

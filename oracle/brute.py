@@ -102,3 +102,47 @@ def decode_ema_brute(U_k, B_k, U_v, B_v, qs, n_kv_heads, head_dim, r_lo, top_k, 
         tops_all.append(tops)
         states.append([list(row) for row in imp] if per_head else list(imp))
     return outs, tops_all, states
+
+
+def decode_segments_brute(segments, q, n_kv_heads, head_dim, scale, dense_k=(), dense_v=()):
+    """Several factored segments plus dense tokens, with explicit loops: per segment and
+    head, rank its tokens by the low-rank score (its own r_lo, top_k), score each token
+    at its rank, then one softmax over every segment's tokens and the dense ones."""
+    d = head_dim
+    Hq = len(q) // d
+    G = Hq // n_kv_heads
+    out = [0.0] * (Hq * d)
+    tops = [[] for _ in segments]
+    for h in range(Hq):
+        g = h // G
+        qh = [float(q[h * d + j]) for j in range(d)]
+
+        def dot(a, b):
+            return sum(x * y for x, y in zip(a, b))
+
+        scores, values = [], []
+        for si, sg in enumerate(segments):
+            Uk, Bk, Uv, Bv = sg["U_k"], sg["B_k"], sg["U_v"], sg["B_v"]
+            r_lo, k = sg["r_lo"], sg["top_k"]
+            N, r = len(Uk), len(Bk)
+
+            def rec(U, B, n, rank):
+                return [sum(float(U[n][i]) * float(B[i][g * d + j]) for i in range(rank)) for j in range(d)]
+
+            s_lo = [scale * dot(rec(Uk, Bk, n, r_lo), qh) for n in range(N)]
+            ranked = sorted(range(N), key=lambda n: (-s_lo[n], n))
+            chosen = set(ranked[:k])
+            tops[si].append(sorted(chosen))
+            for n in range(N):
+                rank = r if n in chosen else r_lo
+                scores.append(scale * dot(rec(Uk, Bk, n, rank), qh))
+                values.append(rec(Uv, Bv, n, rank))
+        for t in range(len(dense_k)):
+            scores.append(scale * dot([float(dense_k[t][g * d + j]) for j in range(d)], qh))
+            values.append([float(dense_v[t][g * d + j]) for j in range(d)])
+        mx = max(scores)
+        w = [math.exp(s - mx) for s in scores]
+        z = sum(w)
+        for j in range(d):
+            out[h * d + j] = sum(w[i] / z * values[i][j] for i in range(len(w)))
+    return out, tops

@@ -149,3 +149,69 @@ def recon_error(A, U, B) -> float:
     A = np.asarray(A, np.float64)
     R = A - np.asarray(U, np.float64) @ np.asarray(B, np.float64)
     return float(np.linalg.norm(R) / np.linalg.norm(A))
+
+
+def decode_segments(segments, q, n_kv_heads: int, head_dim: int, scale: float,
+                    dense_k=None, dense_v=None):
+    """One decode step over several separately factored segments plus dense tokens.
+
+    [es §2.A], [fr §2.A "Traitement séparé"], [de §2.A "Optimierung"]: visual and
+    text tokens are factored by separate SVDs.  Each segment here is a dict with its
+    own factors U_k, B_k, U_v, B_v (its own rank) and its own reduced rank r_lo and
+    full-rank count top_k; the attention-aware decompression of [fr §2.B] is applied
+    inside each segment (its top_k tokens by its own low-rank score, per query head,
+    ties to the lower index).  Dense tokens (dense_k, dense_v, e.g. tokens appended
+    during decoding and not yet factored) join at full precision.
+
+    Written as the plain definition: every segment is decompressed explicitly, the
+    keys and values of all segments and the dense tokens are concatenated, and one
+    dense softmax attention runs over them.  Returns dict(out [Hq*d], top: per segment
+    [Hq][top_k] ascending ids, p: per segment [Hq][N_seg] attention weights).
+    """
+    q = np.asarray(q, np.float64)
+    d = head_dim
+    Hq = q.shape[0] // d
+    G = Hq // n_kv_heads
+    segs = [{k: (np.asarray(v, np.float64) if k in ("U_k", "B_k", "U_v", "B_v") else v)
+             for k, v in s.items()} for s in segments]
+    T = 0 if dense_k is None else np.asarray(dense_k).shape[0]
+    dk = np.asarray(dense_k, np.float64) if T else None
+    dv = np.asarray(dense_v, np.float64) if T else None
+    out = np.zeros(Hq * d)
+    tops = [[] for _ in segs]
+    ps = [[] for _ in segs]
+    for h in range(Hq):
+        g = h // G
+        cols = slice(g * d, (g + 1) * d)
+        qh = q[h * d:(h + 1) * d]
+        K_parts, V_parts, sizes = [], [], []
+        for i, s in enumerate(segs):
+            r_lo, k = s["r_lo"], s["top_k"]
+            Uk, Bk, Uv, Bv = s["U_k"], s["B_k"], s["U_v"], s["B_v"]
+            K_lo = Uk[:, :r_lo] @ Bk[:r_lo, cols]
+            top = select_top(scale * (K_lo @ qh), k)
+            rank_of = np.full(Uk.shape[0], r_lo)
+            rank_of[top] = Uk.shape[1]
+            # explicit decompression of every token at its own rank
+            K_hat = np.stack([Uk[n, :rank_of[n]] @ Bk[:rank_of[n], cols] for n in range(Uk.shape[0])])
+            V_hat = np.stack([Uv[n, :rank_of[n]] @ Bv[:rank_of[n], cols] for n in range(Uv.shape[0])])
+            K_parts.append(K_hat)
+            V_parts.append(V_hat)
+            sizes.append(Uk.shape[0])
+            tops[i].append(top)
+        if T:
+            K_parts.append(dk[:, cols])
+            V_parts.append(dv[:, cols])
+        K_all = np.concatenate(K_parts)
+        V_all = np.concatenate(V_parts)
+        s_all = scale * (K_all @ qh)
+        p = np.exp(s_all - s_all.max())
+        p /= p.sum()
+        out[h * d:(h + 1) * d] = p @ V_all
+        off = 0
+        for i, n in enumerate(sizes):
+            ps[i].append(p[off:off + n])
+            off += n
+    return dict(out=out,
+                top=[np.array(t, dtype=np.int64).reshape(Hq, s["top_k"]) for t, s in zip(tops, segs)],
+                p=[np.array(x) for x in ps])

@@ -169,3 +169,38 @@ def test_real_quantizer_passes_pins():
 ])
 def test_quantizer_mutants_are_caught(old, new):
     assert not _quant_pins_ok(_mutant(qnt, old, new))
+
+
+# ---------------------------------------------------------------- segments
+def _segments_pin_ok(mod):
+    from oracle.brute import decode_segments_brute
+    from test_oracle_pins import _seg_case
+    try:
+        for seed, T in ((80, 2), (82, 5)):
+            segs, Kd, Vd, q = _seg_case(seed, T=T)
+            res = mod.decode_segments(segs, q, 2, 3, 0.6, Kd, Vd)
+            lsegs = [{k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in s.items()} for s in segs]
+            out, tops = decode_segments_brute(lsegs, q.tolist(), 2, 3, 0.6, Kd.tolist(), Vd.tolist())
+            if np.max(np.abs(res["out"] - np.array(out))) > 1e-12:
+                return False
+            if any([list(t) for t in res["top"][i]] != tops[i] for i in range(len(segs))):
+                return False
+    except Exception:
+        return False
+    return True
+
+
+def test_real_segments_pass_brute_pin():
+    assert _segments_pin_ok(dec)
+
+
+@pytest.mark.parametrize("old,new", [
+    ('r_lo, k = s["r_lo"], s["top_k"]', 'r_lo, k = segs[0]["r_lo"], s["top_k"]'),      # one r_lo for all
+    ("            K_parts.append(dk[:, cols])\n            V_parts.append(dv[:, cols])",
+     "            K_parts.append(dk[:, cols])\n            V_parts.append(0 * dv[:, cols])"),  # dense values dropped
+    ("top = select_top(scale * (K_lo @ qh), k)",
+     "top = select_top(scale * ((Uk @ Bk[:, cols]) @ qh), k)"),                          # ranked at full rank
+    ("rank_of[top] = Uk.shape[1]", "rank_of[top] = Uk.shape[1] - 1"),                  # one rank short
+])
+def test_segments_mutants_are_caught(old, new):
+    assert not _segments_pin_ok(_mutant(dec, old, new))

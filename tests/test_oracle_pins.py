@@ -517,3 +517,79 @@ def test_p14_quant_scales_are_per_block_and_column():
     c3, s3 = quantize_u4(U3)
     assert s3[0, 0] != scales[0, 0] and np.array_equal(s3[1:], scales[1:])
     assert np.array_equal(c3[32:], codes[32:])
+
+
+# ------------------------------------------------------------------ P15
+# Decode over separately factored segments (text factored apart from the visual tokens)
+# plus dense appended tokens (oracle.decode.decode_segments).
+from oracle.brute import decode_segments_brute
+from oracle.decode import decode_segments
+
+
+def _seg_case(seed, sizes=((9, 4, 2, 3), (6, 3, 1, 2)), Hkv=2, Hq=4, d=3, T=2):
+    g = np.random.default_rng(seed)
+    W = Hkv * d
+    segs = []
+    for N, r, r_lo, k in sizes:
+        Uk, Uv = g.standard_normal((N, r)), g.standard_normal((N, r))
+        Bk, Bv = g.standard_normal((r, W)), g.standard_normal((r, W))
+        segs.append(dict(U_k=Uk, B_k=Bk, U_v=Uv, B_v=Bv, r_lo=r_lo, top_k=k))
+    Kd, Vd = g.standard_normal((T, W)), g.standard_normal((T, W))
+    q = g.standard_normal(Hq * d)
+    return segs, Kd, Vd, q
+
+
+@pytest.mark.parametrize("seed,T", [(80, 2), (81, 0), (82, 5)])
+def test_p15_segments_brute_force(seed, T):
+    segs, Kd, Vd, q = _seg_case(seed, T=T)
+    res = decode_segments(segs, q, 2, 3, 0.6, Kd if T else None, Vd if T else None)
+    lsegs = [{k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in s.items()} for s in segs]
+    out, tops = decode_segments_brute(lsegs, q.tolist(), 2, 3, 0.6,
+                                      Kd.tolist() if T else (), Vd.tolist() if T else ())
+    assert np.max(np.abs(res["out"] - np.array(out))) <= 1e-12
+    for i in range(len(segs)):
+        assert [list(t) for t in res["top"][i]] == tops[i]
+
+
+def test_p15_one_segment_equals_decode_ref():
+    # the single-segment decode (latent-space formulation in decode_ref) and the
+    # segment list (explicit per-token decompression, concatenation) agree
+    segs, Kd, Vd, q = _seg_case(83, sizes=((11, 5, 2, 4),))
+    s = segs[0]
+    a = decode_segments(segs, q, 2, 3, 0.7, Kd, Vd)
+    b = decode_ref(s["U_k"], s["B_k"], s["U_v"], s["B_v"], q, 2, 3, 2, 4, 0.7, Kd, Vd)
+    assert np.max(np.abs(a["out"] - b["out"])) <= 1e-12
+    assert np.array_equal(a["top"][0], b["top"])
+    assert np.max(np.abs(a["p"][0] - b["p"])) <= 1e-13
+
+
+def test_p15_segment_order_does_not_matter():
+    segs, Kd, Vd, q = _seg_case(84)
+    a = decode_segments(segs, q, 2, 3, 0.6, Kd, Vd)
+    b = decode_segments(segs[::-1], q, 2, 3, 0.6, Kd, Vd)
+    assert np.max(np.abs(a["out"] - b["out"])) <= 1e-12
+    assert all(np.array_equal(x, y) for x, y in zip(a["top"], b["top"][::-1]))
+
+
+def test_p15_full_rank_segments_are_dense_attention():
+    # r_lo = r in every segment: attention over the stacked products U B and the dense
+    # tokens, whatever top_k is
+    segs, Kd, Vd, q = _seg_case(85, sizes=((7, 3, 3, 1), (5, 4, 4, 0)))
+    res = decode_segments(segs, q, 2, 3, 0.5, Kd, Vd)
+    K = np.concatenate([s["U_k"] @ s["B_k"] for s in segs] + [Kd])
+    V = np.concatenate([s["U_v"] @ s["B_v"] for s in segs] + [Vd])
+    ref = _sdpa(q, K, V, 2, 3, 0.5)
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12
+
+
+def test_p15_dense_tokens_move_into_a_full_rank_segment():
+    # a dense block equals a factored segment that reproduces it exactly (U = K, B = I
+    # restricted to the K columns is not square here, so use the exact SVD of the
+    # block at full rank, every token at full rank)
+    segs, Kd, Vd, q = _seg_case(86, T=4)
+    Uk, sk, Vk = np.linalg.svd(Kd, full_matrices=False)
+    Uv, sv, Vv = np.linalg.svd(Vd, full_matrices=False)
+    seg_d = dict(U_k=Uk * sk, B_k=Vk, U_v=Uv * sv, B_v=Vv, r_lo=len(sk), top_k=4)
+    a = decode_segments(segs, q, 2, 3, 0.6, Kd, Vd)
+    b = decode_segments(segs + [seg_d], q, 2, 3, 0.6)
+    assert np.max(np.abs(a["out"] - b["out"])) <= 1e-12
