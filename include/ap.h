@@ -181,6 +181,20 @@ typedef struct {
                             [B][N] (EMA_TOKEN) or [B][Hq][N] (EMA_HEAD)                    */
   float* ema_scratch;    /* device float32 workspace [B][Hq][N], caller-owned: the step's
                             logits; contents undefined between calls                      */
+  /* A second factored segment.  [es §2.A], [fr §2.A "Traitement séparé"], [de §2.A
+   * "Optimierung"]: text tokens are factored by their own SVD, apart from the visual
+   * ones.  text_cache: a cache of the same batch, query/KV heads and head_dim holding
+   * the text tokens' factors (its own rank, token count and storage), or NULL.  Its
+   * tokens are selected and decompressed like the visual ones, within the segment: per
+   * query head the text_top_k tokens of largest low-rank score (first text_r_lo
+   * components) at the text cache's full rank, the rest at text_r_lo.  All segments
+   * (visual, factored text, dense tokens) share one softmax.  The call writes the text
+   * cache's decode workspace, so the text cache must not be in use on another stream.
+   * The dense tokens above then serve as the tokens appended while decoding and not yet
+   * factored; re-factoring them together with the text is the caller's (ap_compress). */
+  const ap_cache* text_cache;
+  int32_t text_r_lo;     /* 1 <= text_r_lo <= the text cache's rank (when text_cache set)   */
+  int32_t text_top_k;    /* 0 <= text_top_k <= the text cache's n_tokens                    */
 } ap_decode_params;
 
 enum { AP_SELECT_LOGIT = 0, AP_SELECT_EMA_TOKEN = 1, AP_SELECT_EMA_HEAD = 2 };
@@ -203,11 +217,14 @@ enum { AP_SELECT_LOGIT = 0, AP_SELECT_EMA_TOKEN = 1, AP_SELECT_EMA_HEAD = 2 };
  *
  * q:    device [B][Hq*d] float32, caller-owned.
  * out:  device [B][Hq*d] float32, caller-owned, fully overwritten.
+ * With a factored text segment (text_cache) the visual sum above also runs over the
+ * text segment's tokens, each scored and decompressed at its own rank in that segment.
  * The call allocates nothing.  It enqueues one kernel on `stream` when splits == 0 and
  * the shape allows (bf16 factors, r <= 64, r_lo <= 32, N <= 8192, head_dim a power of
- * two multiple of 8, T <= 1024, B * ceil(Hq/4) <= 256): one workgroup per (sequence,
- * 4 query heads) then selects, attends over all tokens and projects.  Otherwise three
- * kernels: selection, split-N flash-decode, combine.
+ * two multiple of 8, T <= 1024, B * ceil(Hq/4) <= 256, no text_cache, the logit
+ * selector): one workgroup per (sequence, 4 query heads) then selects, attends over all
+ * tokens and projects.  Otherwise three kernels: selection, split-N flash-decode,
+ * combine, and three more before them for a factored text segment.
  * Errors: AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_UNSUPPORTED (r_lo or r not
  * supported by the tiling), AP_ERR_HIP.
  */
@@ -222,10 +239,11 @@ void ap_free(ap_cache* c);
  * around each of its kernels on the caller's stream (at most max_calls calls are
  * recorded; later calls are not timed).  ap_timing_read waits for the recorded events,
  * writes the summed milliseconds per kernel (index: 0 select, 1 attention, 2 combine,
- * 3 the single-kernel decode, 4 the importance-state update) and the number of timed
- * calls, and starts a new recording.  max_calls == 0 disables. */
+ * 3 the single-kernel decode, 4 the importance-state update, 5 the three kernels of the
+ * factored text segment together) and the number of timed calls, and starts a new
+ * recording.  max_calls == 0 disables. */
 enum { AP_KERNEL_SELECT = 0, AP_KERNEL_ATTN = 1, AP_KERNEL_COMBINE = 2, AP_KERNEL_DECODE = 3,
-       AP_KERNEL_EMA = 4, AP_N_KERNELS = 5 };
+       AP_KERNEL_EMA = 4, AP_KERNEL_TEXT = 5, AP_N_KERNELS = 6 };
 ap_status ap_timing_enable(ap_cache* c, int32_t max_calls);
 ap_status ap_timing_read(ap_cache* c, float* ms_per_kernel /* [AP_N_KERNELS] */, int32_t* calls);
 

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libap.so")
 AP_OK, AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_BAD_DTYPE, AP_ERR_UNSUPPORTED, \
     AP_ERR_OUT_OF_MEMORY, AP_ERR_HIP = range(7)
 AP_F32, AP_BF16, AP_INT4 = 0, 1, 2
-KERNEL_NAMES = ("select", "attn", "combine", "decode", "ema")
+KERNEL_NAMES = ("select", "attn", "combine", "decode", "ema", "text")
 
 EXPORTED = (
     "ap_compress", "ap_recompress", "ap_cache_set_factors", "ap_cache_get_factors",
@@ -44,6 +44,7 @@ class DecodeParams(ctypes.Structure):
         ("sel_out", ctypes.c_void_p), ("splits", ctypes.c_int32),
         ("select_mode", ctypes.c_int32), ("ema_alpha", ctypes.c_float), ("ema_first", ctypes.c_int32),
         ("importance", ctypes.c_void_p), ("ema_scratch", ctypes.c_void_p),
+        ("text_cache", ctypes.c_void_p), ("text_r_lo", ctypes.c_int32), ("text_top_k", ctypes.c_int32),
     ]
 
 
@@ -226,19 +227,23 @@ def decode(cache: Cache, q: torch.Tensor, *, r_lo: int, top_k: int, scale: float
            out: Optional[torch.Tensor] = None, sel_out: Optional[torch.Tensor] = None,
            splits: int = 0, select: str = "logit", ema_alpha: float = 0.0,
            ema_first: bool = False, importance: Optional[torch.Tensor] = None,
-           ema_scratch: Optional[torch.Tensor] = None) -> torch.Tensor:
+           ema_scratch: Optional[torch.Tensor] = None, text_cache: Optional["Cache"] = None,
+           text_r_lo: int = 0, text_top_k: int = 0) -> torch.Tensor:
     """ap_decode_attn: q [B, Hq*d] float32 -> out [B, Hq*d] float32.
 
     select: "logit" (current-step low-rank logit), "ema_token" or "ema_head" (moving
     average of the attention weights; importance float32 [B, N] or [B, Hq, N] is read
-    and updated in place; ema_scratch float32 [B, Hq, N] is the step's workspace)."""
+    and updated in place; ema_scratch float32 [B, Hq, N] is the step's workspace).
+    text_cache: the text tokens factored apart (a second segment, its own text_r_lo and
+    text_top_k); text_k / text_v then hold the dense tokens appended since."""
     if out is None:
         out = torch.empty_like(q)
     n_text = 0 if text_k is None else text_k.shape[1]
     p = DecodeParams(r_lo, top_k, scale, n_text, _ptr(text_k) if n_text else None,
                      _ptr(text_v) if n_text else None, _ptr(sel_out), splits,
                      SELECT_MODES[select], ema_alpha, 1 if ema_first else 0, _ptr(importance),
-                     _ptr(ema_scratch))
+                     _ptr(ema_scratch), text_cache.handle.value if text_cache is not None else None,
+                     text_r_lo, text_top_k)
     _check(lib.ap_decode_attn(cache.handle, _ptr(q), _ptr(out), ctypes.byref(p), _stream()),
            "ap_decode_attn")
     return out

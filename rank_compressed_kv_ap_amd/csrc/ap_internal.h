@@ -57,6 +57,8 @@ struct ap_cache {
   float* part_z = nullptr;    // [B][S_cap][Hq_pad][r_pad]
   float* part_ml = nullptr;   // [B][S_cap][Hq_pad][2]  (running max in log2 units, sum)
   float* ml_final = nullptr;  // [B][Hq][2] softmax max (log2 units) and sum of the last step
+  float* out_part = nullptr;  // [B][Hq][d] this cache's normalised attention output when it
+                              // serves as another cache's second (text) segment
   size_t factor_bytes = 0;
   size_t device_bytes = 0;
   hipStream_t last_stream = nullptr;
@@ -84,9 +86,12 @@ bool decode_fused_supported(const Dims& dm, int r_lo, int n_text);
 hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, int r_lo, int top_k,
                                int32_t* sel_out, int n_text, const void* text_k, const void* text_v,
                                float sl2, hipStream_t st, const KernelEvents& ev);
+// xo, xml (optional): another segment's normalised output [B][Hq][d] and its softmax
+// maximum and sum [B][Hq][2], merged as one more partial.
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float scale_log2e,
                           int S, int T, const void* text_k, const void* text_v, float* ml_out,
-                          hipStream_t st, const KernelEvents& ev);
+                          const float* xo, const float* xml, hipStream_t st,
+                          const KernelEvents& ev);
 hipError_t launch_ema_update(const ap_cache* c, const float* s, const float* ml, float* imp,
                              bool per_head, bool first, float alpha, hipStream_t st,
                              const KernelEvents& ev);

@@ -27,6 +27,22 @@ static ap_status hip_fail(hipError_t e, const char* what) {
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// N-splits of the flash-decode kernel for one cache: about two workgroups per CU, >= 5
+// token blocks each (measured best on the batch-32 LLaVA layer: 16 splits of 5-6 blocks);
+// splits > 0 is the caller's count.  Returns the split count and sets the blocks per split.
+static int split_plan(const Dims& dm, int splits, int* CB) {
+  int S = splits;
+  if (S == 0) {
+    S = ceil_div(512, dm.B);
+    S = std::min(S, std::max(1, dm.nblk / 5));
+  }
+  // 4-bit codes: a workgroup stages the block scales of its tokens in LDS (<= 64 blocks)
+  if (dm.storage == AP_INT4) S = std::max(S, ceil_div(dm.nblk, 64));
+  S = std::max(1, std::min(S, dm.S_cap));
+  *CB = ceil_div(dm.nblk, S);
+  return ceil_div(dm.nblk, *CB);
+}
+
 static ap_status validate_shape(const ap_compress_params* p) {
   if (p->storage != AP_F32 && p->storage != AP_BF16 && p->storage != AP_INT4)
     return fail(AP_ERR_BAD_DTYPE, "storage must be AP_F32, AP_BF16 or AP_INT4");
@@ -81,7 +97,8 @@ static Dims make_dims(const ap_compress_params* p) {
 }
 
 static void free_all(ap_cache* c) {
-  void* ptrs[] = {c->Uk, c->Usc, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->qt, c->mask, c->part_z, c->part_ml, c->ml_final};
+  void* ptrs[] = {c->Uk, c->Usc, c->Bk, c->Bv, c->sigma_k, c->sigma_v, c->qt, c->mask, c->part_z, c->part_ml,
+                  c->ml_final, c->out_part};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   for (hipEvent_t e : c->timing.ev) (void)hipEventDestroy(e);
@@ -105,6 +122,7 @@ static ap_status alloc_cache(ap_cache* c) {
       {reinterpret_cast<void**>(&c->part_z), (size_t)dm.B * dm.S_cap * dm.Hq_pad * dm.r_pad * 4},
       {reinterpret_cast<void**>(&c->part_ml), (size_t)dm.B * dm.S_cap * dm.Hq_pad * 2 * 4},
       {reinterpret_cast<void**>(&c->ml_final), (size_t)dm.B * dm.Hq * 2 * 4},
+      {reinterpret_cast<void**>(&c->out_part), (size_t)dm.B * dm.Hq * dm.d * 4},
   };
   size_t total = 0;
   for (const Req& r : reqs) {
@@ -292,6 +310,16 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
   const bool ema = p->select_mode != AP_SELECT_LOGIT;
   if (ema && !(p->ema_alpha >= 0.f && p->ema_alpha < 1.f))
     return fail(AP_ERR_BAD_SHAPE, "ema_alpha must satisfy 0 <= alpha < 1");
+  ap_cache* tc = const_cast<ap_cache*>(p->text_cache);   // its workspace is written
+  if (tc) {
+    const Dims& dt = tc->dm;
+    if (tc == c) return fail(AP_ERR_BAD_SHAPE, "text_cache must be another cache");
+    if (dt.B != dm.B || dt.Hq != dm.Hq || dt.Hkv != dm.Hkv || dt.d != dm.d)
+      return fail(AP_ERR_BAD_SHAPE, "text_cache must have the same batch, query/KV heads and head_dim");
+    if (p->text_r_lo < 1 || p->text_r_lo > dt.r) return fail(AP_ERR_BAD_SHAPE, "need 1 <= text_r_lo <= text rank");
+    if (p->text_top_k < 0 || p->text_top_k > dt.N)
+      return fail(AP_ERR_BAD_SHAPE, "need 0 <= text_top_k <= text n_tokens");
+  }
   if (dm.B == 0) return AP_OK;
   if (!q || !out) return fail(AP_ERR_NULL_ARG, "q and out must not be NULL");
   if (p->n_text > 0 && (!p->text_k || !p->text_v)) return fail(AP_ERR_NULL_ARG, "text_k/text_v must be set when n_text > 0");
@@ -299,18 +327,8 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
   if (ema && (!p->importance || !p->ema_scratch))
     return fail(AP_ERR_NULL_ARG, "importance and ema_scratch must be set for the moving-average selector");
 
-  // N-splits of the flash-decode kernel: about two workgroups per CU, >= 5 token blocks
-  // each (measured best on the batch-32 LLaVA layer: 16 splits of 5-6 blocks)
-  int S = p->splits;
-  if (S == 0) {
-    S = ceil_div(512, dm.B);
-    S = std::min(S, std::max(1, dm.nblk / 5));
-  }
-  // 4-bit codes: a workgroup stages the block scales of its tokens in LDS (<= 64 blocks)
-  if (dm.storage == AP_INT4) S = std::max(S, ceil_div(dm.nblk, 64));
-  S = std::max(1, std::min(S, dm.S_cap));
-  const int CB = ceil_div(dm.nblk, S);
-  S = ceil_div(dm.nblk, CB);
+  int CB = 0;
+  const int S = split_plan(dm, p->splits, &CB);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   c->last_stream = st;
@@ -331,7 +349,24 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
     for (int k = 0; k < AP_N_KERNELS; ++k) tm.used[(size_t)tm.calls * AP_N_KERNELS + k] = 0;
   hipError_t e = hipSuccess;
   const bool per_head = p->select_mode == AP_SELECT_EMA_HEAD;
-  if (!ema && p->splits == 0 && decode_fused_supported(dm, p->r_lo, p->n_text)) {
+  if (tc) {
+    // the factored text segment first: its own selection, flash-decode and combine give
+    // its normalised output and softmax statistics, merged by the visual combine below
+    tc->last_stream = st;
+    int CBt = 0;
+    const int St = split_plan(tc->dm, 0, &CBt);
+    const KernelEvents evt = events(AP_KERNEL_TEXT);
+    e = launch_select(tc, q, p->text_r_lo, p->text_top_k, nullptr, nullptr, false, st,
+                      KernelEvents{evt.start, nullptr});
+    if (e == hipSuccess) e = launch_attn(tc, p->text_r_lo, sl2, St, CBt, nullptr, st, KernelEvents{});
+    if (e == hipSuccess)
+      e = launch_combine(tc, q, tc->out_part, sl2, St, 0, nullptr, nullptr, tc->ml_final, nullptr, nullptr,
+                         st, KernelEvents{nullptr, evt.stop});
+    if (e != hipSuccess) return hip_fail(e, "text segment launch");
+  }
+  const float* xo = tc ? tc->out_part : nullptr;
+  const float* xml = tc ? tc->ml_final : nullptr;
+  if (!ema && !tc && p->splits == 0 && decode_fused_supported(dm, p->r_lo, p->n_text)) {
     // one kernel per step: each (sequence, 4 heads) workgroup selects, attends and projects
     e = launch_decode_fused(c, q, out, p->r_lo, p->top_k, p->sel_out, p->n_text, p->text_k,
                             p->text_v, sl2, st, events(AP_KERNEL_DECODE));
@@ -344,7 +379,7 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
       e = launch_attn(c, p->r_lo, sl2, S, CB, ema ? p->ema_scratch : nullptr, st, events(AP_KERNEL_ATTN));
     if (e == hipSuccess)
       e = launch_combine(c, q, out, sl2, S, p->n_text, p->text_k, p->text_v, ema ? c->ml_final : nullptr,
-                         st, events(AP_KERNEL_COMBINE));
+                         xo, xml, st, events(AP_KERNEL_COMBINE));
     if (e == hipSuccess && ema)
       e = launch_ema_update(c, p->ema_scratch, c->ml_final, p->importance, per_head, p->ema_first != 0,
                             p->ema_alpha, st, events(AP_KERNEL_EMA));

@@ -503,7 +503,8 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
     const float* __restrict__ part_z, const float* __restrict__ part_ml, const T* __restrict__ Bv,
     const float* __restrict__ q, float* __restrict__ out, const T* __restrict__ text_k,
     const T* __restrict__ text_v, int S, int Hq, int HP, int RP, int W, int d, int G, int Tn,
-    float sl2, float* __restrict__ ml_out) {
+    float sl2, float* __restrict__ ml_out, const float* __restrict__ xo,
+    const float* __restrict__ xml) {
   constexpr int V = Vec16<T>::n;
   constexpr int U = 8;                   // rows per thread with loads in flight
   extern __shared__ __align__(16) float smem_c[];
@@ -587,7 +588,12 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
     __syncthreads();
   }
 
-  const float M = fmaxf(mv, mt);
+  // another segment's attention, already merged over its own tokens: its normalised
+  // output xo with its softmax maximum and sum (xml), joined as one more partial
+  const size_t bh = (size_t)b * Hq + h;
+  const float xm = xml != nullptr ? xml[bh * 2] : kNegBig;
+  const float xl = xml != nullptr ? xml[bh * 2 + 1] : 0.f;
+  const float M = fmaxf(fmaxf(mv, mt), xm);
   float L = 0.f;
   for (int s = tid; s < S; s += kCombThreads) {
     const float w = exp2f(ws[s] - M);
@@ -596,7 +602,8 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
   }
   L = block_reduce(L, red, false);   // also publishes the weights
   const float wt = exp2f(mt - M);
-  L += wt * lt;
+  const float wx = exp2f(xm - M) * xl;
+  L += wt * lt + wx;
 
   // merge the split partials: z[i] = sum_s w_s z_s[i]
   for (int i = tid; i < RP; i += kCombThreads) {
@@ -637,7 +644,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
     ml_out[((size_t)b * Hq + h) * 2 + 1] = L;
   }
   for (int j = tid; j < d; j += kCombThreads) {
-    float o = 0.f;
+    float o = xml != nullptr ? wx * xo[bh * d + j] : 0.f;
     for (int r = 0; r < RPP; ++r) o += accb[r * d + j];
     out[((size_t)b * Hq + h) * d + j] = o * invL;
   }
@@ -649,7 +656,8 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
     const float* __restrict__ part_z, const float* __restrict__ part_ml, const T* __restrict__ Bv,
     const float* __restrict__ q, float* __restrict__ out, const T* __restrict__ text_k,
     const T* __restrict__ text_v, int S, int Hq, int HP, int RP, int W, int d, int G, int Tn,
-    float sl2, float* __restrict__ ml_out) {
+    float sl2, float* __restrict__ ml_out, const float* __restrict__ xo,
+    const float* __restrict__ xml) {
   extern __shared__ __align__(16) float smem_c[];
   float* qh = smem_c;
   float* zz = qh + d;
@@ -695,7 +703,10 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
     }
     __syncthreads();
   }
-  const float M = fmaxf(mv, mt);
+  const size_t bh = (size_t)b * Hq + h;
+  const float xm = xml != nullptr ? xml[bh * 2] : kNegBig;
+  const float xl = xml != nullptr ? xml[bh * 2 + 1] : 0.f;
+  const float M = fmaxf(fmaxf(mv, mt), xm);
   float L = 0.f;
   for (int s = tid; s < S; s += kCombThreads) {
     const float* ml = part_ml + (pb + (size_t)s * HP + h) * 2;
@@ -703,7 +714,8 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
   }
   L = block_reduce(L, red, false);
   const float wt = exp2f(mt - M);
-  L += wt * lt;
+  const float wx = exp2f(xm - M) * xl;
+  L += wt * lt + wx;
   for (int i = tid; i < RP; i += kCombThreads) {
     float z = 0.f;
     for (int s = 0; s < S; ++s)
@@ -719,7 +731,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
   for (int jj = 0; jj < kMaxJ; ++jj) {
     const int j = tid + kCombThreads * jj;
     if (j < d) {
-      float o = wt * acc[jj];
+      float o = wt * acc[jj] + (xml != nullptr ? wx * xo[bh * d + j] : 0.f);
       const T* col = Bv + (size_t)b * RP * W + (size_t)g * d + j;
       for (int i = 0; i < RP; ++i) o = fmaf(zz[i], to_f32(col[(size_t)i * W]), o);
       out[((size_t)b * Hq + h) * d + j] = o * invL;
@@ -811,7 +823,8 @@ hipError_t launch_attn(const ap_cache* c, int r_lo, float sl2, int S, int CB, fl
 template <class T>
 static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out, float sl2, int S,
                                    int Tn, const void* tk, const void* tv, float* ml_out,
-                                   hipStream_t st, const KernelEvents& ev) {
+                                   const float* xo, const float* xml, hipStream_t st,
+                                   const KernelEvents& ev) {
   const Dims& dm = c->dm;
   constexpr int V = 16 / sizeof(T);
   const int lpr = dm.d / V;
@@ -825,24 +838,25 @@ static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out
                           ev.stop, 0, c->part_z,
                        c->part_ml, static_cast<const T*>(c->Bv), q, out, static_cast<const T*>(tk),
                        static_cast<const T*>(tv), S, dm.Hq, dm.Hq_pad, dm.r_pad, dm.W, dm.d, dm.G, Tn,
-                       sl2, ml_out);
+                       sl2, ml_out, xo, xml);
   } else {
     const size_t lds = (size_t)(dm.d + dm.r_pad + kCombThreads + 4) * sizeof(float);
     hipExtLaunchKernelGGL(k_combine_scalar<T>, dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st,
                           ev.start, ev.stop, 0,
                        c->part_z, c->part_ml, static_cast<const T*>(c->Bv), q, out,
                        static_cast<const T*>(tk), static_cast<const T*>(tv), S, dm.Hq, dm.Hq_pad,
-                       dm.r_pad, dm.W, dm.d, dm.G, Tn, sl2, ml_out);
+                       dm.r_pad, dm.W, dm.d, dm.G, Tn, sl2, ml_out, xo, xml);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float sl2, int S, int Tn,
-                          const void* tk, const void* tv, float* ml_out, hipStream_t st,
-                          const KernelEvents& ev) {
+                          const void* tk, const void* tv, float* ml_out, const float* xo,
+                          const float* xml, hipStream_t st, const KernelEvents& ev) {
   // B and the text tokens are bf16 for 4-bit caches too
-  if (c->dm.storage != AP_F32) return launch_combine_t<bf16_t>(c, q, out, sl2, S, Tn, tk, tv, ml_out, st, ev);
-  return launch_combine_t<float>(c, q, out, sl2, S, Tn, tk, tv, ml_out, st, ev);
+  if (c->dm.storage != AP_F32)
+    return launch_combine_t<bf16_t>(c, q, out, sl2, S, Tn, tk, tv, ml_out, xo, xml, st, ev);
+  return launch_combine_t<float>(c, q, out, sl2, S, Tn, tk, tv, ml_out, xo, xml, st, ev);
 }
 
 // ================================================================ k_ema_update
