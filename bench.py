@@ -50,6 +50,9 @@ def parse():
                     help="which tokens get full rank: the current low-rank logit (default), or "
                          "the moving average of past attention per token or per (head, token)")
     ap.add_argument("--ema-alpha", type=float, default=0.9)
+    ap.add_argument("--text-rank", type=int, default=0,
+                    help="factor the workload's text tokens apart at this rank (a second segment; "
+                         "rank/4 components and a quarter of the text tokens at full rank)")
     ap.add_argument("--storage", default=None, choices=["int4"],
                     help="int4: the workload with 4-bit token factors (U codes + block scales; B, "
                          "K, V and text in bf16)")
@@ -65,7 +68,7 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_bytes(w, select="logit"):
+def kernel_bytes(w, select="logit", text_rank=0):
     """Algorithmic bytes per sequence read/written by each decode kernel.  With a
     moving-average selector the importance state (fp32, per token or per (head, token))
     is read by the selection and read + written by the update; the per-step logits the
@@ -80,6 +83,12 @@ def kernel_bytes(w, select="logit"):
         "attn": 2 * u,                            # U_k, U_v
         "combine": s * r * W + s * 2 * T * W + qb,  # B_v, text K/V, out
     }
+    if text_rank:
+        # the text tokens factored apart: their U (same storage as the visual one) and B
+        # replace the dense text rows
+        k["combine"] -= s * 2 * T * W
+        ut = T * text_rank // 2 + (T + 31) // 32 * text_rank * 2 if w.storage == "int4" else s * T * text_rank
+        k["text"] = 2 * ut + 2 * s * text_rank * W + qb
     if select != "logit":
         state = 4 * N * (w.n_q_heads if select == "ema_head" else 1)
         k["select"] += state
@@ -204,17 +213,31 @@ def main():
     def stack(key, dtype):
         return torch.from_numpy(np.stack([seqs[b % S][key] for b in range(B)])).to(dtype).to(dev)
 
-    kb = kernel_bytes(w, args.select)
+    kb = kernel_bytes(w, args.select, args.text_rank)
     step_bytes = B * kb["decode"]   # every byte of one step, whichever path runs
     R = max(1, math.ceil(2 * MALL_BYTES / step_bytes))
-    caches, qs, texts = [], [], []
+    caches, qs, texts, tcaches = [], [], [], []
+    Rt = args.text_rank
+    tr_lo, tk_top = max(1, Rt // 4), (w.n_text + 3) // 4
+    if Rt and not (w.n_text and Rt <= w.n_text):
+        sys.exit("--text-rank needs a workload with at least that many text tokens")
     for _ in range(R):
         c = binding.compress(None, None, batch=B, n_tokens=w.n_tokens, n_kv_heads=w.n_kv_heads,
                              n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=w.rank, storage=st_arg)
         c.set_factors(stack("U_k", du), stack("B_k", dt), stack("U_v", du), stack("B_v", dt))
         caches.append(c)
         qs.append(stack("q", torch.float32))
-        texts.append((stack("text_k", dt), stack("text_v", dt)) if w.n_text else (None, None))
+        if Rt:
+            # the text segment factored on the GPU (ap_compress), no dense text left
+            tc = binding.compress(stack("text_k", dt).contiguous(), stack("text_v", dt).contiguous(),
+                                  batch=B, n_tokens=w.n_text, n_kv_heads=w.n_kv_heads,
+                                  n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=Rt,
+                                  storage=st_arg, seed=3)
+            tcaches.append(tc)
+            texts.append((None, None))
+        else:
+            tcaches.append(None)
+            texts.append((stack("text_k", dt), stack("text_v", dt)) if w.n_text else (None, None))
     out = torch.empty(B, w.n_q_heads * w.head_dim, dtype=torch.float32, device=dev)
     ema = args.select != "logit"
     # moving-average selector: one importance state per cache copy (the first call of
@@ -231,7 +254,8 @@ def main():
         binding.decode(caches[j], qs[j], r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, text_k=tk,
                        text_v=tv, out=out, splits=args.splits, select=args.select,
                        ema_alpha=args.ema_alpha, ema_first=first[j], importance=imps[j],
-                       ema_scratch=scratch)
+                       ema_scratch=scratch, text_cache=tcaches[j], text_r_lo=tr_lo,
+                       text_top_k=tk_top)
         first[j] = False
 
     for i in range(args.warmup):
@@ -298,7 +322,8 @@ def main():
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "rank": w.rank, "r_lo": w.r_lo, "top_k": w.top_k, "storage": w.storage,
                    "cache_copies_rotated": R, "distinct_sequences": S, "select": args.select,
-                   **({"ema_alpha": args.ema_alpha} if ema else {})},
+                   **({"ema_alpha": args.ema_alpha} if ema else {}),
+                   **({"text_rank": Rt, "text_r_lo": tr_lo, "text_top_k": tk_top} if Rt else {})},
         "ms_per_step_hip_events": event_ms,
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "GB/s": step_bytes / (elapsed / args.steps) / 1e9,
@@ -309,9 +334,9 @@ def main():
                      "algorithmic_bytes_per_launch": dom_bytes},
     }
 
-    for c in caches:
+    for c in caches + [t for t in tcaches if t is not None]:
         c.free()
-    del caches, qs, texts
+    del caches, qs, texts, tcaches
 
     if not args.no_compress:
         result["compress"] = compress_leg(w, args.compress_reps, binding, wl, np, torch)
