@@ -92,6 +92,12 @@ hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float s
                           int S, int T, const void* text_k, const void* text_v, float* ml_out,
                           const float* xo, const float* xml, hipStream_t st,
                           const KernelEvents& ev);
+// A small factored segment (its factors and one KV head's B rows fit 96 KB of LDS) of
+// every (sequence, query head) in one kernel: writes c->out_part and c->ml_final, merged
+// by another cache's combine.
+bool text_seg_supported(const Dims& dm);
+hipError_t launch_text_seg(const ap_cache* c, const float* q, int r_lo, int top_k, float sl2,
+                           hipStream_t st, const KernelEvents& ev);
 hipError_t launch_ema_update(const ap_cache* c, const float* s, const float* ml, float* imp,
                              bool per_head, bool first, float alpha, hipStream_t st,
                              const KernelEvents& ev);

@@ -353,15 +353,20 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
     // the factored text segment first: its own selection, flash-decode and combine give
     // its normalised output and softmax statistics, merged by the visual combine below
     tc->last_stream = st;
-    int CBt = 0;
-    const int St = split_plan(tc->dm, 0, &CBt);
     const KernelEvents evt = events(AP_KERNEL_TEXT);
-    e = launch_select(tc, q, p->text_r_lo, p->text_top_k, nullptr, nullptr, false, st,
-                      KernelEvents{evt.start, nullptr});
-    if (e == hipSuccess) e = launch_attn(tc, p->text_r_lo, sl2, St, CBt, nullptr, st, KernelEvents{});
-    if (e == hipSuccess)
-      e = launch_combine(tc, q, tc->out_part, sl2, St, 0, nullptr, nullptr, tc->ml_final, nullptr, nullptr,
-                         st, KernelEvents{nullptr, evt.stop});
+    if (text_seg_supported(tc->dm)) {
+      // small segment: the whole segment of a (sequence, head) in one workgroup
+      e = launch_text_seg(tc, q, p->text_r_lo, p->text_top_k, sl2, st, evt);
+    } else {
+      int CBt = 0;
+      const int St = split_plan(tc->dm, 0, &CBt);
+      e = launch_select(tc, q, p->text_r_lo, p->text_top_k, nullptr, nullptr, false, st,
+                        KernelEvents{evt.start, nullptr});
+      if (e == hipSuccess) e = launch_attn(tc, p->text_r_lo, sl2, St, CBt, nullptr, st, KernelEvents{});
+      if (e == hipSuccess)
+        e = launch_combine(tc, q, tc->out_part, sl2, St, 0, nullptr, nullptr, tc->ml_final, nullptr,
+                           nullptr, st, KernelEvents{nullptr, evt.stop});
+    }
     if (e != hipSuccess) return hip_fail(e, "text segment launch");
   }
   const float* xo = tc ? tc->out_part : nullptr;

@@ -859,6 +859,247 @@ hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float s
   return launch_combine_t<float>(c, q, out, sl2, S, Tn, tk, tv, ml_out, xo, xml, st, ev);
 }
 
+// ================================================================ k_text_seg
+// A small factored segment (the text tokens factored apart) of one (sequence, query
+// head), whole, in one workgroup: latent query q~ = B_k[:, g's columns] q_h, scores of
+// every token at the low rank and the remainder up to the full rank, the segment's
+// top_k tokens by low-rank score (ties to the lower id) at full rank, softmax, latent
+// values z = sum_n p[n] U_v[n, :r(n)], projection through the segment's B_v.  Writes
+// the normalised output and the softmax maximum and sum (log2 units), which the visual
+// combine merges as one more partial.  The segment's U_k, U_v (through the tiled
+// layouts, 4-bit codes with their block scales) and this KV head's rows of B_k, B_v are
+// first staged in LDS in one round of independent loads.
+constexpr int kSegThreads = 256;
+
+// One lane's 8 elements of a tiled panel as floats (4-bit codes times their block scales).
+template <class T>
+__device__ __forceinline__ void seg_lane8(const T* __restrict__ U, const bf16_t* __restrict__ Usc,
+                                          bool vl, int b, int p, int blk, int lane, int NP, int nblk,
+                                          float (&v)[8]) {
+  const size_t base = tile_base(b, p, blk, NP, nblk);
+  if constexpr (std::is_same<T, i4_t>::value) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(tile_ptr(U, base))[lane];
+    const bf16_t* srow = Usc + (((size_t)b * nblk + blk) * 2 + (vl ? 1 : 0)) * 16 * NP;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int col = vl ? 16 * p + (lane & 15) : 16 * p + 4 * (lane >> 4) + (i & 3);
+      v[i] = static_cast<float>(static_cast<int>((w >> q4_shift(i)) & 0xFu) - 8) *
+             bf16_to_f32(srow[scale_slot(col, NP)]);
+    }
+  } else if constexpr (std::is_same<T, bf16_t>::value) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(U + base + lane * 8);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float((i & 1) ? (wd[i >> 1] & 0xFFFF0000u) : (wd[i >> 1] << 16));
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(U + base + lane * 8);
+    const float4 c = *reinterpret_cast<const float4*>(U + base + lane * 8 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(kSegThreads) void k_text_seg(
+    const T* __restrict__ Uk, const T* __restrict__ Uv, const bf16_t* __restrict__ Usc,
+    const StoreB<T>* __restrict__ Bk, const StoreB<T>* __restrict__ Bv, const float* __restrict__ q,
+    float* __restrict__ xo, float* __restrict__ xml, int N, int nblk, int NP, int r, int W, int d,
+    int G, int Hq, int r_lo, int top_k, float sl2) {
+  extern __shared__ __align__(16) float smem_s[];
+  const int RP = 16 * NP, US = RP + 1;   // padded rows: no bank conflicts across tokens
+  float* uk = smem_s;            // [N][US] U_k of the segment (columns >= r zero)
+  float* uv = uk + N * US;       // [N][US] U_v
+  float* bv = uv + N * US;       // [RP][d] this KV head's columns of B_v
+  float* qt = bv + RP * d;       // [RP] latent query, scaled to log2 units
+  float* slo = qt + RP;          // [N] low-rank scores
+  float* sc = slo + N;           // [N] scores, then weights
+  float* fl = sc + N;            // [N] 1 for the segment's top_k tokens
+  float* zz = fl + N;            // [RP]
+  float* red = zz + RP;          // [kSegThreads / 64]
+  const int b = blockIdx.x / Hq, h = blockIdx.x - (blockIdx.x / Hq) * Hq;
+  const int g = h / G, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto block_red = [&](float v, bool is_max) {   // also publishes earlier LDS writes
+    for (int off = 32; off > 0; off >>= 1) {
+      const float o = __shfl_xor(v, off, 64);
+      v = is_max ? fmaxf(v, o) : v + o;
+    }
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float x = red[0];
+    for (int w = 1; w < kSegThreads / 64; ++w) x = is_max ? fmaxf(x, red[w]) : x + red[w];
+    __syncthreads();
+    return x;
+  };
+  // ---- stage everything the segment reads: batches of 4 independent 16-byte loads per
+  // thread (indices clamped, so every load is issued), then the LDS stores
+  // Latent query from the loaded chunks: a row of B_k is cpr consecutive lanes (cpr a
+  // power of two dividing 64), each dotting its chunk with q, summed across the lanes.
+  using TB = StoreB<T>;
+  constexpr int V = Vec16<TB>::n;
+  const float* qg = q + ((size_t)b * Hq + h) * d;
+  const int cpr = d / V, nch = RP * cpr;
+  for (int c0 = 0; c0 < nch; c0 += 4 * kSegThreads) {
+    Vec16<TB> xk[4], xv[4];
+    float qv[4][V];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cc = min(c0 + u * kSegThreads + tid, nch - 1), i = cc / cpr, jc = cc - (cc / cpr) * cpr;
+      const size_t off = ((size_t)b * RP + i) * W + (size_t)g * d + jc * V;
+      xk[u].load(Bk + off);
+      xv[u].load(Bv + off);
+#pragma unroll
+      for (int e = 0; e < V; ++e) qv[u][e] = qg[jc * V + e];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cc = c0 + u * kSegThreads + tid;
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) part = fmaf(xk[u].get(e), qv[u][e], part);
+      part = group_sum(part, cpr);   // uniform trip count: every lane takes part
+      if (cc < nch) {
+        const int i = cc / cpr, jc = cc - (cc / cpr) * cpr;
+        if (jc == 0) qt[i] = i < r ? part * sl2 : 0.f;
+#pragma unroll
+        for (int e = 0; e < V; ++e) bv[i * d + jc * V + e] = xv[u].get(e);
+      }
+    }
+  }
+  const int nlw = nblk * NP * 64;   // lane words of one factor
+  for (int w0 = 0; w0 < nlw; w0 += 2 * kSegThreads) {
+    float a[2][8], c[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = min(w0 + u * kSegThreads + tid, nlw - 1);
+      const int ln = idx & 63, p = (idx >> 6) % NP, blk = (idx >> 6) / NP;
+      seg_lane8<T>(Uk, Usc, false, b, p, blk, ln, NP, nblk, a[u]);
+      seg_lane8<T>(Uv, Usc, true, b, p, blk, ln, NP, nblk, c[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = w0 + u * kSegThreads + tid;
+      if (idx < nlw) {
+        const int ln = idx & 63, p = (idx >> 6) % NP, blk = (idx >> 6) / NP;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int half = i >> 2, e = i & 3;
+          const int tk = 32 * blk + 16 * half + (ln & 15), ck = 16 * p + 4 * (ln >> 4) + e;   // K layout
+          const int tv = 32 * blk + 16 * half + 4 * (ln >> 4) + e, cv = 16 * p + (ln & 15);  // V layout
+          if (tk < N) uk[tk * US + ck] = ck < r ? a[u][i] : 0.f;
+          if (tv < N) uv[tv * US + cv] = cv < r ? c[u][i] : 0.f;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int n = tid; n < N; n += kSegThreads) {
+    float lo = 0.f, hi = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < RP; ++i) {
+      const float v = uk[n * US + i] * qt[i];
+      if (i < r_lo) lo += v; else hi += v;
+    }
+    slo[n] = lo;
+    sc[n] = hi;
+  }
+  __syncthreads();
+  // the segment's top_k by low-rank score, ties to the lower id: n is taken when fewer
+  // than top_k tokens rank ahead of it.  Four lanes count for one token, a quarter of
+  // the tokens each, and their counts are summed across the quad.
+  float mloc = -INFINITY;
+  const int quarter = (N + 3) / 4;
+  for (int n0 = 0; n0 < N; n0 += kSegThreads / 4) {
+    const int n = n0 + (tid >> 2), part = tid & 3;
+    const float s = slo[min(n, N - 1)];
+    int ahead = 0;
+    const int m1 = min(N, (part + 1) * quarter);
+#pragma unroll 4
+    for (int m = part * quarter; m < m1; ++m) {
+      const float t = slo[m];
+      ahead += (t > s || (t == s && m < n)) ? 1 : 0;
+    }
+    ahead += __shfl_xor(ahead, 1, 64);
+    ahead += __shfl_xor(ahead, 2, 64);
+    if (n < N && part == 0) {
+      const bool sel = ahead < top_k;
+      const float v = sel ? s + sc[n] : s;
+      sc[n] = v;
+      fl[n] = sel ? 1.f : 0.f;
+      mloc = fmaxf(mloc, v);
+    }
+  }
+  const float M = block_red(mloc, true);
+  float lsum = 0.f;
+  for (int n = tid; n < N; n += kSegThreads) {
+    const float e = hw_exp2(sc[n] - M);
+    sc[n] = e;
+    lsum += e;
+  }
+  const float L = block_red(lsum, false);
+  // latent values: 16 lanes per latent column, each over every 16th token, then summed
+  // across the 16 lanes (fixed order)
+  for (int i0 = 0; i0 < RP; i0 += kSegThreads / 16) {
+    const int i = i0 + (tid >> 4), part = tid & 15;
+    float z = 0.f;
+    if (i < RP) {
+#pragma unroll 4
+      for (int n = part; n < N; n += 16) z = fmaf((i < r_lo || fl[n] > 0.f) ? sc[n] : 0.f, uv[n * US + i], z);
+    }
+    z = group_sum(z, 16);
+    if (i < RP && part == 0) zz[i] = z;
+  }
+  __syncthreads();
+  const float invL = 1.f / L;
+  for (int j = tid; j < d; j += kSegThreads) {
+    float o = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < RP; ++i) o = fmaf(zz[i], bv[i * d + j], o);
+    xo[((size_t)b * Hq + h) * d + j] = o * invL;
+  }
+  if (tid == 0) {
+    xml[((size_t)b * Hq + h) * 2] = M;
+    xml[((size_t)b * Hq + h) * 2 + 1] = L;
+  }
+}
+
+static size_t text_seg_lds(const Dims& dm) {
+  return (size_t)(2 * dm.N * (dm.r_pad + 1) + dm.r_pad * dm.d + 2 * dm.r_pad + 3 * dm.N +
+                  kSegThreads / 64) * sizeof(float);
+}
+
+bool text_seg_supported(const Dims& dm) {
+  // B rows read as 16-byte chunks of this head's columns, a power of two of them per row
+  const int V = dm.storage == AP_F32 ? 4 : 8;
+  const int cpr = dm.d / V;
+  return text_seg_lds(dm) <= 96 * 1024 && dm.d % V == 0 && dm.W % V == 0 && cpr <= 64 &&
+         (cpr & (cpr - 1)) == 0;
+}
+
+hipError_t launch_text_seg(const ap_cache* c, const float* q, int r_lo, int top_k, float sl2,
+                           hipStream_t st, const KernelEvents& ev) {
+  const Dims& dm = c->dm;
+  const size_t lds = text_seg_lds(dm);
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_text_seg<T>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipExtLaunchKernelGGL(k_text_seg<T>, dim3(dm.B * dm.Hq), dim3(kSegThreads), lds, st, ev.start,
+                          ev.stop, 0, static_cast<const T*>(c->Uk), static_cast<const T*>(c->Uv),
+                          reinterpret_cast<const bf16_t*>(c->Usc), static_cast<const StoreB<T>*>(c->Bk),
+                          static_cast<const StoreB<T>*>(c->Bv), q, c->out_part, c->ml_final, dm.N,
+                          dm.nblk, dm.NP, dm.r, dm.W, dm.d, dm.G, dm.Hq, r_lo, top_k, sl2);
+    return hipGetLastError();
+  };
+  if (dm.storage == AP_INT4) return go(i4_t{});
+  if (dm.storage == AP_BF16) return go(bf16_t{});
+  return go(float{});
+}
+
 // ================================================================ k_ema_update
 // Moving-average importance after a step ([fr §2.B "Score d'importance"]): the weight
 // of visual token n for head h is p = exp2(s - M_h) / L_h, with s the step's logit

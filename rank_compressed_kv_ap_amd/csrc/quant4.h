@@ -19,6 +19,8 @@
 //     g*4*NP + 4p + e, so a lane group g finds the scales of its columns (the same
 //     columns in both layouts' MFMA operands) in one contiguous run.
 #pragma once
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace ap {
@@ -28,6 +30,10 @@ struct i4_t {   // storage tag: pointers of this type count bytes of packed code
 };
 
 constexpr int kQMax = 7;
+
+// Element type of B (and of the dense tokens): the storage type, bf16 for 4-bit U.
+template <class T>
+using StoreB = typename std::conditional<std::is_same<T, i4_t>::value, bf16_t, T>::type;
 
 __device__ __forceinline__ const i4_t* tile_ptr(const i4_t* base, size_t elem) { return base + elem / 2; }
 __device__ __forceinline__ i4_t* tile_ptr(i4_t* base, size_t elem) { return base + elem / 2; }

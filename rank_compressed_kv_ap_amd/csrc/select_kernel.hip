@@ -306,10 +306,6 @@ template <> struct SelQ<i4_t> {
   }
 };
 
-// Element type of B: the storage type, bf16 for 4-bit token factors.
-template <class T>
-using StoreB = typename std::conditional<std::is_same<T, i4_t>::value, bf16_t, T>::type;
-
 // Operands of the single-kernel decode (unused by the selection-only kernel).
 struct FusedArgs {
   const void* Uv;       // V-layout panels

@@ -92,6 +92,7 @@ def check(w, tw, vis, txt, out, sel, r_lo_t, k_t, dense=None):
     ("int4", "bf16", 40, 32, 16, 10),     # 4-bit visual factors, bf16 text factors
     ("bf16", "int4", 100, 32, 16, 25),    # 4-bit text factors
     ("f32_gqa", "f32", 33, 12, 4, 33),    # fp32, GQA, every text token at full rank
+    ("bf16", "bf16", 1100, 16, 8, 275),   # too large to stage in LDS: the three-kernel path
 ])
 def test_text_segment_parity(gpu_lib, vis, text_storage, n_tok, rank, r_lo_t, k_t):
     w = VIS[vis]
