@@ -328,7 +328,7 @@ struct FusedArgs {
 // accumulation steps per wavefront (2, 3, 4 or 8).  FUSED: the same workgroup goes on
 // to the attention of its heads over all tokens, the text tokens and the output
 // projection (bf16 factors, HG = 4, r <= 64), so one kernel makes the whole step.
-template <class T, int HG, int NPL, int NACC, bool FUSED>
+template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0>
 __device__ __forceinline__ void select_body(
     const T* __restrict__ Uk, const StoreB<T>* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
@@ -338,6 +338,10 @@ __device__ __forceinline__ void select_body(
                 "single-kernel decode: bf16, four heads per workgroup");
   constexpr bool U4 = std::is_same<T, i4_t>::value;
   using TB = StoreB<T>;   // element type of B (and of the text tokens)
+  // NPX > 0 (single-kernel decode): the factors have NPX panels and r_lo = 16 * NPL, so
+  // the panel loops of the attention phases are resolved at compile time
+  const int NPr = NPX > 0 ? NPX : NP;
+  const int rlo = NPX > 0 ? 16 * NPL : r_lo;
   constexpr int NSL = 8 / HG;                                   // token blocks per step
   constexpr int KPL = 4 * NACC;                                 // scores per lane
   constexpr int NSTEP = NACC * NPL;
@@ -493,14 +497,14 @@ __device__ __forceinline__ void select_body(
   constexpr int NPM = 4;                        // panels (r <= 64)
   constexpr int NSK = NACC * NPM;               // steps of each pass
   constexpr int PD = NACC <= 4 ? 4 : 2;
-  const int p0 = r_lo >> 4;                     // first panel with a column >= r_lo
+  const int p0 = rlo >> 4;                      // first panel with a column >= r_lo
   LaneTile<T> rb[FUSED ? PD : 1][NSL];
   auto ld = [&](int s) {   // s is a compile-time constant after unrolling
     const bool isv = s >= NSK;
     const int ss = isv ? s - NSK : s;
     const int a = ss / NPM, j = ss % NPM;
     const int grp = wave + nwv * a;
-    const int pan = isv ? min(j, NP - 1) : min(p0 + j, NP - 1);
+    const int pan = isv ? min(j, NPr - 1) : min(p0 + j, NPr - 1);
     const T* base = isv ? static_cast<const T*>(fa.Uv) : Uk;
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
@@ -889,7 +893,7 @@ __device__ __forceinline__ void select_body(
 
     // ---- F2. full-rank part of the selected tokens' scores (columns >= r_lo), on the
     // same block-diagonal tiles as the low-rank scores; final scores in log2 units
-    const int nph = NP - p0;
+    const int nph = NPr - p0;
     uint2 qhi[NPM];
 #pragma unroll
     for (int j = 0; j < NPM; ++j) {
@@ -898,7 +902,7 @@ __device__ __forceinline__ void select_body(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int col = 16 * p + 4 * lg + e;
-        v[e] = (my_on && p < NP && col >= r_lo) ? qs[my_h * r_pad + col] : 0.f;
+        v[e] = (my_on && p < NPr && col >= rlo) ? qs[my_h * r_pad + col] : 0.f;
       }
       qhi[j] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
@@ -1002,19 +1006,19 @@ __device__ __forceinline__ void select_body(
 #pragma unroll
       for (int p = 0; p < NPM; ++p) {
         const int s = NSK + a * NPM + p;
-        if (p < NP) {
+        if (p < NPr) {
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) {
             const bool on = sl == my_slot;
             const v8bf ba = __builtin_bit_cast(v8bf, on ? BA : z4);
             const v8bf bs = __builtin_bit_cast(v8bf, on ? BS : z4);
             const v8bf av = __builtin_bit_cast(v8bf, rb[s % PD][sl].raw);
-            if (16 * p + 16 <= r_lo) {
+            if (16 * p + 16 <= rlo) {
               Z[p] = mfma_bf16_k32(av, ba, Z[p]);
-            } else if (16 * p >= r_lo) {
+            } else if (16 * p >= rlo) {
               Z[p] = mfma_bf16_k32(av, bs, Z[p]);
             } else {   // panel straddling r_lo: this lane's A row is latent column 16p + c16
-              const bool lo_row = 16 * p + c16 < r_lo;
+              const bool lo_row = 16 * p + c16 < rlo;
               const v8bf zz = __builtin_bit_cast(v8bf, z4);
               Z[p] = mfma_bf16_k32(lo_row ? av : zz, ba, Z[p]);
               Z[p] = mfma_bf16_k32(lo_row ? zz : av, bs, Z[p]);
@@ -1034,7 +1038,7 @@ __device__ __forceinline__ void select_body(
     if (c16 < HG) {
 #pragma unroll
       for (int p = 0; p < NPM; ++p)
-        if (p < NP) {
+        if (p < NPr) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) zpart[(wave * HG + c16) * r_pad + 16 * p + 4 * lg + t] = Z[p][t];
         }
@@ -1102,14 +1106,14 @@ __global__ __launch_bounds__(1024) void k_select(
 }
 
 // The whole decode step of four query heads of one sequence (bf16 factors).
-template <int NPL, int NACC>
+template <int NPL, int NACC, int NPX>
 __global__ __launch_bounds__(1024) void k_decode(
     const bf16_t* __restrict__ Uk, const bf16_t* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
     int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
     int r_lo, int top_k, FusedArgs fa) {
-  select_body<bf16_t, 4, NPL, NACC, true>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad, W,
-                                          d, G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
+  select_body<bf16_t, 4, NPL, NACC, true, NPX>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad,
+                                               W, d, G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1139,7 +1143,7 @@ static SelPlan select_plan(const Dims& dm, int r_lo, bool single_kernel) {
   return pl;
 }
 
-template <class T, int HG, int NPL, int NACC, bool FUSED>
+template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0>
 static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, int top_k,
                                   int32_t* sel_out, int waves, const FusedArgs& fa, hipStream_t st,
                                   const KernelEvents& ev) {
@@ -1150,7 +1154,7 @@ static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, i
   if ((dm.nblk + 8 / HG - 1) / (8 / HG) > waves * NACC) return hipErrorInvalidValue;
   if (HG * dm.d > 64 * waves) return hipErrorInvalidValue;
   const void* fn;
-  if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<NPL, NACC>);
+  if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<NPL, NACC, NPX>);
   else fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC>);
   static bool attr_set = false;
   if (!attr_set) {
@@ -1160,7 +1164,7 @@ static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, i
   }
   const int grid = ((dm.B + 7) / 8) * 8 * HGN;
   if constexpr (FUSED)
-    hipExtLaunchKernelGGL((k_decode<NPL, NACC>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
+    hipExtLaunchKernelGGL((k_decode<NPL, NACC, NPX>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
                           ev.stop, 0, static_cast<const T*>(c->Uk), static_cast<const T*>(c->Bk), q,
                           c->qt, c->mask, sel_out, dm.B, dm.N, dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d,
                           dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo, top_k, fa);
@@ -1236,17 +1240,25 @@ hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, in
   fa.keys = nullptr;
   fa.keys_per_head = 0;
   fa.Usc = nullptr;
+  // r = 64 (4 panels) with r_lo = 16: the panel split known at compile time (variants
+  // that fit the registers without spilling)
+  const bool exact = c->dm.NP == 4 && r_lo == 16 * pl.NPL;
 #define AP_FUS(NPLV, NACCV)                                                             \
   if (pl.NPL == NPLV && pl.NACC == NACCV)                                               \
-    return launch_select_v<bf16_t, 4, NPLV, NACCV, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
-  AP_FUS(1, 2)
-  AP_FUS(1, 3)
+    return launch_select_v<bf16_t, 4, NPLV, NACCV, true, 0>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
+#define AP_FUS_X(NPLV, NACCV)                                                           \
+  if (pl.NPL == NPLV && pl.NACC == NACCV)                                               \
+    return exact ? launch_select_v<bf16_t, 4, NPLV, NACCV, true, 4>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev) \
+                 : launch_select_v<bf16_t, 4, NPLV, NACCV, true, 0>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
+  AP_FUS_X(1, 2)
+  AP_FUS_X(1, 3)
   AP_FUS(1, 4)
   AP_FUS(1, 8)
   AP_FUS(2, 2)
   AP_FUS(2, 3)
   AP_FUS(2, 4)
   AP_FUS(2, 8)
+#undef AP_FUS_X
 #undef AP_FUS
   return hipErrorInvalidValue;
 }

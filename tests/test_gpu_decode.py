@@ -32,6 +32,10 @@ SMALL = {
                                            head_dim=64, n_tokens=200, n_text=70, rank=48, r_lo=20,
                                            top_k=50, grid=None, inner_dim=200),
     "f32_text_long": wl.TINY.replace(cfg_id=106, batch=2, n_text=300, n_tokens=90, top_k=22),
+    # rank 64 with r_lo 16: the single-kernel decode with its panel split fixed at compile time
+    "bf16_rank64_lo16": wl.LLAVA.replace(cfg_id=108, batch=2, n_q_heads=8, n_kv_heads=8, head_dim=64,
+                                         n_tokens=300, n_text=10, rank=64, r_lo=16, top_k=75,
+                                         grid=None, inner_dim=300),
 }
 
 
@@ -129,6 +133,7 @@ def test_decode_is_deterministic(gpu_lib, name, splits):
 
 
 @pytest.mark.parametrize("name,splits,path", [("bf16_straddle_text", 0, "decode"),
+                                              ("bf16_rank64_lo16", 0, "decode"),
                                               ("bf16_straddle_text", 2, "split"),
                                               ("bf16_rank128", 0, "split"),
                                               ("f32_text_long", 0, "split")])
