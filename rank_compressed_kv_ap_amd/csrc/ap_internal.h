@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <string>
 #include <vector>
 
@@ -68,6 +69,19 @@ struct ap_cache {
 namespace ap {
 
 void set_error(const std::string& msg);
+
+// Raise a kernel's dynamic LDS limit on the current device, once per device (devices
+// 0..31 remembered in `done`, one flag set per kernel instantiation).
+inline hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<uint32_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint32_t bit = 1u << (dev & 31);
+  if (dev < 32 && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && dev < 32) done.fetch_or(bit, std::memory_order_relaxed);
+  return e;
+}
 
 // Events that a launch's own dispatch timestamps at the kernel's start and end
 // (hipExtLaunchKernelGGL), or null for an untimed launch.

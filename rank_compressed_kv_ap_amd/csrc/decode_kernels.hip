@@ -748,13 +748,9 @@ static hipError_t launch_attn_t(const ap_cache* c, int r_lo, float sl2, int S, i
   // merge buffers, then (4-bit codes) the workgroup's block scales
   const size_t lds = (size_t)(4 * HP * (RP + 1) + 8 * HP) * sizeof(float) +
                      (std::is_same<T, i4_t>::value ? (size_t)CB * RP * 4 : 0);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<T, NP, HT, PLT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint32_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&k_attn<T, NP, HT, PLT>), 160 * 1024, lds_set);
+  if (e != hipSuccess) return e;
   hipExtLaunchKernelGGL((k_attn<T, NP, HT, PLT>), dim3(dm.B * S), dim3(256), lds, st, ev.start, ev.stop, 0,
                      static_cast<const T*>(c->Uk), static_cast<const T*>(c->Uv),
                      reinterpret_cast<const bf16_t*>(c->Usc), c->qt, c->mask,
@@ -1081,13 +1077,9 @@ hipError_t launch_text_seg(const ap_cache* c, const float* q, int r_lo, int top_
   const size_t lds = text_seg_lds(dm);
   auto go = [&](auto tag) {
     using T = decltype(tag);
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_text_seg<T>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static std::atomic<uint32_t> lds_set{0};
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&k_text_seg<T>), 96 * 1024, lds_set);
+    if (e != hipSuccess) return e;
     hipExtLaunchKernelGGL(k_text_seg<T>, dim3(dm.B * dm.Hq), dim3(kSegThreads), lds, st, ev.start,
                           ev.stop, 0, static_cast<const T*>(c->Uk), static_cast<const T*>(c->Uv),
                           reinterpret_cast<const bf16_t*>(c->Usc), static_cast<const StoreB<T>*>(c->Bk),

@@ -1156,12 +1156,9 @@ static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, i
   const void* fn;
   if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<NPL, NACC, NPX>);
   else fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC>);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint32_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(fn, 160 * 1024, lds_set);
+  if (e != hipSuccess) return e;
   const int grid = ((dm.B + 7) / 8) * 8 * HGN;
   if constexpr (FUSED)
     hipExtLaunchKernelGGL((k_decode<NPL, NACC, NPX>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
