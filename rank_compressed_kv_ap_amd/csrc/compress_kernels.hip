@@ -151,6 +151,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
 #pragma unroll
     for (int c = 0; c < NT; ++c) acc[i][c] = v4f{0, 0, 0, 0};
 
+  // For TRANS the A tile is written as 8-byte pieces of rows 8 apart, which the padded
+  // row stride maps onto the same LDS banks; the 16-byte chunk index of row r is then
+  // XOR-ed with (r >> 3) & 7 on the write and on the read.
+  auto achunk = [](int row, int chunk) { return TRANS ? (chunk ^ ((row >> 3) & 7)) : chunk; };
   auto pack8 = [](const uint16_t* t) {
     return make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16),
                       t[4] | (uint32_t(t[5]) << 16), t[6] | (uint32_t(t[7]) << 16));
@@ -228,8 +232,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
       for (int c = 0; c < 4; ++c) {
         const uint2 ev = make_uint2((r0[c] & 0xffffu) | (r1[c] << 16), (r2[c] & 0xffffu) | (r3[c] << 16));
         const uint2 od = make_uint2((r0[c] >> 16) | (r1[c] & 0xffff0000u), (r2[c] >> 16) | (r3[c] & 0xffff0000u));
-        *reinterpret_cast<uint2*>(&As[(mm + 2 * c) * kGemmLdsStride + kk]) = ev;
-        *reinterpret_cast<uint2*>(&As[(mm + 2 * c + 1) * kGemmLdsStride + kk]) = od;
+        const int re = mm + 2 * c, ro = re + 1;   // 16-byte chunk kk / 8, 8-byte half (kk / 4) & 1
+        *reinterpret_cast<uint2*>(&As[re * kGemmLdsStride + 8 * achunk(re, kk >> 3) + (kk & 4)]) = ev;
+        *reinterpret_cast<uint2*>(&As[ro * kGemmLdsStride + 8 * achunk(ro, kk >> 3) + (kk & 4)]) = od;
       }
     }
 #pragma unroll
@@ -252,9 +257,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
     for (int s2 = 0; s2 < 2; ++s2) {
       v8bf ab[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) {
+        const int row = 32 * wave + 16 * i + l16;
         ab[i] = __builtin_bit_cast(
-            v8bf, *reinterpret_cast<const uint4*>(&As[(32 * wave + 16 * i + l16) * kGemmLdsStride + 32 * s2 + 8 * lg]));
+            v8bf, *reinterpret_cast<const uint4*>(&As[row * kGemmLdsStride + 8 * achunk(row, 4 * s2 + lg)]));
+      }
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
         const int xo = (16 * c + l16) * kGemmLdsStride + 32 * s2 + 8 * lg;
