@@ -602,11 +602,38 @@ __global__ __launch_bounds__(256) void k_apply(float* __restrict__ Y, int M, int
   const float* Rm = Rinv + (size_t)mat * ellp * ellp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  for (int idx = tid; idx < rows * ellp; idx += 256) {
-    const int r = idx / ellp, j = idx % ellp;
-    Ys[r * S + j] = m0 + r < M ? Ym[(size_t)(m0 + r) * ellp + j] : 0.f;
+  // stage the Y tile and R^-1: 16-byte loads, 8 independent ones in flight per thread
+  // (indices clamped so every load is issued; rows past M are zeroed after the load)
+  const int ell4 = ellp / 4;   // ellp is a multiple of 16
+  const int ny = rows * ell4, nr = ellp * ell4;
+  for (int i0 = 0; i0 < ny + nr; i0 += 8 * 256) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = min(i0 + u * 256 + tid, ny + nr - 1);
+      if (idx < ny) {
+        const int r = idx / ell4, j4 = idx - r * ell4;
+        v[u] = *reinterpret_cast<const float4*>(Ym + (size_t)min(m0 + r, M - 1) * ellp + 4 * j4);
+      } else {
+        v[u] = *reinterpret_cast<const float4*>(Rm + (size_t)4 * (idx - ny));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = i0 + u * 256 + tid;
+      if (idx < ny) {
+        const int r = idx / ell4, j4 = idx - r * ell4;
+        const bool live = m0 + r < M;
+        float* d = Ys + r * S + 4 * j4;
+        d[0] = live ? v[u].x : 0.f;
+        d[1] = live ? v[u].y : 0.f;
+        d[2] = live ? v[u].z : 0.f;
+        d[3] = live ? v[u].w : 0.f;
+      } else if (idx < ny + nr) {
+        *reinterpret_cast<float4*>(Rs + 4 * (idx - ny)) = v[u];
+      }
+    }
   }
-  for (int idx = tid; idx < ellp * ellp; idx += 256) Rs[idx] = Rm[idx];
   __syncthreads();
   const int T16 = ellp / 16;
   // wave owns row tiles wave and wave + 4 (16 rows each), all column tiles
