@@ -582,12 +582,13 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
 // Row tile of k_apply.
 static int apply_rows(int) { return 128; }
 
-// Q = Y Rinv for a tile of rows per workgroup (fp32 MFMA), written in place; optionally
-// Q^T in storage precision for the next product (XT[mat][j][m]), and the rounding
-// remainder Q^T - XT in XTlo for a two-term product.  The Q tile is kept in LDS so
-// that Q^T leaves in 16-byte runs along m.
+// Q = Y Rinv for a tile of rows per workgroup (fp32 MFMA), written to Qout (Y itself for
+// a basis that is orthonormalised again, another buffer for a basis kept for the
+// factors, or nowhere when only Q^T is used); optionally Q^T in storage precision for
+// the next product (XT[mat][j][m]), and the rounding remainder Q^T - XT in XTlo for a
+// two-term product.  The Q tile is kept in LDS so that Q^T leaves in 16-byte runs along m.
 template <class T>
-__global__ __launch_bounds__(256) void k_apply(float* __restrict__ Y, int M, int ellp,
+__global__ __launch_bounds__(256) void k_apply(const float* Y, float* Qout, int M, int ellp,
                                                const float* __restrict__ Rinv, T* __restrict__ XT,
                                                T* __restrict__ XTlo, size_t xt_mat_stride, int tiles_m,
                                                int rows) {
@@ -598,7 +599,8 @@ __global__ __launch_bounds__(256) void k_apply(float* __restrict__ Y, int M, int
   float* Rs = Ys + rows * S;       // [ellp][ellp]
   const int mat = blockIdx.x / tiles_m;
   const int m0 = (blockIdx.x % tiles_m) * rows;
-  float* Ym = Y + (size_t)mat * M * ellp;
+  const float* Ym = Y + (size_t)mat * M * ellp;
+  float* Qm = Qout != nullptr ? Qout + (size_t)mat * M * ellp : nullptr;
   const float* Rm = Rinv + (size_t)mat * ellp * ellp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -663,7 +665,7 @@ __global__ __launch_bounds__(256) void k_apply(float* __restrict__ Y, int M, int
       for (int t = 0; t < 4; ++t) {
         const int r = 16 * rt + 4 * lg + t, j = 16 * c + l16;
         Ys[r * S + j] = acc[i][c][t];
-        if (m0 + r < M) Ym[(size_t)(m0 + r) * ellp + j] = acc[i][c][t];
+        if (Qm != nullptr && m0 + r < M) Qm[(size_t)(m0 + r) * ellp + j] = acc[i][c][t];
       }
     }
   }
@@ -990,12 +992,13 @@ static void gram_split(int M, int nmat, int& rows, int& nsplit) {
   nsplit = (M + rows - 1) / rows;
 }
 
-// Shifted Cholesky QR of Y [nmat][M][ellp] in place, `passes` times (1 for bases that
-// only feed the next power-iteration product, 2 where U or B are built from the
-// basis); Q^T to XT after the last pass (if given); R to Racc (if given).
+// Shifted Cholesky QR of Y [nmat][M][ellp], `passes` times (1 for bases that only feed
+// the next power-iteration product, 2 where U or B are built from the basis): earlier
+// passes write Q over Y, the last one to Qlast (if given; [nmat][M][ellp]); Q^T to XT
+// after the last pass (if given); R to Racc (if given).
 template <class T>
 static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void* XTlo, float* Racc,
-                       int passes, hipStream_t st) {
+                       int passes, float* Qlast, hipStream_t st) {
   const Dims& dm = c->dm;
   const int nmat = 2 * dm.B, ellp = ws.ellp;
   const size_t lds_gram = (size_t)ellp * (ellp + 1) * sizeof(float);
@@ -1026,7 +1029,8 @@ static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void*
     }
     hipLaunchKernelGGL(k_chol, dim3(nmat), dim3(kCholThreads), lds_chol, st, Gsum, 1, dm.ell, ellp,
                        ws.Rinv, pass == 0 ? nullptr : Racc, Racc);
-    hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, M, ellp, ws.Rinv,
+    hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, last ? Qlast : ws.Y, M,
+                       ellp, ws.Rinv,
                        static_cast<T*>(last ? XT : nullptr), static_cast<T*>(last ? XTlo : nullptr),
                        (size_t)ellp * ws.M, tiles_m, arows);
   }
@@ -1127,22 +1131,22 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   // fp32 Q; with Q rounded to 8 bits here the two would disagree at 2^-9).
   e = gemm<T>(c, k, v, ws.omT, nullptr, ws.Y, false, (size_t)ellp * dm.W, st);
   if (e != hipSuccess) return fail_stage(e, "A Omega");
-  e = orth<T>(c, ws, dm.N, ws.XT, dm.q == 0 ? ws.XTlo : nullptr, nullptr, dm.q == 0 ? 2 : 1, st);
+  e = orth<T>(c, ws, dm.N, ws.XT, dm.q == 0 ? ws.XTlo : nullptr, nullptr, dm.q == 0 ? 2 : 1,
+              dm.q == 0 ? ws.Qn : nullptr, st);
   if (e != hipSuccess) return fail_stage(e, "orthonormalisation of A Omega");
   for (int it = 0; it < dm.q; ++it) {
     const bool final_basis = it == dm.q - 1;
     e = gemm<T>(c, k, v, ws.XT, nullptr, ws.Y, true, (size_t)ellp * ws.M, st);     // A^T Q
-    if (e == hipSuccess) e = orth<T>(c, ws, dm.W, ws.XT, nullptr, nullptr, 1, st);
+    if (e == hipSuccess) e = orth<T>(c, ws, dm.W, ws.XT, nullptr, nullptr, 1, nullptr, st);
     if (e == hipSuccess) e = gemm<T>(c, k, v, ws.XT, nullptr, ws.Y, false, (size_t)ellp * ws.M, st);  // A Q~
     if (e == hipSuccess)
-      e = orth<T>(c, ws, dm.N, ws.XT, final_basis ? ws.XTlo : nullptr, nullptr, final_basis ? 2 : 1, st);
+      e = orth<T>(c, ws, dm.N, ws.XT, final_basis ? ws.XTlo : nullptr, nullptr, final_basis ? 2 : 1,
+                  final_basis ? ws.Qn : nullptr, st);
     if (e != hipSuccess) return fail_stage(e, "power iteration");
   }
-  // keep Q (fp32) for U, then C^T = A^T Q and its QR
-  e = hipMemcpyAsync(ws.Qn, ws.Y, (size_t)nmat * dm.N * ellp * 4, hipMemcpyDeviceToDevice, st);
-  if (e == hipSuccess) e = gemm<T>(c, k, v, ws.XT, ws.XTlo, ws.Y, true, (size_t)ellp * ws.M, st);
-  if (e == hipSuccess) e = orth<T>(c, ws, dm.W, nullptr, nullptr, ws.Racc, 2, st);
-  if (e == hipSuccess) e = hipMemcpyAsync(ws.Qc, ws.Y, (size_t)nmat * dm.W * ellp * 4, hipMemcpyDeviceToDevice, st);
+  // Q (fp32, kept in Qn for U), then C^T = A^T Q and its QR (basis kept in Qc for B)
+  e = gemm<T>(c, k, v, ws.XT, ws.XTlo, ws.Y, true, (size_t)ellp * ws.M, st);
+  if (e == hipSuccess) e = orth<T>(c, ws, dm.W, nullptr, nullptr, ws.Racc, 2, ws.Qc, st);
   if (e != hipSuccess) return fail_stage(e, "projection C^T = A^T Q");
   const int jac_threads = std::min(1024, std::max(64, (16 * ((dm.ell + 1) / 2) + 63) / 64 * 64));
   hipLaunchKernelGGL(k_jacobi, dim3(nmat), dim3(jac_threads), lds_jac, st, ws.Racc, dm.ell, ellp, ws.PS,

@@ -42,8 +42,15 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return
 // Order-preserving map of a float score to an unsigned key (larger score -> larger key).
 // -0 is folded onto +0 so that equal scores give equal keys.
 __device__ __forceinline__ uint32_t score_key(float s) {
-  uint32_t u = __float_as_uint(s + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  // negative: all bits flipped; otherwise only the sign bit set
+  const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31);
+  return u ^ (neg | 0x80000000u);
+}
+
+// All ones when bit i of m is set, else zero (a select without a lane mask register).
+__device__ __forceinline__ uint32_t bit_mask(uint32_t m, int i) {
+  return static_cast<uint32_t>(-static_cast<int32_t>((m >> i) & 1u));
 }
 
 // 2^x with the hardware v_exp_f32 alone (exp2f adds a range check and rescale for

@@ -583,21 +583,23 @@ __device__ __forceinline__ void select_body(
     }
   }
 
+  // bit 4a+t: score of a real token of a present head
+  uint32_t vm = 0u;
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) {
+    const int nv = min(max(N - tok(a), 0), 4);
+    vm |= (my_on ? (1u << nv) - 1u : 0u) << (4 * a);
+  }
+
   if (select) {
     // ---- C. per-head range, linear bins, histogram, boundary bin
     {
-      uint32_t kmax = 0u, kmin = 0u;   // kmin holds ~key
+      uint32_t kmax = 0u, kmin = 0u;   // kmin holds ~key; absent scores add 0
 #pragma unroll
-      for (int a = 0; a < NACC; ++a) {
-        const int n0 = tok(a);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (n0 + t < N) {
-            const uint32_t k = score_key(sc[4 * a + t]);
-            kmax = max(kmax, k);
-            kmin = max(kmin, ~k);
-          }
-        }
+      for (int i = 0; i < KPL; ++i) {
+        const uint32_t k = score_key(sc[i]), m = bit_mask(vm, i);
+        kmax = max(kmax, k & m);
+        kmin = max(kmin, ~k & m);
       }
       kmax = head_max<HG>(kmax);
       kmin = head_max<HG>(kmin);
@@ -624,12 +626,7 @@ __device__ __forceinline__ void select_body(
       // back to back; any float maps to a bin inside the head's range
       uint32_t* hh = hist + my_h * HS;
 #pragma unroll
-      for (int a = 0; a < NACC; ++a) {
-        const int n0 = tok(a);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          atomicAdd(&hh[bin_of(sc[4 * a + t])], (my_on && n0 + t < N) ? 1u : 0u);
-      }
+      for (int i = 0; i < KPL; ++i) atomicAdd(&hh[bin_of(sc[i])], (vm >> i) & 1u);
     }
     lds_barrier();
     if (wave < nh) {
@@ -665,7 +662,7 @@ __device__ __forceinline__ void select_body(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int bn = static_cast<int>(bin_of(sc[4 * a + t]));
-          const bool ok = my_on && n0 + t < N;
+          const bool ok = (vm >> (4 * a + t)) & 1u;
           nib |= (ok && bn >= bwhole) ? (1u << t) : 0u;
           cbits |= (ok && mode_h == kRank && bn == bstar_h) ? (1u << (4 * a + t)) : 0u;
         }
@@ -906,6 +903,15 @@ __device__ __forceinline__ void select_body(
       }
       qhi[j] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
+    // block-diagonal B operands: a lane feeds only the dwords of its own slot and tile half
+    uint32_t om[NSL][2];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) om[sl][hf] = (sl == my_slot && hf == my_j) ? ~0u : 0u;
+    auto diag = [&](uint32_t x, uint32_t y, int sl) {
+      return __builtin_bit_cast(v8bf, make_uint4(x & om[sl][0], y & om[sl][0], x & om[sl][1], y & om[sl][1]));
+    };
     uint32_t selb = 0;   // bit 4a+t: token at full rank
 #pragma unroll
     for (int a = 0; a < NACC; ++a) {
@@ -916,20 +922,15 @@ __device__ __forceinline__ void select_body(
       for (int j = 0; j < NPM; ++j) {
         const int s = a * NPM + j;
         if (j < nph) {
-          const uint4 bo = my_j == 0 ? make_uint4(qhi[j].x, qhi[j].y, 0u, 0u)
-                                     : make_uint4(0u, 0u, qhi[j].x, qhi[j].y);
 #pragma unroll
-          for (int sl = 0; sl < NSL; ++sl) {
-            const uint4 bb = sl == my_slot ? bo : make_uint4(0u, 0u, 0u, 0u);
-            acc = mfma_bf16_k32(__builtin_bit_cast(v8bf, rb[s % PD][sl].raw),
-                                __builtin_bit_cast(v8bf, bb), acc);
-          }
+          for (int sl = 0; sl < NSL; ++sl)
+            acc = mfma_bf16_k32(__builtin_bit_cast(v8bf, rb[s % PD][sl].raw), diag(qhi[j].x, qhi[j].y, sl), acc);
         }
         if (s + PD < 2 * NSK) ld(s + PD);
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const bool ok = my_on && tok(a) + t < N;
+        const bool ok = (vm >> (4 * a + t)) & 1u;
         const bool full = ok && ((w >> t) & 1u);
         selb |= full ? (1u << (4 * a + t)) : 0u;
         sc[4 * a + t] = ok ? sl2 * (sc[4 * a + t] + (full ? acc[t] : 0.f)) : -INFINITY;
@@ -969,12 +970,15 @@ __device__ __forceinline__ void select_body(
     }
     // output rows (F5): thread = (head, 16-byte column chunk, row group); rows 0..r_pad-1
     // of a head are B_v rows, then its text V rows.  The first UP rows of each thread are
-    // requested as soon as the value pass has issued its last tile load
-    const int ounits = nh * LPR;
-    const int RS = nthr / ounits;
-    const int ounit = tid % ounits, rsub = tid / ounits;
-    const int ohl = ounit / LPR, occ = ounit - ohl * LPR;
-    const int og = ((h0 + ohl) * ginv_num) >> 16;
+    // requested as soon as the value pass has issued its last tile load.  Units cover all
+    // HG heads (a power of two: LPR is one here); units of absent heads read the last
+    // present head's rows and store nothing.
+    const int lpr_sh = 31 - __builtin_clz(LPR);
+    const int ounits = HG * LPR;
+    const int RS = nthr >> (lpr_sh + 2);
+    const int ounit = tid & (ounits - 1), rsub = tid >> (lpr_sh + 2);
+    const int ohl = ounit >> lpr_sh, occ = ounit & (LPR - 1);
+    const int og = ((h0 + min(ohl, nh - 1)) * ginv_num) >> 16;
     const int orows = r_pad + Tn;
     constexpr int UP = 8;
     Vec16<T> xo[UP];
@@ -996,22 +1000,19 @@ __device__ __forceinline__ void select_body(
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int a = 0; a < NACC; ++a) {
-      const uint32_t sb = selb >> (4 * a);
       const float* pv = sc + 4 * a;
       const uint32_t pa0 = pack_bf16x2(pv[0], pv[1]), pa1 = pack_bf16x2(pv[2], pv[3]);
-      const uint32_t ps0 = pack_bf16x2((sb & 1u) ? pv[0] : 0.f, (sb & 2u) ? pv[1] : 0.f);
-      const uint32_t ps1 = pack_bf16x2((sb & 4u) ? pv[2] : 0.f, (sb & 8u) ? pv[3] : 0.f);
-      const uint4 BA = my_j == 0 ? make_uint4(pa0, pa1, 0u, 0u) : make_uint4(0u, 0u, pa0, pa1);
-      const uint4 BS = my_j == 0 ? make_uint4(ps0, ps1, 0u, 0u) : make_uint4(0u, 0u, ps0, ps1);
+      // the same probabilities with those of tokens below full rank cleared
+      auto sel_p = [&](int t) { return __uint_as_float(__float_as_uint(pv[t]) & bit_mask(selb, 4 * a + t)); };
+      const uint32_t ps0 = pack_bf16x2(sel_p(0), sel_p(1)), ps1 = pack_bf16x2(sel_p(2), sel_p(3));
 #pragma unroll
       for (int p = 0; p < NPM; ++p) {
         const int s = NSK + a * NPM + p;
         if (p < NPr) {
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) {
-            const bool on = sl == my_slot;
-            const v8bf ba = __builtin_bit_cast(v8bf, on ? BA : z4);
-            const v8bf bs = __builtin_bit_cast(v8bf, on ? BS : z4);
+            const v8bf ba = diag(pa0, pa1, sl);
+            const v8bf bs = diag(ps0, ps1, sl);
             const v8bf av = __builtin_bit_cast(v8bf, rb[s % PD][sl].raw);
             if (16 * p + 16 <= rlo) {
               Z[p] = mfma_bf16_k32(av, ba, Z[p]);
@@ -1026,7 +1027,7 @@ __device__ __forceinline__ void select_body(
           }
         }
         if (s + PD < 2 * NSK) ld(s + PD);
-        if (s + PD == 2 * NSK - 1) load_out(min(rsub, RS - 1));   // right after the last tile load
+        if (s + PD == 2 * NSK - 1) load_out(rsub);   // right after the last tile load
       }
     }
     // lane l holds Z for latent columns 16p + 4lg + t and tile column c16: sum the
@@ -1086,8 +1087,8 @@ __device__ __forceinline__ void select_body(
       for (int idx = tid; idx < units * V; idx += nthr) {
         float o = 0.f;
         for (int r = 0; r < RS; ++r) o += red[(size_t)r * units * V + idx];
-        const int h2 = idx / d, j = idx - h2 * d;
-        fa.out[((size_t)b * Hq + h0 + h2) * d + j] = o / lfin[h2];
+        const int h2 = idx >> (lpr_sh + 3), j = idx & (d - 1);   // d = 8 LPR
+        if (h2 < nh) fa.out[((size_t)b * Hq + h0 + h2) * d + j] = o / lfin[h2];
       }
     }
   }
