@@ -36,6 +36,14 @@ SMALL = {
     "bf16_rank64_lo16": wl.LLAVA.replace(cfg_id=108, batch=2, n_q_heads=8, n_kv_heads=8, head_dim=64,
                                          n_tokens=300, n_text=10, rank=64, r_lo=16, top_k=75,
                                          grid=None, inner_dim=300),
+    # query heads not a multiple of 4: the last head group of the single-kernel decode and
+    # of the selector holds fewer heads (2 and 1)
+    "bf16_6_heads_gqa": wl.LLAVA.replace(cfg_id=109, batch=3, n_q_heads=6, n_kv_heads=3, head_dim=64,
+                                         n_tokens=150, n_text=7, rank=32, r_lo=16, top_k=40,
+                                         grid=None, inner_dim=150),
+    "bf16_5_heads": wl.LLAVA.replace(cfg_id=110, batch=2, n_q_heads=5, n_kv_heads=5, head_dim=32,
+                                     n_tokens=97, n_text=0, rank=48, r_lo=16, top_k=30, grid=None,
+                                     inner_dim=97),
 }
 
 
@@ -46,6 +54,15 @@ def test_decode_parity_small(gpu_lib, name):
     out, sel = run_decode(w, seqs, gpu_lib)
     err, flips = check_against_oracle(w, seqs, out, sel)
     print(f"{name}: max abs err {err:.3e}, band flips {flips}")
+
+
+@pytest.mark.parametrize("name", ["bf16_6_heads_gqa", "bf16_5_heads"])
+def test_decode_partial_head_group_split_path(gpu_lib, name):
+    """The same shapes through selection + split-N flash-decode + combine."""
+    w = SMALL[name]
+    seqs = make_inputs(w)
+    out, sel = run_decode(w, seqs, gpu_lib, splits=2)
+    check_against_oracle(w, seqs, out, sel)
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7])
@@ -134,6 +151,8 @@ def test_decode_is_deterministic(gpu_lib, name, splits):
 
 @pytest.mark.parametrize("name,splits,path", [("bf16_straddle_text", 0, "decode"),
                                               ("bf16_rank64_lo16", 0, "decode"),
+                                              ("bf16_6_heads_gqa", 0, "decode"),
+                                              ("bf16_5_heads", 0, "decode"),
                                               ("bf16_straddle_text", 2, "split"),
                                               ("bf16_rank128", 0, "split"),
                                               ("f32_text_long", 0, "split")])
