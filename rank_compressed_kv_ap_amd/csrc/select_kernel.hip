@@ -328,7 +328,7 @@ struct FusedArgs {
 // accumulation steps per wavefront (2, 3, 4 or 8).  FUSED: the same workgroup goes on
 // to the attention of its heads over all tokens, the text tokens and the output
 // projection (bf16 factors, HG = 4, r <= 64), so one kernel makes the whole step.
-template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0>
+template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0, bool MQ = false>
 __device__ __forceinline__ void select_body(
     const T* __restrict__ Uk, const StoreB<T>* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
@@ -404,7 +404,61 @@ __device__ __forceinline__ void select_body(
       x[u].load(Bk + ((size_t)b * r_pad + i) * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + seg * V);
     }
   };
-  if (vec) load_rows(wave * RPW + rw);
+  // bf16 rows with d a multiple of 32 (up to 128): latent queries and text scores on
+  // MFMA.  A wavefront takes (head, 16-row tile) pairs; lane l loads the 8 elements of
+  // row l%16 at d-offset 32 ks + 8 (l/16) of each 32-wide k step (its A operand) into
+  // the same registers the other path uses, and q_h, split into bf16 hi + lo, is the only
+  // non-zero column (0) of the B operand, so lanes 0, 16, 32, 48 end up holding the
+  // tile's 16 dot products.
+  // MQ: chosen at launch for bf16 rows with d a multiple of 32 up to 128
+  constexpr bool kBfRows = MQ && std::is_same<TB, bf16_t>::value;
+  constexpr bool mq = kBfRows;
+  const int nks = d >> 5;
+  const int qtiles = r_pad >> 4;                      // latent-row tiles per head
+  const int npair_q = nh * qtiles;
+  auto load_tile_rows = [&](Vec16<TB>(&dst)[XB], const TB* base, int row, int hl) {
+    if constexpr (kBfRows) {
+      const TB* src = base + (size_t)row * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < XB; ++ks)
+        if (ks < nks) dst[ks].load(src + 32 * ks);
+    }
+  };
+  // the tile's dot products with q_h (this lane's A operands in a)
+  auto tile_dot = [&](const Vec16<TB>(&a)[XB], int hl) {
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kBfRows) {
+      const uint32_t on = c16 == 0 ? ~0u : 0u;
+#pragma unroll
+      for (int ks = 0; ks < XB; ++ks) {
+        if (ks < nks) {
+          const float* qp = qh + hl * d + 32 * ks + 8 * lg;
+          const float4 q0 = *reinterpret_cast<const float4*>(qp);
+          const float4 q1 = *reinterpret_cast<const float4*>(qp + 4);
+          const float v[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hw[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+            lw[e] = pack_bf16x2(v[2 * e] - __uint_as_float(hw[e] << 16),
+                                v[2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u));
+          }
+          const v8bf av = __builtin_bit_cast(v8bf, a[ks].raw);
+          acc = mfma_bf16_k32(av, __builtin_bit_cast(v8bf, make_uint4(hw[0] & on, hw[1] & on, hw[2] & on, hw[3] & on)), acc);
+          acc = mfma_bf16_k32(av, __builtin_bit_cast(v8bf, make_uint4(lw[0] & on, lw[1] & on, lw[2] & on, lw[3] & on)), acc);
+        }
+      }
+    }
+    return acc;
+  };
+  if (mq) {
+    if (wave < npair_q) {
+      const int hl = wave / qtiles, it = wave - hl * qtiles;
+      load_tile_rows(x, Bk + (size_t)b * r_pad * W, 16 * it + c16, hl);
+    }
+  } else if (vec) {
+    load_rows(wave * RPW + rw);
+  }
   // one q value per thread (HG * d <= threads, checked at launch); stored unconditionally so the
   // load is never sunk behind the tile loads
   const int nq = nh * d;
@@ -414,7 +468,7 @@ __device__ __forceinline__ void select_body(
   const int nrt = nh * Tn;                   // text rows (head, token)
   // with no text the loads read B_k instead (always valid), so they stay unconditional
   const TB* __restrict__ tk = Tn > 0 ? static_cast<const TB*>(fa.text_k) : Bk;
-  Vec16<TB> xt[FUSED ? XB : 1];
+  Vec16<TB> xt[XB];
   auto load_text = [&](int r0) {
 #pragma unroll
     for (int u = 0; u < XB; ++u) {
@@ -460,7 +514,17 @@ __device__ __forceinline__ void select_body(
   }
   lds_barrier();
   // latent queries q~[h][i] = B_k[i, g*d : g*d+d] . q_h
-  if (vec) {
+  if (mq) {
+    for (int pair = wave; pair < npair_q; pair += nwv) {
+      const int hl = pair / qtiles, it = pair - hl * qtiles;
+      if (pair != wave) load_tile_rows(x, Bk + (size_t)b * r_pad * W, 16 * it + c16, hl);
+      const v4f acc = tile_dot(x, hl);
+      if (c16 == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qs[hl * r_pad + 16 * it + 4 * lg + t] = acc[t];
+      }
+    }
+  } else if (vec) {
     for (int r0 = wave * RPW + rw; r0 - rw < nrows; r0 += XB * rstep) {
       if (r0 != wave * RPW + rw) load_rows(r0);
 #pragma unroll
@@ -489,7 +553,19 @@ __device__ __forceinline__ void select_body(
   lds_barrier();
   // single-kernel decode: the text K rows are requested now, behind B_k, and scored
   // after the selection
-  if constexpr (FUSED) load_text(wave * RPW + rw);
+  const int ttiles = max((Tn + 15) >> 4, 1);          // 16-token tiles per head
+  const int npair_t = Tn > 0 ? nh * ttiles : 0;
+  auto load_text_tile = [&](int pair) {
+    const int hl = pair / ttiles, it = pair - hl * ttiles;
+    load_tile_rows(xt, tk + (size_t)b * Tn * W, min(16 * it + c16, Tn - 1), hl);
+  };
+  if constexpr (FUSED) {
+    if (mq) {
+      if (wave < npair_t) load_text_tile(wave);
+    } else {
+      load_text(wave * RPW + rw);
+    }
+  }
 
   // single-kernel decode: tiles of the full-rank score pass (U_k panels holding columns
   // >= r_lo) and then of the value pass (all U_v panels), 2 tiles per step, PD steps in
@@ -594,12 +670,29 @@ __device__ __forceinline__ void select_body(
   if (select) {
     // ---- C. per-head range, linear bins, histogram, boundary bin
     {
-      uint32_t kmax = 0u, kmin = 0u;   // kmin holds ~key; absent scores add 0
+      uint32_t kmax = 0u, kmin = 0u;   // kmin holds ~key; absent scores add nothing
+      if constexpr (FUSED) {
+        // branch-free (measured faster in the single-kernel decode; in the selection-only
+        // kernel with 8 steps it costs registers the branches do not)
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        const uint32_t k = score_key(sc[i]), m = bit_mask(vm, i);
-        kmax = max(kmax, k & m);
-        kmin = max(kmin, ~k & m);
+        for (int i = 0; i < KPL; ++i) {
+          const uint32_t k = score_key(sc[i]), m = bit_mask(vm, i);
+          kmax = max(kmax, k & m);
+          kmin = max(kmin, ~k & m);
+        }
+      } else {
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) {
+          const int n0 = tok(a);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (n0 + t < N) {
+              const uint32_t k = score_key(sc[4 * a + t]);
+              kmax = max(kmax, k);
+              kmin = max(kmin, ~k);
+            }
+          }
+        }
       }
       kmax = head_max<HG>(kmax);
       kmin = head_max<HG>(kmin);
@@ -880,7 +973,24 @@ __device__ __forceinline__ void select_body(
         }
       }
     };
-    if (Tn > 0) {
+    if (mq) {
+      for (int pair = wave; pair < npair_t; pair += nwv) {
+        const int hl = pair / ttiles, it = pair - hl * ttiles;
+        if (pair != wave) load_text_tile(pair);
+        const v4f acc = tile_dot(xt, hl);
+        if (c16 == 0) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int tok = 16 * it + 4 * lg + t;
+            if (tok < Tn) {
+              const float sv = acc[t] * fa.sl2;
+              sts[hl * Tn + tok] = sv;
+              atomicMax(&hmx[hl], score_key(sv));
+            }
+          }
+        }
+      }
+    } else if (Tn > 0) {
       text_scores(wave * RPW + rw);
       for (int r0 = wave * RPW + rw + XB * rstep; r0 - rw < nrt; r0 += XB * rstep) {
         load_text(r0);
@@ -1096,25 +1206,25 @@ __device__ __forceinline__ void select_body(
 
 // Selection only: writes the selection words and the latent queries for the split-N
 // flash-decode kernel.
-template <class T, int HG, int NPL, int NACC>
+template <class T, int HG, int NPL, int NACC, bool MQ>
 __global__ __launch_bounds__(1024) void k_select(
     const T* __restrict__ Uk, const StoreB<T>* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
     int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
     int r_lo, int top_k, FusedArgs fa) {
-  select_body<T, HG, NPL, NACC, false>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad, W, d,
-                                       G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
+  select_body<T, HG, NPL, NACC, false, 0, MQ>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad, W, d,
+                                              G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
 }
 
 // The whole decode step of four query heads of one sequence (bf16 factors).
-template <int NPL, int NACC, int NPX>
+template <int NPL, int NACC, int NPX, bool MQ>
 __global__ __launch_bounds__(1024) void k_decode(
     const bf16_t* __restrict__ Uk, const bf16_t* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
     int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
     int r_lo, int top_k, FusedArgs fa) {
-  select_body<bf16_t, 4, NPL, NACC, true, NPX>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad,
-                                               W, d, G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
+  select_body<bf16_t, 4, NPL, NACC, true, NPX, MQ>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad,
+                                                   W, d, G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1144,7 +1254,7 @@ static SelPlan select_plan(const Dims& dm, int r_lo, bool single_kernel) {
   return pl;
 }
 
-template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0>
+template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0, bool MQ = false>
 static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, int top_k,
                                   int32_t* sel_out, int waves, const FusedArgs& fa, hipStream_t st,
                                   const KernelEvents& ev) {
@@ -1155,19 +1265,19 @@ static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, i
   if ((dm.nblk + 8 / HG - 1) / (8 / HG) > waves * NACC) return hipErrorInvalidValue;
   if (HG * dm.d > 64 * waves) return hipErrorInvalidValue;
   const void* fn;
-  if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<NPL, NACC, NPX>);
-  else fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC>);
+  if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<NPL, NACC, NPX, MQ>);
+  else fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC, MQ>);
   static std::atomic<uint32_t> lds_set{0};
   hipError_t e = ensure_lds_limit(fn, 160 * 1024, lds_set);
   if (e != hipSuccess) return e;
   const int grid = ((dm.B + 7) / 8) * 8 * HGN;
   if constexpr (FUSED)
-    hipExtLaunchKernelGGL((k_decode<NPL, NACC, NPX>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
+    hipExtLaunchKernelGGL((k_decode<NPL, NACC, NPX, MQ>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
                           ev.stop, 0, static_cast<const T*>(c->Uk), static_cast<const T*>(c->Bk), q,
                           c->qt, c->mask, sel_out, dm.B, dm.N, dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d,
                           dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo, top_k, fa);
   else
-    hipExtLaunchKernelGGL((k_select<T, HG, NPL, NACC>), dim3(grid), dim3(64 * waves), lds, st,
+    hipExtLaunchKernelGGL((k_select<T, HG, NPL, NACC, MQ>), dim3(grid), dim3(64 * waves), lds, st,
                           ev.start, ev.stop, 0, static_cast<const T*>(c->Uk),
                           static_cast<const StoreB<T>*>(c->Bk), q, c->qt, c->mask, sel_out, dm.B, dm.N,
                           dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d, dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo,
@@ -1184,9 +1294,14 @@ static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, i
   fa.keys = keys;
   fa.keys_per_head = keys_per_head ? 1 : 0;
   fa.Usc = reinterpret_cast<const bf16_t*>(c->Usc);
+  // latent queries on MFMA for bf16 B_k rows with d a multiple of 32 up to 128 (not
+  // with 8 steps of four heads, whose registers are already spilling: measured slower)
+  constexpr bool kMq = !std::is_same<T, float>::value;
+  const bool mq = kMq && c->dm.d % 32 == 0 && c->dm.d <= 128 && (pl.NACC <= 4 || pl.HG == 1);
 #define AP_SEL(HGV, NPLV, NACCV)                                                        \
   if (pl.HG == HGV && pl.NPL == NPLV && pl.NACC == NACCV)                               \
-    return launch_select_v<T, HGV, NPLV, NACCV, false>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
+    return mq ? launch_select_v<T, HGV, NPLV, NACCV, false, 0, kMq>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev) \
+              : launch_select_v<T, HGV, NPLV, NACCV, false>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
   AP_SEL(4, 1, 2)
   AP_SEL(4, 1, 3)
   AP_SEL(4, 1, 4)
@@ -1241,12 +1356,15 @@ hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, in
   // r = 64 (4 panels) with r_lo = 16: the panel split known at compile time (variants
   // that fit the registers without spilling)
   const bool exact = c->dm.NP == 4 && r_lo == 16 * pl.NPL;
+  // latent queries and text scores on MFMA: d a multiple of 32 up to 128
+  const bool mq = c->dm.d % 32 == 0 && c->dm.d <= 128;
 #define AP_FUS(NPLV, NACCV)                                                             \
   if (pl.NPL == NPLV && pl.NACC == NACCV)                                               \
     return launch_select_v<bf16_t, 4, NPLV, NACCV, true, 0>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
 #define AP_FUS_X(NPLV, NACCV)                                                           \
   if (pl.NPL == NPLV && pl.NACC == NACCV)                                               \
-    return exact ? launch_select_v<bf16_t, 4, NPLV, NACCV, true, 4>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev) \
+    return exact ? (mq ? launch_select_v<bf16_t, 4, NPLV, NACCV, true, 4, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev) \
+                       : launch_select_v<bf16_t, 4, NPLV, NACCV, true, 4>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev)) \
                  : launch_select_v<bf16_t, 4, NPLV, NACCV, true, 0>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
   AP_FUS_X(1, 2)
   AP_FUS_X(1, 3)
