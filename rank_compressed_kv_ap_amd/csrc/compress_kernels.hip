@@ -120,7 +120,12 @@ __global__ __launch_bounds__(256) void k_omega_copy(const float* __restrict__ om
 // (software pipelining: the loads of slice s+1 are in flight during the MFMAs of s).
 constexpr int kGemmBM = 128, kGemmBK = 64, kGemmLdsStride = kGemmBK + 8;  // padded bf16 row
 
-template <class T, bool TRANS, int NT, bool SPLIT>
+// VEC (W and K multiples of 8, K >= 8): every load of a slice is issued unconditionally,
+// clamped in bounds, so the compiler tracks the slice in flight exactly and waits only
+// for the slice being staged.  Past the edge of K the X^T values are zeroed, which
+// cancels the clamped (finite) A values they meet; A values past M only reach output
+// rows that are not stored.  Otherwise per-element fallbacks for unaligned rows.
+template <class T, bool TRANS, int NT, bool SPLIT, bool VEC>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kmat,
                                                         const T* __restrict__ Vmat,
                                                         const T* __restrict__ XT,
@@ -166,7 +171,38 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
     uint4 x[XU];
     uint4 xl[SPLIT ? XU : 1];
   };
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
   auto load_slice = [&](int k0, Slice& sl) {
+    if constexpr (VEC) {
+      if (!TRANS) {
+        // rows (tid >> 3) + 32 h, k = k0 + 8 (tid & 7) .. +7 (a run lies wholly inside K or past it)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int row = (tid >> 3) + 32 * h, gk = k0 + (tid & 7) * 8;
+          const uint4 t = *reinterpret_cast<const uint4*>(A + (size_t)min(m0 + row, M - 1) * W + min(gk, K - 8));
+          sl.a[h] = t;
+        }
+      } else {
+        // k rows 4 (tid >> 4) + h, m = m0 + 8 (tid & 15) .. +7
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int gk = k0 + 4 * (tid >> 4) + h, gm = m0 + (tid & 15) * 8;
+          sl.a[h] = *reinterpret_cast<const uint4*>(A + (size_t)min(gk, K - 1) * W + min(gm, M - 8));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < XU; ++u) {
+        const int idx = min(tid + u * kGemmThreads, XR * 8 - 1);
+        const int j = idx >> 3, gk = k0 + 8 * (idx & 7);
+        const size_t off = (size_t)j * K + min(gk, K - 8);
+        const uint4 t = *reinterpret_cast<const uint4*>(X + off);
+        sl.x[u] = gk < K ? t : z4;
+        if constexpr (SPLIT) {
+          const uint4 tl = *reinterpret_cast<const uint4*>(Xl + off);
+          sl.xl[u] = gk < K ? tl : z4;
+        }
+      }
+    } else {
     if (!TRANS) {
       // rows (tid >> 3) + 32 h, k = k0 + 8 (tid & 7) .. +7
 #pragma unroll
@@ -215,6 +251,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
         if constexpr (SPLIT) sl.xl[u] = pack8(tl);
       }
     }
+    }
   };
   auto stage = [&](const Slice& sl) {
     if (!TRANS) {
@@ -246,13 +283,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
     }
   };
 
-  Slice cur, nxt;
-  load_slice(0, cur);
-  for (int k0 = 0; k0 < K; k0 += kGemmBK) {
-    const bool more = k0 + kGemmBK < K;
-    if (more) load_slice(k0 + kGemmBK, nxt);   // in flight during this slice's MFMAs
-    stage(cur);
-    __syncthreads();
+  auto multiply = [&]() {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       v8bf ab[2];
@@ -275,6 +306,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
         }
       }
     }
+  };
+  Slice cur, nxt;
+  load_slice(0, cur);
+  for (int k0 = 0; k0 < K; k0 += kGemmBK) {
+    const bool more = k0 + kGemmBK < K;
+    if (more) load_slice(k0 + kGemmBK, nxt);   // in flight during this slice's MFMAs
+    stage(cur);
+    __syncthreads();
+    multiply();
     __syncthreads();
     if (more) cur = nxt;
   }
@@ -952,11 +992,18 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int tiles_m = (M + kGemmBM - 1) / kGemmBM;
     const dim3 grid(nmat * tiles_m);
-#define AP_GEMM_LAUNCH(TR, NTV, SP)                                                                     \
-  hipLaunchKernelGGL((k_gemm<bf16_t, TR, NTV, SP>), grid, dim3(kGemmThreads), 0, st,                   \
+    const int K = trans ? dm.N : dm.W;
+    const bool vec = dm.W % 8 == 0 && K % 8 == 0 && K >= 8;
+#define AP_GEMM_LAUNCH_V(TR, NTV, SP, VC)                                                               \
+  hipLaunchKernelGGL((k_gemm<bf16_t, TR, NTV, SP, VC>), grid, dim3(kGemmThreads), 0, st,               \
                      static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),                     \
                      static_cast<const bf16_t*>(XT), static_cast<const bf16_t*>(XTlo), Y, dm.N, dm.W, \
                      ellp, x_stride, tiles_m)
+#define AP_GEMM_LAUNCH(TR, NTV, SP)                                                                     \
+  do {                                                                                                  \
+    if (vec) AP_GEMM_LAUNCH_V(TR, NTV, SP, true);                                                       \
+    else AP_GEMM_LAUNCH_V(TR, NTV, SP, false);                                                          \
+  } while (0)
 #define AP_GEMM_CASE(NTV)                                                                              \
   case NTV:                                                                                            \
     if (trans && XTlo != nullptr) AP_GEMM_LAUNCH(true, NTV, true);                                     \
@@ -970,6 +1017,7 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
     }
 #undef AP_GEMM_CASE
 #undef AP_GEMM_LAUNCH
+#undef AP_GEMM_LAUNCH_V
   } else {
     if (trans)
       hipLaunchKernelGGL((k_gemm_f32<true>), grid_1d((size_t)nmat * M * ellp), dim3(256), 0, st,
