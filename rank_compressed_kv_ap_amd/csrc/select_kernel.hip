@@ -6,8 +6,9 @@
 // the k largest are chosen, ties to the lower token index.
 //
 // One workgroup per (sequence, group of HG query heads), 16 wavefronts:
-//  A. latent queries q~_h = B_k[:, head g's columns] q_h (also written out for the
-//     flash-decode kernel), with the first U_k low-panel tiles already in flight;
+//  A. latent queries q~_h = B_k[:, head g's columns] q_h (on MFMA for bf16 rows with d a
+//     multiple of 32 up to 128; also written out for the flash-decode kernel), with the
+//     first U_k low-panel tiles already in flight;
 //  B. low-rank scores of every token on MFMA.  The 16 output columns of a 16x16x32 tile
 //     are (token block, tile half, head) triples: the latent-query operand of a column
 //     is non-zero only in the k-slots of its own half and only for its own block, so
@@ -953,9 +954,10 @@ __device__ __forceinline__ void select_body(
     // during its LDS-bound phases slow them more than they gain)
 #pragma unroll
     for (int s = 0; s < PD; ++s) ld(s);
-    // ---- F1. text scores in log2 units (LPR lanes per text row), running max per head
-    // the first XB * rstep rows come from the loads issued after the latent queries;
-    // any further rows are loaded here
+    // ---- F1. text scores in log2 units, running max per head: on MFMA, one (head,
+    // 16-token tile) pair per wavefront, or LPR lanes per text row; the first pair or
+    // XB * rstep rows come from the loads issued after the latent queries, any further
+    // ones are loaded here
     auto text_scores = [&](int r0) {
 #pragma unroll
       for (int u = 0; u < XB; ++u) {
