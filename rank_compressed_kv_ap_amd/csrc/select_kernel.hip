@@ -1296,10 +1296,9 @@ static hipError_t launch_select_t(const ap_cache* c, const float* q, int r_lo, i
   fa.keys = keys;
   fa.keys_per_head = keys_per_head ? 1 : 0;
   fa.Usc = reinterpret_cast<const bf16_t*>(c->Usc);
-  // latent queries on MFMA for bf16 B_k rows with d a multiple of 32 up to 128 (not
-  // with 8 steps of four heads, whose registers are already spilling: measured slower)
+  // latent queries on MFMA for bf16 B_k rows with d a multiple of 32 up to 128
   constexpr bool kMq = !std::is_same<T, float>::value;
-  const bool mq = kMq && c->dm.d % 32 == 0 && c->dm.d <= 128 && (pl.NACC <= 4 || pl.HG == 1);
+  const bool mq = kMq && c->dm.d % 32 == 0 && c->dm.d <= 128;
 #define AP_SEL(HGV, NPLV, NACCV)                                                        \
   if (pl.HG == HGV && pl.NPL == NPLV && pl.NACC == NACCV)                               \
     return mq ? launch_select_v<T, HGV, NPLV, NACCV, false, 0, kMq>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev) \
