@@ -794,9 +794,12 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
         g = group_sum(g, 16);
         if (g == 0.f || fabsf(g) <= 3e-6f * sqrtf(a * bsum)) continue;
         if (l16 == 0) rotated = 1u;
-        const float zeta = (bsum - a) / (2.f * g);
-        const float t = copysignf(1.f, zeta) / (fabsf(zeta) + sqrtf(1.f + zeta * zeta));
-        const float c = 1.f / sqrtf(1.f + t * t), s = c * t;
+        // rotation angle from the hardware reciprocal and reciprocal square root (about
+        // 1 ulp each): any rotation close to the exact one is orthogonal to within
+        // rounding (c^2 + s^2 = 1), and the next sweep measures what is left
+        const float zeta = (bsum - a) * __builtin_amdgcn_rcpf(2.f * g);
+        const float t = copysignf(__builtin_amdgcn_rcpf(fabsf(zeta) + __builtin_amdgcn_sqrtf(fmaf(zeta, zeta, 1.f))), zeta);
+        const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), s = c * t;
         for (int i = l16; i < ellp; i += 16) {
           const float x = Mj[i * S + p], y = Mj[i * S + qq];
           Mj[i * S + p] = c * x - s * y;
