@@ -44,6 +44,10 @@ SMALL = {
     "bf16_5_heads": wl.LLAVA.replace(cfg_id=110, batch=2, n_q_heads=5, n_kv_heads=5, head_dim=32,
                                      n_tokens=97, n_text=0, rank=48, r_lo=16, top_k=30, grid=None,
                                      inner_dim=97),
+    # one latent panel (r = 16): a single 16-row latent-query tile per head
+    "bf16_rank16": wl.LLAVA.replace(cfg_id=111, batch=3, n_q_heads=8, n_kv_heads=4, head_dim=128,
+                                    n_tokens=130, n_text=20, rank=16, r_lo=4, top_k=33, grid=None,
+                                    inner_dim=130),
 }
 
 
@@ -56,7 +60,7 @@ def test_decode_parity_small(gpu_lib, name):
     print(f"{name}: max abs err {err:.3e}, band flips {flips}")
 
 
-@pytest.mark.parametrize("name", ["bf16_6_heads_gqa", "bf16_5_heads"])
+@pytest.mark.parametrize("name", ["bf16_6_heads_gqa", "bf16_5_heads", "bf16_rank16"])
 def test_decode_partial_head_group_split_path(gpu_lib, name):
     """The same shapes through selection + split-N flash-decode + combine."""
     w = SMALL[name]
@@ -153,6 +157,7 @@ def test_decode_is_deterministic(gpu_lib, name, splits):
                                               ("bf16_rank64_lo16", 0, "decode"),
                                               ("bf16_6_heads_gqa", 0, "decode"),
                                               ("bf16_5_heads", 0, "decode"),
+                                              ("bf16_rank16", 0, "decode"),
                                               ("bf16_straddle_text", 2, "split"),
                                               ("bf16_rank128", 0, "split"),
                                               ("f32_text_long", 0, "split")])
