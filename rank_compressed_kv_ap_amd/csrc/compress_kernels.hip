@@ -137,8 +137,18 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
   constexpr int XU = (XR * 8 + kGemmThreads - 1) / kGemmThreads;   // 16-byte X loads per thread
   __shared__ __align__(16) bf16_t As[kGemmBM * kGemmLdsStride];
   __shared__ __align__(16) bf16_t Xs[(SPLIT ? 2 : 1) * XR * kGemmLdsStride];
-  const int mat = blockIdx.x / tiles_m;
-  const int m0 = (blockIdx.x % tiles_m) * kGemmBM;
+  // workgroups are dealt to the 8 XCDs in turn: when the matrices come in eights, the
+  // row tiles of one matrix all land on one XCD, whose L2 then holds its X^T slices
+  int mat, tile;
+  if ((gridDim.x / tiles_m) % 8 == 0) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    mat = (slot / tiles_m) * 8 + xcd;
+    tile = slot % tiles_m;
+  } else {
+    mat = blockIdx.x / tiles_m;
+    tile = blockIdx.x % tiles_m;
+  }
+  const int m0 = tile * kGemmBM;
   const int b = mat >> 1;
   const T* A = ((mat & 1) ? Vmat : Kmat) + (size_t)b * N * W;
   const int M = TRANS ? W : N;
