@@ -40,7 +40,6 @@ constexpr int kSelCap = 128;     // boundary-bin tokens ranked exactly by compar
 enum SelMode : int { kNone = 0, kAll = 1, kWholeBin = 2, kRank = 3, kRadix = 4 };
 
 struct SelState {
-  float lo, mul;   // bin(s) = min(kSelBins - 1, (s - lo) * mul)
   int bstar;       // boundary bin
   int need;        // tokens still to take inside the boundary bin (radix: ties at tau)
   int cnt;         // tokens in the boundary bin
@@ -703,14 +702,15 @@ __device__ __forceinline__ void select_body(
       }
     }
     lds_barrier();
-    if (tid < nh) {
-      const float hi = key_score(rng[2 * tid]), lo = key_score(~rng[2 * tid + 1]);
-      const float range = hi - lo;
-      st[tid].lo = lo;
-      st[tid].mul = (range > 1e-30f && range < 3.0e38f) ? static_cast<float>(kSelBins - 1) / range : 0.f;
+    // bin(s) = min(kSelBins - 1, (s - lo) * mul): every lane derives its head's lo and
+    // mul from the range words itself (the same arithmetic in every lane of a head)
+    float lo_h = 0.f, mul_h = 0.f;
+    if (my_on) {
+      const float hi = key_score(rng[2 * my_h]);
+      lo_h = key_score(~rng[2 * my_h + 1]);
+      const float range = hi - lo_h;
+      mul_h = (range > 1e-30f && range < 3.0e38f) ? static_cast<float>(kSelBins - 1) / range : 0.f;
     }
-    lds_barrier();
-    const float lo_h = my_on ? st[my_h].lo : 0.f, mul_h = my_on ? st[my_h].mul : 0.f;
     // clamped in float first: any input (NaN included) gives a bin in [0, kSelBins)
     auto bin_of = [&](float s) {
       return static_cast<uint32_t>(fminf(fmaxf((s - lo_h) * mul_h, 0.f), static_cast<float>(kSelBins - 1)));
