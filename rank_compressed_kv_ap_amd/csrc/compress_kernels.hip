@@ -1047,7 +1047,7 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
 // Row split of the Gram of an M-row basis: about 1024 workgroups over all matrices,
 // at least 64 rows each.
 static void gram_split(int M, int nmat, int& rows, int& nsplit) {
-  int want = (1024 + nmat - 1) / std::max(nmat, 1);
+  int want = (512 + nmat - 1) / std::max(nmat, 1);
   want = std::max(1, std::min(want, (M + 63) / 64));
   rows = ((M + want - 1) / want + 63) / 64 * 64;
   nsplit = (M + rows - 1) / rows;
