@@ -630,7 +630,7 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
 }
 
 // Row tile of k_apply.
-static int apply_rows(int) { return 128; }
+static int apply_rows(int) { return 64; }
 
 // Q = Y Rinv for a tile of rows per workgroup (fp32 MFMA), written to Qout (Y itself for
 // a basis that is orthonormalised again, another buffer for a basis kept for the
@@ -643,7 +643,8 @@ __global__ __launch_bounds__(256) void k_apply(const float* Y, float* Qout, int 
                                                T* __restrict__ XTlo, size_t xt_mat_stride, int tiles_m,
                                                int rows) {
   extern __shared__ __align__(16) float sh[];
-  constexpr int kMaxRT = 2, kMaxCT = kMaxEll / 16;   // row tiles per wavefront (rows = 128)
+  constexpr int kMaxRT = 2, kMaxCT = kMaxEll / 16;   // row tiles per wavefront (rows <= 128)
+  const int nrt = rows / 64;                          // rows is 64 or 128
   const int S = ellp + 1;
   float* Ys = sh;                  // [rows][S]
   float* Rs = Ys + rows * S;       // [ellp][ellp]
@@ -697,6 +698,7 @@ __global__ __launch_bounds__(256) void k_apply(const float* Y, float* Qout, int 
 #pragma unroll
   for (int i = 0; i < kMaxRT; ++i) {
     const int rt = wave + 4 * i;
+    if (i >= nrt) break;
     for (int k0 = 0; k0 < ellp; k0 += 4) {
       const float a = Ys[(16 * rt + l16) * S + k0 + lg];
 #pragma unroll
@@ -708,6 +710,7 @@ __global__ __launch_bounds__(256) void k_apply(const float* Y, float* Qout, int 
 #pragma unroll
   for (int i = 0; i < kMaxRT; ++i) {
     const int rt = wave + 4 * i;
+    if (i >= nrt) break;
 #pragma unroll
     for (int c = 0; c < kMaxCT; ++c) {
       if (c >= T16) continue;
