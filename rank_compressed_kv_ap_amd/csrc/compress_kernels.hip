@@ -1047,7 +1047,7 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
   return hipGetLastError();
 }
 
-// Row split of the Gram of an M-row basis: about 1024 workgroups over all matrices,
+// Row split of the Gram of an M-row basis: about 512 workgroups over all matrices,
 // at least 64 rows each.
 static void gram_split(int M, int nmat, int& rows, int& nsplit) {
   int want = (512 + nmat - 1) / std::max(nmat, 1);
