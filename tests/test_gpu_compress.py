@@ -87,6 +87,9 @@ SMALL = {
                                                    inner_dim=128, oversample=0, power_iters=0), {}),
     "bf16_rank128": (wl.VIDEO.replace(cfg_id=206, batch=1, n_kv_heads=2, n_q_heads=2, n_tokens=600,
                                       frames=None, inner_dim=256, oversample=0), {}),
+    # 8 matrices: the product kernels deal each matrix's row tiles to one XCD
+    "bf16_eight_matrices": (wl.LLAVA.replace(cfg_id=209, batch=4, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                                             n_tokens=300, rank=24, grid=None, inner_dim=120), {}),
 }
 
 
