@@ -508,13 +508,31 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
   const int l16 = lane & 15, lg = lane >> 4;
   const int T = ellp / 16;
   const size_t e2 = (size_t)ellp * ellp;
-  // ---- sum of the partial Grams (fixed order), X = 0
-  const float* gp = Gpart + (size_t)mat * nsplit * e2;
-  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
-    float v = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) v += gp[sp * e2 + idx];
-    G[(idx / ellp) * S + idx % ellp] = v;
-    X[(idx / ellp) * S + idx % ellp] = 0.f;
+  // ---- sum of the partial Grams (fixed order), X = 0.  16-byte loads, a batch of 8 per
+  // thread issued before any is used (ellp^2 / 4 is a multiple of 64)
+  const float4* gp = reinterpret_cast<const float4*>(Gpart + (size_t)mat * nsplit * e2);
+  const int e4 = static_cast<int>(e2 / 4);
+  for (int i0 = 0; i0 < e4; i0 += 8 * kCholThreads) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = gp[min(i0 + u * kCholThreads + tid, e4 - 1)];
+    for (int sp = 1; sp < nsplit; ++sp)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float4 w = gp[(size_t)sp * e4 + min(i0 + u * kCholThreads + tid, e4 - 1)];
+        v[u].x += w.x; v[u].y += w.y; v[u].z += w.z; v[u].w += w.w;
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kCholThreads + tid;
+      if (i < e4) {
+        const int r = (4 * i) / ellp, c = 4 * i - r * ellp;
+        float* g = G + r * S + c;
+        g[0] = v[u].x; g[1] = v[u].y; g[2] = v[u].z; g[3] = v[u].w;
+        float* x = X + r * S + c;
+        x[0] = 0.f; x[1] = 0.f; x[2] = 0.f; x[3] = 0.f;
+      }
+    }
   }
   __syncthreads();
   // ---- shift; padded rows and columns become the identity
@@ -612,10 +630,28 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
   if (Rout == nullptr) return;
   __syncthreads();
   // ---- R = L^T Rprev
-  const float* Rp = Rprev ? Rprev + (size_t)mat * e2 : nullptr;
-  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
-    const int i = idx / ellp, j = idx % ellp;
-    X[i * S + j] = Rp ? Rp[idx] : (i == j ? 1.f : 0.f);
+  const float4* Rp = Rprev ? reinterpret_cast<const float4*>(Rprev + (size_t)mat * e2) : nullptr;
+  for (int i0 = 0; i0 < e4; i0 += 8 * kCholThreads) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + u * kCholThreads + tid, e4 - 1);
+      if (Rp) {
+        v[u] = Rp[i];
+      } else {
+        const int r = (4 * i) / ellp, c = 4 * i - r * ellp;
+        v[u] = make_float4(r == c, r == c + 1, r == c + 2, r == c + 3);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kCholThreads + tid;
+      if (i < e4) {
+        const int r = (4 * i) / ellp, c = 4 * i - r * ellp;
+        float* x = X + r * S + c;
+        x[0] = v[u].x; x[1] = v[u].y; x[2] = v[u].z; x[3] = v[u].w;
+      }
+    }
   }
   __syncthreads();
   float* Ro = Rout + (size_t)mat * e2;
