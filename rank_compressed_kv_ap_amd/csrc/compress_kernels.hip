@@ -561,8 +561,10 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
       for (int c = 0; c < 16; ++c) row[c] = G[(c0 + li) * S + c0 + c];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float d = sqrtf(fmaxf(lane_bcast(row[j], j), 1e-30f));
-        const float inv = 1.f / d;
+        // hardware square root and reciprocal (about 1 ulp each): the second pass of the
+        // orthonormalisation removes what the first leaves
+        const float d = __builtin_amdgcn_sqrtf(fmaxf(lane_bcast(row[j], j), 1e-30f));
+        const float inv = __builtin_amdgcn_rcpf(d);
         row[j] = lane == j ? d : (lane > j ? row[j] * inv : 0.f);
 #pragma unroll
         for (int k = j + 1; k < 16; ++k) row[k] = fmaf(-row[j], lane_bcast(row[j], k), row[k]);
@@ -574,7 +576,7 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
         float v = lane == i ? 1.f : 0.f;
 #pragma unroll
         for (int k = 0; k < i; ++k) v = fmaf(-lane_bcast(row[k], i), x[k], v);
-        x[i] = v / lane_bcast(row[i], i);
+        x[i] = v * __builtin_amdgcn_rcpf(lane_bcast(row[i], i));
       }
       if (lane < 16) {
 #pragma unroll
