@@ -890,6 +890,38 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
 }
 
 // ================================================================ assembly
+// Stages a rows x cols block of fp32 (cols a multiple of 4; global rows 16-byte aligned
+// with stride gs, cols <= gs) into LDS with row stride ls: 16-byte loads, 8 per thread
+// issued before any is stored.  Rows >= vrows (vrows >= 1) and columns >= vcols read
+// as zero; their loads are clamped into the block.
+__device__ __forceinline__ void stage_f32(float* dst, int ls, const float* src, int gs, int rows, int cols,
+                                          int vrows, int vcols) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int c4 = cols / 4, n4 = rows * c4;
+  for (int i0 = 0; i0 < n4; i0 += 8 * nthr) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + u * nthr + tid, n4 - 1);
+      const int r = i / c4, c = 4 * (i - r * c4);
+      v[u] = *reinterpret_cast<const float4*>(src + (size_t)min(r, vrows - 1) * gs + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * nthr + tid;
+      if (i < n4) {
+        const int r = i / c4, c = 4 * (i - r * c4);
+        const bool live = r < vrows;
+        float* d = dst + r * ls + c;
+        d[0] = live && c < vcols ? v[u].x : 0.f;
+        d[1] = live && c + 1 < vcols ? v[u].y : 0.f;
+        d[2] = live && c + 2 < vcols ? v[u].z : 0.f;
+        d[3] = live && c + 3 < vcols ? v[u].w : 0.f;
+      }
+    }
+  }
+}
+
 // U[n][i] = sum_j Qn[n][j] PS[j][i] (i < r) into the decode tiles of one 32-token block;
 // the block's 32 rows of Qn and the r_pad used columns of PS are staged in LDS.
 template <class T>
@@ -905,15 +937,8 @@ __global__ __launch_bounds__(256) void k_assemble_u(const float* __restrict__ Qn
   const bool vl = mat & 1;
   const float* Q = Qn + (size_t)mat * N * ellp;
   const float* P = PS + (size_t)mat * ellp * ellp;
-  for (int idx = threadIdx.x; idx < 32 * ellp; idx += blockDim.x) {
-    const int rr = idx / ellp, j = idx % ellp;
-    const int token = kBlockTok * t + rr;
-    Qs[rr * (ellp + 1) + j] = token < N ? Q[(size_t)token * ellp + j] : 0.f;
-  }
-  for (int idx = threadIdx.x; idx < ellp * rp; idx += blockDim.x) {
-    const int j = idx / rp, col = idx % rp;
-    Ps[idx] = col < r ? P[j * ellp + col] : 0.f;
-  }
+  stage_f32(Qs, ellp + 1, Q + (size_t)kBlockTok * t * ellp, ellp, 32, ellp, N - kBlockTok * t, ellp);
+  stage_f32(Ps, rp, P, ellp, ellp, rp, ellp, r);
   __syncthreads();
   T* base = Ukv + (vl ? (size_t)NP * kBlockElems : 0);
   for (int idx = threadIdx.x; idx < NP * kBlockElems; idx += blockDim.x) {
@@ -949,15 +974,8 @@ __global__ __launch_bounds__(256) void k_assemble_u4(const float* __restrict__ Q
   const bool vl = mat & 1;
   const float* Q = Qn + (size_t)mat * N * ellp;
   const float* P = PS + (size_t)mat * ellp * ellp;
-  for (int idx = threadIdx.x; idx < 32 * ellp; idx += blockDim.x) {
-    const int rr = idx / ellp, j = idx % ellp;
-    const int token = kBlockTok * t + rr;
-    Qs[rr * (ellp + 1) + j] = token < N ? Q[(size_t)token * ellp + j] : 0.f;
-  }
-  for (int idx = threadIdx.x; idx < ellp * rp; idx += blockDim.x) {
-    const int j = idx / rp, col = idx % rp;
-    Ps[idx] = col < r ? P[j * ellp + col] : 0.f;
-  }
+  stage_f32(Qs, ellp + 1, Q + (size_t)kBlockTok * t * ellp, ellp, 32, ellp, N - kBlockTok * t, ellp);
+  stage_f32(Ps, rp, P, ellp, ellp, rp, ellp, r);
   __syncthreads();
   for (int idx = threadIdx.x; idx < 32 * rp; idx += blockDim.x) {
     const int rr = idx / rp, col = idx % rp;
@@ -987,14 +1005,8 @@ __global__ __launch_bounds__(256) void k_assemble_b(const float* __restrict__ Qc
   const int w0 = (blockIdx.x % tiles_w) * 64;
   const float* Q = Qc + (size_t)mat * W * ellp;
   const float* Sm = Sv + (size_t)mat * ellp * ellp;
-  for (int idx = threadIdx.x; idx < 64 * ellp; idx += blockDim.x) {
-    const int ww = idx / ellp, j = idx % ellp;
-    Qs[ww * QS + j] = w0 + ww < W ? Q[(size_t)(w0 + ww) * ellp + j] : 0.f;
-  }
-  for (int idx = threadIdx.x; idx < ellp * r_pad; idx += blockDim.x) {
-    const int j = idx / r_pad, i = idx % r_pad;
-    Ss[idx] = i < r ? Sm[j * ellp + i] : 0.f;
-  }
+  stage_f32(Qs, QS, Q + (size_t)w0 * ellp, ellp, 64, ellp, W - w0, ellp);
+  stage_f32(Ss, r_pad, Sm, ellp, ellp, r_pad, ellp, r);
   __syncthreads();
   T* B = ((mat & 1) ? Bv : Bk) + (size_t)(mat >> 1) * r_pad * W;
   const int wb = (threadIdx.x & 15) * 4;          // 4 consecutive columns
