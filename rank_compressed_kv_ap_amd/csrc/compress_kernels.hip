@@ -833,8 +833,13 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
         int qq = 1 + (x1 - 1 + step) % (E - 1);
         if (p > qq) { const int t = p; p = qq; qq = t; }
         if (qq >= ell) continue;           // uniform over the 16-lane group
+        // rows ell..ellp-1 of Mj are zero: the loops run over ellp rows, unrolled with a
+        // wavefront-uniform bound so that the LDS reads of a column issue together
         float a = 0.f, bsum = 0.f, g = 0.f;
-        for (int i = l16; i < ell; i += 16) {
+#pragma unroll
+        for (int k = 0; k < kMaxEll / 16; ++k) {
+          if (16 * k >= ellp) break;
+          const int i = l16 + 16 * k;
           const float x = Mj[i * S + p], y = Mj[i * S + qq];
           a = fmaf(x, x, a);
           bsum = fmaf(y, y, bsum);
@@ -851,7 +856,10 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
         const float zeta = (bsum - a) * __builtin_amdgcn_rcpf(2.f * g);
         const float t = copysignf(__builtin_amdgcn_rcpf(fabsf(zeta) + __builtin_amdgcn_sqrtf(fmaf(zeta, zeta, 1.f))), zeta);
         const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), s = c * t;
-        for (int i = l16; i < ellp; i += 16) {
+#pragma unroll
+        for (int k = 0; k < kMaxEll / 16; ++k) {
+          if (16 * k >= ellp) break;
+          const int i = l16 + 16 * k;
           const float x = Mj[i * S + p], y = Mj[i * S + qq];
           Mj[i * S + p] = c * x - s * y;
           Mj[i * S + qq] = s * x + c * y;
