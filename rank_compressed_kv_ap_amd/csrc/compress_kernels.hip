@@ -931,15 +931,17 @@ __device__ __forceinline__ void stage_f32(float* dst, int ls, const float* src, 
 }
 
 // U[n][i] = sum_j Qn[n][j] PS[j][i] (i < r) into the decode tiles of one 32-token block;
-// the block's 32 rows of Qn and the r_pad used columns of PS are staged in LDS.
+// the block's 32 rows of Qn and the r_pad used columns of PS are staged in LDS, their
+// product formed on fp32 MFMA (16 x 16 tiles, one or two per wavefront) into LDS.
 template <class T>
 __global__ __launch_bounds__(256) void k_assemble_u(const float* __restrict__ Qn, const float* __restrict__ PS,
                                                     T* __restrict__ Ukv, int N, int ellp, int r, int NP,
                                                     int nblk) {
   extern __shared__ __align__(16) float sh[];
-  const int rp = 16 * NP;
+  const int rp = 16 * NP, ld = rp + 1;
   float* Qs = sh;                      // [32][ellp + 1]
   float* Ps = Qs + 32 * (ellp + 1);    // [ellp][rp]
+  float* Ub = Ps + ellp * rp;          // [32][ld]
   const int mat = blockIdx.x / nblk, t = blockIdx.x % nblk;
   const int b = mat >> 1;
   const bool vl = mat & 1;
@@ -947,6 +949,17 @@ __global__ __launch_bounds__(256) void k_assemble_u(const float* __restrict__ Qn
   const float* P = PS + (size_t)mat * ellp * ellp;
   stage_f32(Qs, ellp + 1, Q + (size_t)kBlockTok * t * ellp, ellp, 32, ellp, N - kBlockTok * t, ellp);
   stage_f32(Ps, rp, P, ellp, ellp, rp, ellp, r);
+  __syncthreads();
+  {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lg = lane >> 4;
+    for (int tl = wave; tl < 2 * NP; tl += 4) {   // tile tl: rows 16 (tl & 1), columns 16 (tl >> 1)
+      v4f acc = v4f{0, 0, 0, 0};
+      for (int kb = 0; kb < ellp; kb += 16)
+        acc = tile_mma<false, false, false>(Qs, 16 * (tl & 1), kb, ellp + 1, Ps, kb, 16 * (tl >> 1), rp, acc,
+                                            l16, lg);
+      tile_store(Ub, 16 * (tl & 1), 16 * (tl >> 1), ld, l16, lg, acc);
+    }
+  }
   __syncthreads();
   T* base = Ukv + (vl ? (size_t)NP * kBlockElems : 0);
   for (int idx = threadIdx.x; idx < NP * kBlockElems; idx += blockDim.x) {
@@ -960,9 +973,7 @@ __global__ __launch_bounds__(256) void k_assemble_u(const float* __restrict__ Qn
       rr = 16 * half + 4 * (lane >> 4) + e;
       col = 16 * p + (lane & 15);
     }
-    float v = 0.f;
-    for (int j = 0; j < ellp; ++j) v = fmaf(Qs[rr * (ellp + 1) + j], Ps[j * rp + col], v);
-    base[tile_base(b, p, t, NP, nblk) + within] = from_f32<T>(v);
+    base[tile_base(b, p, t, NP, nblk) + within] = from_f32<T>(Ub[rr * ld + col]);
   }
 }
 
@@ -1231,8 +1242,8 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   const size_t lds_jac = (size_t)(2 * ellp * (ellp + 1) + 2 * ellp) * sizeof(float);
   const size_t lds_apply = (size_t)(apply_rows(ellp) * (ellp + 1) + ellp * ellp) * sizeof(float);
   const bool u4 = dm.storage == AP_INT4;
-  const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP +
-                                (u4 ? 32 * (16 * dm.NP + 1) + 16 * dm.NP : 0)) * sizeof(float);
+  const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP + 32 * (16 * dm.NP + 1) +
+                                (u4 ? 16 * dm.NP : 0)) * sizeof(float);
   const size_t lds_b = (size_t)(64 * (ellp + 1) + ellp * dm.r_pad) * sizeof(float);
   const struct { const void* fn; size_t bytes; const char* name; } lds_req[] = {
       {reinterpret_cast<const void*>(&k_gram<8>), (size_t)ellp * (ellp + 1) * sizeof(float), "LDS size of k_gram"},
