@@ -204,3 +204,31 @@ def test_real_segments_pass_brute_pin():
 ])
 def test_segments_mutants_are_caught(old, new):
     assert not _segments_pin_ok(_mutant(dec, old, new))
+
+
+# ---------------------------------------------------------------- acceptance band
+def _band_pins_ok(mod):
+    from test_oracle_pins import BAND_CASES
+    try:
+        return all(np.flatnonzero(mod.band_mask(np.array(s), k)).tolist() == want
+                   for s, k, want in BAND_CASES)
+    except Exception:
+        return False
+
+
+def test_real_band_passes_pins():
+    assert _band_pins_ok(dec)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("tau = np.sort(s_lo_h)[::-1][k - 1]", "tau = np.sort(s_lo_h)[::-1][k]"),        # one token off
+    ("tau = np.sort(s_lo_h)[::-1][k - 1]", "tau = np.sort(s_lo_h)[k - 1]"),          # k-th smallest
+    ("rel * max(abs(tau), rel * float(np.max(np.abs(s_lo_h))))",
+     "rel * max(abs(tau), float(np.max(np.abs(s_lo_h))))"),                           # floor too wide
+    ("rel * max(abs(tau), rel * float(np.max(np.abs(s_lo_h))))", "rel * abs(tau)"),  # no floor
+    ("rel * max(abs(tau), rel * float(np.max(np.abs(s_lo_h))))",
+     "rel * max(tau, rel * float(np.max(np.abs(s_lo_h))))"),                          # signed cutoff
+    ("if k == 0 or k >= s_lo_h.shape[0]:", "if k == 0 or k > s_lo_h.shape[0]:"),     # k = N not empty
+])
+def test_band_mutants_are_caught(old, new):
+    assert not _band_pins_ok(_mutant(dec, old, new))

@@ -15,6 +15,9 @@ Each test names the pin it implements:
   P13 the moving-average importance selector over several steps: brute force,
       alpha = 0 closed form, weights that stay a distribution, shared == per-head
       for one head, first step == the low-rank-logit selector
+  P16 the acceptance band of the top-k comparison: hand-computed cases (the cutoff
+      is the k-th largest score, the relative width, the absolute floor for a cutoff
+      near zero, ties at the cutoff, empty for k = 0 and k = N)
 """
 import json
 import math
@@ -26,7 +29,7 @@ import torch
 
 import oracle
 from oracle.brute import decode_brute, decode_ema_brute
-from oracle.decode import decode_ema_steps, decode_ref, select_top
+from oracle.decode import band_mask, decode_ema_steps, decode_ref, select_top
 from oracle.jacobi import jacobi_svd
 from oracle.factorize import orth_mgs2, rsvd, round_to_storage
 from oracle import accounting
@@ -290,6 +293,53 @@ def test_select_top_ties_and_bounds():
     assert select_top(s, 4).tolist() == [1, 2, 3, 4]
     assert select_top(s, 0).tolist() == []
     assert select_top(s, 6).tolist() == [0, 1, 2, 3, 4, 5]
+
+
+# ------------------------------------------------------------------ P16
+# Each case is worked by hand: tau = the k-th largest score, width
+# w = 1e-3 * max(|tau|, 1e-3 * max|s|), band = {n : |s[n] - tau| <= w}.
+BAND_CASES = [
+    # distinct scores, k = 2: tau = 4, w = 4e-3 -> only the score 4 (index 4).  A tau one
+    # token off (the 3rd largest, 3) or the k-th smallest (2) gives another index.
+    ([5.0, 1.0, 3.0, 2.0, 4.0], 2, [4]),
+    # the same scores, k = 4: tau = 2 -> index 3
+    ([5.0, 1.0, 3.0, 2.0, 4.0], 4, [3]),
+    # a neighbour inside the relative width: k = 4 gives tau = 3, w = 3e-3; 3.002 is
+    # inside, 3.004 is not
+    ([3.002, 9.0, 3.0, 3.004, 0.0], 4, [0, 2]),
+    # ties at the cutoff: tau = 2, every copy of 2 is in the band
+    ([2.0, 2.0, 2.0, 1.0], 2, [0, 1, 2]),
+    # negative cutoff: tau = -2, w = 2e-3 (|tau| is used), so -2.001 is inside
+    ([-1.0, -2.0, -2.001, -3.0], 2, [1, 2]),
+    # cutoff near zero: tau = 4e-4; the floor 1e-3 * 1e-3 * max|s| = 1e-3 sets the width,
+    # so -3e-4 is inside and 0.5 is not (without the floor only index 1 would be)
+    ([1000.0, 4e-4, -3e-4, 0.5, -2.0], 3, [1, 2]),
+    # k = 0 and k = N: no cutoff, empty band
+    ([1.0, 2.0, 3.0], 0, []),
+    ([1.0, 2.0, 3.0], 3, []),
+    # k = N - 1: tau = the second smallest
+    ([1.0, 2.0, 3.0], 2, [1]),
+]
+
+
+@pytest.mark.parametrize("s,k,want", BAND_CASES)
+def test_p16_band_mask_hand_computed(s, k, want):
+    got = np.flatnonzero(band_mask(np.array(s), k)).tolist()
+    assert got == want
+
+
+def test_p16_band_holds_the_cutoff_token():
+    # on random scores the k-th largest itself is always in the band, and the band is
+    # symmetric around it: every member's score lies within the width of tau
+    g = np.random.default_rng(90)
+    for _ in range(50):
+        s = g.standard_normal(int(g.integers(2, 60)))
+        k = int(g.integers(1, s.shape[0]))
+        m = band_mask(s, k)
+        tau = np.sort(s)[::-1][k - 1]
+        w = 1e-3 * max(abs(tau), 1e-3 * np.max(np.abs(s)))
+        assert m[int(np.flatnonzero(s == tau)[0])]
+        assert np.all(np.abs(s[m] - tau) <= w) and np.all(np.abs(s[~m] - tau) > w)
 
 
 # ------------------------------------------------------------------ P11
