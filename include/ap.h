@@ -156,7 +156,9 @@ typedef struct {
   int32_t top_k;         /* tokens at full rank per (sequence, query head), 0 <= k <= N   */
   float scale;           /* softmax scale, finite and > 0 (usually 1/sqrt(d))              */
   int32_t n_text;        /* T >= 0 dense text tokens joining the softmax                  */
-  const void* text_k;    /* device [B][T][W] storage dtype (bf16 for AP_INT4), NULL iff T == 0 */
+  const void* text_k;    /* device [B][T][W] storage dtype (bf16 for AP_INT4), NULL iff T == 0
+                            (set with T == 0, or NULL with T > 0: AP_ERR_BAD_SHAPE /
+                            AP_ERR_NULL_ARG)                                             */
   const void* text_v;    /* device [B][T][W] storage dtype (bf16 for AP_INT4), NULL iff T == 0 */
   int32_t* sel_out;      /* optional device [B][Hq][top_k] int32: the selected token ids,
                             ascending per (sequence, head); NULL to skip                  */
@@ -195,6 +197,9 @@ typedef struct {
   const ap_cache* text_cache;
   int32_t text_r_lo;     /* 1 <= text_r_lo <= the text cache's rank (when text_cache set)   */
   int32_t text_top_k;    /* 0 <= text_top_k <= the text cache's n_tokens                    */
+  int32_t* text_sel_out; /* optional device [B][Hq][text_top_k] int32: the text segment's
+                            tokens taken at full rank, ascending per (sequence, head); NULL
+                            to skip (ignored without text_cache)                          */
 } ap_decode_params;
 
 enum { AP_SELECT_LOGIT = 0, AP_SELECT_EMA_TOKEN = 1, AP_SELECT_EMA_HEAD = 2 };

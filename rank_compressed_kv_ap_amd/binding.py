@@ -45,6 +45,7 @@ class DecodeParams(ctypes.Structure):
         ("select_mode", ctypes.c_int32), ("ema_alpha", ctypes.c_float), ("ema_first", ctypes.c_int32),
         ("importance", ctypes.c_void_p), ("ema_scratch", ctypes.c_void_p),
         ("text_cache", ctypes.c_void_p), ("text_r_lo", ctypes.c_int32), ("text_top_k", ctypes.c_int32),
+        ("text_sel_out", ctypes.c_void_p),
     ]
 
 
@@ -228,14 +229,16 @@ def decode(cache: Cache, q: torch.Tensor, *, r_lo: int, top_k: int, scale: float
            splits: int = 0, select: str = "logit", ema_alpha: float = 0.0,
            ema_first: bool = False, importance: Optional[torch.Tensor] = None,
            ema_scratch: Optional[torch.Tensor] = None, text_cache: Optional["Cache"] = None,
-           text_r_lo: int = 0, text_top_k: int = 0) -> torch.Tensor:
+           text_r_lo: int = 0, text_top_k: int = 0,
+           text_sel_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """ap_decode_attn: q [B, Hq*d] float32 -> out [B, Hq*d] float32.
 
     select: "logit" (current-step low-rank logit), "ema_token" or "ema_head" (moving
     average of the attention weights; importance float32 [B, N] or [B, Hq, N] is read
     and updated in place; ema_scratch float32 [B, Hq, N] is the step's workspace).
     text_cache: the text tokens factored apart (a second segment, its own text_r_lo and
-    text_top_k); text_k / text_v then hold the dense tokens appended since."""
+    text_top_k); text_k / text_v then hold the dense tokens appended since;
+    text_sel_out int32 [B, Hq, text_top_k] receives that segment's selected ids."""
     if out is None:
         out = torch.empty_like(q)
     n_text = 0 if text_k is None else text_k.shape[1]
@@ -243,7 +246,7 @@ def decode(cache: Cache, q: torch.Tensor, *, r_lo: int, top_k: int, scale: float
                      _ptr(text_v) if n_text else None, _ptr(sel_out), splits,
                      SELECT_MODES[select], ema_alpha, 1 if ema_first else 0, _ptr(importance),
                      _ptr(ema_scratch), text_cache.handle.value if text_cache is not None else None,
-                     text_r_lo, text_top_k)
+                     text_r_lo, text_top_k, _ptr(text_sel_out))
     _check(lib.ap_decode_attn(cache.handle, _ptr(q), _ptr(out), ctypes.byref(p), _stream()),
            "ap_decode_attn")
     return out

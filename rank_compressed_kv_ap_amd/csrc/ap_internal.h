@@ -108,10 +108,10 @@ hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float s
                           const KernelEvents& ev);
 // A small factored segment (its factors and one KV head's B rows fit 96 KB of LDS) of
 // every (sequence, query head) in one kernel: writes c->out_part and c->ml_final, merged
-// by another cache's combine.
+// by another cache's combine; sel_out (optional) receives the selected ids [B][Hq][top_k].
 bool text_seg_supported(const Dims& dm);
-hipError_t launch_text_seg(const ap_cache* c, const float* q, int r_lo, int top_k, float sl2,
-                           hipStream_t st, const KernelEvents& ev);
+hipError_t launch_text_seg(const ap_cache* c, const float* q, int r_lo, int top_k, int32_t* sel_out,
+                           float sl2, hipStream_t st, const KernelEvents& ev);
 hipError_t launch_ema_update(const ap_cache* c, const float* s, const float* ml, float* imp,
                              bool per_head, bool first, float alpha, hipStream_t st,
                              const KernelEvents& ev);

@@ -298,18 +298,22 @@ ap_status ap_cache_info(const ap_cache* c, ap_compress_params* p_out, size_t* fa
 }
 
 ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decode_params* p, void* stream) {
-  if (!c || !p) return fail(AP_ERR_NULL_ARG, "cache and params must not be NULL");
-  const Dims& dm = c->dm;
-  if (p->r_lo < 1 || p->r_lo > dm.r) return fail(AP_ERR_BAD_SHAPE, "need 1 <= r_lo <= rank");
-  if (p->top_k < 0 || p->top_k > dm.N) return fail(AP_ERR_BAD_SHAPE, "need 0 <= top_k <= n_tokens");
+  if (!p) return fail(AP_ERR_NULL_ARG, "params must not be NULL");
+  // checks of the parameters alone come first, then those against the cache
   if (!(std::isfinite(p->scale) && p->scale > 0.f)) return fail(AP_ERR_BAD_SHAPE, "scale must be finite and > 0");
   if (p->n_text < 0) return fail(AP_ERR_BAD_SHAPE, "n_text < 0");
+  if (p->n_text == 0 && (p->text_k || p->text_v))
+    return fail(AP_ERR_BAD_SHAPE, "text_k/text_v must be NULL when n_text == 0");
   if (p->splits < 0) return fail(AP_ERR_BAD_SHAPE, "splits < 0");
   if (p->select_mode < AP_SELECT_LOGIT || p->select_mode > AP_SELECT_EMA_HEAD)
     return fail(AP_ERR_BAD_SHAPE, "select_mode must be AP_SELECT_LOGIT, AP_SELECT_EMA_TOKEN or AP_SELECT_EMA_HEAD");
   const bool ema = p->select_mode != AP_SELECT_LOGIT;
   if (ema && !(p->ema_alpha >= 0.f && p->ema_alpha < 1.f))
     return fail(AP_ERR_BAD_SHAPE, "ema_alpha must satisfy 0 <= alpha < 1");
+  if (!c) return fail(AP_ERR_NULL_ARG, "cache must not be NULL");
+  const Dims& dm = c->dm;
+  if (p->r_lo < 1 || p->r_lo > dm.r) return fail(AP_ERR_BAD_SHAPE, "need 1 <= r_lo <= rank");
+  if (p->top_k < 0 || p->top_k > dm.N) return fail(AP_ERR_BAD_SHAPE, "need 0 <= top_k <= n_tokens");
   ap_cache* tc = const_cast<ap_cache*>(p->text_cache);   // its workspace is written
   if (tc) {
     const Dims& dt = tc->dm;
@@ -356,11 +360,11 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
     const KernelEvents evt = events(AP_KERNEL_TEXT);
     if (text_seg_supported(tc->dm)) {
       // small segment: the whole segment of a (sequence, head) in one workgroup
-      e = launch_text_seg(tc, q, p->text_r_lo, p->text_top_k, sl2, st, evt);
+      e = launch_text_seg(tc, q, p->text_r_lo, p->text_top_k, p->text_sel_out, sl2, st, evt);
     } else {
       int CBt = 0;
       const int St = split_plan(tc->dm, 0, &CBt);
-      e = launch_select(tc, q, p->text_r_lo, p->text_top_k, nullptr, nullptr, false, st,
+      e = launch_select(tc, q, p->text_r_lo, p->text_top_k, p->text_sel_out, nullptr, false, st,
                         KernelEvents{evt.start, nullptr});
       if (e == hipSuccess) e = launch_attn(tc, p->text_r_lo, sl2, St, CBt, nullptr, st, KernelEvents{});
       if (e == hipSuccess)

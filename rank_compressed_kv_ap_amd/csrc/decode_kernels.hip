@@ -898,8 +898,8 @@ template <class T>
 __global__ __launch_bounds__(kSegThreads) void k_text_seg(
     const T* __restrict__ Uk, const T* __restrict__ Uv, const bf16_t* __restrict__ Usc,
     const StoreB<T>* __restrict__ Bk, const StoreB<T>* __restrict__ Bv, const float* __restrict__ q,
-    float* __restrict__ xo, float* __restrict__ xml, int N, int nblk, int NP, int r, int W, int d,
-    int G, int Hq, int r_lo, int top_k, float sl2) {
+    float* __restrict__ xo, float* __restrict__ xml, int32_t* __restrict__ sel_out, int N, int nblk,
+    int NP, int r, int W, int d, int G, int Hq, int r_lo, int top_k, float sl2) {
   extern __shared__ __align__(16) float smem_s[];
   const int RP = 16 * NP, US = RP + 1;   // padded rows: no bank conflicts across tokens
   float* uk = smem_s;            // [N][US] U_k of the segment (columns >= r zero)
@@ -1024,7 +1024,20 @@ __global__ __launch_bounds__(kSegThreads) void k_text_seg(
       mloc = fmaxf(mloc, v);
     }
   }
-  const float M = block_red(mloc, true);
+  const float M = block_red(mloc, true);   // its barriers also publish fl[]
+  if (sel_out != nullptr && wave == 0) {
+    // the selected ids in ascending order: ballots over 64 tokens at a time
+    int32_t* so = sel_out + ((size_t)b * Hq + h) * top_k;
+    int carry = 0;
+    for (int n0 = 0; n0 < N; n0 += 64) {
+      const int n = n0 + lane;
+      const bool taken = n < N && fl[n] > 0.f;
+      const unsigned long long m = __ballot(taken);
+      const int pos = carry + __popcll(m & ((1ull << lane) - 1ull));
+      if (taken && pos < top_k) so[pos] = n;
+      carry += __popcll(m);
+    }
+  }
   float lsum = 0.f;
   for (int n = tid; n < N; n += kSegThreads) {
     const float e = hw_exp2(sc[n] - M);
@@ -1071,8 +1084,8 @@ bool text_seg_supported(const Dims& dm) {
          (cpr & (cpr - 1)) == 0;
 }
 
-hipError_t launch_text_seg(const ap_cache* c, const float* q, int r_lo, int top_k, float sl2,
-                           hipStream_t st, const KernelEvents& ev) {
+hipError_t launch_text_seg(const ap_cache* c, const float* q, int r_lo, int top_k, int32_t* sel_out,
+                           float sl2, hipStream_t st, const KernelEvents& ev) {
   const Dims& dm = c->dm;
   const size_t lds = text_seg_lds(dm);
   auto go = [&](auto tag) {
@@ -1083,7 +1096,7 @@ hipError_t launch_text_seg(const ap_cache* c, const float* q, int r_lo, int top_
     hipExtLaunchKernelGGL(k_text_seg<T>, dim3(dm.B * dm.Hq), dim3(kSegThreads), lds, st, ev.start,
                           ev.stop, 0, static_cast<const T*>(c->Uk), static_cast<const T*>(c->Uv),
                           reinterpret_cast<const bf16_t*>(c->Usc), static_cast<const StoreB<T>*>(c->Bk),
-                          static_cast<const StoreB<T>*>(c->Bv), q, c->out_part, c->ml_final, dm.N,
+                          static_cast<const StoreB<T>*>(c->Bv), q, c->out_part, c->ml_final, sel_out, dm.N,
                           dm.nblk, dm.NP, dm.r, dm.W, dm.d, dm.G, dm.Hq, r_lo, top_k, sl2);
     return hipGetLastError();
   };

@@ -104,3 +104,16 @@ def test_compress_rejects_large_probe_count_before_touching_memory():
                            ctypes.byref(out))
     assert st == b.AP_ERR_UNSUPPORTED and out.value is None
     assert b"128" in b.lib.ap_last_error()
+
+
+def test_decode_rejects_text_pointers_without_text_tokens():
+    # text_k / text_v are NULL iff n_text == 0; checked before the cache is looked at, so
+    # a NULL cache handle is safe here (CPU only)
+    from rank_compressed_kv_ap_amd import binding as b
+    for tk, tv in ((ctypes.c_void_p(64), None), (None, ctypes.c_void_p(64)),
+                   (ctypes.c_void_p(64), ctypes.c_void_p(128))):
+        dp = b.DecodeParams(4, 8, 0.1, 0, tk, tv, None, 0)
+        assert b.lib.ap_decode_attn(None, None, None, ctypes.byref(dp), None) == b.AP_ERR_BAD_SHAPE
+        assert b"n_text" in b.lib.ap_last_error()
+    dp = b.DecodeParams(4, 8, 0.1, 0, None, None, None, 0)
+    assert b.lib.ap_decode_attn(None, None, None, ctypes.byref(dp), None) == b.AP_ERR_NULL_ARG

@@ -228,3 +228,42 @@ def test_factor_roundtrip(gpu_lib):
         assert np.array_equal(B_k[b].float().cpu().numpy(), s["B_k"])
         assert np.array_equal(B_v[b].float().cpu().numpy(), s["B_v"])
     cache.free()
+
+
+def _decode_once(gpu_lib, w, cache, q, tk, tv, with_sel, timed=False):
+    sel = None
+    if with_sel:
+        sel = torch.full((w.batch, w.n_q_heads, w.top_k), -1, dtype=torch.int32, device="cuda")
+    if timed:
+        cache.timing_enable(1)
+    out = gpu_lib.decode(cache, q, r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, text_k=tk, text_v=tv,
+                         sel_out=sel, splits=0)
+    ms = None
+    if timed:
+        ms, n = cache.timing_read()
+        assert n == 1
+        cache.timing_enable(0)
+    torch.cuda.synchronize()
+    return out.cpu(), (sel.cpu().numpy() if sel is not None else None), ms
+
+
+@pytest.mark.parametrize("name", ["llava_full", "bf16_straddle_text", "bf16_rank64_lo16",
+                                  "bf16_6_heads_gqa", "bf16_rank16"])
+def test_decode_without_sel_out_is_the_checked_call(gpu_lib, name):
+    """The call the benchmark times: splits = 0 and no sel_out, through the single-kernel
+    decode.  Its output is compared with the oracle, and it must equal bit for bit the
+    output of the same call with sel_out (whose sets are checked as well)."""
+    w = wl.WORKLOADS[2] if name == "llava_full" else SMALL[name]
+    seqs = make_inputs(w, 3)
+    cache, q, tk, tv = upload_decode(w, seqs, gpu_lib)
+    out0, _, ms = _decode_once(gpu_lib, w, cache, q, tk, tv, with_sel=False, timed=True)
+    assert ms["decode"] > 0 and ms["select"] == ms["attn"] == ms["combine"] == 0, ms
+    out1, sel, _ = _decode_once(gpu_lib, w, cache, q, tk, tv, with_sel=True)
+    cache.free()
+    assert torch.equal(out0, out1)
+    out0 = out0.numpy()
+    err, _ = check_against_oracle(w, seqs, out0, None)
+    check_against_oracle(w, seqs, out1.numpy(), sel)
+    for b in range(len(seqs), w.batch):
+        assert np.array_equal(out0[b], out0[b % len(seqs)]), f"replica {b}"
+    print(f"{name}: max abs err {err:.3e} without sel_out")

@@ -59,7 +59,26 @@ def seg_of(w, s, r_lo, top_k):
                 r_lo=r_lo, top_k=top_k)
 
 
-def check(w, tw, vis, txt, out, sel, r_lo_t, k_t, dense=None):
+def check_set(got, want, s_lo, k, where):
+    """Selected ids ascending, and equal to the oracle's outside the 1e-3 band of the
+    k-th largest low-rank score."""
+    assert np.all(np.diff(got) > 0), (where, "ids not strictly ascending")
+    diff = set(got.tolist()) ^ set(want.tolist())
+    if diff:
+        band = band_mask(s_lo, k)
+        assert all(band[n] for n in diff), (where, sorted(diff)[:8])
+    return len(diff)
+
+
+def seg_s_lo(w, f, q, h, r_lo):
+    """A segment's low-rank scores for query head h (the ranking the oracle uses)."""
+    g = h // (w.n_q_heads // w.n_kv_heads)
+    cols = slice(g * w.head_dim, (g + 1) * w.head_dim)
+    qh = q[h * w.head_dim:(h + 1) * w.head_dim]
+    return w.scale * (f["U_k"][:, :r_lo] @ (f["B_k"][:r_lo, cols] @ qh))
+
+
+def check(w, tw, vis, txt, out, sel, r_lo_t, k_t, dense=None, tsel=None):
     tol = max(TOL[w.storage], TOL[tw.storage])
     worst = 0.0
     for b in range(len(vis)):
@@ -71,18 +90,15 @@ def check(w, tw, vis, txt, out, sel, r_lo_t, k_t, dense=None):
         err = float(np.max(np.abs(out[b] - ref["out"])))
         worst = max(worst, err)
         assert err <= tol, (b, err)
-        if sel is not None:
-            Hq = w.n_q_heads
-            for h in range(Hq):
-                diff = set(sel[b, h].tolist()) ^ set(ref["top"][0][h].tolist())
-                if diff:
-                    # band of the visual segment's low-rank scores
-                    g = h // (Hq // w.n_kv_heads)
-                    cols = slice(g * w.head_dim, (g + 1) * w.head_dim)
-                    U = seg_of(w, s, w.r_lo, w.top_k)["U_k"]
-                    s_lo = w.scale * (U[:, :w.r_lo] @ (s["B_k"][:w.r_lo, cols] @ s["q"][h * w.head_dim:(h + 1) * w.head_dim]))
-                    band = band_mask(s_lo, w.top_k)
-                    assert all(band[n] for n in diff), (b, h, sorted(diff)[:8])
+        for h in range(w.n_q_heads):
+            if sel is not None:
+                vs = seg_of(w, s, w.r_lo, w.top_k)
+                check_set(sel[b, h], ref["top"][0][h], seg_s_lo(w, vs, s["q"], h, w.r_lo), w.top_k,
+                          ("visual", b, h))
+            if tsel is not None:
+                ts = seg_of(tw, t, r_lo_t, k_t)
+                check_set(tsel[b, h], ref["top"][1][h], seg_s_lo(w, ts, s["q"], h, r_lo_t), k_t,
+                          ("text", b, h))
     return worst
 
 
@@ -105,10 +121,13 @@ def test_text_segment_parity(gpu_lib, vis, text_storage, n_tok, rank, r_lo_t, k_
     dt = torch_storage(w)
     tk, tv = stack("text_k", dt), stack("text_v", dt)
     sel = torch.full((w.batch, w.n_q_heads, w.top_k), -1, dtype=torch.int32, device="cuda")
+    tsel = torch.full((w.batch, w.n_q_heads, k_t), -1, dtype=torch.int32, device="cuda")
     out = gpu_lib.decode(c, q, r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, text_k=tk, text_v=tv,
-                         sel_out=sel, text_cache=tc, text_r_lo=r_lo_t, text_top_k=k_t)
+                         sel_out=sel, text_cache=tc, text_r_lo=r_lo_t, text_top_k=k_t,
+                         text_sel_out=tsel if k_t else None)
     torch.cuda.synchronize()
-    err = check(w, tw, vseqs, tseqs, out.cpu().numpy(), sel.cpu().numpy(), r_lo_t, k_t)
+    err = check(w, tw, vseqs, tseqs, out.cpu().numpy(), sel.cpu().numpy(), r_lo_t, k_t,
+                tsel=tsel.cpu().numpy())
     print(f"{vis} + text {text_storage}: max abs err {err:.3e}")
     c.free()
     tc.free()
@@ -124,14 +143,16 @@ def test_text_segment_full_layer(gpu_lib):
     c, stack = upload_cache(w, vseqs, gpu_lib)
     tc, _ = upload_cache(tw.replace(batch=w.batch), tseqs, gpu_lib)
     q = stack("q", torch.float32)
+    tsel = torch.full((w.batch, w.n_q_heads, 32), -1, dtype=torch.int32, device="cuda")
     out = gpu_lib.decode(c, q, r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, text_cache=tc,
-                         text_r_lo=8, text_top_k=32)
+                         text_r_lo=8, text_top_k=32, text_sel_out=tsel)
     torch.cuda.synchronize()
-    out = out.cpu().numpy()
+    out, tsel = out.cpu().numpy(), tsel.cpu().numpy()
     empty = np.zeros((0, w.width), np.float32)
-    check(w, tw, vseqs, tseqs, out, None, 8, 32, dense=[(empty, empty)] * 2)
+    check(w, tw, vseqs, tseqs, out, None, 8, 32, dense=[(empty, empty)] * 2, tsel=tsel)
     for b in range(2, w.batch):
         assert np.array_equal(out[b], out[b % 2]), b
+        assert np.array_equal(tsel[b], tsel[b % 2]), b
     c.free()
     tc.free()
 
@@ -173,11 +194,12 @@ def test_cache_growth_with_refactoring(gpu_lib):
         tk = torch.from_numpy(np.stack([t[0] for t in tail])).to(torch.bfloat16).cuda()
         tv = torch.from_numpy(np.stack([t[1] for t in tail])).to(torch.bfloat16).cuda()
         n_t = tc.n_tokens
+        tsel = torch.full((w.batch, w.n_q_heads, n_t // 2), -1, dtype=torch.int32, device="cuda")
         out = gpu_lib.decode(c, q, r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, text_k=tk, text_v=tv,
-                             text_cache=tc, text_r_lo=r_lo_t, text_top_k=n_t // 2)
+                             text_cache=tc, text_r_lo=r_lo_t, text_top_k=n_t // 2, text_sel_out=tsel)
         U_k, B_k, U_v, B_v = (x.float().cpu().numpy() for x in tc.get_factors())
         torch.cuda.synchronize()
-        out = out.cpu().numpy()
+        out, tsel = out.cpu().numpy(), tsel.cpu().numpy()
         for b in range(w.batch):
             s = vseqs[b % len(vseqs)]
             t = dict(U_k=U_k[b], B_k=B_k[b], U_v=U_v[b], B_v=B_v[b], r_lo=r_lo_t, top_k=n_t // 2)
@@ -185,6 +207,9 @@ def test_cache_growth_with_refactoring(gpu_lib):
                                   w.head_dim, w.scale, tail[b][0], tail[b][1])
             err = float(np.max(np.abs(out[b] - ref["out"])))
             assert err <= 2e-2, (step, b, err)
+            for h in range(w.n_q_heads):
+                check_set(tsel[b, h], ref["top"][1][h], seg_s_lo(w, t, qn[b], h, r_lo_t), n_t // 2,
+                          ("text", step, b, h))
         if step % 2 == 1:     # re-factor text + appended tokens; the dense part restarts
             tc.free()
             tc = refactor()
