@@ -101,9 +101,10 @@ typedef struct ap_cache ap_cache;
  *         memory synchronously (the cache, plus a workspace of about
  *         2B * ell * (3 max(N, W) + N + W) * 4 bytes held until the enqueued work is
  *         done), then enqueues the factorisation on `stream`.
- * Limit:  when factoring (k, v set) ell = min(r + p, N, W) must be <= 128: the core
- *         SVD and the orthonormalisation of each matrix live in one workgroup's LDS.
- *         Larger ell is AP_ERR_UNSUPPORTED before anything is allocated.
+ * Limit:  when factoring (k, v set) ell = min(r + p, N, W) must be <= 144 (r = 128 with
+ *         the usual p = 16): the Cholesky and the core SVD keep an ell x ell matrix of
+ *         each factorisation in one workgroup's LDS.  Larger ell is AP_ERR_UNSUPPORTED
+ *         before anything is allocated.
  * Errors: AP_ERR_NULL_ARG, AP_ERR_BAD_SHAPE, AP_ERR_BAD_DTYPE, AP_ERR_UNSUPPORTED,
  *         AP_ERR_OUT_OF_MEMORY, AP_ERR_HIP.
  */
@@ -118,7 +119,7 @@ ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p,
  * k, v:   device [B][N][W] in the cache's storage dtype, caller-owned, read on `stream`.
  * omega:  optional device [B][2][W][ell] float32 test matrices (as in
  *         ap_compress_params); NULL: random signs from `seed`, as ap_compress draws them.
- * Errors: AP_ERR_NULL_ARG, AP_ERR_UNSUPPORTED (ell > 128), AP_ERR_OUT_OF_MEMORY,
+ * Errors: AP_ERR_NULL_ARG, AP_ERR_UNSUPPORTED (ell > 144), AP_ERR_OUT_OF_MEMORY,
  *         AP_ERR_HIP.  On an error the factors are unspecified. */
 ap_status ap_recompress(ap_cache* c, const void* k, const void* v, const float* omega, uint64_t seed,
                         void* stream);

@@ -184,7 +184,7 @@ ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p,
   if (k != nullptr) {
     const int W = p->n_kv_heads * p->head_dim;
     const int ell = std::min(std::min(p->rank + p->oversample, p->n_tokens), W);
-    if (ell > 128) return fail(AP_ERR_UNSUPPORTED, "min(rank + oversample, n_tokens, width) must be <= 128");
+    if (ell > 144) return fail(AP_ERR_UNSUPPORTED, "min(rank + oversample, n_tokens, width) must be <= 144");
   }
   ap_cache* c = new (std::nothrow) ap_cache();
   if (!c) return fail(AP_ERR_OUT_OF_MEMORY, "host allocation failed");
@@ -222,7 +222,7 @@ ap_status ap_recompress(ap_cache* c, const void* k, const void* v, const float* 
   if (!c || !k || !v) return fail(AP_ERR_NULL_ARG, "cache, k and v must not be NULL");
   const Dims& dm = c->dm;
   const int ell = std::min(std::min(dm.r + dm.p, dm.N), dm.W);
-  if (ell > 128) return fail(AP_ERR_UNSUPPORTED, "min(rank + oversample, n_tokens, width) must be <= 128");
+  if (ell > 144) return fail(AP_ERR_UNSUPPORTED, "min(rank + oversample, n_tokens, width) must be <= 144");
   if (dm.B == 0) return AP_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   c->last_stream = st;

@@ -32,7 +32,8 @@
 namespace ap {
 
 constexpr int kGemmThreads = 256;
-constexpr int kMaxEll = 128;          // largest ell the LDS-resident Cholesky/Jacobi handle
+constexpr int kMaxEll = 144;          // largest ell: 9 column tiles of 16; the Cholesky and the
+                                      // core SVD keep one ell x ell matrix per workgroup in LDS
 
 // ---------------------------------------------------------------- workspace
 struct CompressWs {
@@ -461,10 +462,20 @@ __global__ __launch_bounds__(256) void k_gram_reduce(const float* __restrict__ G
 // columns: the diagonal block is factored and inverted in registers by wavefront 0
 // (lane i holds row i; values broadcast with readlane), the panel below it is
 // L_IJ = A_IJ L_JJ^-T and the trailing update A_IK -= L_IJ L_KJ^T, both on fp32
-// MFMA.  L^-1 follows by block forward substitution (X_IJ = -X_II sum_K L_IK X_KJ),
-// Rinv = L^-T is written, and when Rout is given R = L^T Rprev (Rprev NULL:
-// identity; Rprev may equal Rout: it is staged in LDS before R is written).
+// MFMA.  X = L^-1 follows by block forward substitution, one block column per
+// wavefront at a time (X_IJ = -X_II sum_K L_IK X_KJ involves block column J only),
+// each column written out as rows of Rinv = X^T; when Rout is given, R = L^T Rprev
+// block column by block column (Rprev NULL: identity; Rprev may equal Rout: a
+// wavefront stages the whole block column it reads before it writes that column).
+// Only the Gram / L is ell x ell in LDS, so ell up to 144 fits.
 constexpr int kCholThreads = 256;
+constexpr int kTileF = 16 * 17;      // one padded 16 x 16 tile in LDS (floats)
+
+__host__ __device__ inline size_t chol_lds_floats(int ellp) {
+  // L [ellp][ellp + 1], diagonal inverses [T][16][17], one block column per wavefront
+  // [4][ellp][17], one tile of scratch per wavefront [4][16][17]
+  return (size_t)ellp * (ellp + 1) + (size_t)(ellp / 16) * kTileF + 4 * (size_t)ellp * 17 + 4 * kTileF;
+}
 
 __device__ __forceinline__ float lane_bcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
@@ -500,15 +511,16 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
                                                        float* __restrict__ Rout) {
   extern __shared__ __align__(16) float sh[];
   const int S = ellp + 1;
+  const int T = ellp / 16;
   float* G = sh;                 // [ellp][S] Gram, then L (lower; diagonal blocks exact)
-  float* X = G + ellp * S;       // [ellp][S] L^-1, later Rprev
-  float* Wk = X + ellp * S;      // [4][16][17] per-wavefront scratch tile
+  float* D = G + ellp * S;       // [T][16][17] inverses of the diagonal blocks of L
+  float* Cb = D + T * kTileF;    // [4][ellp][17] per-wavefront block column
+  float* Wk = Cb + 4 * ellp * 17;  // [4][16][17] per-wavefront scratch tile
   const int mat = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int T = ellp / 16;
   const size_t e2 = (size_t)ellp * ellp;
-  // ---- sum of the partial Grams (fixed order), X = 0.  16-byte loads, a batch of 8 per
+  // ---- sum of the partial Grams (fixed order).  16-byte loads, a batch of 8 per
   // thread issued before any is used (ellp^2 / 4 is a multiple of 64)
   const float4* gp = reinterpret_cast<const float4*>(Gpart + (size_t)mat * nsplit * e2);
   const int e4 = static_cast<int>(e2 / 4);
@@ -529,8 +541,6 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
         const int r = (4 * i) / ellp, c = 4 * i - r * ellp;
         float* g = G + r * S + c;
         g[0] = v[u].x; g[1] = v[u].y; g[2] = v[u].z; g[3] = v[u].w;
-        float* x = X + r * S + c;
-        x[0] = 0.f; x[1] = 0.f; x[2] = 0.f; x[3] = 0.f;
       }
     }
   }
@@ -554,6 +564,7 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
   // ---- blocked Cholesky
   for (int J = 0; J < T; ++J) {
     const int c0 = 16 * J;
+    float* DJ = D + J * kTileF;
     if (wave == 0) {
       const int li = lane < 16 ? lane : 15;
       float row[16];
@@ -582,13 +593,13 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
 #pragma unroll
         for (int c = 0; c < 16; ++c) G[(c0 + lane) * S + c0 + c] = row[c];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) X[(c0 + i) * S + c0 + lane] = x[i];
+        for (int i = 0; i < 16; ++i) DJ[i * 17 + lane] = x[i];
       }
     }
     __syncthreads();
     // panel: L_IJ = A_IJ X_JJ^T
     for (int I = J + 1 + wave; I < T; I += 4) {
-      const v4f p = tile_mma<false, true, false>(G, 16 * I, c0, S, X, c0, c0, S, v4f{0, 0, 0, 0}, l16, lg);
+      const v4f p = tile_mma<false, true, false>(G, 16 * I, c0, S, DJ, 0, 0, 17, v4f{0, 0, 0, 0}, l16, lg);
       tile_store(G, 16 * I, c0, S, l16, lg, p);
     }
     __syncthreads();
@@ -604,66 +615,71 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
     }
     __syncthreads();
   }
-  // ---- L^-1 below the diagonal blocks, block row by block row
-  float* wk = Wk + wave * 16 * 17;
-  for (int I = 1; I < T; ++I) {
-    for (int Jb = wave; Jb < I; Jb += 4) {
+  // ---- X = L^-1 by block columns (wavefront-private: no workgroup barrier inside)
+  float* cb = Cb + wave * ellp * 17;   // rows 16 Jb .. ellp - 1 of this block column of X
+  float* wk = Wk + wave * kTileF;
+  auto wave_sync = []() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  float* Ri = Rinv + (size_t)mat * e2;
+  for (int Jb = wave; Jb < T; Jb += 4) {
+    const float* DJ = D + Jb * kTileF;
+    for (int idx = lane; idx < 256; idx += 64) cb[(16 * Jb + (idx >> 4)) * 17 + (idx & 15)] = DJ[(idx >> 4) * 17 + (idx & 15)];
+    wave_sync();
+    for (int I = Jb + 1; I < T; ++I) {
       v4f acc = v4f{0, 0, 0, 0};
       for (int K = Jb; K < I; ++K)
-        acc = tile_mma<false, false, false>(G, 16 * I, 16 * K, S, X, 16 * K, 16 * Jb, S, acc, l16, lg);
+        acc = tile_mma<false, false, false>(G, 16 * I, 16 * K, S, cb, 16 * K, 0, 17, acc, l16, lg);
       tile_store(wk, 0, 0, 17, l16, lg, acc);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const v4f xr = tile_mma<false, false, true>(X, 16 * I, 16 * I, S, wk, 0, 0, 17, v4f{0, 0, 0, 0}, l16, lg);
-      tile_store(X, 16 * I, 16 * Jb, S, l16, lg, xr);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync();
+      const v4f xr = tile_mma<false, false, true>(D + I * kTileF, 0, 0, 17, wk, 0, 0, 17, v4f{0, 0, 0, 0}, l16, lg);
+      tile_store(cb, 16 * I, 0, 17, l16, lg, xr);
+      wave_sync();
     }
-    __syncthreads();
-  }
-  // ---- Rinv = X^T
-  float* Ri = Rinv + (size_t)mat * e2;
-  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
-    const int i = idx / ellp, j = idx % ellp;
-    Ri[idx] = X[j * S + i];
+    // rows 16 Jb .. 16 Jb + 15 of Rinv = X^T: Rinv[16 Jb + c][i] = X[i][16 Jb + c], zero for
+    // i below the block column's first row
+    for (int idx = lane; idx < 16 * ellp; idx += 64) {
+      const int c = idx / ellp, i = idx - c * ellp;
+      Ri[(size_t)(16 * Jb + c) * ellp + i] = i < 16 * Jb ? 0.f : cb[i * 17 + c];
+    }
+    wave_sync();
   }
   if (Rout == nullptr) return;
-  __syncthreads();
-  // ---- R = L^T Rprev
-  const float4* Rp = Rprev ? reinterpret_cast<const float4*>(Rprev + (size_t)mat * e2) : nullptr;
-  for (int i0 = 0; i0 < e4; i0 += 8 * kCholThreads) {
-    float4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = min(i0 + u * kCholThreads + tid, e4 - 1);
-      if (Rp) {
-        v[u] = Rp[i];
-      } else {
-        const int r = (4 * i) / ellp, c = 4 * i - r * ellp;
-        v[u] = make_float4(r == c, r == c + 1, r == c + 2, r == c + 3);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * kCholThreads + tid;
-      if (i < e4) {
-        const int r = (4 * i) / ellp, c = 4 * i - r * ellp;
-        float* x = X + r * S + c;
-        x[0] = v[u].x; x[1] = v[u].y; x[2] = v[u].z; x[3] = v[u].w;
-      }
-    }
-  }
-  __syncthreads();
+  // ---- R = L^T Rprev, block column by block column: R[:, Jb] = L^T Rprev[:, Jb]
+  const float* Rp = Rprev ? Rprev + (size_t)mat * e2 : nullptr;
   float* Ro = Rout + (size_t)mat * e2;
-  for (int t = wave; t < T * T; t += 4) {
-    const int I = t / T, Jb = t % T;
-    v4f acc = v4f{0, 0, 0, 0};
-    for (int K = I; K < T; ++K)
-      acc = tile_mma<true, false, false>(G, 16 * K, 16 * I, S, X, 16 * K, 16 * Jb, S, acc, l16, lg);
+  for (int Jb = wave; Jb < T; Jb += 4) {
+    // stage Rprev[:, 16 Jb .. 16 Jb + 15] (4 consecutive columns per load)
+    for (int i0 = 0; i0 < 4 * ellp; i0 += 4 * 64) {
+      float4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) Ro[(size_t)(16 * I + 4 * lg + u) * ellp + 16 * Jb + l16] = acc[u];
+      for (int u = 0; u < 4; ++u) {
+        const int idx = min(i0 + u * 64 + lane, 4 * ellp - 1);
+        const int r = idx >> 2, c = 4 * (idx & 3);
+        v[u] = Rp ? *reinterpret_cast<const float4*>(Rp + (size_t)r * ellp + 16 * Jb + c)
+                  : make_float4(r == 16 * Jb + c, r == 16 * Jb + c + 1, r == 16 * Jb + c + 2, r == 16 * Jb + c + 3);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = i0 + u * 64 + lane;
+        if (idx < 4 * ellp) {
+          const int r = idx >> 2, c = 4 * (idx & 3);
+          float* x = cb + r * 17 + c;
+          x[0] = v[u].x; x[1] = v[u].y; x[2] = v[u].z; x[3] = v[u].w;
+        }
+      }
+    }
+    wave_sync();
+    for (int I = 0; I < T; ++I) {
+      v4f acc = v4f{0, 0, 0, 0};
+      for (int K = I; K < T; ++K)
+        acc = tile_mma<true, false, false>(G, 16 * K, 16 * I, S, cb, 16 * K, 0, 17, acc, l16, lg);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Ro[(size_t)(16 * I + 4 * lg + u) * ellp + 16 * Jb + l16] = acc[u];
+    }
+    wave_sync();
   }
 }
 
@@ -802,25 +818,44 @@ __global__ __launch_bounds__(256) void k_apply(const float* Y, float* Qout, int 
 // by DPP inside the group; a step's E/2 disjoint pairs run at once, one barrier per
 // step.  Stops when every pair is orthogonal to 3e-6 relative (fp32), or after 40
 // sweeps.
+// The rotations depend on Mj alone, and each row of J is rotated independently of
+// the others.  When Mj and all of J do not fit one workgroup's LDS (ell > 128), the
+// rows of J are split over `jsplit` workgroups per matrix: each runs the same
+// rotations on its own copy of Mj (the same arithmetic in the same order, so the
+// copies stay identical) and accumulates its share of J's rows; the first writes
+// P Sigma and the singular values.
+__host__ __device__ inline int jacobi_rows(int ellp, int jsplit) {   // rows of J per workgroup
+  return ((ellp / 16 + jsplit - 1) / jsplit) * 16;
+}
+__host__ __device__ inline size_t jacobi_lds_floats(int ellp, int jsplit) {
+  return (size_t)(ellp + jacobi_rows(ellp, jsplit)) * (ellp + 1) + 2 * (size_t)ellp;
+}
+
 __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, int ell, int ellp,
-                                                 float* __restrict__ PS, float* __restrict__ Sv,
-                                                 float* __restrict__ sig) {
+                                                 int jsplit, float* __restrict__ PS,
+                                                 float* __restrict__ Sv, float* __restrict__ sig) {
   extern __shared__ __align__(16) float sh[];
   const int S = ellp + 1;
   const int E = (ell + 1) & ~1;            // even number of columns for the tournament
+  const int mat = blockIdx.x / jsplit, js = blockIdx.x - (blockIdx.x / jsplit) * jsplit;
+  const int JR = jacobi_rows(ellp, jsplit);
+  const int j0 = js * JR;                  // first row of J held here
+  const int jn = min(JR, ellp - j0);       // rows held (a multiple of 16, >= 16)
   float* Mj = sh;                          // [ellp][S]  (row i, column j)
-  float* J = Mj + ellp * S;                // [ellp][S]
-  float* nrm = J + ellp * S;               // [ellp]
+  float* J = Mj + ellp * S;                // [JR][S]    rows j0 .. j0 + jn - 1 of J
+  float* nrm = J + JR * S;                 // [ellp]
   int* perm = reinterpret_cast<int*>(nrm + ellp);  // [ellp]
   __shared__ unsigned int rotated;
-  const int mat = blockIdx.x;
   const float* R = Rm + (size_t)mat * ellp * ellp;
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int l16 = tid & 15, slot = tid >> 4, nslot = nthr >> 4;
   for (int idx = tid; idx < ellp * ellp; idx += nthr) {
     const int i = idx / ellp, j = idx % ellp;
     Mj[i * S + j] = (i < ell && j < ell) ? R[j * ellp + i] : 0.f;   // transpose
-    J[i * S + j] = i == j ? 1.f : 0.f;
+  }
+  for (int idx = tid; idx < jn * ellp; idx += nthr) {
+    const int i = idx / ellp, j = idx % ellp;
+    J[i * S + j] = j0 + i == j ? 1.f : 0.f;
   }
   __syncthreads();
   for (int sweep = 0; sweep < 40; ++sweep) {
@@ -863,6 +898,11 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
           const float x = Mj[i * S + p], y = Mj[i * S + qq];
           Mj[i * S + p] = c * x - s * y;
           Mj[i * S + qq] = s * x + c * y;
+        }
+#pragma unroll
+        for (int k = 0; k < kMaxEll / 16; ++k) {
+          if (16 * k >= jn) break;
+          const int i = l16 + 16 * k;
           const float u = J[i * S + p], v = J[i * S + qq];
           J[i * S + p] = c * u - s * v;
           J[i * S + qq] = s * u + c * v;
@@ -888,13 +928,17 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
   __syncthreads();
   float* PSm = PS + (size_t)mat * ellp * ellp;
   float* Sm = Sv + (size_t)mat * ellp * ellp;
-  for (int idx = tid; idx < ellp * ellp; idx += nthr) {
-    const int i = idx / ellp, c = idx % ellp;
-    const int j = perm[c];
-    PSm[idx] = Mj[i * S + j];
-    Sm[idx] = J[i * S + j];
+  if (js == 0) {
+    for (int idx = tid; idx < ellp * ellp; idx += nthr) {
+      const int i = idx / ellp, c = idx % ellp;
+      PSm[idx] = Mj[i * S + perm[c]];
+    }
+    for (int c = tid; c < ellp; c += nthr) sig[(size_t)mat * ellp + c] = fmaxf(nrm[perm[c]], 0.f);
   }
-  for (int c = tid; c < ellp; c += nthr) sig[(size_t)mat * ellp + c] = fmaxf(nrm[perm[c]], 0.f);
+  for (int idx = tid; idx < jn * ellp; idx += nthr) {
+    const int i = idx / ellp, c = idx % ellp;
+    Sm[(size_t)(j0 + i) * ellp + c] = J[i * S + perm[c]];
+  }
 }
 
 // ================================================================ assembly
@@ -1097,7 +1141,7 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
     break;
     switch (ellp / 16) {
       AP_GEMM_CASE(1) AP_GEMM_CASE(2) AP_GEMM_CASE(3) AP_GEMM_CASE(4)
-      AP_GEMM_CASE(5) AP_GEMM_CASE(6) AP_GEMM_CASE(7) AP_GEMM_CASE(8)
+      AP_GEMM_CASE(5) AP_GEMM_CASE(6) AP_GEMM_CASE(7) AP_GEMM_CASE(8) AP_GEMM_CASE(9)
       default: return hipErrorInvalidValue;
     }
 #undef AP_GEMM_CASE
@@ -1135,7 +1179,7 @@ static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void*
   const Dims& dm = c->dm;
   const int nmat = 2 * dm.B, ellp = ws.ellp;
   const size_t lds_gram = (size_t)ellp * (ellp + 1) * sizeof(float);
-  const size_t lds_chol = (size_t)(2 * ellp * (ellp + 1) + 4 * 16 * 17) * sizeof(float);
+  const size_t lds_chol = chol_lds_floats(ellp) * sizeof(float);
   const int arows = apply_rows(ellp);
   const size_t lds_apply = (size_t)(arows * (ellp + 1) + ellp * ellp) * sizeof(float);
   const int tiles_m = (M + arows - 1) / arows;
@@ -1150,7 +1194,7 @@ static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void*
                        rows, nsplit, ws.Gpart);                                                       \
     break;
       AP_GRAM_CASE(1) AP_GRAM_CASE(2) AP_GRAM_CASE(3) AP_GRAM_CASE(4)
-      AP_GRAM_CASE(5) AP_GRAM_CASE(6) AP_GRAM_CASE(7) AP_GRAM_CASE(8)
+      AP_GRAM_CASE(5) AP_GRAM_CASE(6) AP_GRAM_CASE(7) AP_GRAM_CASE(8) AP_GRAM_CASE(9)
 #undef AP_GRAM_CASE
       default: return hipErrorInvalidValue;
     }
@@ -1178,7 +1222,7 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   ws.M = std::max(dm.N, dm.W);
   ws.ellp = (dm.ell + 15) / 16 * 16;
   if (ws.ellp > kMaxEll) {
-    set_error("ap_compress: ell = min(rank + oversample, n_tokens, width) must be <= 128");
+    set_error("ap_compress: ell = min(rank + oversample, n_tokens, width) must be <= 144");
     return hipErrorNotSupported;
   }
   const int nmat = ws.nmat, ellp = ws.ellp;
@@ -1238,15 +1282,19 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   if (e != hipSuccess) return fail_stage(e, "test matrix");
 
   // dynamic LDS above the 64 KB default: request exactly what each launch uses
-  const size_t lds_chol = (size_t)(2 * ellp * (ellp + 1) + 4 * 16 * 17) * sizeof(float);
-  const size_t lds_jac = (size_t)(2 * ellp * (ellp + 1) + 2 * ellp) * sizeof(float);
+  const size_t lds_chol = chol_lds_floats(ellp) * sizeof(float);
+  // the rows of the core SVD's rotation matrix are split over two workgroups per matrix
+  // when they do not fit one workgroup's LDS beside the matrix itself
+  const int jsplit = jacobi_lds_floats(ellp, 1) * sizeof(float) <= 160 * 1024 ? 1 : 2;
+  const size_t lds_jac = jacobi_lds_floats(ellp, jsplit) * sizeof(float);
   const size_t lds_apply = (size_t)(apply_rows(ellp) * (ellp + 1) + ellp * ellp) * sizeof(float);
   const bool u4 = dm.storage == AP_INT4;
   const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP + 32 * (16 * dm.NP + 1) +
                                 (u4 ? 16 * dm.NP : 0)) * sizeof(float);
   const size_t lds_b = (size_t)(64 * (ellp + 1) + ellp * dm.r_pad) * sizeof(float);
   const struct { const void* fn; size_t bytes; const char* name; } lds_req[] = {
-      {reinterpret_cast<const void*>(&k_gram<8>), (size_t)ellp * (ellp + 1) * sizeof(float), "LDS size of k_gram"},
+      {ellp / 16 == 9 ? reinterpret_cast<const void*>(&k_gram<9>) : reinterpret_cast<const void*>(&k_gram<8>),
+       (size_t)ellp * (ellp + 1) * sizeof(float), "LDS size of k_gram"},
       {reinterpret_cast<const void*>(&k_chol), lds_chol, "LDS size of k_chol"},
       {reinterpret_cast<const void*>(&k_assemble_b<T>), lds_b, "LDS size of k_assemble_b"},
       {reinterpret_cast<const void*>(&k_jacobi), lds_jac, "LDS size of k_jacobi"},
@@ -1282,8 +1330,8 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   if (e == hipSuccess) e = orth<T>(c, ws, dm.W, nullptr, nullptr, ws.Racc, 2, ws.Qc, st);
   if (e != hipSuccess) return fail_stage(e, "projection C^T = A^T Q");
   const int jac_threads = std::min(1024, std::max(64, (16 * ((dm.ell + 1) / 2) + 63) / 64 * 64));
-  hipLaunchKernelGGL(k_jacobi, dim3(nmat), dim3(jac_threads), lds_jac, st, ws.Racc, dm.ell, ellp, ws.PS,
-                     ws.Sv, ws.sig);
+  hipLaunchKernelGGL(k_jacobi, dim3(nmat * jsplit), dim3(jac_threads), lds_jac, st, ws.Racc, dm.ell, ellp,
+                     jsplit, ws.PS, ws.Sv, ws.sig);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_stage(e, "core SVD");
   if (u4)

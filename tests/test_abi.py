@@ -95,15 +95,15 @@ def test_null_arguments():
 
 
 def test_compress_rejects_large_probe_count_before_touching_memory():
-    # ell = min(r + p, N, W) = 144 > 128: refused during validation, so the (never
+    # ell = min(r + p, N, W) = 160 > 144: refused during validation, so the (never
     # dereferenced) fake device pointers are safe on a machine without a GPU
     from rank_compressed_kv_ap_amd import binding as b
-    p = b.CompressParams(1, 512, 4, 4, 64, 128, 16, 2, b.AP_BF16, 0, 0, None)
+    p = b.CompressParams(1, 512, 4, 4, 64, 128, 32, 2, b.AP_BF16, 0, 0, None)
     out = ctypes.c_void_p(1)
     st = b.lib.ap_compress(ctypes.c_void_p(256), ctypes.c_void_p(512), ctypes.byref(p), None,
                            ctypes.byref(out))
     assert st == b.AP_ERR_UNSUPPORTED and out.value is None
-    assert b"128" in b.lib.ap_last_error()
+    assert b"144" in b.lib.ap_last_error()
 
 
 def test_decode_rejects_text_pointers_without_text_tokens():

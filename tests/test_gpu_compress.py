@@ -87,6 +87,16 @@ SMALL = {
                                                    inner_dim=128, oversample=0, power_iters=0), {}),
     "bf16_rank128": (wl.VIDEO.replace(cfg_id=206, batch=1, n_kv_heads=2, n_q_heads=2, n_tokens=600,
                                       frames=None, inner_dim=256, oversample=0), {}),
+    # rank 128 with the default oversampling: ell = 144, nine 16-column tiles; the core
+    # SVD's rotation rows are split over two workgroups per matrix
+    "bf16_rank128_ell144": (wl.VIDEO.replace(cfg_id=210, batch=2, n_kv_heads=2, n_q_heads=4, n_tokens=700,
+                                             frames=None, inner_dim=256), {}),
+    # ell = 136: nine tiles with a ragged last one (ell < ellp)
+    "bf16_ell136": (wl.VIDEO.replace(cfg_id=211, batch=2, n_kv_heads=3, n_q_heads=3, n_tokens=400,
+                                     rank=120, frames=None, inner_dim=300), {}),
+    # fp32 at ell = 144
+    "f32_ell144": (wl.TINY.replace(cfg_id=212, batch=1, n_kv_heads=4, n_q_heads=4, head_dim=64,
+                                   n_tokens=300, rank=128, inner_dim=200), {}),
     # 8 matrices: the product kernels deal each matrix's row tiles to one XCD
     "bf16_eight_matrices": (wl.LLAVA.replace(cfg_id=209, batch=4, n_q_heads=4, n_kv_heads=4, head_dim=64,
                                              n_tokens=300, rank=24, grid=None, inner_dim=120), {}),
@@ -164,15 +174,16 @@ def test_compress_empty_batch(gpu_lib):
     c.free()
 
 
-@pytest.mark.parametrize("cfg", [2, 5])
-def test_compress_full_configs_then_decode(gpu_lib, cfg):
-    """Full batch at the workload's real shape (two distinct sequences tiled over
-    it): distinct sequences match the oracle's factorisation, replicas equal their
-    originals bit for bit, and one decode step on the GPU's own factors matches the
-    oracle's decode of those factors."""
+@pytest.mark.parametrize("cfg,n_distinct", [(2, 2), (3, 2), (4, 1), (5, 2)])
+def test_compress_full_configs_then_decode(gpu_lib, cfg, n_distinct):
+    """Full batch at the workload's real shape, with the default p = 16, q = 2 (the
+    long-video layer: r = 128, ell = 144), distinct sequences tiled over it: they match
+    the oracle's factorisation, replicas equal their originals bit for bit, and one
+    decode step on the GPU's own factors matches the oracle's decode of those factors."""
     from gpu_helpers import check_against_oracle
     w = wl.WORKLOADS[cfg]
-    K, V, om = host_inputs(w, 2)
+    assert w.oversample == 16 and w.power_iters == 2
+    K, V, om = host_inputs(w, n_distinct)
     c, (U_k, B_k, U_v, B_v, sk, sv) = gpu_compress(w, K, V, gpu_lib, om=om)
     S = len(K)
     for b in range(S):
