@@ -124,6 +124,21 @@ ap_status ap_compress(const void* k, const void* v, const ap_compress_params* p,
 ap_status ap_recompress(ap_cache* c, const void* k, const void* v, const float* omega, uint64_t seed,
                         void* stream);
 
+/* The same re-factorisation as ap_recompress, allocating nothing: for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops that
+ * forbid hipMalloc).  Its factorisation workspace is a fixed device array inside the
+ * library, 128 MiB (134217728 bytes) on each GPU the library runs on, held until the
+ * process ends.  A shape whose workspace does not fit returns AP_ERR_UNSUPPORTED (the
+ * message gives the bytes needed) before anything is enqueued.  The workspace needs
+ * about 2B * ell_pad * (W s + max(N, W) (4 + 2 s) + N 4 + W 4) bytes, ell_pad = ell
+ * rounded up to 16, s = 2 (bf16, 4-bit) or 4 (fp32).
+ * Every call on a GPU uses that GPU's one array, which keeps the last call's contents:
+ * calls that overlap on one GPU (several streams, or several host threads) race and
+ * must be serialised by the caller.  Results equal ap_recompress's bit for bit.
+ * Arguments, ownership and the other errors as for ap_recompress. */
+ap_status ap_recompress_noalloc(ap_cache* c, const void* k, const void* v, const float* omega, uint64_t seed,
+                                void* stream);
+
 /* Load factors into a cache: U_k, U_v device [B][N][r], B_k, B_v device [B][r][W],
  * row-major, in the cache's storage dtype, caller-owned, read on `stream`.  The
  * layout is the plain one of [fr §2.A "Mécanisme"] (K ~= U_k B_k); the cache keeps

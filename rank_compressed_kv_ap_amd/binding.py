@@ -22,7 +22,7 @@ AP_F32, AP_BF16, AP_INT4 = 0, 1, 2
 KERNEL_NAMES = ("select", "attn", "combine", "decode", "ema", "text")
 
 EXPORTED = (
-    "ap_compress", "ap_recompress", "ap_cache_set_factors", "ap_cache_get_factors",
+    "ap_compress", "ap_recompress", "ap_recompress_noalloc", "ap_cache_set_factors", "ap_cache_get_factors",
     "ap_cache_get_sigma", "ap_cache_info", "ap_decode_attn", "ap_free", "ap_timing_enable",
     "ap_timing_read", "ap_status_string", "ap_last_error",
 )
@@ -59,6 +59,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.ap_compress.argtypes = [vp, vp, ctypes.POINTER(CompressParams), vp, ctypes.POINTER(vp)]
     lib.ap_recompress.argtypes = [vp, vp, vp, vp, ctypes.c_uint64, vp]
+    lib.ap_recompress_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_uint64, vp]
     lib.ap_cache_set_factors.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.ap_cache_get_factors.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.ap_cache_get_sigma.argtypes = [vp, vp, vp, vp]
@@ -73,7 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ap_status_string.restype = ctypes.c_char_p
     lib.ap_last_error.argtypes = []
     lib.ap_last_error.restype = ctypes.c_char_p
-    for name in ("ap_compress", "ap_recompress", "ap_cache_set_factors", "ap_cache_get_factors", "ap_cache_get_sigma",
+    for name in ("ap_compress", "ap_recompress", "ap_recompress_noalloc", "ap_cache_set_factors", "ap_cache_get_factors", "ap_cache_get_sigma",
                  "ap_cache_info", "ap_decode_attn", "ap_timing_enable", "ap_timing_read"):
         getattr(lib, name).restype = i32
     return lib
@@ -158,6 +159,12 @@ class Cache:
         """ap_recompress: factor new k, v [B, N, W] into this cache."""
         _check(lib.ap_recompress(self.handle, _ptr(k), _ptr(v), _ptr(omega), seed, _stream()),
                "ap_recompress")
+
+    def recompress_noalloc(self, k: torch.Tensor, v: torch.Tensor, *, seed: int = 0,
+                           omega: Optional[torch.Tensor] = None) -> None:
+        """ap_recompress_noalloc: as recompress, with the library's fixed workspace."""
+        _check(lib.ap_recompress_noalloc(self.handle, _ptr(k), _ptr(v), _ptr(omega), seed, _stream()),
+               "ap_recompress_noalloc")
 
     def set_factors(self, U_k, B_k, U_v, B_v) -> None:
         _check(lib.ap_cache_set_factors(self.handle, _ptr(U_k), _ptr(B_k), _ptr(U_v), _ptr(B_v),

@@ -124,5 +124,9 @@ hipError_t launch_unpack_u(const ap_cache* c, const void* src, void* dst, bool v
 
 // ---- launchers (compress_kernels.hip)
 hipError_t run_compress(ap_cache* c, const void* k, const void* v, hipStream_t st);
+// The same factorisation with its workspace in the library's fixed device array of
+// kNoAllocWorkspaceBytes (no allocation; hipErrorNotSupported when it does not fit).
+constexpr size_t kNoAllocWorkspaceBytes = size_t(128) << 20;
+hipError_t run_compress_noalloc(ap_cache* c, const void* k, const void* v, hipStream_t st);
 
 }  // namespace ap

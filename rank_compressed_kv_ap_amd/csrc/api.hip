@@ -243,6 +243,32 @@ ap_status ap_recompress(ap_cache* c, const void* k, const void* v, const float* 
   return AP_OK;
 }
 
+ap_status ap_recompress_noalloc(ap_cache* c, const void* k, const void* v, const float* omega, uint64_t seed,
+                                void* stream) {
+  if (!c || !k || !v) return fail(AP_ERR_NULL_ARG, "cache, k and v must not be NULL");
+  const Dims& dm = c->dm;
+  const int ell = std::min(std::min(dm.r + dm.p, dm.N), dm.W);
+  if (ell > 144) return fail(AP_ERR_UNSUPPORTED, "min(rank + oversample, n_tokens, width) must be <= 144");
+  if (dm.B == 0) return AP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  set_error("");
+  const float* omega0 = c->params.omega;
+  const uint64_t seed0 = c->params.seed;
+  c->params.omega = omega;
+  c->params.seed = seed;
+  hipError_t e = run_compress_noalloc(c, k, v, st);
+  c->params.omega = omega0;
+  if (e != hipSuccess) {
+    c->params.seed = seed0;
+    std::string detail = g_last_error;
+    if (e == hipErrorNotSupported) return fail(AP_ERR_UNSUPPORTED, detail);
+    return fail(AP_ERR_HIP, std::string("ap_recompress_noalloc: ") + hipGetErrorString(e) +
+                                (detail.empty() ? std::string() : " (" + detail + ")"));
+  }
+  c->last_stream = st;
+  return AP_OK;
+}
+
 ap_status ap_cache_set_factors(ap_cache* c, const void* U_k, const void* B_k, const void* U_v,
                                const void* B_v, void* stream) {
   if (!c || !U_k || !B_k || !U_v || !B_v) return fail(AP_ERR_NULL_ARG, "cache and all factor pointers must be set");

@@ -23,6 +23,8 @@
 //                         Philox4x32-10 (Salmon et al., SC'11) keyed by the seed
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <string>
 #include <type_traits>
 
 #include "ap_internal.h"
@@ -1105,6 +1107,13 @@ __global__ void k_copy_sigma(const float* __restrict__ sig, float* __restrict__ 
 }
 
 // ================================================================ driver
+// Clears a buffer (16-byte words; a kernel rather than hipMemsetAsync, so that a caller
+// may capture the whole factorisation in a graph).
+__global__ __launch_bounds__(256) void k_zero(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 static dim3 grid_1d(size_t total, int threads = 256) {
   size_t g = (total + threads - 1) / threads;
   g = g < 1 ? 1 : (g > 65536 ? 65536 : g);
@@ -1214,8 +1223,12 @@ static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void*
   return hipGetLastError();
 }
 
+// The factorisation workspace comes from stream-ordered allocations (fixed == nullptr)
+// or is carved out of the caller's fixed buffer of fixed_bytes (then nothing is
+// allocated, and a workspace that does not fit is refused before anything is enqueued).
 template <class T>
-static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStream_t st) {
+static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStream_t st, void* fixed,
+                             size_t fixed_bytes) {
   const Dims& dm = c->dm;
   CompressWs ws;
   ws.nmat = 2 * dm.B;
@@ -1248,12 +1261,30 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
       {reinterpret_cast<void**>(&ws.sig), (size_t)nmat * ellp * 4},
   };
   hipError_t e = hipSuccess;
-  for (Buf& bf : bufs) {
-    if (bf.bytes == 0) continue;
-    e = hipMallocAsync(bf.p, bf.bytes, st);
-    if (e != hipSuccess) break;
+  if (fixed != nullptr) {
+    // 256-byte aligned pieces of the fixed buffer, in order
+    size_t off = 0;
+    for (Buf& bf : bufs) {
+      if (bf.bytes == 0) continue;
+      off = (off + 255) & ~(size_t)255;
+      *bf.p = static_cast<unsigned char*>(fixed) + off;
+      off += bf.bytes;
+    }
+    if (off > fixed_bytes) {
+      for (Buf& bf : bufs) *bf.p = nullptr;
+      set_error("ap_recompress_noalloc: this shape needs " + std::to_string(off) +
+                " bytes of factorisation workspace, the fixed workspace holds " + std::to_string(fixed_bytes));
+      return hipErrorNotSupported;
+    }
+  } else {
+    for (Buf& bf : bufs) {
+      if (bf.bytes == 0) continue;
+      e = hipMallocAsync(bf.p, bf.bytes, st);
+      if (e != hipSuccess) break;
+    }
   }
   auto release = [&]() {
+    if (fixed != nullptr) return;
     for (Buf& bf : bufs)
       if (*bf.p) (void)hipFreeAsync(*bf.p, st);
   };
@@ -1267,10 +1298,14 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
     release();
     return err;
   };
-  // padded rows of Omega^T and X^T must read as zero
-  e = hipMemsetAsync(ws.omT, 0, (size_t)nmat * ellp * dm.W * es, st);
-  if (e == hipSuccess) e = hipMemsetAsync(ws.XT, 0, (size_t)nmat * ellp * ws.M * es, st);
-  if (e == hipSuccess && ws.XTlo) e = hipMemsetAsync(ws.XTlo, 0, (size_t)nmat * ellp * ws.M * es, st);
+  // padded rows of Omega^T and X^T must read as zero (each buffer's byte count is a
+  // multiple of 16: ellp is a multiple of 16)
+  for (void* z : {ws.omT, ws.XT, ws.XTlo}) {
+    if (z == nullptr) continue;
+    const size_t bytes = (size_t)nmat * ellp * (z == ws.omT ? dm.W : ws.M) * es;
+    hipLaunchKernelGGL(k_zero, grid_1d(bytes / 16), dim3(256), 0, st, static_cast<uint4*>(z), bytes / 16);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return fail_stage(e, "workspace clear");
   if (c->params.omega != nullptr)
     hipLaunchKernelGGL(k_omega_copy<T>, grid_1d((size_t)nmat * dm.ell * dm.W), dim3(256), 0, st,
@@ -1354,8 +1389,47 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
 
 hipError_t run_compress(ap_cache* c, const void* k, const void* v, hipStream_t st) {
   // 4-bit caches take bf16 K and V and keep B in bf16; only U's assembly differs
-  if (c->dm.storage != AP_F32) return compress_t<bf16_t>(c, k, v, st);
-  return compress_t<float>(c, k, v, st);
+  if (c->dm.storage != AP_F32) return compress_t<bf16_t>(c, k, v, st, nullptr, 0);
+  return compress_t<float>(c, k, v, st, nullptr, 0);
+}
+
+// ---------------------------------------------------------------- fixed workspace
+// The factorisation workspace of the allocation-free re-factorisation: one fixed
+// device array, which every GPU the library runs on holds until the process ends.
+// Host code never passes the array's name to a kernel: on the host it is only a
+// stand-in for the symbol.  Its device address on each GPU is looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+static __device__ __align__(256) unsigned char scratch[kNoAllocWorkspaceBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[64];   // per device: the address of that device's copy
+
+static hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t run_compress_noalloc(ap_cache* c, const void* k, const void* v, hipStream_t st) {
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) {
+    set_error(std::string("ap_recompress_noalloc: device address of the fixed workspace: ") +
+              hipGetErrorString(e));
+    return e;
+  }
+  if (c->dm.storage != AP_F32) return compress_t<bf16_t>(c, k, v, st, ws, kNoAllocWorkspaceBytes);
+  return compress_t<float>(c, k, v, st, ws, kNoAllocWorkspaceBytes);
 }
 
 }  // namespace ap
