@@ -14,9 +14,13 @@ Timed regions, in order:
      synchronisations, and HIP events on the launch stream as a cross-check);
   2. K more steps with the library's per-kernel HIP events (ap_timing_*) for the
      kernel breakdown and the dominant kernel's roofline;
-  3. the compressor: ap_recompress of the same batch's K and V (randomized
+  3. max(K, 100) single calls, each bracketed by its own pair of HIP events on the
+     launch stream: median and p10 / p90 per call;
+  4. the compressor: ap_recompress of the same batch's K and V (randomized
      subspace iteration), which runs once per cache, not per step;
-  4. the CPU oracle's decode step on a bounded sample of the same sequences.
+  5. end to end (--e2e, on by default): ap_compress of the batch-256 4096 x 4096
+     layer's 512 K and V matrices followed by 16 decode steps with fresh queries;
+  6. the CPU oracle's decode step on a bounded sample of the same sequences.
 
 Prints one JSON line.  `--calib-copy` instead runs only a plain device copy of a
 known size (the calibration run for the HBM byte counters).
@@ -57,6 +61,8 @@ def parse():
                     help="int4: the workload with 4-bit token factors (U codes + block scales; B, "
                          "K, V and text in bf16)")
     ap.add_argument("--no-compress", action="store_true")
+    ap.add_argument("--no-e2e", action="store_true",
+                    help="skip the end-to-end leg (compress the batch-256 layer + 16 decode steps)")
     ap.add_argument("--compress-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -290,6 +296,20 @@ def main():
         c.timing_enable(0)
     kernel_avg_ms = {k: v / max(ncalls, 1) for k, v in kms.items() if v > 0}
 
+    # ---- 3. per-call distribution: each call between its own two events
+    ncall = max(args.steps, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncall)]
+    torch.cuda.synchronize()
+    for i in range(ncall):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) for a, b in evs)
+
+    def pct(x):
+        return per_call[min(len(per_call) - 1, int(round(x * (len(per_call) - 1))))]
+
     ms_per_step = 1e3 * elapsed / args.steps
     tokens_per_step = B * (w.n_tokens + w.n_text)
     value = tokens_per_step / (elapsed / args.steps)
@@ -325,6 +345,8 @@ def main():
                    **({"ema_alpha": args.ema_alpha} if ema else {}),
                    **({"text_rank": Rt, "text_r_lo": tr_lo, "text_top_k": tk_top} if Rt else {})},
         "ms_per_step_hip_events": event_ms,
+        "per_call_ms": {"calls": ncall, "median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9),
+                        "min": per_call[0], "max": per_call[-1]},
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "GB/s": step_bytes / (elapsed / args.steps) / 1e9,
                 "frac_of_peak": step_bytes / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBPS},
@@ -340,6 +362,8 @@ def main():
 
     if not args.no_compress:
         result["compress"] = compress_leg(w, args.compress_reps, binding, wl, np, torch)
+    if not args.no_e2e:
+        result["e2e"] = e2e_leg(binding, wl, np, torch)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, seqs, args.cpu_seconds)
@@ -371,6 +395,48 @@ def compress_leg(w, reps, binding, wl, np, torch):
     return {"ms": ms, "reps": reps, "matrices": 2 * w.batch, "ell": w.ell,
             "power_iters": w.power_iters, "algorithmic_bytes": nbytes,
             "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
+def e2e_leg(binding, wl, np, torch):
+    """The batch-256 layer end to end: the factorisation of its 256 K and 256 V matrices
+    (4096 x 4096 bf16, p = 16, q = 2; two distinct sequences tiled over the batch) into
+    an allocated cache (ap_recompress, the serving-slot form of ap_compress), then 16
+    decode steps with fresh queries on the new factors, timed with HIP events on the
+    launch stream.  A warm-up run of the same sequence comes first."""
+    w = wl.WORKLOADS[5]
+    S = 2
+    idx = torch.tensor([b % S for b in range(w.batch)], device="cuda")
+    k = torch.from_numpy(np.stack([wl.gen_kv(w, b, 0) for b in range(S)])).to(torch.bfloat16).cuda()[idx].contiguous()
+    v = torch.from_numpy(np.stack([wl.gen_kv(w, b, 1) for b in range(S)])).to(torch.bfloat16).cuda()[idx].contiguous()
+    qs = [torch.from_numpy(np.stack([wl.gen_q(w, b % S, step=t) for b in range(w.batch)])).cuda()
+          for t in range(w.decode_steps)]
+    out = torch.empty(w.batch, w.n_q_heads * w.head_dim, dtype=torch.float32, device="cuda")
+    c = binding.compress(None, None, batch=w.batch, n_tokens=w.n_tokens, n_kv_heads=w.n_kv_heads,
+                         n_q_heads=w.n_q_heads, head_dim=w.head_dim, rank=w.rank,
+                         storage=torch.bfloat16, oversample=w.oversample, power_iters=w.power_iters)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+
+    def run(seed):
+        e0.record()
+        c.recompress(k, v, seed=seed)
+        e1.record()
+        for t in range(w.decode_steps):
+            binding.decode(c, qs[t], r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, out=out)
+        e2.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e2), e0.elapsed_time(e1)
+
+    run(1)
+    total, comp = run(2)
+    c.free()
+    s = 2
+    cbytes = (2 * w.power_iters + 2) * 2 * w.batch * w.n_tokens * w.width * s
+    dbytes = w.decode_steps * w.batch * kernel_bytes(w)["decode"]
+    ideal = (cbytes + dbytes) / (HBM_PEAK_GBPS * 1e9) * 1e3
+    return {"workload": w.name, "ms": total, "compress_ms": comp, "decode_ms": total - comp,
+            "decode_steps": w.decode_steps, "matrices": 2 * w.batch, "ell": w.ell,
+            "algorithmic_bytes": cbytes + dbytes, "ideal_ms_at_hbm_peak": ideal,
+            "frac_of_hbm_peak": ideal / total}
 
 
 def cpu_baseline(w, seqs, budget_s):

@@ -49,7 +49,7 @@ struct SelState {
 };
 
 struct SelLayout {
-  size_t qh, qs, st, rng, hist, selw, cand;
+  size_t qh, qb, qs, st, rng, hist, selw, cand;
   size_t sts, zs, hmx, lpart, ltx, lfin, red;   // single-kernel decode only
   size_t total;
   int hs;          // words per head in hist
@@ -66,6 +66,7 @@ __host__ __device__ inline SelLayout sel_layout(int HG, int nblk, int r_pad, int
   L.hs = kSelBins > 256 + 2 * nblk ? kSelBins : 256 + 2 * nblk;
   size_t o = 0;
   L.qh = o;   o = up(o + (size_t)(HG * d > 1024 ? HG * d : 1024) * 4);   // >= one float per thread
+  L.qb = o;   o = up(o + (size_t)2 * HG * d * 2);                          // q as bf16 hi, then lo
   L.qs = o;   o = up(o + (size_t)HG * r_pad * 4);
   L.st = o;   o = up(o + (size_t)HG * sizeof(SelState));
   L.rng = o;  o = up(o + (size_t)HG * 2 * 4);
@@ -368,6 +369,7 @@ __device__ __forceinline__ void select_body(
 
   const SelLayout Ly = sel_layout(HG, nblk, r_pad, d, FUSED, FUSED ? fa.Tn : 0);
   float* qh = reinterpret_cast<float*>(smem_raw + Ly.qh);
+  bf16_t* qb = reinterpret_cast<bf16_t*>(smem_raw + Ly.qb);
   float* qs = reinterpret_cast<float*>(smem_raw + Ly.qs);
   SelState* st = reinterpret_cast<SelState*>(smem_raw + Ly.st);
   uint32_t* rng = reinterpret_cast<uint32_t*>(smem_raw + Ly.rng);
@@ -380,8 +382,11 @@ __device__ __forceinline__ void select_body(
   const bool select = !none && !all;
   const int nplo = (r_lo + 15) >> 4;
 
-  // ---- A. loads in flight together: B_k rows first (the latent queries wait only for
-  // them), then q, then the first U_k low-panel tiles
+  // ---- A. loads in flight together: q first, then the B_k rows the low-rank scores
+  // need and the first U_k low-panel tiles; (bf16 rows on MFMA) the B_k rows of the
+  // latent columns >= r_lo are requested once the low rows are in and used at the end
+  // of the selection.  Rows read once are loaded non-temporally, so that they do not
+  // push the token factors, which the head groups of a sequence share, out of L2.
   constexpr int V = Vec16<TB>::n;
   constexpr int XB = 4;    // B_k row slices per lane in flight
   const int ginv_num = (65536 + G - 1) / G;   // (h * ginv_num) >> 16 == h / G for h, G <= 64
@@ -401,7 +406,7 @@ __device__ __forceinline__ void select_body(
     for (int u = 0; u < XB; ++u) {
       const int row = min(r0 + u * rstep, nrows - 1);   // clamped: loads stay unconditional
       const int hl = head_of(row), i = row - hl * r_pad;
-      x[u].load(Bk + ((size_t)b * r_pad + i) * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + seg * V);
+      x[u].load_nt(Bk + ((size_t)b * r_pad + i) * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + seg * V);
     }
   };
   // bf16 rows with d a multiple of 32 (up to 128): latent queries and text scores on
@@ -421,10 +426,11 @@ __device__ __forceinline__ void select_body(
       const TB* src = base + (size_t)row * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + 8 * lg;
 #pragma unroll
       for (int ks = 0; ks < XB; ++ks)
-        if (ks < nks) dst[ks].load(src + 32 * ks);
+        if (ks < nks) dst[ks].load_nt(src + 32 * ks);
     }
   };
-  // the tile's dot products with q_h (this lane's A operands in a)
+  // the tile's dot products with q_h (this lane's A operands in a); q_h's bf16 hi and lo
+  // halves come from LDS (qb), non-zero only in column 0 of the B operand
   auto tile_dot = [&](const Vec16<TB>(&a)[XB], int hl) {
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
     if constexpr (kBfRows) {
@@ -432,37 +438,31 @@ __device__ __forceinline__ void select_body(
 #pragma unroll
       for (int ks = 0; ks < XB; ++ks) {
         if (ks < nks) {
-          const float* qp = qh + hl * d + 32 * ks + 8 * lg;
-          const float4 q0 = *reinterpret_cast<const float4*>(qp);
-          const float4 q1 = *reinterpret_cast<const float4*>(qp + 4);
-          const float v[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-          uint32_t hw[4], lw[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hw[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-            lw[e] = pack_bf16x2(v[2 * e] - __uint_as_float(hw[e] << 16),
-                                v[2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u));
-          }
+          const int o = hl * d + 32 * ks + 8 * lg;
+          const uint4 hw = *reinterpret_cast<const uint4*>(qb + o);
+          const uint4 lw = *reinterpret_cast<const uint4*>(qb + HG * d + o);
           const v8bf av = __builtin_bit_cast(v8bf, a[ks].raw);
-          acc = mfma_bf16_k32(av, __builtin_bit_cast(v8bf, make_uint4(hw[0] & on, hw[1] & on, hw[2] & on, hw[3] & on)), acc);
-          acc = mfma_bf16_k32(av, __builtin_bit_cast(v8bf, make_uint4(lw[0] & on, lw[1] & on, lw[2] & on, lw[3] & on)), acc);
+          acc = mfma_bf16_k32(av, __builtin_bit_cast(v8bf, make_uint4(hw.x & on, hw.y & on, hw.z & on, hw.w & on)), acc);
+          acc = mfma_bf16_k32(av, __builtin_bit_cast(v8bf, make_uint4(lw.x & on, lw.y & on, lw.z & on, lw.w & on)), acc);
         }
       }
     }
     return acc;
   };
+  // (head, latent-row tile) pairs whose rows lie below r_lo: needed by the low-rank scores
+  auto lo_pair = [&](int pair) { return 16 * (pair - (pair / qtiles) * qtiles) < rlo; };
+  // one q value per thread (HG * d <= threads, checked at launch); stored unconditionally so the
+  // load is never sunk behind the tile loads
+  const int nq = nh * d;
+  const float qv = q[((size_t)b * Hq + h0) * d + min(tid, nq - 1)];
   if (mq) {
-    if (wave < npair_q) {
+    if (wave < npair_q && lo_pair(wave)) {
       const int hl = wave / qtiles, it = wave - hl * qtiles;
       load_tile_rows(x, Bk + (size_t)b * r_pad * W, 16 * it + c16, hl);
     }
   } else if (vec) {
     load_rows(wave * RPW + rw);
   }
-  // one q value per thread (HG * d <= threads, checked at launch); stored unconditionally so the
-  // load is never sunk behind the tile loads
-  const int nq = nh * d;
-  const float qv = q[((size_t)b * Hq + h0) * d + min(tid, nq - 1)];
   // single-kernel decode: the first text K rows ride along (text scores need only q)
   const int Tn = FUSED ? fa.Tn : 0;
   const int nrt = nh * Tn;                   // text rows (head, token)
@@ -474,7 +474,7 @@ __device__ __forceinline__ void select_body(
     for (int u = 0; u < XB; ++u) {
       const int row = max(min(r0 + u * rstep, nrt - 1), 0);
       const int hl = row / max(Tn, 1), t = row - hl * Tn;
-      xt[u].load(tk + ((size_t)b * Tn + t) * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + seg * V);
+      xt[u].load_nt(tk + ((size_t)b * Tn + t) * W + (size_t)(((h0 + hl) * ginv_num) >> 16) * d + seg * V);
     }
   };
 
@@ -500,6 +500,11 @@ __device__ __forceinline__ void select_body(
     for (int s = 0; s < PREF; ++s) load_step(s);
   }
   qh[tid] = qv;
+  if (tid < HG * d) {
+    const bf16_t hi = f32_to_bf16(qv);
+    qb[tid] = hi;
+    qb[HG * d + tid] = f32_to_bf16(qv - bf16_to_f32(hi));
+  }
   for (int i = tid; i < nh * HS; i += nthr) hist[i] = 0;
   for (int i = tid; i < nh * nblk; i += nthr) selw[i] = 0;
   if (tid < nh) {
@@ -513,16 +518,32 @@ __device__ __forceinline__ void select_body(
     }
   }
   lds_barrier();
-  // latent queries q~[h][i] = B_k[i, g*d : g*d+d] . q_h
-  if (mq) {
+  // latent queries q~[h][i] = B_k[i, g*d : g*d+d] . q_h (on MFMA: the rows below r_lo
+  // now, the others at the end of the selection)
+  bool x_first = true;   // x still holds the rows of this wavefront's first pair
+  auto latent_pairs = [&](bool low) {
     for (int pair = wave; pair < npair_q; pair += nwv) {
+      if (lo_pair(pair) != low) continue;
       const int hl = pair / qtiles, it = pair - hl * qtiles;
-      if (pair != wave) load_tile_rows(x, Bk + (size_t)b * r_pad * W, 16 * it + c16, hl);
+      if (pair != wave || !x_first) {
+        load_tile_rows(x, Bk + (size_t)b * r_pad * W, 16 * it + c16, hl);
+        x_first = false;
+      }
       const v4f acc = tile_dot(x, hl);
       if (c16 == 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) qs[hl * r_pad + 16 * it + 4 * lg + t] = acc[t];
       }
+    }
+  };
+  if (mq) {
+    latent_pairs(true);
+    // the B_k rows of the latent columns >= r_lo: requested only now, so that they do not
+    // hold up q and the low rows in the memory system at the start
+    if (wave < npair_q && !lo_pair(wave)) {
+      const int hl = wave / qtiles, it = wave - hl * qtiles;
+      load_tile_rows(x, Bk + (size_t)b * r_pad * W, 16 * it + c16, hl);
+      x_first = true;
     }
   } else if (vec) {
     for (int r0 = wave * RPW + rw; r0 - rw < nrows; r0 += XB * rstep) {
@@ -891,6 +912,8 @@ __device__ __forceinline__ void select_body(
       }
     }
   }
+  // the remaining latent queries: their B_k rows arrived during the selection
+  if (mq) latent_pairs(false);
   lds_barrier();
 
   // ---- E. selection bits per (head, 32-token block)
@@ -1100,7 +1123,7 @@ __device__ __forceinline__ void select_body(
         const int row = min(r0 + u * RS, orows - 1);   // clamped: loads stay unconditional
         const T* src = row < r_pad ? Bv + ((size_t)b * r_pad + row) * W
                                    : tv + ((size_t)b * Tn + (row - r_pad)) * W;
-        xo[u].load(src + (size_t)og * d + occ * V);
+        xo[u].load_nt(src + (size_t)og * d + occ * V);
       }
     };
 

@@ -132,10 +132,16 @@ __device__ __forceinline__ v4f value_mma(const LaneTile<float>& a, int hf, bool 
 
 // 16 bytes of storage elements read with one vector load.
 template <class T> struct Vec16;   // 16 bytes of storage elements
+// load_nt: a non-temporal load, for rows a workgroup reads once, so that they do not
+// push the token factors (which the head groups of a sequence re-read) out of L2.
 template <> struct Vec16<bf16_t> {
   static constexpr int n = 8;
   uint4 raw;
   __device__ __forceinline__ void load(const bf16_t* p) { raw = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_nt(const bf16_t* p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    raw = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  }
   __device__ __forceinline__ float get(int e) const {
     const uint32_t w = e < 2 ? raw.x : (e < 4 ? raw.y : (e < 6 ? raw.z : raw.w));
     return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
@@ -145,6 +151,10 @@ template <> struct Vec16<float> {
   static constexpr int n = 4;
   float4 v;
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    v = __builtin_bit_cast(float4, __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)));
+  }
   __device__ __forceinline__ float get(int e) const { return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w)); }
 };
 
