@@ -103,6 +103,39 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 }
 
 template <int N>
+__device__ __forceinline__ float dpp_ror_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, true)));
+}
+template <int N>
+__device__ __forceinline__ float dpp_ror_min(float v) {
+  return fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, true)));
+}
+// Maximum and minimum of floats over the lanes of a wavefront that hold the same head
+// (lane%16 congruent mod HG), as head_max below.
+template <int HG>
+__device__ __forceinline__ float head_fmax(float v) {
+  if constexpr (HG <= 1) v = dpp_ror_max<1>(v);
+  if constexpr (HG <= 2) v = dpp_ror_max<2>(v);
+  if constexpr (HG <= 4) v = dpp_ror_max<4>(v);
+  if constexpr (HG <= 8) v = dpp_ror_max<8>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+template <int HG>
+__device__ __forceinline__ float head_fmin(float v) {
+  if constexpr (HG <= 1) v = dpp_ror_min<1>(v);
+  if constexpr (HG <= 2) v = dpp_ror_min<2>(v);
+  if constexpr (HG <= 4) v = dpp_ror_min<4>(v);
+  if constexpr (HG <= 8) v = dpp_ror_min<8>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+template <int N>
 __device__ __forceinline__ uint32_t dpp_ror(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x120 + N, 0xF, 0xF, true));
 }
@@ -693,14 +726,19 @@ __device__ __forceinline__ void select_body(
     {
       uint32_t kmax = 0u, kmin = 0u;   // kmin holds ~key; absent scores add nothing
       if constexpr (FUSED) {
-        // branch-free (measured faster in the single-kernel decode; in the selection-only
-        // kernel with 8 steps it costs registers the branches do not)
+        // branch-free, on the float scores (absent scores replaced by -inf / +inf), with
+        // one conversion to keys per lane
+        float fmx = -INFINITY, fmn = INFINITY;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
-          const uint32_t k = score_key(sc[i]), m = bit_mask(vm, i);
-          kmax = max(kmax, k & m);
-          kmin = max(kmin, ~k & m);
+          const bool ok = (vm >> i) & 1u;
+          fmx = fmaxf(fmx, ok ? sc[i] : -INFINITY);
+          fmn = fminf(fmn, ok ? sc[i] : INFINITY);
         }
+        fmx = head_fmax<HG>(fmx);
+        fmn = head_fmin<HG>(fmn);
+        kmax = fmx == -INFINITY ? 0u : score_key(fmx);
+        kmin = fmn == INFINITY ? 0u : ~score_key(fmn);
       } else {
 #pragma unroll
         for (int a = 0; a < NACC; ++a) {
@@ -715,8 +753,10 @@ __device__ __forceinline__ void select_body(
           }
         }
       }
-      kmax = head_max<HG>(kmax);
-      kmin = head_max<HG>(kmin);
+      if constexpr (!FUSED) {
+        kmax = head_max<HG>(kmax);
+        kmin = head_max<HG>(kmin);
+      }
       if (lg == 0 && c16 < HG && my_on) {
         atomicMax(&rng[2 * my_h], kmax);
         atomicMax(&rng[2 * my_h + 1], kmin);
@@ -732,9 +772,11 @@ __device__ __forceinline__ void select_body(
       const float range = hi - lo_h;
       mul_h = (range > 1e-30f && range < 3.0e38f) ? static_cast<float>(kSelBins - 1) / range : 0.f;
     }
-    // clamped in float first: any input (NaN included) gives a bin in [0, kSelBins)
+    // bin(s) = s * mul - lo * mul, clamped in float first (one fma and one med3): a
+    // monotone map, and any input (NaN included) gives a bin in [0, kSelBins)
+    const float off_h = -lo_h * mul_h;
     auto bin_of = [&](float s) {
-      return static_cast<uint32_t>(fminf(fmaxf((s - lo_h) * mul_h, 0.f), static_cast<float>(kSelBins - 1)));
+      return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(fmaf(s, mul_h, off_h), 0.f, static_cast<float>(kSelBins - 1)));
     };
     {
       // branch-free: tokens past N (and absent heads) add 0, so the LDS atomics issue
@@ -781,8 +823,18 @@ __device__ __forceinline__ void select_body(
           nib |= (ok && bn >= bwhole) ? (1u << t) : 0u;
           cbits |= (ok && mode_h == kRank && bn == bstar_h) ? (1u << (4 * a + t)) : 0u;
         }
-        // n0 < 32 * nblk always (blocks past the end hold no set bits but stay in range)
-        atomicOr(&selw[my_h * nblk + min(n0 >> 5, nblk - 1)], nib << (n0 & 31));
+        // The eight lanes holding the tokens of one (head, block) word are the two tile
+        // halves (lane%16 apart by HG) in each of the four 16-lane rows: OR them together
+        // (a rotation by HG inside the row leaves the pair in the upper half's lane, then
+        // the row swaps), and the upper half's lane of row 0 stores the word.
+        uint32_t wv = nib << (n0 & 31);
+        wv |= dpp_ror<HG>(wv);
+        const auto r1 = __builtin_amdgcn_permlane16_swap(wv, wv, false, false);
+        wv = r1[0] | r1[1];
+        const auto r2 = __builtin_amdgcn_permlane32_swap(wv, wv, false, false);
+        wv = r2[0] | r2[1];
+        const int blk = n0 >> 5;
+        if (my_j == 1 && lg == 0 && my_on && blk < nblk) selw[my_h * nblk + blk] = wv;
       }
       if (cbits) {
 #pragma unroll
@@ -973,10 +1025,6 @@ __device__ __forceinline__ void select_body(
     float* zpart = reinterpret_cast<float*>(hist);                 // [waves][HG][r_pad]
     float* red = reinterpret_cast<float*>(smem_raw + Ly.red);      // [row groups][HG * d]
 
-    // first tiles of the full-rank score pass (after the selection: requests in flight
-    // during its LDS-bound phases slow them more than they gain)
-#pragma unroll
-    for (int s = 0; s < PD; ++s) ld(s);
     // ---- F1. text scores in log2 units, running max per head: on MFMA, one (head,
     // 16-token tile) pair per wavefront, or LPR lanes per text row; the first pair or
     // XB * rstep rows come from the loads issued after the latent queries, any further
@@ -1023,6 +1071,11 @@ __device__ __forceinline__ void select_body(
       }
     }
 
+    // first tiles of the full-rank score pass: requested after the text scores, whose
+    // rows then are the only loads ahead of them (requests in flight during the
+    // selection's LDS-bound phases slow them more than they gain)
+#pragma unroll
+    for (int s = 0; s < PD; ++s) ld(s);
     // ---- F2. full-rank part of the selected tokens' scores (columns >= r_lo), on the
     // same block-diagonal tiles as the low-rank scores; final scores in log2 units
     const int nph = NPr - p0;
@@ -1073,11 +1126,12 @@ __device__ __forceinline__ void select_body(
     }
     // ---- F3. softmax over text and visual tokens: per-head maximum, probabilities, sums
     {
-      uint32_t km = 0u;
+      // absent scores are -inf; a head's maximum of finite scores is finite
+      float fm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) km = max(km, score_key(sc[i]));
-      km = head_max<HG>(km);
-      if (lg == 0 && c16 < HG && my_on) atomicMax(&hmx[my_h], km);
+      for (int i = 0; i < KPL; ++i) fm = fmaxf(fm, sc[i]);
+      fm = head_fmax<HG>(fm);
+      if (lg == 0 && c16 < HG && my_on) atomicMax(&hmx[my_h], fm == -INFINITY ? 0u : score_key(fm));
     }
     lds_barrier();
     {
@@ -1162,7 +1216,12 @@ __device__ __forceinline__ void select_body(
           }
         }
         if (s + PD < 2 * NSK) ld(s + PD);
-        if (s + PD == 2 * NSK - 1) load_out(rsub);   // right after the last tile load
+        if (s + PD == 2 * NSK - 1) {
+          load_out(rsub);   // right after the last tile load
+          // a compiler memory barrier: the loads stay here instead of being sunk to their
+          // use after the value reduction (it waits for nothing)
+          asm volatile("" ::: "memory");
+        }
       }
     }
     // lane l holds Z for latent columns 16p + 4lg + t and tile column c16: sum the
