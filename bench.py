@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--compress-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--leg", choices=["compress", "e2e"], default=None,
+                    help="run only this leg (for profiling) and print its JSON")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (counter calibration)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
@@ -207,6 +209,12 @@ def main():
         w = w.replace(storage=args.storage)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.leg == "compress":
+        print(json.dumps({"compress": compress_leg(w, args.compress_reps, binding, wl, np, torch)}))
+        return
+    if args.leg == "e2e":
+        print(json.dumps({"e2e": e2e_leg(binding, wl, np, torch)}))
+        return
     dt = torch.float32 if w.storage == "f32" else torch.bfloat16      # B, text
     du = torch.bfloat16 if w.storage == "bf16" else torch.float32     # U handed to set_factors
     st_arg = "int4" if w.storage == "int4" else dt
