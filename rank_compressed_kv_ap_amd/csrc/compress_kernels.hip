@@ -137,7 +137,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
                                                         int tiles_m) {
   static_assert(std::is_same<T, bf16_t>::value, "MFMA GEMM path is bf16");
   constexpr int XR = NT * 16;                        // rows of X^T (= ellp)
-  constexpr int XU = (XR * 8 + kGemmThreads - 1) / kGemmThreads;   // 16-byte X loads per thread
+  constexpr int CPR = kGemmBK / 8;                   // 16-byte chunks per k slice row
+  constexpr int XU = (XR * CPR + kGemmThreads - 1) / kGemmThreads;   // 16-byte X loads per thread
+  constexpr int AU = kGemmBM * CPR / kGemmThreads;   // 16-byte A loads per thread
+  constexpr int RPP = kGemmThreads / CPR;            // A rows per pass (not TRANS)
   __shared__ __align__(16) bf16_t As[kGemmBM * kGemmLdsStride];
   __shared__ __align__(16) bf16_t Xs[(SPLIT ? 2 : 1) * XR * kGemmLdsStride];
   // workgroups are dealt to the 8 XCDs in turn: when the matrices come in eights, the
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
   // ---- one 64-wide k slice in registers: A (4 x 8 elements per thread) and X^T
   // (XU x 8 elements per thread), both staged in LDS before the MFMAs
   struct Slice {
-    uint4 a[4];
+    uint4 a[AU];
     uint4 x[XU];
     uint4 xl[SPLIT ? XU : 1];
   };
@@ -188,25 +191,25 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
   auto load_slice = [&](int k0, Slice& sl) {
     if constexpr (VEC) {
       if (!TRANS) {
-        // rows (tid >> 3) + 32 h, k = k0 + 8 (tid & 7) .. +7 (a run lies wholly inside K or past it)
+        // rows tid / CPR + RPP h, k = k0 + 8 (tid % CPR) .. +7 (a run lies wholly inside K or past it)
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int row = (tid >> 3) + 32 * h, gk = k0 + (tid & 7) * 8;
+        for (int h = 0; h < AU; ++h) {
+          const int row = tid / CPR + RPP * h, gk = k0 + (tid % CPR) * 8;
           const uint4 t = *reinterpret_cast<const uint4*>(A + (size_t)min(m0 + row, M - 1) * W + min(gk, K - 8));
           sl.a[h] = t;
         }
       } else {
-        // k rows 4 (tid >> 4) + h, m = m0 + 8 (tid & 15) .. +7
+        // k rows AU (tid >> 4) + h, m = m0 + 8 (tid & 15) .. +7
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int gk = k0 + 4 * (tid >> 4) + h, gm = m0 + (tid & 15) * 8;
+        for (int h = 0; h < AU; ++h) {
+          const int gk = k0 + AU * (tid >> 4) + h, gm = m0 + (tid & 15) * 8;
           sl.a[h] = *reinterpret_cast<const uint4*>(A + (size_t)min(gk, K - 1) * W + min(gm, M - 8));
         }
       }
 #pragma unroll
       for (int u = 0; u < XU; ++u) {
-        const int idx = min(tid + u * kGemmThreads, XR * 8 - 1);
-        const int j = idx >> 3, gk = k0 + 8 * (idx & 7);
+        const int idx = min(tid + u * kGemmThreads, XR * CPR - 1);
+        const int j = idx / CPR, gk = k0 + 8 * (idx % CPR);
         const size_t off = (size_t)j * K + min(gk, K - 8);
         const uint4 t = *reinterpret_cast<const uint4*>(X + off);
         sl.x[u] = gk < K ? t : z4;
@@ -217,10 +220,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
       }
     } else {
     if (!TRANS) {
-      // rows (tid >> 3) + 32 h, k = k0 + 8 (tid & 7) .. +7
+      // rows tid / CPR + RPP h, k = k0 + 8 (tid % CPR) .. +7
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int row = (tid >> 3) + 32 * h, kk = (tid & 7) * 8;
+      for (int h = 0; h < AU; ++h) {
+        const int row = tid / CPR + RPP * h, kk = (tid % CPR) * 8;
         const int gm = min(m0 + row, M - 1), gk = k0 + kk;
         if (avec && gk + 8 <= K) {
           sl.a[h] = *reinterpret_cast<const uint4*>(A + (size_t)gm * W + gk);
@@ -231,10 +234,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
         }
       }
     } else {
-      // k rows 4 (tid >> 4) + h, m = m0 + 8 (tid & 15) .. +7 (transposed into LDS later)
+      // k rows AU (tid >> 4) + h, m = m0 + 8 (tid & 15) .. +7 (transposed into LDS later)
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int kk = 4 * (tid >> 4) + h, mm = (tid & 15) * 8;
+      for (int h = 0; h < AU; ++h) {
+        const int kk = AU * (tid >> 4) + h, mm = (tid & 15) * 8;
         const int gk = k0 + kk, gm = m0 + mm;
         if (avec && gk < K && gm + 8 <= M) {
           sl.a[h] = *reinterpret_cast<const uint4*>(A + (size_t)gk * W + gm);
@@ -248,8 +251,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
     // X^T rows j = idx / 8, k = k0 + 8 (idx % 8) .. +7 (zero past K)
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-      const int idx = min(tid + u * kGemmThreads, XR * 8 - 1);
-      const int j = idx >> 3, gk = k0 + 8 * (idx & 7);
+      const int idx = min(tid + u * kGemmThreads, XR * CPR - 1);
+      const int j = idx / CPR, gk = k0 + 8 * (idx % CPR);
       const size_t off = (size_t)j * K + gk;
       if (xvec && gk + 8 <= K) {
         sl.x[u] = *reinterpret_cast<const uint4*>(X + off);
@@ -269,28 +272,32 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
   auto stage = [&](const Slice& sl) {
     if (!TRANS) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        *reinterpret_cast<uint4*>(&As[((tid >> 3) + 32 * h) * kGemmLdsStride + (tid & 7) * 8]) = sl.a[h];
+      for (int h = 0; h < AU; ++h)
+        *reinterpret_cast<uint4*>(&As[(tid / CPR + RPP * h) * kGemmLdsStride + (tid % CPR) * 8]) = sl.a[h];
     } else {
-      // 4 k rows x 8 m columns in registers -> 8 columns of 4 consecutive k (8 bytes)
-      const int kk = 4 * (tid >> 4), mm = (tid & 15) * 8;
-      const uint32_t r0[4] = {sl.a[0].x, sl.a[0].y, sl.a[0].z, sl.a[0].w};
-      const uint32_t r1[4] = {sl.a[1].x, sl.a[1].y, sl.a[1].z, sl.a[1].w};
-      const uint32_t r2[4] = {sl.a[2].x, sl.a[2].y, sl.a[2].z, sl.a[2].w};
-      const uint32_t r3[4] = {sl.a[3].x, sl.a[3].y, sl.a[3].z, sl.a[3].w};
+      // groups of 4 k rows x 8 m columns in registers -> 8 columns of 4 consecutive k (8 bytes)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint2 ev = make_uint2((r0[c] & 0xffffu) | (r1[c] << 16), (r2[c] & 0xffffu) | (r3[c] << 16));
-        const uint2 od = make_uint2((r0[c] >> 16) | (r1[c] & 0xffff0000u), (r2[c] >> 16) | (r3[c] & 0xffff0000u));
-        const int re = mm + 2 * c, ro = re + 1;   // 16-byte chunk kk / 8, 8-byte half (kk / 4) & 1
-        *reinterpret_cast<uint2*>(&As[re * kGemmLdsStride + 8 * achunk(re, kk >> 3) + (kk & 4)]) = ev;
-        *reinterpret_cast<uint2*>(&As[ro * kGemmLdsStride + 8 * achunk(ro, kk >> 3) + (kk & 4)]) = od;
+      for (int q = 0; q < AU / 4; ++q) {
+        const int kk = AU * (tid >> 4) + 4 * q, mm = (tid & 15) * 8;
+        const uint4 a0 = sl.a[4 * q], a1 = sl.a[4 * q + 1], a2 = sl.a[4 * q + 2], a3 = sl.a[4 * q + 3];
+        const uint32_t r0[4] = {a0.x, a0.y, a0.z, a0.w};
+        const uint32_t r1[4] = {a1.x, a1.y, a1.z, a1.w};
+        const uint32_t r2[4] = {a2.x, a2.y, a2.z, a2.w};
+        const uint32_t r3[4] = {a3.x, a3.y, a3.z, a3.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint2 ev = make_uint2((r0[c] & 0xffffu) | (r1[c] << 16), (r2[c] & 0xffffu) | (r3[c] << 16));
+          const uint2 od = make_uint2((r0[c] >> 16) | (r1[c] & 0xffff0000u), (r2[c] >> 16) | (r3[c] & 0xffff0000u));
+          const int re = mm + 2 * c, ro = re + 1;   // 16-byte chunk kk / 8, 8-byte half (kk / 4) & 1
+          *reinterpret_cast<uint2*>(&As[re * kGemmLdsStride + 8 * achunk(re, kk >> 3) + (kk & 4)]) = ev;
+          *reinterpret_cast<uint2*>(&As[ro * kGemmLdsStride + 8 * achunk(ro, kk >> 3) + (kk & 4)]) = od;
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-      const int idx = min(tid + u * kGemmThreads, XR * 8 - 1);
-      const int o = (idx >> 3) * kGemmLdsStride + 8 * (idx & 7);
+      const int idx = min(tid + u * kGemmThreads, XR * CPR - 1);
+      const int o = (idx / CPR) * kGemmLdsStride + 8 * (idx % CPR);
       *reinterpret_cast<uint4*>(&Xs[o]) = sl.x[u];
       if constexpr (SPLIT) *reinterpret_cast<uint4*>(&Xs[XR * kGemmLdsStride + o]) = sl.xl[u];
     }
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
 
   auto multiply = [&]() {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int s2 = 0; s2 < kGemmBK / 32; ++s2) {
       v8bf ab[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -374,27 +381,34 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ Kmat
 //
 // k_gram: partial Grams.  Workgroup (mat, split) takes rows [split*rows, +rows) of
 // Y [M][ellp]; each wavefront accumulates every upper 16x16 tile (fp32 MFMA 16x16x4,
-// one 4-row slice per k-step) over its quarter of them, the four are summed in LDS
-// and the workgroup writes Gpart[mat][split] (full, symmetric).  Deterministic:
-// the partials are summed in a fixed order by k_chol.
+// one 4-row slice per k-step) over its share of them, all loads of UR slices issued
+// before their products.  The wavefronts' tiles are summed by halving (the upper half
+// of the wavefronts hands its tiles to the lower half through LDS, one float4 per lane
+// and tile), and wavefront 0 writes Gpart[mat][split] (full, symmetric) from its
+// registers.  Deterministic: a fixed order throughout, and the partials are summed in
+// a fixed order by k_chol.
 constexpr int kGramThreads = 256;
+constexpr int kGramChunk = 15;   // tiles handed over per LDS round
+
+__host__ __device__ inline size_t gram_lds_floats() { return (size_t)(kGramThreads / 128) * kGramChunk * 256; }
 
 template <int T>   // ellp / 16
 __global__ __launch_bounds__(kGramThreads) void k_gram(const float* __restrict__ Y, int M, int ellp,
                                                        int rows, int nsplit, float* __restrict__ Gpart) {
   extern __shared__ __align__(16) float sh[];
-  const int S = ellp + 1;
-  float* G = sh;   // [ellp][S]
+  constexpr int NW = kGramThreads / 64, NTILE = T * (T + 1) / 2;
+  constexpr int NCH = (NTILE + kGramChunk - 1) / kGramChunk;
+  float4* red = reinterpret_cast<float4*>(sh);   // [NW / 2][kGramChunk][64 lanes]
   const int mat = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
   const float* Ym = Y + (size_t)mat * M * ellp;
   const int r0 = split * rows, r1 = min(M, r0 + rows);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  v4f acc[T * (T + 1) / 2];
+  v4f acc[NTILE];
 #pragma unroll
-  for (int t = 0; t < T * (T + 1) / 2; ++t) acc[t] = v4f{0, 0, 0, 0};
+  for (int t = 0; t < NTILE; ++t) acc[t] = v4f{0, 0, 0, 0};
   constexpr int UR = 4;   // 4-row k-steps whose loads are in flight together
-  for (int n0 = r0 + 4 * UR * wave; n0 < r1; n0 += 4 * UR * 4) {
+  for (int n0 = r0 + 4 * UR * wave; n0 < r1; n0 += 4 * UR * NW) {
     float y[UR][T];
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
@@ -407,6 +421,9 @@ __global__ __launch_bounds__(kGramThreads) void k_gram(const float* __restrict__
         y[u][t] = live ? v : 0.f;
       }
     }
+    // every load of the slice is issued before the first product (left to itself the
+    // scheduler moves each load down to its use, leaving a few in flight)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
       int idx = 0;
@@ -416,29 +433,42 @@ __global__ __launch_bounds__(kGramThreads) void k_gram(const float* __restrict__
         for (int tj = ti; tj < T; ++tj, ++idx) acc[idx] = mfma_f32(y[u][ti], y[u][tj], acc[idx]);
     }
   }
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-      int idx = 0;
+  // ---- sum over the wavefronts by halving
 #pragma unroll
-      for (int ti = 0; ti < T; ++ti)
+  for (int ch = 0; ch < NCH; ++ch) {
+    for (int h = NW / 2; h >= 1; h >>= 1) {
+      if (wave >= h && wave < 2 * h) {
 #pragma unroll
-        for (int tj = ti; tj < T; ++tj, ++idx) {
+        for (int idx = ch * kGramChunk; idx < NTILE && idx < (ch + 1) * kGramChunk; ++idx)
+          red[((wave - h) * kGramChunk + idx - ch * kGramChunk) * 64 + lane] =
+              make_float4(acc[idx][0], acc[idx][1], acc[idx][2], acc[idx][3]);
+      }
+      __syncthreads();
+      if (wave < h) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int i = 16 * ti + 4 * lg + t, j = 16 * tj + l16;
-            const float v = acc[idx][t] + (w == 0 ? 0.f : G[i * S + j]);
-            G[i * S + j] = v;
-            if (ti != tj) G[j * S + i] = v;
-          }
+        for (int idx = ch * kGramChunk; idx < NTILE && idx < (ch + 1) * kGramChunk; ++idx) {
+          const float4 o = red[(wave * kGramChunk + idx - ch * kGramChunk) * 64 + lane];
+          acc[idx][0] += o.x; acc[idx][1] += o.y; acc[idx][2] += o.z; acc[idx][3] += o.w;
         }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
+  if (wave != 0) return;
+  // lane holds G[16 ti + 4 lg + t][16 tj + l16], t = 0..3; the mirrored tile takes the
+  // four as one 16-byte run of row 16 tj + l16
   float* out = Gpart + ((size_t)mat * nsplit + split) * ellp * ellp;
-  for (int idx = tid; idx < ellp * ellp; idx += kGramThreads) {
-    const int i = idx / ellp, j = idx % ellp;
-    out[idx] = G[i * S + j];
-  }
+  int idx = 0;
+#pragma unroll
+  for (int ti = 0; ti < T; ++ti)
+#pragma unroll
+    for (int tj = ti; tj < T; ++tj, ++idx) {
+      const int i = 16 * ti + 4 * lg, j = 16 * tj + l16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) out[(size_t)(i + t) * ellp + j] = acc[idx][t];
+      if (ti != tj)
+        *reinterpret_cast<float4*>(out + (size_t)j * ellp + i) = make_float4(acc[idx][0], acc[idx][1], acc[idx][2], acc[idx][3]);
+    }
 }
 
 // Sum of the partial Grams in a fixed order (deterministic), four floats per thread.
@@ -685,131 +715,129 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
   }
 }
 
-// Row tile of k_apply.
-static int apply_rows(int) { return 64; }
-
-// Q = Y Rinv for a tile of rows per workgroup (fp32 MFMA), written to Qout (Y itself for
-// a basis that is orthonormalised again, another buffer for a basis kept for the
+// Q = Y Rinv for 256 rows per workgroup (fp32 MFMA 16x16x4; wavefront w takes rows
+// 64w .. 64w + 63 of the tile as four 16-row tiles), written to Qout (Y itself for a
+// basis that is orthonormalised again, another buffer for a basis kept for the
 // factors, or nowhere when only Q^T is used); optionally Q^T in storage precision for
 // the next product (XT[mat][j][m]), and the rounding remainder Q^T - XT in XTlo for a
-// two-term product.  The Q tile is kept in LDS so that Q^T leaves in 16-byte runs along m.
-template <class T>
-__global__ __launch_bounds__(256) void k_apply(const float* Y, float* Qout, int M, int ellp,
+// two-term product.
+// The rows of Y go straight from HBM into registers, all of a wavefront's loads issued
+// before the first product: lane (i, g) of a row tile holds columns 16 kc + 4 g .. +3
+// of row i, so the MFMA k index runs over (kc, g, e) -> 16 kc + 4 g + e and R^-1 (in
+// LDS) is read with the same order.  R^-1 is upper triangular: column tile c of Q
+// takes k < 16 (c + 1) only.  Each lane ends with four consecutive rows of one column
+// of Q, written to Q^T as one 4-element run.
+constexpr int kApplyRT = 4;                  // 16-row tiles per wavefront
+constexpr int kApplyRows = 64 * kApplyRT;    // rows per workgroup
+
+template <class T, int NT>   // NT = ellp / 16
+__global__ __launch_bounds__(256) void k_apply(const float* Y, float* Qout, int M,
                                                const float* __restrict__ Rinv, T* __restrict__ XT,
-                                               T* __restrict__ XTlo, size_t xt_mat_stride, int tiles_m,
-                                               int rows) {
+                                               T* __restrict__ XTlo, size_t xt_mat_stride, int tiles_m) {
   extern __shared__ __align__(16) float sh[];
-  constexpr int kMaxRT = 2, kMaxCT = kMaxEll / 16;   // row tiles per wavefront (rows <= 128)
-  const int nrt = rows / 64;                          // rows is 64 or 128
-  const int S = ellp + 1;
-  float* Ys = sh;                  // [rows][S]
-  float* Rs = Ys + rows * S;       // [ellp][ellp]
+  constexpr int ellp = 16 * NT;
+  constexpr int RS = ellp + 4;     // LDS row stride: the four 4-row groups of a read meet
+                                   // different banks (4 RS = 16 mod 64 words)
+  float* Rs = sh;                  // [ellp][RS]
   const int mat = blockIdx.x / tiles_m;
-  const int m0 = (blockIdx.x % tiles_m) * rows;
+  const int m0 = (blockIdx.x - mat * tiles_m) * kApplyRows;
   const float* Ym = Y + (size_t)mat * M * ellp;
   float* Qm = Qout != nullptr ? Qout + (size_t)mat * M * ellp : nullptr;
   const float* Rm = Rinv + (size_t)mat * ellp * ellp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  // stage the Y tile and R^-1: 16-byte loads, 8 independent ones in flight per thread
-  // (indices clamped so every load is issued; rows past M are zeroed after the load)
-  const int ell4 = ellp / 4;   // ellp is a multiple of 16
-  const int ny = rows * ell4, nr = ellp * ell4;
-  for (int i0 = 0; i0 < ny + nr; i0 += 8 * 256) {
+  const int base = m0 + 64 * wave;   // first row of this wavefront
+  float4 y[kApplyRT][NT];
+#pragma unroll
+  for (int rt = 0; rt < kApplyRT; ++rt) {
+    const int row = min(base + 16 * rt + l16, M - 1);   // rows past M: clamped, never stored
+#pragma unroll
+    for (int kc = 0; kc < NT; ++kc)
+      y[rt][kc] = *reinterpret_cast<const float4*>(Ym + (size_t)row * ellp + 16 * kc + 4 * lg);
+  }
+  // R^-1 into LDS (16-byte loads, 8 in flight per thread)
+  constexpr int nr4 = ellp * ellp / 4;
+  for (int i0 = 0; i0 < nr4; i0 += 8 * 256) {
     float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = min(i0 + u * 256 + tid, ny + nr - 1);
-      if (idx < ny) {
-        const int r = idx / ell4, j4 = idx - r * ell4;
-        v[u] = *reinterpret_cast<const float4*>(Ym + (size_t)min(m0 + r, M - 1) * ellp + 4 * j4);
-      } else {
-        v[u] = *reinterpret_cast<const float4*>(Rm + (size_t)4 * (idx - ny));
-      }
-    }
+    for (int u = 0; u < 8; ++u) v[u] = reinterpret_cast<const float4*>(Rm)[min(i0 + u * 256 + tid, nr4 - 1)];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int idx = i0 + u * 256 + tid;
-      if (idx < ny) {
-        const int r = idx / ell4, j4 = idx - r * ell4;
-        const bool live = m0 + r < M;
-        float* d = Ys + r * S + 4 * j4;
-        d[0] = live ? v[u].x : 0.f;
-        d[1] = live ? v[u].y : 0.f;
-        d[2] = live ? v[u].z : 0.f;
-        d[3] = live ? v[u].w : 0.f;
-      } else if (idx < ny + nr) {
-        *reinterpret_cast<float4*>(Rs + 4 * (idx - ny)) = v[u];
-      }
+      const int i = i0 + u * 256 + tid;
+      if (i < nr4) *reinterpret_cast<float4*>(Rs + (i / (ellp / 4)) * RS + 4 * (i % (ellp / 4))) = v[u];
     }
   }
   __syncthreads();
-  const int T16 = ellp / 16;
-  // wave owns row tiles wave and wave + 4 (16 rows each), all column tiles
-  v4f acc[kMaxRT][kMaxCT];
-#pragma unroll
-  for (int i = 0; i < kMaxRT; ++i)
-#pragma unroll
-    for (int c = 0; c < kMaxCT; ++c) acc[i][c] = v4f{0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < kMaxRT; ++i) {
-    const int rt = wave + 4 * i;
-    if (i >= nrt) break;
-    for (int k0 = 0; k0 < ellp; k0 += 4) {
-      const float a = Ys[(16 * rt + l16) * S + k0 + lg];
-#pragma unroll
-      for (int c = 0; c < kMaxCT; ++c)
-        if (c < T16) acc[i][c] = mfma_f32(a, Rs[(k0 + lg) * ellp + 16 * c + l16], acc[i][c]);
-    }
-  }
-  __syncthreads();   // every read of the Y tile is done: it now takes Q
-#pragma unroll
-  for (int i = 0; i < kMaxRT; ++i) {
-    const int rt = wave + 4 * i;
-    if (i >= nrt) break;
-#pragma unroll
-    for (int c = 0; c < kMaxCT; ++c) {
-      if (c >= T16) continue;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 16 * rt + 4 * lg + t, j = 16 * c + l16;
-        Ys[r * S + j] = acc[i][c][t];
-        if (Qm != nullptr && m0 + r < M) Qm[(size_t)(m0 + r) * ellp + j] = acc[i][c][t];
-      }
-    }
-  }
-  if (XT == nullptr) return;
-  __syncthreads();
-  // Q^T[j][m0 .. m0 + rows): 8 consecutive m per thread
-  const int R8 = rows / 8;
-  T* xt = XT + (size_t)mat * xt_mat_stride;
+  T* xt = XT != nullptr ? XT + (size_t)mat * xt_mat_stride : nullptr;
   T* xl = XTlo != nullptr ? XTlo + (size_t)mat * xt_mat_stride : nullptr;
-  const bool vec = std::is_same<T, bf16_t>::value && (M & 7) == 0;
-  for (int idx = tid; idx < ellp * R8; idx += 256) {
-    const int j = idx / R8, m8 = idx - (idx / R8) * R8;
-    const int mb = m0 + 8 * m8;
-    float v[8];
+  const bool vec4 = (M & 3) == 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = Ys[(8 * m8 + e) * S + j];
-    if (vec && mb + 8 <= M) {
-      uint32_t hw[4], lw[4];
+  for (int c = 0; c < NT; ++c) {
+    v4f acc[kApplyRT];
+#pragma unroll
+    for (int rt = 0; rt < kApplyRT; ++rt) acc[rt] = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int kc = 0; kc <= c; ++kc) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hw[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-        const float r0 = v[2 * e] - __uint_as_float(hw[e] << 16);
-        const float r1 = v[2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u);
-        lw[e] = pack_bf16x2(r0, r1);
-      }
-      *reinterpret_cast<uint4*>(xt + (size_t)j * M + mb) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      if (xl != nullptr) *reinterpret_cast<uint4*>(xl + (size_t)j * M + mb) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    } else {
-      for (int e = 0; e < 8; ++e) {
-        if (mb + e >= M) break;
-        const T hi = from_f32<T>(v[e]);
-        xt[(size_t)j * M + mb + e] = hi;
-        if (xl != nullptr) xl[(size_t)j * M + mb + e] = from_f32<T>(v[e] - to_f32<T>(hi));
+        const float b = Rs[(16 * kc + 4 * lg + e) * RS + 16 * c + l16];
+#pragma unroll
+        for (int rt = 0; rt < kApplyRT; ++rt) {
+          const float a = e == 0 ? y[rt][kc].x : e == 1 ? y[rt][kc].y : e == 2 ? y[rt][kc].z : y[rt][kc].w;
+          acc[rt] = mfma_f32(a, b, acc[rt]);
+        }
       }
     }
+    // lane holds Q[r + t][j], r = base + 16 rt + 4 lg, t = 0..3, j = 16 c + l16
+    const int j = 16 * c + l16;
+#pragma unroll
+    for (int rt = 0; rt < kApplyRT; ++rt) {
+      const int r = base + 16 * rt + 4 * lg;
+      if (Qm != nullptr) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (r + t < M) Qm[(size_t)(r + t) * ellp + j] = acc[rt][t];
+      }
+      if (xt == nullptr) continue;
+      T* dst = xt + (size_t)j * M + r;
+      T* dlo = xl != nullptr ? xl + (size_t)j * M + r : nullptr;
+      if constexpr (std::is_same<T, bf16_t>::value) {
+        if (vec4 && r + 4 <= M) {
+          const uint32_t h0 = pack_bf16x2(acc[rt][0], acc[rt][1]), h1 = pack_bf16x2(acc[rt][2], acc[rt][3]);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(h0, h1);
+          if (dlo != nullptr)
+            *reinterpret_cast<uint2*>(dlo) =
+                make_uint2(pack_bf16x2(acc[rt][0] - __uint_as_float(h0 << 16), acc[rt][1] - __uint_as_float(h0 & 0xffff0000u)),
+                           pack_bf16x2(acc[rt][2] - __uint_as_float(h1 << 16), acc[rt][3] - __uint_as_float(h1 & 0xffff0000u)));
+          continue;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (r + t >= M) break;
+        const T hi = from_f32<T>(acc[rt][t]);
+        dst[t] = hi;
+        if (dlo != nullptr) dlo[t] = from_f32<T>(acc[rt][t] - to_f32<T>(hi));
+      }
+    }
+  }
+}
+
+template <class T>
+using ApplyFn = void (*)(const float*, float*, int, const float*, T*, T*, size_t, int);
+template <class T>
+static ApplyFn<T> apply_kernel(int nt) {
+  switch (nt) {
+    case 1: return &k_apply<T, 1>;
+    case 2: return &k_apply<T, 2>;
+    case 3: return &k_apply<T, 3>;
+    case 4: return &k_apply<T, 4>;
+    case 5: return &k_apply<T, 5>;
+    case 6: return &k_apply<T, 6>;
+    case 7: return &k_apply<T, 7>;
+    case 8: return &k_apply<T, 8>;
+    case 9: return &k_apply<T, 9>;
+    default: return nullptr;
   }
 }
 
@@ -833,18 +861,23 @@ __host__ __device__ inline size_t jacobi_lds_floats(int ellp, int jsplit) {
   return (size_t)(ellp + jacobi_rows(ellp, jsplit)) * (ellp + 1) + 2 * (size_t)ellp;
 }
 
+// NT = ellp / 16 and JT = jacobi_rows / 16 are compile-time, so that every LDS read
+// of a step (both columns of Mj and of this workgroup's rows of J) is issued at once
+// and the columns stay in registers from the dot products to the rotation: one LDS
+// round trip per step instead of one per 16-row slice.
+template <int NT, int JT>
 __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, int ell, int ellp,
                                                  int jsplit, float* __restrict__ PS,
                                                  float* __restrict__ Sv, float* __restrict__ sig) {
   extern __shared__ __align__(16) float sh[];
-  const int S = ellp + 1;
+  constexpr int S = 16 * NT + 1;           // ellp + 1: row offsets become immediates
   const int E = (ell + 1) & ~1;            // even number of columns for the tournament
   const int mat = blockIdx.x / jsplit, js = blockIdx.x - (blockIdx.x / jsplit) * jsplit;
-  const int JR = jacobi_rows(ellp, jsplit);
+  const int JR = 16 * JT;                  // rows of J per workgroup
   const int j0 = js * JR;                  // first row of J held here
   const int jn = min(JR, ellp - j0);       // rows held (a multiple of 16, >= 16)
   float* Mj = sh;                          // [ellp][S]  (row i, column j)
-  float* J = Mj + ellp * S;                // [JR][S]    rows j0 .. j0 + jn - 1 of J
+  float* J = Mj + ellp * S;                // [JR][S]    rows j0 .. j0 + JR - 1 of J
   float* nrm = J + JR * S;                 // [ellp]
   int* perm = reinterpret_cast<int*>(nrm + ellp);  // [ellp]
   __shared__ unsigned int rotated;
@@ -855,7 +888,7 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
     const int i = idx / ellp, j = idx % ellp;
     Mj[i * S + j] = (i < ell && j < ell) ? R[j * ellp + i] : 0.f;   // transpose
   }
-  for (int idx = tid; idx < jn * ellp; idx += nthr) {
+  for (int idx = tid; idx < JR * ellp; idx += nthr) {   // rows past jn: zero, never stored
     const int i = idx / ellp, j = idx % ellp;
     J[i * S + j] = j0 + i == j ? 1.f : 0.f;
   }
@@ -865,27 +898,41 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
     __syncthreads();
     for (int step = 0; step < E - 1; ++step) {
       for (int pr = slot; pr < E / 2; pr += nslot) {
-        const int x0 = pr, x1 = E - 1 - pr;
-        int p = x0 == 0 ? 0 : 1 + (x0 - 1 + step) % (E - 1);
-        int qq = 1 + (x1 - 1 + step) % (E - 1);
+        // round-robin pairing: slot pr meets positions pr and E-1-pr; every position but
+        // 0 moves one place per step (indices below 2(E-1): one conditional subtraction)
+        int p = 0;
+        if (pr != 0) { p = pr - 1 + step; p = 1 + (p >= E - 1 ? p - (E - 1) : p); }
+        int qq = E - 2 - pr + step;
+        qq = 1 + (qq >= E - 1 ? qq - (E - 1) : qq);
         if (p > qq) { const int t = p; p = qq; qq = t; }
         if (qq >= ell) continue;           // uniform over the 16-lane group
-        // rows ell..ellp-1 of Mj are zero: the loops run over ellp rows, unrolled with a
-        // wavefront-uniform bound so that the LDS reads of a column issue together
+        // rows ell..ellp-1 of Mj are zero; all reads of the step are issued together
+        float x[NT], y[NT], u[JT], v[JT];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+          x[k] = Mj[(l16 + 16 * k) * S + p];
+          y[k] = Mj[(l16 + 16 * k) * S + qq];
+        }
+#pragma unroll
+        for (int k = 0; k < JT; ++k) {
+          u[k] = J[(l16 + 16 * k) * S + p];
+          v[k] = J[(l16 + 16 * k) * S + qq];
+        }
         float a = 0.f, bsum = 0.f, g = 0.f;
 #pragma unroll
-        for (int k = 0; k < kMaxEll / 16; ++k) {
-          if (16 * k >= ellp) break;
-          const int i = l16 + 16 * k;
-          const float x = Mj[i * S + p], y = Mj[i * S + qq];
-          a = fmaf(x, x, a);
-          bsum = fmaf(y, y, bsum);
-          g = fmaf(x, y, g);
+        for (int k = 0; k < NT; ++k) {
+          a = fmaf(x[k], x[k], a);
+          bsum = fmaf(y[k], y[k], bsum);
+          g = fmaf(x[k], y[k], g);
         }
         a = group_sum(a, 16);
         bsum = group_sum(bsum, 16);
         g = group_sum(g, 16);
-        if (g == 0.f || fabsf(g) <= 3e-6f * sqrtf(a * bsum)) continue;
+        // J's rows stay requested with the columns (not sunk below the test)
+#pragma unroll
+        for (int k = 0; k < JT; ++k) asm volatile("" ::"v"(u[k]), "v"(v[k]));
+        // |g| <= 3e-6 sqrt(a b), squared (column norms are far from the fp32 range ends)
+        if (g * g <= 9e-12f * (a * bsum)) continue;
         if (l16 == 0) rotated = 1u;
         // rotation angle from the hardware reciprocal and reciprocal square root (about
         // 1 ulp each): any rotation close to the exact one is orthogonal to within
@@ -894,20 +941,14 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
         const float t = copysignf(__builtin_amdgcn_rcpf(fabsf(zeta) + __builtin_amdgcn_sqrtf(fmaf(zeta, zeta, 1.f))), zeta);
         const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), s = c * t;
 #pragma unroll
-        for (int k = 0; k < kMaxEll / 16; ++k) {
-          if (16 * k >= ellp) break;
-          const int i = l16 + 16 * k;
-          const float x = Mj[i * S + p], y = Mj[i * S + qq];
-          Mj[i * S + p] = c * x - s * y;
-          Mj[i * S + qq] = s * x + c * y;
+        for (int k = 0; k < NT; ++k) {
+          Mj[(l16 + 16 * k) * S + p] = c * x[k] - s * y[k];
+          Mj[(l16 + 16 * k) * S + qq] = s * x[k] + c * y[k];
         }
 #pragma unroll
-        for (int k = 0; k < kMaxEll / 16; ++k) {
-          if (16 * k >= jn) break;
-          const int i = l16 + 16 * k;
-          const float u = J[i * S + p], v = J[i * S + qq];
-          J[i * S + p] = c * u - s * v;
-          J[i * S + qq] = s * u + c * v;
+        for (int k = 0; k < JT; ++k) {
+          J[(l16 + 16 * k) * S + p] = c * u[k] - s * v[k];
+          J[(l16 + 16 * k) * S + qq] = s * u[k] + c * v[k];
         }
       }
       __syncthreads();
@@ -941,6 +982,26 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
     const int i = idx / ellp, c = idx % ellp;
     Sm[(size_t)(j0 + i) * ellp + c] = J[i * S + perm[c]];
   }
+}
+
+using JacobiFn = void (*)(const float*, int, int, int, float*, float*, float*);
+// The instances in use: J whole (JT = NT) up to 128 columns, or split in two at 144.
+static JacobiFn jacobi_kernel(int nt, int jt) {
+  if (nt == jt) {
+    switch (nt) {
+      case 1: return &k_jacobi<1, 1>;
+      case 2: return &k_jacobi<2, 2>;
+      case 3: return &k_jacobi<3, 3>;
+      case 4: return &k_jacobi<4, 4>;
+      case 5: return &k_jacobi<5, 5>;
+      case 6: return &k_jacobi<6, 6>;
+      case 7: return &k_jacobi<7, 7>;
+      case 8: return &k_jacobi<8, 8>;
+      default: return nullptr;
+    }
+  }
+  if (nt == 9 && jt == 5) return &k_jacobi<9, 5>;
+  return nullptr;
 }
 
 // ================================================================ assembly
@@ -1187,11 +1248,12 @@ static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void*
                        int passes, float* Qlast, hipStream_t st) {
   const Dims& dm = c->dm;
   const int nmat = 2 * dm.B, ellp = ws.ellp;
-  const size_t lds_gram = (size_t)ellp * (ellp + 1) * sizeof(float);
+  const size_t lds_gram = gram_lds_floats() * sizeof(float);
   const size_t lds_chol = chol_lds_floats(ellp) * sizeof(float);
-  const int arows = apply_rows(ellp);
-  const size_t lds_apply = (size_t)(arows * (ellp + 1) + ellp * ellp) * sizeof(float);
-  const int tiles_m = (M + arows - 1) / arows;
+  const size_t lds_apply = (size_t)ellp * (ellp + 4) * sizeof(float);
+  const int tiles_m = (M + kApplyRows - 1) / kApplyRows;
+  const ApplyFn<T> apply_fn = apply_kernel<T>(ellp / 16);
+  if (apply_fn == nullptr) return hipErrorInvalidValue;
   int rows, nsplit;
   gram_split(M, nmat, rows, nsplit);
   for (int pass = 0; pass < passes; ++pass) {
@@ -1215,10 +1277,9 @@ static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void*
     }
     hipLaunchKernelGGL(k_chol, dim3(nmat), dim3(kCholThreads), lds_chol, st, Gsum, 1, dm.ell, ellp,
                        ws.Rinv, pass == 0 ? nullptr : Racc, Racc);
-    hipLaunchKernelGGL(k_apply<T>, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, last ? Qlast : ws.Y, M,
-                       ellp, ws.Rinv,
-                       static_cast<T*>(last ? XT : nullptr), static_cast<T*>(last ? XTlo : nullptr),
-                       (size_t)ellp * ws.M, tiles_m, arows);
+    hipLaunchKernelGGL(apply_fn, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, last ? Qlast : ws.Y, M,
+                       ws.Rinv, static_cast<T*>(last ? XT : nullptr), static_cast<T*>(last ? XTlo : nullptr),
+                       (size_t)ellp * ws.M, tiles_m);
   }
   return hipGetLastError();
 }
@@ -1322,18 +1383,20 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   // when they do not fit one workgroup's LDS beside the matrix itself
   const int jsplit = jacobi_lds_floats(ellp, 1) * sizeof(float) <= 160 * 1024 ? 1 : 2;
   const size_t lds_jac = jacobi_lds_floats(ellp, jsplit) * sizeof(float);
-  const size_t lds_apply = (size_t)(apply_rows(ellp) * (ellp + 1) + ellp * ellp) * sizeof(float);
+  const JacobiFn jac_fn = jacobi_kernel(ellp / 16, jacobi_rows(ellp, jsplit) / 16);
+  if (jac_fn == nullptr) return fail_stage(hipErrorInvalidValue, "core SVD shape");
+  const size_t lds_apply = (size_t)ellp * (ellp + 4) * sizeof(float);
+  const ApplyFn<T> apply_fn = apply_kernel<T>(ellp / 16);
+  if (apply_fn == nullptr) return fail_stage(hipErrorInvalidValue, "orthonormalisation shape");
   const bool u4 = dm.storage == AP_INT4;
   const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP + 32 * (16 * dm.NP + 1) +
                                 (u4 ? 16 * dm.NP : 0)) * sizeof(float);
   const size_t lds_b = (size_t)(64 * (ellp + 1) + ellp * dm.r_pad) * sizeof(float);
   const struct { const void* fn; size_t bytes; const char* name; } lds_req[] = {
-      {ellp / 16 == 9 ? reinterpret_cast<const void*>(&k_gram<9>) : reinterpret_cast<const void*>(&k_gram<8>),
-       (size_t)ellp * (ellp + 1) * sizeof(float), "LDS size of k_gram"},
       {reinterpret_cast<const void*>(&k_chol), lds_chol, "LDS size of k_chol"},
       {reinterpret_cast<const void*>(&k_assemble_b<T>), lds_b, "LDS size of k_assemble_b"},
-      {reinterpret_cast<const void*>(&k_jacobi), lds_jac, "LDS size of k_jacobi"},
-      {reinterpret_cast<const void*>(&k_apply<T>), lds_apply, "LDS size of k_apply"},
+      {reinterpret_cast<const void*>(jac_fn), lds_jac, "LDS size of k_jacobi"},
+      {reinterpret_cast<const void*>(apply_fn), lds_apply, "LDS size of k_apply"},
       {u4 ? reinterpret_cast<const void*>(&k_assemble_u4) : reinterpret_cast<const void*>(&k_assemble_u<T>),
        lds_u, "LDS size of k_assemble_u"},
   };
@@ -1365,7 +1428,7 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   if (e == hipSuccess) e = orth<T>(c, ws, dm.W, nullptr, nullptr, ws.Racc, 2, ws.Qc, st);
   if (e != hipSuccess) return fail_stage(e, "projection C^T = A^T Q");
   const int jac_threads = std::min(1024, std::max(64, (16 * ((dm.ell + 1) / 2) + 63) / 64 * 64));
-  hipLaunchKernelGGL(k_jacobi, dim3(nmat * jsplit), dim3(jac_threads), lds_jac, st, ws.Racc, dm.ell, ellp,
+  hipLaunchKernelGGL(jac_fn, dim3(nmat * jsplit), dim3(jac_threads), lds_jac, st, ws.Racc, dm.ell, ellp,
                      jsplit, ws.PS, ws.Sv, ws.sig);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_stage(e, "core SVD");
