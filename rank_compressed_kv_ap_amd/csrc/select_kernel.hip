@@ -722,41 +722,33 @@ __device__ __forceinline__ void select_body(
   }
 
   if (select) {
+    // every score of this wavefront is a real token of a present head (wave-uniform):
+    // the range, histogram and mark loops then run without per-score validity tests
+    const uint32_t vfull = KPL >= 32 ? 0xFFFFFFFFu : ((1u << (KPL & 31)) - 1u);
+    const bool all_ok = __ballot(vm != vfull) == 0ull;
     // ---- C. per-head range, linear bins, histogram, boundary bin
     {
-      uint32_t kmax = 0u, kmin = 0u;   // kmin holds ~key; absent scores add nothing
-      if constexpr (FUSED) {
-        // branch-free, on the float scores (absent scores replaced by -inf / +inf), with
-        // one conversion to keys per lane
-        float fmx = -INFINITY, fmn = INFINITY;
+      // range on the float scores (fmax / fmin ignore NaN), one conversion to keys per
+      // lane; absent scores replaced by -inf / +inf
+      float fmx = -INFINITY, fmn = INFINITY;
+      if (all_ok) {
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          fmx = fmaxf(fmx, sc[i]);
+          fmn = fminf(fmn, sc[i]);
+        }
+      } else {
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
           const bool ok = (vm >> i) & 1u;
           fmx = fmaxf(fmx, ok ? sc[i] : -INFINITY);
           fmn = fminf(fmn, ok ? sc[i] : INFINITY);
         }
-        fmx = head_fmax<HG>(fmx);
-        fmn = head_fmin<HG>(fmn);
-        kmax = fmx == -INFINITY ? 0u : score_key(fmx);
-        kmin = fmn == INFINITY ? 0u : ~score_key(fmn);
-      } else {
-#pragma unroll
-        for (int a = 0; a < NACC; ++a) {
-          const int n0 = tok(a);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            if (n0 + t < N) {
-              const uint32_t k = score_key(sc[4 * a + t]);
-              kmax = max(kmax, k);
-              kmin = max(kmin, ~k);
-            }
-          }
-        }
       }
-      if constexpr (!FUSED) {
-        kmax = head_max<HG>(kmax);
-        kmin = head_max<HG>(kmin);
-      }
+      fmx = head_fmax<HG>(fmx);
+      fmn = head_fmin<HG>(fmn);
+      const uint32_t kmax = fmx == -INFINITY ? 0u : score_key(fmx);
+      const uint32_t kmin = fmn == INFINITY ? 0u : ~score_key(fmn);   // kmin holds ~key
       if (lg == 0 && c16 < HG && my_on) {
         atomicMax(&rng[2 * my_h], kmax);
         atomicMax(&rng[2 * my_h + 1], kmin);
@@ -773,7 +765,7 @@ __device__ __forceinline__ void select_body(
       mul_h = (range > 1e-30f && range < 3.0e38f) ? static_cast<float>(kSelBins - 1) / range : 0.f;
     }
     // bin(s) = s * mul - lo * mul, clamped in float first (one fma and one med3): a
-    // monotone map, and any input (NaN included) gives a bin in [0, kSelBins)
+    // monotone map, and any input (NaN included: bin 0) gives a bin in [0, kSelBins)
     const float off_h = -lo_h * mul_h;
     auto bin_of = [&](float s) {
       return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(fmaf(s, mul_h, off_h), 0.f, static_cast<float>(kSelBins - 1)));
@@ -782,8 +774,13 @@ __device__ __forceinline__ void select_body(
       // branch-free: tokens past N (and absent heads) add 0, so the LDS atomics issue
       // back to back; any float maps to a bin inside the head's range
       uint32_t* hh = hist + my_h * HS;
+      if (all_ok) {
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) atomicAdd(&hh[bin_of(sc[i])], (vm >> i) & 1u);
+        for (int i = 0; i < KPL; ++i) atomicAdd(&hh[bin_of(sc[i])], 1u);
+      } else {
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) atomicAdd(&hh[bin_of(sc[i])], (vm >> i) & 1u);
+      }
     }
     lds_barrier();
     if (wave < nh) {
@@ -810,32 +807,49 @@ __device__ __forceinline__ void select_body(
     const int bstar_h = my_on ? st[my_h].bstar : 0;
     const int mode_h = my_on ? st[my_h].mode : kNone;
     {
+      // Bins compared through x = fma(s, mul, off), the value bin_of clamps and
+      // truncates: for an integer B in [1, kSelBins - 1], bin_of(s) >= B exactly when
+      // x >= B (NaN: bin 0, and x >= B is false).  B <= 0 takes every score; B >=
+      // kSelBins none (a NaN threshold compares false).
       const int bwhole = mode_h == kWholeBin ? bstar_h : bstar_h + 1;   // lowest bin taken whole
+      const bool take_all = bwhole <= 0;
+      const float fwhole = bwhole >= kSelBins ? __builtin_nanf("") : static_cast<float>(bwhole);
+      // a partly taken boundary bin (mode kRank, bwhole = bstar + 1): bin(s) == bstar
+      // exactly when s is not taken and (bstar == 0 or x >= bstar)
+      const bool rank_h = mode_h == kRank;
+      const bool b0 = bstar_h == 0;
+      const float fbstar = static_cast<float>(bstar_h);
       uint32_t cbits = 0;   // scores in a partly taken boundary bin (bit 4a+t)
+      auto mark = [&](auto RANK) {
 #pragma unroll
-      for (int a = 0; a < NACC; ++a) {
-        const int n0 = tok(a);
-        uint32_t nib = 0;
+        for (int a = 0; a < NACC; ++a) {
+          const int n0 = tok(a);
+          uint32_t nib = 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int bn = static_cast<int>(bin_of(sc[4 * a + t]));
-          const bool ok = (vm >> (4 * a + t)) & 1u;
-          nib |= (ok && bn >= bwhole) ? (1u << t) : 0u;
-          cbits |= (ok && mode_h == kRank && bn == bstar_h) ? (1u << (4 * a + t)) : 0u;
+          for (int t = 0; t < 4; ++t) {
+            const float x = fmaf(sc[4 * a + t], mul_h, off_h);
+            bool take = take_all || x >= fwhole;
+            const bool ok = all_ok || ((vm >> (4 * a + t)) & 1u);
+            nib |= (ok && take) ? (1u << t) : 0u;
+            if constexpr (decltype(RANK)::value)
+              cbits |= (ok && rank_h && !take && (b0 || x >= fbstar)) ? (1u << (4 * a + t)) : 0u;
+          }
+          // The eight lanes holding the tokens of one (head, block) word are the two tile
+          // halves (lane%16 apart by HG) in each of the four 16-lane rows: OR them together
+          // (a rotation by HG inside the row leaves the pair in the upper half's lane, then
+          // the row swaps), and the upper half's lane of row 0 stores the word.
+          uint32_t wv = nib << (n0 & 31);
+          wv |= dpp_ror<HG>(wv);
+          const auto r1 = __builtin_amdgcn_permlane16_swap(wv, wv, false, false);
+          wv = r1[0] | r1[1];
+          const auto r2 = __builtin_amdgcn_permlane32_swap(wv, wv, false, false);
+          wv = r2[0] | r2[1];
+          const int blk = n0 >> 5;
+          if (my_j == 1 && lg == 0 && my_on && blk < nblk) selw[my_h * nblk + blk] = wv;
         }
-        // The eight lanes holding the tokens of one (head, block) word are the two tile
-        // halves (lane%16 apart by HG) in each of the four 16-lane rows: OR them together
-        // (a rotation by HG inside the row leaves the pair in the upper half's lane, then
-        // the row swaps), and the upper half's lane of row 0 stores the word.
-        uint32_t wv = nib << (n0 & 31);
-        wv |= dpp_ror<HG>(wv);
-        const auto r1 = __builtin_amdgcn_permlane16_swap(wv, wv, false, false);
-        wv = r1[0] | r1[1];
-        const auto r2 = __builtin_amdgcn_permlane32_swap(wv, wv, false, false);
-        wv = r2[0] | r2[1];
-        const int blk = n0 >> 5;
-        if (my_j == 1 && lg == 0 && my_on && blk < nblk) selw[my_h * nblk + blk] = wv;
-      }
+      };
+      if (any_rank) mark(std::true_type{});
+      else mark(std::false_type{});
       if (cbits) {
 #pragma unroll
         for (int a = 0; a < NACC; ++a) {
