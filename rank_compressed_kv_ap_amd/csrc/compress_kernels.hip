@@ -1068,19 +1068,28 @@ __global__ __launch_bounds__(256) void k_assemble_u(const float* __restrict__ Qn
     }
   }
   __syncthreads();
+  // one thread per (panel, tile lane): the lane's 8 elements [half][e] are consecutive in
+  // the tile, so they leave in one 16-byte store (two for fp32)
   T* base = Ukv + (vl ? (size_t)NP * kBlockElems : 0);
-  for (int idx = threadIdx.x; idx < NP * kBlockElems; idx += blockDim.x) {
-    const int p = idx / kBlockElems, within = idx % kBlockElems;
-    const int e = within & 3, half = (within >> 2) & 1, lane = within >> 3;
-    int rr, col;
-    if (!vl) {
-      rr = 16 * half + (lane & 15);
-      col = 16 * p + 4 * (lane >> 4) + e;
+  for (int idx = threadIdx.x; idx < NP * 64; idx += blockDim.x) {
+    const int p = idx >> 6, lane = idx & 63;
+    float v[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = vl ? 16 * half + 4 * (lane >> 4) + e : 16 * half + (lane & 15);
+        const int col = vl ? 16 * p + (lane & 15) : 16 * p + 4 * (lane >> 4) + e;
+        v[4 * half + e] = Ub[rr * ld + col];
+      }
+    T* dst = base + tile_base(b, p, t, NP, nblk) + 8 * lane;
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
     } else {
-      rr = 16 * half + 4 * (lane >> 4) + e;
-      col = 16 * p + (lane & 15);
+      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
     }
-    base[tile_base(b, p, t, NP, nblk) + within] = from_f32<T>(Ub[rr * ld + col]);
   }
 }
 
