@@ -33,7 +33,6 @@
 
 namespace ap {
 
-constexpr int kGemmThreads = 256;
 constexpr int kMaxEll = 144;          // largest ell: 9 column tiles of 16; the Cholesky and the
                                       // core SVD keep one ell x ell matrix per workgroup in LDS
 
@@ -114,34 +113,39 @@ __global__ __launch_bounds__(256) void k_omega_copy(const float* __restrict__ om
 }
 
 // ================================================================ tall-skinny GEMMs
-// Output Y[mat][m][j] (fp32, row stride ellp) for m in a 128-row tile:
+// Output Y[mat][m][j] (fp32, row stride ellp) for m in a BM-row tile (BM = 128 or 256,
+// 32 rows per wavefront):
 //   TRANS = false: Y = A X,   A [M][K] rows m, X^T [ellp][K]        (M = N, K = W)
 //   TRANS = true : Y = A^T X, A [K][M] columns m, X^T [ellp][K]     (M = W, K = N)
-// A 64-wide k slice of A is staged in LDS as [128 m][64 k] (transposed on the way in
+// A 64-wide k slice of A is staged in LDS as [BM m][64 k] (transposed on the way in
 // for TRANS), so both MFMA operands read 8 consecutive k values per lane.  The next
 // slice of A and of X is loaded into registers while the current one is multiplied
 // (software pipelining: the loads of slice s+1 are in flight during the MFMAs of s).
-constexpr int kGemmBM = 128, kGemmBK = 64, kGemmLdsStride = kGemmBK + 8;  // padded bf16 row
+constexpr int kGemmBK = 64, kGemmLdsStride = kGemmBK + 8;  // padded bf16 row
 
 // VEC (W and K multiples of 8, K >= 8): every load of a slice is issued unconditionally,
 // clamped in bounds, so the compiler tracks the slice in flight exactly and waits only
 // for the slice being staged.  Past the edge of K the X^T values are zeroed, which
 // cancels the clamped (finite) A values they meet; A values past M only reach output
 // rows that are not stored.  Otherwise per-element fallbacks for unaligned rows.
-template <class T, bool TRANS, int NT, bool SPLIT, bool VEC>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kmat,
+template <class T, bool TRANS, int NT, bool SPLIT, bool VEC, int BM>
+__global__ __launch_bounds__(2 * BM) void k_gemm(const T* __restrict__ Kmat,
                                                         const T* __restrict__ Vmat,
                                                         const T* __restrict__ XT,
                                                         const T* __restrict__ XTlo, float* __restrict__ Y,
                                                         int N, int W, int ellp, size_t x_mat_stride,
                                                         int tiles_m) {
   static_assert(std::is_same<T, bf16_t>::value, "MFMA GEMM path is bf16");
+  constexpr int GT = 2 * BM;                         // threads: 32 rows per wavefront
   constexpr int XR = NT * 16;                        // rows of X^T (= ellp)
   constexpr int CPR = kGemmBK / 8;                   // 16-byte chunks per k slice row
-  constexpr int XU = (XR * CPR + kGemmThreads - 1) / kGemmThreads;   // 16-byte X loads per thread
-  constexpr int AU = kGemmBM * CPR / kGemmThreads;   // 16-byte A loads per thread
-  constexpr int RPP = kGemmThreads / CPR;            // A rows per pass (not TRANS)
-  __shared__ __align__(16) bf16_t As[kGemmBM * kGemmLdsStride];
+  constexpr int XU = (XR * CPR + GT - 1) / GT;   // 16-byte X loads per thread
+  constexpr int AU = BM * CPR / GT;   // 16-byte A loads per thread
+  constexpr int RPP = GT / CPR;            // A rows per pass (not TRANS)
+  constexpr int MG = BM / 8;                    // 8-wide m groups of a k row (TRANS)
+  static_assert(BM == 32 * (GT / 64) && AU * (GT / MG) == kGemmBK,
+                "32 rows per wavefront; TRANS: AU k rows per thread cover the slice");
+  __shared__ __align__(16) bf16_t As[BM * kGemmLdsStride];
   __shared__ __align__(16) bf16_t Xs[(SPLIT ? 2 : 1) * XR * kGemmLdsStride];
   // workgroups are dealt to the 8 XCDs in turn: when the matrices come in eights, the
   // row tiles of one matrix all land on one XCD, whose L2 then holds its X^T slices
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
     mat = blockIdx.x / tiles_m;
     tile = blockIdx.x % tiles_m;
   }
-  const int m0 = tile * kGemmBM;
+  const int m0 = tile * BM;
   const int b = mat >> 1;
   const T* A = ((mat & 1) ? Vmat : Kmat) + (size_t)b * N * W;
   const int M = TRANS ? W : N;
@@ -199,16 +203,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
           sl.a[h] = t;
         }
       } else {
-        // k rows AU (tid >> 4) + h, m = m0 + 8 (tid & 15) .. +7
+        // k rows AU (tid / MG) + h, m = m0 + 8 (tid % MG) .. +7
 #pragma unroll
         for (int h = 0; h < AU; ++h) {
-          const int gk = k0 + AU * (tid >> 4) + h, gm = m0 + (tid & 15) * 8;
+          const int gk = k0 + AU * (tid / MG) + h, gm = m0 + (tid % MG) * 8;
           sl.a[h] = *reinterpret_cast<const uint4*>(A + (size_t)min(gk, K - 1) * W + min(gm, M - 8));
         }
       }
 #pragma unroll
       for (int u = 0; u < XU; ++u) {
-        const int idx = min(tid + u * kGemmThreads, XR * CPR - 1);
+        const int idx = min(tid + u * GT, XR * CPR - 1);
         const int j = idx / CPR, gk = k0 + 8 * (idx % CPR);
         const size_t off = (size_t)j * K + min(gk, K - 8);
         const uint4 t = *reinterpret_cast<const uint4*>(X + off);
@@ -234,10 +238,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
         }
       }
     } else {
-      // k rows AU (tid >> 4) + h, m = m0 + 8 (tid & 15) .. +7 (transposed into LDS later)
+      // k rows AU (tid / MG) + h, m = m0 + 8 (tid % MG) .. +7 (transposed into LDS later)
 #pragma unroll
       for (int h = 0; h < AU; ++h) {
-        const int kk = AU * (tid >> 4) + h, mm = (tid & 15) * 8;
+        const int kk = AU * (tid / MG) + h, mm = (tid % MG) * 8;
         const int gk = k0 + kk, gm = m0 + mm;
         if (avec && gk < K && gm + 8 <= M) {
           sl.a[h] = *reinterpret_cast<const uint4*>(A + (size_t)gk * W + gm);
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
     // X^T rows j = idx / 8, k = k0 + 8 (idx % 8) .. +7 (zero past K)
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-      const int idx = min(tid + u * kGemmThreads, XR * CPR - 1);
+      const int idx = min(tid + u * GT, XR * CPR - 1);
       const int j = idx / CPR, gk = k0 + 8 * (idx % CPR);
       const size_t off = (size_t)j * K + gk;
       if (xvec && gk + 8 <= K) {
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
       // groups of 4 k rows x 8 m columns in registers -> 8 columns of 4 consecutive k (8 bytes)
 #pragma unroll
       for (int q = 0; q < AU / 4; ++q) {
-        const int kk = AU * (tid >> 4) + 4 * q, mm = (tid & 15) * 8;
+        const int kk = AU * (tid / MG) + 4 * q, mm = (tid % MG) * 8;
         const uint4 a0 = sl.a[4 * q], a1 = sl.a[4 * q + 1], a2 = sl.a[4 * q + 2], a3 = sl.a[4 * q + 3];
         const uint32_t r0[4] = {a0.x, a0.y, a0.z, a0.w};
         const uint32_t r1[4] = {a1.x, a1.y, a1.z, a1.w};
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const T* __restrict__ Kma
     }
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-      const int idx = min(tid + u * kGemmThreads, XR * CPR - 1);
+      const int idx = min(tid + u * GT, XR * CPR - 1);
       const int o = (idx / CPR) * kGemmLdsStride + 8 * (idx % CPR);
       *reinterpret_cast<uint4*>(&Xs[o]) = sl.x[u];
       if constexpr (SPLIT) *reinterpret_cast<uint4*>(&Xs[XR * kGemmLdsStride + o]) = sl.xl[u];
@@ -1198,19 +1202,25 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
   const int ellp = (dm.ell + 15) / 16 * 16;
   const int M = trans ? dm.W : dm.N;
   if constexpr (std::is_same<T, bf16_t>::value) {
-    const int tiles_m = (M + kGemmBM - 1) / kGemmBM;
-    const dim3 grid(nmat * tiles_m);
     const int K = trans ? dm.N : dm.W;
     const bool vec = dm.W % 8 == 0 && K % 8 == 0 && K >= 8;
-#define AP_GEMM_LAUNCH_V(TR, NTV, SP, VC)                                                               \
-  hipLaunchKernelGGL((k_gemm<bf16_t, TR, NTV, SP, VC>), grid, dim3(kGemmThreads), 0, st,               \
-                     static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),                     \
-                     static_cast<const bf16_t*>(XT), static_cast<const bf16_t*>(XTlo), Y, dm.N, dm.W, \
-                     ellp, x_stride, tiles_m)
+    // 256-row tiles (8 wavefronts) for the plain transposed product, where the larger
+    // tile halves the X^T re-reads per byte of A (350 -> 283 us per pass on the batch-32
+    // layer); 128-row tiles elsewhere (the two-term product needs the registers, and the
+    // untransposed one loses more to the last partial round of tiles than it gains)
+#define AP_GEMM_LAUNCH_V(TR, NTV, SP, VC, BMV)                                                          \
+  do {                                                                                                  \
+    const int tiles_m = (M + (BMV) - 1) / (BMV);                                                        \
+    hipLaunchKernelGGL((k_gemm<bf16_t, TR, NTV, SP, VC, BMV>), dim3(nmat * tiles_m), dim3(2 * (BMV)), 0, \
+                       st, static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),                \
+                       static_cast<const bf16_t*>(XT), static_cast<const bf16_t*>(XTlo), Y, dm.N, dm.W, \
+                       ellp, x_stride, tiles_m);                                                        \
+  } while (0)
 #define AP_GEMM_LAUNCH(TR, NTV, SP)                                                                     \
   do {                                                                                                  \
-    if (vec) AP_GEMM_LAUNCH_V(TR, NTV, SP, true);                                                       \
-    else AP_GEMM_LAUNCH_V(TR, NTV, SP, false);                                                          \
+    constexpr int kBM = (TR) && !(SP) ? 256 : 128;                                                      \
+    if (vec) AP_GEMM_LAUNCH_V(TR, NTV, SP, true, kBM);                                                  \
+    else AP_GEMM_LAUNCH_V(TR, NTV, SP, false, kBM);                                                     \
   } while (0)
 #define AP_GEMM_CASE(NTV)                                                                              \
   case NTV:                                                                                            \
