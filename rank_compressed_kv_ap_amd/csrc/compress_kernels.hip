@@ -1204,10 +1204,11 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
   if constexpr (std::is_same<T, bf16_t>::value) {
     const int K = trans ? dm.N : dm.W;
     const bool vec = dm.W % 8 == 0 && K % 8 == 0 && K >= 8;
-    // 256-row tiles (8 wavefronts) for the plain transposed product, where the larger
-    // tile halves the X^T re-reads per byte of A (350 -> 283 us per pass on the batch-32
-    // layer); 128-row tiles elsewhere (the two-term product needs the registers, and the
-    // untransposed one loses more to the last partial round of tiles than it gains)
+    // 256-row tiles (8 wavefronts) halve the X^T re-reads per byte of A: the plain
+    // transposed product (batch-32 layer 350 -> 283 us per pass, batch-256 layer 3.82 ->
+    // 3.15 ms) and the untransposed one when M is a multiple of 256 (batch-256 layer
+    // 3.55 -> 3.38 ms; at M = 2880 its last, mostly empty tile costs more than it saves).
+    // The two-term product keeps 128-row tiles: it needs the registers.
 #define AP_GEMM_LAUNCH_V(TR, NTV, SP, VC, BMV)                                                          \
   do {                                                                                                  \
     const int tiles_m = (M + (BMV) - 1) / (BMV);                                                        \
@@ -1216,11 +1217,16 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
                        static_cast<const bf16_t*>(XT), static_cast<const bf16_t*>(XTlo), Y, dm.N, dm.W, \
                        ellp, x_stride, tiles_m);                                                        \
   } while (0)
+#define AP_GEMM_LAUNCH_B(TR, NTV, SP, BMV)                                                              \
+  do {                                                                                                  \
+    if (vec) AP_GEMM_LAUNCH_V(TR, NTV, SP, true, BMV);                                                  \
+    else AP_GEMM_LAUNCH_V(TR, NTV, SP, false, BMV);                                                     \
+  } while (0)
 #define AP_GEMM_LAUNCH(TR, NTV, SP)                                                                     \
   do {                                                                                                  \
-    constexpr int kBM = (TR) && !(SP) ? 256 : 128;                                                      \
-    if (vec) AP_GEMM_LAUNCH_V(TR, NTV, SP, true, kBM);                                                  \
-    else AP_GEMM_LAUNCH_V(TR, NTV, SP, false, kBM);                                                     \
+    if constexpr (SP) AP_GEMM_LAUNCH_B(TR, NTV, SP, 128);                                               \
+    else if ((TR) || M % 256 == 0) AP_GEMM_LAUNCH_B(TR, NTV, SP, 256);                                  \
+    else AP_GEMM_LAUNCH_B(TR, NTV, SP, 128);                                                            \
   } while (0)
 #define AP_GEMM_CASE(NTV)                                                                              \
   case NTV:                                                                                            \
@@ -1235,6 +1241,7 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
     }
 #undef AP_GEMM_CASE
 #undef AP_GEMM_LAUNCH
+#undef AP_GEMM_LAUNCH_B
 #undef AP_GEMM_LAUNCH_V
   } else {
     if (trans)
