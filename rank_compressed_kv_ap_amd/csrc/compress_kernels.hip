@@ -853,8 +853,9 @@ static ApplyFn<T> apply_kernel(int nt) {
 // step.  Stops when every pair is orthogonal to 3e-6 relative (fp32), or after 40
 // sweeps.
 // The rotations depend on Mj alone, and each row of J is rotated independently of
-// the others.  When Mj and all of J do not fit one workgroup's LDS (ell > 128), the
-// rows of J are split over `jsplit` workgroups per matrix: each runs the same
+// the others.  When Mj and all of J do not fit one workgroup's LDS (ell > 128), or
+// when the matrices are too few to occupy the CUs, the rows of J are split over
+// `jsplit` workgroups per matrix (at most 4): each runs the same
 // rotations on its own copy of Mj (the same arithmetic in the same order, so the
 // copies stay identical) and accumulates its share of J's rows; the first writes
 // P Sigma and the singular values.
@@ -989,23 +990,28 @@ __global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, i
 }
 
 using JacobiFn = void (*)(const float*, int, int, int, float*, float*, float*);
-// The instances in use: J whole (JT = NT) up to 128 columns, or split in two at 144.
-static JacobiFn jacobi_kernel(int nt, int jt) {
-  if (nt == jt) {
-    switch (nt) {
-      case 1: return &k_jacobi<1, 1>;
-      case 2: return &k_jacobi<2, 2>;
-      case 3: return &k_jacobi<3, 3>;
-      case 4: return &k_jacobi<4, 4>;
-      case 5: return &k_jacobi<5, 5>;
-      case 6: return &k_jacobi<6, 6>;
-      case 7: return &k_jacobi<7, 7>;
-      case 8: return &k_jacobi<8, 8>;
-      default: return nullptr;
-    }
-  }
-  if (nt == 9 && jt == 5) return &k_jacobi<9, 5>;
+// Instances: NT = ellp / 16 up to 9, JT = ceil(NT / jsplit) for jsplit = 1 .. 4.
+template <int NT>
+static JacobiFn jacobi_kernel_nt(int jt) {
+  if (jt == NT) return &k_jacobi<NT, NT>;
+  if (jt == (NT + 1) / 2) return &k_jacobi<NT, (NT + 1) / 2>;
+  if (jt == (NT + 2) / 3) return &k_jacobi<NT, (NT + 2) / 3>;
+  if (jt == (NT + 3) / 4) return &k_jacobi<NT, (NT + 3) / 4>;
   return nullptr;
+}
+static JacobiFn jacobi_kernel(int nt, int jt) {
+  switch (nt) {
+    case 1: return jacobi_kernel_nt<1>(jt);
+    case 2: return jacobi_kernel_nt<2>(jt);
+    case 3: return jacobi_kernel_nt<3>(jt);
+    case 4: return jacobi_kernel_nt<4>(jt);
+    case 5: return jacobi_kernel_nt<5>(jt);
+    case 6: return jacobi_kernel_nt<6>(jt);
+    case 7: return jacobi_kernel_nt<7>(jt);
+    case 8: return jacobi_kernel_nt<8>(jt);
+    case 9: return jacobi_kernel_nt<9>(jt);
+    default: return nullptr;
+  }
 }
 
 // ================================================================ assembly
@@ -1407,7 +1413,12 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   const size_t lds_chol = chol_lds_floats(ellp) * sizeof(float);
   // the rows of the core SVD's rotation matrix are split over two workgroups per matrix
   // when they do not fit one workgroup's LDS beside the matrix itself
-  const int jsplit = jacobi_lds_floats(ellp, 1) * sizeof(float) <= 160 * 1024 ? 1 : 2;
+  int jsplit = jacobi_lds_floats(ellp, 1) * sizeof(float) <= 160 * 1024 ? 1 : 2;
+  // while the matrices leave CUs idle, the rotation matrix's rows are spread over more
+  // workgroups (up to 4 per matrix): each step then rotates fewer rows per workgroup
+  while (jsplit < 4 && (size_t)nmat * (jsplit + 1) <= 256 &&
+         jacobi_rows(ellp, jsplit + 1) < jacobi_rows(ellp, jsplit))
+    ++jsplit;
   const size_t lds_jac = jacobi_lds_floats(ellp, jsplit) * sizeof(float);
   const JacobiFn jac_fn = jacobi_kernel(ellp / 16, jacobi_rows(ellp, jsplit) / 16);
   if (jac_fn == nullptr) return fail_stage(hipErrorInvalidValue, "core SVD shape");
