@@ -541,13 +541,17 @@ __device__ __forceinline__ void tile_store(float* M, int r0, int c0, int S, int 
   for (int t = 0; t < 4; ++t) M[(r0 + 4 * lg + t) * S + c0 + l16] = d[t];
 }
 
+// TT = ellp / 16 is a template argument: the index arithmetic of the staging, shift
+// and write-back loops then divides by constants.
+template <int TT>
 __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__ Gpart, int nsplit, int ell,
-                                                       int ellp, float* __restrict__ Rinv,
+                                                       float* __restrict__ Rinv,
                                                        const float* __restrict__ Rprev,
                                                        float* __restrict__ Rout) {
   extern __shared__ __align__(16) float sh[];
-  const int S = ellp + 1;
-  const int T = ellp / 16;
+  constexpr int ellp = 16 * TT;
+  constexpr int S = ellp + 1;
+  constexpr int T = TT;
   float* G = sh;                 // [ellp][S] Gram, then L (lower; diagonal blocks exact)
   float* D = G + ellp * S;       // [T][16][17] inverses of the diagonal blocks of L
   float* Cb = D + T * kTileF;    // [4][ellp][17] per-wavefront block column
@@ -591,10 +595,12 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
   }
   __syncthreads();
   const float eps = 1e-6f * (trace_sh / static_cast<float>(ell > 0 ? ell : 1)) + 1e-30f;
-  for (int idx = tid; idx < ellp * ellp; idx += kCholThreads) {
-    const int i = idx / ellp, j = idx % ellp;
-    if (i >= ell || j >= ell) G[i * S + j] = i == j ? 1.f : 0.f;
-    else if (i == j) G[i * S + j] += eps;
+  // the diagonal only, then the padded rows and columns (none when ell = ellp)
+  for (int i = tid; i < ell; i += kCholThreads) G[i * S + i] += eps;
+  for (int idx = tid; idx < (ellp - ell) * ellp; idx += kCholThreads) {
+    const int i = ell + idx / ellp, j = idx % ellp;   // row i >= ell, and its mirror column
+    G[i * S + j] = i == j ? 1.f : 0.f;
+    G[j * S + i] = i == j ? 1.f : 0.f;
   }
   __syncthreads();
   // ---- blocked Cholesky
@@ -716,6 +722,22 @@ __global__ __launch_bounds__(kCholThreads) void k_chol(const float* __restrict__
       for (int u = 0; u < 4; ++u) Ro[(size_t)(16 * I + 4 * lg + u) * ellp + 16 * Jb + l16] = acc[u];
     }
     wave_sync();
+  }
+}
+
+using CholFn = void (*)(const float*, int, int, float*, const float*, float*);
+static CholFn chol_kernel(int t) {
+  switch (t) {
+    case 1: return &k_chol<1>;
+    case 2: return &k_chol<2>;
+    case 3: return &k_chol<3>;
+    case 4: return &k_chol<4>;
+    case 5: return &k_chol<5>;
+    case 6: return &k_chol<6>;
+    case 7: return &k_chol<7>;
+    case 8: return &k_chol<8>;
+    case 9: return &k_chol<9>;
+    default: return nullptr;
   }
 }
 
@@ -1286,6 +1308,8 @@ static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void*
   const int tiles_m = (M + kApplyRows - 1) / kApplyRows;
   const ApplyFn<T> apply_fn = apply_kernel<T>(ellp / 16);
   if (apply_fn == nullptr) return hipErrorInvalidValue;
+  const CholFn chol_fn = chol_kernel(ellp / 16);
+  if (chol_fn == nullptr) return hipErrorInvalidValue;
   int rows, nsplit;
   gram_split(M, nmat, rows, nsplit);
   for (int pass = 0; pass < passes; ++pass) {
@@ -1307,7 +1331,7 @@ static hipError_t orth(const ap_cache* c, CompressWs& ws, int M, void* XT, void*
                          nsplit, nmat, ellp * ellp, ws.Gsum);
       Gsum = ws.Gsum;
     }
-    hipLaunchKernelGGL(k_chol, dim3(nmat), dim3(kCholThreads), lds_chol, st, Gsum, 1, dm.ell, ellp,
+    hipLaunchKernelGGL(chol_fn, dim3(nmat), dim3(kCholThreads), lds_chol, st, Gsum, 1, dm.ell,
                        ws.Rinv, pass == 0 ? nullptr : Racc, Racc);
     hipLaunchKernelGGL(apply_fn, dim3(nmat * tiles_m), dim3(256), lds_apply, st, ws.Y, last ? Qlast : ws.Y, M,
                        ws.Rinv, static_cast<T*>(last ? XT : nullptr), static_cast<T*>(last ? XTlo : nullptr),
@@ -1430,7 +1454,7 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
                                 (u4 ? 16 * dm.NP : 0)) * sizeof(float);
   const size_t lds_b = (size_t)(64 * (ellp + 1) + ellp * dm.r_pad) * sizeof(float);
   const struct { const void* fn; size_t bytes; const char* name; } lds_req[] = {
-      {reinterpret_cast<const void*>(&k_chol), lds_chol, "LDS size of k_chol"},
+      {reinterpret_cast<const void*>(chol_kernel(ellp / 16)), lds_chol, "LDS size of k_chol"},
       {reinterpret_cast<const void*>(&k_assemble_b<T>), lds_b, "LDS size of k_assemble_b"},
       {reinterpret_cast<const void*>(jac_fn), lds_jac, "LDS size of k_jacobi"},
       {reinterpret_cast<const void*>(apply_fn), lds_apply, "LDS size of k_apply"},
