@@ -59,7 +59,8 @@ typedef enum { AP_F32 = 0, AP_BF16 = 1, AP_INT4 = 2 } ap_dtype;
  * U (N x rank) and a decompression matrix B (rank x W).
  */
 typedef struct {
-  int32_t batch;        /* B >= 0 sequences (0: an empty cache, every call is a no-op)  */
+  int32_t batch;        /* 0 <= B <= 32767 sequences (0: an empty cache, every call is  
+                           a no-op; larger B: AP_ERR_UNSUPPORTED)                        */
   int32_t n_tokens;     /* N, 1 <= N <= 32768 visual tokens per sequence                */
   int32_t n_kv_heads;   /* Hkv >= 1                                                      */
   int32_t n_q_heads;    /* Hq, a multiple of Hkv, Hq <= 64 (decode workspace is sized here) */

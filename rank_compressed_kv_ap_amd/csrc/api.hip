@@ -58,6 +58,7 @@ static ap_status validate_shape(const ap_compress_params* p) {
   if (p->power_iters < 0) return fail(AP_ERR_BAD_SHAPE, "power_iters < 0");
   // limits of this build's tiling
   if (p->n_tokens > 32768) return fail(AP_ERR_UNSUPPORTED, "n_tokens > 32768");
+  if (p->batch > 32767) return fail(AP_ERR_UNSUPPORTED, "batch > 32767 (2 * batch matrices index one grid dimension)");
   if (p->head_dim > 256) return fail(AP_ERR_UNSUPPORTED, "head_dim > 256");
   if (p->n_q_heads > 64) return fail(AP_ERR_UNSUPPORTED, "n_q_heads > 64");
   if (p->rank > 128) return fail(AP_ERR_UNSUPPORTED, "rank > 128");

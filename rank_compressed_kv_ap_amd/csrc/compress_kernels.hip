@@ -77,20 +77,31 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint2 k) {
 template <class T>
 __global__ __launch_bounds__(256) void k_omega_philox(T* __restrict__ omT, int nmat, int W, int ell,
                                                       int ellp, uint64_t seed) {
-  const size_t per = (size_t)ell * W;
-  const size_t groups = (per + 7) / 8;
+  // grid: x over the 8-element groups of one matrix, y over the matrices (32-bit
+  // indices: ell * W is far below 2^31)
+  const int per = ell * W;
+  const int groups = (per + 7) / 8;
+  const int mat = blockIdx.y;
   const uint2 key = make_uint2(static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
-  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups * nmat;
-       g += (size_t)gridDim.x * blockDim.x) {
-    const int mat = static_cast<int>(g / groups);
-    const size_t i0 = 8 * (g % groups);
-    const size_t blk = i0 / 128;
-    const uint4 x = philox4x32_10(make_uint4(static_cast<uint32_t>(blk), static_cast<uint32_t>(mat), 0u, 0u), key);
-    const int t0 = static_cast<int>(i0 % 128);
+  for (int g = blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += gridDim.x * blockDim.x) {
+    const int i0 = 8 * g;
+    const uint4 x = philox4x32_10(make_uint4(static_cast<uint32_t>(i0 / 128), static_cast<uint32_t>(mat), 0u, 0u), key);
+    const int t0 = i0 & 127;
     const uint32_t word = (t0 >> 5) == 0 ? x.x : ((t0 >> 5) == 1 ? x.y : ((t0 >> 5) == 2 ? x.z : x.w));
     const uint32_t bits = (word >> (t0 & 31)) & 0xffu;
-    int j = static_cast<int>(i0 / W), w = static_cast<int>(i0 % W);
-    const int cnt = static_cast<int>(per - i0 < 8 ? per - i0 : 8);
+    int j = i0 / W, w = i0 - (i0 / W) * W;
+    const int cnt = per - i0 < 8 ? per - i0 : 8;
+    T* dst = omT + ((size_t)mat * ellp + j) * W + w;
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      if (cnt == 8 && w + 8 <= W && (W & 7) == 0) {   // 8 signs of one row: one 16-byte store
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          h[e] = (((bits >> (2 * e)) & 1u) ? 0xBF80u : 0x3F80u) | ((((bits >> (2 * e + 1)) & 1u) ? 0xBF80u : 0x3F80u) << 16);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
+        continue;
+      }
+    }
     for (int t = 0; t < cnt; ++t) {
       omT[((size_t)mat * ellp + j) * W + w] = from_f32<T>(((bits >> t) & 1u) ? -1.f : 1.f);
       if (++w == W) { w = 0; ++j; }
@@ -479,16 +490,16 @@ __global__ __launch_bounds__(kGramThreads) void k_gram(const float* __restrict__
 __global__ __launch_bounds__(256) void k_gram_reduce(const float* __restrict__ Gpart, int nsplit, int nmat,
                                                      int e2, float* __restrict__ G) {
   const int e4 = e2 >> 2;   // e2 = ellp^2 is a multiple of 256
-  const size_t total = (size_t)nmat * e4;
-  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += (size_t)gridDim.x * blockDim.x) {
-    const size_t mat = g / e4, i = g % e4;
-    const float4* src = reinterpret_cast<const float4*>(Gpart + mat * nsplit * (size_t)e2) + i;
+  const int total = nmat * e4;   // 32-bit: at most 2^31 / 4 matrices of 144^2
+  for (int g = blockIdx.x * blockDim.x + threadIdx.x; g < total; g += gridDim.x * blockDim.x) {
+    const int mat = g / e4, i = g - (g / e4) * e4;
+    const float4* src = reinterpret_cast<const float4*>(Gpart + (size_t)mat * nsplit * e2) + i;
     float4 acc = src[0];
     for (int sp = 1; sp < nsplit; ++sp) {
       const float4 v = src[(size_t)sp * e4];
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
-    reinterpret_cast<float4*>(G + mat * (size_t)e2)[i] = acc;
+    reinterpret_cast<float4*>(G + (size_t)mat * e2)[i] = acc;
   }
 }
 
@@ -893,11 +904,13 @@ __host__ __device__ inline size_t jacobi_lds_floats(int ellp, int jsplit) {
 // and the columns stay in registers from the dot products to the rotation: one LDS
 // round trip per step instead of one per 16-row slice.
 template <int NT, int JT>
-__global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, int ell, int ellp,
+__global__ __launch_bounds__(1024) void k_jacobi(const float* __restrict__ Rm, int ell, int ellp_arg,
                                                  int jsplit, float* __restrict__ PS,
                                                  float* __restrict__ Sv, float* __restrict__ sig) {
   extern __shared__ __align__(16) float sh[];
-  constexpr int S = 16 * NT + 1;           // ellp + 1: row offsets become immediates
+  (void)ellp_arg;
+  constexpr int ellp = 16 * NT;            // index arithmetic divides by constants
+  constexpr int S = ellp + 1;              // row offsets become immediates
   const int E = (ell + 1) & ~1;            // even number of columns for the tournament
   const int mat = blockIdx.x / jsplit, js = blockIdx.x - (blockIdx.x / jsplit) * jsplit;
   const int JR = 16 * JT;                  // rows of J per workgroup
@@ -1428,7 +1441,9 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
     hipLaunchKernelGGL(k_omega_copy<T>, grid_1d((size_t)nmat * dm.ell * dm.W), dim3(256), 0, st,
                        c->params.omega, static_cast<T*>(ws.omT), nmat, dm.W, dm.ell, ellp);
   else
-    hipLaunchKernelGGL(k_omega_philox<T>, grid_1d((size_t)nmat * ((dm.ell * (size_t)dm.W + 7) / 8)),
+    hipLaunchKernelGGL(k_omega_philox<T>,
+                       dim3(static_cast<unsigned>(std::min<size_t>(((dm.ell * (size_t)dm.W + 7) / 8 + 255) / 256, 4096)),
+                            static_cast<unsigned>(nmat)),
                        dim3(256), 0, st, static_cast<T*>(ws.omT), nmat, dm.W, dm.ell, ellp, c->params.seed);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_stage(e, "test matrix");

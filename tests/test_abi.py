@@ -106,6 +106,17 @@ def test_compress_rejects_large_probe_count_before_touching_memory():
     assert b"144" in b.lib.ap_last_error()
 
 
+def test_compress_rejects_batch_beyond_the_grid_limit():
+    # 2 * batch matrices index one grid dimension (at most 65535): batch 32768 is refused
+    # during validation, before any device memory is touched (CPU only)
+    from rank_compressed_kv_ap_amd import binding as b
+    p = b.CompressParams(32768, 64, 1, 1, 64, 8, 4, 1, b.AP_BF16, 0, 0, None)
+    out = ctypes.c_void_p(1)
+    st = b.lib.ap_compress(None, None, ctypes.byref(p), None, ctypes.byref(out))
+    assert st == b.AP_ERR_UNSUPPORTED and out.value is None
+    assert b"32767" in b.lib.ap_last_error()
+
+
 def test_decode_rejects_text_pointers_without_text_tokens():
     # text_k / text_v are NULL iff n_text == 0; checked before the cache is looked at, so
     # a NULL cache handle is safe here (CPU only)
