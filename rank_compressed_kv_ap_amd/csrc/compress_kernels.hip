@@ -1082,59 +1082,123 @@ __device__ __forceinline__ void stage_f32(float* dst, int ls, const float* src, 
   }
 }
 
-// U[n][i] = sum_j Qn[n][j] PS[j][i] (i < r) into the decode tiles of one 32-token block;
-// the block's 32 rows of Qn and the r_pad used columns of PS are staged in LDS, their
-// product formed on fp32 MFMA (16 x 16 tiles, one or two per wavefront) into LDS.
-template <class T>
+// U[n][i] = sum_j Qn[n][j] PS[j][i] (i < r) straight into the decode tiles, on fp32
+// MFMA 16x16x4 in the layout of k_apply: 256 tokens per workgroup (wavefront wv takes
+// tokens 64 wv .. 64 wv + 63, two 32-token blocks of two 16-row tiles), each lane holding
+// four consecutive columns j of one token in registers, PS[:, :r_pad] in LDS.
+// V tiles (element [lane][half][e] = token 16 half + 4 (lane / 16) + e, column lane % 16)
+// are the MFMA output layout itself; K tiles (token 16 half + lane % 16, column
+// 4 (lane / 16) + e) are its transpose, so for U_k the two operands swap places (PS
+// columns as the A operand, tokens as the B operand).  Either way a lane ends with the
+// 8 elements it owns in a tile, written in one 16-byte store (two for fp32).  Tokens
+// past N read as zero.
+template <class T, int NT, int NR>   // NT = ellp / 16, NR = r_pad / 16
 __global__ __launch_bounds__(256) void k_assemble_u(const float* __restrict__ Qn, const float* __restrict__ PS,
-                                                    T* __restrict__ Ukv, int N, int ellp, int r, int NP,
-                                                    int nblk) {
+                                                    T* __restrict__ Ukv, int N, int r, int nblk, int tiles_n) {
   extern __shared__ __align__(16) float sh[];
-  const int rp = 16 * NP, ld = rp + 1;
-  float* Qs = sh;                      // [32][ellp + 1]
-  float* Ps = Qs + 32 * (ellp + 1);    // [ellp][rp]
-  float* Ub = Ps + ellp * rp;          // [32][ld]
-  const int mat = blockIdx.x / nblk, t = blockIdx.x % nblk;
+  constexpr int ellp = 16 * NT, rp = 16 * NR;
+  constexpr int PSS = rp + 4;      // LDS row stride (4 PSS = 16 mod 64 words)
+  float* Ps = sh;                  // [ellp][PSS]
+  const int mat = blockIdx.x / tiles_n;
+  const int n0 = (blockIdx.x - mat * tiles_n) * 256;
   const int b = mat >> 1;
   const bool vl = mat & 1;
   const float* Q = Qn + (size_t)mat * N * ellp;
   const float* P = PS + (size_t)mat * ellp * ellp;
-  stage_f32(Qs, ellp + 1, Q + (size_t)kBlockTok * t * ellp, ellp, 32, ellp, N - kBlockTok * t, ellp);
-  stage_f32(Ps, rp, P, ellp, ellp, rp, ellp, r);
-  __syncthreads();
-  {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lg = lane >> 4;
-    for (int tl = wave; tl < 2 * NP; tl += 4) {   // tile tl: rows 16 (tl & 1), columns 16 (tl >> 1)
-      v4f acc = v4f{0, 0, 0, 0};
-      for (int kb = 0; kb < ellp; kb += 16)
-        acc = tile_mma<false, false, false>(Qs, 16 * (tl & 1), kb, ellp + 1, Ps, kb, 16 * (tl >> 1), rp, acc,
-                                            l16, lg);
-      tile_store(Ub, 16 * (tl & 1), 16 * (tl >> 1), ld, l16, lg, acc);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int base = n0 + 64 * wave;
+  float4 y[4][NT];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int tok = base + 16 * rt + l16;
+    const float* row = Q + (size_t)min(tok, N - 1) * ellp + 4 * lg;
+#pragma unroll
+    for (int kc = 0; kc < NT; ++kc) {
+      const float4 v = *reinterpret_cast<const float4*>(row + 16 * kc);
+      y[rt][kc] = tok < N ? v : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
+  for (int idx = tid; idx < ellp * (rp / 4); idx += 256) {
+    const int j = idx / (rp / 4), c = 4 * (idx - j * (rp / 4));
+    float4 v = *reinterpret_cast<const float4*>(P + (size_t)j * ellp + c);
+    if (c + 0 >= r) v.x = 0.f;
+    if (c + 1 >= r) v.y = 0.f;
+    if (c + 2 >= r) v.z = 0.f;
+    if (c + 3 >= r) v.w = 0.f;
+    *reinterpret_cast<float4*>(Ps + j * PSS + c) = v;
+  }
   __syncthreads();
-  // one thread per (panel, tile lane): the lane's 8 elements [half][e] are consecutive in
-  // the tile, so they leave in one 16-byte store (two for fp32)
-  T* base = Ukv + (vl ? (size_t)NP * kBlockElems : 0);
-  for (int idx = threadIdx.x; idx < NP * 64; idx += blockDim.x) {
-    const int p = idx >> 6, lane = idx & 63;
-    float v[8];
+  T* tiles = Ukv + (vl ? (size_t)(rp / 16) * kBlockElems : 0);
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
+  for (int p = 0; p < NR; ++p) {
+    v4f acc[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int kc = 0; kc < NT; ++kc) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int rr = vl ? 16 * half + 4 * (lane >> 4) + e : 16 * half + (lane & 15);
-        const int col = vl ? 16 * p + (lane & 15) : 16 * p + 4 * (lane >> 4) + e;
-        v[4 * half + e] = Ub[rr * ld + col];
+        const float pv = Ps[(16 * kc + 4 * lg + e) * PSS + 16 * p + l16];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const float tv = e == 0 ? y[rt][kc].x : e == 1 ? y[rt][kc].y : e == 2 ? y[rt][kc].z : y[rt][kc].w;
+          acc[rt] = vl ? mfma_f32(tv, pv, acc[rt]) : mfma_f32(pv, tv, acc[rt]);
+        }
       }
-    T* dst = base + tile_base(b, p, t, NP, nblk) + 8 * lane;
-    if constexpr (std::is_same<T, bf16_t>::value) {
-      *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-    } else {
-      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
     }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {        // the wavefront's two 32-token blocks
+      const int blk = (base >> 5) + hb;
+      if (blk >= nblk) continue;
+      T* dst = tiles + tile_base(b, p, blk, rp / 16, nblk) + 8 * lane;
+      const v4f h0 = acc[2 * hb], h1 = acc[2 * hb + 1];   // tile halves 0 and 1
+      if constexpr (std::is_same<T, bf16_t>::value) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(h0[0], h0[1]), pack_bf16x2(h0[2], h0[3]),
+                                                    pack_bf16x2(h1[0], h1[1]), pack_bf16x2(h1[2], h1[3]));
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(h0[0], h0[1], h0[2], h0[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(h1[0], h1[1], h1[2], h1[3]);
+      }
+    }
+  }
+}
+
+template <class T>
+using AssembleUFn = void (*)(const float*, const float*, T*, int, int, int, int);
+template <class T, int NT, int NR>
+static AssembleUFn<T> assemble_u_if() {
+  if constexpr (NR <= NT) return &k_assemble_u<T, NT, NR>;
+  else return nullptr;
+}
+template <class T, int NT>
+static AssembleUFn<T> assemble_u_nt(int nr) {
+  switch (nr) {
+    case 1: return assemble_u_if<T, NT, 1>();
+    case 2: return assemble_u_if<T, NT, 2>();
+    case 3: return assemble_u_if<T, NT, 3>();
+    case 4: return assemble_u_if<T, NT, 4>();
+    case 5: return assemble_u_if<T, NT, 5>();
+    case 6: return assemble_u_if<T, NT, 6>();
+    case 7: return assemble_u_if<T, NT, 7>();
+    case 8: return assemble_u_if<T, NT, 8>();
+    default: return nullptr;
+  }
+}
+template <class T>
+static AssembleUFn<T> assemble_u_kernel(int nt, int nr) {
+  if (nr > nt) return nullptr;
+  switch (nt) {
+    case 1: return assemble_u_nt<T, 1>(nr);
+    case 2: return assemble_u_nt<T, 2>(nr);
+    case 3: return assemble_u_nt<T, 3>(nr);
+    case 4: return assemble_u_nt<T, 4>(nr);
+    case 5: return assemble_u_nt<T, 5>(nr);
+    case 6: return assemble_u_nt<T, 6>(nr);
+    case 7: return assemble_u_nt<T, 7>(nr);
+    case 8: return assemble_u_nt<T, 8>(nr);
+    case 9: return assemble_u_nt<T, 9>(nr);
+    default: return nullptr;
   }
 }
 
@@ -1170,46 +1234,121 @@ __global__ __launch_bounds__(256) void k_assemble_u4(const float* __restrict__ Q
   else q4_store_block<false>(Ub, ld, NP, tiles, srow, scl);
 }
 
-// B[i][w] = sum_j Qc[w][j] S[j][i] for i < r (rows r..r_pad-1 stay zero).  One
-// workgroup per (matrix, 64 columns w): the 64 rows of Qc and S[:, :r_pad] are staged
-// in LDS; each thread accumulates a 4 (i) x 4 (w) block and stores 4 consecutive w.
-template <class T>
+// B[i][w] = sum_j Qc[w][j] S[j][i] for i < r (rows r..r_pad-1 stay zero), on fp32 MFMA
+// 16x16x4 in the layout of k_apply: 256 rows w per workgroup (wavefront wv takes rows
+// 64 wv .. 64 wv + 63 as four 16-row tiles), each lane holding four consecutive columns
+// j of one row in registers straight from HBM, S[:, :r_pad] in LDS read in the same k
+// order.  A lane ends with B[i][w .. w+3] for one i: one 4-element run per store.
+template <class T, int NT, int NR>   // NT = ellp / 16, NR = r_pad / 16
 __global__ __launch_bounds__(256) void k_assemble_b(const float* __restrict__ Qc, const float* __restrict__ Sv,
-                                                    T* __restrict__ Bk, T* __restrict__ Bv, int W, int ellp,
-                                                    int r, int r_pad, int tiles_w) {
+                                                    T* __restrict__ Bk, T* __restrict__ Bv, int W, int r,
+                                                    int tiles_w) {
   extern __shared__ __align__(16) float sh[];
-  const int QS = ellp + 1;
-  float* Qs = sh;                 // [64][QS]
-  float* Ss = Qs + 64 * QS;       // [ellp][r_pad]
+  constexpr int ellp = 16 * NT, rp = 16 * NR;
+  constexpr int SS = rp + 4;       // LDS row stride: the four 4-row groups of a read meet
+                                   // different banks (4 SS = 16 mod 64 words)
+  float* Ss = sh;                  // [ellp][SS]
   const int mat = blockIdx.x / tiles_w;
-  const int w0 = (blockIdx.x % tiles_w) * 64;
+  const int w0 = (blockIdx.x - mat * tiles_w) * 256;
   const float* Q = Qc + (size_t)mat * W * ellp;
   const float* Sm = Sv + (size_t)mat * ellp * ellp;
-  stage_f32(Qs, QS, Q + (size_t)w0 * ellp, ellp, 64, ellp, W - w0, ellp);
-  stage_f32(Ss, r_pad, Sm, ellp, ellp, r_pad, ellp, r);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int base = w0 + 64 * wave;
+  float4 y[4][NT];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int row = min(base + 16 * rt + l16, W - 1);   // rows past W: clamped, never stored
+#pragma unroll
+    for (int kc = 0; kc < NT; ++kc)
+      y[rt][kc] = *reinterpret_cast<const float4*>(Q + (size_t)row * ellp + 16 * kc + 4 * lg);
+  }
+  // S[:, :rp] into LDS, columns >= r zeroed
+  for (int idx = tid; idx < ellp * (rp / 4); idx += 256) {
+    const int j = idx / (rp / 4), c = 4 * (idx - j * (rp / 4));
+    float4 v = *reinterpret_cast<const float4*>(Sm + (size_t)j * ellp + c);
+    if (c + 0 >= r) v.x = 0.f;
+    if (c + 1 >= r) v.y = 0.f;
+    if (c + 2 >= r) v.z = 0.f;
+    if (c + 3 >= r) v.w = 0.f;
+    *reinterpret_cast<float4*>(Ss + j * SS + c) = v;
+  }
   __syncthreads();
-  T* B = ((mat & 1) ? Bv : Bk) + (size_t)(mat >> 1) * r_pad * W;
-  const int wb = (threadIdx.x & 15) * 4;          // 4 consecutive columns
-  for (int ib = (threadIdx.x >> 4) * 4; ib < r; ib += 64) {
-    float acc[4][4] = {};
-    for (int j = 0; j < ellp; ++j) {
-      const float4 sv = *reinterpret_cast<const float4*>(&Ss[j * r_pad + ib]);
-      const float sj[4] = {sv.x, sv.y, sv.z, sv.w};
+  T* B = ((mat & 1) ? Bv : Bk) + (size_t)(mat >> 1) * rp * W;
+  const bool vec4 = (W & 3) == 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float q = Qs[(wb + c) * QS + j];
+  for (int c = 0; c < NR; ++c) {
+    v4f acc[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u][c] = fmaf(q, sj[u], acc[u][c]);
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int kc = 0; kc < NT; ++kc) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float bv = Ss[(16 * kc + 4 * lg + e) * SS + 16 * c + l16];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const float av = e == 0 ? y[rt][kc].x : e == 1 ? y[rt][kc].y : e == 2 ? y[rt][kc].z : y[rt][kc].w;
+          acc[rt] = mfma_f32(av, bv, acc[rt]);
+        }
       }
     }
+    // lane holds B[i][w + t], i = 16 c + l16, w = base + 16 rt + 4 lg, t = 0..3
+    const int i = 16 * c + l16;
+    if (i >= r) continue;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = ib + u;
-      if (i >= r) break;
+    for (int rt = 0; rt < 4; ++rt) {
+      const int w = base + 16 * rt + 4 * lg;
+      T* dst = B + (size_t)i * W + w;
+      if (vec4 && w + 4 <= W) {
+        if constexpr (std::is_same<T, bf16_t>::value)
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[rt][0], acc[rt][1]), pack_bf16x2(acc[rt][2], acc[rt][3]));
+        else
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[rt][0], acc[rt][1], acc[rt][2], acc[rt][3]);
+      } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (w0 + wb + c < W) B[(size_t)i * W + w0 + wb + c] = from_f32<T>(acc[u][c]);
+        for (int t = 0; t < 4; ++t)
+          if (w + t < W) dst[t] = from_f32<T>(acc[rt][t]);
+      }
     }
+  }
+}
+
+template <class T>
+using AssembleBFn = void (*)(const float*, const float*, T*, T*, int, int, int);
+template <class T, int NT, int NR>
+static AssembleBFn<T> assemble_b_if() {
+  if constexpr (NR <= NT) return &k_assemble_b<T, NT, NR>;
+  else return nullptr;
+}
+template <class T, int NT>
+static AssembleBFn<T> assemble_b_nt(int nr) {
+  switch (nr) {
+    case 1: return assemble_b_if<T, NT, 1>();
+    case 2: return assemble_b_if<T, NT, 2>();
+    case 3: return assemble_b_if<T, NT, 3>();
+    case 4: return assemble_b_if<T, NT, 4>();
+    case 5: return assemble_b_if<T, NT, 5>();
+    case 6: return assemble_b_if<T, NT, 6>();
+    case 7: return assemble_b_if<T, NT, 7>();
+    case 8: return assemble_b_if<T, NT, 8>();
+    default: return nullptr;
+  }
+}
+template <class T>
+static AssembleBFn<T> assemble_b_kernel(int nt, int nr) {
+  if (nr > nt) return nullptr;
+  switch (nt) {
+    case 1: return assemble_b_nt<T, 1>(nr);
+    case 2: return assemble_b_nt<T, 2>(nr);
+    case 3: return assemble_b_nt<T, 3>(nr);
+    case 4: return assemble_b_nt<T, 4>(nr);
+    case 5: return assemble_b_nt<T, 5>(nr);
+    case 6: return assemble_b_nt<T, 6>(nr);
+    case 7: return assemble_b_nt<T, 7>(nr);
+    case 8: return assemble_b_nt<T, 8>(nr);
+    case 9: return assemble_b_nt<T, 9>(nr);
+    default: return nullptr;
   }
 }
 
@@ -1467,14 +1606,19 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
   const bool u4 = dm.storage == AP_INT4;
   const size_t lds_u = (size_t)(32 * (ellp + 1) + ellp * 16 * dm.NP + 32 * (16 * dm.NP + 1) +
                                 (u4 ? 16 * dm.NP : 0)) * sizeof(float);
-  const size_t lds_b = (size_t)(64 * (ellp + 1) + ellp * dm.r_pad) * sizeof(float);
+  const size_t lds_u2 = (size_t)ellp * (dm.r_pad + 4) * sizeof(float);
+  const AssembleUFn<T> asm_u_fn = u4 ? nullptr : assemble_u_kernel<T>(ellp / 16, dm.r_pad / 16);
+  if (!u4 && asm_u_fn == nullptr) return fail_stage(hipErrorInvalidValue, "factor assembly shape");
+  const size_t lds_b = (size_t)ellp * (dm.r_pad + 4) * sizeof(float);
+  const AssembleBFn<T> asm_b_fn = assemble_b_kernel<T>(ellp / 16, dm.r_pad / 16);
+  if (asm_b_fn == nullptr) return fail_stage(hipErrorInvalidValue, "factor assembly shape");
   const struct { const void* fn; size_t bytes; const char* name; } lds_req[] = {
       {reinterpret_cast<const void*>(chol_kernel(ellp / 16)), lds_chol, "LDS size of k_chol"},
-      {reinterpret_cast<const void*>(&k_assemble_b<T>), lds_b, "LDS size of k_assemble_b"},
+      {reinterpret_cast<const void*>(asm_b_fn), lds_b, "LDS size of k_assemble_b"},
       {reinterpret_cast<const void*>(jac_fn), lds_jac, "LDS size of k_jacobi"},
       {reinterpret_cast<const void*>(apply_fn), lds_apply, "LDS size of k_apply"},
-      {u4 ? reinterpret_cast<const void*>(&k_assemble_u4) : reinterpret_cast<const void*>(&k_assemble_u<T>),
-       lds_u, "LDS size of k_assemble_u"},
+      {u4 ? reinterpret_cast<const void*>(&k_assemble_u4) : reinterpret_cast<const void*>(asm_u_fn),
+       u4 ? lds_u : lds_u2, "LDS size of k_assemble_u"},
   };
   for (const auto& rq : lds_req) {
     e = hipFuncSetAttribute(rq.fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rq.bytes));
@@ -1513,11 +1657,11 @@ static hipError_t compress_t(ap_cache* c, const void* k, const void* v, hipStrea
                        static_cast<i4_t*>(c->Uk), reinterpret_cast<bf16_t*>(c->Usc), dm.N, ellp, dm.r,
                        dm.NP, dm.nblk);
   else
-    hipLaunchKernelGGL(k_assemble_u<T>, dim3(nmat * dm.nblk), dim3(256), lds_u, st, ws.Qn, ws.PS,
-                       static_cast<T*>(c->Uk), dm.N, ellp, dm.r, dm.NP, dm.nblk);
-  const int tiles_w = (dm.W + 63) / 64;
-  hipLaunchKernelGGL(k_assemble_b<T>, dim3(nmat * tiles_w), dim3(256), lds_b, st, ws.Qc, ws.Sv,
-                     static_cast<T*>(c->Bk), static_cast<T*>(c->Bv), dm.W, ellp, dm.r, dm.r_pad, tiles_w);
+    hipLaunchKernelGGL(asm_u_fn, dim3(nmat * ((dm.N + 255) / 256)), dim3(256), lds_u2, st, ws.Qn, ws.PS,
+                       static_cast<T*>(c->Uk), dm.N, dm.r, dm.nblk, (dm.N + 255) / 256);
+  const int tiles_w = (dm.W + 255) / 256;
+  hipLaunchKernelGGL(asm_b_fn, dim3(nmat * tiles_w), dim3(256), lds_b, st, ws.Qc, ws.Sv,
+                     static_cast<T*>(c->Bk), static_cast<T*>(c->Bv), dm.W, dm.r, tiles_w);
   hipLaunchKernelGGL(k_copy_sigma, grid_1d((size_t)nmat * dm.r), dim3(256), 0, st, ws.sig, c->sigma_k,
                      c->sigma_v, nmat, ellp, dm.r);
   e = hipGetLastError();
