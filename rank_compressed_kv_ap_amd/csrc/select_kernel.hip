@@ -15,7 +15,7 @@
 //     one accumulation yields the scores of 8/HG blocks x 32 tokens x HG heads and
 //     every lane holds four scores of one head.  Scores stay in registers;
 //  C. each head's scores are mapped by a monotone linear map over [min, max] onto
-//     2048 bins; one LDS histogram locates the bin b* holding the k-th largest score;
+//     1024 bins; one LDS histogram locates the bin b* holding the k-th largest score;
 //  D. tokens above b* are taken; inside b*, either all of it is taken, or its few
 //     tokens are ranked exactly by (score desc, index asc), or - when b* is crowded
 //     (ties, a zero query, an outlier stretching the range) - an MSB-first radix
