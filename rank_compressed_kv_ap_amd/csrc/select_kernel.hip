@@ -368,9 +368,10 @@ __device__ __forceinline__ void select_body(
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
     int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
     int r_lo, int top_k, const FusedArgs& fa) {
-  static_assert(!FUSED || (HG == 4 && NPL <= 2 && std::is_same<T, bf16_t>::value),
-                "single-kernel decode: bf16, four heads per workgroup");
   constexpr bool U4 = std::is_same<T, i4_t>::value;
+  static_assert(!FUSED || (HG == 4 && NPL <= 2 && (std::is_same<T, bf16_t>::value || (U4 && NPX > 0))),
+                "single-kernel decode: bf16, or 4-bit codes with the panel split known at compile "
+                "time, four heads per workgroup");
   using TB = StoreB<T>;   // element type of B (and of the text tokens)
   // NPX > 0 (single-kernel decode): the factors have NPX panels and r_lo = 16 * NPL, so
   // the panel loops of the attention phases are resolved at compile time
@@ -513,9 +514,10 @@ __device__ __forceinline__ void select_body(
 
   LaneTile<T> tb[PREF][NSL];
   [[maybe_unused]] uint2 tsc[PREF];   // 4-bit codes: K scales of this lane's slot and columns
-  // 4-bit codes: K scale word of block blk, panel p, for this lane's columns 16p + 4lg + e
-  auto scale_word = [&](int blk, int p) {
-    const bf16_t* row = fa.Usc + ((size_t)b * nblk + blk) * 2 * r_pad + lg * 4 * NP + 4 * p;
+  // 4-bit codes: K (or V) scale word of block blk, panel p, for this lane's columns
+  // 16p + 4lg + e
+  auto scale_word = [&](int blk, int p, bool vrow = false) {
+    const bf16_t* row = fa.Usc + (((size_t)b * nblk + blk) * 2 + (vrow ? 1 : 0)) * r_pad + lg * 4 * NP + 4 * p;
     return *reinterpret_cast<const uint2*>(row);
   };
   auto load_step = [&](int s) {   // s is a compile-time constant after unrolling
@@ -629,6 +631,9 @@ __device__ __forceinline__ void select_body(
   constexpr int PD = NACC <= 4 ? 4 : 2;
   const int p0 = rlo >> 4;                      // first panel with a column >= r_lo
   LaneTile<T> rb[FUSED ? PD : 1][NSL];
+  // 4-bit codes: the K (full-rank pass) or V (value pass) scales of the block in this
+  // lane's slot, for the lane's columns of the step's panel
+  [[maybe_unused]] uint2 rsc[FUSED && U4 ? PD : 1];
   auto ld = [&](int s) {   // s is a compile-time constant after unrolling
     const bool isv = s >= NSK;
     const int ss = isv ? s - NSK : s;
@@ -641,6 +646,7 @@ __device__ __forceinline__ void select_body(
       const int blk = min(grp * NSL + sl, nblk - 1);   // clamped: loads stay unconditional
       rb[s % PD][sl].load(tile_ptr(base, tile_base(b, pan, blk, NP, nblk)), lane);
     }
+    if constexpr (FUSED && U4) rsc[s % PD] = scale_word(min(grp * NSL + my_slot, nblk - 1), pan, isv);
   };
 
   // ---- B. scores of this lane's tokens (head my_h), kept in registers
@@ -1026,8 +1032,8 @@ __device__ __forceinline__ void select_body(
   } else {
     // ================= single-kernel decode of heads h0..h0+nh-1 over every token
     const T* __restrict__ Uv = static_cast<const T*>(fa.Uv);
-    const T* __restrict__ Bv = static_cast<const T*>(fa.Bv);
-    const T* __restrict__ tv = static_cast<const T*>(fa.text_v);
+    const TB* __restrict__ Bv = static_cast<const TB*>(fa.Bv);
+    const TB* __restrict__ tv = static_cast<const TB*>(fa.text_v);
     const float sl2 = fa.sl2;
     (void)Uv;
     float* sts = reinterpret_cast<float*>(smem_raw + Ly.sts);      // [HG][Tn] text scores, then p
@@ -1094,6 +1100,7 @@ __device__ __forceinline__ void select_body(
     // same block-diagonal tiles as the low-rank scores; final scores in log2 units
     const int nph = NPr - p0;
     uint2 qhi[NPM];
+    [[maybe_unused]] float qhf[U4 ? NPM : 1][4];   // 4-bit codes: the values, scaled per block below
 #pragma unroll
     for (int j = 0; j < NPM; ++j) {
       const int p = p0 + j;
@@ -1103,7 +1110,12 @@ __device__ __forceinline__ void select_body(
         const int col = 16 * p + 4 * lg + e;
         v[e] = (my_on && p < NPr && col >= rlo) ? qs[my_h * r_pad + col] : 0.f;
       }
-      qhi[j] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      if constexpr (U4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qhf[j][e] = v[e];
+      } else {
+        qhi[j] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
     }
     // block-diagonal B operands: a lane feeds only the dwords of its own slot and tile half
     uint32_t om[NSL][2];
@@ -1114,6 +1126,15 @@ __device__ __forceinline__ void select_body(
     auto diag = [&](uint32_t x, uint32_t y, int sl) {
       return __builtin_bit_cast(v8bf, make_uint4(x & om[sl][0], y & om[sl][0], x & om[sl][1], y & om[sl][1]));
     };
+    // 4-bit codes: a lane's operand for every slot at once (non-zero in its own slot only),
+    // against which one product with -136 in every A element cancels the offset 136 the
+    // expanded codes of all the step's tiles carry
+    [[maybe_unused]] const uint32_t mj0 = my_j == 0 ? ~0u : 0u, mj1 = ~mj0;
+    [[maybe_unused]] auto own = [&](uint32_t x, uint32_t y) {
+      return __builtin_bit_cast(v8bf, make_uint4(x & mj0, y & mj0, x & mj1, y & mj1));
+    };
+    [[maybe_unused]] const v8bf an8 = __builtin_bit_cast(
+        v8bf, make_uint4(kQ4NegOffset2, kQ4NegOffset2, kQ4NegOffset2, kQ4NegOffset2));
     uint32_t selb = 0;   // bit 4a+t: token at full rank
 #pragma unroll
     for (int a = 0; a < NACC; ++a) {
@@ -1124,9 +1145,21 @@ __device__ __forceinline__ void select_body(
       for (int j = 0; j < NPM; ++j) {
         const int s = a * NPM + j;
         if (j < nph) {
+          if constexpr (U4) {
+            // the K scales of the block in this lane's slot, folded into its latent-query values
+            float sk[4];
+            q4_scales(rsc[s % PD], sk);
+            const uint32_t x = pack_bf16x2(qhf[j][0] * sk[0], qhf[j][1] * sk[1]);
+            const uint32_t y = pack_bf16x2(qhf[j][2] * sk[2], qhf[j][3] * sk[3]);
 #pragma unroll
-          for (int sl = 0; sl < NSL; ++sl)
-            acc = mfma_bf16_k32(__builtin_bit_cast(v8bf, rb[s % PD][sl].raw), diag(qhi[j].x, qhi[j].y, sl), acc);
+            for (int sl = 0; sl < NSL; ++sl)
+              acc = mfma_bf16_k32(__builtin_bit_cast(v8bf, rb[s % PD][sl].deq()), diag(x, y, sl), acc);
+            acc = mfma_bf16_k32(an8, own(x, y), acc);
+          } else {
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl)
+              acc = mfma_bf16_k32(__builtin_bit_cast(v8bf, rb[s % PD][sl].raw), diag(qhi[j].x, qhi[j].y, sl), acc);
+          }
         }
         if (s + PD < 2 * NSK) ld(s + PD);
       }
@@ -1184,13 +1217,13 @@ __device__ __forceinline__ void select_body(
     const int og = ((h0 + min(ohl, nh - 1)) * ginv_num) >> 16;
     const int orows = r_pad + Tn;
     constexpr int UP = 8;
-    Vec16<T> xo[UP];
+    Vec16<TB> xo[UP];
     auto load_out = [&](int r0) {
 #pragma unroll
       for (int u = 0; u < UP; ++u) {
         const int row = min(r0 + u * RS, orows - 1);   // clamped: loads stay unconditional
-        const T* src = row < r_pad ? Bv + ((size_t)b * r_pad + row) * W
-                                   : tv + ((size_t)b * Tn + (row - r_pad)) * W;
+        const TB* src = row < r_pad ? Bv + ((size_t)b * r_pad + row) * W
+                                    : tv + ((size_t)b * Tn + (row - r_pad)) * W;
         xo[u].load_nt(src + (size_t)og * d + occ * V);
       }
     };
@@ -1208,10 +1241,33 @@ __device__ __forceinline__ void select_body(
       // the same probabilities with those of tokens below full rank cleared
       auto sel_p = [&](int t) { return __uint_as_float(__float_as_uint(pv[t]) & bit_mask(selb, 4 * a + t)); };
       const uint32_t ps0 = pack_bf16x2(sel_p(0), sel_p(1)), ps1 = pack_bf16x2(sel_p(2), sel_p(3));
+      // 4-bit codes: the offset products of this step (all tokens, and selected tokens only)
+      [[maybe_unused]] v4f cpa, cps;
+      if constexpr (U4) {
+        const v4f z0 = v4f{0.f, 0.f, 0.f, 0.f};
+        cpa = mfma_bf16_k32(an8, own(pa0, pa1), z0);
+        cps = mfma_bf16_k32(an8, own(ps0, ps1), z0);
+      }
 #pragma unroll
       for (int p = 0; p < NPM; ++p) {
         const int s = NSK + a * NPM + p;
-        if (p < NPr) {
+        if constexpr (U4) {
+          // per step: D = sum over the step's tokens of code * p (offset cancelled), then
+          // Z += scale * D, the V scale of the block in this lane's slot for D's row
+          // (latent column 16p + 4lg + t); no panel straddles r_lo (r_lo = 16 NPL)
+          if (p < NPr) {
+            const bool lo = 16 * p + 16 <= rlo;
+            v4f D = lo ? cpa : cps;
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl)
+              D = mfma_bf16_k32(__builtin_bit_cast(v8bf, rb[s % PD][sl].deq()),
+                                lo ? diag(pa0, pa1, sl) : diag(ps0, ps1, sl), D);
+            float sv[4];
+            q4_scales(rsc[s % PD], sv);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Z[p][t] = fmaf(sv[t], D[t], Z[p][t]);
+          }
+        } else if (p < NPr) {
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) {
             const v8bf ba = diag(pa0, pa1, sl);
@@ -1314,15 +1370,16 @@ __global__ __launch_bounds__(1024) void k_select(
                                               G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
 }
 
-// The whole decode step of four query heads of one sequence (bf16 factors).
-template <int NPL, int NACC, int NPX, bool MQ>
+// The whole decode step of four query heads of one sequence (bf16 factors, or 4-bit U
+// codes with bf16 B).
+template <class T, int NPL, int NACC, int NPX, bool MQ>
 __global__ __launch_bounds__(1024) void k_decode(
-    const bf16_t* __restrict__ Uk, const bf16_t* __restrict__ Bk, const float* __restrict__ q,
+    const T* __restrict__ Uk, const StoreB<T>* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
     int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
     int r_lo, int top_k, FusedArgs fa) {
-  select_body<bf16_t, 4, NPL, NACC, true, NPX, MQ>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad,
-                                                   W, d, G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
+  select_body<T, 4, NPL, NACC, true, NPX, MQ>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad,
+                                              W, d, G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1363,15 +1420,15 @@ static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, i
   if ((dm.nblk + 8 / HG - 1) / (8 / HG) > waves * NACC) return hipErrorInvalidValue;
   if (HG * dm.d > 64 * waves) return hipErrorInvalidValue;
   const void* fn;
-  if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<NPL, NACC, NPX, MQ>);
+  if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<T, NPL, NACC, NPX, MQ>);
   else fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC, MQ>);
   static std::atomic<uint32_t> lds_set{0};
   hipError_t e = ensure_lds_limit(fn, 160 * 1024, lds_set);
   if (e != hipSuccess) return e;
   const int grid = ((dm.B + 7) / 8) * 8 * HGN;
   if constexpr (FUSED)
-    hipExtLaunchKernelGGL((k_decode<NPL, NACC, NPX, MQ>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
-                          ev.stop, 0, static_cast<const T*>(c->Uk), static_cast<const T*>(c->Bk), q,
+    hipExtLaunchKernelGGL((k_decode<T, NPL, NACC, NPX, MQ>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
+                          ev.stop, 0, static_cast<const T*>(c->Uk), static_cast<const StoreB<T>*>(c->Bk), q,
                           c->qt, c->mask, sel_out, dm.B, dm.N, dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d,
                           dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo, top_k, fa);
   else
@@ -1421,10 +1478,18 @@ hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
   return launch_select_t<float>(c, q, r_lo, top_k, sel_out, keys, keys_per_head, st, ev);
 }
 
+// 4-bit codes take the single kernel only in its compile-time panel split: r = 64 (4
+// panels) with r_lo = 16, latent queries on MFMA, 2 or 3 steps per wavefront.
+static bool fused_u4_shape(const Dims& dm, int r_lo, const SelPlan& pl) {
+  return dm.NP == 4 && pl.NPL == 1 && r_lo == 16 && (pl.NACC == 2 || pl.NACC == 3) &&
+         dm.d % 32 == 0 && dm.d <= 128;
+}
+
 bool decode_fused_supported(const Dims& dm, int r_lo, int n_text) {
-  if (dm.storage != AP_BF16 || dm.NP > 4 || n_text > 1024) return false;
+  if ((dm.storage != AP_BF16 && dm.storage != AP_INT4) || dm.NP > 4 || n_text > 1024) return false;
   const SelPlan pl = select_plan(dm, r_lo, true);
   if (pl.HG != 4) return false;
+  if (dm.storage == AP_INT4 && !fused_u4_shape(dm, r_lo, pl)) return false;
   // each workgroup re-reads its sequence's U_k / U_v from L2 and runs one long chain:
   // worth it while the workgroups fit the GPU at one per CU (256 CUs); with more, the
   // split-N path spreads the same bytes better (measured on the batch-64 GQA and the
@@ -1449,12 +1514,18 @@ hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, in
   fa.sl2 = sl2;
   fa.keys = nullptr;
   fa.keys_per_head = 0;
-  fa.Usc = nullptr;
+  fa.Usc = reinterpret_cast<const bf16_t*>(c->Usc);
   // r = 64 (4 panels) with r_lo = 16: the panel split known at compile time (variants
   // that fit the registers without spilling)
   const bool exact = c->dm.NP == 4 && r_lo == 16 * pl.NPL;
   // latent queries and text scores on MFMA: d a multiple of 32 up to 128
   const bool mq = c->dm.d % 32 == 0 && c->dm.d <= 128;
+  if (c->dm.storage == AP_INT4) {
+    if (!fused_u4_shape(c->dm, r_lo, pl)) return hipErrorInvalidValue;
+    if (pl.NACC == 2)
+      return launch_select_v<i4_t, 4, 1, 2, true, 4, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
+    return launch_select_v<i4_t, 4, 1, 3, true, 4, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
+  }
 #define AP_FUS(NPLV, NACCV)                                                             \
   if (pl.NPL == NPLV && pl.NACC == NACCV)                                               \
     return launch_select_v<bf16_t, 4, NPLV, NACCV, true, 0>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);

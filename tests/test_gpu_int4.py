@@ -85,6 +85,52 @@ def test_int4_decode_parity_small(gpu_lib, name):
     print(f"{name}: max abs err {err:.3e}, band flips {flips}")
 
 
+# Shapes the single-kernel decode takes with 4-bit codes: r = 64 (four panels), r_lo =
+# 16, head_dim a multiple of 32, two or three steps per wavefront.
+FUSED = {
+    "gqa6_text_tail": wl.LLAVA.replace(cfg_id=306, batch=3, n_q_heads=6, n_kv_heads=2, head_dim=64,
+                                       n_tokens=300, n_text=20, rank=64, r_lo=16, top_k=75,
+                                       grid=None, inner_dim=300, storage="int4"),
+    "three_steps": wl.LLAVA.replace(cfg_id=307, batch=2, n_q_heads=4, n_kv_heads=4, head_dim=32,
+                                    n_tokens=2100, n_text=0, rank=64, r_lo=16, top_k=500,
+                                    grid=None, inner_dim=256, storage="int4"),
+}
+
+
+def _decode_timed(gpu_lib, w, cache, q, tk, tv, with_sel, splits=0):
+    sel = None
+    if with_sel:
+        sel = torch.full((w.batch, w.n_q_heads, w.top_k), -1, dtype=torch.int32, device="cuda")
+    cache.timing_enable(1)
+    out = gpu_lib.decode(cache, q, r_lo=w.r_lo, top_k=w.top_k, scale=w.scale, text_k=tk, text_v=tv,
+                         sel_out=sel, splits=splits)
+    ms, n = cache.timing_read()
+    cache.timing_enable(0)
+    torch.cuda.synchronize()
+    assert n == 1
+    return out.cpu().numpy(), (sel.cpu().numpy() if sel is not None else None), ms
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_int4_single_kernel_parity(gpu_lib, name):
+    """4-bit codes through the single-kernel decode: that kernel alone runs; output and
+    top-k sets match the oracle; the call without sel_out (the one the benchmark times)
+    gives the same output bit for bit; the split-N path agrees with the oracle too."""
+    w = FUSED[name]
+    seqs = make_inputs(w)
+    cache, q, tk, tv = upload_decode(w, seqs, gpu_lib)
+    out, sel, ms = _decode_timed(gpu_lib, w, cache, q, tk, tv, with_sel=True)
+    assert ms["decode"] > 0 and ms["select"] == ms["attn"] == ms["combine"] == 0, ms
+    err, flips = check_against_oracle(w, seqs, out, sel)
+    out0, _, _ = _decode_timed(gpu_lib, w, cache, q, tk, tv, with_sel=False)
+    assert np.array_equal(out0, out)
+    out3, sel3, ms3 = _decode_timed(gpu_lib, w, cache, q, tk, tv, with_sel=True, splits=3)
+    assert ms3["decode"] == 0 and ms3["attn"] > 0, ms3
+    check_against_oracle(w, seqs, out3, sel3)
+    cache.free()
+    print(f"{name}: max abs err {err:.3e}, band flips {flips}")
+
+
 @pytest.mark.parametrize("top_k,r_lo", [(0, 8), (100, 8), (25, 24), (1, 1)])
 def test_int4_decode_edge_selection(gpu_lib, top_k, r_lo):
     w = SHAPES["ragged"].replace(top_k=top_k, r_lo=r_lo)
