@@ -192,14 +192,18 @@ typedef struct {
    * average modes rank by the importance the earlier steps left (ema_first: no history
    * yet, rank by the low-rank logit), then blend in this step's attention weights p
    * (softmax over text and visual tokens): I <- alpha * I + (1 - alpha) * p, or I <- p
-   * on the first step.  They always run the split-N path.                              */
+   * on the first step.  With splits == 0, bf16 factors of rank 64 and r_lo = 16 run
+   * them in the single-kernel decode (per token, a second kernel then folds the
+   * per-head-group sums of the weights into the state); otherwise the split-N path. */
   int32_t select_mode;
   float ema_alpha;       /* 0 <= alpha < 1: weight of the history                          */
   int32_t ema_first;     /* nonzero on the first step of a sequence's decode              */
   float* importance;     /* device float32 state, caller-owned, read then updated in place:
                             [B][N] (EMA_TOKEN) or [B][Hq][N] (EMA_HEAD)                    */
   float* ema_scratch;    /* device float32 workspace [B][Hq][N], caller-owned: the step's
-                            logits; contents undefined between calls                      */
+                            logits (split-N path) or sums of the weights per group of four
+                            query heads (single kernel, per token); contents undefined
+                            between calls                                                 */
   /* A second factored segment.  [es §2.A], [fr §2.A "Traitement séparé"], [de §2.A
    * "Optimierung"]: text tokens are factored by their own SVD, apart from the visual
    * ones.  text_cache: a cache of the same batch, query/KV heads and head_dim holding

@@ -96,10 +96,23 @@ hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
 hipError_t launch_attn(const ap_cache* c, int r_lo, float scale_log2e, int S, int CB, float* ema_s,
                        hipStream_t st, const KernelEvents& ev);
 // Single-kernel decode (select_kernel.hip): shapes it takes, and its launch.
+// The moving-average selector in the single kernel: keys = the state it ranks by (null
+// on the first step: the low-rank logits); per head the kernel blends the step's
+// weights into imp itself, per token it writes per-head-group sums to part, which
+// launch_ema_fold then folds into imp.
+struct FusedEma {
+  const float* keys;
+  float* imp;
+  float* part;
+  float alpha;
+  bool per_head;
+  bool first;
+};
 bool decode_fused_supported(const Dims& dm, int r_lo, int n_text);
+bool decode_fused_ema_supported(const Dims& dm, int r_lo, int n_text);
 hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, int r_lo, int top_k,
                                int32_t* sel_out, int n_text, const void* text_k, const void* text_v,
-                               float sl2, hipStream_t st, const KernelEvents& ev);
+                               float sl2, const FusedEma* ema, hipStream_t st, const KernelEvents& ev);
 // xo, xml (optional): another segment's normalised output [B][Hq][d] and its softmax
 // maximum and sum [B][Hq][2], merged as one more partial.
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float scale_log2e,
@@ -115,6 +128,10 @@ hipError_t launch_text_seg(const ap_cache* c, const float* q, int r_lo, int top_
 hipError_t launch_ema_update(const ap_cache* c, const float* s, const float* ml, float* imp,
                              bool per_head, bool first, float alpha, hipStream_t st,
                              const KernelEvents& ev);
+// Per-token state after a single-kernel step: I[b][n] <- alpha I + (1 - alpha) mean_h p
+// from the per-head-group sums part [B][ceil(Hq / 4)][N] (summed in group order).
+hipError_t launch_ema_fold(const ap_cache* c, const float* part, float* imp, bool first, float alpha,
+                           hipStream_t st, const KernelEvents& ev);
 
 // ---- launchers (pack_kernels.hip)
 hipError_t launch_pack_u(const ap_cache* c, const void* src, void* dst, bool v_layout,

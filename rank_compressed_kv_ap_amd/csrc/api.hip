@@ -405,7 +405,18 @@ ap_status ap_decode_attn(ap_cache* c, const float* q, float* out, const ap_decod
   if (!ema && !tc && p->splits == 0 && decode_fused_supported(dm, p->r_lo, p->n_text)) {
     // one kernel per step: each (sequence, 4 heads) workgroup selects, attends and projects
     e = launch_decode_fused(c, q, out, p->r_lo, p->top_k, p->sel_out, p->n_text, p->text_k,
-                            p->text_v, sl2, st, events(AP_KERNEL_DECODE));
+                            p->text_v, sl2, nullptr, st, events(AP_KERNEL_DECODE));
+  } else if (ema && !tc && p->splits == 0 && decode_fused_ema_supported(dm, p->r_lo, p->n_text)) {
+    // the moving-average selector in the same kernel: it ranks by the state and blends
+    // the step's weights into it (per head), or leaves per-head-group sums of the weights
+    // in ema_scratch for a fold into the per-token state
+    const FusedEma fe{p->importance, p->importance, p->ema_scratch, p->ema_alpha, per_head,
+                      p->ema_first != 0};
+    e = launch_decode_fused(c, q, out, p->r_lo, p->top_k, p->sel_out, p->n_text, p->text_k,
+                            p->text_v, sl2, &fe, st, events(AP_KERNEL_DECODE));
+    if (e == hipSuccess && !per_head)
+      e = launch_ema_fold(c, p->ema_scratch, p->importance, p->ema_first != 0, p->ema_alpha, st,
+                          events(AP_KERNEL_EMA));
   } else {
     // the moving-average selector ranks by the importance state, except on its first
     // step (no history yet), which ranks by the low-rank logits like the default

@@ -1146,6 +1146,32 @@ __global__ __launch_bounds__(256) void k_ema_update(const float* __restrict__ s,
   }
 }
 
+// Per-token state after a single-kernel step: part [B][G4][N] holds, per group of four
+// query heads, the sum of their weights p; I[b][n] <- alpha I + (1 - alpha) mean_h p with
+// the groups summed in order (I <- mean_h p on the first step).  One thread per token.
+__global__ __launch_bounds__(256) void k_ema_fold(const float* __restrict__ part,
+                                                  float* __restrict__ imp, int G4, int Hq, int N,
+                                                  int first, float alpha) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const size_t b = blockIdx.y;
+  const float* pb = part + b * G4 * N + n;
+  float acc = 0.f;
+  for (int g = 0; g < G4; ++g) acc += pb[(size_t)g * N];
+  const float p = acc / static_cast<float>(Hq);
+  const size_t idx = b * N + n;
+  imp[idx] = first ? p : fmaf(alpha, imp[idx], (1.f - alpha) * p);
+}
+
+hipError_t launch_ema_fold(const ap_cache* c, const float* part, float* imp, bool first, float alpha,
+                           hipStream_t st, const KernelEvents& ev) {
+  const Dims& dm = c->dm;
+  if (dm.B > 65535) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL(k_ema_fold, dim3((unsigned)((dm.N + 255) / 256), (unsigned)dm.B), dim3(256), 0, st,
+                        ev.start, ev.stop, 0, part, imp, (dm.Hq + 3) / 4, dm.Hq, dm.N, first ? 1 : 0, alpha);
+  return hipGetLastError();
+}
+
 hipError_t launch_ema_update(const ap_cache* c, const float* s, const float* ml, float* imp,
                              bool per_head, bool first, float alpha, hipStream_t st,
                              const KernelEvents& ev) {

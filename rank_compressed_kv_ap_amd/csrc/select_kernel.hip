@@ -51,6 +51,7 @@ struct SelState {
 struct SelLayout {
   size_t qh, qb, qs, st, rng, hist, selw, cand;
   size_t sts, zs, hmx, lpart, ltx, lfin, red;   // single-kernel decode only
+  size_t pst;      // single-kernel moving-average selector: [stash][1024 threads] weights
   size_t total;
   int hs;          // words per head in hist
 };
@@ -60,7 +61,7 @@ struct SelLayout {
 // decode as the per-wavefront latent sums and then the output partial sums.
 // Tn > 0 (text tokens) or fused adds the single-kernel decode regions.
 __host__ __device__ inline SelLayout sel_layout(int HG, int nblk, int r_pad, int d, bool fused = false,
-                                                int Tn = 0) {
+                                                int Tn = 0, int stash = 0) {
   auto up = [](size_t x) { return (x + 15) & ~(size_t)15; };
   SelLayout L;
   L.hs = kSelBins > 256 + 2 * nblk ? kSelBins : 256 + 2 * nblk;
@@ -83,6 +84,7 @@ __host__ __device__ inline SelLayout sel_layout(int HG, int nblk, int r_pad, int
     L.lfin = o;  o = up(o + (size_t)HG * 4);
     // the output partial sums [1024 threads][8 floats]
     L.red = o;   o = up(o + (size_t)1024 * 8 * 4);
+    L.pst = o;   o = up(o + (size_t)stash * 1024 * 4);
   }
   L.total = o;
   return L;
@@ -355,6 +357,14 @@ struct FusedArgs {
   int keys_per_head;
   // 4-bit codes: bf16 block scales [B][nblk][2][r_pad] (quant4.h)
   const bf16_t* Usc;
+  // single-kernel decode with the moving-average selector: it ranks by keys (the state;
+  // null on a sequence's first step: by the low-rank logits), then per head blends the
+  // step's attention weights into imp ([B][Hq][N]), or per token writes the sum of its
+  // heads' weights to ema_part ([B][head groups][N]) for the fold that follows
+  float* imp;
+  float* ema_part;
+  float alpha;
+  int ema_first;
 };
 
 // HG: query heads per workgroup (4 or 1); NPL: low panels (1 or 2 with the tiles of
@@ -362,7 +372,7 @@ struct FusedArgs {
 // accumulation steps per wavefront (2, 3, 4 or 8).  FUSED: the same workgroup goes on
 // to the attention of its heads over all tokens, the text tokens and the output
 // projection (bf16 factors, HG = 4, r <= 64), so one kernel makes the whole step.
-template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0, bool MQ = false>
+template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0, bool MQ = false, bool EMA = false>
 __device__ __forceinline__ void select_body(
     const T* __restrict__ Uk, const StoreB<T>* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
@@ -401,7 +411,7 @@ __device__ __forceinline__ void select_body(
   const int my_slot = c16 / (2 * HG), my_j = (c16 / HG) & 1, my_h = c16 % HG;
   const bool my_on = my_h < nh;
 
-  const SelLayout Ly = sel_layout(HG, nblk, r_pad, d, FUSED, FUSED ? fa.Tn : 0);
+  const SelLayout Ly = sel_layout(HG, nblk, r_pad, d, FUSED, FUSED ? fa.Tn : 0, FUSED && EMA ? 4 * NACC : 0);
   float* qh = reinterpret_cast<float*>(smem_raw + Ly.qh);
   bf16_t* qb = reinterpret_cast<bf16_t*>(smem_raw + Ly.qb);
   float* qs = reinterpret_cast<float*>(smem_raw + Ly.qs);
@@ -653,6 +663,7 @@ __device__ __forceinline__ void select_body(
   float sc[KPL];
   // token of score 4a+t: 32 * (block of step a) + 16 * my_j + 4 * lg + t
   auto tok = [&](int a) { return 32 * ((wave + nwv * a) * NSL + my_slot) + 16 * my_j + 4 * lg; };
+
   if (!FUSED && fa.keys != nullptr) {
     // moving-average selector: the keys are the importance state, read from memory
     if (select) {
@@ -719,6 +730,24 @@ __device__ __forceinline__ void select_body(
     }
   }
 
+  // single-kernel decode with the moving-average selector: the selection ranks this
+  // lane's tokens by the state, requested once the score tiles are consumed (earlier,
+  // its registers would be live beside the tile prefetch); the logits wait in the
+  // lane's own LDS slots
+  if constexpr (FUSED && EMA) {
+    if (fa.keys != nullptr) {
+      const size_t kb = fa.keys_per_head ? ((size_t)b * Hq + h0 + (my_on ? my_h : 0)) * N : (size_t)b * N;
+      float* pst = reinterpret_cast<float*>(smem_raw + Ly.pst);
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) pst[i * nthr + tid] = sc[i];
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) {
+        const int n0 = tok(a);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sc[4 * a + t] = (my_on && n0 + t < N) ? fa.keys[kb + n0 + t] : 0.f;
+      }
+    }
+  }
   // bit 4a+t: score of a real token of a present head
   uint32_t vm = 0u;
 #pragma unroll
@@ -1044,6 +1073,13 @@ __device__ __forceinline__ void select_body(
     float* lfin = reinterpret_cast<float*>(smem_raw + Ly.lfin);    // [HG] softmax denominators
     float* zpart = reinterpret_cast<float*>(hist);                 // [waves][HG][r_pad]
     float* red = reinterpret_cast<float*>(smem_raw + Ly.red);      // [row groups][HG * d]
+    if constexpr (EMA) {
+      if (fa.keys != nullptr) {   // the logits back in sc
+        const float* pst = reinterpret_cast<const float*>(smem_raw + Ly.pst);
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) sc[i] = pst[i * nthr + tid];
+      }
+    }
 
     // ---- F1. text scores in log2 units, running max per head: on MFMA, one (head,
     // 16-token tile) pair per wavefront, or LPR lanes per text row; the first pair or
@@ -1294,6 +1330,13 @@ __device__ __forceinline__ void select_body(
         }
       }
     }
+    // moving-average selector: this lane's exp2(s - M) wait in LDS (lane-private slots)
+    // for the softmax sums, which the reductions below complete
+    if constexpr (EMA) {
+      float* pst = reinterpret_cast<float*>(smem_raw + Ly.pst);
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) pst[i * nthr + tid] = sc[i];
+    }
     // lane l holds Z for latent columns 16p + 4lg + t and tile column c16: sum the
     // columns of one head inside the row, one partial per wavefront (fixed-order sums)
 #pragma unroll
@@ -1321,6 +1364,20 @@ __device__ __forceinline__ void select_body(
       lfin[tid] = l;
     }
     lds_barrier();
+    // moving-average selector per head (not the first step): the state this step blends
+    // into, requested before the output pass, which hides the wait
+    [[maybe_unused]] float old[EMA ? KPL : 1];
+    if constexpr (EMA) {
+      if (fa.imp != nullptr && fa.ema_first == 0 && fa.keys != nullptr) {
+        const float* row = fa.imp + ((size_t)b * Hq + h0 + (my_on ? my_h : 0)) * N;
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) {
+          const int n0 = tok(a);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) old[4 * a + t] = row[min(n0 + t, N - 1)];
+        }
+      }
+    }
 
     // ---- F5. out_h = (z_h B_v[:, g's columns] + sum_t p_t V_text[t, g's columns]) / l_h:
     // weighted sums of the r_pad + Tn output rows, partial sums per row group
@@ -1355,6 +1412,42 @@ __device__ __forceinline__ void select_body(
         if (h2 < nh) fa.out[((size_t)b * Hq + h0 + h2) * d + j] = o / lfin[h2];
       }
     }
+    if constexpr (EMA) {
+      // the step's attention weights of this lane's tokens, p = exp2(s - M) / l (0 for
+      // absent tokens and heads)
+      const float* pst = reinterpret_cast<const float*>(smem_raw + Ly.pst);
+      const float linv = my_on ? 1.0f / lfin[my_h] : 0.f;
+      if (fa.imp != nullptr) {
+        // per head: I <- alpha I + (1 - alpha) p, or I <- p on the first step
+        float* row = fa.imp + ((size_t)b * Hq + h0 + (my_on ? my_h : 0)) * N;
+        const float al = fa.alpha, bl = 1.f - fa.alpha;
+        const bool first = fa.ema_first != 0 || fa.keys == nullptr;
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) {
+          const int n0 = tok(a);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float pw = pst[(4 * a + t) * nthr + tid] * linv;
+            if (my_on && n0 + t < N) row[n0 + t] = first ? pw : fmaf(al, old[4 * a + t], bl * pw);
+          }
+        }
+      } else {
+        // per token: the sum over this workgroup's heads (the four lanes of a quad hold the
+        // four heads of the same tokens), one store per token
+        float* row = fa.ema_part + ((size_t)b * HGN + hg) * N;
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) {
+          const int n0 = tok(a);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            float v = pst[(4 * a + t) * nthr + tid] * linv;
+            v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+            v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+            if (my_h == 0 && n0 + t < N) row[n0 + t] = v;
+          }
+        }
+      }
+    }
   }
 }
 
@@ -1372,14 +1465,14 @@ __global__ __launch_bounds__(1024) void k_select(
 
 // The whole decode step of four query heads of one sequence (bf16 factors, or 4-bit U
 // codes with bf16 B).
-template <class T, int NPL, int NACC, int NPX, bool MQ>
+template <class T, int NPL, int NACC, int NPX, bool MQ, bool EMA>
 __global__ __launch_bounds__(1024) void k_decode(
     const T* __restrict__ Uk, const StoreB<T>* __restrict__ Bk, const float* __restrict__ q,
     float* __restrict__ qt, uint32_t* __restrict__ mask, int32_t* __restrict__ sel_out, int B,
     int N, int nblk, int NP, int r_pad, int W, int d, int G, int Hq, int Hq_pad, int HGN,
     int r_lo, int top_k, FusedArgs fa) {
-  select_body<T, 4, NPL, NACC, true, NPX, MQ>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad,
-                                              W, d, G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
+  select_body<T, 4, NPL, NACC, true, NPX, MQ, EMA>(Uk, Bk, q, qt, mask, sel_out, B, N, nblk, NP, r_pad,
+                                                   W, d, G, Hq, Hq_pad, HGN, r_lo, top_k, fa);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1409,25 +1502,25 @@ static SelPlan select_plan(const Dims& dm, int r_lo, bool single_kernel) {
   return pl;
 }
 
-template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0, bool MQ = false>
+template <class T, int HG, int NPL, int NACC, bool FUSED, int NPX = 0, bool MQ = false, bool EMA = false>
 static hipError_t launch_select_v(const ap_cache* c, const float* q, int r_lo, int top_k,
                                   int32_t* sel_out, int waves, const FusedArgs& fa, hipStream_t st,
                                   const KernelEvents& ev) {
   const Dims& dm = c->dm;
   const int HGN = (dm.Hq + HG - 1) / HG;
-  const size_t lds = sel_layout(HG, dm.nblk, dm.r_pad, dm.d, FUSED, FUSED ? fa.Tn : 0).total;
+  const size_t lds = sel_layout(HG, dm.nblk, dm.r_pad, dm.d, FUSED, FUSED ? fa.Tn : 0, FUSED && EMA ? 4 * NACC : 0).total;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   if ((dm.nblk + 8 / HG - 1) / (8 / HG) > waves * NACC) return hipErrorInvalidValue;
   if (HG * dm.d > 64 * waves) return hipErrorInvalidValue;
   const void* fn;
-  if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<T, NPL, NACC, NPX, MQ>);
+  if constexpr (FUSED) fn = reinterpret_cast<const void*>(&k_decode<T, NPL, NACC, NPX, MQ, EMA>);
   else fn = reinterpret_cast<const void*>(&k_select<T, HG, NPL, NACC, MQ>);
   static std::atomic<uint32_t> lds_set{0};
   hipError_t e = ensure_lds_limit(fn, 160 * 1024, lds_set);
   if (e != hipSuccess) return e;
   const int grid = ((dm.B + 7) / 8) * 8 * HGN;
   if constexpr (FUSED)
-    hipExtLaunchKernelGGL((k_decode<T, NPL, NACC, NPX, MQ>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
+    hipExtLaunchKernelGGL((k_decode<T, NPL, NACC, NPX, MQ, EMA>), dim3(grid), dim3(64 * waves), lds, st, ev.start,
                           ev.stop, 0, static_cast<const T*>(c->Uk), static_cast<const StoreB<T>*>(c->Bk), q,
                           c->qt, c->mask, sel_out, dm.B, dm.N, dm.nblk, dm.NP, dm.r_pad, dm.W, dm.d,
                           dm.G, dm.Hq, dm.Hq_pad, HGN, r_lo, top_k, fa);
@@ -1478,9 +1571,10 @@ hipError_t launch_select(const ap_cache* c, const float* q, int r_lo, int top_k,
   return launch_select_t<float>(c, q, r_lo, top_k, sel_out, keys, keys_per_head, st, ev);
 }
 
-// 4-bit codes take the single kernel only in its compile-time panel split: r = 64 (4
-// panels) with r_lo = 16, latent queries on MFMA, 2 or 3 steps per wavefront.
-static bool fused_u4_shape(const Dims& dm, int r_lo, const SelPlan& pl) {
+// The single kernel's compile-time panel split: r = 64 (4 panels) with r_lo = 16,
+// latent queries on MFMA, 2 or 3 steps per wavefront.  4-bit codes and the
+// moving-average selector take the single kernel only there.
+static bool fused_exact_shape(const Dims& dm, int r_lo, const SelPlan& pl) {
   return dm.NP == 4 && pl.NPL == 1 && r_lo == 16 && (pl.NACC == 2 || pl.NACC == 3) &&
          dm.d % 32 == 0 && dm.d <= 128;
 }
@@ -1489,7 +1583,7 @@ bool decode_fused_supported(const Dims& dm, int r_lo, int n_text) {
   if ((dm.storage != AP_BF16 && dm.storage != AP_INT4) || dm.NP > 4 || n_text > 1024) return false;
   const SelPlan pl = select_plan(dm, r_lo, true);
   if (pl.HG != 4) return false;
-  if (dm.storage == AP_INT4 && !fused_u4_shape(dm, r_lo, pl)) return false;
+  if (dm.storage == AP_INT4 && !fused_exact_shape(dm, r_lo, pl)) return false;
   // each workgroup re-reads its sequence's U_k / U_v from L2 and runs one long chain:
   // worth it while the workgroups fit the GPU at one per CU (256 CUs); with more, the
   // split-N path spreads the same bytes better (measured on the batch-64 GQA and the
@@ -1500,9 +1594,18 @@ bool decode_fused_supported(const Dims& dm, int r_lo, int n_text) {
   return sel_layout(4, dm.nblk, dm.r_pad, dm.d, true, n_text).total <= 160 * 1024;
 }
 
+// The moving-average selector in the single kernel: bf16 factors in the same
+// compile-time panel split (the state's registers fit beside the scores there).
+bool decode_fused_ema_supported(const Dims& dm, int r_lo, int n_text) {
+  if (dm.storage != AP_BF16 || !decode_fused_supported(dm, r_lo, n_text)) return false;
+  const SelPlan pl = select_plan(dm, r_lo, true);
+  return fused_exact_shape(dm, r_lo, pl) &&
+         sel_layout(4, dm.nblk, dm.r_pad, dm.d, true, n_text, 4 * pl.NACC).total <= 160 * 1024;
+}
+
 hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, int r_lo, int top_k,
                                int32_t* sel_out, int n_text, const void* text_k, const void* text_v,
-                               float sl2, hipStream_t st, const KernelEvents& ev) {
+                               float sl2, const FusedEma* ema, hipStream_t st, const KernelEvents& ev) {
   const SelPlan pl = select_plan(c->dm, r_lo, true);
   FusedArgs fa;
   fa.Uv = c->Uv;
@@ -1515,13 +1618,29 @@ hipError_t launch_decode_fused(const ap_cache* c, const float* q, float* out, in
   fa.keys = nullptr;
   fa.keys_per_head = 0;
   fa.Usc = reinterpret_cast<const bf16_t*>(c->Usc);
+  fa.imp = nullptr;
+  fa.ema_part = nullptr;
+  fa.alpha = 0.f;
+  fa.ema_first = 0;
   // r = 64 (4 panels) with r_lo = 16: the panel split known at compile time (variants
   // that fit the registers without spilling)
   const bool exact = c->dm.NP == 4 && r_lo == 16 * pl.NPL;
   // latent queries and text scores on MFMA: d a multiple of 32 up to 128
   const bool mq = c->dm.d % 32 == 0 && c->dm.d <= 128;
+  if (ema != nullptr) {
+    if (c->dm.storage != AP_BF16 || !fused_exact_shape(c->dm, r_lo, pl)) return hipErrorInvalidValue;
+    fa.keys = ema->first ? nullptr : ema->keys;
+    fa.keys_per_head = ema->per_head ? 1 : 0;
+    fa.imp = ema->per_head ? ema->imp : nullptr;
+    fa.ema_part = ema->per_head ? nullptr : ema->part;
+    fa.alpha = ema->alpha;
+    fa.ema_first = ema->first ? 1 : 0;
+    if (pl.NACC == 2)
+      return launch_select_v<bf16_t, 4, 1, 2, true, 4, true, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
+    return launch_select_v<bf16_t, 4, 1, 3, true, 4, true, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
+  }
   if (c->dm.storage == AP_INT4) {
-    if (!fused_u4_shape(c->dm, r_lo, pl)) return hipErrorInvalidValue;
+    if (!fused_exact_shape(c->dm, r_lo, pl)) return hipErrorInvalidValue;
     if (pl.NACC == 2)
       return launch_select_v<i4_t, 4, 1, 2, true, 4, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);
     return launch_select_v<i4_t, 4, 1, 3, true, 4, true>(c, q, r_lo, top_k, sel_out, pl.waves, fa, st, ev);

@@ -32,6 +32,13 @@ SHAPES = {
     "f32_gqa": wl.GQA.replace(cfg_id=122, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=32,
                               n_tokens=70, rank=40, r_lo=20, top_k=17, storage="f32", inner_dim=64),
     "llava7b_layer": wl.LLAVA,
+    # rank 64 with r_lo = 16: the single-kernel decode (two and three steps per wavefront)
+    "bf16_single": wl.LLAVA.replace(cfg_id=124, batch=3, n_q_heads=6, n_kv_heads=2, head_dim=64,
+                                    n_tokens=300, n_text=20, rank=64, r_lo=16, top_k=75, grid=None,
+                                    inner_dim=300),
+    "bf16_single_3": wl.LLAVA.replace(cfg_id=125, batch=2, n_q_heads=4, n_kv_heads=4, head_dim=32,
+                                      n_tokens=2100, n_text=0, rank=64, r_lo=16, top_k=500,
+                                      grid=None, inner_dim=256),
     # more selection workgroups than CUs: the 8-wavefront selector
     "bf16_many_wgs": wl.LLAVA.replace(cfg_id=123, batch=70, n_q_heads=16, n_kv_heads=16,
                                       head_dim=64, n_tokens=300, n_text=5, rank=32, r_lo=16,
@@ -73,7 +80,7 @@ def _oracle_with_sets(w, s, q, sets):
                       s["text_v"] if w.n_text else None, select_keys=keys)
 
 
-def _run(gpu_lib, w, mode, alpha, steps, n_distinct=None, seed=5):
+def _run(gpu_lib, w, mode, alpha, steps, n_distinct=None, seed=5, splits=0, path=None):
     seqs = make_inputs(w, n_distinct)
     cache, q0, tk, tv = upload_decode(w, seqs, gpu_lib)
     B, Hq, N, k = w.batch, w.n_q_heads, w.n_tokens, w.top_k
@@ -86,9 +93,20 @@ def _run(gpu_lib, w, mode, alpha, steps, n_distinct=None, seed=5):
         q = torch.from_numpy(np.stack([qs[t][b % len(seqs)] for b in range(B)])).cuda()
         before = imp.cpu().numpy().astype(np.float64)
         sel = torch.full((B, Hq, k), -1, dtype=torch.int32, device="cuda")
+        if path is not None:
+            cache.timing_enable(1)
         out = gpu_lib.decode(cache, q, r_lo=w.r_lo, top_k=k, scale=w.scale, text_k=tk, text_v=tv,
                              sel_out=sel, select=mode, ema_alpha=alpha, ema_first=(t == 0),
-                             importance=imp, ema_scratch=scratch)
+                             importance=imp, ema_scratch=scratch, splits=splits)
+        if path is not None:
+            ms, n = cache.timing_read()
+            cache.timing_enable(0)
+            assert n == 1
+            if path == "decode":   # the single kernel, plus the fold of the per-token state
+                assert ms["decode"] > 0 and ms["select"] == ms["attn"] == ms["combine"] == 0, ms
+                assert (ms["ema"] > 0) == (mode == "ema_token"), ms
+            else:
+                assert ms["decode"] == 0 and min(ms["select"], ms["attn"], ms["ema"]) > 0, ms
         torch.cuda.synchronize()
         out, sel, after = out.cpu().numpy(), sel.cpu().numpy(), imp.cpu().numpy().astype(np.float64)
         for b in range(len(seqs)):
@@ -128,6 +146,16 @@ def _run(gpu_lib, w, mode, alpha, steps, n_distinct=None, seed=5):
 @pytest.mark.parametrize("name,alpha", [("bf16_text", 0.8), ("f32_gqa", 0.5)])
 def test_ema_selector_steps(gpu_lib, name, mode, alpha):
     _run(gpu_lib, SHAPES[name], mode, alpha, steps=4)
+
+
+@pytest.mark.parametrize("mode", ["ema_token", "ema_head"])
+@pytest.mark.parametrize("name,splits,path", [("bf16_single", 0, "decode"), ("bf16_single_3", 0, "decode"),
+                                              ("bf16_single", 2, "split")])
+def test_ema_selector_single_kernel(gpu_lib, name, splits, path, mode):
+    """Shapes the single-kernel decode takes: the state is ranked, blended (per head) or
+    folded from per-head-group sums (per token) there; an explicit split count runs the
+    split-N path on the same shape."""
+    _run(gpu_lib, SHAPES[name], mode, 0.8, steps=3, splits=splits, path=path)
 
 
 @pytest.mark.parametrize("mode", ["ema_token", "ema_head"])
