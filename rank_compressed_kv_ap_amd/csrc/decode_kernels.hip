@@ -87,6 +87,10 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
   using QT = typename std::conditional<
       U4, float4, typename std::conditional<BF, v4s, QOp<float>>::type>::type;
   QT qop[NP][HT];
+  // bf16 factors: the bf16 rounding remainder of the latent query's columns below r_lo
+  // (zero above), a second operand for the low-rank logits, which then carry about 16
+  // bits of q~ as the selector's do (4-bit codes form it per block, after the scales)
+  [[maybe_unused]] v4s qrem[U4 || !BF ? 1 : NP][HT];
   {
     float4 qraw[NP][HT];
 #pragma unroll
@@ -106,6 +110,11 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
         } else if constexpr (BF) {
           const uint2 w = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
           qop[p][ht] = __builtin_bit_cast(v4s, w);
+          float rr[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            rr[e] = 16 * p + 4 * lg + e < r_lo ? v[e] - bf16_to_f32(f32_to_bf16(v[e])) : 0.f;
+          qrem[p][ht] = __builtin_bit_cast(v4s, make_uint2(pack_bf16x2(rr[0], rr[1]), pack_bf16x2(rr[2], rr[3])));
         } else {
           qop[p][ht].set(v);
         }
@@ -171,17 +180,25 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         v4f slo[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}}, shi[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}};
-        v4s qb[NP];   // this block's latent-query operands
+        v4s qb[NP], qr[NP];   // this block's latent-query operands, and the remainders
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           if constexpr (U4) {
             float s[4];
             q4_scales(ssc[0][p], s);
             const float4 qv = qop[p][ht];
-            qb[p] = __builtin_bit_cast(v4s, make_uint2(pack_bf16x2(qv.x * s[0], qv.y * s[1]),
-                                                       pack_bf16x2(qv.z * s[2], qv.w * s[3])));
+            const float f[4] = {qv.x * s[0], qv.y * s[1], qv.z * s[2], qv.w * s[3]};
+            qb[p] = __builtin_bit_cast(v4s, make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])));
+            if (!hi_panel(p)) {
+              float rr[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                rr[e] = 16 * p + 4 * lg + e < r_lo ? f[e] - bf16_to_f32(f32_to_bf16(f[e])) : 0.f;
+              qr[p] = __builtin_bit_cast(v4s, make_uint2(pack_bf16x2(rr[0], rr[1]), pack_bf16x2(rr[2], rr[3])));
+            }
           } else {
             qb[p] = qop[p][ht];
+            if (!hi_panel(p)) qr[p] = qrem[p][ht];
           }
         }
 #pragma unroll
@@ -196,6 +213,7 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
             }
             if (lo_panel(p)) {
               slo[hf] = mfma_bf16(a, qb[p], slo[hf]);
+              slo[hf] = mfma_bf16(a, qr[p], slo[hf]);
             } else if (hi_panel(p)) {
               shi[hf] = mfma_bf16(a, qb[p], shi[hf]);
             } else {
@@ -205,6 +223,7 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
                 if (16 * p + 4 * lg + e < r_lo) qh[e] = 0; else ql[e] = 0;
               }
               slo[hf] = mfma_bf16(a, ql, slo[hf]);
+              slo[hf] = mfma_bf16(a, qr[p], slo[hf]);   // zero at the columns >= r_lo
               shi[hf] = mfma_bf16(a, qh, shi[hf]);
             }
           }
@@ -217,6 +236,7 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
           for (int p = 0; p < NP; ++p) {
             if (lo_panel(p)) {
               clo = mfma_bf16(an, qb[p], clo);
+              clo = mfma_bf16(an, qr[p], clo);
             } else if (hi_panel(p)) {
               chi = mfma_bf16(an, qb[p], chi);
             } else {
@@ -226,6 +246,7 @@ __global__ __launch_bounds__(256, (NP * HT * kAttnElemRegBytes<T> <= 16) ? 2 : 1
                 if (16 * p + 4 * lg + e < r_lo) qh[e] = 0; else ql[e] = 0;
               }
               clo = mfma_bf16(an, ql, clo);
+              clo = mfma_bf16(an, qr[p], clo);
               chi = mfma_bf16(an, qh, chi);
             }
           }

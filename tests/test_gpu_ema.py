@@ -10,10 +10,12 @@ Each step is checked on its own against the CPU oracle:
     fp32) and the attention weights p; the GPU's new state must equal
     alpha * (state before) + (1 - alpha) * p (or p on the first step), per head or
     averaged over heads, within a bound derived from the arithmetic: with bf16 factors
-    the flash-decode kernel rounds the latent query q~ to bf16 (relative 2^-9 per
-    element, products and sums in fp32), so a logit moves by at most
-    2^-8 * scale * sum_i |U_k[n,i] q~_i| and a weight p = exp(s - M) / L by at most
-    twice the largest such move, relatively; fp32 factors: 1e-4.
+    the decode kernels round the latent query q~ to bf16 in its columns at or above
+    r_lo (relative 2^-9 per element, products and sums in fp32; the columns below r_lo
+    carry a hi + lo split), so a logit moves by at most
+    2^-8 * scale * sum_i |U_k[n,i] q~_i| (taken over every column, an upper bound) and
+    a weight p = exp(s - M) / L by at most twice the largest such move, relatively;
+    fp32 factors: 1e-4.
 """
 import numpy as np
 import pytest
