@@ -365,29 +365,97 @@ __global__ __launch_bounds__(2 * BM) void k_gemm(const T* __restrict__ Kmat,
       }
 }
 
-// fp32 storage: plain VALU products (small shapes only).
-template <bool TRANS>
+// fp32 storage: the same products on fp32 MFMA (16x16x4), operands read straight from
+// global memory (L1/L2 serve the re-reads; fp32 factorisation is for small layers).
+// Workgroup = (matrix, 128 rows of Y), four wavefronts of two 16-row tiles each, every
+// 16-column tile of Y.  A 16-wide k step is four MFMA k steps; lane l supplies the k
+// values 4 (l / 16) + s of sub-step s, so that its four A (and X^T) values of a step are
+// consecutive in k.
+//   TRANS = false: D = A X with A as the MFMA A operand (rows m, 4 consecutive k per
+//                  lane: one float4 when W is a multiple of 4);
+//   TRANS = true : D^T = X^T A with X^T as the A operand and A's rows (consecutive m
+//                  across the 16 lanes of a row group) as the B operand, so each lane
+//                  ends holding 4 consecutive columns of one row of Y.
+// k past K reads as zero on both operands.
+constexpr int kGemmF32Rows = 128;
+
+template <bool TRANS, int NT>
 __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ Kmat,
                                                   const float* __restrict__ Vmat,
                                                   const float* __restrict__ XT, float* __restrict__ Y,
-                                                  int N, int W, int ellp, size_t x_mat_stride, int nmat) {
+                                                  int N, int W, int ellp, size_t x_mat_stride, int tiles_m) {
   const int M = TRANS ? W : N, K = TRANS ? N : W;
-  const size_t total = (size_t)nmat * M * ellp;
-  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
-       g += (size_t)gridDim.x * blockDim.x) {
-    const int j = static_cast<int>(g % ellp);
-    const int m = static_cast<int>((g / ellp) % M);
-    const int mat = static_cast<int>(g / ((size_t)ellp * M));
-    const float* A = ((mat & 1) ? Vmat : Kmat) + (size_t)(mat >> 1) * N * W;
-    const float* x = XT + (size_t)mat * x_mat_stride + (size_t)j * K;
-    float acc = 0.f;
-    if (!TRANS) {
-      for (int k = 0; k < K; ++k) acc = fmaf(A[(size_t)m * W + k], x[k], acc);
-    } else {
-      for (int k = 0; k < K; ++k) acc = fmaf(A[(size_t)k * W + m], x[k], acc);
+  const int mat = blockIdx.x / tiles_m, tm = blockIdx.x - mat * tiles_m;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const float* A = ((mat & 1) ? Vmat : Kmat) + (size_t)(mat >> 1) * N * W;
+  const float* X = XT + (size_t)mat * x_mat_stride;
+  const int mb = tm * kGemmF32Rows + 32 * wave;   // this wavefront's two 16-row tiles
+  v4f acc[2][NT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  const bool kvec = K % 4 == 0;   // rows of X^T (and of A when not transposed) as float4
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const int kk = k0 + 4 * lg;   // this lane's first k of the step
+    float a[2][4], x[NT][4];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      const float* xr = X + (size_t)(16 * c + l16) * K;
+      if (kvec) {
+        const float4 v = kk < K ? *reinterpret_cast<const float4*>(xr + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[c][0] = v.x; x[c][1] = v.y; x[c][2] = v.z; x[c][3] = v.w;
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x[c][s] = kk + s < K ? xr[kk + s] : 0.f;
+      }
     }
-    Y[((size_t)mat * M + m) * ellp + j] = acc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = mb + 16 * i + l16;
+      const bool live = m < M;
+      if (!TRANS) {
+        const float* ar = A + (size_t)(live ? m : 0) * W;
+        if (kvec) {
+          const float4 v = live && kk < K ? *reinterpret_cast<const float4*>(ar + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+          a[i][0] = v.x; a[i][1] = v.y; a[i][2] = v.z; a[i][3] = v.w;
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) a[i][s] = live && kk + s < K ? ar[kk + s] : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a[i][s] = live && kk + s < K ? A[(size_t)(kk + s) * W + m] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+          acc[i][c] = TRANS ? mfma_f32(x[c][s], a[i][s], acc[i][c]) : mfma_f32(a[i][s], x[c][s], acc[i][c]);
   }
+  // D row 4 lg + t, column l16: (m, 16c + l16) untransposed, (m = l16 tile row,
+  // 16c + 4 lg + t) transposed
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      if (!TRANS) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int m = mb + 16 * i + 4 * lg + t;
+          if (m < M) Y[((size_t)mat * M + m) * ellp + 16 * c + l16] = acc[i][c][t];
+        }
+      } else {
+        const int m = mb + 16 * i + l16;
+        if (m < M)
+          *reinterpret_cast<float4*>(Y + ((size_t)mat * M + m) * ellp + 16 * c + 4 * lg) =
+              make_float4(acc[i][c][0], acc[i][c][1], acc[i][c][2], acc[i][c][3]);
+      }
+    }
 }
 
 // ================================================================ orthonormalisation
@@ -1424,14 +1492,24 @@ static hipError_t gemm(const ap_cache* c, const void* k, const void* v, const vo
 #undef AP_GEMM_LAUNCH_B
 #undef AP_GEMM_LAUNCH_V
   } else {
-    if (trans)
-      hipLaunchKernelGGL((k_gemm_f32<true>), grid_1d((size_t)nmat * M * ellp), dim3(256), 0, st,
-                         static_cast<const float*>(k), static_cast<const float*>(v),
-                         static_cast<const float*>(XT), Y, dm.N, dm.W, ellp, x_stride, nmat);
-    else
-      hipLaunchKernelGGL((k_gemm_f32<false>), grid_1d((size_t)nmat * M * ellp), dim3(256), 0, st,
-                         static_cast<const float*>(k), static_cast<const float*>(v),
-                         static_cast<const float*>(XT), Y, dm.N, dm.W, ellp, x_stride, nmat);
+    const int tiles_m = (M + kGemmF32Rows - 1) / kGemmF32Rows;
+#define AP_GEMM_F32_CASE(NTV)                                                                         \
+  case NTV:                                                                                           \
+    if (trans)                                                                                        \
+      hipLaunchKernelGGL((k_gemm_f32<true, NTV>), dim3(nmat * tiles_m), dim3(256), 0, st,             \
+                         static_cast<const float*>(k), static_cast<const float*>(v),                  \
+                         static_cast<const float*>(XT), Y, dm.N, dm.W, ellp, x_stride, tiles_m);      \
+    else                                                                                              \
+      hipLaunchKernelGGL((k_gemm_f32<false, NTV>), dim3(nmat * tiles_m), dim3(256), 0, st,            \
+                         static_cast<const float*>(k), static_cast<const float*>(v),                  \
+                         static_cast<const float*>(XT), Y, dm.N, dm.W, ellp, x_stride, tiles_m);      \
+    break;
+    switch (ellp / 16) {
+      AP_GEMM_F32_CASE(1) AP_GEMM_F32_CASE(2) AP_GEMM_F32_CASE(3) AP_GEMM_F32_CASE(4)
+      AP_GEMM_F32_CASE(5) AP_GEMM_F32_CASE(6) AP_GEMM_F32_CASE(7) AP_GEMM_F32_CASE(8) AP_GEMM_F32_CASE(9)
+      default: return hipErrorInvalidValue;
+    }
+#undef AP_GEMM_F32_CASE
   }
   return hipGetLastError();
 }

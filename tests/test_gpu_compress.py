@@ -97,6 +97,13 @@ SMALL = {
     # fp32 at ell = 144
     "f32_ell144": (wl.TINY.replace(cfg_id=212, batch=1, n_kv_heads=4, n_q_heads=4, head_dim=64,
                                    n_tokens=300, rank=128, inner_dim=200), {}),
+    # fp32 over several 128-row tiles and 16-wide k steps of the MFMA products, with a
+    # ragged row tile (1000 rows) and a ragged k step (N = 1000 in A^T Q)
+    "f32_wide": (wl.TINY.replace(cfg_id=213, batch=1, n_kv_heads=8, n_q_heads=8, head_dim=128,
+                                 n_tokens=1000, rank=64, inner_dim=200), {}),
+    # fp32 with widths and token counts not multiples of 4 (element-wise operand loads)
+    "f32_odd": (wl.TINY.replace(cfg_id=214, batch=2, n_kv_heads=3, n_q_heads=3, head_dim=21,
+                                n_tokens=131, rank=16, inner_dim=50), {}),
     # 8 matrices: the product kernels deal each matrix's row tiles to one XCD
     "bf16_eight_matrices": (wl.LLAVA.replace(cfg_id=209, batch=4, n_q_heads=4, n_kv_heads=4, head_dim=64,
                                              n_tokens=300, rank=24, grid=None, inner_dim=120), {}),
