@@ -519,7 +519,7 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 constexpr int kCombThreads = 128;
 constexpr int kTextChunk = 256;
 
-template <class T>
+template <class T, bool TEXT>
 __global__ __launch_bounds__(kCombThreads) void k_combine(
     const float* __restrict__ part_z, const float* __restrict__ part_ml, const T* __restrict__ Bv,
     const float* __restrict__ q, float* __restrict__ out, const T* __restrict__ text_k,
@@ -544,6 +544,23 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
   const int seg = tid % LPR, rg = tid / LPR;
   const size_t pb = (size_t)b * S * HP;
 
+  // Every load that does not wait on another value is issued here, so that one memory
+  // latency covers the partials, the split sums and (with no text tokens, whose row loads
+  // would need the same registers) the first pass of B_v rows: the B_v rows of this
+  // head's columns (the first U * RPP of them) and this thread's latent column's
+  // partials of the first U splits.
+  const T* bbase = Bv + (size_t)b * RP * W + (size_t)g * d + seg * V;
+  Vec16<T> xb[U];
+  if constexpr (!TEXT) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) xb[u].load(bbase + (size_t)min(u * RPP + rg, RP - 1) * W);
+  }
+  float zv0[U];
+  {
+    const float* zb = part_z + pb * RP + (size_t)h * RP + min(tid, RP - 1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) zv0[u] = zb[(size_t)min(u, S - 1) * HP * RP];
+  }
   for (int j = tid; j < d; j += kCombThreads) qh[j] = q[((size_t)b * Hq + h) * d + j];
   float mv = kNegBig;
   for (int s = tid; s < S; s += kCombThreads) {
@@ -558,7 +575,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.f;
   float mt = kNegBig, lt = 0.f;
-  for (int t0 = 0; t0 < Tn; t0 += kTextChunk) {
+  for (int t0 = 0; TEXT && t0 < Tn; t0 += kTextChunk) {
     const int tc = min(kTextChunk, Tn - t0);
     const T* kbase = text_k + ((size_t)b * Tn + t0) * W + (size_t)g * d + seg * V;
     const T* vbase = text_v + ((size_t)b * Tn + t0) * W + (size_t)g * d + seg * V;
@@ -633,27 +650,29 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
     for (int s0 = 0; s0 < S; s0 += U) {
       float zv[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) zv[u] = zb[(size_t)min(s0 + u, S - 1) * HP * RP];
+      for (int u = 0; u < U; ++u)
+        zv[u] = (i == tid && s0 == 0) ? zv0[u] : zb[(size_t)min(s0 + u, S - 1) * HP * RP];
 #pragma unroll
       for (int u = 0; u < U; ++u) z = fmaf(s0 + u < S ? ws[min(s0 + u, S - 1)] : 0.f, zv[u], z);
     }
     zz[i] = z;
   }
   __syncthreads();
-  // projection through B_v: row group rg takes latent rows rg, rg+RPP, ...
+  // projection through B_v: row group rg takes latent rows rg, rg+RPP, ... (the first
+  // pass's rows were loaded at the start when there is no text)
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] *= wt;
-  const T* bbase = Bv + (size_t)b * RP * W + (size_t)g * d + seg * V;
   for (int i0 = 0; i0 < RP; i0 += U * RPP) {
-    Vec16<T> x[U];
+    if (TEXT || i0 > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u].load(bbase + (size_t)min(i0 + u * RPP + rg, RP - 1) * W);
+      for (int u = 0; u < U; ++u) xb[u].load(bbase + (size_t)min(i0 + u * RPP + rg, RP - 1) * W);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * RPP + rg;
       const float zi = i < RP ? zz[min(i, RP - 1)] : 0.f;
 #pragma unroll
-      for (int e = 0; e < V; ++e) acc[e] = fmaf(zi, x[u].get(e), acc[e]);
+      for (int e = 0; e < V; ++e) acc[e] = fmaf(zi, xb[u].get(e), acc[e]);
     }
   }
 #pragma unroll
@@ -851,11 +870,16 @@ static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out
   if (vec) {
     const int rpp = kCombThreads / lpr;
     const size_t lds = (size_t)(dm.d + dm.r_pad + kTextChunk + 4 + rpp * dm.d + 2 * S) * sizeof(float);
-    hipExtLaunchKernelGGL(k_combine<T>, dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st, ev.start,
-                          ev.stop, 0, c->part_z,
-                       c->part_ml, static_cast<const T*>(c->Bv), q, out, static_cast<const T*>(tk),
-                       static_cast<const T*>(tv), S, dm.Hq, dm.Hq_pad, dm.r_pad, dm.W, dm.d, dm.G, Tn,
-                       sl2, ml_out, xo, xml);
+    if (Tn > 0)
+      hipExtLaunchKernelGGL((k_combine<T, true>), dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st, ev.start,
+                            ev.stop, 0, c->part_z, c->part_ml, static_cast<const T*>(c->Bv), q, out,
+                            static_cast<const T*>(tk), static_cast<const T*>(tv), S, dm.Hq, dm.Hq_pad,
+                            dm.r_pad, dm.W, dm.d, dm.G, Tn, sl2, ml_out, xo, xml);
+    else
+      hipExtLaunchKernelGGL((k_combine<T, false>), dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st,
+                            ev.start, ev.stop, 0, c->part_z, c->part_ml, static_cast<const T*>(c->Bv), q,
+                            out, static_cast<const T*>(tk), static_cast<const T*>(tv), S, dm.Hq,
+                            dm.Hq_pad, dm.r_pad, dm.W, dm.d, dm.G, Tn, sl2, ml_out, xo, xml);
   } else {
     const size_t lds = (size_t)(dm.d + dm.r_pad + kCombThreads + 4) * sizeof(float);
     hipExtLaunchKernelGGL(k_combine_scalar<T>, dim3(dm.B * dm.Hq), dim3(kCombThreads), lds, st,
