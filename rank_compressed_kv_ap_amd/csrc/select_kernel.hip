@@ -495,12 +495,43 @@ __device__ __forceinline__ void select_body(
   };
   // (head, latent-row tile) pairs whose rows lie below r_lo: needed by the low-rank scores
   auto lo_pair = [&](int pair) { return 16 * (pair - (pair / qtiles) * qtiles) < rlo; };
+  // More pairs than wavefronts (8 wavefronts, four heads): the pairs are dealt from a
+  // list holding every pair below r_lo first, wavefront w taking items w, w + nwv, ...
+  // Each wavefront's first item is requested at the start; its items below r_lo and its
+  // first item are done before the scores, and only then is its next item requested,
+  // so that those rows arrive during the selection.  No wavefront then waits for a
+  // second load before the scores or at the end.
+  const bool spread = !FUSED && mq && npair_q > nwv;   // (the single kernel runs 16 wavefronts)
+  const int nlo_t = min((rlo + 15) >> 4, qtiles);
+  const int nlo_p = nh * nlo_t, nhi_t = max(qtiles - nlo_t, 1);
+  auto pair_at = [&](int idx) {
+    if (idx < nlo_p) {
+      const int hl = idx / nlo_t;
+      return hl * qtiles + (idx - hl * nlo_t);
+    }
+    const int j = idx - nlo_p, hl = j / nhi_t;
+    return hl * qtiles + nlo_t + (j - hl * nhi_t);
+  };
+  auto load_pair = [&](int pr) {
+    const int hl = pr / qtiles, it = pr - hl * qtiles;
+    load_tile_rows(x, Bk + (size_t)b * r_pad * W, 16 * it + c16, hl);
+  };
+  auto dot_pair = [&](int pr) {
+    const int hl = pr / qtiles, it = pr - hl * qtiles;
+    const v4f acc = tile_dot(x, hl);
+    if (c16 == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qs[hl * r_pad + 16 * it + 4 * lg + t] = acc[t];
+    }
+  };
   // one q value per thread (HG * d <= threads, checked at launch); stored unconditionally so the
   // load is never sunk behind the tile loads
   const int nq = nh * d;
   const float qv = q[((size_t)b * Hq + h0) * d + min(tid, nq - 1)];
   if (mq) {
-    if (wave < npair_q && lo_pair(wave)) {
+    if (spread) {
+      load_pair(pair_at(wave));
+    } else if (wave < npair_q && lo_pair(wave)) {
       const int hl = wave / qtiles, it = wave - hl * qtiles;
       load_tile_rows(x, Bk + (size_t)b * r_pad * W, 16 * it + c16, hl);
     }
@@ -581,7 +612,18 @@ __device__ __forceinline__ void select_body(
       }
     }
   };
-  if (mq) {
+  int next_item = npair_q;   // spread: this wavefront's first item not yet done
+  if (spread) {
+    int idx = wave;
+    for (; idx < npair_q; idx += nwv) {
+      const int pr = pair_at(idx);
+      if (idx != wave && !lo_pair(pr)) break;
+      if (idx != wave) load_pair(pr);
+      dot_pair(pr);
+    }
+    next_item = idx;
+    if (next_item < npair_q) load_pair(pair_at(next_item));
+  } else if (mq) {
     latent_pairs(true);
     // the B_k rows of the latent columns >= r_lo: requested only now, so that they do not
     // hold up q and the low rows in the memory system at the start
@@ -855,20 +897,29 @@ __device__ __forceinline__ void select_body(
       const bool b0 = bstar_h == 0;
       const float fbstar = static_cast<float>(bstar_h);
       uint32_t cbits = 0;   // scores in a partly taken boundary bin (bit 4a+t)
-      auto mark = [&](auto RANK) {
+      // Per step, the four scores' decisions are gathered as nibbles: tn (taken), cn (in
+      // the boundary bin, for the exact ranking); the per-head cases (every score taken,
+      // boundary bin 0) and the validity of each score are applied once per nibble, and
+      // validity only where the wavefront holds absent scores (ALLOK: none).
+      auto mark = [&](auto RANK, auto ALLOK) {
 #pragma unroll
         for (int a = 0; a < NACC; ++a) {
           const int n0 = tok(a);
-          uint32_t nib = 0;
+          uint32_t tn = 0, cn = 0;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const float x = fmaf(sc[4 * a + t], mul_h, off_h);
-            bool take = take_all || x >= fwhole;
-            const bool ok = all_ok || ((vm >> (4 * a + t)) & 1u);
-            nib |= (ok && take) ? (1u << t) : 0u;
-            if constexpr (decltype(RANK)::value)
-              cbits |= (ok && rank_h && !take && (b0 || x >= fbstar)) ? (1u << (4 * a + t)) : 0u;
+            tn |= x >= fwhole ? (1u << t) : 0u;
+            if constexpr (decltype(RANK)::value) cn |= x >= fbstar ? (1u << t) : 0u;
           }
+          tn = take_all ? 0xFu : tn;
+          if constexpr (!decltype(ALLOK)::value) tn &= (vm >> (4 * a)) & 0xFu;
+          if constexpr (decltype(RANK)::value) {
+            cn = (b0 ? 0xFu : cn) & ~tn;
+            if constexpr (!decltype(ALLOK)::value) cn &= (vm >> (4 * a)) & 0xFu;
+            cbits |= cn << (4 * a);
+          }
+          const uint32_t nib = tn;
           // The eight lanes holding the tokens of one (head, block) word are the two tile
           // halves (lane%16 apart by HG) in each of the four 16-lane rows: OR them together
           // (a rotation by HG inside the row leaves the pair in the upper half's lane, then
@@ -883,8 +934,14 @@ __device__ __forceinline__ void select_body(
           if (my_j == 1 && lg == 0 && my_on && blk < nblk) selw[my_h * nblk + blk] = wv;
         }
       };
-      if (any_rank) mark(std::true_type{});
-      else mark(std::false_type{});
+      if (all_ok) {
+        if (any_rank) mark(std::true_type{}, std::true_type{});
+        else mark(std::false_type{}, std::true_type{});
+      } else {
+        if (any_rank) mark(std::true_type{}, std::false_type{});
+        else mark(std::false_type{}, std::false_type{});
+      }
+      if (!rank_h) cbits = 0u;
       if (cbits) {
 #pragma unroll
         for (int a = 0; a < NACC; ++a) {
@@ -1014,7 +1071,15 @@ __device__ __forceinline__ void select_body(
     }
   }
   // the remaining latent queries: their B_k rows arrived during the selection
-  if (mq) latent_pairs(false);
+  if (spread) {
+    for (int idx = next_item; idx < npair_q; idx += nwv) {
+      const int pr = pair_at(idx);
+      if (idx != next_item) load_pair(pr);
+      dot_pair(pr);
+    }
+  } else if (mq) {
+    latent_pairs(false);
+  }
   lds_barrier();
 
   // ---- E. selection bits per (head, 32-token block)
