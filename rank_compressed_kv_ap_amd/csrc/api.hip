@@ -27,13 +27,15 @@ static ap_status hip_fail(hipError_t e, const char* what) {
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// N-splits of the flash-decode kernel for one cache: about two workgroups per CU, >= 5
-// token blocks each (measured best on the batch-32 LLaVA layer: 16 splits of 5-6 blocks);
-// splits > 0 is the caller's count.  Returns the split count and sets the blocks per split.
+// N-splits of the flash-decode kernel for one cache: about one workgroup per CU, >= 5
+// token blocks each; splits > 0 is the caller's count.  Returns the split count and sets the blocks per split.
 static int split_plan(const Dims& dm, int splits, int* CB) {
   int S = splits;
   if (S == 0) {
-    S = ceil_div(512, dm.B);
+    // about one flash-decode workgroup per CU (256): measured best on the batch-4
+    // long-video (64 splits), batch-64 GQA (4), batch-32 LLaVA (8) and batch-256 (1)
+    // layers; twice as many workgroups cost 2-11% more per step
+    S = ceil_div(256, dm.B);
     S = std::min(S, std::max(1, dm.nblk / 5));
   }
   // 4-bit codes: a workgroup stages the block scales of its tokens in LDS (<= 64 blocks)
