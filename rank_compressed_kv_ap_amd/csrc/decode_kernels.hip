@@ -690,6 +690,114 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
   }
 }
 
+// ================================================================ k_combine_wide
+// The combine of a batch with no text tokens and no second segment, for wide rows of
+// B_v: one workgroup per (sequence, block of CW columns = whole KV heads), every query
+// head of those KV heads.  Per head: the log-sum-exp merge of the splits (maximum,
+// split weights, sum); per (head, latent row): the merged latent sum; then each thread
+// takes one V-element column chunk and the latent rows rg, rg + RG, ... of its row
+// group, the first UB of them requested before the merge, and the row groups' partial
+// sums meet in LDS.
+constexpr int kWideThreadsMax = 256;
+constexpr int kWideMaxG = 4;       // query heads per KV head held in registers
+
+template <class T, int G>
+__global__ __launch_bounds__(kWideThreadsMax) void k_combine_wide(
+    const float* __restrict__ part_z, const float* __restrict__ part_ml, const T* __restrict__ Bv,
+    float* __restrict__ out, int S, int Hq, int HP, int RP, int W, int d, int CW, int RG,
+    float* __restrict__ ml_out) {
+  constexpr int V = Vec16<T>::n;
+  constexpr int UB = G <= 1 ? 16 : 8;   // B_v rows per thread in flight (registers)
+  extern __shared__ __align__(16) float smem_w[];
+  const int CH = W / CW;
+  const int b = blockIdx.x / CH, cb = blockIdx.x - (blockIdx.x / CH) * CH;
+  const int c0 = cb * CW;
+  const int kv0 = c0 / d;
+  const int h0 = kv0 * G;                // first query head of this block
+  const int nh = (CW / d) * G;           // query heads of this block
+  const int nchunk = CW / V;
+  const int tid = threadIdx.x;
+  const int chunk = tid % nchunk, rg = tid / nchunk;   // blockDim = nchunk * RG
+  float* zf = smem_w;                    // [nh][RP] merged latent sums
+  float* linv = zf + nh * RP;            // [nh] 1 / softmax sum
+  float* wgt = linv + nh;                // [nh][S] split weights
+  float* red = wgt + nh * S;             // [RG][G][CW] row-group partial sums
+  const size_t pb = (size_t)b * S * HP;
+  const int col = c0 + chunk * V;        // first column of this thread's chunk
+  const int hl0 = (col / d - kv0) * G;   // its first query head, local
+  const T* bbase = Bv + (size_t)b * RP * W + col;
+  const int nrow = (RP - rg + RG - 1) / RG;
+
+  Vec16<T> xb[UB];
+#pragma unroll
+  for (int u = 0; u < UB; ++u) xb[u].load(bbase + (size_t)min(rg + u * RG, RP - 1) * W);
+
+  for (int hl = tid; hl < nh; hl += blockDim.x) {
+    const int h = h0 + hl;
+    float M = kNegBig;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[(pb + (size_t)s * HP + h) * 2]);
+    float L = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float2 ml = *reinterpret_cast<const float2*>(part_ml + (pb + (size_t)s * HP + h) * 2);
+      const float w = exp2f(ml.x - M);
+      wgt[hl * S + s] = w;
+      L += w * ml.y;
+    }
+    linv[hl] = 1.f / L;
+    if (ml_out != nullptr) {   // softmax max (log2 units) and sum, for the selector state
+      ml_out[((size_t)b * Hq + h) * 2] = M;
+      ml_out[((size_t)b * Hq + h) * 2 + 1] = L;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nh * RP; idx += blockDim.x) {
+    const int hl = idx / RP, i = idx - hl * RP;
+    const float* zb = part_z + (pb + h0 + hl) * RP + i;
+    float z = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) z = fmaf(wgt[hl * S + s], zb[(size_t)s * HP * RP], z);
+    zf[idx] = z;
+  }
+  __syncthreads();
+
+  float acc[G][V];
+#pragma unroll
+  for (int gh = 0; gh < G; ++gh)
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[gh][e] = 0.f;
+  for (int u0 = 0; u0 < nrow; u0 += UB) {
+    if (u0 > 0) {
+#pragma unroll
+      for (int u = 0; u < UB; ++u) xb[u].load(bbase + (size_t)min(rg + (u0 + u) * RG, RP - 1) * W);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int row = rg + (u0 + u) * RG;
+      if (u0 + u < nrow) {
+#pragma unroll
+        for (int gh = 0; gh < G; ++gh) {
+          const float z = zf[(hl0 + gh) * RP + row];
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[gh][e] = fmaf(z, xb[u].get(e), acc[gh][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int gh = 0; gh < G; ++gh)
+#pragma unroll
+    for (int e = 0; e < V; ++e) red[((size_t)rg * G + gh) * CW + chunk * V + e] = acc[gh][e];
+  __syncthreads();
+  for (int idx = tid; idx < G * CW; idx += blockDim.x) {
+    const int gh = idx / CW, cc = idx - gh * CW;
+    const int kv = (c0 + cc) / d, j = (c0 + cc) - kv * d;
+    const int hl = (kv - kv0) * G + gh;
+    float o = 0.f;
+    for (int r = 0; r < RG; ++r) o += red[((size_t)r * G + gh) * CW + cc];
+    out[((size_t)b * Hq + h0 + hl) * d + j] = o * linv[hl];
+  }
+}
+
 // Scalar variant for head sizes the 16-byte path does not tile.
 template <class T>
 __global__ __launch_bounds__(kCombThreads) void k_combine_scalar(
@@ -891,9 +999,60 @@ static hipError_t launch_combine_t(const ap_cache* c, const float* q, float* out
   return hipGetLastError();
 }
 
+// The wide combine's plan: the fewest column blocks (whole KV heads, a divisor of Hkv)
+// that give about 2048 workgroups; row groups as many as the threads, the rows and a
+// 32 KB partial-sum buffer allow.  Returns false where it does not apply.  It serves
+// grouped-query layers (G >= 2: each B_v row chunk is read once for the G query heads
+// that share it, instead of once per query head; batch-64 GQA layer combine 9.9 -> 8.3
+// us) with few splits; with one query head per KV head the per-head kernel is as fast
+// (batch-256 layer: 28 us both), and with many splits (64 on the batch-4 long-video
+// layer) its per-head merge loops are the shorter chain (8.9 against 28 us).
+static bool wide_plan(const Dims& dm, int S, int* CW, int* RG, int* threads, size_t* lds) {
+  constexpr int V = 8;   // bf16 elements per 16-byte load
+  if (dm.storage == AP_F32 || dm.G < 2 || dm.G > kWideMaxG || S > 16 || dm.d % V != 0 || dm.W % V != 0)
+    return false;
+  int CH = dm.Hkv;
+  for (int c = 1; c <= dm.Hkv; ++c)
+    if (dm.Hkv % c == 0 && (long long)dm.B * c >= 2048) { CH = c; break; }
+  const int cw = dm.W / CH;
+  const int nchunk = cw / V;
+  if (nchunk > kWideThreadsMax) return false;
+  int rg = 1;
+  while (2 * rg <= dm.r_pad && nchunk * 2 * rg <= kWideThreadsMax && 2 * rg * dm.G * cw <= 8192) rg *= 2;
+  const int nh = (cw / dm.d) * dm.G;
+  const size_t bytes = ((size_t)nh * dm.r_pad + nh + (size_t)nh * S + (size_t)rg * dm.G * cw) * sizeof(float);
+  if (bytes > 64 * 1024) return false;
+  *CW = cw;
+  *RG = rg;
+  *threads = nchunk * rg;
+  *lds = bytes;
+  return true;
+}
+
+template <int G>
+static hipError_t launch_wide_g(const ap_cache* c, float* out, int S, int CW, int RG, int threads, size_t lds,
+                                float* ml_out, hipStream_t st, const KernelEvents& ev) {
+  const Dims& dm = c->dm;
+  hipExtLaunchKernelGGL((k_combine_wide<bf16_t, G>), dim3(dm.B * (dm.W / CW)), dim3(threads), lds, st,
+                        ev.start, ev.stop, 0, c->part_z, c->part_ml, static_cast<const bf16_t*>(c->Bv), out,
+                        S, dm.Hq, dm.Hq_pad, dm.r_pad, dm.W, dm.d, CW, RG, ml_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const ap_cache* c, const float* q, float* out, float sl2, int S, int Tn,
                           const void* tk, const void* tv, float* ml_out, const float* xo,
                           const float* xml, hipStream_t st, const KernelEvents& ev) {
+  // grouped-query layers with no text tokens and no second segment: the wide combine
+  int CW = 0, RG = 0, threads = 0;
+  size_t lds = 0;
+  if (Tn == 0 && xo == nullptr && xml == nullptr && wide_plan(c->dm, S, &CW, &RG, &threads, &lds)) {
+    switch (c->dm.G) {
+      case 2: return launch_wide_g<2>(c, out, S, CW, RG, threads, lds, ml_out, st, ev);
+      case 3: return launch_wide_g<3>(c, out, S, CW, RG, threads, lds, ml_out, st, ev);
+      case 4: return launch_wide_g<4>(c, out, S, CW, RG, threads, lds, ml_out, st, ev);
+      default: break;
+    }
+  }
   // B and the text tokens are bf16 for 4-bit caches too
   if (c->dm.storage != AP_F32)
     return launch_combine_t<bf16_t>(c, q, out, sl2, S, Tn, tk, tv, ml_out, xo, xml, st, ev);
