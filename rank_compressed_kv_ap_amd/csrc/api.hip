@@ -32,10 +32,12 @@ static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 static int split_plan(const Dims& dm, int splits, int* CB) {
   int S = splits;
   if (S == 0) {
-    // about one flash-decode workgroup per CU (256): measured best on the batch-4
-    // long-video (64 splits), batch-64 GQA (4), batch-32 LLaVA (8) and batch-256 (1)
-    // layers; twice as many workgroups cost 2-11% more per step
-    S = ceil_div(256, dm.B);
+    // about one flash-decode workgroup per CU (256) for bf16 factors: measured best on
+    // the batch-4 long-video (64 splits), batch-64 GQA (4), batch-32 LLaVA (8) and
+    // batch-256 (1) layers, where twice as many workgroups cost 2-11% more per step; 4-bit
+    // codes keep two per CU (the expansion makes that kernel issue-bound: batch-64 GQA
+    // attention 26.9 us at 8 splits, 34.7 us at 4)
+    S = ceil_div(dm.storage == AP_INT4 ? 512 : 256, dm.B);
     S = std::min(S, std::max(1, dm.nblk / 5));
   }
   // 4-bit codes: a workgroup stages the block scales of its tokens in LDS (<= 64 blocks)
