@@ -41,6 +41,12 @@ SHAPES = {
     "bf16_single_3": wl.LLAVA.replace(cfg_id=125, batch=2, n_q_heads=4, n_kv_heads=4, head_dim=32,
                                       n_tokens=2100, n_text=0, rank=64, r_lo=16, top_k=500,
                                       grid=None, inner_dim=256),
+    # grouped-query heads with no text on the split path: the combine that reads each
+    # B_v row chunk once for the four query heads of a KV head writes the softmax
+    # statistics the state update reads
+    "bf16_gqa_split": wl.LLAVA.replace(cfg_id=126, batch=3, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                                       n_tokens=300, n_text=0, rank=48, r_lo=16, top_k=75, grid=None,
+                                       inner_dim=128),
     # more selection workgroups than CUs: the 8-wavefront selector
     "bf16_many_wgs": wl.LLAVA.replace(cfg_id=123, batch=70, n_q_heads=16, n_kv_heads=16,
                                       head_dim=64, n_tokens=300, n_text=5, rank=32, r_lo=16,
@@ -145,7 +151,7 @@ def _run(gpu_lib, w, mode, alpha, steps, n_distinct=None, seed=5, splits=0, path
 
 
 @pytest.mark.parametrize("mode", ["ema_token", "ema_head"])
-@pytest.mark.parametrize("name,alpha", [("bf16_text", 0.8), ("f32_gqa", 0.5)])
+@pytest.mark.parametrize("name,alpha", [("bf16_text", 0.8), ("f32_gqa", 0.5), ("bf16_gqa_split", 0.6)])
 def test_ema_selector_steps(gpu_lib, name, mode, alpha):
     _run(gpu_lib, SHAPES[name], mode, alpha, steps=4)
 
