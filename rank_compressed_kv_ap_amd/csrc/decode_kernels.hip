@@ -32,9 +32,11 @@ namespace ap {
 // ================================================================ k_attn
 // Each wavefront walks its 32-token blocks with the next blocks' U_k / U_v tiles and
 // selection words already in flight (a ring of 2-4 stages, as deep as the registers
-// allow), and updates the online softmax per 16-token half so few values stay live.  The latent query is rounded
-// once to bf16 here (the selection kernel keeps it split for exact ranking); the
-// rounding moves a score by about 2^-9 of its size, far inside the output tolerance.
+// allow), and updates the online softmax per 16-token half so few values stay live.  The
+// latent query's columns below r_lo enter the low-rank logits as bf16 hi + lo (about 16
+// bits, as in the selection kernel's scores); the columns at and above r_lo are rounded
+// once to bf16, which moves a selected token's full-rank term by about 2^-9 of its size,
+// far inside the output tolerance.
 template <class T, int NP, int HT>
 __device__ __forceinline__ void attn_load(const T* __restrict__ Uk, const T* __restrict__ Uv,
                                           const uint32_t* __restrict__ mask, int b, int blk,
