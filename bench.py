@@ -368,6 +368,16 @@ def main():
         c.free()
     del caches, qs, texts, tcaches
 
+    # the device's streaming-read ceiling (a plain read kernel over 1 GiB, beyond the
+    # 256 MB last-level cache), next to the datasheet peak: measured after the timed
+    # steps, outside them
+    rbuf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    read_gbps = binding.read_bandwidth(rbuf, passes=10)
+    del rbuf
+    result["hbm"]["read_ceiling_GB/s"] = read_gbps
+    result["hbm"]["frac_of_read_ceiling"] = result["hbm"]["GB/s"] / read_gbps
+    result["roofline"]["frac_of_read_ceiling"] = achieved / read_gbps
+
     if not args.no_compress:
         result["compress"] = compress_leg(w, args.compress_reps, binding, wl, np, torch)
     if not args.no_e2e:

@@ -273,6 +273,15 @@ enum { AP_KERNEL_SELECT = 0, AP_KERNEL_ATTN = 1, AP_KERNEL_COMBINE = 2, AP_KERNE
 ap_status ap_timing_enable(ap_cache* c, int32_t max_calls);
 ap_status ap_timing_read(ap_cache* c, float* ms_per_kernel /* [AP_N_KERNELS] */, int32_t* calls);
 
+/* Streaming-read ceiling of the device (a measurement aid, not part of the method): one
+ * untimed and then `passes` timed runs of a plain grid-stride kernel that reads all of
+ * `buf` (device memory, caller-owned, 16-byte aligned, `bytes` a multiple of 16) on
+ * `stream`; writes the mean milliseconds per pass and returns after the passes finish.
+ * Use a buffer well beyond the 256 MB last-level cache so that the reads come from HBM.
+ * AP_ERR_NULL_ARG / AP_ERR_BAD_SHAPE before anything is enqueued; AP_ERR_HIP on a
+ * runtime failure. */
+ap_status ap_read_bandwidth(const void* buf, size_t bytes, int32_t passes, void* stream, float* ms_per_pass);
+
 /* Text for a status code, and the detail of the calling thread's last failure. */
 const char* ap_status_string(ap_status s);
 const char* ap_last_error(void);

@@ -24,7 +24,7 @@ KERNEL_NAMES = ("select", "attn", "combine", "decode", "ema", "text")
 EXPORTED = (
     "ap_compress", "ap_recompress", "ap_recompress_noalloc", "ap_cache_set_factors", "ap_cache_get_factors",
     "ap_cache_get_sigma", "ap_cache_info", "ap_decode_attn", "ap_free", "ap_timing_enable",
-    "ap_timing_read", "ap_status_string", "ap_last_error",
+    "ap_timing_read", "ap_status_string", "ap_last_error", "ap_read_bandwidth",
 )
 
 
@@ -74,8 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ap_status_string.restype = ctypes.c_char_p
     lib.ap_last_error.argtypes = []
     lib.ap_last_error.restype = ctypes.c_char_p
+    lib.ap_read_bandwidth.argtypes = [vp, ctypes.c_size_t, i32, vp, ctypes.POINTER(ctypes.c_float)]
     for name in ("ap_compress", "ap_recompress", "ap_recompress_noalloc", "ap_cache_set_factors", "ap_cache_get_factors", "ap_cache_get_sigma",
-                 "ap_cache_info", "ap_decode_attn", "ap_timing_enable", "ap_timing_read"):
+                 "ap_cache_info", "ap_decode_attn", "ap_timing_enable", "ap_timing_read", "ap_read_bandwidth"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -257,3 +258,12 @@ def decode(cache: Cache, q: torch.Tensor, *, r_lo: int, top_k: int, scale: float
     _check(lib.ap_decode_attn(cache.handle, _ptr(q), _ptr(out), ctypes.byref(p), _stream()),
            "ap_decode_attn")
     return out
+
+
+def read_bandwidth(buf: torch.Tensor, passes: int = 10) -> float:
+    """ap_read_bandwidth: the device's streaming-read rate over buf (GB/s)."""
+    ms = ctypes.c_float()
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.ap_read_bandwidth(_ptr(buf), nbytes, passes, _stream(), ctypes.byref(ms)),
+           "ap_read_bandwidth")
+    return nbytes / (ms.value * 1e-3) / 1e9

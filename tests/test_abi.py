@@ -128,3 +128,15 @@ def test_decode_rejects_text_pointers_without_text_tokens():
         assert b"n_text" in b.lib.ap_last_error()
     dp = b.DecodeParams(4, 8, 0.1, 0, None, None, None, 0)
     assert b.lib.ap_decode_attn(None, None, None, ctypes.byref(dp), None) == b.AP_ERR_NULL_ARG
+
+
+def test_read_bandwidth_rejects_bad_arguments_before_any_launch():
+    # every check runs before a device call, so bogus (never dereferenced) pointers are safe
+    from rank_compressed_kv_ap_amd import binding as b
+    ms = ctypes.c_float()
+    assert b.lib.ap_read_bandwidth(None, 1024, 1, None, ctypes.byref(ms)) == b.AP_ERR_NULL_ARG
+    assert b.lib.ap_read_bandwidth(ctypes.c_void_p(256), 1024, 1, None, None) == b.AP_ERR_NULL_ARG
+    for ptr, nbytes, passes in ((256, 1000, 1), (256, 0, 1), (8, 1024, 1), (256, 1024, 0), (256, 1024, 1001)):
+        assert b.lib.ap_read_bandwidth(ctypes.c_void_p(ptr), nbytes, passes, None,
+                                       ctypes.byref(ms)) == b.AP_ERR_BAD_SHAPE, (ptr, nbytes, passes)
+    assert b"16-byte" in b.lib.ap_last_error()
