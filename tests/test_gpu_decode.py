@@ -192,6 +192,20 @@ def test_decode_more_selection_workgroups_than_cus(gpu_lib):
         assert np.array_equal(out[b], out[b % 2]) and np.array_equal(sel[b], sel[b % 2]), b
 
 
+@pytest.mark.parametrize("n_text", [0, 7])
+def test_decode_many_selection_workgroups_of_16_wavefronts(gpu_lib, n_text):
+    """B * Hq / 4 > 256 workgroups whose four heads' tokens need more than 8 steps of 8
+    wavefronts (N > 4096): the selector keeps 16 wavefronts per workgroup and runs two
+    rounds of workgroups; grouped-query heads, a ragged token tail, with and without text."""
+    w = wl.GQA.replace(cfg_id=113, batch=33, n_q_heads=32, n_kv_heads=8, head_dim=32,
+                       n_tokens=4200, n_text=n_text, rank=32, r_lo=16, top_k=1050, inner_dim=256)
+    seqs = make_inputs(w, 2)
+    out, sel = run_decode(w, seqs, gpu_lib)
+    check_against_oracle(w, seqs, out, sel)
+    for b in range(2, w.batch):
+        assert np.array_equal(out[b], out[b % 2]) and np.array_equal(sel[b], sel[b % 2]), b
+
+
 @pytest.mark.parametrize("cfg,n_distinct,splits", [(2, 3, 0), (2, 3, 16), (3, 2, 0), (4, 2, 0),
                                                    (5, 2, 0)])
 def test_decode_parity_full_configs(gpu_lib, cfg, n_distinct, splits):
