@@ -7,7 +7,7 @@ reduced rank (the French page gives R/4 as the example); attention then runs
 over the decompressed keys and values.  25% of the tokens at full rank is the
 setting the Spanish page reports ([es §4 "Análisis de Sensibilidad"]).
 
-Readings taken where the summaries are open (each listed in the design doc):
+Readings taken where the summaries are open:
   * importance of a token for query head h at this step = its low-rank
     attention logit s_lo (the score from the first r_lo components).  The
     summaries instead keep a moving average of accumulated attention scores
@@ -105,7 +105,7 @@ def decode_ema_steps(U_k, B_k, U_v, B_v, qs, n_kv_heads: int, head_dim: int, r_l
     [es §2.B], [fr §2.B "Score d'importance"], [de §2.B "Mechanismus"]: each token's
     importance is a moving average, with parameter alpha, of the attention it has
     received; the tokens of highest importance are decompressed at full rank.
-    Readings (listed in the design doc): the average is taken over the attention weights
+    Readings where the pages are open: the average is taken over the attention weights
     p of each step, I <- alpha * I + (1 - alpha) * p; a step selects with the
     importance left by the steps before it; the first step (state None) has no
     history and selects by its own low-rank logit, and then I = p.  per_head: one

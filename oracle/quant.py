@@ -6,7 +6,7 @@ Modular"], [fr §4 "Compatibilité"], [de §3 "Kombinierbarkeit"], [de §4
 "Kombination mit anderen Techniken"]).  They also note that plain quantization
 struggles with outlier values ([fr §1 "Limites des solutions existantes"],
 [de §1 "Ineffizienz bestehender Lösungen"]).  They give no format, so this module
-states one (each reading is listed in the design doc):
+states one; these are readings, not the pages' format:
 
   * only the token factor U (N x r, singular values folded in) is quantized;
     the r x W factor B stays at the storage precision;
