@@ -281,3 +281,22 @@ def test_decode_without_sel_out_is_the_checked_call(gpu_lib, name):
     for b in range(len(seqs), w.batch):
         assert np.array_equal(out0[b], out0[b % len(seqs)]), f"replica {b}"
     print(f"{name}: max abs err {err:.3e} without sel_out")
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_split_path_bench_call_without_sel_out(gpu_lib, cfg):
+    """The call `bench.py --cfg N` times on the other workloads at full size: splits = 0
+    and no sel_out, through the three-kernel path (the default split count).  Its output
+    is compared with the oracle, and it equals bit for bit the same call with sel_out."""
+    w = wl.WORKLOADS[cfg]
+    seqs = make_inputs(w, 2)
+    cache, q, tk, tv = upload_decode(w, seqs, gpu_lib)
+    out0, _, ms = _decode_once(gpu_lib, w, cache, q, tk, tv, with_sel=False, timed=True)
+    assert ms["decode"] == 0 and ms["select"] > 0 and ms["attn"] > 0 and ms["combine"] > 0, ms
+    out1, sel, _ = _decode_once(gpu_lib, w, cache, q, tk, tv, with_sel=True)
+    cache.free()
+    assert torch.equal(out0, out1)
+    err, _ = check_against_oracle(w, seqs, out0.numpy(), None)
+    for b in range(len(seqs), w.batch):
+        assert np.array_equal(out0.numpy()[b], out0.numpy()[b % len(seqs)]), f"replica {b}"
+    print(f"cfg {cfg}: max abs err {err:.3e} without sel_out")
