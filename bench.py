@@ -189,7 +189,7 @@ def calib_copy():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     if args.calib_copy:
         calib_copy()

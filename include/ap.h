@@ -33,7 +33,7 @@ typedef enum {
   AP_ERR_NULL_ARG = 1,       /* a required pointer was NULL                          */
   AP_ERR_BAD_SHAPE = 2,      /* sizes out of range or inconsistent                   */
   AP_ERR_BAD_DTYPE = 3,      /* storage dtype not one of ap_dtype                    */
-  AP_ERR_UNSUPPORTED = 4,    /* valid by the method, outside what this build handles */
+  AP_ERR_UNSUPPORTED = 4,    /* valid by the method, outside what the library handles */
   AP_ERR_OUT_OF_MEMORY = 5,  /* a device allocation failed                           */
   AP_ERR_HIP = 6             /* a HIP runtime call failed                            */
 } ap_status;

@@ -60,7 +60,7 @@ static ap_status validate_shape(const ap_compress_params* p) {
   if (p->rank < 1 || p->rank > p->n_tokens || p->rank > W) return fail(AP_ERR_BAD_SHAPE, "need 1 <= rank <= min(n_tokens, n_kv_heads*head_dim)");
   if (p->oversample < 0) return fail(AP_ERR_BAD_SHAPE, "oversample < 0");
   if (p->power_iters < 0) return fail(AP_ERR_BAD_SHAPE, "power_iters < 0");
-  // limits of this build's tiling
+  // limits of the kernels' tiling
   if (p->n_tokens > 32768) return fail(AP_ERR_UNSUPPORTED, "n_tokens > 32768");
   if (p->batch > 32767) return fail(AP_ERR_UNSUPPORTED, "batch > 32767 (2 * batch matrices index one grid dimension)");
   if (p->head_dim > 256) return fail(AP_ERR_UNSUPPORTED, "head_dim > 256");

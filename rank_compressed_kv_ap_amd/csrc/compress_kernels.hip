@@ -1428,7 +1428,7 @@ __global__ void k_copy_sigma(const float* __restrict__ sig, float* __restrict__ 
   ((mat & 1) ? sv : sk)[(size_t)(mat >> 1) * r + i] = sig[(size_t)mat * ellp + i];
 }
 
-// ================================================================ driver
+// ================================================================ launch sequence
 // Clears a buffer (16-byte words; a kernel rather than hipMemsetAsync, so that a caller
 // may capture the whole factorisation in a graph).
 __global__ __launch_bounds__(256) void k_zero(uint4* __restrict__ p, size_t n16) {
