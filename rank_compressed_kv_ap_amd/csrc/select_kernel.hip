@@ -1167,22 +1167,37 @@ __device__ __forceinline__ void select_body(
         }
       }
     };
-    if (mq) {
-      for (int pair = wave; pair < npair_t; pair += nwv) {
-        const int hl = pair / ttiles, it = pair - hl * ttiles;
-        if (pair != wave) load_text_tile(pair);
-        const v4f acc = tile_dot(xt, hl);
-        if (c16 == 0) {
+    // at most one (head, tile) pair per wavefront (its rows already in xt): the first
+    // tiles of the full-rank score pass are requested before the text scores, whose
+    // products then overlap their latency; with more pairs (text rows loaded here) they
+    // are requested after them
+    const bool one_pair = mq && npair_t <= nwv;
+    if (one_pair) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int tok = 16 * it + 4 * lg + t;
-            if (tok < Tn) {
-              const float sv = acc[t] * fa.sl2;
-              sts[hl * Tn + tok] = sv;
-              atomicMax(&hmx[hl], score_key(sv));
-            }
+      for (int s = 0; s < PD; ++s) ld(s);
+    }
+    auto text_pair = [&](int pair) {
+      const int hl = pair / ttiles, it = pair - hl * ttiles;
+      const v4f acc = tile_dot(xt, hl);
+      if (c16 == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int tok = 16 * it + 4 * lg + t;
+          if (tok < Tn) {
+            const float sv = acc[t] * fa.sl2;
+            sts[hl * Tn + tok] = sv;
+            atomicMax(&hmx[hl], score_key(sv));
           }
         }
+      }
+    };
+    if (one_pair) {
+      // straight-line code: the wait before the product counts the tile loads above
+      if (wave < npair_t) text_pair(wave);
+    } else if (mq) {
+      for (int pair = wave; pair < npair_t; pair += nwv) {
+        if (pair != wave) load_text_tile(pair);
+        text_pair(pair);
       }
     } else if (Tn > 0) {
       text_scores(wave * RPW + rw);
@@ -1192,11 +1207,13 @@ __device__ __forceinline__ void select_body(
       }
     }
 
-    // first tiles of the full-rank score pass: requested after the text scores, whose
-    // rows then are the only loads ahead of them (requests in flight during the
-    // selection's LDS-bound phases slow them more than they gain)
+    // first tiles of the full-rank score pass (unless requested above): requested after
+    // the text scores, whose rows then are the only loads ahead of them (requests in
+    // flight during the selection's LDS-bound phases slow them more than they gain)
+    if (!one_pair) {
 #pragma unroll
-    for (int s = 0; s < PD; ++s) ld(s);
+      for (int s = 0; s < PD; ++s) ld(s);
+    }
     // ---- F2. full-rank part of the selected tokens' scores (columns >= r_lo), on the
     // same block-diagonal tiles as the low-rank scores; final scores in log2 units
     const int nph = NPr - p0;
