@@ -229,7 +229,10 @@ def main():
 
     kb = kernel_bytes(w, args.select, args.text_rank)
     step_bytes = B * kb["decode"]   # every byte of one step, whichever path runs
-    R = max(1, math.ceil(2 * MALL_BYTES / step_bytes))
+    # rotated cache copies: together at least twice the 256 MB last-level cache, and never
+    # fewer than two, so that no step finds its factors left in that cache by the step
+    # before (a single copy larger than the cache still leaves part of it resident)
+    R = max(2, math.ceil(2 * MALL_BYTES / step_bytes))
     caches, qs, texts, tcaches = [], [], [], []
     Rt = args.text_rank
     tr_lo, tk_top = max(1, Rt // 4), (w.n_text + 3) // 4

@@ -553,9 +553,11 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
   // partials of the first U splits.
   const T* bbase = Bv + (size_t)b * RP * W + (size_t)g * d + seg * V;
   Vec16<T> xb[U];
+  // B_v rows are read once per step (non-temporal: they do not displace the token
+  // factors in the caches; batch-256 layer combine 28.5 -> 26.3 us)
   if constexpr (!TEXT) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) xb[u].load(bbase + (size_t)min(u * RPP + rg, RP - 1) * W);
+    for (int u = 0; u < U; ++u) xb[u].load_nt(bbase + (size_t)min(u * RPP + rg, RP - 1) * W);
   }
   float zv0[U];
   {
@@ -667,7 +669,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
   for (int i0 = 0; i0 < RP; i0 += U * RPP) {
     if (TEXT || i0 > 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) xb[u].load(bbase + (size_t)min(i0 + u * RPP + rg, RP - 1) * W);
+      for (int u = 0; u < U; ++u) xb[u].load_nt(bbase + (size_t)min(i0 + u * RPP + rg, RP - 1) * W);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
