@@ -104,6 +104,9 @@ SMALL = {
     # fp32 with widths and token counts not multiples of 4 (element-wise operand loads)
     "f32_odd": (wl.TINY.replace(cfg_id=214, batch=2, n_kv_heads=3, n_q_heads=3, head_dim=21,
                                 n_tokens=131, rank=16, inner_dim=50), {}),
+    # 576 tokens: A X over four and a half 128-row tiles, eight matrices
+    "bf16_rows576": (wl.LLAVA.replace(cfg_id=215, batch=4, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                                      n_tokens=576, rank=32, grid=None, inner_dim=256), {}),
     # 8 matrices: the product kernels deal each matrix's row tiles to one XCD
     "bf16_eight_matrices": (wl.LLAVA.replace(cfg_id=209, batch=4, n_q_heads=4, n_kv_heads=4, head_dim=64,
                                              n_tokens=300, rank=24, grid=None, inner_dim=120), {}),
